@@ -1,0 +1,59 @@
+"""Brute-force scaled dot-product attention in 50-digit arithmetic (mpmath).
+
+TEST INFRASTRUCTURE ONLY (same rule as ``sdpa_oracle``: only ``tests/``,
+``__graft_entry__.smoke()`` and ``bench.py``'s cpu_baseline leg may use it).
+
+A second, separately written evaluation of Eq. (1) of 《精读 Attention Is All
+You Need：原始 Transformer 论文》 ("缩放点积注意力：点积为什么要缩放"), with
+scalar loops only and no array library, used to check the fp64 oracle on tiny
+shapes.  For every query i it walks the keys j, keeps those that are legal
+(causal: j ≤ i, per 《Attention Is All You Need：注意力就是你所需要的一切》
+§3.2.3; padding: j < clamp(len, 0, m)), forms exp(scale · q_i·k_j) over them
+only (illegal keys carry weight exactly zero), and divides the weighted sum of
+the values by the sum of the exponentials.  A query with no legal key yields
+the zero vector.  It does not subtract a row maximum: at 50 digits and the
+small magnitudes used in tests nothing overflows, which makes this a genuinely
+different route from the oracle's.
+"""
+
+from __future__ import annotations
+
+import mpmath
+
+
+def attention_mp(q, k, v, scale, causal=False, key_lens=None, dps=50):
+    """q: [B][h][n][d_k], k: [B][h][m][d_k], v: [B][h][m][d_v] nested sequences.
+
+    Returns nested lists of ``mpmath.mpf`` with shape [B][h][n][d_v].
+    """
+    with mpmath.workdps(dps):
+        sc = mpmath.mpf(scale) if not isinstance(scale, mpmath.mpf) else scale
+        out = []
+        for b in range(len(q)):
+            L = None if key_lens is None else int(key_lens[b])
+            heads = []
+            for hh in range(len(q[b])):
+                Q, K, V = q[b][hh], k[b][hh], v[b][hh]
+                m = len(K)
+                d_v = len(V[0]) if m else 0
+                lim = m if L is None else min(max(L, 0), m)
+                rows = []
+                for i in range(len(Q)):
+                    num = [mpmath.mpf(0)] * d_v
+                    den = mpmath.mpf(0)
+                    for j in range(m):
+                        if j >= lim or (causal and j > i):
+                            continue
+                        dot = mpmath.fsum(mpmath.mpf(float(Q[i][t])) * mpmath.mpf(float(K[j][t]))
+                                          for t in range(len(Q[i])))
+                        e = mpmath.exp(sc * dot)
+                        den += e
+                        for c in range(d_v):
+                            num[c] += e * mpmath.mpf(float(V[j][c]))
+                    if den == 0:
+                        rows.append([mpmath.mpf(0)] * d_v)
+                    else:
+                        rows.append([x / den for x in num])
+                heads.append(rows)
+            out.append(heads)
+        return out

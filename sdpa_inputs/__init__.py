@@ -1,0 +1,131 @@
+"""Seeded synthetic inputs for scaled dot-product attention.
+
+This module only draws and rounds numbers; it holds none of the attention
+arithmetic.  It is the one module that both the CPU oracle's tests and the GPU
+path's tests and benchmark use, so that both sides see bit-identical inputs.
+
+Distribution: Q, K and V components are iid N(0, 1).  That is the pages' own
+model of query and key components (《Attention Is All You Need：注意力就是你所
+需要的一切》 §3.2.1, footnote 4: independent components with mean 0 and
+variance 1, so that q·k has mean 0 and variance d_k).  Shapes follow the base
+model (h = 8, d_k = d_v = 64, d_model = 512) and the big model (h = 16,
+d_k = d_v = 64, d_model = 1024) of Table 3 on the page 《精读 Attention Is All
+You Need：原始 Transformer 论文》.  Synthetic N(0, 1) batches stand in for the
+pages' WMT 2014 sentence batches, which are not used here.
+
+Draw order for a seed: ``rng = numpy.random.default_rng(seed)`` (PCG64), then
+Q, K, V via ``rng.standard_normal(shape, dtype=float32)``, then the per-sequence
+key lengths via ``rng.integers(lo, hi, size=B, endpoint=True)``.  bf16 inputs
+are the round-to-nearest-even bf16 values of those float32 draws; the arrays
+returned here hold exactly the values the device sees (as float32).
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+__all__ = ["Workload", "WORKLOADS", "make_inputs", "round_to_bf16", "bf16_bits", "bits_to_f32"]
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    h: int
+    n: int
+    m: int
+    d_k: int
+    d_v: int
+    causal: bool
+    key_len_range: tuple | None  # inclusive (lo, hi) or None for no padding
+    seed: int
+    dtypes: tuple = field(default=("bf16",))
+    what: str = ""
+
+
+WORKLOADS = {
+    "single_head_16": Workload(
+        "single_head_16", B=1, h=1, n=16, m=16, d_k=64, d_v=64, causal=False,
+        key_len_range=None, seed=1001, dtypes=("f32",),
+        what="one head, 16 queries over 16 keys, no mask"),
+    "encoder_self_base": Workload(
+        "encoder_self_base", B=64, h=8, n=64, m=64, d_k=64, d_v=64, causal=False,
+        key_len_range=(8, 64), seed=1002, dtypes=("f32", "bf16"),
+        what="encoder self-attention, base shape, key padding U[8,64]"),
+    "decoder_causal_base": Workload(
+        "decoder_causal_base", B=64, h=8, n=64, m=64, d_k=64, d_v=64, causal=True,
+        key_len_range=(8, 64), seed=1003, dtypes=("bf16",),
+        what="decoder masked self-attention, base shape, causal + key padding U[8,64]"),
+    "cross_big": Workload(
+        "cross_big", B=32, h=16, n=48, m=64, d_k=64, d_v=64, causal=False,
+        key_len_range=(16, 64), seed=1004, dtypes=("bf16",),
+        what="encoder-decoder cross-attention, big shape, 48 queries over 64 source keys, "
+             "source key padding U[16,64]"),
+    "long_causal_8k": Workload(
+        "long_causal_8k", B=4, h=16, n=8192, m=8192, d_k=64, d_v=64, causal=True,
+        key_len_range=None, seed=1005, dtypes=("bf16",),
+        what="long-sequence causal self-attention, 8192 tokens, no padding"),
+}
+
+
+def round_to_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest bf16 (ties to even); returns float32."""
+    return bits_to_f32(bf16_bits(x))
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """uint16 bf16 bit patterns of float32 ``x`` (round to nearest, ties to even)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    r = ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
+    nan = np.isnan(x)
+    if nan.any():
+        r[nan] = ((u[nan] >> 16) | 0x40).astype(np.uint16)  # keep NaNs quiet NaNs
+    return r
+
+
+def bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """float32 values of uint16 bf16 bit patterns (exact)."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def make_inputs(wl: Workload | str, dtype: str | None = None, seed: int | None = None):
+    """Draw one batch for workload ``wl``.
+
+    Returns a dict with float32 arrays ``q`` [B,h,n,d_k], ``k`` [B,h,m,d_k],
+    ``v`` [B,h,m,d_v] holding exactly the device values (bf16-rounded when
+    ``dtype == "bf16"``), ``key_lens`` (int32 [B] or None), ``causal``,
+    ``dtype`` and the workload.
+    """
+    if isinstance(wl, str):
+        wl = WORKLOADS[wl]
+    dtype = dtype or wl.dtypes[-1]
+    if dtype not in ("f32", "bf16"):
+        raise ValueError(dtype)
+    rng = np.random.default_rng(wl.seed if seed is None else seed)
+    q = rng.standard_normal((wl.B, wl.h, wl.n, wl.d_k), dtype=np.float32)
+    k = rng.standard_normal((wl.B, wl.h, wl.m, wl.d_k), dtype=np.float32)
+    v = rng.standard_normal((wl.B, wl.h, wl.m, wl.d_v), dtype=np.float32)
+    key_lens = None
+    if wl.key_len_range is not None:
+        lo, hi = wl.key_len_range
+        key_lens = rng.integers(lo, hi, size=wl.B, endpoint=True).astype(np.int32)
+    if dtype == "bf16":
+        q, k, v = round_to_bf16(q), round_to_bf16(k), round_to_bf16(v)
+    return {"q": q, "k": k, "v": v, "key_lens": key_lens, "causal": wl.causal,
+            "dtype": dtype, "workload": wl}
+
+
+def random_case(rng: np.random.Generator, B, h, n, m, d_k, d_v, dtype="f32", causal=False,
+                key_lens=None):
+    """Free-shape N(0,1) case from an existing generator (for parity sweeps)."""
+    q = rng.standard_normal((B, h, n, d_k), dtype=np.float32)
+    k = rng.standard_normal((B, h, m, d_k), dtype=np.float32)
+    v = rng.standard_normal((B, h, m, d_v), dtype=np.float32)
+    if dtype == "bf16":
+        q, k, v = round_to_bf16(q), round_to_bf16(k), round_to_bf16(v)
+    kl = None if key_lens is None else np.asarray(key_lens, dtype=np.int32)
+    return {"q": q, "k": k, "v": v, "key_lens": kl, "causal": causal, "dtype": dtype}

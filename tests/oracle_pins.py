@@ -1,0 +1,254 @@
+"""Pins for the fp64 oracle: facts fixed by the pages and by mathematics.
+
+Each ``pin_*`` function takes the oracle module and raises AssertionError if
+the oracle disagrees with a fact that does not come from the oracle itself:
+printed numbers of the pages' worked examples (fixtures under tests/golden/),
+closed forms, invariants of Eq. (1), special cases that reduce to plain
+arithmetic, and a 50-digit brute-force evaluation on tiny shapes.  The pin
+tests run them as they are; the mutation tests run them against copies of the
+oracle with one planted mistake each and require that some pin fails.
+"""
+
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name), encoding="utf-8") as f:
+        return json.load(f)
+
+
+def _half_unit(printed: str) -> float:
+    """Half a unit in the last printed digit of a decimal string."""
+    if "." in printed:
+        return 0.5 * 10.0 ** (-len(printed.split(".")[1]))
+    return 0.5
+
+
+def _worked_example():
+    g = _load("worked_example_2d.json")
+    q = np.array(g["query"], dtype=np.float64)
+    K = np.array([e["k"] for e in g["keys"]], dtype=np.float64)
+    return g, q, K
+
+
+# --- worked example (《精读 …》, figure 「一句话里的注意力」) -------------------
+
+def pin_worked_example_scores(so):
+    """Printed scores q·k/√2 (two decimals) of the seven keys."""
+    g, q, K = _worked_example()
+    s = so.scores(q[None, :], K, 1.0 / math.sqrt(2.0))[0]
+    for e, val in zip(g["keys"], s):
+        p = e["printed_score"]
+        assert abs(val - float(p)) <= _half_unit(p) + 1e-12, (e["token"], val, p)
+
+
+def pin_worked_example_weights(so):
+    """Printed weights (percent, two significant digits), through the full path.
+
+    V = identity makes the output row equal to the weight row exactly
+    (each output column j is w_j·1 plus zeros).  The scale is left to the
+    oracle's default, so this also pins 1/√d_k with d_k = 2.
+    """
+    g, q, K = _worked_example()
+    eye = np.eye(len(K))
+    out = so.attention(q[None, None, None, :], K[None, None], eye[None, None])[0, 0, 0]
+    for e, w in zip(g["keys"], out):
+        p = e["printed_weight_percent"]
+        assert abs(100.0 * w - float(p)) <= _half_unit(p) + 1e-9, (e["token"], 100 * w, p)
+    assert abs(out.sum() - 1.0) < 1e-15
+    # the largest weight sits on 猫 = [2, 0.4] and is about two thirds
+    assert int(np.argmax(out)) == 1 and 0.65 < out[1] < 0.67
+
+
+def pin_worked_example_causal(so):
+    """Causal toggle: 它 is position 4 (0-based) of 7 and sees keys 0..4 only.
+
+    The page prints no numbers for this view; the pin is that the masked
+    softmax equals the unmasked weights of the visible keys renormalised,
+    with exactly zero weight on the two later keys.
+    """
+    g, q, K = _worked_example()
+    i = g["query_position"]
+    Q = K.copy()
+    Q[i] = q  # self-attention over the 7 tokens; only row i is checked
+    eye = np.eye(len(K))
+    full = so.attention(Q[None, None], K[None, None], eye[None, None])[0, 0, i]
+    caus = so.attention(Q[None, None], K[None, None], eye[None, None], causal=True)[0, 0, i]
+    assert np.all(caus[i + 1:] == 0.0)
+    ref = full[: i + 1] / full[: i + 1].sum()
+    assert np.allclose(caus[: i + 1], ref, rtol=0, atol=1e-14), (caus, ref)
+
+
+# --- two-key saturation (《精读 …》, after footnote 4) ---------------------------
+
+def pin_two_key_saturation(so):
+    g = _load("two_key_saturation.json")
+    for case in g["cases"]:
+        s0, s1 = case["raw_scores"]
+        # q·k1 = s0, q·k2 = s1 with q = [1, 0], k1 = [s0, 0], k2 = [s1, 1]
+        q = np.array([[[[1.0, 0.0]]]])
+        k = np.array([[[[s0, 0.0], [s1, 1.0]]]])
+        v = np.eye(2)[None, None]
+        w = so.attention(q, k, v, scale=case["scale"])[0, 0, 0]
+        # closed form: softmax of two logits is the logistic function of their gap
+        x = case["scale"] * (s0 - s1)
+        assert abs(w[0] - 1.0 / (1.0 + math.exp(-x))) < 1e-15
+        for got, p in zip(w, case["printed_weights"]):
+            if p is not None:
+                assert abs(got - float(p)) <= _half_unit(p) + 1e-12, (got, p)
+        p1 = w[0] * (1.0 - w[0])
+        assert abs(p1 - float(case["printed_p1mp"])) <= _half_unit(case["printed_p1mp"]) + 1e-12
+
+
+# --- invariants and special cases of Eq. (1) -----------------------------------
+
+def _rand(rng, *shape):
+    return rng.standard_normal(shape)
+
+
+def pin_rows_sum_and_exact_zeros(so):
+    """Rows of weights sum to 1; illegal positions get weight exactly +0.0."""
+    rng = np.random.default_rng(7)
+    B, h, n, d = 3, 2, 9, 5
+    m = n
+    q, k = _rand(rng, B, h, n, d), _rand(rng, B, h, m, d)
+    v = np.broadcast_to(np.eye(m), (B, h, m, m)).copy()
+    key_lens = np.array([4, 9, 0], dtype=np.int32)
+    for causal in (False, True):
+        w = so.attention(q, k, v, causal=causal, key_lens=key_lens)
+        for b in range(B):
+            L = key_lens[b]
+            for i in range(n):
+                vis = np.array([(j < L) and (not causal or j <= i) for j in range(m)])
+                row = w[b, :, i]
+                assert np.all(row[:, ~vis] == 0.0) and not np.signbit(row[:, ~vis]).any()
+                if vis.any():
+                    assert np.allclose(row.sum(-1), 1.0, rtol=0, atol=1e-14)
+                    assert np.all(row[:, vis] > 0.0)
+                else:
+                    assert np.all(row == 0.0)
+
+
+def pin_zero_query_gives_mean(so):
+    """Q = 0 ⇒ every legal score is 0 ⇒ the output is the mean of the legal V rows."""
+    rng = np.random.default_rng(11)
+    B, h, n, m, d, dv = 2, 3, 6, 6, 4, 5
+    q = np.zeros((B, h, n, d))
+    k, v = _rand(rng, B, h, m, d), _rand(rng, B, h, m, dv)
+    key_lens = np.array([3, 6])
+    for causal in (False, True):
+        o = so.attention(q, k, v, causal=causal, key_lens=key_lens)
+        for b in range(B):
+            for i in range(n):
+                hi = key_lens[b] if not causal else min(key_lens[b], i + 1)
+                ref = v[b, :, :hi].mean(axis=1)
+                assert np.allclose(o[b, :, i], ref, rtol=0, atol=1e-14)
+
+
+def pin_single_visible_key(so):
+    """One legal key ⇒ weight exactly 1 ⇒ output equals that value row bitwise."""
+    rng = np.random.default_rng(13)
+    q, k, v = _rand(rng, 2, 2, 5, 3), _rand(rng, 2, 2, 5, 3), _rand(rng, 2, 2, 5, 4)
+    o = so.attention(q, k, v, key_lens=np.array([1, 1]))
+    assert np.array_equal(o, np.broadcast_to(v[:, :, :1], o.shape))
+    o = so.attention(q, k, v, causal=True)
+    assert np.array_equal(o[:, :, 0], v[:, :, 0])
+
+
+def pin_permutation_equivariance(so):
+    """Permuting (K, V) rows jointly leaves O unchanged; permuting Q permutes O."""
+    rng = np.random.default_rng(17)
+    B, h, n, m, d, dv = 2, 2, 5, 7, 3, 4
+    q, k, v = _rand(rng, B, h, n, d), _rand(rng, B, h, m, d), _rand(rng, B, h, m, dv)
+    key_lens = np.array([5, 7])
+    o = so.attention(q, k, v, key_lens=key_lens)
+    # permute keys inside the legal prefix of every batch element
+    k2, v2 = k.copy(), v.copy()
+    for b in range(B):
+        p = rng.permutation(key_lens[b])
+        k2[b][:, : key_lens[b]] = k[b][:, p]
+        v2[b][:, : key_lens[b]] = v[b][:, p]
+    assert np.allclose(so.attention(q, k2, v2, key_lens=key_lens), o, rtol=0, atol=1e-13)
+    p = rng.permutation(n)
+    assert np.allclose(so.attention(q[:, :, p], k, v, key_lens=key_lens), o[:, :, p], rtol=0, atol=1e-13)
+
+
+def pin_shift_invariance(so):
+    """K + 1wᵀ shifts each row's logits by a constant ⇒ O unchanged; V + 1cᵀ ⇒ O + cᵀ."""
+    rng = np.random.default_rng(19)
+    B, h, n, m, d, dv = 1, 2, 6, 6, 3, 3
+    q, k, v = _rand(rng, B, h, n, d), _rand(rng, B, h, m, d), _rand(rng, B, h, m, dv)
+    w = rng.standard_normal(d)
+    c = rng.standard_normal(dv)
+    for causal in (False, True):
+        o = so.attention(q, k, v, causal=causal)
+        assert np.allclose(so.attention(q, k + w, v, causal=causal), o, rtol=0, atol=1e-12)
+        assert np.allclose(so.attention(q, k, v + c, causal=causal), o + c, rtol=0, atol=1e-12)
+
+
+def pin_hard_limit(so):
+    """Large scale with distinct scores ⇒ the softmax picks the arg-max key."""
+    rng = np.random.default_rng(23)
+    q, k, v = _rand(rng, 1, 1, 4, 3), _rand(rng, 1, 1, 6, 3), _rand(rng, 1, 1, 6, 2)
+    o = so.attention(q, k, v, scale=1e4)
+    best = np.argmax(q[0, 0] @ k[0, 0].T, axis=1)
+    assert np.allclose(o[0, 0], v[0, 0, best], rtol=0, atol=1e-9)
+
+
+def pin_cross_attention_shapes(so):
+    """n ≠ m (encoder–decoder attention) and the multi-head shape walk.
+
+    《精读 …》's ten-token walk: per head 10×64 queries, a 10×10 weight matrix,
+    a 10×64 output; eight heads concatenate back to 10×512.
+    """
+    rng = np.random.default_rng(29)
+    q, k, v = _rand(rng, 1, 8, 10, 64), _rand(rng, 1, 8, 10, 64), _rand(rng, 1, 8, 10, 64)
+    o = so.attention(q, k, v)
+    assert o.shape == (1, 8, 10, 64)
+    assert o[0].transpose(1, 0, 2).reshape(10, 512).shape == (10, 512)
+    q2 = _rand(rng, 2, 3, 4, 5)
+    k2, v2 = _rand(rng, 2, 3, 7, 5), _rand(rng, 2, 3, 7, 6)
+    assert so.attention(q2, k2, v2).shape == (2, 3, 4, 6)
+
+
+def pin_brute_force_mp(so):
+    """50-digit scalar-loop evaluation on tiny shapes, every mask kind."""
+    from oracle.brute_mp import attention_mp
+
+    rng = np.random.default_rng(31)
+    shapes = [(2, 3, 4, 4, 3, 2), (2, 2, 3, 5, 2, 3), (1, 2, 5, 5, 4, 4)]
+    for (B, h, n, m, d, dv) in shapes:
+        q, k, v = _rand(rng, B, h, n, d), _rand(rng, B, h, m, d), _rand(rng, B, h, m, dv)
+        kls = [None, rng.integers(0, m + 2, size=B)]
+        for key_lens in kls:
+            for causal in ([False, True] if n == m else [False]):
+                scale = 0.7
+                o = so.attention(q, k, v, scale=scale, causal=causal, key_lens=key_lens)
+                ref = attention_mp(q.tolist(), k.tolist(), v.tolist(), scale, causal,
+                                   None if key_lens is None else key_lens.tolist())
+                ref = np.array([[[[float(x) for x in r] for r in hd] for hd in bb] for bb in ref])
+                assert np.allclose(o, ref, rtol=0, atol=1e-13), (B, h, n, m, causal, key_lens)
+
+
+ALL_PINS = [
+    pin_worked_example_scores,
+    pin_worked_example_weights,
+    pin_worked_example_causal,
+    pin_two_key_saturation,
+    pin_rows_sum_and_exact_zeros,
+    pin_zero_query_gives_mean,
+    pin_single_visible_key,
+    pin_permutation_equivariance,
+    pin_shift_invariance,
+    pin_hard_limit,
+    pin_cross_attention_shapes,
+    pin_brute_force_mp,
+]

@@ -1,0 +1,130 @@
+"""Plant one plausible mistake in the oracle at a time; some pin must catch it.
+
+The mistakes are planted in the CPU oracle only (never in the GPU path), by
+replacing one step function of ``oracle.sdpa_oracle`` for the duration of a
+test.  Each mutant below is a mistake a careful reader could make when writing
+Eq. (1) out: a dropped or wrong scale, a transposed operand, a strict instead
+of inclusive causal mask, an off-by-one or misplaced key-padding mask, a finite
+stand-in for −∞, a softmax over the wrong axis or without its normaliser, or a
+key length taken from the wrong index.
+"""
+
+import numpy as np
+import pytest
+
+import oracle.sdpa_oracle as so
+from tests.oracle_pins import ALL_PINS
+
+_orig_visible = so.visible_keys
+
+
+def _vis_strict_causal(query_pos, m, causal, key_len):
+    vis = _orig_visible(query_pos, m, False, key_len)
+    if causal:
+        vis &= np.arange(m)[None, :] < np.asarray(query_pos)[:, None]
+    return vis
+
+
+def _vis_pad_off_by_one(query_pos, m, causal, key_len):
+    return _orig_visible(query_pos, m, causal, None if key_len is None else key_len + 1)
+
+
+def _vis_ignore_padding(query_pos, m, causal, key_len):
+    return _orig_visible(query_pos, m, causal, None)
+
+
+def _vis_pad_on_queries(query_pos, m, causal, key_len):
+    vis = _orig_visible(query_pos, m, causal, None)
+    if key_len is not None:
+        vis &= (np.asarray(query_pos) < key_len)[:, None]
+    return vis
+
+
+def _mask_finite(s, vis):
+    out = s.copy()
+    out[~vis] = -1e9
+    return out
+
+
+def _softmax_cols(s):
+    t = np.where(np.isfinite(s), s, -np.inf)
+    mx = np.max(np.where(np.isfinite(t), t, -1e300), axis=0, keepdims=True)
+    e = np.exp(t - mx)
+    den = e.sum(axis=0, keepdims=True)
+    return np.divide(e, den, out=np.zeros_like(e), where=den > 0)
+
+
+def _softmax_unnormalised(s):
+    out = np.zeros_like(s)
+    for i in range(s.shape[0]):
+        if np.isfinite(s[i]).any():
+            out[i] = np.exp(s[i] - s[i][np.isfinite(s[i])].max())
+    return out
+
+
+def _softmax_no_max_guard_uniform(s):
+    # fully masked rows become uniform instead of zero (a −1e9-style fill)
+    w = so_row_softmax_orig(s)
+    for i in range(s.shape[0]):
+        if not np.isfinite(s[i]).any():
+            w[i] = 1.0 / s.shape[1]
+    return w
+
+
+so_row_softmax_orig = so.row_softmax
+
+
+MUTANTS = {
+    "scale_dropped": ("scores", lambda q, k, scale: q @ k.T),
+    "scale_squared": ("scores", lambda q, k, scale: scale * scale * (q @ k.T)),
+    "scores_transposed": ("scores", lambda q, k, scale: (scale * (q @ k.T)).T),
+    "keys_as_queries": ("scores", lambda q, k, scale: scale * (k[: q.shape[0]] @ k.T)),
+    "causal_strict": ("visible_keys", _vis_strict_causal),
+    "padding_off_by_one": ("visible_keys", _vis_pad_off_by_one),
+    "padding_ignored": ("visible_keys", _vis_ignore_padding),
+    "padding_on_queries": ("visible_keys", _vis_pad_on_queries),
+    "mask_finite_fill": ("apply_mask", _mask_finite),
+    "mask_skipped": ("apply_mask", lambda s, vis: s.copy()),
+    "softmax_over_columns": ("row_softmax", _softmax_cols),
+    "softmax_unnormalised": ("row_softmax", _softmax_unnormalised),
+    "masked_row_uniform": ("row_softmax", _softmax_no_max_guard_uniform),
+    # only expressible when the weight matrix is square (n == m)
+    "weights_transposed": ("weighted_values", lambda w, v: w.T @ v if w.shape[0] == w.shape[1] else w @ v),
+    "values_dropped_last": ("weighted_values", lambda w, v: w[:, :-1] @ v[:-1]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_some_pin_catches_mutant(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(so, attr, fn)
+    caught = []
+    for pin in ALL_PINS:
+        try:
+            pin(so)
+        except Exception as e:  # an assertion or a shape error both count
+            caught.append((pin.__name__, type(e).__name__))
+    assert caught, f"no pin detects mutant {name}"
+
+
+def test_key_length_taken_from_head_index(monkeypatch):
+    """A key length looked up by head instead of batch element must be caught."""
+    def attention_wrong(q, k, v, scale=None, causal=False, key_lens=None):
+        B, h, n, d_k = q.shape
+        if scale is None:
+            scale = so.default_scale(d_k)
+        out = np.empty((B, h, n, v.shape[3]))
+        for b in range(B):
+            for hh in range(h):
+                L = None if key_lens is None else int(key_lens[min(hh, len(key_lens) - 1)])
+                out[b, hh] = so.attention_head(q[b, hh], k[b, hh], v[b, hh], scale, causal, L)
+        return out
+
+    monkeypatch.setattr(so, "attention", attention_wrong)
+    caught = []
+    for pin in ALL_PINS:
+        try:
+            pin(so)
+        except Exception:
+            caught.append(pin.__name__)
+    assert caught

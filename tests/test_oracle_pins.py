@@ -1,0 +1,11 @@
+"""The oracle against what the pages and mathematics fix (CPU only)."""
+
+import pytest
+
+import oracle.sdpa_oracle as so
+from tests.oracle_pins import ALL_PINS
+
+
+@pytest.mark.parametrize("pin", ALL_PINS, ids=[p.__name__ for p in ALL_PINS])
+def test_pin(pin):
+    pin(so)
