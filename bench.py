@@ -1,0 +1,279 @@
+#!/usr/bin/env python3
+"""Throughput of the fused attention forward on one MI355X (gfx950).
+
+A "step" is one sdpa_forward over one batch of the workload (every step of the
+path: staging, scores, masking, online softmax, weighted sum, store).  Inputs
+are seeded synthetic N(0,1) tensors already resident in HBM; the timed steps
+rotate over enough copies of the batch (> 2× the 256 MB Infinity Cache) that
+the data really streams from HBM.  The K timed steps are captured in one HIP
+graph (the launches are a few microseconds each, below Python's call rate) and
+timed with HIP events on the stream they run on.
+
+Prints ONE JSON line.  Default workload: the base-model encoder self-attention
+batch (B=64, h=8, n=m=64, d_k=d_v=64, bf16, key padding U[8,64]).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--dtype bf16|f32]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from sdpa_inputs import WORKLOADS, make_inputs  # noqa: E402
+
+# MI355X published peaks (dense, no sparsity).
+PEAK_HBM_GBS = 8000.0
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
+INFINITY_CACHE_BYTES = 256 << 20
+
+CSRC = os.path.join(ROOT, "transformer_attention_sdpa_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+HEADLINE = ("encoder_self_base", "bf16")
+EXTRA = [("single_head_16", "f32"), ("encoder_self_base", "f32"), ("decoder_causal_base", "bf16"),
+         ("cross_big", "bf16"), ("long_causal_8k", "bf16")]
+
+
+def algorithmic_work(wl, dtype, key_lens):
+    """FLOPs and HBM bytes one step must move, counting legal (query, key) pairs only.
+
+    FLOPs: 2·d_k per score plus 2·d_v per weighted value, i.e. 4·d per legal
+    pair (4·n·m·d per head when nothing is masked).  Bytes: Q and O in full,
+    plus the K and V rows below each sequence's key length (padded rows are
+    never read).
+    """
+    esz = 2 if dtype == "bf16" else 4
+    pairs = 0
+    kv_rows = 0
+    for b in range(wl.B):
+        L = wl.m if key_lens is None else min(max(int(key_lens[b]), 0), wl.m)
+        if wl.causal:
+            # query i sees min(i + 1, L) keys
+            k = min(L, wl.n)
+            p = k * (k + 1) // 2 + (wl.n - k) * L
+        else:
+            p = wl.n * L
+        pairs += wl.h * p
+        kv_rows += wl.h * L
+    flops = 2 * (wl.d_k + wl.d_v) * pairs
+    nbytes = esz * (wl.B * wl.h * wl.n * (wl.d_k + wl.d_v) + kv_rows * (wl.d_k + wl.d_v))
+    dense_flops = 2 * (wl.d_k + wl.d_v) * wl.B * wl.h * wl.n * wl.m
+    return flops, nbytes, dense_flops
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".hpp", ".cpp", ".h")):
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, dtype):
+    """Per-launch HBM bytes from committed rocprofv3 counter runs, if still current."""
+    path = os.path.join(PROFILES, f"traffic_{workload}_{dtype}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path, encoding="utf-8") as f:
+        t = json.load(f)
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None  # the kernel changed since the counters were taken
+    return t.get("bytes_per_launch")
+
+
+def time_workload(name, dtype, steps, warmup):
+    import torch
+
+    from transformer_attention_sdpa_amd import _lib
+
+    _lib.load()
+    wl = WORKLOADS[name]
+    case = make_inputs(wl, dtype)
+    dev = torch.device("cuda:0")
+    if dtype == "bf16":
+        from sdpa_inputs import bf16_bits
+        import numpy as np
+
+        def up(x):
+            return torch.from_numpy(bf16_bits(x).view(np.int16)).to(dev).view(torch.bfloat16)
+        tdt, code = torch.bfloat16, _lib.SDPA_BF16
+    else:
+        def up(x):
+            return torch.from_numpy(x).to(dev)
+        tdt, code = torch.float32, _lib.SDPA_F32
+    q0, k0, v0 = up(case["q"]), up(case["k"]), up(case["v"])
+    set_bytes = (q0.numel() + k0.numel() + v0.numel() + q0.numel()) * q0.element_size()
+    nsets = max(1, min(64, math.ceil(2 * INFINITY_CACHE_BYTES / set_bytes)))
+    sets = []
+    for _ in range(nsets):
+        q, k, v = q0.clone(), k0.clone(), v0.clone()
+        o = torch.empty((wl.B, wl.h, wl.n, wl.d_v), dtype=tdt, device=dev)
+        sets.append((q, k, v, o))
+    kl = None
+    kl_ptr = None
+    if case["key_lens"] is not None:
+        kl = torch.from_numpy(case["key_lens"]).to(dev)
+        kl_ptr = kl.data_ptr()
+    scale = 1.0 / math.sqrt(wl.d_k)
+    mask = _lib.SDPA_MASK_CAUSAL if wl.causal else _lib.SDPA_MASK_NONE
+    ptrs = [(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr()) for (q, k, v, o) in sets]
+
+    def launch(i, stream):
+        p = ptrs[i % nsets]
+        rc = _lib.sdpa_forward(p[0], p[1], p[2], p[3], wl.B, wl.h, wl.n, wl.m, wl.d_k, wl.d_v,
+                               scale, mask, kl_ptr, code, stream)
+        if rc != _lib.SDPA_OK:
+            raise RuntimeError(_lib.sdpa_strerror(rc))
+
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    for i in range(warmup):
+        launch(i, stream)
+    torch.cuda.synchronize()
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        cs = torch.cuda.current_stream(dev).cuda_stream
+        for i in range(steps):
+            launch(i, cs)
+    graph.replay()  # first replay uploads the graph; not timed
+    torch.cuda.synchronize()
+
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    e0.record()
+    graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    graph_ms = e0.elapsed_time(e1)
+
+    # Same steps launched one by one from Python (host launch rate included).
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(steps):
+        launch(i, stream)
+    e1.record()
+    torch.cuda.synchronize()
+    eager_ms = e0.elapsed_time(e1)
+
+    flops, nbytes, dense = algorithmic_work(wl, dtype, case["key_lens"])
+    t = graph_ms / 1e3 / steps
+    del graph, sets
+    torch.cuda.empty_cache()
+    return {
+        "workload": name, "dtype": dtype, "steps": steps, "sets_rotated": nsets,
+        "ms_per_step": graph_ms / steps, "ms_per_step_eager": eager_ms / steps,
+        "wall_s_timed": wall,
+        "alg_flops": flops, "dense_flops": dense, "alg_bytes": nbytes,
+        "tflops": flops / t / 1e12, "gbs": nbytes / t / 1e9,
+        "frac_mfma_peak": flops / t / 1e12 / PEAK_TFLOPS[dtype],
+        "frac_hbm_peak": nbytes / t / 1e9 / PEAK_HBM_GBS,
+    }
+
+
+def cpu_baseline(name, dtype, budget_s=10.0):
+    """The fp64 oracle, as it stands, on the host cores: whole batches until the budget."""
+    import oracle.sdpa_oracle as so
+    from threadpoolctl import threadpool_limits
+
+    wl = WORKLOADS[name]
+    case = make_inputs(wl, dtype)
+    flops, _, _ = algorithmic_work(wl, dtype, case["key_lens"])
+    reps = 0
+    with threadpool_limits(limits=1):  # 64×64 products stay on one BLAS thread anyway
+        t0 = time.perf_counter()
+        while True:
+            so.attention(case["q"], case["k"], case["v"], causal=wl.causal, key_lens=case["key_lens"])
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s:
+                break
+    per = el / reps
+    return {"value": flops / per / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"whole {name} batch ({wl.B * wl.h} heads, {dtype} values in fp64), "
+                      f"{reps} passes in {el:.1f} s, {per * 1e3:.1f} ms per pass"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default=HEADLINE[0], choices=sorted(WORKLOADS))
+    ap.add_argument("--dtype", default=HEADLINE[1], choices=["bf16", "f32"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: every (batch, head) pair is independent and this "
+              "build has no multi-GPU path; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    wl = WORKLOADS[args.workload]
+    head = time_workload(args.workload, args.dtype, args.steps, args.warmup)
+    extra = {}
+    if not args.no_extra:
+        for name, dt in EXTRA:
+            if (name, dt) == (args.workload, args.dtype):
+                continue
+            st = max(10, min(args.steps, 200)) if name != "long_causal_8k" else 20
+            r = time_workload(name, dt, st, min(args.warmup, 5))
+            extra[f"{name}-{dt}"] = {k: r[k] for k in (
+                "ms_per_step", "tflops", "gbs", "frac_mfma_peak", "frac_hbm_peak", "steps",
+                "sets_rotated", "ms_per_step_eager")}
+
+    bound = "mfma" if head["alg_flops"] / head["alg_bytes"] > PEAK_TFLOPS[args.dtype] * 1e12 / (PEAK_HBM_GBS * 1e9) else "hbm"
+    if bound == "hbm":
+        roof = {"bound": "hbm", "achieved": head["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": head["gbs"] / PEAK_HBM_GBS}
+    else:
+        roof = {"bound": "mfma", "achieved": head["tflops"], "peak": PEAK_TFLOPS[args.dtype],
+                "unit": "TFLOP/s", "frac": head["tflops"] / PEAK_TFLOPS[args.dtype]}
+    roof["traffic"] = measured_traffic(args.workload, args.dtype)
+
+    line = {
+        "metric": "attention TFLOP/s and % of MI355X bf16 MFMA / HBM peak, h=8 d_k=64",
+        "value": head["tflops"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": args.dtype,
+        "data": "synthetic N(0,1), seeded",
+        "config": {"workload": args.workload, "B": wl.B, "h": wl.h, "n": wl.n, "m": wl.m,
+                   "d_k": wl.d_k, "d_v": wl.d_v, "causal": wl.causal,
+                   "key_len_range": wl.key_len_range, "seed": wl.seed},
+        "roofline": roof,
+        "alg_bytes_per_step": head["alg_bytes"],
+        "alg_flops_per_step": head["alg_flops"],
+        "frac_hbm_peak": head["frac_hbm_peak"],
+        "frac_mfma_peak": head["frac_mfma_peak"],
+        "ms_per_step_eager": head["ms_per_step_eager"],
+        "sets_rotated": head["sets_rotated"],
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    if extra:
+        line["other_workloads"] = extra
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(args.workload, args.dtype)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,99 @@
+/*
+ * sdpa.h — C ABI of the MI355X (gfx950) scaled dot-product attention library.
+ *
+ * The operation is Eq. (1) of the page 《精读 Attention Is All You Need：原始
+ * Transformer 论文》 (section "缩放点积注意力：点积为什么要缩放"):
+ *
+ *     Attention(Q, K, V) = softmax(Q Kᵀ · scale) V,   scale = 1/√d_k by default,
+ *
+ * applied independently to each of B·h (batch, head) pairs, as the multi-head
+ * section of the same page runs h heads in parallel.  The three uses the pages
+ * list (《Attention Is All You Need：注意力就是你所需要的一切》 §3.2.3) are all
+ * this one call:
+ *   - encoder self-attention:            n == m, mask_kind = SDPA_MASK_NONE;
+ *   - decoder (masked) self-attention:   n == m, mask_kind = SDPA_MASK_CAUSAL
+ *                                        (query i sees keys j <= i, inclusive);
+ *   - encoder–decoder attention:         queries from the decoder (n), keys and
+ *                                        values from the encoder (m), n != m allowed.
+ * Illegal logits are set to −∞ before the softmax, so their weights are exactly
+ * zero (same §3.2.3).  A query row that has no legal key returns the zero vector.
+ *
+ * Names: n = number of queries, m = number of keys/values, as in the page
+ * 《企业官网建设流程全解析》 §2.2 (Q is n×d_k, K is m×d_k, V is m×d_v).
+ */
+#ifndef SDPA_H
+#define SDPA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Only the entry points below are exported from libsdpa.so. */
+#define SDPA_API __attribute__((visibility("default")))
+
+/* Status codes returned by every entry point.  No exception crosses the ABI. */
+#define SDPA_OK               0
+#define SDPA_ERR_NULL        -1 /* a required pointer is NULL                        */
+#define SDPA_ERR_SHAPE       -2 /* a dimension < 1, or an element count overflows   */
+#define SDPA_ERR_UNSUPPORTED -3 /* d_k / d_v not supported by this build (64 only)   */
+#define SDPA_ERR_ALIGN       -4 /* a pointer is not 16-byte aligned                  */
+#define SDPA_ERR_MASK        -5 /* unknown mask_kind, or causal with n != m          */
+#define SDPA_ERR_DTYPE       -6 /* unknown dtype                                     */
+#define SDPA_ERR_LAUNCH      -7 /* the HIP runtime refused the kernel launch         */
+#define SDPA_ERR_SCALE       -8 /* scale is not finite, or not > 0                   */
+#define SDPA_ERR_ALIAS       -9 /* out overlaps q, k or v                            */
+
+/* Element types (input and output share one type). */
+#define SDPA_F32  0 /* fp32 in, fp32 arithmetic, fp32 out                          */
+#define SDPA_BF16 1 /* bf16 in, fp32 accumulate and softmax, bf16 out (RNE)        */
+
+/* Mask kinds. */
+#define SDPA_MASK_NONE   0
+#define SDPA_MASK_CAUSAL 1 /* inclusive: query i sees keys j <= i; needs n == m    */
+
+/*
+ * sdpa_forward — one fused forward pass over all B·h heads.
+ *
+ * q        device pointer, [B, h, n, d_k], contiguous row-major, element type `dtype`.
+ * k        device pointer, [B, h, m, d_k], contiguous.
+ * v        device pointer, [B, h, m, d_v], contiguous.
+ * out      device pointer, [B, h, n, d_v], contiguous; written completely (rows
+ *          with no legal key are written as zeros).  Must not overlap q, k, v.
+ * B, h     batch size and number of heads (>= 1).
+ * n, m     number of queries and of keys/values per head (>= 1).
+ * d_k, d_v query/key and value widths; this build supports d_k == d_v == 64.
+ * scale    multiplier of the dot products; pass 1/sqrt(d_k) for Eq. (1).  Must
+ *          be finite and > 0 (scale = 1 runs the unscaled dot-product form).
+ * mask_kind SDPA_MASK_NONE or SDPA_MASK_CAUSAL.
+ * key_lens NULL for no key padding, else a DEVICE pointer to int32[B]: key j of
+ *          batch element b is legal only if j < clamp(key_lens[b], 0, m).  It
+ *          applies to every head of b and to keys only; query rows are never
+ *          masked.  Keys at j >= key_lens[b] are never read, so they may hold
+ *          anything (also NaN).  Causally hidden keys are read and must be finite.
+ * dtype    SDPA_F32 or SDPA_BF16.
+ * stream   a hipStream_t (as void*; NULL = the default stream).
+ *
+ * All device pointers must be 16-byte aligned.  The call is asynchronous on
+ * `stream`: it validates the arguments on the host (before any HIP call),
+ * enqueues one kernel, and returns.  It allocates nothing, keeps no pointer
+ * after returning, holds no mutable global state and is thread-safe.  The
+ * caller owns every buffer.  Returns SDPA_OK or a negative status.
+ */
+SDPA_API int sdpa_forward(const void* q, const void* k, const void* v, void* out,
+                 int32_t B, int32_t h, int32_t n, int32_t m, int32_t d_k, int32_t d_v,
+                 float scale, int32_t mask_kind, const int32_t* key_lens,
+                 int32_t dtype, void* stream);
+
+/* Static text for a status code (never NULL). */
+SDPA_API const char* sdpa_strerror(int status);
+
+/* Library version: major*10000 + minor*100 + patch. */
+SDPA_API int sdpa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SDPA_H */

@@ -1,0 +1,96 @@
+"""The C ABI without a GPU: exports, constants and host-side validation.
+
+Every call here fails validation, which happens on the host before any HIP
+call, so nothing touches a device.
+"""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from transformer_attention_sdpa_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "sdpa.h")
+
+
+def _header():
+    with open(HEADER, encoding="utf-8") as f:
+        return f.read()
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_every_declared_entry_point_is_exported(lib):
+    names = re.findall(r"SDPA_API\s+[\w\s\*]+?\b(sdpa_\w+)\s*\(", _header())
+    assert set(names) == {"sdpa_forward", "sdpa_strerror", "sdpa_version"}
+    for name in names:
+        assert isinstance(getattr(lib, name), ctypes._CFuncPtr)
+
+
+def test_header_constants_match_binding():
+    defs = dict(re.findall(r"#define\s+(SDPA_[A-Z0-9_]+)\s+(-?\d+)", _header()))
+    assert defs, "no constants parsed"
+    for name, val in defs.items():
+        assert getattr(_lib, name) == int(val), name
+
+
+def test_version_and_strerror(lib):
+    assert _lib.sdpa_version() >= 10000
+    for code in range(-9, 1):
+        msg = _lib.sdpa_strerror(code)
+        assert msg and msg != "unknown status"
+    assert _lib.sdpa_strerror(-1234) == "unknown status"
+
+
+P = 1 << 20  # fake, 16-byte aligned "device" addresses; never dereferenced
+
+
+def call(q=P, k=2 * P, v=3 * P, out=4 * P, B=2, h=2, n=8, m=8, d_k=64, d_v=64, scale=0.125,
+         mask=0, key_lens=None, dtype=1):
+    return _lib.sdpa_forward(q, k, v, out, B, h, n, m, d_k, d_v, scale, mask, key_lens, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), _lib.SDPA_ERR_NULL),
+    (dict(k=None), _lib.SDPA_ERR_NULL),
+    (dict(v=None), _lib.SDPA_ERR_NULL),
+    (dict(out=None), _lib.SDPA_ERR_NULL),
+    (dict(B=0), _lib.SDPA_ERR_SHAPE),
+    (dict(h=-1), _lib.SDPA_ERR_SHAPE),
+    (dict(n=0), _lib.SDPA_ERR_SHAPE),
+    (dict(m=0), _lib.SDPA_ERR_SHAPE),
+    (dict(B=1 << 20, h=1 << 10, n=1 << 20), _lib.SDPA_ERR_SHAPE),
+    (dict(d_k=32, d_v=32), _lib.SDPA_ERR_UNSUPPORTED),
+    (dict(d_v=128), _lib.SDPA_ERR_UNSUPPORTED),
+    (dict(q=P + 8), _lib.SDPA_ERR_ALIGN),
+    (dict(out=4 * P + 2), _lib.SDPA_ERR_ALIGN),
+    (dict(key_lens=5 * P + 2), _lib.SDPA_ERR_ALIGN),
+    (dict(mask=2), _lib.SDPA_ERR_MASK),
+    (dict(mask=1, n=8, m=9), _lib.SDPA_ERR_MASK),
+    (dict(dtype=2), _lib.SDPA_ERR_DTYPE),
+    (dict(dtype=-1), _lib.SDPA_ERR_DTYPE),
+    (dict(scale=math.nan), _lib.SDPA_ERR_SCALE),
+    (dict(scale=math.inf), _lib.SDPA_ERR_SCALE),
+    (dict(scale=0.0), _lib.SDPA_ERR_SCALE),
+    (dict(scale=-0.125), _lib.SDPA_ERR_SCALE),
+    (dict(out=P), _lib.SDPA_ERR_ALIAS),
+    (dict(out=3 * P + 1024), _lib.SDPA_ERR_ALIAS),
+])
+def test_validation_rejects_before_any_hip_call(kw, code):
+    assert call(**kw) == code
+
+
+def test_torch_wrapper_rejects_cpu_tensors():
+    import torch
+
+    from transformer_attention_sdpa_amd import forward
+
+    x = torch.zeros(1, 1, 4, 64)
+    with pytest.raises(ValueError):
+        forward(x, x, x)

@@ -1,0 +1,68 @@
+"""MI355X-native fused scaled dot-product attention (gfx950 HIP kernels).
+
+``forward(q, k, v, *, causal=False, key_lens=None, scale=None, out=None)``
+computes Eq. (1) of the pages, softmax(Q Kᵀ/√d_k) V, per (batch, head) on
+[B, h, len, 64] tensors of dtype float32 or bfloat16 that live on the GPU.
+PyTorch only supplies the device memory and the current stream; the work is
+one launch of the HIP library ``libsdpa.so`` through its C ABI.
+"""
+
+from __future__ import annotations
+
+import math
+
+from . import _lib
+from ._lib import sdpa_forward, sdpa_strerror, sdpa_version  # noqa: F401
+
+__all__ = ["forward", "sdpa_forward", "sdpa_strerror", "sdpa_version"]
+
+
+def forward(q, k, v, *, causal: bool = False, key_lens=None, scale: float | None = None,
+            out=None):
+    """Attention over [B, h, n, d_k] queries and [B, h, m, d] keys/values.
+
+    key_lens: None or an int32 tensor [B] on the same device (key j of batch
+    element b is legal iff j < key_lens[b]).  Returns ``out`` ([B, h, n, d_v],
+    same dtype as q).  Raises RuntimeError with the library's message on a
+    nonzero status.
+    """
+    import torch
+
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [B, h, len, d]")
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("q, k, v must be GPU tensors")
+    if q.dtype != k.dtype or q.dtype != v.dtype:
+        raise ValueError("q, k, v must share one dtype")
+    if q.dtype == torch.float32:
+        dt = _lib.SDPA_F32
+    elif q.dtype == torch.bfloat16:
+        dt = _lib.SDPA_BF16
+    else:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    for t in (q, k, v):
+        if not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous")
+    B, h, n, d_k = q.shape
+    m, d_v = k.shape[2], v.shape[3]
+    if tuple(k.shape) != (B, h, m, d_k) or tuple(v.shape) != (B, h, m, d_v):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
+    kl_ptr = None
+    if key_lens is not None:
+        if key_lens.dtype != torch.int32 or key_lens.device != q.device or key_lens.numel() != B:
+            raise ValueError("key_lens must be an int32 tensor of B elements on q's device")
+        key_lens = key_lens.contiguous()
+        kl_ptr = key_lens.data_ptr()
+    if out is None:
+        out = torch.empty((B, h, n, d_v), dtype=q.dtype, device=q.device)
+    elif tuple(out.shape) != (B, h, n, d_v) or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B, h, n, d_v] tensor of q's dtype")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d_k)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    rc = sdpa_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, h, n, m,
+                      d_k, d_v, float(scale), _lib.SDPA_MASK_CAUSAL if causal else _lib.SDPA_MASK_NONE,
+                      kl_ptr, dt, stream)
+    if rc != _lib.SDPA_OK:
+        raise RuntimeError(f"sdpa_forward failed ({rc}): {sdpa_strerror(rc)}")
+    return out

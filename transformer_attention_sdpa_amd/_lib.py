@@ -1,0 +1,69 @@
+"""ctypes binding of libsdpa.so — argument marshalling only.
+
+Every function here has the name of the C entry point it forwards to (see
+include/sdpa.h); all arithmetic runs in the HIP kernels behind the C ABI.  The
+library is looked up next to this file (built in-tree by ``build_lib``); if it
+is missing, ``load()`` raises — there is no fallback of any kind.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsdpa.so")
+
+# Mirrors of the #defines in include/sdpa.h (a CPU test checks they agree).
+SDPA_OK = 0
+SDPA_ERR_NULL = -1
+SDPA_ERR_SHAPE = -2
+SDPA_ERR_UNSUPPORTED = -3
+SDPA_ERR_ALIGN = -4
+SDPA_ERR_MASK = -5
+SDPA_ERR_DTYPE = -6
+SDPA_ERR_LAUNCH = -7
+SDPA_ERR_SCALE = -8
+SDPA_ERR_ALIAS = -9
+SDPA_F32 = 0
+SDPA_BF16 = 1
+SDPA_MASK_NONE = 0
+SDPA_MASK_CAUSAL = 1
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libsdpa.so once and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python -m transformer_attention_sdpa_amd.build_lib` "
+            "(the attention path has no non-HIP fallback)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32 = ctypes.c_void_p, ctypes.c_int32
+    lib.sdpa_forward.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                 ctypes.c_float, i32, vp, i32, vp]
+    lib.sdpa_forward.restype = ctypes.c_int
+    lib.sdpa_strerror.argtypes = [ctypes.c_int]
+    lib.sdpa_strerror.restype = ctypes.c_char_p
+    lib.sdpa_version.argtypes = []
+    lib.sdpa_version.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def sdpa_forward(q, k, v, out, B, h, n, m, d_k, d_v, scale, mask_kind, key_lens, dtype,
+                 stream) -> int:
+    """Forward to the C entry point; pointers and the stream are plain integers (or None)."""
+    return load().sdpa_forward(q, k, v, out, B, h, n, m, d_k, d_v, scale, mask_kind,
+                               key_lens, dtype, stream)
+
+
+def sdpa_strerror(status: int) -> str:
+    return load().sdpa_strerror(status).decode()
+
+
+def sdpa_version() -> int:
+    return load().sdpa_version()

@@ -1,0 +1,82 @@
+// C ABI of the attention library: argument validation on the host (before any
+// HIP call), then one kernel launch on the caller's stream.  See include/sdpa.h
+// for the contract of each entry point.
+#include "sdpa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "sdpa_common.hpp"
+
+namespace {
+
+constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// [lo, lo + bytes) and [lo2, lo2 + bytes2) share a byte.
+bool overlap(const void* a, uint64_t na, const void* b, uint64_t nb) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+}
+
+int validate(const void* q, const void* k, const void* v, void* out, int32_t B, int32_t h,
+             int32_t n, int32_t m, int32_t d_k, int32_t d_v, float scale, int32_t mask_kind,
+             const int32_t* key_lens, int32_t dtype) {
+    if (!q || !k || !v || !out) return SDPA_ERR_NULL;
+    if (dtype != SDPA_F32 && dtype != SDPA_BF16) return SDPA_ERR_DTYPE;
+    if (B < 1 || h < 1 || n < 1 || m < 1 || d_k < 1 || d_v < 1) return SDPA_ERR_SHAPE;
+    // Element counts and the launch grid must stay well inside 64-bit offsets and
+    // a 31-bit grid: B·h·max(n, m)·max(d) < 2^48 and B·h·⌈n/32⌉ < 2^31.
+    const uint64_t heads = (uint64_t)B * (uint64_t)h;
+    const uint64_t rows = (uint64_t)(n > m ? n : m);
+    const uint64_t width = (uint64_t)(d_k > d_v ? d_k : d_v);
+    if (heads * rows * width >= (1ull << 48)) return SDPA_ERR_SHAPE;
+    if (heads * (((uint64_t)n + 31) / 32) >= (1ull << 31)) return SDPA_ERR_SHAPE;
+    if (d_k != sdpa::kHeadDim || d_v != sdpa::kHeadDim) return SDPA_ERR_UNSUPPORTED;
+    if (mask_kind != SDPA_MASK_NONE && mask_kind != SDPA_MASK_CAUSAL) return SDPA_ERR_MASK;
+    if (mask_kind == SDPA_MASK_CAUSAL && n != m) return SDPA_ERR_MASK;
+    if (!std::isfinite(scale) || !(scale > 0.f)) return SDPA_ERR_SCALE;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return SDPA_ERR_ALIGN;
+    if (key_lens && (reinterpret_cast<uintptr_t>(key_lens) & 3u)) return SDPA_ERR_ALIGN;
+    const uint64_t esz = dtype == SDPA_F32 ? 4 : 2;
+    const uint64_t qb = heads * n * d_k * esz, kb = heads * m * d_k * esz;
+    const uint64_t vb = heads * m * d_v * esz, ob = heads * n * d_v * esz;
+    if (overlap(out, ob, q, qb) || overlap(out, ob, k, kb) || overlap(out, ob, v, vb))
+        return SDPA_ERR_ALIAS;
+    return SDPA_OK;
+}
+
+}  // namespace
+
+extern "C" int sdpa_forward(const void* q, const void* k, const void* v, void* out, int32_t B,
+                            int32_t h, int32_t n, int32_t m, int32_t d_k, int32_t d_v, float scale,
+                            int32_t mask_kind, const int32_t* key_lens, int32_t dtype,
+                            void* stream) {
+    const int st = validate(q, k, v, out, B, h, n, m, d_k, d_v, scale, mask_kind, key_lens, dtype);
+    if (st != SDPA_OK) return st;
+    sdpa::Args a{q, k, v, out, B, h, n, m, scale, mask_kind == SDPA_MASK_CAUSAL ? 1 : 0, key_lens};
+    const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const hipError_t e = dtype == SDPA_BF16 ? sdpa::launch_bf16(a, s) : sdpa::launch_f32(a, s);
+    return e == hipSuccess ? SDPA_OK : SDPA_ERR_LAUNCH;
+}
+
+extern "C" const char* sdpa_strerror(int status) {
+    switch (status) {
+        case SDPA_OK: return "ok";
+        case SDPA_ERR_NULL: return "a required pointer is NULL";
+        case SDPA_ERR_SHAPE: return "bad shape: a dimension is < 1 or an element count overflows";
+        case SDPA_ERR_UNSUPPORTED: return "unsupported head width: this build supports d_k = d_v = 64";
+        case SDPA_ERR_ALIGN: return "a device pointer is not 16-byte aligned (key_lens: 4-byte)";
+        case SDPA_ERR_MASK: return "bad mask: unknown mask_kind, or causal with n != m";
+        case SDPA_ERR_DTYPE: return "unknown dtype (SDPA_F32 = 0, SDPA_BF16 = 1)";
+        case SDPA_ERR_LAUNCH: return "the HIP runtime refused the kernel launch";
+        case SDPA_ERR_SCALE: return "scale must be finite and > 0";
+        case SDPA_ERR_ALIAS: return "out overlaps q, k or v";
+        default: return "unknown status";
+    }
+}
+
+extern "C" int sdpa_version(void) { return kVersion; }

@@ -1,0 +1,221 @@
+// Fused single-pass attention forward for fp32 inputs on gfx950 (MI355X).
+//
+// Same computation as the bf16 kernel — Eq. (1) of 《精读 Attention Is All You
+// Need：原始 Transformer 论文》, softmax(Q Kᵀ·scale) V per (batch, head), with
+// illegal logits at −∞ (《Attention Is All You Need：注意力就是你所需要的一切》
+// §3.2.3) — but fp32 end to end: fp32 products on the matrix cores
+// (v_mfma_f32_32x32x2_f32), fp32 weights (no bf16 rounding anywhere), fp32
+// output.  gfx950 has no reduced-precision fp32 (xf32) MFMA, so nothing is
+// truncated.
+//
+// One wave owns 32 queries of one head; keys stream through LDS in tiles of 32
+// rows.  Products are computed transposed (Sᵀ = K·Qᵀ, Oᵀ += Vᵀ·Pᵀ) so each lane
+// holds one query's column, as in the bf16 kernel.  With one k value per lane
+// per MFMA, Vᵀ is read straight from the row-major V tile (no transpose read).
+#include "sdpa_common.hpp"
+
+namespace sdpa {
+namespace {
+
+constexpr int D = kHeadDim;  // 64
+constexpr int BN = 32;       // keys per LDS tile
+constexpr int QW = 32;       // queries per wave
+
+// 16-byte chunk c (0..15) of tile row r sits at chunk position c ^ (r & 15).
+__device__ __forceinline__ int swz16(int row, int chunk) { return row * 16 + (chunk ^ (row & 15)); }
+
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void sdpa_fwd_f32(
+    const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
+    float* __restrict__ O, int BH, int H, int n, int m, float c_log2, int causal,
+    const int32_t* __restrict__ key_lens, int nqb) {
+    constexpr int NT = NW * 64;
+    constexpr int CHUNKS = BN * D * 4 / 16;  // 512
+    constexpr int CPT = (CHUNKS + NT - 1) / NT;
+
+    __shared__ f32x4 sK[BN * 16];
+    __shared__ f32x4 sV[BN * 16];
+
+    const int tid = threadIdx.x;
+    const int w = tid >> 6;
+    const int lane = tid & 63;
+    const int l32 = lane & 31;
+    const int hf = lane >> 5;
+
+    const int g = blockIdx.x;
+    const int bh = g % BH;
+    const int qb = nqb - 1 - g / BH;
+    const int b = bh / H;
+    const int q0 = qb * (NW * QW);
+
+    int L = m;
+    if (key_lens) {
+        const int t = key_lens[b];
+        L = t < 0 ? 0 : (t > m ? m : t);
+    }
+    int kend = L;
+    if (causal) kend = min(kend, q0 + NW * QW);
+    const int ntiles = (kend + BN - 1) / BN;
+
+    const size_t qbase = (size_t)bh * n * D;
+    const size_t kvbase = (size_t)bh * m * D;
+
+    // Qᵀ operand: MFMA step ks contracts d = ks (half-wave 0) and d = 32 + ks
+    // (half-wave 1), so a lane keeps d = 32·hf + [0..31] of its query.
+    const int qrow = q0 + w * QW + l32;
+    float qop[32];
+    if (qrow < n) {
+        const f32x4* src = reinterpret_cast<const f32x4*>(Q + qbase + (size_t)qrow * D + 32 * hf);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const f32x4 x = src[c];
+            qop[4 * c + 0] = x[0]; qop[4 * c + 1] = x[1]; qop[4 * c + 2] = x[2]; qop[4 * c + 3] = x[3];
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) qop[i] = 0.f;
+    }
+
+    f32x4 rk[CPT], rv[CPT];
+    auto gload = [&](int t) {
+        const int k0 = t * BN;
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int c = tid + i * NT;
+            const int key = k0 + (c >> 4);
+            if (c < CHUNKS && key < L) {
+                rk[i] = reinterpret_cast<const f32x4*>(K + kvbase + (size_t)key * D)[c & 15];
+                rv[i] = reinterpret_cast<const f32x4*>(V + kvbase + (size_t)key * D)[c & 15];
+            } else {
+                rk[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+                rv[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+    };
+    auto swrite = [&]() {
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int c = tid + i * NT;
+            if (c < CHUNKS) {
+                const int idx = swz16(c >> 4, c & 15);
+                sK[idx] = rk[i];
+                sV[idx] = rv[i];
+            }
+        }
+    };
+
+    f32x16 oacc[2];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) { oacc[0][i] = 0.f; oacc[1][i] = 0.f; }
+    float mrun = -INFINITY;
+    float lrun = 0.f;
+
+    const int wq_lo = q0 + w * QW;
+    const int wq_hi = wq_lo + QW - 1;
+    const int my_q = wq_lo + l32;
+    const float* sVf = reinterpret_cast<const float*>(sV);
+
+    if (ntiles > 0) gload(0);
+    for (int t = 0; t < ntiles; ++t) {
+        __syncthreads();
+        swrite();
+        __syncthreads();
+        if (t + 1 < ntiles) gload(t + 1);
+
+        const int k0 = t * BN;
+        if (causal && k0 > wq_hi) continue;
+
+        // Sᵀ (32 keys × 32 queries) = K · Qᵀ, 32 steps of k = 2.
+        f32x16 s;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[i] = 0.f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const f32x4 a4 = sK[swz16(l32, 8 * hf + c)];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s = mfma32x32x2_f32(a4[e], qop[4 * c + e], s);
+        }
+
+        const bool need_mask = (k0 + BN > L) || (causal && k0 + BN - 1 > wq_lo);
+        if (need_mask) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int key = k0 + 8 * (i >> 2) + 4 * hf + (i & 3);
+                if (key >= L || (causal && key > my_q)) s[i] = -INFINITY;
+            }
+        }
+
+        float mt = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[i]);
+        mt = half_swap_max(mt);
+        const float mnew = fmaxf(mrun, mt);
+        const float muse = (mnew == -INFINITY) ? 0.f : mnew;
+        const float alpha = exp2_hw((mrun - muse) * c_log2);
+        mrun = mnew;
+        const float mc = muse * c_log2;
+        lrun *= alpha;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) { oacc[0][i] *= alpha; oacc[1][i] *= alpha; }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const float p = exp2_hw(__builtin_fmaf(s[i], c_log2, -mc));
+            s[i] = p;
+            lrun += p;
+        }
+
+        // Oᵀ += Vᵀ · Pᵀ: step i contracts, for half-wave hf, the key held in
+        // Sᵀ register i, i.e. tile row 8·(i/4) + 4·hf + i%4.
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int r = 8 * (i >> 2) + 4 * hf + (i & 3);
+#pragma unroll
+            for (int dt = 0; dt < 2; ++dt) {
+                const int dv = 32 * dt + l32;
+                const float a = sVf[swz16(r, dv >> 2) * 4 + (dv & 3)];
+                oacc[dt] = mfma32x32x2_f32(a, s[i], oacc[dt]);
+            }
+        }
+    }
+
+    const float ltot = half_swap_sum(lrun);
+    if (qrow < n) {
+        float* dst = O + qbase + (size_t)qrow * D;
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+                const int dv = 32 * dt + 8 * i4 + 4 * hf;
+                f32x4 o;
+                // true division keeps the fp32 path within a few ulp of the exact result
+                o[0] = ltot > 0.f ? oacc[dt][4 * i4 + 0] / ltot : 0.f;
+                o[1] = ltot > 0.f ? oacc[dt][4 * i4 + 1] / ltot : 0.f;
+                o[2] = ltot > 0.f ? oacc[dt][4 * i4 + 2] / ltot : 0.f;
+                o[3] = ltot > 0.f ? oacc[dt][4 * i4 + 3] / ltot : 0.f;
+                *reinterpret_cast<f32x4*>(dst + dv) = o;
+            }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_f32(const Args& a, hipStream_t stream) {
+    const int BH = a.B * a.H;
+    const float c_log2 = (float)((double)a.scale * 1.4426950408889634);
+    if (a.n <= 32) {
+        constexpr int NW = 1;
+        const int nqb = (a.n + NW * QW - 1) / (NW * QW);
+        hipLaunchKernelGGL(sdpa_fwd_f32<NW>, dim3(nqb * BH), dim3(NW * 64), 0, stream,
+                           (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.out,
+                           BH, a.H, a.n, a.m, c_log2, a.causal, a.key_lens, nqb);
+    } else {
+        constexpr int NW = 2;
+        const int nqb = (a.n + NW * QW - 1) / (NW * QW);
+        hipLaunchKernelGGL(sdpa_fwd_f32<NW>, dim3(nqb * BH), dim3(NW * 64), 0, stream,
+                           (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.out,
+                           BH, a.H, a.n, a.m, c_log2, a.causal, a.key_lens, nqb);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace sdpa
