@@ -182,6 +182,27 @@ def time_workload(name, dtype, steps, warmup):
     }
 
 
+def copy_reference(steps, warmup, nbytes=256 << 20):
+    """A plain device-to-device copy of known size: the yardstick that scales the
+    FETCH_SIZE / WRITE_SIZE counters of the attention kernel to bytes."""
+    import torch
+
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / 1e3 / steps
+    return {"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "steps": steps,
+            "ms_per_copy": t * 1e3, "gbs_read_plus_write": 2 * nbytes / t / 1e9}
+
+
 def cpu_baseline(name, dtype, budget_s=10.0):
     """The fp64 oracle, as it stands, on the host cores: whole batches until the budget."""
     import oracle.sdpa_oracle as so
@@ -214,12 +235,20 @@ def main():
     ap.add_argument("--dtype", default=HEADLINE[1], choices=["bf16", "f32"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="time a plain device copy instead (reference for HBM counters)")
+    ap.add_argument("--copy-mib", type=float, default=256.0, help="size of --calibrate-copy")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: every (batch, head) pair is independent and this "
               "build has no multi-GPU path; run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+
+    if args.calibrate_copy:
+        print(json.dumps(copy_reference(args.steps, args.warmup, int(args.copy_mib * (1 << 20)))),
+              flush=True)
+        return
 
     wl = WORKLOADS[args.workload]
     head = time_workload(args.workload, args.dtype, args.steps, args.warmup)

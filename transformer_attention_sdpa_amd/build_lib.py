@@ -21,12 +21,15 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsdpa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["sdpa_api.cpp", "sdpa_bf16.hip", "sdpa_f32.hip"]
+SOURCES = ["sdpa_api.cpp", "sdpa_bf16.hip", "sdpa_bf16_short.hip", "sdpa_f32.hip"]
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops.
+# -amdgpu-mfma-vgpr-form: MFMA accumulators in VGPRs, so the softmax reads
+#   the scores and rescales the output without AGPR copies.
 FLAGS = [
     "-x", "hip", "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-fvisibility=hidden", "-Wall", "-Wno-unused-function",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]

@@ -1,4 +1,5 @@
-// Fused single-pass attention forward for bf16 inputs on gfx950 (MI355X).
+// Fused single-pass attention forward for bf16 inputs on gfx950 (MI355X),
+// for any n and m (the long-sequence path; n, m <= 64 take the short kernel).
 //
 // Computes Eq. (1) of 《精读 Attention Is All You Need：原始 Transformer 论文》
 // ("缩放点积注意力：点积为什么要缩放"), softmax(Q Kᵀ·scale) V, for every
@@ -8,25 +9,36 @@
 // rounded to bf16 (RNE) for the P·V product, which accumulates in fp32; the
 // output is rounded once to bf16.
 //
-// Layout of the work.  One workgroup owns BM = NW·32 consecutive queries of one
-// head; each of its NW waves owns 32 of them.  The keys of the head stream
-// through LDS in tiles of 64 rows (K and V, 8 KiB each), and each wave keeps a
-// running maximum and sum per query (online softmax), so no n×m score matrix
-// ever exists.  Both products run on the matrix cores with
+// Work layout.  A workgroup owns BM = NW·64 consecutive queries of one head;
+// each wave owns 64 of them as two 32-query sub-blocks (QT = 2) that share
+// every K/V operand read from LDS.  Keys stream through LDS in tiles of 64 rows
+// (K and V, 8 KiB each), double-buffered, one barrier per tile.  Tiles move
+// HBM → LDS with buffer_load_dwordx4 … lds (no VGPR staging); the buffer range
+// ends at the sequence's key length, so rows past it arrive as zeros without
+// being read.  Each wave keeps a running reference maximum and sum per query
+// (online softmax), so no n×m score matrix ever exists.  Both products run on
 // v_mfma_f32_32x32x16_bf16, computed transposed:
 //
 //   Sᵀ (64 keys × 32 queries)  = K · Qᵀ          A = K rows from LDS, B = Qᵀ in VGPRs
 //   Oᵀ (64 dv  × 32 queries) += Vᵀ · Pᵀ          A = Vᵀ via LDS transpose reads,
 //                                                B = Pᵀ straight from the Sᵀ registers
 //
-// With the transposed form every lane holds one query's column, so the row
-// max/sum of the softmax are lane-local plus one exchange between the two
-// half-waves, and the per-query rescale of Oᵀ is a per-lane multiply.
+// so every lane holds one query's column: the row max/sum are lane-local plus
+// one exchange between half-waves, and the rescale of Oᵀ is a per-lane multiply.
 //
-// Causal blocks: a workgroup only visits key tiles up to its last query; a wave
-// skips tiles that lie entirely after its queries; masking code only runs on
-// tiles that straddle the diagonal or the padding edge.  Keys at or beyond the
-// padding length are never read from HBM (their LDS rows are zero-filled).
+// VALU economy (at d = 64 the softmax costs about as much issue time as the
+// matrix products):
+//   * the reference maximum only moves when a tile's maximum exceeds it by more
+//     than 2^TAU in weight, and the Oᵀ/l rescale is skipped unless some lane of
+//     the wave needs it — exact, because any common reference cancels in
+//     Σ p·v / Σ p; the weights are then bounded by 2^TAU;
+//   * one FMA + one v_exp_f32 per score (scale·log2 e folded into the FMA);
+//   * row sums with v_dot2_f32_bf16 on the packed bf16 weights (the same values
+//     that enter P·V);
+//   * masking (selects to −∞) only on tiles that straddle the causal diagonal or
+//     the padding edge; tiles entirely after a wave's queries are skipped;
+//   * LDS addresses are per-lane constants plus immediate offsets (the tile
+//     loop is unrolled by two so the buffer index is a constant).
 #include "sdpa_common.hpp"
 
 namespace sdpa {
@@ -34,230 +46,337 @@ namespace {
 
 constexpr int D = kHeadDim;  // 64
 constexpr int BN = 64;       // keys per LDS tile
-constexpr int QW = 32;       // queries per wave
+constexpr int QT = 2;        // 32-query sub-blocks per wave
+constexpr int QW = 32 * QT;  // queries per wave
+constexpr float TAU = 8.f;   // weights stay below 2^TAU between rescales
+constexpr int TILE_BYTES = BN * D * 2;  // 8 KiB
 
-// 16-byte chunk c (0..7) of tile row r sits at chunk position c ^ (r & 7):
-// rows that lanes read at the same column then fall in different banks.
-__device__ __forceinline__ int swz(int row, int chunk) { return row * 8 + (chunk ^ (row & 7)); }
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 template <int NW>
-__global__ __launch_bounds__(NW * 64) void sdpa_fwd_bf16(
+struct LongKernel {
+    static constexpr int NT = NW * 64;
+    static constexpr int BM = NW * QW;
+    static constexpr int LOADS = TILE_BYTES / 1024 / NW;  // 1 KiB loads per wave per tensor per tile
+
+    // LDS: [buf][K | V] tiles of 8 KiB; 16-byte chunk c of row r at lds_swz(r, c).
+    char* lds;
+    // Per-lane constants.
+    int lane, l32, hf, gi;
+    int kaddr[4];        // K operand byte offset for k-step ks (rows l32, chunk 2·ks + hf)
+    int vaddr[2][2];     // Vᵀ transpose-read byte offset for [dv tile dt][first/second 4 keys], k-step 0
+    int ld_voff[LOADS];  // global byte offset (within a tile) of this lane's loads
+    int ld_lds[LOADS];   // LDS byte offset (within a tile) of those loads (wave-uniform)
+    // Per-wave state.
+    bf16x8 qop[QT][4];
+    f32x16 oacc[QT][2];
+    float mref[QT], lsum[QT];
+    // Per-workgroup scalars.
+    const char* kg;
+    const char* vg;
+    int L, causal, wq0;
+    float c_log2;
+
+    __device__ void issue_tile_load(int t, int buf) {
+        const int k0 = t * BN;
+        const int left = (L - k0) * (D * 2);  // bytes of legal rows from k0 on (> 0 here)
+        const i32x4 rk = make_rsrc(kg + (size_t)k0 * D * 2, (uint32_t)left);
+        const i32x4 rv = make_rsrc(vg + (size_t)k0 * D * 2, (uint32_t)left);
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            load16_to_lds(rk, lds + buf * 2 * TILE_BYTES + ld_lds[i], ld_voff[i]);
+            load16_to_lds(rv, lds + buf * 2 * TILE_BYTES + TILE_BYTES + ld_lds[i], ld_voff[i]);
+        }
+    }
+
+    // −∞ on the illegal logits of sub-block qt (tiles on the causal diagonal or
+    // the padding edge).  Register i of sub-tile kt is key
+    // k0 + 32·kt + 8·(i/4) + 4·hf + i%4 of query wq0 + 32·qt + l32.
+    __device__ void mask_block(int qt, int k0, f32x16 (&s)[2]) {
+        const int qrow = wq0 + 32 * qt + l32;
+        const int lim = (causal ? min(L, qrow + 1) : L) - k0 - 4 * hf;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int off = 32 * kt + 8 * (i >> 2) + (i & 3);
+                s[kt][i] = off < lim ? s[kt][i] : -INFINITY;
+            }
+    }
+
+    // P = 2^(s·c − m·c) = e^(scale·(s − m)) for sub-block qt (masked entries
+    // give exactly 0), packed into the four bf16 B operands of Oᵀ += Vᵀ·Pᵀ, and
+    // the row sum.  k-step j takes sub-tile j/2, registers 8·(j%2)..+7, i.e. for
+    // half-wave hf the keys 16·j + 4·hf + [0..3] and 16·j + 8 + 4·hf + [0..3].
+    __device__ void softmax_weights(int qt, float mc, const f32x16 (&s)[2], bf16x8 (&pb)[4]) {
+        const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
+        float l = lsum[qt];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int kt = j >> 1, vb = 8 * (j & 1);
+            float p[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) p[e] = exp2_hw(__builtin_fmaf(s[kt][vb + e], c_log2, -mc));
+            const bf16x8 v = to_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
+            pb[j] = v;
+            l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), ones, l, false);
+            l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), ones, l, false);
+            l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), ones, l, false);
+            l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), ones, l, false);
+        }
+        lsum[qt] = l;
+    }
+
+    // One tile of math for both sub-blocks.  Every K operand read from LDS feeds
+    // the Sᵀ products of both sub-blocks, and every Vᵀ operand both P·V products.
+    // (The masking branch also bounds how far the compiler hoists the softmax
+    // into the products, which keeps the wave at two per SIMD.)
+    template <int BUF>
+    __device__ void compute_tile(int k0) {
+        const char* sk = lds + BUF * 2 * TILE_BYTES;
+        const char* sv = sk + TILE_BYTES;
+
+        // Sᵀ = K · Qᵀ over d = 64 (four k-steps of 16).
+        f32x16 s[QT][2];
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) s[qt][kt][i] = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(sk + kaddr[ks] + kt * 32 * 128);
+#pragma unroll
+                for (int qt = 0; qt < QT; ++qt) s[qt][kt] = mfma32x32x16_bf16(a, qop[qt][ks], s[qt][kt]);
+            }
+
+        // −∞ on illegal logits: tiles on the causal diagonal or the padding edge.
+        if ((k0 + BN > L) || (causal && k0 + BN - 1 > wq0)) {
+            mask_block(0, k0, s[0]);
+            mask_block(1, k0, s[1]);
+        }
+
+        // Tile maxima; the reference maximum only moves when this tile would push
+        // some weight of the wave past 2^TAU, and then Oᵀ and l are rescaled.
+        float mt[QT];
+        bool need = false;
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) {
+            float x = max3(s[qt][0][0], s[qt][0][1], s[qt][0][2]);
+#pragma unroll
+            for (int i = 3; i < 15; i += 2) x = max3(x, s[qt][0][i], s[qt][0][i + 1]);
+            x = max3(x, s[qt][0][15], s[qt][1][0]);
+#pragma unroll
+            for (int i = 1; i < 15; i += 2) x = max3(x, s[qt][1][i], s[qt][1][i + 1]);
+            x = max2(x, s[qt][1][15]);
+            mt[qt] = half_swap_max(x);
+            need |= (mt[qt] - mref[qt]) * c_log2 > TAU;  // NaN (−∞ − −∞) compares false
+        }
+        if (__builtin_amdgcn_ballot_w64(need) != 0) {  // wave-uniform
+#pragma unroll
+            for (int qt = 0; qt < QT; ++qt) {
+                const float mnew = fmaxf(mref[qt], mt[qt]);
+                // mref = −∞ (nothing accumulated yet) gives alpha = 0 on zeros;
+                // mnew = −∞ (every key so far illegal) keeps alpha = 1.
+                const float alpha = mnew == -INFINITY ? 1.f : exp2_hw((mref[qt] - mnew) * c_log2);
+                mref[qt] = mnew;
+                lsum[qt] *= alpha;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) { oacc[qt][0][i] *= alpha; oacc[qt][1][i] *= alpha; }
+            }
+        }
+        bf16x8 pb[QT][4];
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt)
+            softmax_weights(qt, (mref[qt] == -INFINITY ? 0.f : mref[qt]) * c_log2, s[qt], pb[qt]);
+
+        // Oᵀ += Vᵀ · Pᵀ.  The Vᵀ operand lists the same keys as Pᵀ: two LDS
+        // transpose reads, each giving 4 consecutive keys (rows 16·j + 4·hf +
+        // [0..3], then + 8) of one dv column to every lane.
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int dt = 0; dt < 2; ++dt) {
+                const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                    (lds_bf16x4*)(sv + vaddr[dt][0] + j * 16 * 128));
+                const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                    (lds_bf16x4*)(sv + vaddr[dt][1] + j * 16 * 128));
+                const bf16x8 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+                for (int qt = 0; qt < QT; ++qt) oacc[qt][dt] = mfma32x32x16_bf16(va, pb[qt][j], oacc[qt][dt]);
+            }
+    }
+
+    // One tile: start the next tile's HBM → LDS copy into the other buffer, do
+    // this tile's math, then wait for the copy and meet at the barrier.  The
+    // other buffer was last read before the previous barrier, so overwriting it
+    // here is safe.
+    template <int BUF>
+    __device__ void step(int t, int ntiles) {
+        if (t + 1 < ntiles) issue_tile_load(t + 1, BUF ^ 1);
+        const int k0 = t * BN;
+        if (!(causal && k0 > wq0 + QW - 1)) {  // else: tile after all our queries
+            compute_tile<BUF>(k0);
+        }
+        wait_vmem();
+        __syncthreads();
+    }
+};
+
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void sdpa_long_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
     int BH, int H, int n, int m, float c_log2, int causal,
     const int32_t* __restrict__ key_lens, int nqb) {
-    constexpr int NT = NW * 64;
-    constexpr int CPT = (BN * D * 2 / 16) / NT;  // 16-byte chunks per thread per tile
-    static_assert(CPT * NT * 16 == BN * D * 2, "tile must split evenly");
-
-    __shared__ u32x4 sK[BN * 8];
-    __shared__ u32x4 sV[BN * 8];
+    using KT = LongKernel<NW>;
+    __shared__ __attribute__((aligned(16))) char lds[2 * 2 * TILE_BYTES];
+    KT k;
+    k.lds = lds;
 
     const int tid = threadIdx.x;
-    const int w = tid >> 6;
-    const int lane = tid & 63;
-    const int l32 = lane & 31;
-    const int hf = lane >> 5;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    k.lane = tid & 63;
+    k.l32 = k.lane & 31;
+    k.hf = k.lane >> 5;
+    k.gi = k.lane & 15;
+    k.causal = causal;
+    k.c_log2 = c_log2;
 
-    // Heaviest query blocks (latest under a causal mask) are dispatched first.
+    // Heaviest query blocks (latest under a causal mask) are dispatched first;
+    // consecutive workgroups take different heads, so with B·h a multiple of 8
+    // each XCD (workgroups are dealt round-robin over 8) always serves the same
+    // heads and keeps their K/V in its own L2.
     const int g = blockIdx.x;
     const int bh = g % BH;
     const int qb = nqb - 1 - g / BH;
     const int b = bh / H;
-    const int q0 = qb * (NW * QW);
+    const int q0 = qb * KT::BM;
 
     int L = m;
     if (key_lens) {
         const int t = key_lens[b];
         L = t < 0 ? 0 : (t > m ? m : t);
     }
+    k.L = L;
     int kend = L;
-    if (causal) kend = min(kend, q0 + NW * QW);
+    if (causal) kend = min(kend, q0 + KT::BM);
     const int ntiles = (kend + BN - 1) / BN;
 
     const size_t qbase = (size_t)bh * n * D;
     const size_t kvbase = (size_t)bh * m * D;
+    k.kg = reinterpret_cast<const char*>(K + kvbase);
+    k.vg = reinterpret_cast<const char*>(V + kvbase);
+    k.wq0 = q0 + w * QW;
 
-    // Qᵀ as the B operand: lane holds query l32, d = 16·ks + 8·hf + [0..7].
-    const int qrow = q0 + w * QW + l32;
-    bf16x8 qop[4];
-    if (qrow < n) {
-        const u32x4* src = reinterpret_cast<const u32x4*>(Q + qbase + (size_t)qrow * D);
+    // Per-lane LDS read offsets (tile-relative, buffer 0).
+    {
+        const int f = swz_f(k.l32);  // rows l32 and l32 + 32 share it
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) qop[ks] = __builtin_bit_cast(bf16x8, src[2 * ks + hf]);
-    } else {
+        for (int ks = 0; ks < 4; ++ks) k.kaddr[ks] = k.l32 * 128 + (((2 * ks + k.hf) ^ f) << 4);
+        // Rows 4·hf + gi/4 (+ 8 for the second read) of k-step 0; k-step j adds
+        // 16·j rows, which leaves swz_f unchanged (it reads row bits 1..3).
+        const int r0 = 4 * k.hf + (k.gi >> 2);
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) qop[ks] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+        for (int dt = 0; dt < 2; ++dt) {
+            const int dv0 = 32 * dt + 16 * ((k.lane >> 4) & 1) + 4 * (k.gi & 3);
+            k.vaddr[dt][0] = lds_swz(r0, dv0 >> 3) * 16 + (dv0 & 7) * 2;
+            k.vaddr[dt][1] = lds_swz(r0 + 8, dv0 >> 3) * 16 + (dv0 & 7) * 2;
+        }
+    }
+    // Per-lane load offsets: wave w's i-th 1 KiB load fills tile rows
+    // 8·(w·LOADS + i) .. +7; lane ln lands in LDS slot (row ln/8, position ln%8),
+    // which holds logical chunk (ln%8) ^ f(row).
+#pragma unroll
+    for (int i = 0; i < KT::LOADS; ++i) {
+        const int row = 8 * (w * KT::LOADS + i) + (k.lane >> 3);
+        const int pos = k.lane & 7;
+        const int chunk = pos ^ swz_f(row);
+        k.ld_voff[i] = row * 128 + chunk * 16;
+        k.ld_lds[i] = 8 * (w * KT::LOADS + i) * 128;
     }
 
-    u32x4 rk[CPT], rv[CPT];
-    auto gload = [&](int t) {
-        const int k0 = t * BN;
+    // Qᵀ as the B operand: sub-block qt, lane holds query wq0 + 32·qt + l32,
+    // d = 16·ks + 8·hf + [0..7].
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const int c = tid + i * NT;
-            const int key = k0 + (c >> 3);
-            if (key < L) {
-                rk[i] = reinterpret_cast<const u32x4*>(K + kvbase + (size_t)key * D)[c & 7];
-                rv[i] = reinterpret_cast<const u32x4*>(V + kvbase + (size_t)key * D)[c & 7];
-            } else {
-                rk[i] = u32x4{0, 0, 0, 0};
-                rv[i] = u32x4{0, 0, 0, 0};
-            }
+    for (int qt = 0; qt < QT; ++qt) {
+        const int qrow = k.wq0 + 32 * qt + k.l32;
+        if (qrow < n) {
+            const u32x4* src = reinterpret_cast<const u32x4*>(Q + qbase + (size_t)qrow * D);
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) k.qop[qt][ks] = __builtin_bit_cast(bf16x8, src[2 * ks + k.hf]);
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) k.qop[qt][ks] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
         }
-    };
-    auto swrite = [&]() {
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const int c = tid + i * NT;
-            const int idx = swz(c >> 3, c & 7);
-            sK[idx] = rk[i];
-            sV[idx] = rv[i];
-        }
-    };
+        for (int i = 0; i < 16; ++i) { k.oacc[qt][0][i] = 0.f; k.oacc[qt][1][i] = 0.f; }
+        k.mref[qt] = -INFINITY;
+        k.lsum[qt] = 0.f;
+    }
 
-    f32x16 oacc[2];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) { oacc[0][i] = 0.f; oacc[1][i] = 0.f; }
-    float mrun = -INFINITY;  // running max of raw scores q·k of this lane's query
-    float lrun = 0.f;        // running sum of weights over this half-wave's keys
+    if (ntiles > 0) {
+        k.issue_tile_load(0, 0);
+        wait_vmem();
+    }
+    __syncthreads();
+    int t = 0;
+    for (; t + 1 < ntiles; t += 2) {
+        k.template step<0>(t, ntiles);
+        k.template step<1>(t + 1, ntiles);
+    }
+    if (t < ntiles) k.template step<0>(t, ntiles);
 
-    const int wq_lo = q0 + w * QW;
-    const int wq_hi = wq_lo + QW - 1;
-    const int my_q = wq_lo + l32;
-
-    if (ntiles > 0) gload(0);
-    for (int t = 0; t < ntiles; ++t) {
-        __syncthreads();  // every wave is done reading the previous tile
-        swrite();
-        __syncthreads();
-        if (t + 1 < ntiles) gload(t + 1);  // next tile's HBM reads overlap this tile's math
-
-        const int k0 = t * BN;
-        if (causal && k0 > wq_hi) continue;  // tile lies entirely after this wave's queries
-
-        // Sᵀ = K · Qᵀ over d = 64 (four k-steps of 16).
-        f32x16 s[2];
+    // ---- Oᵀ / l and store.  Register i of oacc[qt][dt] is dv = 32·dt + 8·(i/4)
+    // + 4·hf + i%4 of query wq0 + 32·qt + l32.
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
+    for (int qt = 0; qt < QT; ++qt) {
+        const int qrow = k.wq0 + 32 * qt + k.l32;
+        const float ltot = half_swap_sum(k.lsum[qt]);
+        const float inv = ltot > 0.f ? 1.f / ltot : 0.f;  // no legal key ⇒ zero row
+        if (qrow < n) {
+            uint16_t* dst = O + qbase + (size_t)qrow * D;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) s[kt][i] = 0.f;
-            const int krow = kt * 32 + l32;
+            for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const bf16x8 a = __builtin_bit_cast(bf16x8, sK[swz(krow, 2 * ks + hf)]);
-                s[kt] = mfma32x32x16_bf16(a, qop[ks], s[kt]);
-            }
-        }
-
-        // −∞ on illegal logits: Sᵀ register i of lane (l32, hf) in sub-tile kt is
-        // key k0 + 32·kt + 8·(i/4) + 4·hf + i%4 for query my_q.
-        const bool need_mask = (k0 + BN > L) || (causal && k0 + BN - 1 > wq_lo);
-        if (need_mask) {
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int key = k0 + kt * 32 + 8 * (i >> 2) + 4 * hf + (i & 3);
-                    if (key >= L || (causal && key > my_q)) s[kt][i] = -INFINITY;
+                for (int i4 = 0; i4 < 4; ++i4) {
+                    const int dv = 32 * dt + 8 * i4 + 4 * k.hf;
+                    bf16x4 o;
+                    o[0] = (__bf16)(k.oacc[qt][dt][4 * i4 + 0] * inv);
+                    o[1] = (__bf16)(k.oacc[qt][dt][4 * i4 + 1] * inv);
+                    o[2] = (__bf16)(k.oacc[qt][dt][4 * i4 + 2] * inv);
+                    o[3] = (__bf16)(k.oacc[qt][dt][4 * i4 + 3] * inv);
+                    *reinterpret_cast<bf16x4*>(dst + dv) = o;
                 }
         }
-
-        float mt = -INFINITY;
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[kt][i]);
-        mt = half_swap_max(mt);
-        const float mnew = fmaxf(mrun, mt);
-        const float muse = (mnew == -INFINITY) ? 0.f : mnew;  // no (−∞) − (−∞)
-        const float alpha = exp2_hw((mrun - muse) * c_log2);
-        mrun = mnew;
-        const float mc = muse * c_log2;
-        lrun *= alpha;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) { oacc[0][i] *= alpha; oacc[1][i] *= alpha; }
-
-        // P = 2^(s·c − m·c) = e^(scale·(s − m)); masked entries give exactly 0.
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float p = exp2_hw(__builtin_fmaf(s[kt][i], c_log2, -mc));
-                s[kt][i] = p;
-                lrun += p;
-            }
-
-        // Oᵀ += Vᵀ · Pᵀ in four k-steps of 16 keys.  k-step j takes Sᵀ sub-tile
-        // j/2, registers 8·(j%2) .. +7; in tile rows that is, for half-wave hf,
-        // keys kb + 4·hf + [0..3] and kb + 8 + 4·hf + [0..3] with kb = 16·j.
-        // The Vᵀ operand must list the same keys: two LDS transpose reads, each
-        // giving 4 consecutive keys of one dv column to every lane.
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int kt = j >> 1, vb = 8 * (j & 1);
-            const bf16x8 pb = to_bf16x8(s[kt][vb + 0], s[kt][vb + 1], s[kt][vb + 2], s[kt][vb + 3],
-                                        s[kt][vb + 4], s[kt][vb + 5], s[kt][vb + 6], s[kt][vb + 7]);
-            const int kb = 16 * j;
-            const int gi = lane & 15;
-            const int r0 = kb + 4 * hf + (gi >> 2);
-#pragma unroll
-            for (int dt = 0; dt < 2; ++dt) {
-                const int dv0 = 32 * dt + 16 * ((lane >> 4) & 1) + 4 * (gi & 3);
-                const int r1 = r0 + 8;
-                const char* base = reinterpret_cast<const char*>(sV);
-                const int off0 = swz(r0, dv0 >> 3) * 16 + (dv0 & 7) * 2;
-                const int off1 = swz(r1, dv0 >> 3) * 16 + (dv0 & 7) * 2;
-                typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-                const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                    (lds_bf16x4*)(base + off0));
-                const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                    (lds_bf16x4*)(base + off1));
-                const bf16x8 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                oacc[dt] = mfma32x32x16_bf16(va, pb, oacc[dt]);
-            }
-        }
     }
+}
 
-    // Oᵀ / l.  Register i of oacc[dt] is dv = 32·dt + 8·(i/4) + 4·hf + i%4 of query my_q.
-    const float ltot = half_swap_sum(lrun);
-    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;  // no legal key ⇒ zero row
-    if (qrow < n) {
-        uint16_t* dst = O + qbase + (size_t)qrow * D;
-#pragma unroll
-        for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-            for (int i4 = 0; i4 < 4; ++i4) {
-                const int dv = 32 * dt + 8 * i4 + 4 * hf;
-                bf16x4 o;
-                o[0] = (__bf16)(oacc[dt][4 * i4 + 0] * inv);
-                o[1] = (__bf16)(oacc[dt][4 * i4 + 1] * inv);
-                o[2] = (__bf16)(oacc[dt][4 * i4 + 2] * inv);
-                o[3] = (__bf16)(oacc[dt][4 * i4 + 3] * inv);
-                *reinterpret_cast<bf16x4*>(dst + dv) = o;
-            }
-    }
+template <int NW>
+hipError_t launch_long(const Args& a, hipStream_t stream) {
+    const int BH = a.B * a.H;
+    const float c_log2 = (float)((double)a.scale * 1.4426950408889634);  // scale·log2(e)
+    const int nqb = (a.n + NW * QW - 1) / (NW * QW);
+    hipLaunchKernelGGL(sdpa_long_bf16<NW>, dim3(nqb * BH), dim3(NW * 64), 0, stream,
+                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                       (uint16_t*)a.out, BH, a.H, a.n, a.m, c_log2, a.causal, a.key_lens, nqb);
+    return hipGetLastError();
 }
 
 }  // namespace
 
+hipError_t launch_bf16_long(const Args& a, hipStream_t stream) {
+    // 4 waves (256 queries) per workgroup once there are enough query blocks to
+    // fill the chip; 2 waves (128 queries) otherwise.
+    const long long blocks4 = (long long)a.B * a.H * ((a.n + 4 * QW - 1) / (4 * QW));
+    return blocks4 >= 1024 ? launch_long<4>(a, stream) : launch_long<2>(a, stream);
+}
+
 hipError_t launch_bf16(const Args& a, hipStream_t stream) {
-    const int BH = a.B * a.H;
-    const float c_log2 = (float)((double)a.scale * 1.4426950408889634);  // scale·log2(e)
-    if (a.n <= 64) {
-        constexpr int NW = 2;
-        const int nqb = (a.n + NW * QW - 1) / (NW * QW);
-        hipLaunchKernelGGL(sdpa_fwd_bf16<NW>, dim3(nqb * BH), dim3(NW * 64), 0, stream,
-                           (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                           (uint16_t*)a.out, BH, a.H, a.n, a.m, c_log2, a.causal, a.key_lens, nqb);
-    } else {
-        constexpr int NW = 4;
-        const int nqb = (a.n + NW * QW - 1) / (NW * QW);
-        hipLaunchKernelGGL(sdpa_fwd_bf16<NW>, dim3(nqb * BH), dim3(NW * 64), 0, stream,
-                           (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                           (uint16_t*)a.out, BH, a.H, a.n, a.m, c_log2, a.causal, a.key_lens, nqb);
-    }
-    return hipGetLastError();
+    return short_bf16_fits(a) ? launch_bf16_short(a, stream) : launch_bf16_long(a, stream);
 }
 
 }  // namespace sdpa

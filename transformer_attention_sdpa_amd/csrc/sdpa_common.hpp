@@ -31,8 +31,25 @@ struct Args {
     const int32_t* key_lens;  // device int32[B] or nullptr
 };
 
-hipError_t launch_bf16(const Args& a, hipStream_t stream);
+hipError_t launch_bf16(const Args& a, hipStream_t stream);        // picks one of the two below
+hipError_t launch_bf16_long(const Args& a, hipStream_t stream);   // any n, m
+hipError_t launch_bf16_short(const Args& a, hipStream_t stream);  // n, m <= 64
+bool short_bf16_fits(const Args& a);
 hipError_t launch_f32(const Args& a, hipStream_t stream);
+
+// max(a, b, c) in one v_max3_f32 and max(a, b) in one v_max_f32.  Written as
+// instructions because fmaxf on MFMA results is lowered with an extra
+// NaN-quieting v_max per operand.
+__device__ __forceinline__ float max3(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+__device__ __forceinline__ float max2(float a, float b) {
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
 
 // Both halves of a wave64 combined: after the call every lane holds
 // op(x[lane], x[lane ^ 32]).  v_permlane32_swap exchanges the upper 32 lanes
@@ -40,7 +57,7 @@ hipError_t launch_f32(const Args& a, hipStream_t stream);
 // in both, the pair it returns is {x[lane], x[lane ^ 32]} in some order.
 __device__ __forceinline__ float half_swap_max(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    return max2(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float half_swap_sum(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -56,6 +73,43 @@ __device__ __forceinline__ f32x16 mfma32x32x16_bf16(bf16x8 a, bf16x8 b, f32x16 c
 __device__ __forceinline__ f32x16 mfma32x32x2_f32(float a, float b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
+
+// LDS layout of a 64-column bf16 tile (128-byte rows, 16-byte chunks).  Chunk
+// c of row r sits at chunk position c ^ swz_f(r), where swz_f(r) is the 3-bit
+// reversal of (r/2 mod 8).  gfx950's LDS serves 256 bytes (64 banks) per pass,
+// so two rows share a pass when they have the same parity; the XOR keeps
+//   * 16 consecutive rows read at one chunk (a 16-byte MFMA operand per lane,
+//     16 lanes per pass) on 16 different bank groups, and
+//   * the 32-byte runs that ds_read_b64_tr_b16 takes from 4 or 8 consecutive
+//     rows (32 lanes per pass) on disjoint bank groups.
+__device__ __forceinline__ int swz_f(int row) {
+    return (((row >> 1) & 1) << 2) | (((row >> 2) & 1) << 1) | ((row >> 3) & 1);
+}
+__device__ __forceinline__ int lds_swz(int row, int chunk) { return row * 8 + (chunk ^ swz_f(row)); }
+
+// Raw buffer resource over [base, base + nbytes): loads at offsets >= nbytes
+// return zeros without touching memory (gfx9 descriptor, dword 3 = 0x00020000).
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t nbytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    i32x4 r;
+    r[0] = (int32_t)(uint32_t)a;
+    r[1] = (int32_t)(uint32_t)((a >> 32) & 0xffffu);
+    r[2] = (int32_t)nbytes;
+    r[3] = 0x00020000;
+    return r;
+}
+
+// buffer_load_dwordx4 … lds: lane i's 16 bytes from rsrc + voffset land at
+// LDS address lds + 16·i (lds must be wave-uniform); out-of-range lanes write
+// zeros.  Asynchronous: wait with s_waitcnt vmcnt before reading the LDS.
+extern "C" __device__ void sdpa_llvm_buffer_load_lds(i32x4 rsrc, __attribute__((address_space(3))) void* lds,
+                                                     int size, int voffset, int soffset, int offset,
+                                                     int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+__device__ __forceinline__ void load16_to_lds(i32x4 rsrc, void* lds, int voffset) {
+    sdpa_llvm_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds, 16, voffset, 0, 0, 0);
+}
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Round-to-nearest-even float → bf16 of eight values (v_cvt_pk_bf16_f32 on gfx950).
 __device__ __forceinline__ bf16x8 to_bf16x8(float a0, float a1, float a2, float a3,
