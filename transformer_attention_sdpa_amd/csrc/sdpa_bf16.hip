@@ -28,10 +28,11 @@
 //
 // VALU economy (at d = 64 the softmax costs about as much issue time as the
 // matrix products):
-//   * the reference maximum only moves when a tile's maximum exceeds it by more
-//     than 2^TAU in weight, and the Oᵀ/l rescale is skipped unless some lane of
-//     the wave needs it — exact, because any common reference cancels in
-//     Σ p·v / Σ p; the weights are then bounded by 2^TAU;
+//   * the weights are formed against a reference maximum that only moves when a
+//     tile's weights would exceed 2^14 (checked on the row sums, so the tile
+//     maximum is not even computed on most tiles), and the Oᵀ/l rescale only
+//     happens then — exact, because any common reference cancels in
+//     Σ p·v / Σ p;
 //   * one FMA + one v_exp_f32 per score (scale·log2 e folded into the FMA);
 //   * row sums with v_dot2_f32_bf16 on the packed bf16 weights (the same values
 //     that enter P·V);
@@ -48,7 +49,9 @@ constexpr int D = kHeadDim;  // 64
 constexpr int BN = 64;       // keys per LDS tile
 constexpr int QT = 2;        // 32-query sub-blocks per wave
 constexpr int QW = 32 * QT;  // queries per wave
-constexpr float TAU = 8.f;   // weights stay below 2^TAU between rescales
+// A lane's partial weight sum over one tile may reach this before the reference
+// maximum moves: weights stay below it (2^14), far inside bf16 and fp32 range.
+constexpr float SUM_LIMIT = 16384.f;
 constexpr int TILE_BYTES = BN * D * 2;  // 8 KiB
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
@@ -105,12 +108,13 @@ struct LongKernel {
     }
 
     // P = 2^(s·c − m·c) = e^(scale·(s − m)) for sub-block qt (masked entries
-    // give exactly 0), packed into the four bf16 B operands of Oᵀ += Vᵀ·Pᵀ, and
-    // the row sum.  k-step j takes sub-tile j/2, registers 8·(j%2)..+7, i.e. for
-    // half-wave hf the keys 16·j + 4·hf + [0..3] and 16·j + 8 + 4·hf + [0..3].
-    __device__ void softmax_weights(int qt, float mc, const f32x16 (&s)[2], bf16x8 (&pb)[4]) {
+    // give exactly 0), packed into the four bf16 B operands of Oᵀ += Vᵀ·Pᵀ.
+    // Returns this lane's partial sum of the (bf16) weights.  k-step j takes
+    // sub-tile j/2, registers 8·(j%2)..+7, i.e. for half-wave hf the keys
+    // 16·j + 4·hf + [0..3] and 16·j + 8 + 4·hf + [0..3].
+    __device__ float softmax_weights(float mc, const f32x16 (&s)[2], bf16x8 (&pb)[4]) {
         const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
-        float l = lsum[qt];
+        float l = 0.f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int kt = j >> 1, vb = 8 * (j & 1);
@@ -124,7 +128,7 @@ struct LongKernel {
             l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), ones, l, false);
             l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), ones, l, false);
         }
-        lsum[qt] = l;
+        return l;
     }
 
     // One tile of math for both sub-blocks.  Every K operand read from LDS feeds
@@ -159,26 +163,32 @@ struct LongKernel {
             mask_block(1, k0, s[1]);
         }
 
-        // Tile maxima; the reference maximum only moves when this tile would push
-        // some weight of the wave past 2^TAU, and then Oᵀ and l are rescaled.
-        float mt[QT];
-        bool need = false;
+        // Weights against the current reference maximum, without computing this
+        // tile's maximum: if every lane's partial sum stays within 2^SUM_LOG2,
+        // no weight exceeds it and the tile is done (the reference cancels in
+        // Σ p·v / Σ p).  Otherwise — and on a wave's first tile, where there is
+        // no reference yet — take the tile maxima, move the reference to them,
+        // rescale Oᵀ and l, and recompute the weights (all ≤ 1).
+        bf16x8 pb[QT][4];
+        float lt[QT];
+        bool exact = __builtin_amdgcn_ballot_w64(mref[0] == -INFINITY || mref[1] == -INFINITY) != 0;
+        if (!exact) {
 #pragma unroll
-        for (int qt = 0; qt < QT; ++qt) {
-            float x = max3(s[qt][0][0], s[qt][0][1], s[qt][0][2]);
-#pragma unroll
-            for (int i = 3; i < 15; i += 2) x = max3(x, s[qt][0][i], s[qt][0][i + 1]);
-            x = max3(x, s[qt][0][15], s[qt][1][0]);
-#pragma unroll
-            for (int i = 1; i < 15; i += 2) x = max3(x, s[qt][1][i], s[qt][1][i + 1]);
-            x = max2(x, s[qt][1][15]);
-            mt[qt] = half_swap_max(x);
-            need |= (mt[qt] - mref[qt]) * c_log2 > TAU;  // NaN (−∞ − −∞) compares false
+            for (int qt = 0; qt < QT; ++qt) lt[qt] = softmax_weights(mref[qt] * c_log2, s[qt], pb[qt]);
+            // overflow gives +inf, which fails the test; NaN (from NaN inputs) passes
+            exact = __builtin_amdgcn_ballot_w64(lt[0] > SUM_LIMIT || lt[1] > SUM_LIMIT) != 0;
         }
-        if (__builtin_amdgcn_ballot_w64(need) != 0) {  // wave-uniform
+        if (exact) {
 #pragma unroll
             for (int qt = 0; qt < QT; ++qt) {
-                const float mnew = fmaxf(mref[qt], mt[qt]);
+                float x = max3(s[qt][0][0], s[qt][0][1], s[qt][0][2]);
+#pragma unroll
+                for (int i = 3; i < 15; i += 2) x = max3(x, s[qt][0][i], s[qt][0][i + 1]);
+                x = max3(x, s[qt][0][15], s[qt][1][0]);
+#pragma unroll
+                for (int i = 1; i < 15; i += 2) x = max3(x, s[qt][1][i], s[qt][1][i + 1]);
+                x = max2(x, s[qt][1][15]);
+                const float mnew = fmaxf(mref[qt], half_swap_max(x));
                 // mref = −∞ (nothing accumulated yet) gives alpha = 0 on zeros;
                 // mnew = −∞ (every key so far illegal) keeps alpha = 1.
                 const float alpha = mnew == -INFINITY ? 1.f : exp2_hw((mref[qt] - mnew) * c_log2);
@@ -186,12 +196,11 @@ struct LongKernel {
                 lsum[qt] *= alpha;
 #pragma unroll
                 for (int i = 0; i < 16; ++i) { oacc[qt][0][i] *= alpha; oacc[qt][1][i] *= alpha; }
+                lt[qt] = softmax_weights((mnew == -INFINITY ? 0.f : mnew) * c_log2, s[qt], pb[qt]);
             }
         }
-        bf16x8 pb[QT][4];
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt)
-            softmax_weights(qt, (mref[qt] == -INFINITY ? 0.f : mref[qt]) * c_log2, s[qt], pb[qt]);
+        lsum[0] += lt[0];
+        lsum[1] += lt[1];
 
         // Oᵀ += Vᵀ · Pᵀ.  The Vᵀ operand lists the same keys as Pᵀ: two LDS
         // transpose reads, each giving 4 consecutive keys (rows 16·j + 4·hf +
