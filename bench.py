@@ -203,6 +203,75 @@ def copy_reference(steps, warmup, nbytes=256 << 20):
             "ms_per_copy": t * 1e3, "gbs_read_plus_write": 2 * nbytes / t / 1e9}
 
 
+def rocprof_summary(db_path) -> str:
+    """Text summary of a rocprofv3 results database: per-kernel dispatch
+    durations (kernel trace) and per-dispatch means of any PMC counters."""
+    import sqlite3
+    import statistics
+    from collections import defaultdict
+
+    con = sqlite3.connect(db_path)
+    out = []
+    rows = list(con.execute("select name, start, end from kernels order by start"))
+    per = defaultdict(list)
+    for name, t0, t1 in rows:
+        per[name].append((t1 - t0) / 1e3)
+    if per:
+        out.append(f"{'kernel':64s} {'calls':>6s} {'mean_us':>9s} {'median_us':>9s} "
+                   f"{'p10_us':>8s} {'p90_us':>8s}")
+        for name, d in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+            d2 = sorted(d)
+            out.append(f"{name[:64]:64s} {len(d):6d} {statistics.mean(d):9.3f} "
+                       f"{d2[len(d2) // 2]:9.3f} {d2[len(d2) // 10]:8.3f} {d2[9 * len(d2) // 10]:8.3f}")
+    try:
+        pmc = list(con.execute("select kernel_name, counter_name, value from counters_collection"))
+    except sqlite3.Error:
+        pmc = []
+    if pmc:
+        agg = defaultdict(list)
+        for k, c, v in pmc:
+            agg[(k, c)].append(v)
+        out.append("")
+        out.append(f"{'kernel':64s} {'counter':28s} {'dispatches':>10s} {'mean_per_dispatch':>18s}")
+        for (k, c), v in sorted(agg.items()):
+            out.append(f"{k[:64]:64s} {c:28s} {len(v):10d} {statistics.mean(v):18.6g}")
+    return "\n".join(out)
+
+
+def pmc_mean(db_path, kernel_substr, counter):
+    import sqlite3
+    import statistics
+
+    con = sqlite3.connect(db_path)
+    vals = [v for k, c, v in con.execute(
+        "select kernel_name, counter_name, value from counters_collection")
+        if kernel_substr in k and c == counter]
+    if not vals:
+        raise SystemExit(f"no {counter} samples for a kernel matching {kernel_substr!r} in {db_path}")
+    return statistics.mean(vals)
+
+
+def traffic_record(fetch_db, write_db, copy_fetch_db, copy_write_db, copy_bytes, kernel, workload,
+                   dtype):
+    """Per-launch HBM bytes of `kernel` from FETCH_SIZE / WRITE_SIZE runs, each
+    scaled by what the same counter reads for a copy of `copy_bytes` bytes."""
+    f = pmc_mean(fetch_db, kernel, "FETCH_SIZE")
+    w = pmc_mean(write_db, kernel, "WRITE_SIZE")
+    cf = pmc_mean(copy_fetch_db, "copyBuffer", "FETCH_SIZE")
+    cw = pmc_mean(copy_write_db, "copyBuffer", "WRITE_SIZE")
+    sf = copy_bytes / 1024.0 / cf
+    sw = copy_bytes / 1024.0 / cw
+    read_b = f * sf * 1024.0
+    write_b = w * sw * 1024.0
+    return {"kernel": kernel, "workload": workload, "dtype": dtype,
+            "fetch_kib_per_dispatch": f, "write_kib_per_dispatch": w,
+            "copy_bytes": copy_bytes, "copy_fetch_kib": cf, "copy_write_kib": cw,
+            "fetch_scale": sf, "write_scale": sw,
+            "read_bytes_per_launch": read_b, "write_bytes_per_launch": write_b,
+            "bytes_per_launch": read_b + write_b,
+            "kernel_source_hash": kernel_source_hash()}
+
+
 def cpu_baseline(name, dtype, budget_s=10.0):
     """The fp64 oracle, as it stands, on the host cores: whole batches until the budget."""
     import oracle.sdpa_oracle as so
@@ -238,7 +307,24 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="time a plain device copy instead (reference for HBM counters)")
     ap.add_argument("--copy-mib", type=float, default=256.0, help="size of --calibrate-copy")
+    ap.add_argument("--rocprof-summary", nargs="+", metavar="DB",
+                    help="print a text summary of rocprofv3 result databases and exit")
+    ap.add_argument("--traffic-json", nargs=4, metavar=("FETCH_DB", "WRITE_DB", "COPY_FETCH_DB",
+                                                        "COPY_WRITE_DB"),
+                    help="print the per-launch HBM traffic record of --kernel and exit")
+    ap.add_argument("--kernel", default="sdpa_short_bf16", help="kernel name for --traffic-json")
     args = ap.parse_args()
+
+    if args.rocprof_summary:
+        for db in args.rocprof_summary:
+            print(f"== {db}")
+            print(rocprof_summary(db))
+        return
+    if args.traffic_json:
+        rec = traffic_record(*args.traffic_json, int(args.copy_mib * (1 << 20)), args.kernel,
+                             args.workload, args.dtype)
+        print(json.dumps(rec, indent=1))
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: every (batch, head) pair is independent and this "

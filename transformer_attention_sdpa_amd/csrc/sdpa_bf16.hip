@@ -159,8 +159,8 @@ struct LongKernel {
 
         // −∞ on illegal logits: tiles on the causal diagonal or the padding edge.
         if ((k0 + BN > L) || (causal && k0 + BN - 1 > wq0)) {
-            mask_block(0, k0, s[0]);
-            mask_block(1, k0, s[1]);
+#pragma unroll
+            for (int qt = 0; qt < QT; ++qt) mask_block(qt, k0, s[qt]);
         }
 
         // Weights against the current reference maximum, without computing this
@@ -171,12 +171,18 @@ struct LongKernel {
         // rescale Oᵀ and l, and recompute the weights (all ≤ 1).
         bf16x8 pb[QT][4];
         float lt[QT];
-        bool exact = __builtin_amdgcn_ballot_w64(mref[0] == -INFINITY || mref[1] == -INFINITY) != 0;
+        bool unset = false;
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) unset |= mref[qt] == -INFINITY;
+        bool exact = __builtin_amdgcn_ballot_w64(unset) != 0;
         if (!exact) {
 #pragma unroll
             for (int qt = 0; qt < QT; ++qt) lt[qt] = softmax_weights(mref[qt] * c_log2, s[qt], pb[qt]);
             // overflow gives +inf, which fails the test; NaN (from NaN inputs) passes
-            exact = __builtin_amdgcn_ballot_w64(lt[0] > SUM_LIMIT || lt[1] > SUM_LIMIT) != 0;
+            bool big = false;
+#pragma unroll
+            for (int qt = 0; qt < QT; ++qt) big |= lt[qt] > SUM_LIMIT;
+            exact = __builtin_amdgcn_ballot_w64(big) != 0;
         }
         if (exact) {
 #pragma unroll
@@ -199,8 +205,8 @@ struct LongKernel {
                 lt[qt] = softmax_weights((mnew == -INFINITY ? 0.f : mnew) * c_log2, s[qt], pb[qt]);
             }
         }
-        lsum[0] += lt[0];
-        lsum[1] += lt[1];
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) lsum[qt] += lt[qt];
 
         // Oᵀ += Vᵀ · Pᵀ.  The Vᵀ operand lists the same keys as Pᵀ: two LDS
         // transpose reads, each giving 4 consecutive keys (rows 16·j + 4·hf +

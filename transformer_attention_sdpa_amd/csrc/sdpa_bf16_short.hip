@@ -11,9 +11,11 @@
 //     tile, so the softmax is an exact two-pass one with no running rescale;
 //   * four waves of 16 queries each on v_mfma_f32_16x16x32_bf16, so each wave's
 //     serial MFMA/softmax chain is a quarter of a head;
-//   * Q goes straight from HBM into the B-operand registers; K and V are read
-//     once per head, 16 bytes per lane, into LDS; rows at or past the key
-//     length are not read (zero-filled);
+//   * Q, K and V move HBM → LDS with buffer_load_dwordx4 … lds; Q and K are
+//     issued before the key length is even known (K rows past it only yield
+//     scores the mask discards), V right after it, with its buffer range ending
+//     at the key length so padded V rows are never read; the scores and the
+//     softmax run while V is still in flight;
 //   * Sᵀ = K·Qᵀ and Oᵀ = Vᵀ·Pᵀ (transposed, as in the long kernel) so the row
 //     max/sum are lane-local plus two half/quarter-wave exchanges, and Vᵀ comes
 //     from LDS transpose reads (ds_read_b64_tr_b16).
@@ -56,11 +58,14 @@ __global__ __launch_bounds__(NT) void sdpa_short_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
     int H, int n, int m, float c_log2, int causal, const int32_t* __restrict__ key_lens) {
-    __shared__ u32x4 sK[MAXLEN * 8];
-    __shared__ u32x4 sV[MAXLEN * 8];
+    // K tile at 0, Q tile at 8 KiB, V tile at 16 KiB (64 rows × 128 B each).
+    __shared__ __attribute__((aligned(16))) char lds[3 * MAXLEN * 128];
+    const u32x4* sK = reinterpret_cast<const u32x4*>(lds);
+    const u32x4* sQ = reinterpret_cast<const u32x4*>(lds + MAXLEN * 128);
+    const char* sVb = lds + 2 * MAXLEN * 128;
 
     const int tid = threadIdx.x;
-    const int w = tid >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int l16 = lane & 15;
     const int G = lane >> 4;  // 16-lane group 0..3
@@ -70,42 +75,51 @@ __global__ __launch_bounds__(NT) void sdpa_short_bf16(
     const size_t qbase = (size_t)bh * n * D;
     const size_t kvbase = (size_t)bh * m * D;
 
-    // Qᵀ as the B operand: lane holds query q, d = 32·ks + 8·G + [0..7].
-    const int q = w * QW + l16;
-    bf16x8 qop[2];
-    if (q < n) {
-        const u32x4* src = reinterpret_cast<const u32x4*>(Q + qbase + (size_t)q * D);
-        qop[0] = __builtin_bit_cast(bf16x8, src[G]);
-        qop[1] = __builtin_bit_cast(bf16x8, src[4 + G]);
-    } else {
-        qop[0] = qop[1] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+    // HBM → LDS with buffer_load_dwordx4 … lds.  Wave w moves tile rows
+    // 8·(2w + i) .. +7 (i = 0, 1) of each tensor; lane ln lands in LDS slot
+    // (row ln/8, position ln%8), which holds logical chunk (ln%8) ^ swz_f(row).
+    int ld_off[2], ld_lds[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int row = 8 * (2 * w + i) + (lane >> 3);
+        ld_off[i] = row * 128 + ((lane & 7) ^ swz_f(row)) * 16;
+        ld_lds[i] = 8 * (2 * w + i) * 128;
     }
-
+    // K and Q go first, without waiting for the key length: K rows past it
+    // only produce scores that the mask discards, and rows past m or n arrive
+    // as zeros (buffer range).  Then the key length, then V, whose buffer range
+    // stops at it, so its padded rows arrive as zeros without being read (they
+    // meet weight 0 in P·V, and 0 · garbage must not happen).  The scores and
+    // the softmax run while V is still in flight.
+    const i32x4 rk = make_rsrc(K + kvbase, (uint32_t)(m * D * 2));
+    const i32x4 rq = make_rsrc(Q + qbase, (uint32_t)(n * D * 2));
+    load16_to_lds(rk, lds + ld_lds[0], ld_off[0]);
+    load16_to_lds(rk, lds + ld_lds[1], ld_off[1]);
+    load16_to_lds(rq, lds + MAXLEN * 128 + ld_lds[0], ld_off[0]);
+    load16_to_lds(rq, lds + MAXLEN * 128 + ld_lds[1], ld_off[1]);
     int L = m;
     if (key_lens) {
         const int t = key_lens[b];
         L = t < 0 ? 0 : (t > m ? m : t);
     }
+    const i32x4 rv = make_rsrc(V + kvbase, (uint32_t)(L * D * 2));
+    load16_to_lds(rv, lds + 2 * MAXLEN * 128 + ld_lds[0], ld_off[0]);
+    load16_to_lds(rv, lds + 2 * MAXLEN * 128 + ld_lds[1], ld_off[1]);
+    asm volatile("s_waitcnt vmcnt(2)" ::: "memory");  // K and Q in; V may still fly
+    lds_barrier();
+    const bool active = w * QW < n;  // this wave has queries (n < 64 leaves some idle)
 
-    // The head's legal K/V rows → LDS (rows ≥ L are zero: V rows enter P·V with
-    // weight 0, and 0 · garbage must not happen).
-#pragma unroll
-    for (int i = 0; i < (MAXLEN * 8) / NT; ++i) {
-        const int c = tid + i * NT;
-        const int row = c >> 3;
-        u32x4 kx = {0, 0, 0, 0}, vx = {0, 0, 0, 0};
-        if (row < L) {
-            kx = reinterpret_cast<const u32x4*>(K + kvbase + (size_t)row * D)[c & 7];
-            vx = reinterpret_cast<const u32x4*>(V + kvbase + (size_t)row * D)[c & 7];
-        }
-        sK[swz(row, c & 7)] = kx;
-        sV[swz(row, c & 7)] = vx;
-    }
-    __syncthreads();
-    if (w * QW >= n) return;  // no queries for this wave (n < 64)
+    // Qᵀ as the B operand: lane holds query q, d = 32·ks + 8·G + [0..7].
+    const int q = w * QW + l16;
+    bf16x8 qop[2];
+    qop[0] = __builtin_bit_cast(bf16x8, sQ[swz(q, G)]);
+    qop[1] = __builtin_bit_cast(bf16x8, sQ[swz(q, 4 + G)]);
 
     // Sᵀ = K · Qᵀ: four 16-key tiles; register r of tile kt is key 16·kt + 4·G + r.
     f32x4 s[4];
+    bf16x8 pb[2];
+    float l = 0.f;
+    if (active) {
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
         s[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -123,11 +137,10 @@ __global__ __launch_bounds__(NT) void sdpa_short_bf16(
         for (int r = 0; r < 4; ++r) {
             const int key = 16 * kt + 4 * G + r;
             if (key >= L || (causal && key > q)) s[kt][r] = -INFINITY;
-            mx = fmaxf(mx, s[kt][r]);
+            mx = max2(mx, s[kt][r]);
         }
     mx = quad_max(mx);
     const float mc = (mx == -INFINITY ? 0.f : mx) * c_log2;  // no (−∞) − (−∞)
-    float l = 0.f;
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
@@ -137,6 +150,14 @@ __global__ __launch_bounds__(NT) void sdpa_short_bf16(
             l += p;
         }
     l = quad_sum(l);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+        pb[j] = to_bf16x8(s[2 * j][0], s[2 * j][1], s[2 * j][2], s[2 * j][3],
+                          s[2 * j + 1][0], s[2 * j + 1][1], s[2 * j + 1][2], s[2 * j + 1][3]);
+    }
+    wait_vmem();  // V in
+    lds_barrier();
+    if (!active) return;
 
     // Oᵀ = Vᵀ · Pᵀ: k-step j covers keys 32·j + 4·G + [0..3] (slots 0..3, from
     // tile 2j) and 32·j + 16 + 4·G + [0..3] (slots 4..7, from tile 2j+1).
@@ -144,11 +165,9 @@ __global__ __launch_bounds__(NT) void sdpa_short_bf16(
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-    const char* vb = reinterpret_cast<const char*>(sV);
+    const char* vb = sVb;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-        const bf16x8 pb = to_bf16x8(s[2 * j][0], s[2 * j][1], s[2 * j][2], s[2 * j][3],
-                                    s[2 * j + 1][0], s[2 * j + 1][1], s[2 * j + 1][2], s[2 * j + 1][3]);
         const int r0 = 32 * j + 4 * G + (l16 >> 2);
         const int r1 = r0 + 16;
 #pragma unroll
@@ -158,7 +177,7 @@ __global__ __launch_bounds__(NT) void sdpa_short_bf16(
                 (lds_bf16x4*)(vb + swz(r0, dv0 >> 3) * 16 + (dv0 & 7) * 2));
             const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
                 (lds_bf16x4*)(vb + swz(r1, dv0 >> 3) * 16 + (dv0 & 7) * 2));
-            o[dt] = mfma16(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pb, o[dt]);
+            o[dt] = mfma16(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pb[j], o[dt]);
         }
     }
 

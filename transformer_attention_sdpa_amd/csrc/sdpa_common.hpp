@@ -109,7 +109,20 @@ extern "C" __device__ void sdpa_llvm_buffer_load_lds(i32x4 rsrc, __attribute__((
 __device__ __forceinline__ void load16_to_lds(i32x4 rsrc, void* lds, int voffset) {
     sdpa_llvm_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds, 16, voffset, 0, 0, 0);
 }
+// buffer_load_dwordx4 into VGPRs; offsets at or past the descriptor's range
+// read as zeros.
+extern "C" __device__ i32x4 sdpa_llvm_buffer_load_v4i32(i32x4 rsrc, int voffset, int soffset,
+                                                        int aux) __asm("llvm.amdgcn.raw.buffer.load.v4i32");
+__device__ __forceinline__ u32x4 load16(i32x4 rsrc, int voffset) {
+    return __builtin_bit_cast(u32x4, sdpa_llvm_buffer_load_v4i32(rsrc, voffset, 0, 0));
+}
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Workgroup barrier without the release fence of __syncthreads (which waits
+// for every outstanding global load, LDS DMA included).  For LDS data written
+// by buffer loads: wait for them (s_waitcnt vmcnt) before the barrier.  No
+// ds_write may be pending across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Round-to-nearest-even float → bf16 of eight values (v_cvt_pk_bf16_f32 on gfx950).
 __device__ __forceinline__ bf16x8 to_bf16x8(float a0, float a1, float a2, float a3,
