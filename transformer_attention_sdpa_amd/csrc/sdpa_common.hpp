@@ -35,7 +35,10 @@ hipError_t launch_bf16(const Args& a, hipStream_t stream);        // picks one o
 hipError_t launch_bf16_long(const Args& a, hipStream_t stream);   // any n, m
 hipError_t launch_bf16_short(const Args& a, hipStream_t stream);  // n, m <= 64
 bool short_bf16_fits(const Args& a);
-hipError_t launch_f32(const Args& a, hipStream_t stream);
+hipError_t launch_f32(const Args& a, hipStream_t stream);        // picks one of the two below
+hipError_t launch_f32_long(const Args& a, hipStream_t stream);   // any n, m
+hipError_t launch_f32_short(const Args& a, hipStream_t stream);  // n, m <= 64
+bool short_f32_fits(const Args& a);
 
 // max(a, b, c) in one v_max3_f32 and max(a, b) in one v_max_f32.  Written as
 // instructions because fmaxf on MFMA results is lowered with an extra

@@ -199,7 +199,7 @@ __global__ __launch_bounds__(NW * 64) void sdpa_fwd_f32(
 
 }  // namespace
 
-hipError_t launch_f32(const Args& a, hipStream_t stream) {
+hipError_t launch_f32_long(const Args& a, hipStream_t stream) {
     const int BH = a.B * a.H;
     const float c_log2 = (float)((double)a.scale * 1.4426950408889634);
     if (a.n <= 32) {
@@ -216,6 +216,10 @@ hipError_t launch_f32(const Args& a, hipStream_t stream) {
                            BH, a.H, a.n, a.m, c_log2, a.causal, a.key_lens, nqb);
     }
     return hipGetLastError();
+}
+
+hipError_t launch_f32(const Args& a, hipStream_t stream) {
+    return short_f32_fits(a) ? launch_f32_short(a, stream) : launch_f32_long(a, stream);
 }
 
 }  // namespace sdpa

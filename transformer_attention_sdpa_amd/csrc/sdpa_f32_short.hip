@@ -1,0 +1,221 @@
+// Sentence-length attention forward (n, m <= 64), fp32, gfx950.
+//
+// Same computation as the other kernels — Eq. (1) of 《精读 Attention Is All You
+// Need：原始 Transformer 论文》, softmax(Q Kᵀ·scale) V per (batch, head), with
+// illegal logits at −∞ (《Attention Is All You Need：注意力就是你所需要的一切》
+// §3.2.3) — in fp32 end to end: fp32 products on the matrix cores
+// (v_mfma_f32_16x16x4_f32; gfx950 has no reduced-precision fp32 MFMA, so
+// nothing is truncated), fp32 weights, fp32 output.
+//
+// Built like the bf16 sentence-length kernel: one workgroup per (batch, head),
+// four waves of 16 queries, the whole head (≤ 64 keys) as one tile so the
+// softmax is an exact two-pass one.  Q and K move HBM → LDS (buffer_load …
+// lds) before the key length is known (K rows past it only give scores the
+// mask discards), V right after it with its buffer range ending at the key
+// length (padded V rows are never read), and the scores and softmax run while
+// V is in flight.  Key tiles of 16 wholly past the key length (or, causal,
+// past a wave's queries) are skipped.
+//
+// Products, transposed as elsewhere (each lane owns one query column):
+//   Sᵀ (16 keys × 16 queries) = K · Qᵀ, 16 k-steps of 4; in k-step ks the
+//     16-lane group G contributes d = 16·G + ks (a permutation of the
+//     contraction index), so each lane reads 16 consecutive floats of its K
+//     row and of its Q row;
+//   Oᵀ (16 dv × 16 queries) += Vᵀ · Pᵀ, one k-step per (key tile kt, r): group
+//     G contributes key 16·kt + 4·G + r, which is exactly the Sᵀ register
+//     (kt, r) the lane already holds — Pᵀ never moves.
+#include "sdpa_common.hpp"
+
+namespace sdpa {
+namespace {
+
+constexpr int D = kHeadDim;  // 64
+constexpr int MAXLEN = 64;
+constexpr int QW = 16;       // queries per wave
+constexpr int NW = 4;
+constexpr int NT = NW * 64;
+constexpr int ROW = D * 4;   // 256-byte rows
+constexpr int TILE = MAXLEN * ROW;  // 16 KiB
+
+// fp32 tile in LDS: 16 chunks of 16 B per row; chunk c of row r sits at
+// position c ^ (r mod 16), so 16 consecutive rows read at one chunk, and one
+// row read as 4 consecutive chunks by 4 rows 4 apart, hit distinct banks.
+__device__ __forceinline__ int f32_swz(int row, int chunk) { return row * 16 + (chunk ^ (row & 15)); }
+
+__device__ __forceinline__ f32x4 mfma16x16x4(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+// op over lanes {l, l^16, l^32, l^48}.
+__device__ __forceinline__ float quad_max_f(float x) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return half_swap_max(max2(__uint_as_float(r[0]), __uint_as_float(r[1])));
+}
+__device__ __forceinline__ float quad_sum_f(float x) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return half_swap_sum(__uint_as_float(r[0]) + __uint_as_float(r[1]));
+}
+
+__global__ __launch_bounds__(NT) void sdpa_short_f32(
+    const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
+    float* __restrict__ O, int H, int n, int m, float c_log2, int causal,
+    const int32_t* __restrict__ key_lens) {
+    // K tile at 0, Q at 16 KiB, V at 32 KiB.
+    __shared__ __attribute__((aligned(16))) char lds[3 * TILE];
+    const f32x4* sK = reinterpret_cast<const f32x4*>(lds);
+    const f32x4* sQ = reinterpret_cast<const f32x4*>(lds + TILE);
+    const float* sV = reinterpret_cast<const float*>(lds + 2 * TILE);
+
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int l16 = lane & 15;
+    const int G = lane >> 4;
+
+    const int bh = blockIdx.x;
+    const int b = bh / H;
+    const size_t qbase = (size_t)bh * n * D;
+    const size_t kvbase = (size_t)bh * m * D;
+
+    // Wave w moves tile rows 4·(4w + i) .. +3 (i = 0..3) of each tensor: one
+    // 1 KiB load each; lane ln lands in LDS slot (row ln/16, position ln%16),
+    // which holds logical chunk (ln%16) ^ (row mod 16).
+    int ld_off[4], ld_lds[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = 4 * (4 * w + i) + (lane >> 4);
+        ld_off[i] = row * ROW + ((lane & 15) ^ (row & 15)) * 16;
+        ld_lds[i] = 4 * (4 * w + i) * ROW;
+    }
+    const i32x4 rk = make_rsrc(K + kvbase, (uint32_t)(m * ROW));
+    const i32x4 rq = make_rsrc(Q + qbase, (uint32_t)(n * ROW));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) load16_to_lds(rk, lds + ld_lds[i], ld_off[i]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) load16_to_lds(rq, lds + TILE + ld_lds[i], ld_off[i]);
+    int L = m;
+    if (key_lens) {
+        const int t = key_lens[b];
+        L = t < 0 ? 0 : (t > m ? m : t);
+    }
+    const i32x4 rv = make_rsrc(V + kvbase, (uint32_t)(L * ROW));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) load16_to_lds(rv, lds + 2 * TILE + ld_lds[i], ld_off[i]);
+    asm volatile("s_waitcnt vmcnt(4)" ::: "memory");  // K and Q in; V may still fly
+    lds_barrier();
+
+    const int q = w * QW + l16;
+    const int wq_last = w * QW + QW - 1;
+    // Key tiles with any legal key for this wave: below the key length and
+    // (causal) not after the wave's last query.
+    int nkt = (L + 15) >> 4;
+    if (causal) nkt = min(nkt, (wq_last >> 4) + 1);
+    const bool active = w * QW < n;
+
+    // Qᵀ operand: d = 16·G + ks for k-step ks, i.e. Q[q][16G .. 16G+15].
+    float qop[16];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const f32x4 x = sQ[f32_swz(q, 4 * G + j)];
+        qop[4 * j + 0] = x[0]; qop[4 * j + 1] = x[1]; qop[4 * j + 2] = x[2]; qop[4 * j + 3] = x[3];
+    }
+
+    // Sᵀ tiles; register r of tile kt is key 16·kt + 4·G + r of query q.
+    f32x4 s[4];
+    float l = 0.f;
+    if (active) {
+        // Key tiles in pairs (a tile of a pair past nkt is masked out below):
+        // four independent accumulation chains keep the matrix pipe busy.
+#pragma unroll
+        for (int kp = 0; kp < 2; ++kp) {
+            s[2 * kp] = s[2 * kp + 1] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+            if (2 * kp < nkt) {  // uniform
+                f32x4 acc[2][2];
+#pragma unroll
+                for (int u = 0; u < 2; ++u) acc[u][0] = acc[u][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) {
+                        const f32x4 a = sK[f32_swz(16 * (2 * kp + u) + l16, 4 * G + j)];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            acc[u][j & 1] = mfma16x16x4(a[e], qop[4 * j + e], acc[u][j & 1]);
+                    }
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int kt = 2 * kp + u;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int key = 16 * kt + 4 * G + r;
+                        const float x = acc[u][0][r] + acc[u][1][r];
+                        s[kt][r] = (key < L && !(causal && key > q)) ? x : -INFINITY;
+                    }
+                }
+            }
+        }
+        float mx = max3(max3(s[0][0], s[0][1], s[0][2]), max3(s[0][3], s[1][0], s[1][1]),
+                        max3(s[1][2], s[1][3], s[2][0]));
+        mx = max3(mx, max3(s[2][1], s[2][2], s[2][3]), max3(s[3][0], s[3][1], s[3][2]));
+        mx = quad_max_f(max2(mx, s[3][3]));
+        const float mc = (mx == -INFINITY ? 0.f : mx) * c_log2;  // no (−∞) − (−∞)
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float p = exp2_hw(__builtin_fmaf(s[kt][r], c_log2, -mc));
+                s[kt][r] = p;
+                l += p;
+            }
+        l = quad_sum_f(l);
+    }
+    wait_vmem();  // V in
+    lds_barrier();
+    if (!active) return;
+
+    // Oᵀ += Vᵀ · Pᵀ; register r of o[dt] is dv = 16·dt + 4·G + r of query q.
+    f32x4 o[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+        if (kt >= nkt) continue;  // uniform; these weights are all zero
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int vrow = 16 * kt + 4 * G + r;
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) {
+                const int dv = 16 * dt + l16;
+                const float a = sV[f32_swz(vrow, dv >> 2) * 4 + (dv & 3)];
+                o[dt] = mfma16x16x4(a, s[kt][r], o[dt]);
+            }
+        }
+    }
+
+    if (q < n) {
+        float* dst = O + qbase + (size_t)q * D;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+            f32x4 ov;
+            // true division keeps the fp32 path within a few ulp of the exact result
+            ov[0] = l > 0.f ? o[dt][0] / l : 0.f;  // no legal key ⇒ zero row
+            ov[1] = l > 0.f ? o[dt][1] / l : 0.f;
+            ov[2] = l > 0.f ? o[dt][2] / l : 0.f;
+            ov[3] = l > 0.f ? o[dt][3] / l : 0.f;
+            *reinterpret_cast<f32x4*>(dst + 16 * dt + 4 * G) = ov;
+        }
+    }
+}
+
+}  // namespace
+
+bool short_f32_fits(const Args& a) { return a.n <= MAXLEN && a.m <= MAXLEN; }
+
+hipError_t launch_f32_short(const Args& a, hipStream_t stream) {
+    const float c_log2 = (float)((double)a.scale * 1.4426950408889634);  // scale·log2(e)
+    hipLaunchKernelGGL(sdpa_short_f32, dim3(a.B * a.H), dim3(NT), 0, stream,
+                       (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.out,
+                       a.H, a.n, a.m, c_log2, a.causal, a.key_lens);
+    return hipGetLastError();
+}
+
+}  // namespace sdpa
