@@ -11,11 +11,13 @@
 //     tile, so the softmax is an exact two-pass one with no running rescale;
 //   * four waves of 16 queries each on v_mfma_f32_16x16x32_bf16, so each wave's
 //     serial MFMA/softmax chain is a quarter of a head;
-//   * Q, K and V move HBM → LDS with buffer_load_dwordx4 … lds; Q and K are
-//     issued before the key length is even known (K rows past it only yield
-//     scores the mask discards), V right after it, with its buffer range ending
-//     at the key length so padded V rows are never read; the scores and the
-//     softmax run while V is still in flight;
+//   * Q, K and V move HBM → LDS with buffer_load_dwordx4 … lds; Q is issued
+//     before the key length is known, K and V right after it with their buffer
+//     range ending at the key length, so padded rows are never read (they
+//     arrive as zeros); the scores and the softmax run while V is in flight;
+//   * key tiles of 16 wholly past the key length (or, causal, past the wave's
+//     queries) are skipped in both products, and only tiles that straddle the
+//     padding edge or the diagonal are masked;
 //   * Sᵀ = K·Qᵀ and Oᵀ = Vᵀ·Pᵀ (transposed, as in the long kernel) so the row
 //     max/sum are lane-local plus two half/quarter-wave exchanges, and Vᵀ comes
 //     from LDS transpose reads (ds_read_b64_tr_b16).
@@ -85,16 +87,12 @@ __global__ __launch_bounds__(NT) void sdpa_short_bf16(
         ld_off[i] = row * 128 + ((lane & 7) ^ swz_f(row)) * 16;
         ld_lds[i] = 8 * (2 * w + i) * 128;
     }
-    // K and Q go first, without waiting for the key length: K rows past it
-    // only produce scores that the mask discards, and rows past m or n arrive
-    // as zeros (buffer range).  Then the key length, then V, whose buffer range
-    // stops at it, so its padded rows arrive as zeros without being read (they
-    // meet weight 0 in P·V, and 0 · garbage must not happen).  The scores and
-    // the softmax run while V is still in flight.
-    const i32x4 rk = make_rsrc(K + kvbase, (uint32_t)(m * D * 2));
+    // Q goes first, without waiting for the key length.  Then the key length,
+    // then K and V, whose buffer ranges stop at it: their padded rows arrive as
+    // zeros without being read (a zero K row only gives a score the mask
+    // discards; a zero V row meets weight 0 in P·V, and 0 · garbage must not
+    // happen).  The scores and the softmax run while V is still in flight.
     const i32x4 rq = make_rsrc(Q + qbase, (uint32_t)(n * D * 2));
-    load16_to_lds(rk, lds + ld_lds[0], ld_off[0]);
-    load16_to_lds(rk, lds + ld_lds[1], ld_off[1]);
     load16_to_lds(rq, lds + MAXLEN * 128 + ld_lds[0], ld_off[0]);
     load16_to_lds(rq, lds + MAXLEN * 128 + ld_lds[1], ld_off[1]);
     int L = m;
@@ -102,10 +100,13 @@ __global__ __launch_bounds__(NT) void sdpa_short_bf16(
         const int t = key_lens[b];
         L = t < 0 ? 0 : (t > m ? m : t);
     }
+    const i32x4 rk = make_rsrc(K + kvbase, (uint32_t)(L * D * 2));
+    load16_to_lds(rk, lds + ld_lds[0], ld_off[0]);
+    load16_to_lds(rk, lds + ld_lds[1], ld_off[1]);
     const i32x4 rv = make_rsrc(V + kvbase, (uint32_t)(L * D * 2));
     load16_to_lds(rv, lds + 2 * MAXLEN * 128 + ld_lds[0], ld_off[0]);
     load16_to_lds(rv, lds + 2 * MAXLEN * 128 + ld_lds[1], ld_off[1]);
-    asm volatile("s_waitcnt vmcnt(2)" ::: "memory");  // K and Q in; V may still fly
+    asm volatile("s_waitcnt vmcnt(2)" ::: "memory");  // Q and K in; V may still fly
     lds_barrier();
     const bool active = w * QW < n;  // this wave has queries (n < 64 leaves some idle)
 
@@ -115,45 +116,55 @@ __global__ __launch_bounds__(NT) void sdpa_short_bf16(
     qop[0] = __builtin_bit_cast(bf16x8, sQ[swz(q, G)]);
     qop[1] = __builtin_bit_cast(bf16x8, sQ[swz(q, 4 + G)]);
 
-    // Sᵀ = K · Qᵀ: four 16-key tiles; register r of tile kt is key 16·kt + 4·G + r.
+    // Key tiles with any legal key for this wave: below the key length and
+    // (causal) not after the wave's last query (tile w holds its diagonal).
+    int nkt = (L + 15) >> 4;
+    if (causal) nkt = min(nkt, w + 1);
+    // Legal keys of this lane's query: key < lim.  Register r of tile kt is key
+    // 16·kt + 4·G + r, so the test is 16·kt + r < lim − 4·G.
+    const int lim = (causal ? min(L, q + 1) : L) - 4 * G;
+
+    // Sᵀ = K · Qᵀ: register r of tile kt is key 16·kt + 4·G + r.
     f32x4 s[4];
     bf16x8 pb[2];
     float l = 0.f;
     if (active) {
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-        s[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const int krow = 16 * kt + l16;
+        for (int kt = 0; kt < 4; ++kt) {
+            s[kt] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+            if (kt < nkt) {  // uniform
+                const int krow = 16 * kt + l16;
+                f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const bf16x8 a = __builtin_bit_cast(bf16x8, sK[swz(krow, 4 * ks + G)]);
-            s[kt] = mfma16(a, qop[ks], s[kt]);
+                for (int ks = 0; ks < 2; ++ks) {
+                    const bf16x8 a = __builtin_bit_cast(bf16x8, sK[swz(krow, 4 * ks + G)]);
+                    acc = mfma16(a, qop[ks], acc);
+                }
+                if (16 * kt + 16 > L || (causal && kt == w)) {  // uniform: tile has illegal keys
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) acc[r] = (16 * kt + r < lim) ? acc[r] : -INFINITY;
+                }
+                s[kt] = acc;
+            }
         }
-    }
-    float mx = -INFINITY;
+        float mx = max3(max3(s[0][0], s[0][1], s[0][2]), max3(s[0][3], s[1][0], s[1][1]),
+                        max3(s[1][2], s[1][3], s[2][0]));
+        mx = max3(mx, max3(s[2][1], s[2][2], s[2][3]), max3(s[3][0], s[3][1], s[3][2]));
+        mx = quad_max(max2(mx, s[3][3]));
+        const float mc = (mx == -INFINITY ? 0.f : mx) * c_log2;  // no (−∞) − (−∞)
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+        for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int key = 16 * kt + 4 * G + r;
-            if (key >= L || (causal && key > q)) s[kt][r] = -INFINITY;
-            mx = max2(mx, s[kt][r]);
-        }
-    mx = quad_max(mx);
-    const float mc = (mx == -INFINITY ? 0.f : mx) * c_log2;  // no (−∞) − (−∞)
+            for (int r = 0; r < 4; ++r) {
+                const float p = kt < nkt ? exp2_hw(__builtin_fmaf(s[kt][r], c_log2, -mc)) : 0.f;
+                s[kt][r] = p;
+                l += p;
+            }
+        l = quad_sum(l);
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float p = exp2_hw(__builtin_fmaf(s[kt][r], c_log2, -mc));
-            s[kt][r] = p;
-            l += p;
-        }
-    l = quad_sum(l);
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-        pb[j] = to_bf16x8(s[2 * j][0], s[2 * j][1], s[2 * j][2], s[2 * j][3],
-                          s[2 * j + 1][0], s[2 * j + 1][1], s[2 * j + 1][2], s[2 * j + 1][3]);
+        for (int j = 0; j < 2; ++j)
+            pb[j] = to_bf16x8(s[2 * j][0], s[2 * j][1], s[2 * j][2], s[2 * j][3],
+                              s[2 * j + 1][0], s[2 * j + 1][1], s[2 * j + 1][2], s[2 * j + 1][3]);
     }
     wait_vmem();  // V in
     lds_barrier();
@@ -168,6 +179,7 @@ __global__ __launch_bounds__(NT) void sdpa_short_bf16(
     const char* vb = sVb;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
+        if (2 * j >= nkt) continue;  // uniform: all these weights are zero
         const int r0 = 32 * j + 4 * G + (l16 >> 2);
         const int r1 = r0 + 16;
 #pragma unroll
@@ -181,10 +193,12 @@ __global__ __launch_bounds__(NT) void sdpa_short_bf16(
         }
     }
 
-    // Register r of o[dt] is dv = 16·dt + 4·G + r of query q.
-    if (q < n) {
-        const float inv = l > 0.f ? 1.f / l : 0.f;  // no legal key ⇒ zero row
-        uint16_t* dst = O + qbase + (size_t)q * D;
+    // Register r of o[dt] is dv = 16·dt + 4·G + r of query q.  The wave's 16
+    // output rows go through its own 2 KiB of the (now free) K tile so that
+    // every store instruction writes whole 128-byte rows, 16 bytes a lane.
+    {
+        const float inv = l > 0.f ? __builtin_amdgcn_rcpf(l) : 0.f;  // no legal key ⇒ zero row
+        char* ob = lds + w * QW * 128;
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
             bf16x4 ov;
@@ -192,7 +206,15 @@ __global__ __launch_bounds__(NT) void sdpa_short_bf16(
             ov[1] = (__bf16)(o[dt][1] * inv);
             ov[2] = (__bf16)(o[dt][2] * inv);
             ov[3] = (__bf16)(o[dt][3] * inv);
-            *reinterpret_cast<bf16x4*>(dst + 16 * dt + 4 * G) = ov;
+            *reinterpret_cast<bf16x4*>(ob + swz(l16, 2 * dt + (G >> 1)) * 16 + (G & 1) * 8) = ov;
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int row = 8 * i + (lane >> 3);
+            const int qq = w * QW + row;
+            const u32x4 x = *reinterpret_cast<const u32x4*>(ob + swz(row, lane & 7) * 16);
+            if (qq < n) *reinterpret_cast<u32x4*>(O + qbase + (size_t)qq * D + 8 * (lane & 7)) = x;
         }
     }
 }

@@ -9,12 +9,12 @@
 //
 // Built like the bf16 sentence-length kernel: one workgroup per (batch, head),
 // four waves of 16 queries, the whole head (≤ 64 keys) as one tile so the
-// softmax is an exact two-pass one.  Q and K move HBM → LDS (buffer_load …
-// lds) before the key length is known (K rows past it only give scores the
-// mask discards), V right after it with its buffer range ending at the key
-// length (padded V rows are never read), and the scores and softmax run while
-// V is in flight.  Key tiles of 16 wholly past the key length (or, causal,
-// past a wave's queries) are skipped.
+// softmax is an exact two-pass one.  Q moves HBM → LDS (buffer_load … lds)
+// before the key length is known, K and V right after it with their buffer
+// ranges ending at the key length (padded rows are never read and arrive as
+// zeros), and the scores and softmax run while V is in flight.  Key tiles of
+// 16 wholly past the key length (or, causal, past a wave's queries) are
+// skipped.
 //
 // Products, transposed as elsewhere (each lane owns one query column):
 //   Sᵀ (16 keys × 16 queries) = K · Qᵀ, 16 k-steps of 4; in k-step ks the
@@ -86,10 +86,7 @@ __global__ __launch_bounds__(NT) void sdpa_short_f32(
         ld_off[i] = row * ROW + ((lane & 15) ^ (row & 15)) * 16;
         ld_lds[i] = 4 * (4 * w + i) * ROW;
     }
-    const i32x4 rk = make_rsrc(K + kvbase, (uint32_t)(m * ROW));
     const i32x4 rq = make_rsrc(Q + qbase, (uint32_t)(n * ROW));
-#pragma unroll
-    for (int i = 0; i < 4; ++i) load16_to_lds(rk, lds + ld_lds[i], ld_off[i]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) load16_to_lds(rq, lds + TILE + ld_lds[i], ld_off[i]);
     int L = m;
@@ -97,10 +94,13 @@ __global__ __launch_bounds__(NT) void sdpa_short_f32(
         const int t = key_lens[b];
         L = t < 0 ? 0 : (t > m ? m : t);
     }
+    const i32x4 rk = make_rsrc(K + kvbase, (uint32_t)(L * ROW));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) load16_to_lds(rk, lds + ld_lds[i], ld_off[i]);
     const i32x4 rv = make_rsrc(V + kvbase, (uint32_t)(L * ROW));
 #pragma unroll
     for (int i = 0; i < 4; ++i) load16_to_lds(rv, lds + 2 * TILE + ld_lds[i], ld_off[i]);
-    asm volatile("s_waitcnt vmcnt(4)" ::: "memory");  // K and Q in; V may still fly
+    asm volatile("s_waitcnt vmcnt(4)" ::: "memory");  // Q and K in; V may still fly
     lds_barrier();
 
     const int q = w * QW + l16;
