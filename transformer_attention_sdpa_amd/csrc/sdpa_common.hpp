@@ -112,6 +112,18 @@ extern "C" __device__ void sdpa_llvm_buffer_load_lds(i32x4 rsrc, __attribute__((
 __device__ __forceinline__ void load16_to_lds(i32x4 rsrc, void* lds, int voffset) {
     sdpa_llvm_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds, 16, voffset, 0, 0, 0);
 }
+// Same with the non-temporal (streaming) hint, for data that is read exactly
+// once: it does not linger in the caches, and a short kernel then ends sooner
+// (measured on the sentence-length kernels).
+constexpr int kCachePolicyNT = 2;
+__device__ __forceinline__ void load16_to_lds_nt(i32x4 rsrc, void* lds, int voffset) {
+    sdpa_llvm_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds, 16, voffset, 0, 0,
+                              kCachePolicyNT);
+}
+// 16-byte global store with the non-temporal hint (outputs are written once).
+__device__ __forceinline__ void store16_nt(void* p, u32x4 x) {
+    __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(p));
+}
 // buffer_load_dwordx4 into VGPRs; offsets at or past the descriptor's range
 // read as zeros.
 extern "C" __device__ i32x4 sdpa_llvm_buffer_load_v4i32(i32x4 rsrc, int voffset, int soffset,

@@ -88,7 +88,7 @@ __global__ __launch_bounds__(NT) void sdpa_short_f32(
     }
     const i32x4 rq = make_rsrc(Q + qbase, (uint32_t)(n * ROW));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) load16_to_lds(rq, lds + TILE + ld_lds[i], ld_off[i]);
+    for (int i = 0; i < 4; ++i) load16_to_lds_nt(rq, lds + TILE + ld_lds[i], ld_off[i]);
     int L = m;
     if (key_lens) {
         const int t = key_lens[b];
@@ -96,10 +96,10 @@ __global__ __launch_bounds__(NT) void sdpa_short_f32(
     }
     const i32x4 rk = make_rsrc(K + kvbase, (uint32_t)(L * ROW));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) load16_to_lds(rk, lds + ld_lds[i], ld_off[i]);
+    for (int i = 0; i < 4; ++i) load16_to_lds_nt(rk, lds + ld_lds[i], ld_off[i]);
     const i32x4 rv = make_rsrc(V + kvbase, (uint32_t)(L * ROW));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) load16_to_lds(rv, lds + 2 * TILE + ld_lds[i], ld_off[i]);
+    for (int i = 0; i < 4; ++i) load16_to_lds_nt(rv, lds + 2 * TILE + ld_lds[i], ld_off[i]);
     asm volatile("s_waitcnt vmcnt(4)" ::: "memory");  // Q and K in; V may still fly
     lds_barrier();
 
@@ -201,7 +201,7 @@ __global__ __launch_bounds__(NT) void sdpa_short_f32(
             ov[1] = l > 0.f ? o[dt][1] / l : 0.f;
             ov[2] = l > 0.f ? o[dt][2] / l : 0.f;
             ov[3] = l > 0.f ? o[dt][3] / l : 0.f;
-            *reinterpret_cast<f32x4*>(dst + 16 * dt + 4 * G) = ov;
+            store16_nt(dst + 16 * dt + 4 * G, __builtin_bit_cast(u32x4, ov));
         }
     }
 }
