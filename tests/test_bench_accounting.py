@@ -1,0 +1,56 @@
+"""The throughput accounting of bench.py, checked on the CPU.
+
+The metric counts 4·d FLOPs per legal (query, key) pair and the HBM bytes of
+Q, O and the legal K/V rows.  Here the closed forms in ``bench.algorithmic_work``
+are compared with a brute-force count of the legal pairs taken from the
+oracle's own visibility rule, for every workload shape (the 8k case on a
+reduced batch, the count being per head).
+"""
+
+import dataclasses
+
+import numpy as np
+import pytest
+
+import bench
+import oracle.sdpa_oracle as so
+from sdpa_inputs import WORKLOADS, make_inputs
+
+
+def _brute(wl, key_lens):
+    pairs = 0
+    kv_rows = 0
+    for b in range(wl.B):
+        kl = None if key_lens is None else int(key_lens[b])
+        vis = so.visible_keys(np.arange(wl.n), wl.m, wl.causal, kl)
+        pairs += wl.h * int(vis.sum())
+        L = wl.m if kl is None else min(max(kl, 0), wl.m)
+        kv_rows += wl.h * L
+    return pairs, kv_rows
+
+
+@pytest.mark.parametrize("name", sorted(WORKLOADS))
+def test_algorithmic_work_matches_brute_force(name):
+    wl = WORKLOADS[name]
+    if wl.n * wl.m > 1 << 20:  # the 8k case: one head is enough, the count is per head
+        wl = dataclasses.replace(wl, B=1, h=1)
+        key_lens = None
+    else:
+        key_lens = make_inputs(wl, wl.dtypes[0])["key_lens"]
+    for dt, esz in (("bf16", 2), ("f32", 4)):
+        flops, nbytes, dense = bench.algorithmic_work(wl, dt, key_lens)
+        pairs, kv_rows = _brute(wl, key_lens)
+        d = wl.d_k
+        assert flops == 2 * (wl.d_k + wl.d_v) * pairs == 4 * d * pairs
+        assert dense == 4 * d * wl.B * wl.h * wl.n * wl.m
+        assert nbytes == esz * (2 * wl.B * wl.h * wl.n * d + 2 * kv_rows * d)
+
+
+def test_key_length_edge_cases():
+    wl = dataclasses.replace(WORKLOADS["decoder_causal_base"], B=4, h=2)
+    kl = np.array([0, 1, 64, 99], dtype=np.int32)  # empty, one key, full, beyond m
+    flops, nbytes, _ = bench.algorithmic_work(wl, "bf16", kl)
+    pairs, kv_rows = _brute(wl, kl)
+    assert flops == 4 * 64 * pairs
+    assert kv_rows == 2 * (0 + 1 + 64 + 64)
+    assert nbytes == 2 * (2 * 4 * 2 * 64 * 64 + 2 * kv_rows * 64)
