@@ -70,9 +70,10 @@ def algorithmic_work(wl, dtype, key_lens):
 
 
 def kernel_source_hash() -> str:
+    """Hash of the device-code sources (the kernels whose traffic is measured)."""
     h = hashlib.sha256()
     for name in sorted(os.listdir(CSRC)):
-        if name.endswith((".hip", ".hpp", ".cpp", ".h")):
+        if name.endswith((".hip", ".hpp")):
             with open(os.path.join(CSRC, name), "rb") as f:
                 h.update(name.encode() + f.read())
     return h.hexdigest()[:16]

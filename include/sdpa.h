@@ -43,7 +43,7 @@ extern "C" {
 #define SDPA_ERR_DTYPE       -6 /* unknown dtype                                     */
 #define SDPA_ERR_LAUNCH      -7 /* the HIP runtime refused the kernel launch         */
 #define SDPA_ERR_SCALE       -8 /* scale is not finite, or not > 0                   */
-#define SDPA_ERR_ALIAS       -9 /* out overlaps q, k or v                            */
+#define SDPA_ERR_ALIAS       -9 /* out overlaps q, k, v or key_lens                   */
 
 /* Element types (input and output share one type). */
 #define SDPA_F32  0 /* fp32 in, fp32 arithmetic, fp32 out                          */
@@ -60,7 +60,7 @@ extern "C" {
  * k        device pointer, [B, h, m, d_k], contiguous.
  * v        device pointer, [B, h, m, d_v], contiguous.
  * out      device pointer, [B, h, n, d_v], contiguous; written completely (rows
- *          with no legal key are written as zeros).  Must not overlap q, k, v.
+ *          with no legal key are written as zeros).  Must not overlap q, k, v, key_lens.
  * B, h     batch size and number of heads (>= 1).
  * n, m     number of queries and of keys/values per head (>= 1).
  * d_k, d_v query/key and value widths; this build supports d_k == d_v == 64.

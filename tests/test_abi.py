@@ -81,6 +81,7 @@ def call(q=P, k=2 * P, v=3 * P, out=4 * P, B=2, h=2, n=8, m=8, d_k=64, d_v=64, s
     (dict(scale=-0.125), _lib.SDPA_ERR_SCALE),
     (dict(out=P), _lib.SDPA_ERR_ALIAS),
     (dict(out=3 * P + 1024), _lib.SDPA_ERR_ALIAS),
+    (dict(key_lens=4 * P + 64), _lib.SDPA_ERR_ALIAS),
 ])
 def test_validation_rejects_before_any_hip_call(kw, code):
     assert call(**kw) == code

@@ -32,6 +32,8 @@ def forward(q, k, v, *, causal: bool = False, key_lens=None, scale: float | None
         raise ValueError("q, k, v must be 4-D [B, h, len, d]")
     if not (q.is_cuda and k.is_cuda and v.is_cuda):
         raise ValueError("q, k, v must be GPU tensors")
+    if k.device != q.device or v.device != q.device:
+        raise ValueError("q, k, v must be on one device")
     if q.dtype != k.dtype or q.dtype != v.dtype:
         raise ValueError("q, k, v must share one dtype")
     if q.dtype == torch.float32:
@@ -55,14 +57,18 @@ def forward(q, k, v, *, causal: bool = False, key_lens=None, scale: float | None
         kl_ptr = key_lens.data_ptr()
     if out is None:
         out = torch.empty((B, h, n, d_v), dtype=q.dtype, device=q.device)
-    elif tuple(out.shape) != (B, h, n, d_v) or out.dtype != q.dtype or not out.is_contiguous():
-        raise ValueError("out must be a contiguous [B, h, n, d_v] tensor of q's dtype")
+    elif (tuple(out.shape) != (B, h, n, d_v) or out.dtype != q.dtype or not out.is_contiguous()
+          or out.device != q.device):
+        raise ValueError("out must be a contiguous [B, h, n, d_v] tensor of q's dtype on q's device")
     if scale is None:
         scale = 1.0 / math.sqrt(d_k)
-    stream = torch.cuda.current_stream(q.device).cuda_stream
-    rc = sdpa_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, h, n, m,
-                      d_k, d_v, float(scale), _lib.SDPA_MASK_CAUSAL if causal else _lib.SDPA_MASK_NONE,
-                      kl_ptr, dt, stream)
+    # The library launches on the calling thread's current HIP device.
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        rc = sdpa_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, h, n, m,
+                          d_k, d_v, float(scale),
+                          _lib.SDPA_MASK_CAUSAL if causal else _lib.SDPA_MASK_NONE, kl_ptr, dt,
+                          stream)
     if rc != _lib.SDPA_OK:
         raise RuntimeError(f"sdpa_forward failed ({rc}): {sdpa_strerror(rc)}")
     return out

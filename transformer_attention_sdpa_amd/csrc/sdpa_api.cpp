@@ -46,6 +46,7 @@ int validate(const void* q, const void* k, const void* v, void* out, int32_t B, 
     const uint64_t vb = heads * m * d_v * esz, ob = heads * n * d_v * esz;
     if (overlap(out, ob, q, qb) || overlap(out, ob, k, kb) || overlap(out, ob, v, vb))
         return SDPA_ERR_ALIAS;
+    if (key_lens && overlap(out, ob, key_lens, (uint64_t)B * sizeof(int32_t))) return SDPA_ERR_ALIAS;
     return SDPA_OK;
 }
 
@@ -74,7 +75,7 @@ extern "C" const char* sdpa_strerror(int status) {
         case SDPA_ERR_DTYPE: return "unknown dtype (SDPA_F32 = 0, SDPA_BF16 = 1)";
         case SDPA_ERR_LAUNCH: return "the HIP runtime refused the kernel launch";
         case SDPA_ERR_SCALE: return "scale must be finite and > 0";
-        case SDPA_ERR_ALIAS: return "out overlaps q, k or v";
+        case SDPA_ERR_ALIAS: return "out overlaps q, k, v or key_lens";
         default: return "unknown status";
     }
 }
