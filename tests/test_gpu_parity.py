@@ -115,6 +115,13 @@ RAGGED = [
     (1, 1, 200, 200, True, False),
     (1, 2, 300, 517, False, True),
     (1, 1, 513, 513, True, True),
+    # sentence-length kernels at and around their 64-row limit, every mask kind
+    (3, 2, 40, 40, True, True),
+    (2, 2, 64, 64, True, True),
+    (2, 2, 64, 63, False, True),
+    (1, 3, 17, 64, False, True),
+    (2, 1, 65, 64, False, True),
+    (1, 2, 64, 65, False, False),
 ]
 
 
