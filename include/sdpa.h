@@ -70,10 +70,9 @@ extern "C" {
  * key_lens NULL for no key padding, else a DEVICE pointer to int32[B]: key j of
  *          batch element b is legal only if j < clamp(key_lens[b], 0, m).  It
  *          applies to every head of b and to keys only; query rows are never
- *          masked.  K and V rows at j >= key_lens[b] may hold anything (also
- *          NaN): V rows there are never read, and K rows there are at most read
- *          into scores that the mask discards.  Causally hidden keys are read
- *          and must be finite.
+ *          masked.  K and V rows at j >= key_lens[b] are never read and may
+ *          hold anything (also NaN).  Causally hidden keys are read and must be
+ *          finite.
  * dtype    SDPA_F32 or SDPA_BF16.
  * stream   a hipStream_t (as void*; NULL = the default stream).
  *
