@@ -95,3 +95,15 @@ def test_torch_wrapper_rejects_cpu_tensors():
     x = torch.zeros(1, 1, 4, 64)
     with pytest.raises(ValueError):
         forward(x, x, x)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """No fallback: without libsdpa.so every entry point of the binding raises."""
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "libsdpa.so"))
+    with pytest.raises(ImportError):
+        _lib.load()
+    with pytest.raises(ImportError):
+        _lib.sdpa_version()
+    with pytest.raises(ImportError):
+        call()

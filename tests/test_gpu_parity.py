@@ -273,3 +273,39 @@ def test_wrapper_errors(gpu_lib):
     q32 = torch.zeros(1, 1, 4, 32, device="cuda", dtype=torch.bfloat16)
     with pytest.raises(RuntimeError, match="64"):
         forward(q32, q32, q32)
+
+
+def test_concurrent_calls_on_separate_streams(gpu_lib):
+    """The library keeps no state: calls from several host threads, each on its
+    own stream, give the same bits as one call at a time."""
+    import threading
+
+    import torch
+
+    rng = np.random.default_rng(31)
+    cases = [random_case(rng, 4, 2, n, n, 64, 64, dtype="bf16", causal=c, key_lens=kl)
+             for n, c, kl in ((64, False, [9, 64, 30, 1]), (200, True, None), (48, False, None),
+                              (130, False, [100, 7, 130, 64]))]
+    solo = [run_gpu(c)[1] for c in cases]
+    results = [None] * len(cases)
+    errors = []
+
+    def worker(i):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                for _ in range(5):
+                    _, got = run_gpu(cases[i])
+            s.synchronize()
+            results[i] = got
+        except Exception as e:  # surfaced below
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(len(cases))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    for a, b in zip(solo, results):
+        assert np.array_equal(a, b)
