@@ -296,6 +296,40 @@ def cpu_baseline(name, dtype, budget_s=10.0):
                       f"{reps} passes in {el:.1f} s, {per * 1e3:.1f} ms per pass"}
 
 
+def oracle_pass(name, dtype, max_s=2.0):
+    """The oracle on one workload, single BLAS thread: a whole batch when it is
+    small, else a seeded sample of output rows (cost counted per legal pair)."""
+    import numpy as np
+
+    import oracle.sdpa_oracle as so
+    from threadpoolctl import threadpool_limits
+
+    wl = WORKLOADS[name]
+    case = make_inputs(wl, dtype)
+    with threadpool_limits(limits=1):
+        if wl.n * wl.m <= 64 * 64:
+            flops, _, _ = algorithmic_work(wl, dtype, case["key_lens"])
+            t0 = time.perf_counter()
+            so.attention(case["q"], case["k"], case["v"], causal=wl.causal,
+                         key_lens=case["key_lens"])
+            el = time.perf_counter() - t0
+            return {"tflops": flops / el / 1e12, "ms_per_pass": el * 1e3, "sample": "whole batch"}
+        rng = np.random.default_rng(7)
+        picks, pairs = [], 0
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < max_s and len(picks) < 4096:
+            b, hh, i = int(rng.integers(wl.B)), int(rng.integers(wl.h)), int(rng.integers(wl.n))
+            so.attention_rows(case["q"], case["k"], case["v"], [(b, hh, i)], causal=wl.causal,
+                              key_lens=case["key_lens"])
+            picks.append((b, hh, i))
+            pairs += (i + 1) if wl.causal else wl.m
+        el = time.perf_counter() - t0
+        flops_s = 2 * (wl.d_k + wl.d_v) * pairs / el
+        full, _, _ = algorithmic_work(wl, dtype, case["key_lens"])
+        return {"tflops": flops_s / 1e12, "ms_per_pass": full / flops_s * 1e3,
+                "sample": f"{len(picks)} random output rows in {el:.1f} s; ms_per_pass extrapolated"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -349,6 +383,8 @@ def main():
             extra[f"{name}-{dt}"] = {k: r[k] for k in (
                 "ms_per_step", "tflops", "gbs", "frac_mfma_peak", "frac_hbm_peak", "steps",
                 "sets_rotated", "ms_per_step_eager")}
+            if not args.no_cpu_baseline:
+                extra[f"{name}-{dt}"]["cpu_oracle_1core"] = oracle_pass(name, dt)
 
     bound = "mfma" if head["alg_flops"] / head["alg_bytes"] > PEAK_TFLOPS[args.dtype] * 1e12 / (PEAK_HBM_GBS * 1e9) else "hbm"
     if bound == "hbm":
