@@ -309,3 +309,36 @@ def test_concurrent_calls_on_separate_streams(gpu_lib):
     assert not errors, errors
     for a, b in zip(solo, results):
         assert np.array_equal(a, b)
+
+
+# --- larger-than-benchmark sizes, checked on sampled rows --------------------
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_many_heads_sentence_length_sampled(gpu_lib, dt):
+    """8192 heads of 64×64 (a 16× larger batch than the encoder workload)."""
+    rng = np.random.default_rng(4242)
+    B, h, n = 1024, 8, 64
+    kl = rng.integers(0, n + 1, size=B)
+    case = random_case(rng, B, h, n, n, 64, 64, dtype=dt, causal=False, key_lens=kl)
+    _, got = run_gpu(case)
+    picks = [(int(rng.integers(B)), int(rng.integers(h)), int(rng.integers(n))) for _ in range(300)]
+    picks += [(B - 1, h - 1, n - 1), (0, 0, 0)]
+    ref = so.attention_rows(case["q"], case["k"], case["v"], picks, key_lens=case["key_lens"])
+    g = np.stack([got[b, hh, i] for (b, hh, i) in picks])
+    assert max_abs_err(g, ref) <= TOL[dt]
+    # rows of sequences with key length 0 are exactly zero
+    for b in np.flatnonzero(case["key_lens"] == 0)[:4]:
+        assert not got[b].any()
+
+
+def test_long_causal_16k_sampled(gpu_lib):
+    """n = m = 16384, causal, bf16: twice the benchmark length."""
+    rng = np.random.default_rng(16384)
+    n = 16384
+    case = random_case(rng, 1, 2, n, n, 64, 64, dtype="bf16", causal=True)
+    _, got = run_gpu(case)
+    rows = [0, 1, 63, 64, 255, 256, 4095, 8191, 8192, 12345, 16319, 16320, 16383]
+    picks = [(0, hh, i) for hh in range(2) for i in rows]
+    ref = so.attention_rows(case["q"], case["k"], case["v"], picks, causal=True)
+    g = np.stack([got[b, hh, i] for (b, hh, i) in picks])
+    assert max_abs_err(g, ref) <= TOL["bf16"]
