@@ -293,7 +293,30 @@ def cpu_baseline(name, dtype, budget_s=10.0):
     per = el / reps
     return {"value": flops / per / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
             "sample": f"whole {name} batch ({wl.B * wl.h} heads, {dtype} values in fp64), "
-                      f"{reps} passes in {el:.1f} s, {per * 1e3:.1f} ms per pass"}
+                      f"{reps} passes in {el:.1f} s, {per * 1e3:.1f} ms per pass",
+            "host": host_description()}
+
+
+def host_description() -> dict:
+    """CPU model, usable cores and the BLAS numpy calls (recorded beside the oracle timing)."""
+    import numpy as np
+
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo", encoding="utf-8") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = "unknown"
+    try:
+        b = np.show_config(mode="dicts").get("Build Dependencies", {}).get("blas", {})
+        blas = f"{b.get('name', '?')} {b.get('version', '')}".strip()
+    except Exception:  # older numpy: no dict mode
+        pass
+    return {"cpu_model": model, "usable_cores": len(os.sched_getaffinity(0)), "blas": blas}
 
 
 def oracle_pass(name, dtype, max_s=2.0):
