@@ -20,9 +20,9 @@ time, in float64:
 * Page 《Attention Is All You Need：注意力就是你所需要的一切》, §3.2 and
   §3.2.1: the weight of each value comes from the compatibility (dot product)
   of the query with the matching key, divided by √d_k, then a softmax.
-* Same page, §3.2.3, and the page 《精读 …》 table of the three uses
-  ("三者的计算完全相同"): encoder self-attention, decoder self-attention and
-  encoder–decoder attention run the identical computation; the decoder's
+* Same page, §3.2.3, and the page 《精读 …》 table of the three uses, which
+  states that they compute the same thing: encoder self-attention, decoder
+  self-attention and encoder–decoder attention run the identical computation; the decoder's
   illegal connections are set to −∞ inside the attention before the softmax,
   so their weights are exactly zero.  Decoder self-attention lets position i
   see every position up to and *including* i.
@@ -30,7 +30,7 @@ time, in float64:
   §2.2: Q is n×d_k (n = number of queries), K is m×d_k and V is m×d_v
   (m = number of key/value pairs).
 
-Readings taken where the pages are silent (each listed in the design doc):
+Readings taken where the pages are silent:
 * a key-padding length ``key_lens[b]`` hides keys j ≥ key_lens[b] of every
   head of batch element b (queries are never masked), clamped to [0, m];
 * a query row with no visible key returns the zero vector (every masked weight
@@ -102,19 +102,20 @@ def apply_mask(s: np.ndarray, vis: np.ndarray) -> np.ndarray:
 
 
 def row_softmax(s: np.ndarray) -> np.ndarray:
-    """Softmax of each row on its own; a row with no finite logit gives zeros.
+    """Softmax of each row on its own; a row whose logits are all −∞ (no
+    legal key) gives zeros.
 
-    Each row is a distribution over the keys that sums to 1 (the worked example
-    of 《精读 …》: "每行单独做一次 softmax，合计 100%").  Subtracting the row
-    maximum leaves the softmax unchanged and keeps exp() finite.
+    Each row is a distribution over the keys that sums to 1 (each row of the
+    worked example in 《精读 …》 is normalised on its own to 100 %).
+    Subtracting the row maximum leaves the softmax unchanged and keeps exp()
+    finite.
     """
     w = np.zeros_like(s)
     for i in range(s.shape[0]):
         row = s[i]
-        finite = row > -np.inf
-        if not finite.any():
+        if np.all(row == -np.inf):
             continue  # fully masked row: every weight is exactly zero
-        mu = row[finite].max()
+        mu = row.max()  # a NaN logit makes mu, and so the whole row, NaN
         e = np.exp(row - mu)  # exp(−∞) == 0.0 exactly
         w[i] = e / e.sum()
     return w
@@ -163,8 +164,8 @@ def _check_shapes(q, k, v, causal):
 def attention(q, k, v, scale=None, causal: bool = False, key_lens=None) -> np.ndarray:
     """Eq. (1) over every (batch, head) pair of [B, h, len, d] arrays, fp64.
 
-    The heads are independent ("在每组投影上并行做注意力", 《精读 …》 multi-head
-    section), so they are simply looped over.
+    The heads are independent (《精读 …》 multi-head section: attention runs in
+    parallel on each set of projections), so they are simply looped over.
     """
     B, h, n, m, d_k, d_v = _check_shapes(q, k, v, causal)
     if scale is None:

@@ -238,6 +238,30 @@ def pin_brute_force_mp(so):
                 assert np.allclose(o, ref, rtol=0, atol=1e-13), (B, h, n, m, causal, key_lens)
 
 
+def pin_nan_propagation(so):
+    """IEEE arithmetic on Eq. (1): a NaN logit of a legal key makes that row's
+    maximum, every weight and so the whole output row NaN; a NaN value
+    component of a key every row sees reaches only that output column; a row
+    with no legal key is the zero vector whatever its query holds, and rows
+    that cannot see a key are untouched by a NaN in it."""
+    rng = np.random.default_rng(19)
+    B, h, n, m, d, dv = 2, 1, 6, 6, 3, 4
+    q, k, v = _rand(rng, B, h, n, d), _rand(rng, B, h, m, d), _rand(rng, B, h, m, dv)
+    q[0, 0, 2, 1] = np.nan  # batch 0: every key legal ⇒ row 2 all NaN
+    q[1, 0, 4, 0] = np.nan  # batch 1: no legal key ⇒ row 4 zero
+    o = so.attention(q, k, v, key_lens=np.array([6, 0]))
+    assert np.isnan(o[0, 0, 2]).all()
+    assert np.isfinite(np.delete(o[0, 0], 2, axis=0)).all()
+    assert np.array_equal(o[1], np.zeros_like(o[1]))
+    q[:] = _rand(rng, B, h, n, d)
+    k[0, 0, 3, 2] = np.nan  # causal: rows 3.. see key 3, rows 0..2 do not
+    v[1, 0, 0, 2] = np.nan  # causal: every row weighs key 0 > 0
+    o = so.attention(q, k, v, causal=True)
+    assert np.isnan(o[0, 0, 3:]).all() and np.isfinite(o[0, 0, :3]).all()
+    assert np.isnan(o[1, 0, :, 2]).all()
+    assert np.isfinite(np.delete(o[1, 0], 2, axis=1)).all()
+
+
 ALL_PINS = [
     pin_worked_example_scores,
     pin_worked_example_weights,
@@ -251,4 +275,5 @@ ALL_PINS = [
     pin_hard_limit,
     pin_cross_attention_shapes,
     pin_brute_force_mp,
+    pin_nan_propagation,
 ]
