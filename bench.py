@@ -353,6 +353,65 @@ def oracle_pass(name, dtype, max_s=2.0):
                 "sample": f"{len(picks)} random output rows in {el:.1f} s; ms_per_pass extrapolated"}
 
 
+def context(steps=400):
+    """What else on this GPU reaches: (1) a plain bf16 GEMM through torch.matmul
+    (hipBLASLt), sustained, the practical matrix-core ceiling under the board's
+    power limit; (2) torch's fused scaled_dot_product_attention, restricted to
+    its flash backend (no math fallback), on the long causal workload's shape,
+    timed beside this library on the same tensors.  Context only; not a step."""
+    import torch
+    import torch.nn.functional as F
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+
+    import transformer_attention_sdpa_amd as sdpa
+
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+
+    def per_call(fn, iters, warm=3):
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3 / iters
+
+    out = {"what": "context: library GEMM ceiling and torch fused SDPA on this GPU"}
+    N = 8192
+    a = torch.randn(N, N, device=dev, dtype=torch.bfloat16, generator=gen)
+    b = torch.randn(N, N, device=dev, dtype=torch.bfloat16, generator=gen)
+    c = torch.empty(N, N, device=dev, dtype=torch.bfloat16)
+    t = per_call(lambda: torch.matmul(a, b, out=c), steps)
+    out["gemm_bf16_8192cubed"] = {"calls": steps, "us_per_call": t * 1e6,
+                                  "tflops": 2 * N ** 3 / t / 1e12,
+                                  "frac_bf16_peak": 2 * N ** 3 / t / 1e12 / PEAK_TFLOPS["bf16"]}
+    del a, b, c
+
+    wl = WORKLOADS["long_causal_8k"]
+    q, k, v = (torch.randn(wl.B, wl.h, wl.n, wl.d_k, device=dev, dtype=torch.bfloat16,
+                           generator=gen) for _ in range(3))
+    flops = 4 * wl.d_k * (wl.n * (wl.n + 1) // 2) * wl.B * wl.h
+    ours = sdpa.forward(q, k, v, causal=True)
+    t = per_call(lambda: sdpa.forward(q, k, v, causal=True, out=ours), 50)
+    out["this_library_long_causal_8k"] = {"us_per_call": t * 1e6, "tflops": flops / t / 1e12}
+    try:
+        with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+            ref = F.scaled_dot_product_attention(q, k, v, is_causal=True)
+            t = per_call(lambda: F.scaled_dot_product_attention(q, k, v, is_causal=True), 20)
+        out["torch_sdpa_flash_long_causal_8k"] = {
+            "us_per_call": t * 1e6, "tflops": flops / t / 1e12,
+            "max_abs_diff_vs_this_library": (ref.float() - ours.float()).abs().max().item()}
+    except RuntimeError as e:
+        out["torch_sdpa_flash_long_causal_8k"] = {"unavailable": str(e)[:200]}
+    out["torch"] = torch.__version__
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -371,6 +430,8 @@ def main():
                                                         "COPY_WRITE_DB"),
                     help="print the per-launch HBM traffic record of --kernel and exit")
     ap.add_argument("--kernel", default="sdpa_short_bf16", help="kernel name for --traffic-json")
+    ap.add_argument("--context", action="store_true",
+                    help="time a library bf16 GEMM and torch's fused SDPA beside this library")
     args = ap.parse_args()
 
     if args.rocprof_summary:
@@ -389,6 +450,9 @@ def main():
               "build has no multi-GPU path; run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
+    if args.context:
+        print(json.dumps(context()), flush=True)
+        return
     if args.calibrate_copy:
         print(json.dumps(copy_reference(args.steps, args.warmup, int(args.copy_mib * (1 << 20)))),
               flush=True)

@@ -37,7 +37,7 @@ extern "C" {
 #define SDPA_OK               0
 #define SDPA_ERR_NULL        -1 /* a required pointer is NULL                        */
 #define SDPA_ERR_SHAPE       -2 /* a dimension < 1, or an element count overflows   */
-#define SDPA_ERR_UNSUPPORTED -3 /* d_k / d_v not supported by this build (64 only)   */
+#define SDPA_ERR_UNSUPPORTED -3 /* d_k / d_v not supported (64 only)                 */
 #define SDPA_ERR_ALIGN       -4 /* a pointer is not 16-byte aligned                  */
 #define SDPA_ERR_MASK        -5 /* unknown mask_kind, or causal with n != m          */
 #define SDPA_ERR_DTYPE       -6 /* unknown dtype                                     */
@@ -63,7 +63,7 @@ extern "C" {
  *          with no legal key are written as zeros).  Must not overlap q, k, v, key_lens.
  * B, h     batch size and number of heads (>= 1).
  * n, m     number of queries and of keys/values per head (>= 1).
- * d_k, d_v query/key and value widths; this build supports d_k == d_v == 64.
+ * d_k, d_v query/key and value widths; the library supports d_k == d_v == 64.
  * scale    multiplier of the dot products; pass 1/sqrt(d_k) for Eq. (1).  Must
  *          be finite and > 0 (scale = 1 runs the unscaled dot-product form).
  * mask_kind SDPA_MASK_NONE or SDPA_MASK_CAUSAL.

@@ -183,6 +183,39 @@ def test_padded_keys_are_never_read(gpu_lib, dt, n, m):
     assert np.isfinite(got2).all()
 
 
+NAN_CASES = [  # dtype, B, h, n, m, causal, key_lens: every kernel family
+    ("bf16", 2, 2, 64, 64, False, [64, 40]),
+    ("bf16", 1, 2, 200, 200, True, None),
+    ("f32", 2, 2, 64, 64, False, [50, 64]),
+    ("f32", 1, 2, 100, 130, False, [97]),
+]
+
+
+@pytest.mark.parametrize("dt,B,h,n,m,causal,kl", NAN_CASES,
+                         ids=[f"{c[0]}-{c[3]}x{c[4]}{'-causal' if c[5] else ''}" for c in NAN_CASES])
+def test_nan_in_legal_inputs_propagates(gpu_lib, dt, B, h, n, m, causal, kl):
+    """NaN in a legal score or value reaches exactly the outputs the oracle says.
+
+    A NaN query component or a NaN component of a legal key makes the whole
+    row NaN for every query that sees it (its weights are NaN); a NaN value
+    component makes only that output column NaN.  Everything else stays finite
+    and within tolerance.  (The pages leave non-finite inputs open; NaN is
+    propagated, never turned into zeros.)
+    """
+    rng = np.random.default_rng(17)
+    case = random_case(rng, B, h, n, m, 64, 64, dtype=dt, causal=causal, key_lens=kl)
+    case["q"][0, 0, 3, 5] = np.nan
+    case["k"][B - 1, h - 1, 10, 7] = np.nan  # legal for every batch element here
+    if not causal:  # a causally hidden NaN value would meet a zero weight: 0 · NaN
+        case["v"][0, 1, 12, 3] = np.nan
+    _, got = run_gpu(case)
+    ref = _oracle(case)
+    nan_ref = np.isnan(ref)
+    assert nan_ref.any() and not nan_ref.all()
+    assert np.array_equal(np.isnan(got), nan_ref)
+    assert max_abs_err(got[~nan_ref], ref[~nan_ref]) <= TOL[dt]
+
+
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_causal_future_keys_do_not_leak(gpu_lib, dt):
     """Changing key/value row j leaves query rows i < j bitwise unchanged."""

@@ -69,7 +69,7 @@ extern "C" const char* sdpa_strerror(int status) {
         case SDPA_OK: return "ok";
         case SDPA_ERR_NULL: return "a required pointer is NULL";
         case SDPA_ERR_SHAPE: return "bad shape: a dimension is < 1 or an element count overflows";
-        case SDPA_ERR_UNSUPPORTED: return "unsupported head width: this build supports d_k = d_v = 64";
+        case SDPA_ERR_UNSUPPORTED: return "unsupported head width: the library supports d_k = d_v = 64";
         case SDPA_ERR_ALIGN: return "a device pointer is not 16-byte aligned (key_lens: 4-byte)";
         case SDPA_ERR_MASK: return "bad mask: unknown mask_kind, or causal with n != m";
         case SDPA_ERR_DTYPE: return "unknown dtype (SDPA_F32 = 0, SDPA_BF16 = 1)";

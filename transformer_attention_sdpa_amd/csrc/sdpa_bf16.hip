@@ -164,7 +164,7 @@ struct LongKernel {
         }
 
         // Weights against the current reference maximum, without computing this
-        // tile's maximum: if every lane's partial sum stays within 2^SUM_LOG2,
+        // tile's maximum: if every lane's partial sum stays within SUM_LIMIT,
         // no weight exceeds it and the tile is done (the reference cancels in
         // Σ p·v / Σ p).  Otherwise — and on a wave's first tile, where there is
         // no reference yet — take the tile maxima, move the reference to them,
@@ -351,7 +351,8 @@ __global__ __launch_bounds__(NW * 64) void sdpa_long_bf16(
     for (int qt = 0; qt < QT; ++qt) {
         const int qrow = k.wq0 + 32 * qt + k.l32;
         const float ltot = half_swap_sum(k.lsum[qt]);
-        const float inv = ltot > 0.f ? 1.f / ltot : 0.f;  // no legal key ⇒ zero row
+        // no legal key ⇒ zero row; a NaN sum (NaN legal inputs) stays NaN
+        const float inv = ltot != 0.f ? 1.f / ltot : 0.f;
         if (qrow < n) {
             uint16_t* dst = O + qbase + (size_t)qrow * D;
 #pragma unroll

@@ -12,12 +12,15 @@
 //   * four waves of 16 queries each on v_mfma_f32_16x16x32_bf16, so each wave's
 //     serial MFMA/softmax chain is a quarter of a head;
 //   * Q, K and V move HBM → LDS with buffer_load_dwordx4 … lds; Q is issued
-//     before the key length is known, K and V right after it with their buffer
-//     range ending at the key length, so padded rows are never read (they
-//     arrive as zeros); the scores and the softmax run while V is in flight;
+//     before the key length is known, K right after it with its buffer range
+//     ending at the key length, so padded rows are never read (they arrive as
+//     zeros); V, ranged the same way, is requested once Q and K have landed,
+//     so grid-wide the score operands go first, and it arrives while the
+//     scores and the softmax run;
 //   * every load and the output store carry the non-temporal hint: each byte
 //     is touched once, and with nothing left dirty or resident in the caches
-//     the kernel's end costs less (about 1 µs of a ≈ 5.5 µs launch);
+//     the kernel's end costs less (it took about 1 µs off each launch at
+//     64 × 8 heads of 64 × 64);
 //   * the output goes through LDS so that each store instruction writes whole
 //     128-byte rows;
 //   * key tiles of 16 wholly past the key length (or, causal, past the wave's
@@ -93,10 +96,10 @@ __global__ __launch_bounds__(NT) void sdpa_short_bf16(
         ld_lds[i] = 8 * (2 * w + i) * 128;
     }
     // Q goes first, without waiting for the key length.  Then the key length,
-    // then K and V, whose buffer ranges stop at it: their padded rows arrive as
-    // zeros without being read (a zero K row only gives a score the mask
-    // discards; a zero V row meets weight 0 in P·V, and 0 · garbage must not
-    // happen).  The scores and the softmax run while V is still in flight.
+    // then K (and V, below), whose buffer ranges stop at it: their padded rows
+    // arrive as zeros without being read (a zero K row only gives a score the
+    // mask discards; a zero V row meets weight 0 in P·V, and 0 · garbage must
+    // not happen).
     const i32x4 rq = make_rsrc(Q + qbase, (uint32_t)(n * D * 2));
     load16_to_lds_nt(rq, lds + MAXLEN * 128 + ld_lds[0], ld_off[0]);
     load16_to_lds_nt(rq, lds + MAXLEN * 128 + ld_lds[1], ld_off[1]);
@@ -108,10 +111,13 @@ __global__ __launch_bounds__(NT) void sdpa_short_bf16(
     const i32x4 rk = make_rsrc(K + kvbase, (uint32_t)(L * D * 2));
     load16_to_lds_nt(rk, lds + ld_lds[0], ld_off[0]);
     load16_to_lds_nt(rk, lds + ld_lds[1], ld_off[1]);
+    // V is requested only once this wave's Q and K rows have landed: across
+    // the grid, every workgroup's Q and K then reach HBM ahead of V traffic,
+    // which the scores do not need.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     const i32x4 rv = make_rsrc(V + kvbase, (uint32_t)(L * D * 2));
     load16_to_lds_nt(rv, lds + 2 * MAXLEN * 128 + ld_lds[0], ld_off[0]);
     load16_to_lds_nt(rv, lds + 2 * MAXLEN * 128 + ld_lds[1], ld_off[1]);
-    asm volatile("s_waitcnt vmcnt(2)" ::: "memory");  // Q and K in; V may still fly
     lds_barrier();
     const bool active = w * QW < n;  // this wave has queries (n < 64 leaves some idle)
 
@@ -202,7 +208,8 @@ __global__ __launch_bounds__(NT) void sdpa_short_bf16(
     // output rows go through its own 2 KiB of the (now free) K tile so that
     // every store instruction writes whole 128-byte rows, 16 bytes a lane.
     {
-        const float inv = l > 0.f ? __builtin_amdgcn_rcpf(l) : 0.f;  // no legal key ⇒ zero row
+        // no legal key ⇒ zero row; a NaN sum (NaN legal inputs) stays NaN
+        const float inv = l != 0.f ? __builtin_amdgcn_rcpf(l) : 0.f;
         char* ob = lds + w * QW * 128;
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {

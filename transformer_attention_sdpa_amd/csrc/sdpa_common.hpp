@@ -14,9 +14,9 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-// Head width this build supports (d_k == d_v == 64, the pages' base and big models).
+// The one head width the kernels support (d_k == d_v == 64, the pages' base and
+// big models).
 constexpr int kHeadDim = 64;
 
 // Everything a launcher needs; validated by the C ABI before any HIP call.
@@ -124,19 +124,12 @@ __device__ __forceinline__ void load16_to_lds_nt(i32x4 rsrc, void* lds, int voff
 __device__ __forceinline__ void store16_nt(void* p, u32x4 x) {
     __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(p));
 }
-// buffer_load_dwordx4 into VGPRs; offsets at or past the descriptor's range
-// read as zeros.
-extern "C" __device__ i32x4 sdpa_llvm_buffer_load_v4i32(i32x4 rsrc, int voffset, int soffset,
-                                                        int aux) __asm("llvm.amdgcn.raw.buffer.load.v4i32");
-__device__ __forceinline__ u32x4 load16(i32x4 rsrc, int voffset) {
-    return __builtin_bit_cast(u32x4, sdpa_llvm_buffer_load_v4i32(rsrc, voffset, 0, 0));
-}
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Workgroup barrier without the release fence of __syncthreads (which waits
-// for every outstanding global load, LDS DMA included).  For LDS data written
-// by buffer loads: wait for them (s_waitcnt vmcnt) before the barrier.  No
-// ds_write may be pending across it.
+// for every outstanding global load, LDS DMA included).  It waits only for the
+// wave's own LDS operations (lgkmcnt); LDS data written by buffer loads needs
+// its own s_waitcnt vmcnt before the barrier.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Round-to-nearest-even float → bf16 of eight values (v_cvt_pk_bf16_f32 on gfx950).

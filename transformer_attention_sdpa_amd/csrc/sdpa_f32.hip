@@ -187,11 +187,12 @@ __global__ __launch_bounds__(NW * 64) void sdpa_fwd_f32(
             for (int i4 = 0; i4 < 4; ++i4) {
                 const int dv = 32 * dt + 8 * i4 + 4 * hf;
                 f32x4 o;
-                // true division keeps the fp32 path within a few ulp of the exact result
-                o[0] = ltot > 0.f ? oacc[dt][4 * i4 + 0] / ltot : 0.f;
-                o[1] = ltot > 0.f ? oacc[dt][4 * i4 + 1] / ltot : 0.f;
-                o[2] = ltot > 0.f ? oacc[dt][4 * i4 + 2] / ltot : 0.f;
-                o[3] = ltot > 0.f ? oacc[dt][4 * i4 + 3] / ltot : 0.f;
+                // True division (within an ulp).  ltot = 0 (no legal key) gives a
+                // zero row; a NaN ltot (NaN among the legal inputs) stays NaN.
+                o[0] = ltot != 0.f ? oacc[dt][4 * i4 + 0] / ltot : 0.f;
+                o[1] = ltot != 0.f ? oacc[dt][4 * i4 + 1] / ltot : 0.f;
+                o[2] = ltot != 0.f ? oacc[dt][4 * i4 + 2] / ltot : 0.f;
+                o[3] = ltot != 0.f ? oacc[dt][4 * i4 + 3] / ltot : 0.f;
                 *reinterpret_cast<f32x4*>(dst + dv) = o;
             }
     }

@@ -10,11 +10,11 @@
 // Built like the bf16 sentence-length kernel: one workgroup per (batch, head),
 // four waves of 16 queries, the whole head (≤ 64 keys) as one tile so the
 // softmax is an exact two-pass one.  Q moves HBM → LDS (buffer_load … lds)
-// before the key length is known, K and V right after it with their buffer
-// ranges ending at the key length (padded rows are never read and arrive as
-// zeros), and the scores and softmax run while V is in flight.  Key tiles of
-// 16 wholly past the key length (or, causal, past a wave's queries) are
-// skipped.
+// before the key length is known, K right after it with its buffer range
+// ending at the key length (padded rows are never read and arrive as zeros),
+// and V, ranged the same way, once Q and K have landed; it arrives while the
+// scores run.  Key tiles of 16 wholly past the key length (or, causal, past a
+// wave's queries) are skipped.
 //
 // Products, transposed as elsewhere (each lane owns one query column):
 //   Sᵀ (16 keys × 16 queries) = K · Qᵀ, 16 k-steps of 4; in k-step ks the
@@ -23,7 +23,8 @@
 //     row and of its Q row;
 //   Oᵀ (16 dv × 16 queries) += Vᵀ · Pᵀ, one k-step per (key tile kt, r): group
 //     G contributes key 16·kt + 4·G + r, which is exactly the Sᵀ register
-//     (kt, r) the lane already holds — Pᵀ never moves.
+//     (kt, r) the lane already holds — Pᵀ never moves.  The 64 dv are spread
+//     over four products so that one 16-byte LDS read feeds all four.
 #include "sdpa_common.hpp"
 
 namespace sdpa {
@@ -38,8 +39,8 @@ constexpr int ROW = D * 4;   // 256-byte rows
 constexpr int TILE = MAXLEN * ROW;  // 16 KiB
 
 // fp32 tile in LDS: 16 chunks of 16 B per row; chunk c of row r sits at
-// position c ^ (r mod 16), so 16 consecutive rows read at one chunk, and one
-// row read as 4 consecutive chunks by 4 rows 4 apart, hit distinct banks.
+// position c ^ (r mod 16), so 16 consecutive rows read at one chunk, and all
+// 16 chunks of one row read by one 16-lane group, hit distinct banks.
 __device__ __forceinline__ int f32_swz(int row, int chunk) { return row * 16 + (chunk ^ (row & 15)); }
 
 __device__ __forceinline__ f32x4 mfma16x16x4(float a, float b, f32x4 c) {
@@ -63,7 +64,7 @@ __global__ __launch_bounds__(NT) void sdpa_short_f32(
     __shared__ __attribute__((aligned(16))) char lds[3 * TILE];
     const f32x4* sK = reinterpret_cast<const f32x4*>(lds);
     const f32x4* sQ = reinterpret_cast<const f32x4*>(lds + TILE);
-    const float* sV = reinterpret_cast<const float*>(lds + 2 * TILE);
+    const f32x4* sV4 = reinterpret_cast<const f32x4*>(lds + 2 * TILE);
 
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -97,10 +98,12 @@ __global__ __launch_bounds__(NT) void sdpa_short_f32(
     const i32x4 rk = make_rsrc(K + kvbase, (uint32_t)(L * ROW));
 #pragma unroll
     for (int i = 0; i < 4; ++i) load16_to_lds_nt(rk, lds + ld_lds[i], ld_off[i]);
+    // V only once this wave's Q and K rows have landed (grid-wide, the score
+    // operands reach HBM ahead of V); it arrives during the scores.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     const i32x4 rv = make_rsrc(V + kvbase, (uint32_t)(L * ROW));
 #pragma unroll
     for (int i = 0; i < 4; ++i) load16_to_lds_nt(rv, lds + 2 * TILE + ld_lds[i], ld_off[i]);
-    asm volatile("s_waitcnt vmcnt(4)" ::: "memory");  // Q and K in; V may still fly
     lds_barrier();
 
     const int q = w * QW + l16;
@@ -172,36 +175,46 @@ __global__ __launch_bounds__(NT) void sdpa_short_f32(
     lds_barrier();
     if (!active) return;
 
-    // Oᵀ += Vᵀ · Pᵀ; register r of o[dt] is dv = 16·dt + 4·G + r of query q.
+    // Oᵀ += Vᵀ · Pᵀ.  Output row i of product dt stands for dv = 4·f(i) + dt
+    // with f(i) = 4·(i mod 4) + i/4, so A-operand lane l16 needs elements
+    // 0..3 of chunk f(l16) of a V row: one 16-byte read serves all four
+    // products.  Register r of o[dt] is then dv = 4·f(4·G + r) + dt
+    // = 16·r + 4·G + dt of query q.
     f32x4 o[4];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int vchunk = 4 * (l16 & 3) + (l16 >> 2);
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
         if (kt >= nkt) continue;  // uniform; these weights are all zero
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int vrow = 16 * kt + 4 * G + r;
+            const f32x4 a = sV4[f32_swz(16 * kt + 4 * G + r, vchunk)];
 #pragma unroll
-            for (int dt = 0; dt < 4; ++dt) {
-                const int dv = 16 * dt + l16;
-                const float a = sV[f32_swz(vrow, dv >> 2) * 4 + (dv & 3)];
-                o[dt] = mfma16x16x4(a, s[kt][r], o[dt]);
-            }
+            for (int dt = 0; dt < 4; ++dt) o[dt] = mfma16x16x4(a[dt], s[kt][r], o[dt]);
         }
     }
 
     if (q < n) {
-        float* dst = O + qbase + (size_t)q * D;
+        // 1/l to about an ulp: the hardware reciprocal refined by one Newton
+        // step.  l = 0 (no legal key) gives a zero row; a NaN l (NaN among the
+        // legal inputs) stays NaN.
+        float inv = 0.f;
+        if (l != 0.f) {
+            inv = __builtin_amdgcn_rcpf(l);
+            inv = __builtin_fmaf(__builtin_fmaf(-l, inv, 1.f), inv, inv);
+        }
+        // Store r writes dv 16·r + 4·G .. +3: the four 16-lane groups cover 64
+        // contiguous bytes of each row per instruction.
+        float* dst = O + qbase + (size_t)q * D + 4 * G;
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
+        for (int r = 0; r < 4; ++r) {
             f32x4 ov;
-            // true division keeps the fp32 path within a few ulp of the exact result
-            ov[0] = l > 0.f ? o[dt][0] / l : 0.f;  // no legal key ⇒ zero row
-            ov[1] = l > 0.f ? o[dt][1] / l : 0.f;
-            ov[2] = l > 0.f ? o[dt][2] / l : 0.f;
-            ov[3] = l > 0.f ? o[dt][3] / l : 0.f;
-            store16_nt(dst + 16 * dt + 4 * G, __builtin_bit_cast(u32x4, ov));
+            ov[0] = o[0][r] * inv;
+            ov[1] = o[1][r] * inv;
+            ov[2] = o[2][r] * inv;
+            ov[3] = o[3][r] * inv;
+            store16_nt(dst + 16 * r, __builtin_bit_cast(u32x4, ov));
         }
     }
 }
