@@ -21,8 +21,13 @@ from __future__ import annotations
 import mpmath
 
 
-def attention_mp(q, k, v, scale, causal=False, key_lens=None, dps=50):
+def attention_mp(q, k, v, scale, causal=False, key_lens=None, dps=50, window=None):
     """q: [B][h][n][d_k], k: [B][h][m][d_k], v: [B][h][m][d_v] nested sequences.
+
+    ``window``: None or (left, right, align): key j is legal for query i only
+    if p − left ≤ j ≤ p + right, where p = i (align 'top_left') or
+    p = i + len − n (align 'bottom_right': the queries end where the keys end);
+    a None side is unbounded.
 
     Returns nested lists of ``mpmath.mpf`` with shape [B][h][n][d_v].
     """
@@ -41,9 +46,16 @@ def attention_mp(q, k, v, scale, causal=False, key_lens=None, dps=50):
                 for i in range(len(Q)):
                     num = [mpmath.mpf(0)] * d_v
                     den = mpmath.mpf(0)
+                    if window is not None:
+                        p = i if window[2] == "top_left" else i + lim - len(Q)
                     for j in range(m):
                         if j >= lim or (causal and j > i):
                             continue
+                        if window is not None:
+                            if window[0] is not None and j < p - window[0]:
+                                continue
+                            if window[1] is not None and j > p + window[1]:
+                                continue
                         dot = mpmath.fsum(mpmath.mpf(float(Q[i][t])) * mpmath.mpf(float(K[j][t]))
                                           for t in range(len(Q[i])))
                         e = mpmath.exp(sc * dot)

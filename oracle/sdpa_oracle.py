@@ -35,7 +35,17 @@ Readings taken where the pages are silent:
   head of batch element b (queries are never masked), clamped to [0, m];
 * a query row with no visible key returns the zero vector (every masked weight
   is exactly zero, so nothing is summed);
-* the causal mask needs n == m (decoder self-attention) and is inclusive.
+* the causal mask needs n == m (decoder self-attention) and is inclusive;
+* restricted self-attention (《精读 …》 Table 1 and the discussion of long
+  sequences after it; 《注意力就是你所需要的一切》 §4: each output position
+  looks only at a neighbourhood of size r around it) is written as a key window
+  [c_i − left, c_i + right] around the query's aligned position c_i, either
+  side unbounded when None; a neighbourhood of size r centred on the query is
+  left = right = ⌊r/2⌋.  c_i = i with top-left alignment, or i + (L − n) with
+  bottom-right alignment, where the n queries are the last n positions of a
+  sequence of L keys (a decoder step against its cached keys); L is the key
+  length of the batch element (m without padding).  The decoder's causal mask
+  is the window (None, 0) with top-left alignment and n == m.
 
 The steps are module-level functions (``scores``, ``visible_keys``,
 ``apply_mask``, ``row_softmax``, ``weighted_values``) that
@@ -72,12 +82,15 @@ def default_scale(d_k: int) -> float:
     return 1.0 / math.sqrt(d_k)
 
 
-def visible_keys(query_pos: np.ndarray, m: int, causal: bool, key_len: int | None) -> np.ndarray:
+def visible_keys(query_pos: np.ndarray, m: int, causal: bool, key_len: int | None,
+                 window=None) -> np.ndarray:
     """Boolean [len(query_pos), m]: True where query i may attend to key j.
 
     Causal (decoder self-attention, 《注意力就是你所需要的一切》 §3.2.3): key j is
     visible to the query at position i iff j ≤ i (inclusive).  Key padding:
-    key j is visible iff j < clamp(key_len, 0, m).
+    key j is visible iff j < clamp(key_len, 0, m).  Window (restricted
+    attention): ``window = (left, right, shift)`` makes key j visible only if
+    c − left ≤ j ≤ c + right, with c = i + shift and a None side unbounded.
     """
     j = np.arange(m)[None, :]
     vis = np.ones((len(query_pos), m), dtype=bool)
@@ -86,6 +99,13 @@ def visible_keys(query_pos: np.ndarray, m: int, causal: bool, key_len: int | Non
     if key_len is not None:
         L = min(max(int(key_len), 0), m)
         vis &= j < L
+    if window is not None:
+        left, right, shift = window
+        c = np.asarray(query_pos)[:, None] + int(shift)
+        if left is not None:
+            vis &= j >= c - int(left)
+        if right is not None:
+            vis &= j <= c + int(right)
     return vis
 
 
@@ -126,11 +146,13 @@ def weighted_values(w: np.ndarray, v: np.ndarray) -> np.ndarray:
     return w @ v
 
 
-def attention_head(q, k, v, scale: float, causal: bool = False, key_len=None, query_pos=None):
+def attention_head(q, k, v, scale: float, causal: bool = False, key_len=None, query_pos=None,
+                   window=None):
     """Eq. (1) for one head.  q: [n', d_k], k: [m, d_k], v: [m, d_v] → [n', d_v].
 
     ``query_pos`` gives the sequence positions of the rows of q (default
-    0..n'-1); only the causal mask uses it.
+    0..n'-1); only the causal mask and the window use it.  ``window`` is
+    (left, right, shift) as in ``visible_keys``.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -142,10 +164,35 @@ def attention_head(q, k, v, scale: float, causal: bool = False, key_len=None, qu
     for r0 in range(0, q.shape[0], _ROW_SLICE):
         r1 = min(r0 + _ROW_SLICE, q.shape[0])
         s = scores(q[r0:r1], k, scale)
-        vis = visible_keys(query_pos[r0:r1], k.shape[0], causal, key_len)
+        if window is None:
+            vis = visible_keys(query_pos[r0:r1], k.shape[0], causal, key_len)
+        else:
+            vis = visible_keys(query_pos[r0:r1], k.shape[0], causal, key_len, window=window)
         w = row_softmax(apply_mask(s, vis))
         out[r0:r1] = weighted_values(w, v)
     return out
+
+
+def _window_of(window, n, m, key_len):
+    """(left, right, shift) of one batch element from the user's window.
+
+    ``window`` is None or (left, right) or (left, right, align) with align
+    'top_left' (default) or 'bottom_right'."""
+    if window is None:
+        return None
+    left, right = window[0], window[1]
+    align = window[2] if len(window) > 2 else "top_left"
+    for side in (left, right):
+        if side is not None and int(side) < 0:
+            raise ValueError("window sides are >= 0 or None (unbounded)")
+    if align == "top_left":
+        shift = 0
+    elif align == "bottom_right":
+        L = m if key_len is None else min(max(int(key_len), 0), m)
+        shift = L - n
+    else:
+        raise ValueError(f"unknown alignment {align!r}")
+    return (left, right, shift)
 
 
 def _check_shapes(q, k, v, causal):
@@ -161,35 +208,52 @@ def _check_shapes(q, k, v, causal):
     return B, h, n, k.shape[2], d_k, v.shape[3]
 
 
-def attention(q, k, v, scale=None, causal: bool = False, key_lens=None) -> np.ndarray:
+def attention(q, k, v, scale=None, causal: bool = False, key_lens=None, window=None) -> np.ndarray:
     """Eq. (1) over every (batch, head) pair of [B, h, len, d] arrays, fp64.
 
     The heads are independent (《精读 …》 multi-head section: attention runs in
     parallel on each set of projections), so they are simply looped over.
+    ``window``: None, or (left, right[, align]) for restricted attention (see
+    the module notes); it is not combined with ``causal``.
     """
+    if window is not None and causal:
+        raise ValueError("give the causal mask as the window (None, 0) instead")
     B, h, n, m, d_k, d_v = _check_shapes(q, k, v, causal)
     if scale is None:
         scale = default_scale(d_k)
     out = np.empty((B, h, n, d_v), dtype=np.float64)
     for b in range(B):
         L = None if key_lens is None else int(key_lens[b])
+        win = _window_of(window, n, m, L)
         for hh in range(h):
-            out[b, hh] = attention_head(q[b, hh], k[b, hh], v[b, hh], scale, causal, L)
+            if win is None:
+                out[b, hh] = attention_head(q[b, hh], k[b, hh], v[b, hh], scale, causal, L)
+            else:
+                out[b, hh] = attention_head(q[b, hh], k[b, hh], v[b, hh], scale, causal, L,
+                                            window=win)
     return out
 
 
-def attention_rows(q, k, v, picks, scale=None, causal: bool = False, key_lens=None):
+def attention_rows(q, k, v, picks, scale=None, causal: bool = False, key_lens=None,
+                   window=None):
     """Eq. (1) for selected output rows only: ``picks`` is a list of (b, head, i).
 
     Returns an array [len(picks), d_v].  Used to check full-size outputs row by
     row where evaluating every row would take too long.
     """
+    if window is not None and causal:
+        raise ValueError("give the causal mask as the window (None, 0) instead")
     B, h, n, m, d_k, d_v = _check_shapes(q, k, v, causal)
     if scale is None:
         scale = default_scale(d_k)
     out = np.empty((len(picks), d_v), dtype=np.float64)
     for r, (b, hh, i) in enumerate(picks):
         L = None if key_lens is None else int(key_lens[b])
-        out[r] = attention_head(q[b, hh, i:i + 1], k[b, hh], v[b, hh], scale, causal, L,
-                                query_pos=np.array([i]))[0]
+        win = _window_of(window, n, m, L)
+        if win is None:
+            out[r] = attention_head(q[b, hh, i:i + 1], k[b, hh], v[b, hh], scale, causal, L,
+                                    query_pos=np.array([i]))[0]
+        else:
+            out[r] = attention_head(q[b, hh, i:i + 1], k[b, hh], v[b, hh], scale, causal, L,
+                                    query_pos=np.array([i]), window=win)[0]
     return out

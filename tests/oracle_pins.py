@@ -262,6 +262,80 @@ def pin_nan_propagation(so):
     assert np.isfinite(np.delete(o[1, 0], 2, axis=1)).all()
 
 
+def _window_slice(i, n, L, left, right, align):
+    """Index range [lo, hi) of the legal keys of query i, by direct reading of the
+    window's definition (no mask arithmetic shared with the oracle)."""
+    p = i if align == "top_left" else i + L - n
+    lo = 0 if left is None else max(0, p - left)
+    hi = L if right is None else min(L, p + right + 1)
+    return lo, max(lo, hi)
+
+
+WINDOWS = [(2, 1, "top_left"), (0, 3, "top_left"), (None, 2, "top_left"), (3, None, "top_left"),
+           (1, 1, "bottom_right"), (None, 0, "bottom_right"), (4, 0, "bottom_right")]
+
+
+def pin_window_zero_query_gives_window_mean(so):
+    """Restricted attention (《精读 …》 Table 1): Q = 0 ⇒ every legal score is 0 ⇒
+    the output row is the plain mean of the value rows inside the query's
+    window (and the zero vector when the window holds no legal key)."""
+    rng = np.random.default_rng(23)
+    B, h, n, m, d, dv = 2, 2, 5, 8, 3, 4
+    q = np.zeros((B, h, n, d))
+    k, v = _rand(rng, B, h, m, d), _rand(rng, B, h, m, dv)
+    key_lens = np.array([8, 3])
+    for left, right, align in WINDOWS:
+        o = so.attention(q, k, v, key_lens=key_lens, window=(left, right, align))
+        for b in range(B):
+            for i in range(n):
+                lo, hi = _window_slice(i, n, int(key_lens[b]), left, right, align)
+                ref = v[b, :, lo:hi].mean(axis=1) if hi > lo else np.zeros((h, dv))
+                assert np.allclose(o[b, :, i], ref, rtol=0, atol=1e-14), (left, right, align, b, i)
+
+
+def pin_window_single_key(so):
+    """Window (0, 0) on self-attention: each query sees only its own position,
+    whose weight is exactly 1, so the output row is that value row bitwise."""
+    rng = np.random.default_rng(29)
+    q, k, v = _rand(rng, 2, 2, 6, 3), _rand(rng, 2, 2, 6, 3), _rand(rng, 2, 2, 6, 4)
+    o = so.attention(q, k, v, window=(0, 0))
+    assert np.array_equal(o, v)
+    # bottom-right with one query: the last legal key only
+    o = so.attention(q[:, :, :1], k, v, key_lens=np.array([6, 4]), window=(0, 0, "bottom_right"))
+    assert np.array_equal(o[0, :, 0], v[0, :, 5]) and np.array_equal(o[1, :, 0], v[1, :, 3])
+
+
+def pin_window_brute_force_mp(so):
+    """The 50-digit evaluator on tiny shapes with every window kind."""
+    from oracle.brute_mp import attention_mp
+
+    rng = np.random.default_rng(31)
+    B, h, n, m, d, dv = 2, 1, 4, 6, 3, 2
+    q, k, v = _rand(rng, B, h, n, d), _rand(rng, B, h, m, d), _rand(rng, B, h, m, dv)
+    key_lens = np.array([6, 2])
+    for left, right, align in WINDOWS:
+        o = so.attention(q, k, v, scale=0.7, key_lens=key_lens, window=(left, right, align))
+        ref = attention_mp(q.tolist(), k.tolist(), v.tolist(), 0.7, key_lens=key_lens.tolist(),
+                           window=(left, right, align))
+        ref = np.array([[[[float(x) for x in row] for row in hd] for hd in bt] for bt in ref])
+        assert np.allclose(o, ref, rtol=0, atol=1e-14), (left, right, align)
+
+
+def pin_window_reduces_to_plain_masks(so):
+    """An unbounded window is no mask; (None, 0) top-left on self-attention is
+    the decoder's causal mask; a single bottom-right query with (None, 0) sees
+    every legal key (it is the last position)."""
+    rng = np.random.default_rng(37)
+    q, k, v = _rand(rng, 2, 2, 5, 3), _rand(rng, 2, 2, 5, 3), _rand(rng, 2, 2, 5, 4)
+    kl = np.array([5, 3])
+    assert np.array_equal(so.attention(q, k, v, key_lens=kl, window=(None, None)),
+                          so.attention(q, k, v, key_lens=kl))
+    assert np.array_equal(so.attention(q, k, v, key_lens=kl, window=(None, 0)),
+                          so.attention(q, k, v, key_lens=kl, causal=True))
+    assert np.array_equal(so.attention(q[:, :, 4:], k, v, key_lens=kl, window=(None, 0, "bottom_right")),
+                          so.attention(q[:, :, 4:], k, v, key_lens=kl))
+
+
 ALL_PINS = [
     pin_worked_example_scores,
     pin_worked_example_weights,
@@ -276,4 +350,8 @@ ALL_PINS = [
     pin_cross_attention_shapes,
     pin_brute_force_mp,
     pin_nan_propagation,
+    pin_window_zero_query_gives_window_mean,
+    pin_window_single_key,
+    pin_window_brute_force_mp,
+    pin_window_reduces_to_plain_masks,
 ]

@@ -40,6 +40,27 @@ def _vis_pad_on_queries(query_pos, m, causal, key_len):
     return vis
 
 
+def _vis_window_left_off_by_one(query_pos, m, causal, key_len, window=None):
+    if window is not None and window[0] is not None:
+        window = (window[0] - 1 if window[0] > 0 else 0, window[1], window[2])
+    return _orig_visible(query_pos, m, causal, key_len, window=window) if window is not None \
+        else _orig_visible(query_pos, m, causal, key_len)
+
+
+def _vis_window_sides_swapped(query_pos, m, causal, key_len, window=None):
+    if window is not None:
+        window = (window[1], window[0], window[2])
+    return _orig_visible(query_pos, m, causal, key_len, window=window) if window is not None \
+        else _orig_visible(query_pos, m, causal, key_len)
+
+
+def _vis_window_alignment_ignored(query_pos, m, causal, key_len, window=None):
+    if window is not None:
+        window = (window[0], window[1], 0)
+    return _orig_visible(query_pos, m, causal, key_len, window=window) if window is not None \
+        else _orig_visible(query_pos, m, causal, key_len)
+
+
 def _mask_finite(s, vis):
     out = s.copy()
     out[~vis] = -1e9
@@ -83,6 +104,9 @@ MUTANTS = {
     "padding_off_by_one": ("visible_keys", _vis_pad_off_by_one),
     "padding_ignored": ("visible_keys", _vis_ignore_padding),
     "padding_on_queries": ("visible_keys", _vis_pad_on_queries),
+    "window_left_off_by_one": ("visible_keys", _vis_window_left_off_by_one),
+    "window_sides_swapped": ("visible_keys", _vis_window_sides_swapped),
+    "window_alignment_ignored": ("visible_keys", _vis_window_alignment_ignored),
     "mask_finite_fill": ("apply_mask", _mask_finite),
     "mask_skipped": ("apply_mask", lambda s, vis: s.copy()),
     "softmax_over_columns": ("row_softmax", _softmax_cols),
