@@ -39,7 +39,7 @@ CSRC = os.path.join(ROOT, "transformer_attention_sdpa_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 HEADLINE = ("encoder_self_base", "bf16")
 EXTRA = [("single_head_16", "f32"), ("encoder_self_base", "f32"), ("decoder_causal_base", "bf16"),
-         ("cross_big", "bf16"), ("long_causal_8k", "bf16")]
+         ("cross_big", "bf16"), ("long_causal_8k", "bf16"), ("local_window_8k", "bf16")]
 
 
 def algorithmic_work(wl, dtype, key_lens):
@@ -55,7 +55,17 @@ def algorithmic_work(wl, dtype, key_lens):
     kv_rows = 0
     for b in range(wl.B):
         L = wl.m if key_lens is None else min(max(int(key_lens[b]), 0), wl.m)
-        if wl.causal:
+        if wl.window is not None:
+            # query i sees keys [lo_i, hi_i) around its aligned position c_i
+            import numpy as np
+
+            left, right = wl.window[0], wl.window[1]
+            align = wl.window[2] if len(wl.window) > 2 else "top_left"
+            c = np.arange(wl.n, dtype=np.int64) + (L - wl.n if align == "bottom_right" else 0)
+            lo = np.zeros_like(c) if left is None else np.clip(c - left, 0, L)
+            hi = np.full_like(c, L) if right is None else np.clip(c + right + 1, 0, L)
+            p = int(np.maximum(hi - lo, 0).sum())
+        elif wl.causal:
             # query i sees min(i + 1, L) keys
             k = min(L, wl.n)
             p = k * (k + 1) // 2 + (wl.n - k) * L
@@ -127,11 +137,21 @@ def time_workload(name, dtype, steps, warmup, clock_warm_s=0.0):
     scale = 1.0 / math.sqrt(wl.d_k)
     mask = _lib.SDPA_MASK_CAUSAL if wl.causal else _lib.SDPA_MASK_NONE
     ptrs = [(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr()) for (q, k, v, o) in sets]
+    if wl.window is not None:
+        wleft = -1 if wl.window[0] is None else wl.window[0]
+        wright = -1 if wl.window[1] is None else wl.window[1]
+        walign = (_lib.SDPA_ALIGN_BOTTOM_RIGHT if len(wl.window) > 2 and wl.window[2] == "bottom_right"
+                  else _lib.SDPA_ALIGN_TOP_LEFT)
 
     def launch(i, stream):
         p = ptrs[i % nsets]
-        rc = _lib.sdpa_forward(p[0], p[1], p[2], p[3], wl.B, wl.h, wl.n, wl.m, wl.d_k, wl.d_v,
-                               scale, mask, kl_ptr, code, stream)
+        if wl.window is None:
+            rc = _lib.sdpa_forward(p[0], p[1], p[2], p[3], wl.B, wl.h, wl.n, wl.m, wl.d_k, wl.d_v,
+                                   scale, mask, kl_ptr, code, stream)
+        else:
+            rc = _lib.sdpa_forward_window(p[0], p[1], p[2], p[3], wl.B, wl.h, wl.n, wl.m, wl.d_k,
+                                          wl.d_v, scale, wleft, wright, walign, kl_ptr, code,
+                                          stream)
         if rc != _lib.SDPA_OK:
             raise RuntimeError(_lib.sdpa_strerror(rc))
 
@@ -291,7 +311,8 @@ def cpu_baseline(name, dtype, budget_s=10.0):
     with threadpool_limits(limits=1):  # 64×64 products stay on one BLAS thread anyway
         t0 = time.perf_counter()
         while True:
-            so.attention(case["q"], case["k"], case["v"], causal=wl.causal, key_lens=case["key_lens"])
+            so.attention(case["q"], case["k"], case["v"], causal=wl.causal, key_lens=case["key_lens"],
+                         window=wl.window)
             reps += 1
             el = time.perf_counter() - t0
             if el >= budget_s:
@@ -325,6 +346,18 @@ def host_description() -> dict:
     return {"cpu_model": model, "usable_cores": len(os.sched_getaffinity(0)), "blas": blas}
 
 
+def _legal_keys(wl, key_lens, b, i):
+    """Number of keys query row i of batch element b may attend to."""
+    L = wl.m if key_lens is None else min(max(int(key_lens[b]), 0), wl.m)
+    if wl.window is not None:
+        left, right = wl.window[0], wl.window[1]
+        c = i + (L - wl.n if len(wl.window) > 2 and wl.window[2] == "bottom_right" else 0)
+        lo = 0 if left is None else min(max(c - left, 0), L)
+        hi = L if right is None else min(max(c + right + 1, 0), L)
+        return max(hi - lo, 0)
+    return min(i + 1, L) if wl.causal else L
+
+
 def oracle_pass(name, dtype, max_s=2.0):
     """The oracle on one workload, single BLAS thread: a whole batch when it is
     small, else a seeded sample of output rows (cost counted per legal pair)."""
@@ -340,7 +373,7 @@ def oracle_pass(name, dtype, max_s=2.0):
             flops, _, _ = algorithmic_work(wl, dtype, case["key_lens"])
             t0 = time.perf_counter()
             so.attention(case["q"], case["k"], case["v"], causal=wl.causal,
-                         key_lens=case["key_lens"])
+                         key_lens=case["key_lens"], window=wl.window)
             el = time.perf_counter() - t0
             return {"tflops": flops / el / 1e12, "ms_per_pass": el * 1e3, "sample": "whole batch"}
         rng = np.random.default_rng(7)
@@ -349,9 +382,9 @@ def oracle_pass(name, dtype, max_s=2.0):
         while time.perf_counter() - t0 < max_s and len(picks) < 4096:
             b, hh, i = int(rng.integers(wl.B)), int(rng.integers(wl.h)), int(rng.integers(wl.n))
             so.attention_rows(case["q"], case["k"], case["v"], [(b, hh, i)], causal=wl.causal,
-                              key_lens=case["key_lens"])
+                              key_lens=case["key_lens"], window=wl.window)
             picks.append((b, hh, i))
-            pairs += (i + 1) if wl.causal else wl.m
+            pairs += _legal_keys(wl, case["key_lens"], b, i)
         el = time.perf_counter() - t0
         flops_s = 2 * (wl.d_k + wl.d_v) * pairs / el
         full, _, _ = algorithmic_work(wl, dtype, case["key_lens"])
@@ -474,7 +507,7 @@ def main():
         for name, dt in EXTRA:
             if (name, dt) == (args.workload, args.dtype):
                 continue
-            st = max(10, min(args.steps, 200)) if name != "long_causal_8k" else 20
+            st = 20 if name.endswith("_8k") else max(10, min(args.steps, 200))
             r = time_workload(name, dt, st, min(args.warmup, 5), clock_warm_s=0.1)
             extra[f"{name}-{dt}"] = {k: r[k] for k in (
                 "ms_per_step", "tflops", "gbs", "frac_mfma_peak", "frac_hbm_peak", "steps",

@@ -39,7 +39,7 @@ extern "C" {
 #define SDPA_ERR_SHAPE       -2 /* a dimension < 1, or an element count overflows   */
 #define SDPA_ERR_UNSUPPORTED -3 /* d_k / d_v not supported (64 only)                 */
 #define SDPA_ERR_ALIGN       -4 /* a pointer is not 16-byte aligned                  */
-#define SDPA_ERR_MASK        -5 /* unknown mask_kind, or causal with n != m          */
+#define SDPA_ERR_MASK        -5 /* unknown mask_kind, causal with n != m, bad window */
 #define SDPA_ERR_DTYPE       -6 /* unknown dtype                                     */
 #define SDPA_ERR_LAUNCH      -7 /* the HIP runtime refused the kernel launch         */
 #define SDPA_ERR_SCALE       -8 /* scale is not finite, or not > 0                   */
@@ -52,6 +52,10 @@ extern "C" {
 /* Mask kinds. */
 #define SDPA_MASK_NONE   0
 #define SDPA_MASK_CAUSAL 1 /* inclusive: query i sees keys j <= i; needs n == m    */
+
+/* Window alignment (sdpa_forward_window). */
+#define SDPA_ALIGN_TOP_LEFT     0 /* query i is at key position i                  */
+#define SDPA_ALIGN_BOTTOM_RIGHT 1 /* query i is at key position i + L - n          */
 
 /*
  * sdpa_forward — one fused forward pass over all B·h heads.
@@ -86,6 +90,40 @@ SDPA_API int sdpa_forward(const void* q, const void* k, const void* v, void* out
                  int32_t B, int32_t h, int32_t n, int32_t m, int32_t d_k, int32_t d_v,
                  float scale, int32_t mask_kind, const int32_t* key_lens,
                  int32_t dtype, void* stream);
+
+/*
+ * sdpa_forward_window — restricted attention: each query sees only a window of
+ * keys around its own position.
+ *
+ * The pages propose restricting self-attention to a neighbourhood of size r
+ * around each output position for long sequences (《精读 Attention Is All You
+ * Need：原始 Transformer 论文》 Table 1 and the discussion after it;
+ * 《Attention Is All You Need：注意力就是你所需要的一切》 §4).  Here query row i
+ * has the aligned position
+ *     c_i = i                 (align = SDPA_ALIGN_TOP_LEFT), or
+ *     c_i = i + L_b - n       (align = SDPA_ALIGN_BOTTOM_RIGHT: the n queries are
+ *                              the last n positions of the L_b keys, as in a
+ *                              decoder step against its cached keys),
+ * where L_b = clamp(key_lens[b], 0, m), or m without key_lens.  Key j is legal
+ * for query i iff
+ *     j < L_b,  j >= c_i - window_left (if window_left >= 0),
+ *     and j <= c_i + window_right (if window_right >= 0);
+ * window_left / window_right = -1 leave that side unbounded.  A neighbourhood
+ * of size r centred on the query is window_left = window_right = r/2 (rounded
+ * down).  sdpa_forward's SDPA_MASK_CAUSAL is the window (-1, 0), top-left;
+ * SDPA_MASK_NONE is (-1, -1).  Any n and m are allowed.  A query with no
+ * legal key returns the zero vector.
+ *
+ * Every other argument, the layout, ownership, execution and error behaviour
+ * are those of sdpa_forward.  Additional errors: SDPA_ERR_MASK if a window
+ * side is < -1 or align is not one of the two SDPA_ALIGN_* values.  Keys
+ * outside a query's window but below L_b may be read (with weight exactly
+ * zero) and must be finite.
+ */
+SDPA_API int sdpa_forward_window(const void* q, const void* k, const void* v, void* out,
+                 int32_t B, int32_t h, int32_t n, int32_t m, int32_t d_k, int32_t d_v,
+                 float scale, int32_t window_left, int32_t window_right, int32_t align,
+                 const int32_t* key_lens, int32_t dtype, void* stream);
 
 /* Static text for a status code (never NULL). */
 SDPA_API const char* sdpa_strerror(int status);

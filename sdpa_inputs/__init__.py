@@ -43,6 +43,7 @@ class Workload:
     seed: int
     dtypes: tuple = field(default=("bf16",))
     what: str = ""
+    window: tuple | None = None  # (left, right[, align]) key window, or None
 
 
 WORKLOADS = {
@@ -67,6 +68,14 @@ WORKLOADS = {
         "long_causal_8k", B=4, h=16, n=8192, m=8192, d_k=64, d_v=64, causal=True,
         key_len_range=None, seed=1005, dtypes=("bf16",),
         what="long-sequence causal self-attention, 8192 tokens, no padding"),
+    # Restricted self-attention (《精读 …》 Table 1: each position attends to a
+    # neighbourhood of size r around it, for long sequences): r = 513 keys
+    # centred on the query, i.e. 256 on either side, on the 8k shape.
+    "local_window_8k": Workload(
+        "local_window_8k", B=4, h=16, n=8192, m=8192, d_k=64, d_v=64, causal=False,
+        key_len_range=None, seed=1006, dtypes=("bf16",), window=(256, 256, "top_left"),
+        what="long-sequence restricted self-attention, 8192 tokens, window of 256 keys "
+             "either side of each query, no padding"),
 }
 
 
@@ -98,7 +107,7 @@ def make_inputs(wl: Workload | str, dtype: str | None = None, seed: int | None =
     Returns a dict with float32 arrays ``q`` [B,h,n,d_k], ``k`` [B,h,m,d_k],
     ``v`` [B,h,m,d_v] holding exactly the device values (bf16-rounded when
     ``dtype == "bf16"``), ``key_lens`` (int32 [B] or None), ``causal``,
-    ``dtype`` and the workload.
+    ``window``, ``dtype`` and the workload.
     """
     if isinstance(wl, str):
         wl = WORKLOADS[wl]
@@ -116,11 +125,11 @@ def make_inputs(wl: Workload | str, dtype: str | None = None, seed: int | None =
     if dtype == "bf16":
         q, k, v = round_to_bf16(q), round_to_bf16(k), round_to_bf16(v)
     return {"q": q, "k": k, "v": v, "key_lens": key_lens, "causal": wl.causal,
-            "dtype": dtype, "workload": wl}
+            "window": wl.window, "dtype": dtype, "workload": wl}
 
 
 def random_case(rng: np.random.Generator, B, h, n, m, d_k, d_v, dtype="f32", causal=False,
-                key_lens=None):
+                key_lens=None, window=None):
     """Free-shape N(0,1) case from an existing generator (for parity sweeps)."""
     q = rng.standard_normal((B, h, n, d_k), dtype=np.float32)
     k = rng.standard_normal((B, h, m, d_k), dtype=np.float32)
@@ -128,4 +137,5 @@ def random_case(rng: np.random.Generator, B, h, n, m, d_k, d_v, dtype="f32", cau
     if dtype == "bf16":
         q, k, v = round_to_bf16(q), round_to_bf16(k), round_to_bf16(v)
     kl = None if key_lens is None else np.asarray(key_lens, dtype=np.int32)
-    return {"q": q, "k": k, "v": v, "key_lens": kl, "causal": causal, "dtype": dtype}
+    return {"q": q, "k": k, "v": v, "key_lens": kl, "causal": causal, "window": window,
+            "dtype": dtype}

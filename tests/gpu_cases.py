@@ -39,7 +39,8 @@ def run_gpu(case: dict, scale=None, out=None):
     kl = None
     if case.get("key_lens") is not None:
         kl = torch.from_numpy(np.asarray(case["key_lens"], dtype=np.int32)).cuda()
-    o = forward(q, k, v, causal=case.get("causal", False), key_lens=kl, scale=scale, out=out)
+    o = forward(q, k, v, causal=case.get("causal", False), key_lens=kl, scale=scale, out=out,
+                window=case.get("window"))
     torch.cuda.synchronize()
     return o, from_device(o)
 

@@ -28,7 +28,7 @@ def lib():
 
 def test_every_declared_entry_point_is_exported(lib):
     names = re.findall(r"SDPA_API\s+[\w\s\*]+?\b(sdpa_\w+)\s*\(", _header())
-    assert set(names) == {"sdpa_forward", "sdpa_strerror", "sdpa_version"}
+    assert set(names) == {"sdpa_forward", "sdpa_forward_window", "sdpa_strerror", "sdpa_version"}
     for name in names:
         assert isinstance(getattr(lib, name), ctypes._CFuncPtr)
 
@@ -85,6 +85,48 @@ def call(q=P, k=2 * P, v=3 * P, out=4 * P, B=2, h=2, n=8, m=8, d_k=64, d_v=64, s
 ])
 def test_validation_rejects_before_any_hip_call(kw, code):
     assert call(**kw) == code
+
+
+def call_window(wl=-1, wr=-1, align=0, **kw):
+    args = dict(q=P, k=2 * P, v=3 * P, out=4 * P, B=2, h=2, n=8, m=8, d_k=64, d_v=64, scale=0.125,
+                key_lens=None, dtype=1)
+    args.update(kw)
+    return _lib.sdpa_forward_window(args["q"], args["k"], args["v"], args["out"], args["B"],
+                                    args["h"], args["n"], args["m"], args["d_k"], args["d_v"],
+                                    args["scale"], wl, wr, align, args["key_lens"], args["dtype"],
+                                    None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(wl=-2), _lib.SDPA_ERR_MASK),
+    (dict(wr=-7), _lib.SDPA_ERR_MASK),
+    (dict(align=2), _lib.SDPA_ERR_MASK),
+    (dict(align=-1), _lib.SDPA_ERR_MASK),
+    (dict(q=None), _lib.SDPA_ERR_NULL),
+    (dict(n=0), _lib.SDPA_ERR_SHAPE),
+    (dict(d_k=128, d_v=128), _lib.SDPA_ERR_UNSUPPORTED),
+    (dict(dtype=3), _lib.SDPA_ERR_DTYPE),
+    (dict(scale=math.inf), _lib.SDPA_ERR_SCALE),
+    (dict(out=P), _lib.SDPA_ERR_ALIAS),
+    (dict(q=P + 4), _lib.SDPA_ERR_ALIGN),
+])
+def test_window_validation_rejects_before_any_hip_call(kw, code, lib):
+    """The window entry point shares sdpa_forward's checks and adds its own.
+
+    Note: n != m is legal with a window (any alignment); only bad sides or an
+    unknown alignment are mask errors."""
+    assert call_window(**kw) == code
+
+
+def test_torch_wrapper_rejects_bad_windows():
+    import torch
+
+    from transformer_attention_sdpa_amd import forward
+
+    x = torch.zeros(1, 1, 4, 64)
+    for kw in (dict(window=(1, 1), causal=True), dict(window=(-1, 2)), dict(window=(1, 1, "middle"))):
+        with pytest.raises(ValueError):
+            forward(x, x, x, **kw)
 
 
 def test_torch_wrapper_rejects_cpu_tensors():

@@ -22,7 +22,14 @@ def _brute(wl, key_lens):
     kv_rows = 0
     for b in range(wl.B):
         kl = None if key_lens is None else int(key_lens[b])
-        vis = so.visible_keys(np.arange(wl.n), wl.m, wl.causal, kl)
+        if wl.window is None:
+            vis = so.visible_keys(np.arange(wl.n), wl.m, wl.causal, kl)
+        else:
+            L = wl.m if kl is None else min(max(kl, 0), wl.m)
+            align = wl.window[2] if len(wl.window) > 2 else "top_left"
+            shift = L - wl.n if align == "bottom_right" else 0
+            vis = so.visible_keys(np.arange(wl.n), wl.m, wl.causal, kl,
+                                  window=(wl.window[0], wl.window[1], shift))
         pairs += wl.h * int(vis.sum())
         L = wl.m if kl is None else min(max(kl, 0), wl.m)
         kv_rows += wl.h * L
@@ -54,3 +61,13 @@ def test_key_length_edge_cases():
     assert flops == 4 * 64 * pairs
     assert kv_rows == 2 * (0 + 1 + 64 + 64)
     assert nbytes == 2 * (2 * 4 * 2 * 64 * 64 + 2 * kv_rows * 64)
+
+
+@pytest.mark.parametrize("window", [(3, 5, "top_left"), (0, 0, "top_left"), (None, 2, "bottom_right"),
+                                    (7, None, "bottom_right"), (2, 0, "bottom_right")])
+def test_window_pair_count(window):
+    wl = dataclasses.replace(WORKLOADS["cross_big"], B=3, h=2, n=20, m=40, window=window)
+    kl = np.array([0, 13, 40], dtype=np.int32)
+    flops, _, _ = bench.algorithmic_work(wl, "bf16", kl)
+    pairs, _ = _brute(wl, kl)
+    assert flops == 4 * 64 * pairs

@@ -24,7 +24,7 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 def _oracle(case, scale=None):
     return so.attention(case["q"], case["k"], case["v"], scale=scale, causal=case["causal"],
-                        key_lens=case["key_lens"])
+                        key_lens=case["key_lens"], window=case.get("window"))
 
 
 # --- the five workloads at their real sizes ---------------------------------
@@ -375,3 +375,109 @@ def test_long_causal_16k_sampled(gpu_lib):
     ref = so.attention_rows(case["q"], case["k"], case["v"], picks, causal=True)
     g = np.stack([got[b, hh, i] for (b, hh, i) in picks])
     assert max_abs_err(g, ref) <= TOL["bf16"]
+
+
+# --- restricted attention: key windows --------------------------------------
+
+WIN_SHAPES = [  # B, h, n, m, key_lens: both kernel families, decode-like and ragged cases
+    (2, 2, 64, 64, [64, 37]),
+    (1, 2, 48, 64, [50]),
+    (1, 2, 40, 64, [10]),       # bottom-right with fewer keys than queries: empty rows
+    (2, 1, 1, 300, [300, 77]),  # one decoding query against cached keys
+    (2, 2, 200, 200, None),
+    (1, 2, 130, 300, [260]),
+]
+WINDOWS = [(2, 1, "top_left"), (0, 0, "top_left"), (None, 5, "top_left"), (7, None, "top_left"),
+           (16, 16, "top_left"), (None, 0, "bottom_right"), (3, 0, "bottom_right"),
+           (40, 40, "bottom_right"), (0, 0, "bottom_right")]
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", WIN_SHAPES, ids=[f"{s[0]}x{s[1]}x{s[2]}x{s[3]}" for s in WIN_SHAPES])
+def test_window_parity(gpu_lib, dt, shape):
+    B, h, n, m, kl = shape
+    rng = np.random.default_rng(zlib.crc32(repr((dt, shape)).encode()))
+    base = random_case(rng, B, h, n, m, 64, 64, dtype=dt, key_lens=kl)
+    worst = 0.0
+    for win in WINDOWS:
+        case = dict(base, window=win)
+        _, got = run_gpu(case)
+        ref = _oracle(case)
+        err = max_abs_err(got, ref)
+        worst = max(worst, err)
+        assert err <= TOL[dt], (win, err)
+        # rows with no legal key are exactly zero
+        for b in range(B):
+            L = m if kl is None else min(kl[b], m)
+            for i in range(n):
+                lo, hi = _window_range(i, n, L, win)
+                if hi <= lo:
+                    assert np.all(got[b, :, i] == 0.0), (win, b, i)
+    print(f"windows {dt} {shape}: max abs err {worst:.3e}")
+
+
+def _window_range(i, n, L, win):
+    left, right, align = win
+    c = i if align == "top_left" else i + L - n
+    lo = 0 if left is None else max(0, c - left)
+    hi = L if right is None else min(L, c + right + 1)
+    return lo, hi
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("n", [64, 300])
+def test_window_special_cases_are_bitwise_the_plain_masks(gpu_lib, dt, n):
+    """(None, 0) top-left is the causal mask and (None, None) is no mask: the
+    same kernels run, so the outputs agree bit for bit."""
+    import torch
+
+    rng = np.random.default_rng(41 + n)
+    case = random_case(rng, 2, 2, n, n, 64, 64, dtype=dt, key_lens=[n, n // 2])
+    o_causal, _ = run_gpu(dict(case, causal=True))
+    o_win, _ = run_gpu(dict(case, window=(None, 0)))
+    assert torch.equal(o_causal, o_win)
+    o_plain, _ = run_gpu(case)
+    o_open, _ = run_gpu(dict(case, window=(None, None)))
+    assert torch.equal(o_plain, o_open)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_keys_outside_a_window_do_not_leak(gpu_lib, dt):
+    """Changing key/value row j leaves bitwise unchanged every query whose
+    window does not contain j."""
+    import torch
+
+    rng = np.random.default_rng(43)
+    n, win = 400, (20, 10, "top_left")
+    case = dict(random_case(rng, 1, 2, n, n, 64, 64, dtype=dt), window=win)
+    o1, _ = run_gpu(case)
+    j = 211
+    case["k"][:, :, j] *= -3.0
+    case["v"][:, :, j] += 5.0
+    o2, _ = run_gpu(case)
+    sees = [i for i in range(n) if i - 20 <= j <= i + 10]  # j inside [i - left, i + right]
+    blind = [i for i in range(n) if i not in sees]
+    assert torch.equal(o1[:, :, blind], o2[:, :, blind])
+    assert not torch.equal(o1[:, :, sees], o2[:, :, sees])
+
+
+def test_local_window_8k_sampled_rows(gpu_lib):
+    """n = m = 8192, 64 heads, 256 keys either side of each query, bf16."""
+    case = make_inputs("local_window_8k", "bf16")
+    _, got = run_gpu(case)
+    wl = WORKLOADS["local_window_8k"]
+    assert np.isfinite(got).all()
+    rng = np.random.default_rng(101)
+    rows = [0, 1, 255, 256, 257, 511, 512, 1000, 4095, 4096, 7935, 7936, 8190, 8191]
+    picks = []
+    for b in range(wl.B):
+        for h in range(wl.h):
+            for i in rows[:3] + list(rng.choice(wl.n, size=3, replace=False)) + rows[-2:]:
+                picks.append((b, h, int(i)))
+    for i in rows:
+        picks.append((2, 9, i))
+    ref = so.attention_rows(case["q"], case["k"], case["v"], picks, window=wl.window)
+    g = np.stack([got[b, h, i] for (b, h, i) in picks])
+    err = max_abs_err(g, ref)
+    print(f"local_window_8k: {len(picks)} sampled rows, max abs err {err:.3e}")
+    assert err <= TOL["bf16"]

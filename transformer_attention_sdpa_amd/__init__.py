@@ -12,21 +12,29 @@ from __future__ import annotations
 import math
 
 from . import _lib
-from ._lib import sdpa_forward, sdpa_strerror, sdpa_version  # noqa: F401
+from ._lib import sdpa_forward, sdpa_forward_window, sdpa_strerror, sdpa_version  # noqa: F401
 
-__all__ = ["forward", "sdpa_forward", "sdpa_strerror", "sdpa_version"]
+__all__ = ["forward", "sdpa_forward", "sdpa_forward_window", "sdpa_strerror", "sdpa_version"]
 
 
 def forward(q, k, v, *, causal: bool = False, key_lens=None, scale: float | None = None,
-            out=None):
+            out=None, window=None):
     """Attention over [B, h, n, d_k] queries and [B, h, m, d] keys/values.
 
     key_lens: None or an int32 tensor [B] on the same device (key j of batch
-    element b is legal iff j < key_lens[b]).  Returns ``out`` ([B, h, n, d_v],
-    same dtype as q).  Raises RuntimeError with the library's message on a
-    nonzero status.
+    element b is legal iff j < key_lens[b]).  window: None, or
+    (left, right) / (left, right, align) for restricted attention: query i
+    sees keys c_i - left .. c_i + right (None = unbounded side), where
+    c_i = i for align "top_left" (default) and c_i = i + L - n for
+    "bottom_right" (L = the batch element's key length); see
+    ``sdpa_forward_window`` in include/sdpa.h.  Not combined with ``causal``.
+    Returns ``out`` ([B, h, n, d_v], same dtype as q).  Raises RuntimeError
+    with the library's message on a nonzero status.
     """
     import torch
+
+    if window is not None and causal:
+        raise ValueError("give the causal mask as window=(None, 0) instead of combining both")
 
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be 4-D [B, h, len, d]")
@@ -62,13 +70,29 @@ def forward(q, k, v, *, causal: bool = False, key_lens=None, scale: float | None
         raise ValueError("out must be a contiguous [B, h, n, d_v] tensor of q's dtype on q's device")
     if scale is None:
         scale = 1.0 / math.sqrt(d_k)
+    if window is not None:
+        left, right = window[0], window[1]
+        align = window[2] if len(window) > 2 else "top_left"
+        if align not in ("top_left", "bottom_right"):
+            raise ValueError(f"unknown window alignment {align!r}")
+        if any(x is not None and int(x) < 0 for x in (left, right)):
+            raise ValueError("window sides are >= 0 or None (unbounded)")
+        # the library treats any side wider than n + m as unbounded
+        wl = -1 if left is None else min(int(left), 2**31 - 1)
+        wr = -1 if right is None else min(int(right), 2**31 - 1)
+        al = _lib.SDPA_ALIGN_BOTTOM_RIGHT if align == "bottom_right" else _lib.SDPA_ALIGN_TOP_LEFT
     # The library launches on the calling thread's current HIP device.
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
-        rc = sdpa_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, h, n, m,
-                          d_k, d_v, float(scale),
-                          _lib.SDPA_MASK_CAUSAL if causal else _lib.SDPA_MASK_NONE, kl_ptr, dt,
-                          stream)
+        if window is None:
+            rc = sdpa_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, h, n,
+                              m, d_k, d_v, float(scale),
+                              _lib.SDPA_MASK_CAUSAL if causal else _lib.SDPA_MASK_NONE, kl_ptr,
+                              dt, stream)
+        else:
+            rc = sdpa_forward_window(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B,
+                                     h, n, m, d_k, d_v, float(scale), wl, wr, al, kl_ptr, dt,
+                                     stream)
     if rc != _lib.SDPA_OK:
         raise RuntimeError(f"sdpa_forward failed ({rc}): {sdpa_strerror(rc)}")
     return out

@@ -28,6 +28,8 @@ SDPA_F32 = 0
 SDPA_BF16 = 1
 SDPA_MASK_NONE = 0
 SDPA_MASK_CAUSAL = 1
+SDPA_ALIGN_TOP_LEFT = 0
+SDPA_ALIGN_BOTTOM_RIGHT = 1
 
 _lib = None
 
@@ -46,6 +48,9 @@ def load() -> ctypes.CDLL:
     lib.sdpa_forward.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                  ctypes.c_float, i32, vp, i32, vp]
     lib.sdpa_forward.restype = ctypes.c_int
+    lib.sdpa_forward_window.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                        ctypes.c_float, i32, i32, i32, vp, i32, vp]
+    lib.sdpa_forward_window.restype = ctypes.c_int
     lib.sdpa_strerror.argtypes = [ctypes.c_int]
     lib.sdpa_strerror.restype = ctypes.c_char_p
     lib.sdpa_version.argtypes = []
@@ -59,6 +64,13 @@ def sdpa_forward(q, k, v, out, B, h, n, m, d_k, d_v, scale, mask_kind, key_lens,
     """Forward to the C entry point; pointers and the stream are plain integers (or None)."""
     return load().sdpa_forward(q, k, v, out, B, h, n, m, d_k, d_v, scale, mask_kind,
                                key_lens, dtype, stream)
+
+
+def sdpa_forward_window(q, k, v, out, B, h, n, m, d_k, d_v, scale, window_left, window_right,
+                        align, key_lens, dtype, stream) -> int:
+    """Forward to the C entry point of the same name (restricted attention)."""
+    return load().sdpa_forward_window(q, k, v, out, B, h, n, m, d_k, d_v, scale, window_left,
+                                      window_right, align, key_lens, dtype, stream)
 
 
 def sdpa_strerror(status: int) -> str:

@@ -12,7 +12,7 @@
 
 namespace {
 
-constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;
+constexpr int kVersion = 1 * 10000 + 1 * 100 + 0;  // 1.1.0: sdpa_forward_window
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -22,8 +22,9 @@ bool overlap(const void* a, uint64_t na, const void* b, uint64_t nb) {
     return x < y + nb && y < x + na;
 }
 
+// Everything but the mask: pointers, dtype, shapes, scale, alignment, aliasing.
 int validate(const void* q, const void* k, const void* v, void* out, int32_t B, int32_t h,
-             int32_t n, int32_t m, int32_t d_k, int32_t d_v, float scale, int32_t mask_kind,
+             int32_t n, int32_t m, int32_t d_k, int32_t d_v, float scale,
              const int32_t* key_lens, int32_t dtype) {
     if (!q || !k || !v || !out) return SDPA_ERR_NULL;
     if (dtype != SDPA_F32 && dtype != SDPA_BF16) return SDPA_ERR_DTYPE;
@@ -36,8 +37,6 @@ int validate(const void* q, const void* k, const void* v, void* out, int32_t B, 
     if (heads * rows * width >= (1ull << 48)) return SDPA_ERR_SHAPE;
     if (heads * (((uint64_t)n + 31) / 32) >= (1ull << 31)) return SDPA_ERR_SHAPE;
     if (d_k != sdpa::kHeadDim || d_v != sdpa::kHeadDim) return SDPA_ERR_UNSUPPORTED;
-    if (mask_kind != SDPA_MASK_NONE && mask_kind != SDPA_MASK_CAUSAL) return SDPA_ERR_MASK;
-    if (mask_kind == SDPA_MASK_CAUSAL && n != m) return SDPA_ERR_MASK;
     if (!std::isfinite(scale) || !(scale > 0.f)) return SDPA_ERR_SCALE;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return SDPA_ERR_ALIGN;
     if (key_lens && (reinterpret_cast<uintptr_t>(key_lens) & 3u)) return SDPA_ERR_ALIGN;
@@ -50,18 +49,44 @@ int validate(const void* q, const void* k, const void* v, void* out, int32_t B, 
     return SDPA_OK;
 }
 
+int launch(const sdpa::Args& a, int32_t dtype, void* stream) {
+    const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const hipError_t e = dtype == SDPA_BF16 ? sdpa::launch_bf16(a, s) : sdpa::launch_f32(a, s);
+    return e == hipSuccess ? SDPA_OK : SDPA_ERR_LAUNCH;
+}
+
 }  // namespace
 
 extern "C" int sdpa_forward(const void* q, const void* k, const void* v, void* out, int32_t B,
                             int32_t h, int32_t n, int32_t m, int32_t d_k, int32_t d_v, float scale,
                             int32_t mask_kind, const int32_t* key_lens, int32_t dtype,
                             void* stream) {
-    const int st = validate(q, k, v, out, B, h, n, m, d_k, d_v, scale, mask_kind, key_lens, dtype);
+    const int st = validate(q, k, v, out, B, h, n, m, d_k, d_v, scale, key_lens, dtype);
     if (st != SDPA_OK) return st;
-    sdpa::Args a{q, k, v, out, B, h, n, m, scale, mask_kind == SDPA_MASK_CAUSAL ? 1 : 0, key_lens};
-    const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    const hipError_t e = dtype == SDPA_BF16 ? sdpa::launch_bf16(a, s) : sdpa::launch_f32(a, s);
-    return e == hipSuccess ? SDPA_OK : SDPA_ERR_LAUNCH;
+    if (mask_kind != SDPA_MASK_NONE && mask_kind != SDPA_MASK_CAUSAL) return SDPA_ERR_MASK;
+    if (mask_kind == SDPA_MASK_CAUSAL && n != m) return SDPA_ERR_MASK;
+    // causal = the window (unbounded, 0) at top-left alignment
+    const sdpa::Args a{q, k, v, out, B, h, n, m, scale, -1, mask_kind == SDPA_MASK_CAUSAL ? 0 : -1,
+                       0, key_lens};
+    return launch(a, dtype, stream);
+}
+
+extern "C" int sdpa_forward_window(const void* q, const void* k, const void* v, void* out,
+                                   int32_t B, int32_t h, int32_t n, int32_t m, int32_t d_k,
+                                   int32_t d_v, float scale, int32_t window_left,
+                                   int32_t window_right, int32_t align, const int32_t* key_lens,
+                                   int32_t dtype, void* stream) {
+    const int st = validate(q, k, v, out, B, h, n, m, d_k, d_v, scale, key_lens, dtype);
+    if (st != SDPA_OK) return st;
+    if (window_left < -1 || window_right < -1) return SDPA_ERR_MASK;
+    if (align != SDPA_ALIGN_TOP_LEFT && align != SDPA_ALIGN_BOTTOM_RIGHT) return SDPA_ERR_MASK;
+    // A side wider than n + m reaches past every key from every query: unbounded.
+    const int64_t reach = (int64_t)n + m;
+    const int32_t wl = window_left > reach ? -1 : window_left;
+    const int32_t wr = window_right > reach ? -1 : window_right;
+    const sdpa::Args a{q, k, v, out, B, h, n, m, scale, wl, wr,
+                       align == SDPA_ALIGN_BOTTOM_RIGHT ? 1 : 0, key_lens};
+    return launch(a, dtype, stream);
 }
 
 extern "C" const char* sdpa_strerror(int status) {
@@ -71,7 +96,8 @@ extern "C" const char* sdpa_strerror(int status) {
         case SDPA_ERR_SHAPE: return "bad shape: a dimension is < 1 or an element count overflows";
         case SDPA_ERR_UNSUPPORTED: return "unsupported head width: the library supports d_k = d_v = 64";
         case SDPA_ERR_ALIGN: return "a device pointer is not 16-byte aligned (key_lens: 4-byte)";
-        case SDPA_ERR_MASK: return "bad mask: unknown mask_kind, or causal with n != m";
+        case SDPA_ERR_MASK:
+            return "bad mask: unknown mask_kind, causal with n != m, window side < -1 or unknown align";
         case SDPA_ERR_DTYPE: return "unknown dtype (SDPA_F32 = 0, SDPA_BF16 = 1)";
         case SDPA_ERR_LAUNCH: return "the HIP runtime refused the kernel launch";
         case SDPA_ERR_SCALE: return "scale must be finite and > 0";

@@ -5,7 +5,9 @@
 // ("缩放点积注意力：点积为什么要缩放"), softmax(Q Kᵀ·scale) V, for every
 // (batch, head) pair, with the decoder's illegal logits set to −∞ before the
 // softmax (《Attention Is All You Need：注意力就是你所需要的一切》 §3.2.3) and key
-// padding handled the same way.  Scores and softmax are fp32; the weights are
+// padding handled the same way.  The mask is a key window around each query
+// (KeyWindow): the causal mask, and the restricted attention of the same
+// pages' Table 1, are both windows.  Scores and softmax are fp32; the weights are
 // rounded to bf16 (RNE) for the P·V product, which accumulates in fp32; the
 // output is rounded once to bf16.
 //
@@ -36,8 +38,10 @@
 //   * one FMA + one v_exp_f32 per score (scale·log2 e folded into the FMA);
 //   * row sums with v_dot2_f32_bf16 on the packed bf16 weights (the same values
 //     that enter P·V);
-//   * masking (selects to −∞) only on tiles that straddle the causal diagonal or
-//     the padding edge; tiles entirely after a wave's queries are skipped;
+//   * masking (selects to −∞) only on tiles that straddle a window edge (the
+//     causal diagonal is one) or the padding edge; the tile loop covers only
+//     the keys the workgroup's queries may see, and a wave skips tiles wholly
+//     outside its own queries' windows;
 //   * LDS addresses are per-lane constants plus immediate offsets (the tile
 //     loop is unrolled by two so the buffer index is a constant).
 #include "sdpa_common.hpp"
@@ -77,7 +81,11 @@ struct LongKernel {
     // Per-workgroup scalars.
     const char* kg;
     const char* vg;
-    int L, causal, wq0;
+    int L, wq0;
+    KeyWindow win;
+    // Per-wave key ranges: [wlo, whi) is needed by some query of the wave,
+    // [flo, fhi) is legal for every query of the wave.
+    int wlo, whi, flo, fhi;
     float c_log2;
 
     __device__ void issue_tile_load(int t, int buf) {
@@ -92,18 +100,19 @@ struct LongKernel {
         }
     }
 
-    // −∞ on the illegal logits of sub-block qt (tiles on the causal diagonal or
-    // the padding edge).  Register i of sub-tile kt is key
+    // −∞ on the illegal logits of sub-block qt (tiles on a window edge or the
+    // padding edge).  Register i of sub-tile kt is key
     // k0 + 32·kt + 8·(i/4) + 4·hf + i%4 of query wq0 + 32·qt + l32.
     __device__ void mask_block(int qt, int k0, f32x16 (&s)[2]) {
         const int qrow = wq0 + 32 * qt + l32;
-        const int lim = (causal ? min(L, qrow + 1) : L) - k0 - 4 * hf;
+        const int llo = win.lo(qrow) - k0 - 4 * hf;
+        const int lhi = win.hi(qrow) - k0 - 4 * hf;
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int off = 32 * kt + 8 * (i >> 2) + (i & 3);
-                s[kt][i] = off < lim ? s[kt][i] : -INFINITY;
+                s[kt][i] = (off >= llo && off < lhi) ? s[kt][i] : -INFINITY;
             }
     }
 
@@ -157,8 +166,8 @@ struct LongKernel {
                 for (int qt = 0; qt < QT; ++qt) s[qt][kt] = mfma32x32x16_bf16(a, qop[qt][ks], s[qt][kt]);
             }
 
-        // −∞ on illegal logits: tiles on the causal diagonal or the padding edge.
-        if ((k0 + BN > L) || (causal && k0 + BN - 1 > wq0)) {
+        // −∞ on illegal logits: tiles not wholly legal for every query of the wave.
+        if (k0 < flo || k0 + BN > fhi) {
 #pragma unroll
             for (int qt = 0; qt < QT; ++qt) mask_block(qt, k0, s[qt]);
         }
@@ -230,10 +239,10 @@ struct LongKernel {
     // other buffer was last read before the previous barrier, so overwriting it
     // here is safe.
     template <int BUF>
-    __device__ void step(int t, int ntiles) {
-        if (t + 1 < ntiles) issue_tile_load(t + 1, BUF ^ 1);
+    __device__ void step(int t, int tend) {
+        if (t + 1 < tend) issue_tile_load(t + 1, BUF ^ 1);
         const int k0 = t * BN;
-        if (!(causal && k0 > wq0 + QW - 1)) {  // else: tile after all our queries
+        if (k0 < whi && k0 + BN > wlo) {  // else: no query of this wave sees the tile
             compute_tile<BUF>(k0);
         }
         wait_vmem();
@@ -245,7 +254,7 @@ template <int NW>
 __global__ __launch_bounds__(NW * 64) void sdpa_long_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
-    int BH, int H, int n, int m, float c_log2, int causal,
+    int BH, int H, int n, int m, float c_log2, int wl, int wr, int bottom_right,
     const int32_t* __restrict__ key_lens, int nqb) {
     using KT = LongKernel<NW>;
     __shared__ __attribute__((aligned(16))) char lds[2 * 2 * TILE_BYTES];
@@ -258,7 +267,6 @@ __global__ __launch_bounds__(NW * 64) void sdpa_long_bf16(
     k.l32 = k.lane & 31;
     k.hf = k.lane >> 5;
     k.gi = k.lane & 15;
-    k.causal = causal;
     k.c_log2 = c_log2;
 
     // Heaviest query blocks (latest under a causal mask) are dispatched first;
@@ -277,15 +285,25 @@ __global__ __launch_bounds__(NW * 64) void sdpa_long_bf16(
         L = t < 0 ? 0 : (t > m ? m : t);
     }
     k.L = L;
-    int kend = L;
-    if (causal) kend = min(kend, q0 + KT::BM);
-    const int ntiles = (kend + BN - 1) / BN;
+    k.win = KeyWindow{wl, wr, bottom_right ? L - n : 0, L};
+    // Key tiles [tbeg, tend): the keys any query of the block may see.
+    const int qlast = min(q0 + KT::BM, n) - 1;
+    const int kbeg = k.win.lo(q0), kend = k.win.hi(qlast);
+    const int tbeg = kbeg / BN;
+    const int tend = kend > kbeg ? (kend + BN - 1) / BN : tbeg;
 
     const size_t qbase = (size_t)bh * n * D;
     const size_t kvbase = (size_t)bh * m * D;
     k.kg = reinterpret_cast<const char*>(K + kvbase);
     k.vg = reinterpret_cast<const char*>(V + kvbase);
     k.wq0 = q0 + w * QW;
+    {
+        const int wlast = min(k.wq0 + QW, n) - 1;  // < wq0 for a wave past n: empty
+        k.wlo = wlast < k.wq0 ? 0 : k.win.lo(k.wq0);
+        k.whi = wlast < k.wq0 ? 0 : k.win.hi(wlast);
+        k.flo = wlast < k.wq0 ? 0 : k.win.lo(wlast);
+        k.fhi = wlast < k.wq0 ? 0 : k.win.hi(k.wq0);
+    }
 
     // Per-lane LDS read offsets (tile-relative, buffer 0).
     {
@@ -333,17 +351,17 @@ __global__ __launch_bounds__(NW * 64) void sdpa_long_bf16(
         k.lsum[qt] = 0.f;
     }
 
-    if (ntiles > 0) {
-        k.issue_tile_load(0, 0);
+    if (tend > tbeg) {
+        k.issue_tile_load(tbeg, 0);
         wait_vmem();
     }
     __syncthreads();
-    int t = 0;
-    for (; t + 1 < ntiles; t += 2) {
-        k.template step<0>(t, ntiles);
-        k.template step<1>(t + 1, ntiles);
+    int t = tbeg;
+    for (; t + 1 < tend; t += 2) {
+        k.template step<0>(t, tend);
+        k.template step<1>(t + 1, tend);
     }
-    if (t < ntiles) k.template step<0>(t, ntiles);
+    if (t < tend) k.template step<0>(t, tend);
 
     // ---- Oᵀ / l and store.  Register i of oacc[qt][dt] is dv = 32·dt + 8·(i/4)
     // + 4·hf + i%4 of query wq0 + 32·qt + l32.
@@ -378,15 +396,22 @@ hipError_t launch_long(const Args& a, hipStream_t stream) {
     const int nqb = (a.n + NW * QW - 1) / (NW * QW);
     hipLaunchKernelGGL(sdpa_long_bf16<NW>, dim3(nqb * BH), dim3(NW * 64), 0, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                       (uint16_t*)a.out, BH, a.H, a.n, a.m, c_log2, a.causal, a.key_lens, nqb);
+                       (uint16_t*)a.out, BH, a.H, a.n, a.m, c_log2, a.wl, a.wr, a.bottom_right,
+                       a.key_lens, nqb);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_bf16_long(const Args& a, hipStream_t stream) {
-    // 4 waves (256 queries) per workgroup once there are enough query blocks to
-    // fill the chip; 2 waves (128 queries) otherwise.
+    // A window bounded on both sides and narrower than 2048 keys: 2 waves
+    // (128 queries) per workgroup.  The workgroup streams the union of its
+    // queries' windows, 64·NW + wl + wr keys, while each wave needs only
+    // 64 + wl + wr of them; with 4 waves the other waves idle at the barrier
+    // on a quarter of the tiles of a 512-key window.
+    if (a.wl >= 0 && a.wr >= 0 && (long long)a.wl + a.wr < 2048) return launch_long<2>(a, stream);
+    // Otherwise 4 waves (256 queries) per workgroup once there are enough query
+    // blocks to fill the chip; 2 waves (128 queries) below that.
     const long long blocks4 = (long long)a.B * a.H * ((a.n + 4 * QW - 1) / (4 * QW));
     return blocks4 >= 1024 ? launch_long<4>(a, stream) : launch_long<2>(a, stream);
 }

@@ -23,16 +23,18 @@
 //     64 × 8 heads of 64 × 64);
 //   * the output goes through LDS so that each store instruction writes whole
 //     128-byte rows;
-//   * key tiles of 16 wholly past the key length (or, causal, past the wave's
-//     queries) are skipped in both products, and only tiles that straddle the
-//     padding edge or the diagonal are masked;
+//   * key tiles of 16 that no query of the wave may see (past the key length,
+//     or outside the queries' key windows: after the diagonal when causal)
+//     are skipped in both products, and only tiles that straddle the padding
+//     edge or a window edge are masked;
 //   * Sᵀ = K·Qᵀ and Oᵀ = Vᵀ·Pᵀ (transposed, as in the long kernel) so the row
 //     max/sum are lane-local plus two half/quarter-wave exchanges, and Vᵀ comes
 //     from LDS transpose reads (ds_read_b64_tr_b16).
 //
 // Same arithmetic contract as the long kernel: fp32 scores and softmax, −∞ on
 // illegal logits (《Attention Is All You Need：注意力就是你所需要的一切》
-// §3.2.3), weights rounded to bf16 for P·V with fp32 accumulation, output
+// §3.2.3) — the keys outside each query's window (KeyWindow) and past the key
+// length — weights rounded to bf16 for P·V with fp32 accumulation, output
 // rounded once to bf16.
 #include "sdpa_common.hpp"
 
@@ -67,7 +69,8 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 __global__ __launch_bounds__(NT) void sdpa_short_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
-    int H, int n, int m, float c_log2, int causal, const int32_t* __restrict__ key_lens) {
+    int H, int n, int m, float c_log2, int wl, int wr, int bottom_right,
+    const int32_t* __restrict__ key_lens) {
     // K tile at 0, Q tile at 8 KiB, V tile at 16 KiB (64 rows × 128 B each).
     __shared__ __attribute__((aligned(16))) char lds[3 * MAXLEN * 128];
     const u32x4* sK = reinterpret_cast<const u32x4*>(lds);
@@ -127,13 +130,17 @@ __global__ __launch_bounds__(NT) void sdpa_short_bf16(
     qop[0] = __builtin_bit_cast(bf16x8, sQ[swz(q, G)]);
     qop[1] = __builtin_bit_cast(bf16x8, sQ[swz(q, 4 + G)]);
 
-    // Key tiles with any legal key for this wave: below the key length and
-    // (causal) not after the wave's last query (tile w holds its diagonal).
-    int nkt = (L + 15) >> 4;
-    if (causal) nkt = min(nkt, w + 1);
-    // Legal keys of this lane's query: key < lim.  Register r of tile kt is key
-    // 16·kt + 4·G + r, so the test is 16·kt + r < lim − 4·G.
-    const int lim = (causal ? min(L, q + 1) : L) - 4 * G;
+    // Key tiles [kt0, nkt) hold every key some query of this wave may see;
+    // keys in [flo, fhi) are legal for all of its queries.
+    const KeyWindow win{wl, wr, bottom_right ? L - n : 0, L};
+    const int wfirst = w * QW, wlast = min(w * QW + QW, n) - 1;
+    const int wlo = win.lo(wfirst), whi = win.hi(wlast);
+    const int kt0 = wlo >> 4;
+    const int nkt = whi > wlo ? (whi + 15) >> 4 : kt0;
+    const int flo = win.lo(wlast), fhi = win.hi(wfirst);
+    // Legal keys of this lane's query: [lo, hi).  Register r of tile kt is key
+    // 16·kt + 4·G + r, so the test is llo <= 16·kt + r < lhi.
+    const int llo = win.lo(q) - 4 * G, lhi = win.hi(q) - 4 * G;
 
     // Sᵀ = K · Qᵀ: register r of tile kt is key 16·kt + 4·G + r.
     f32x4 s[4];
@@ -143,7 +150,7 @@ __global__ __launch_bounds__(NT) void sdpa_short_bf16(
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
             s[kt] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-            if (kt < nkt) {  // uniform
+            if (kt >= kt0 && kt < nkt) {  // uniform
                 const int krow = 16 * kt + l16;
                 f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -151,9 +158,12 @@ __global__ __launch_bounds__(NT) void sdpa_short_bf16(
                     const bf16x8 a = __builtin_bit_cast(bf16x8, sK[swz(krow, 4 * ks + G)]);
                     acc = mfma16(a, qop[ks], acc);
                 }
-                if (16 * kt + 16 > L || (causal && kt == w)) {  // uniform: tile has illegal keys
+                if (16 * kt < flo || 16 * kt + 16 > fhi) {  // uniform: tile has illegal keys
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) acc[r] = (16 * kt + r < lim) ? acc[r] : -INFINITY;
+                    for (int r = 0; r < 4; ++r) {
+                        const int off = 16 * kt + r;
+                        acc[r] = (off >= llo && off < lhi) ? acc[r] : -INFINITY;
+                    }
                 }
                 s[kt] = acc;
             }
@@ -167,7 +177,8 @@ __global__ __launch_bounds__(NT) void sdpa_short_bf16(
         for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const float p = kt < nkt ? exp2_hw(__builtin_fmaf(s[kt][r], c_log2, -mc)) : 0.f;
+                const float p = (kt >= kt0 && kt < nkt) ? exp2_hw(__builtin_fmaf(s[kt][r], c_log2, -mc))
+                                                        : 0.f;
                 s[kt][r] = p;
                 l += p;
             }
@@ -190,7 +201,7 @@ __global__ __launch_bounds__(NT) void sdpa_short_bf16(
     const char* vb = sVb;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-        if (2 * j >= nkt) continue;  // uniform: all these weights are zero
+        if (2 * j >= nkt || 2 * j + 1 < kt0) continue;  // uniform: all these weights are zero
         const int r0 = 32 * j + 4 * G + (l16 >> 2);
         const int r1 = r0 + 16;
 #pragma unroll
@@ -239,7 +250,8 @@ hipError_t launch_bf16_short(const Args& a, hipStream_t stream) {
     const float c_log2 = (float)((double)a.scale * 1.4426950408889634);  // scale·log2(e)
     hipLaunchKernelGGL(sdpa_short_bf16, dim3(a.B * a.H), dim3(NT), 0, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                       (uint16_t*)a.out, a.H, a.n, a.m, c_log2, a.causal, a.key_lens);
+                       (uint16_t*)a.out, a.H, a.n, a.m, c_log2, a.wl, a.wr, a.bottom_right,
+                       a.key_lens);
     return hipGetLastError();
 }
 

@@ -20,6 +20,10 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kHeadDim = 64;
 
 // Everything a launcher needs; validated by the C ABI before any HIP call.
+// The mask is a key window around each query's aligned position c_i (i, or
+// i + L − n when bottom-right aligned): key j is legal iff j < L,
+// j ≥ c_i − wl (wl ≥ 0) and j ≤ c_i + wr (wr ≥ 0); −1 leaves a side open.
+// The decoder's causal mask is (wl, wr) = (−1, 0), top-left.
 struct Args {
     const void* q;
     const void* k;
@@ -27,8 +31,28 @@ struct Args {
     void* out;
     int B, H, n, m;
     float scale;          // > 0, finite
-    int causal;           // 0 or 1 (n == m when 1)
+    int wl, wr;           // window sides, >= -1
+    int bottom_right;     // 0: c_i = i; 1: c_i = i + L - n
     const int32_t* key_lens;  // device int32[B] or nullptr
+};
+
+// Legal key range [lo, hi) of query row i under the window of one batch
+// element (key length L, shift = c_i − i).  Both ends are non-decreasing in i,
+// so a block of consecutive queries needs keys [lo(first), hi(last)) and every
+// key in [lo(last), hi(first)) is legal for all of them.
+// Both results lie in [0, L] (computed in 64 bits: i + shift + wr can pass 2^31).
+struct KeyWindow {
+    int wl, wr, shift, L;
+    __device__ __forceinline__ int lo(int i) const {
+        if (wl < 0) return 0;
+        const long long c = (long long)i + shift - wl;
+        return c <= 0 ? 0 : (c >= L ? L : (int)c);
+    }
+    __device__ __forceinline__ int hi(int i) const {
+        if (wr < 0) return L;
+        const long long c = (long long)i + shift + wr + 1;
+        return c <= 0 ? 0 : (c >= L ? L : (int)c);
+    }
 };
 
 hipError_t launch_bf16(const Args& a, hipStream_t stream);        // picks one of the two below

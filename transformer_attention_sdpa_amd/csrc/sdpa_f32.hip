@@ -27,8 +27,8 @@ __device__ __forceinline__ int swz16(int row, int chunk) { return row * 16 + (ch
 template <int NW>
 __global__ __launch_bounds__(NW * 64) void sdpa_fwd_f32(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
-    float* __restrict__ O, int BH, int H, int n, int m, float c_log2, int causal,
-    const int32_t* __restrict__ key_lens, int nqb) {
+    float* __restrict__ O, int BH, int H, int n, int m, float c_log2, int wl, int wr,
+    int bottom_right, const int32_t* __restrict__ key_lens, int nqb) {
     constexpr int NT = NW * 64;
     constexpr int CHUNKS = BN * D * 4 / 16;  // 512
     constexpr int CPT = (CHUNKS + NT - 1) / NT;
@@ -53,9 +53,11 @@ __global__ __launch_bounds__(NW * 64) void sdpa_fwd_f32(
         const int t = key_lens[b];
         L = t < 0 ? 0 : (t > m ? m : t);
     }
-    int kend = L;
-    if (causal) kend = min(kend, q0 + NW * QW);
-    const int ntiles = (kend + BN - 1) / BN;
+    // Key tiles [tbeg, tend): the keys any query of the block may see (KeyWindow).
+    const KeyWindow win{wl, wr, bottom_right ? L - n : 0, L};
+    const int kbeg = win.lo(q0), kend = win.hi(min(q0 + NW * QW, n) - 1);
+    const int tbeg = kbeg / BN;
+    const int tend = kend > kbeg ? (kend + BN - 1) / BN : tbeg;
 
     const size_t qbase = (size_t)bh * n * D;
     const size_t kvbase = (size_t)bh * m * D;
@@ -111,19 +113,24 @@ __global__ __launch_bounds__(NW * 64) void sdpa_fwd_f32(
     float lrun = 0.f;
 
     const int wq_lo = q0 + w * QW;
-    const int wq_hi = wq_lo + QW - 1;
+    const int wq_hi = min(wq_lo + QW, n) - 1;  // < wq_lo for a wave past n: empty
     const int my_q = wq_lo + l32;
+    // Keys some query of the wave may see: [wlo, whi); legal for all: [flo, fhi).
+    const bool wempty = wq_hi < wq_lo;
+    const int wlo = wempty ? 0 : win.lo(wq_lo), whi = wempty ? 0 : win.hi(wq_hi);
+    const int flo = wempty ? 0 : win.lo(wq_hi), fhi = wempty ? 0 : win.hi(wq_lo);
+    const int qlo = win.lo(my_q), qhi = win.hi(my_q);
     const float* sVf = reinterpret_cast<const float*>(sV);
 
-    if (ntiles > 0) gload(0);
-    for (int t = 0; t < ntiles; ++t) {
+    if (tend > tbeg) gload(tbeg);
+    for (int t = tbeg; t < tend; ++t) {
         __syncthreads();
         swrite();
         __syncthreads();
-        if (t + 1 < ntiles) gload(t + 1);
+        if (t + 1 < tend) gload(t + 1);
 
         const int k0 = t * BN;
-        if (causal && k0 > wq_hi) continue;
+        if (k0 >= whi || k0 + BN <= wlo) continue;  // no query of this wave sees the tile
 
         // Sᵀ (32 keys × 32 queries) = K · Qᵀ, 32 steps of k = 2.
         f32x16 s;
@@ -136,12 +143,12 @@ __global__ __launch_bounds__(NW * 64) void sdpa_fwd_f32(
             for (int e = 0; e < 4; ++e) s = mfma32x32x2_f32(a4[e], qop[4 * c + e], s);
         }
 
-        const bool need_mask = (k0 + BN > L) || (causal && k0 + BN - 1 > wq_lo);
+        const bool need_mask = k0 < flo || k0 + BN > fhi;
         if (need_mask) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int key = k0 + 8 * (i >> 2) + 4 * hf + (i & 3);
-                if (key >= L || (causal && key > my_q)) s[i] = -INFINITY;
+                if (key < qlo || key >= qhi) s[i] = -INFINITY;
             }
         }
 
@@ -208,13 +215,15 @@ hipError_t launch_f32_long(const Args& a, hipStream_t stream) {
         const int nqb = (a.n + NW * QW - 1) / (NW * QW);
         hipLaunchKernelGGL(sdpa_fwd_f32<NW>, dim3(nqb * BH), dim3(NW * 64), 0, stream,
                            (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.out,
-                           BH, a.H, a.n, a.m, c_log2, a.causal, a.key_lens, nqb);
+                           BH, a.H, a.n, a.m, c_log2, a.wl, a.wr, a.bottom_right, a.key_lens,
+                           nqb);
     } else {
         constexpr int NW = 2;
         const int nqb = (a.n + NW * QW - 1) / (NW * QW);
         hipLaunchKernelGGL(sdpa_fwd_f32<NW>, dim3(nqb * BH), dim3(NW * 64), 0, stream,
                            (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.out,
-                           BH, a.H, a.n, a.m, c_log2, a.causal, a.key_lens, nqb);
+                           BH, a.H, a.n, a.m, c_log2, a.wl, a.wr, a.bottom_right, a.key_lens,
+                           nqb);
     }
     return hipGetLastError();
 }

@@ -13,8 +13,8 @@
 // before the key length is known, K right after it with its buffer range
 // ending at the key length (padded rows are never read and arrive as zeros),
 // and V, ranged the same way, once Q and K have landed; it arrives while the
-// scores run.  Key tiles of 16 wholly past the key length (or, causal, past a
-// wave's queries) are skipped.
+// scores run.  Key tiles of 16 that no query of a wave may see (past the key
+// length, or outside the queries' key windows, KeyWindow) are skipped.
 //
 // Products, transposed as elsewhere (each lane owns one query column):
 //   Sᵀ (16 keys × 16 queries) = K · Qᵀ, 16 k-steps of 4; in k-step ks the
@@ -58,7 +58,7 @@ __device__ __forceinline__ float quad_sum_f(float x) {
 
 __global__ __launch_bounds__(NT) void sdpa_short_f32(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
-    float* __restrict__ O, int H, int n, int m, float c_log2, int causal,
+    float* __restrict__ O, int H, int n, int m, float c_log2, int wl, int wr, int bottom_right,
     const int32_t* __restrict__ key_lens) {
     // K tile at 0, Q at 16 KiB, V at 32 KiB.
     __shared__ __attribute__((aligned(16))) char lds[3 * TILE];
@@ -107,11 +107,13 @@ __global__ __launch_bounds__(NT) void sdpa_short_f32(
     lds_barrier();
 
     const int q = w * QW + l16;
-    const int wq_last = w * QW + QW - 1;
-    // Key tiles with any legal key for this wave: below the key length and
-    // (causal) not after the wave's last query.
-    int nkt = (L + 15) >> 4;
-    if (causal) nkt = min(nkt, (wq_last >> 4) + 1);
+    // Key tiles [kt0, nkt) hold every key some query of this wave may see.
+    const KeyWindow win{wl, wr, bottom_right ? L - n : 0, L};
+    const int wfirst = w * QW, wlast = min(w * QW + QW, n) - 1;
+    const int wlo = win.lo(wfirst), whi = win.hi(wlast);
+    const int kt0 = wlo >> 4;
+    const int nkt = whi > wlo ? (whi + 15) >> 4 : kt0;
+    const int qlo = win.lo(q), qhi = win.hi(q);  // this lane's legal keys
     const bool active = w * QW < n;
 
     // Qᵀ operand: d = 16·G + ks for k-step ks, i.e. Q[q][16G .. 16G+15].
@@ -131,7 +133,7 @@ __global__ __launch_bounds__(NT) void sdpa_short_f32(
 #pragma unroll
         for (int kp = 0; kp < 2; ++kp) {
             s[2 * kp] = s[2 * kp + 1] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-            if (2 * kp < nkt) {  // uniform
+            if (2 * kp < nkt && 2 * kp + 1 >= kt0) {  // uniform
                 f32x4 acc[2][2];
 #pragma unroll
                 for (int u = 0; u < 2; ++u) acc[u][0] = acc[u][1] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -151,7 +153,7 @@ __global__ __launch_bounds__(NT) void sdpa_short_f32(
                     for (int r = 0; r < 4; ++r) {
                         const int key = 16 * kt + 4 * G + r;
                         const float x = acc[u][0][r] + acc[u][1][r];
-                        s[kt][r] = (key < L && !(causal && key > q)) ? x : -INFINITY;
+                        s[kt][r] = (key >= qlo && key < qhi) ? x : -INFINITY;
                     }
                 }
             }
@@ -186,7 +188,7 @@ __global__ __launch_bounds__(NT) void sdpa_short_f32(
     const int vchunk = 4 * (l16 & 3) + (l16 >> 2);
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
-        if (kt >= nkt) continue;  // uniform; these weights are all zero
+        if (kt < kt0 || kt >= nkt) continue;  // uniform; these weights are all zero
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const f32x4 a = sV4[f32_swz(16 * kt + 4 * G + r, vchunk)];
@@ -227,7 +229,7 @@ hipError_t launch_f32_short(const Args& a, hipStream_t stream) {
     const float c_log2 = (float)((double)a.scale * 1.4426950408889634);  // scale·log2(e)
     hipLaunchKernelGGL(sdpa_short_f32, dim3(a.B * a.H), dim3(NT), 0, stream,
                        (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.out,
-                       a.H, a.n, a.m, c_log2, a.causal, a.key_lens);
+                       a.H, a.n, a.m, c_log2, a.wl, a.wr, a.bottom_right, a.key_lens);
     return hipGetLastError();
 }
 
