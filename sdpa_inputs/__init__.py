@@ -76,6 +76,21 @@ WORKLOADS = {
         key_len_range=None, seed=1006, dtypes=("bf16",), window=(256, 256, "top_left"),
         what="long-sequence restricted self-attention, 8192 tokens, window of 256 keys "
              "either side of each query, no padding"),
+    # One autoregressive decoder step (《注意力就是你所需要的一切》 §3.1: the
+    # decoder consumes its previously generated symbols; §6.1: beam search
+    # with beam size 4): one new query per sequence against its cached keys,
+    # the cache including the new token, so the query sits at the last
+    # position (bottom-right aligned causal window).
+    "decode_beam_base": Workload(
+        "decode_beam_base", B=256, h=8, n=1, m=128, d_k=64, d_v=64, causal=False,
+        key_len_range=(16, 128), seed=1007, dtypes=("bf16",), window=(None, 0, "bottom_right"),
+        what="decoder self-attention step, base shape, 64 sentences x beam 4, one query "
+             "against 16..128 cached keys"),
+    "decode_long_cache": Workload(
+        "decode_long_cache", B=32, h=8, n=1, m=8192, d_k=64, d_v=64, causal=False,
+        key_len_range=(2048, 8192), seed=1008, dtypes=("bf16",), window=(None, 0, "bottom_right"),
+        what="decoder self-attention step, base shape, one query against 2048..8192 cached "
+             "keys (memory-bound stress case)"),
 }
 
 
@@ -84,21 +99,43 @@ def round_to_bf16(x: np.ndarray) -> np.ndarray:
     return bits_to_f32(bf16_bits(x))
 
 
+_CHUNK = 1 << 22  # elements per pass: keeps the temporaries small on 10^8-element tensors
+
+
+def _bf16_bits_flat(u: np.ndarray, out: np.ndarray) -> None:
+    # u + 0x7FFF + lsb stays below 2^32 for every non-NaN pattern (the largest,
+    # −∞ = 0xFF800000, gains at most 0x8000); NaN patterns are replaced below.
+    t = u >> 16
+    t &= 1
+    t += 0x7FFF
+    t += u
+    t >>= 16
+    out[:] = t
+    nan = (u & 0x7FFFFFFF) > 0x7F800000
+    if nan.any():
+        out[nan] = ((u[nan] >> 16) | 0x40).astype(np.uint16)  # keep NaNs quiet NaNs
+
+
 def bf16_bits(x: np.ndarray) -> np.ndarray:
     """uint16 bf16 bit patterns of float32 ``x`` (round to nearest, ties to even)."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    lsb = (u >> 16) & 1
-    r = ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
-    nan = np.isnan(x)
-    if nan.any():
-        r[nan] = ((u[nan] >> 16) | 0x40).astype(np.uint16)  # keep NaNs quiet NaNs
-    return r
+    u = x.reshape(-1).view(np.uint32)
+    r = np.empty(u.shape, dtype=np.uint16)
+    for i in range(0, u.size, _CHUNK):
+        _bf16_bits_flat(u[i:i + _CHUNK], r[i:i + _CHUNK])
+    return r.reshape(x.shape)
 
 
 def bits_to_f32(bits: np.ndarray) -> np.ndarray:
     """float32 values of uint16 bf16 bit patterns (exact)."""
-    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    flat = b.reshape(-1)
+    out = np.empty(flat.shape, dtype=np.uint32)
+    for i in range(0, flat.size, _CHUNK):
+        o = out[i:i + _CHUNK]
+        o[:] = flat[i:i + _CHUNK]
+        o <<= 16
+    return out.view(np.float32).reshape(b.shape)
 
 
 def make_inputs(wl: Workload | str, dtype: str | None = None, seed: int | None = None):

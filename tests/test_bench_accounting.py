@@ -39,7 +39,8 @@ def _brute(wl, key_lens):
 @pytest.mark.parametrize("name", sorted(WORKLOADS))
 def test_algorithmic_work_matches_brute_force(name):
     wl = WORKLOADS[name]
-    if wl.n * wl.m > 1 << 20:  # the 8k case: one head is enough, the count is per head
+    if wl.B * wl.h * (wl.n + 2 * wl.m) * wl.d_k > 1 << 25:
+        # the 8k and long-cache cases: one head is enough, the count is per head
         wl = dataclasses.replace(wl, B=1, h=1)
         key_lens = None
     else:

@@ -21,7 +21,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsdpa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["sdpa_api.cpp", "sdpa_bf16.hip", "sdpa_bf16_short.hip", "sdpa_f32.hip", "sdpa_f32_short.hip"]
+SOURCES = ["sdpa_api.cpp", "sdpa_bf16.hip", "sdpa_bf16_short.hip", "sdpa_bf16_decode.hip",
+           "sdpa_f32.hip", "sdpa_f32_short.hip"]
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops.
 # -amdgpu-mfma-vgpr-form: MFMA accumulators in VGPRs, so the softmax reads

@@ -1,0 +1,307 @@
+// Decoder-step attention forward (n <= 16 queries per head, m > 64 keys), bf16,
+// gfx950.
+//
+// One autoregressive step of the decoder (《Attention Is All You Need：注意力
+// 就是你所需要的一切》 §3.1: the decoder consumes the symbols it generated
+// before) asks a few new queries per sequence against all of that sequence's
+// cached keys.  The work per key is a 64-wide dot product for each of ≤ 16
+// queries, so the step is bound by reading K and V from HBM, and the kernel is
+// built to keep many K/V bytes in flight:
+//
+//   * one workgroup of four waves per (batch, head); the key range any query
+//     may see (KeyWindow, usually bottom-right causal) is cut into 32-key steps
+//     and the waves take contiguous runs of steps, each with its own online
+//     softmax, so no workgroup barrier sits in the loop;
+//   * K goes straight from HBM into VGPRs as the A operand of
+//     v_mfma_f32_16x16x32_bf16 (Sᵀ = K·Qᵀ, the same transposed form as the other
+//     kernels: each lane owns one query column); V goes HBM → LDS with
+//     buffer_load … lds into the wave's own double-buffered slice and is read
+//     back transposed (ds_read_b64_tr_b16) for Oᵀ += Vᵀ·Pᵀ;
+//   * the next step's K and V are requested before the current step's math;
+//   * buffer ranges end at the key length, so rows past it are never read;
+//   * at the end the four waves' (max, sum, Oᵀ) are merged through LDS with the
+//     usual rescale by exp(max_w − max) and the output is normalised once.
+//
+// Arithmetic contract as in the other bf16 kernels: fp32 scores and softmax,
+// −∞ on illegal logits, weights rounded to bf16 for P·V with fp32
+// accumulation, output rounded once to bf16.
+#include "sdpa_common.hpp"
+
+namespace sdpa {
+namespace {
+
+constexpr int D = kHeadDim;  // 64
+constexpr int QN = 16;       // query columns per head (n <= QN)
+constexpr int NWD = 4;       // waves per workgroup
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ float quad_max(float x) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return half_swap_max(max2(__uint_as_float(r[0]), __uint_as_float(r[1])));
+}
+__device__ __forceinline__ float quad_sum(float x) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return half_swap_sum(__uint_as_float(r[0]) + __uint_as_float(r[1]));
+}
+extern "C" __device__ i32x4 sdpa_dec_buffer_load_v4i32(i32x4 rsrc, int voffset, int soffset, int aux)
+    __asm("llvm.amdgcn.raw.buffer.load.v4i32");
+
+// KS keys per step (a multiple of 32): NTL tiles of 16 keys for the scores, NJ
+// k-steps of 32 keys for P·V, NVL loads of 1 KiB (8 V rows) per step.
+template <int KS>
+__global__ __launch_bounds__(NWD * 64) void sdpa_decode_bf16(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
+    int H, int n, int m, float c_log2, int wl, int wr, int bottom_right,
+    const int32_t* __restrict__ key_lens) {
+    constexpr int NTL = KS / 16, NJ = KS / 32, NVL = KS / 8;
+    constexpr int VBUF = KS * 128;  // one step of V rows in LDS
+    // Per wave: two V step buffers; after the loop the first one holds the
+    // wave's Oᵀ partial (64 × 16 floats = 4 KiB).
+    __shared__ __attribute__((aligned(16))) char lds[NWD * 2 * VBUF];
+    __shared__ float red_m[NWD][QN], red_l[NWD][QN];
+
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int l16 = lane & 15;
+    const int G = lane >> 4;
+
+    const int bh = blockIdx.x;
+    const int b = bh / H;
+    const size_t qbase = (size_t)bh * n * D;
+    const size_t kvbase = (size_t)bh * m * D;
+
+    int L = m;
+    if (key_lens) {
+        const int t = key_lens[b];
+        L = t < 0 ? 0 : (t > m ? m : t);
+    }
+    const KeyWindow win{wl, wr, bottom_right ? L - n : 0, L};
+    // Keys any query may see, in whole steps from kb; this wave's steps [s0, s1).
+    const int kbeg = win.lo(0), kend = win.hi(n - 1);
+    const int kb = kbeg & ~(KS - 1);
+    const int nsteps = kend > kbeg ? (kend - kb + KS - 1) / KS : 0;
+    const int per = (nsteps + NWD - 1) / NWD;
+    const int s0 = min(nsteps, w * per), s1 = min(nsteps, s0 + per);
+    // Keys legal for every query: [flo, fhi).
+    const int flo = win.lo(n - 1), fhi = win.hi(0);
+
+    // Qᵀ as the B operand: lane holds query l16, d = 32·ks + 8·G + [0..7].
+    const int q = l16;
+    bf16x8 qop[2];
+    if (q < n) {
+        const u32x4* src = reinterpret_cast<const u32x4*>(Q + qbase + (size_t)q * D);
+        qop[0] = __builtin_bit_cast(bf16x8, src[G]);
+        qop[1] = __builtin_bit_cast(bf16x8, src[4 + G]);
+    } else {
+        qop[0] = qop[1] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+    }
+    // This lane's legal keys: [qlo, qhi) (empty for a padding column q >= n).
+    const int qlo = q < n ? win.lo(q) : 0;
+    const int qhi = q < n ? win.hi(q) : 0;
+
+    const i32x4 rk = make_rsrc(K + kvbase, (uint32_t)(L * D * 2));
+    const i32x4 rv = make_rsrc(V + kvbase, (uint32_t)(L * D * 2));
+    char* vbuf = lds + w * 2 * VBUF;
+    // V loads: the i-th 1 KiB load of a step fills rows 8·i .. +7; lane ln lands
+    // in LDS slot (row ln/8, position ln%8), which holds chunk (ln%8) ^ swz_f(row).
+    int v_off[NVL];
+#pragma unroll
+    for (int i = 0; i < NVL; ++i) {
+        const int row = 8 * i + (lane >> 3);
+        v_off[i] = row * 128 + (((lane & 7) ^ swz_f(row)) << 4);
+    }
+    // K operand of tile t, k-step ks: key k0 + 16·t + l16, d = 32·ks + 8·G.
+    const int k_off = l16 * 128 + G * 16;
+
+    // Requests step s's K (into kop) and V (into LDS buffer s & 1).  Issued
+    // unconditionally, also one step past the wave's last: there the offsets
+    // start at the key length, so the loads return zeros without touching
+    // memory.  Every step then has the same outstanding loads, which keeps
+    // the compiler's waits on K exact.
+    auto issue = [&](int s, bf16x8 (&kop)[NTL][2]) {
+        const int base = s < s1 ? (kb + s * KS) * 128 : L * 128;
+#pragma unroll
+        for (int t = 0; t < NTL; ++t)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+                kop[t][ks] = __builtin_bit_cast(
+                    bf16x8, sdpa_dec_buffer_load_v4i32(rk, base + 16 * t * 128 + k_off + 64 * ks, 0,
+                                                       kCachePolicyNT));
+        char* dst = vbuf + (s & 1) * VBUF;
+#pragma unroll
+        for (int i = 0; i < NVL; ++i) load16_to_lds_nt(rv, dst + 8 * i * 128, base + v_off[i]);
+    };
+
+    float mrun = -INFINITY, lrun = 0.f;
+    f32x4 o[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // One 32-key step: the next step's K and V are requested first (into the
+    // other register set and LDS buffer), then this step's math.
+    auto step = [&](int s, const bf16x8 (&kuse)[NTL][2], bf16x8 (&knxt)[NTL][2]) {
+        const int k0 = kb + s * KS;
+        // The buffer the next step fills was last read two steps ago; its
+        // transpose reads have completed (their data fed that step's MFMAs).
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        issue(s + 1, knxt);
+
+        // Sᵀ = K · Qᵀ: register r of tile t is key k0 + 16·t + 4·G + r of query q.
+        f32x4 st[NTL];
+#pragma unroll
+        for (int t = 0; t < NTL; ++t) {
+            f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+            acc = mfma16(kuse[t][0], qop[0], acc);
+            st[t] = mfma16(kuse[t][1], qop[1], acc);
+        }
+        if (k0 < flo || k0 + KS > fhi) {  // uniform: some key of the step is illegal somewhere
+#pragma unroll
+            for (int t = 0; t < NTL; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int key = k0 + 16 * t + 4 * G + r;
+                    st[t][r] = (key >= qlo && key < qhi) ? st[t][r] : -INFINITY;
+                }
+        }
+        // Online softmax for the query column (exact running maximum).
+        float mt = max2(st[0][0], st[0][1]);
+        mt = max3(mt, st[0][2], st[0][3]);
+#pragma unroll
+        for (int t = 1; t < NTL; ++t) {
+            mt = max3(mt, st[t][0], st[t][1]);
+            mt = max3(mt, st[t][2], st[t][3]);
+        }
+        mt = quad_max(mt);
+        const float mnew = fmaxf(mrun, mt);
+        // mrun = −∞ (nothing legal yet) gives alpha = 0 on zeros; mnew = −∞
+        // (nothing legal at all so far) keeps alpha = 1.
+        const float alpha = mnew == -INFINITY ? 1.f : exp2_hw((mrun - mnew) * c_log2);
+        const float mc = (mnew == -INFINITY ? 0.f : mnew) * c_log2;
+        mrun = mnew;
+        float p[4 * NTL];
+        float ls = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4 * NTL; ++e) {
+            p[e] = exp2_hw(__builtin_fmaf(st[e >> 2][e & 3], c_log2, -mc));  // −∞ → +0
+            ls += p[e];
+        }
+        lrun = lrun * alpha + quad_sum(ls);
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
+        // Pᵀ as the B operand of k-step j: slots 0..3 are keys 32·j + 4·G + [0..3]
+        // (tile 2·j), slots 4..7 keys 32·j + 16 + 4·G + [0..3] (tile 2·j + 1).
+        bf16x8 pb[NJ];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+            pb[j] = to_bf16x8(p[8 * j], p[8 * j + 1], p[8 * j + 2], p[8 * j + 3], p[8 * j + 4],
+                              p[8 * j + 5], p[8 * j + 6], p[8 * j + 7]);
+
+        // This step's V rows must have landed.  At most the next step's NVL V
+        // loads may still be in flight; the count is right whatever the order
+        // of the next step's K loads against them (at worst it waits longer).
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NVL) : "memory");
+        // Oᵀ += Vᵀ · Pᵀ: the A operand of k-step j lists the same keys as its
+        // Pᵀ, two transpose reads of 4 rows each (rows 32·j + 4·G + l16/4 and
+        // + 16) of one dv column.  Written as instructions (ds_read_tr16_b64),
+        // so the next step's loads stay in flight across them.
+        const char* vb = vbuf + (s & 1) * VBUF;
+        u32x2 vt[NJ][8];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int r0 = 32 * j + 4 * G + (l16 >> 2);
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) {
+                const int dv0 = 16 * dt + 4 * (l16 & 3);
+                vt[j][2 * dt] = ds_read_tr16_b64(vb + lds_swz(r0, dv0 >> 3) * 16 + (dv0 & 7) * 2);
+                vt[j][2 * dt + 1] =
+                    ds_read_tr16_b64(vb + lds_swz(r0 + 16, dv0 >> 3) * 16 + (dv0 & 7) * 2);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) tr_wait(vt[j]);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) {
+                const u32x4 a = {vt[j][2 * dt][0], vt[j][2 * dt][1], vt[j][2 * dt + 1][0],
+                                 vt[j][2 * dt + 1][1]};
+                o[dt] = mfma16(__builtin_bit_cast(bf16x8, a), pb[j], o[dt]);
+            }
+    };
+
+    // Two register sets for K, used alternately (no copies across iterations).
+    bf16x8 kA[NTL][2], kB[NTL][2];
+    issue(s0, kA);
+    for (int s = s0; s < s1; s += 2) {
+        step(s, kA, kB);
+        if (s + 1 >= s1) break;
+        step(s + 1, kB, kA);
+    }
+
+    // ---- merge the four waves' partials.  Register r of o[dt] is dv = 16·dt
+    // + 4·G + r of query q; the wave's Oᵀ goes to its own first V buffer.
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    float* po = reinterpret_cast<float*>(vbuf);  // [dv][QN]
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) po[(16 * dt + 4 * G + r) * QN + q] = o[dt][r];
+    if (G == 0) {
+        red_m[w][q] = mrun;
+        red_l[w][q] = lrun;
+    }
+    __syncthreads();
+    // Thread t finishes query t % 16, dv 4·(t / 16) .. +3.
+    const int fq = tid & (QN - 1);
+    const int fd = 4 * (tid >> 4);
+    if (fq < n) {
+        float mx = red_m[0][fq];
+#pragma unroll
+        for (int u = 1; u < NWD; ++u) mx = fmaxf(mx, red_m[u][fq]);
+        const float mcx = (mx == -INFINITY ? 0.f : mx) * c_log2;
+        float lt = 0.f;
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < NWD; ++u) {
+            // a wave with no legal key (max −∞) contributes exactly nothing
+            const float sc = red_m[u][fq] == -INFINITY ? 0.f : exp2_hw(red_m[u][fq] * c_log2 - mcx);
+            lt += sc * red_l[u][fq];
+            const float* pu = reinterpret_cast<const float*>(lds + u * 2 * VBUF);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] += sc * pu[(fd + e) * QN + fq];
+        }
+        // no legal key ⇒ zero row; a NaN sum (NaN legal inputs) stays NaN
+        const float inv = lt != 0.f ? 1.f / lt : 0.f;
+        bf16x4 ov;
+        ov[0] = (__bf16)(acc[0] * inv);
+        ov[1] = (__bf16)(acc[1] * inv);
+        ov[2] = (__bf16)(acc[2] * inv);
+        ov[3] = (__bf16)(acc[3] * inv);
+        *reinterpret_cast<bf16x4*>(O + qbase + (size_t)fq * D + fd) = ov;
+    }
+}
+
+}  // namespace
+
+bool decode_bf16_fits(const Args& a) {
+    // A few queries against more keys than the sentence-length kernel takes,
+    // and enough heads to give every CU work (one workgroup per head).
+    return a.n <= QN && a.m > 64 && (long long)a.B * a.H >= 256;
+}
+
+hipError_t launch_bf16_decode(const Args& a, hipStream_t stream) {
+    const float c_log2 = (float)((double)a.scale * 1.4426950408889634);  // scale·log2(e)
+    // 32-key steps.  64-key steps (twice the bytes per request round trip)
+    // measured no faster on 2k..8k-key caches and slower on full 8k caches.
+    hipLaunchKernelGGL(sdpa_decode_bf16<32>, dim3(a.B * a.H), dim3(NWD * 64), 0, stream,
+                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                       (uint16_t*)a.out, a.H, a.n, a.m, c_log2, a.wl, a.wr, a.bottom_right,
+                       a.key_lens);
+    return hipGetLastError();
+}
+
+}  // namespace sdpa

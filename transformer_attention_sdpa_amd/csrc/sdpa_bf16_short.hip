@@ -66,6 +66,10 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// WINDOWED = false: no key window or the causal one (wl = −1, wr ∈ {−1, 0},
+// top-left), whose legal keys start at 0; the general window costs this
+// latency-bound kernel a few percent, so it gets its own instantiation.
+template <bool WINDOWED>
 __global__ __launch_bounds__(NT) void sdpa_short_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
@@ -114,6 +118,35 @@ __global__ __launch_bounds__(NT) void sdpa_short_bf16(
     const i32x4 rk = make_rsrc(K + kvbase, (uint32_t)(L * D * 2));
     load16_to_lds_nt(rk, lds + ld_lds[0], ld_off[0]);
     load16_to_lds_nt(rk, lds + ld_lds[1], ld_off[1]);
+
+    // Key tiles [kt0, nkt) hold every key some query of this wave may see;
+    // keys in [flo, fhi) are legal for all of its queries.  Computed while Q
+    // and K are in flight (the empty asm keeps them there).
+    const int q = w * QW + l16;
+    const int wfirst = w * QW, wlast = min(w * QW + QW, n) - 1;
+    int kt0, nkt, flo, fhi, llo, lhi;
+    if constexpr (WINDOWED) {
+        const KeyWindow win{wl, wr, bottom_right ? L - n : 0, L};
+        const int wlo = win.lo32(wfirst), whi = win.hi32(wlast);
+        kt0 = wlo >> 4;
+        nkt = whi > wlo ? (whi + 15) >> 4 : kt0;
+        flo = win.lo32(wlast);
+        fhi = win.hi32(wfirst);
+        // Legal keys of this lane's query: [lo, hi).  Register r of tile kt is
+        // key 16·kt + 4·G + r, so the test is llo <= 16·kt + r < lhi.
+        llo = win.lo32(q) - 4 * G;
+        lhi = win.hi32(q) - 4 * G;
+        asm volatile("" : "+s"(kt0), "+s"(nkt), "+s"(flo), "+s"(fhi), "+v"(llo), "+v"(lhi));
+    } else {
+        const bool causal = wr == 0;  // keys [0, L), or [0, min(L, i + 1)) when causal
+        kt0 = 0;
+        nkt = causal ? min((L + 15) >> 4, w + 1) : (L + 15) >> 4;
+        flo = 0;
+        fhi = causal ? min(L, wfirst + 1) : L;
+        llo = 0;
+        lhi = (causal ? min(L, q + 1) : L) - 4 * G;
+        asm volatile("" : "+s"(nkt), "+s"(fhi), "+v"(lhi));
+    }
     // V is requested only once this wave's Q and K rows have landed: across
     // the grid, every workgroup's Q and K then reach HBM ahead of V traffic,
     // which the scores do not need.
@@ -125,22 +158,10 @@ __global__ __launch_bounds__(NT) void sdpa_short_bf16(
     const bool active = w * QW < n;  // this wave has queries (n < 64 leaves some idle)
 
     // Qᵀ as the B operand: lane holds query q, d = 32·ks + 8·G + [0..7].
-    const int q = w * QW + l16;
     bf16x8 qop[2];
     qop[0] = __builtin_bit_cast(bf16x8, sQ[swz(q, G)]);
     qop[1] = __builtin_bit_cast(bf16x8, sQ[swz(q, 4 + G)]);
 
-    // Key tiles [kt0, nkt) hold every key some query of this wave may see;
-    // keys in [flo, fhi) are legal for all of its queries.
-    const KeyWindow win{wl, wr, bottom_right ? L - n : 0, L};
-    const int wfirst = w * QW, wlast = min(w * QW + QW, n) - 1;
-    const int wlo = win.lo(wfirst), whi = win.hi(wlast);
-    const int kt0 = wlo >> 4;
-    const int nkt = whi > wlo ? (whi + 15) >> 4 : kt0;
-    const int flo = win.lo(wlast), fhi = win.hi(wfirst);
-    // Legal keys of this lane's query: [lo, hi).  Register r of tile kt is key
-    // 16·kt + 4·G + r, so the test is llo <= 16·kt + r < lhi.
-    const int llo = win.lo(q) - 4 * G, lhi = win.hi(q) - 4 * G;
 
     // Sᵀ = K · Qᵀ: register r of tile kt is key 16·kt + 4·G + r.
     f32x4 s[4];
@@ -161,8 +182,13 @@ __global__ __launch_bounds__(NT) void sdpa_short_bf16(
                 if (16 * kt < flo || 16 * kt + 16 > fhi) {  // uniform: tile has illegal keys
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const int off = 16 * kt + r;
-                        acc[r] = (off >= llo && off < lhi) ? acc[r] : -INFINITY;
+                        if constexpr (WINDOWED) {
+                            // llo <= off < lhi as one unsigned compare
+                            const unsigned rel = (unsigned)(16 * kt + r - llo);
+                            acc[r] = rel < (unsigned)(lhi - llo) ? acc[r] : -INFINITY;
+                        } else {
+                            acc[r] = (16 * kt + r < lhi) ? acc[r] : -INFINITY;
+                        }
                     }
                 }
                 s[kt] = acc;
@@ -248,7 +274,9 @@ bool short_bf16_fits(const Args& a) { return a.n <= MAXLEN && a.m <= MAXLEN; }
 
 hipError_t launch_bf16_short(const Args& a, hipStream_t stream) {
     const float c_log2 = (float)((double)a.scale * 1.4426950408889634);  // scale·log2(e)
-    hipLaunchKernelGGL(sdpa_short_bf16, dim3(a.B * a.H), dim3(NT), 0, stream,
+    const bool windowed = a.wl >= 0 || a.wr > 0 || a.bottom_right;
+    hipLaunchKernelGGL(windowed ? sdpa_short_bf16<true> : sdpa_short_bf16<false>, dim3(a.B * a.H),
+                       dim3(NT), 0, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (uint16_t*)a.out, a.H, a.n, a.m, c_log2, a.wl, a.wr, a.bottom_right,
                        a.key_lens);

@@ -14,6 +14,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // The one head width the kernels support (d_k == d_v == 64, the pages' base and
 // big models).
@@ -53,12 +54,20 @@ struct KeyWindow {
         const long long c = (long long)i + shift + wr + 1;
         return c <= 0 ? 0 : (c >= L ? L : (int)c);
     }
+    // The same in 32 bits, for kernels whose n and m are at most 64: the C ABI
+    // caps each window side at n + m, so nothing here can pass 2^31.
+    __device__ __forceinline__ int lo32(int i) const { return wl < 0 ? 0 : min(L, max(0, i + shift - wl)); }
+    __device__ __forceinline__ int hi32(int i) const {
+        return wr < 0 ? L : min(L, max(0, i + shift + wr + 1));
+    }
 };
 
-hipError_t launch_bf16(const Args& a, hipStream_t stream);        // picks one of the two below
+hipError_t launch_bf16(const Args& a, hipStream_t stream);        // picks one of the three below
 hipError_t launch_bf16_long(const Args& a, hipStream_t stream);   // any n, m
 hipError_t launch_bf16_short(const Args& a, hipStream_t stream);  // n, m <= 64
 bool short_bf16_fits(const Args& a);
+hipError_t launch_bf16_decode(const Args& a, hipStream_t stream);  // n <= 16, m > 64
+bool decode_bf16_fits(const Args& a);
 hipError_t launch_f32(const Args& a, hipStream_t stream);        // picks one of the two below
 hipError_t launch_f32_long(const Args& a, hipStream_t stream);   // any n, m
 hipError_t launch_f32_short(const Args& a, hipStream_t stream);  // n, m <= 64
@@ -155,6 +164,27 @@ __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" 
 // wave's own LDS operations (lgkmcnt); LDS data written by buffer loads needs
 // its own s_waitcnt vmcnt before the barrier.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// ds_read_b64_tr_b16 written as an instruction.  Through the builtin, the
+// compiler cannot tell which LDS bytes an in-flight buffer_load … lds writes,
+// so it waits for every outstanding global load before the read, including
+// the prefetch of the next tile into the other buffer.  Written here, the read
+// carries no such wait; the caller must make sure the bytes it reads have
+// landed, and must pass the results through tr_wait (s_waitcnt lgkmcnt(0))
+// before using them.  lds_addr points into __shared__ memory.
+__device__ __forceinline__ u32x2 ds_read_tr16_b64(const void* lds_addr) {
+    const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_addr;
+    u32x2 r;
+    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(a));
+    return r;
+}
+// Waits for the LDS reads above and ties their results to the wait, so no use
+// of them can be scheduled before it.
+__device__ __forceinline__ void tr_wait(u32x2 (&x)[8]) {
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]),
+                   "+v"(x[6]), "+v"(x[7]));
+}
 
 // Round-to-nearest-even float → bf16 of eight values (v_cvt_pk_bf16_f32 on gfx950).
 __device__ __forceinline__ bf16x8 to_bf16x8(float a0, float a1, float a2, float a3,

@@ -110,10 +110,10 @@ __global__ __launch_bounds__(NT) void sdpa_short_f32(
     // Key tiles [kt0, nkt) hold every key some query of this wave may see.
     const KeyWindow win{wl, wr, bottom_right ? L - n : 0, L};
     const int wfirst = w * QW, wlast = min(w * QW + QW, n) - 1;
-    const int wlo = win.lo(wfirst), whi = win.hi(wlast);
+    const int wlo = win.lo32(wfirst), whi = win.hi32(wlast);
     const int kt0 = wlo >> 4;
     const int nkt = whi > wlo ? (whi + 15) >> 4 : kt0;
-    const int qlo = win.lo(q), qhi = win.hi(q);  // this lane's legal keys
+    const int qlo = win.lo32(q), qhi = win.hi32(q);  // this lane's legal keys
     const bool active = w * QW < n;
 
     // Qᵀ operand: d = 16·G + ks for k-step ks, i.e. Q[q][16G .. 16G+15].
