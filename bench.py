@@ -124,8 +124,10 @@ def time_workload(name, dtype, steps, warmup, clock_warm_s=0.0, case=None):
             return torch.from_numpy(x).to(dev)
         tdt, code = torch.float32, _lib.SDPA_F32
     q0, k0, v0 = up(case["q"]), up(case["k"]), up(case["v"])
-    set_bytes = (q0.numel() + k0.numel() + v0.numel() + q0.numel()) * q0.element_size()
-    nsets = max(1, min(64, math.ceil(2 * INFINITY_CACHE_BYTES / set_bytes)))
+    # Enough copies that the bytes the timed steps touch (Q, O and the legal
+    # K/V rows of each copy) exceed twice the Infinity Cache.
+    touched = algorithmic_work(wl, dtype, case["key_lens"])[1]
+    nsets = max(1, min(64, math.ceil(2 * INFINITY_CACHE_BYTES / touched)))
     sets = []
     for _ in range(nsets):
         q, k, v = q0.clone(), k0.clone(), v0.clone()
