@@ -69,3 +69,41 @@ def attention_mp(q, k, v, scale, causal=False, key_lens=None, dps=50, window=Non
                 heads.append(rows)
             out.append(heads)
         return out
+
+
+def multihead_mp(xq, xkv, wq, wk, wv, wo, scale, causal=False, key_lens=None, dps=50):
+    """The multi-head sublayer with scalar loops at ``dps`` digits: every
+    projection is written out as sums of products, each head goes through
+    ``attention_mp``, and the concatenated heads are multiplied by W^O.
+    Shapes as in the oracle's ``multihead``.  Returns nested lists [B][n][d_model]."""
+    with mpmath.workdps(dps):
+        B, n, m = len(xq), len(xq[0]), len(xkv[0])
+        h, d_model, d_k = len(wq), len(wq[0]), len(wq[0][0])
+        d_v = len(wv[0][0])
+
+        def proj(x, w, rows, width):
+            # [b][head][row][col] = Σ_t x[b][row][t] · w[head][t][col]
+            out = []
+            for b in range(B):
+                per_head = []
+                for i in range(h):
+                    per_head.append([[mpmath.fsum(mpmath.mpf(float(x[b][r][t])) *
+                                                  mpmath.mpf(float(w[i][t][c]))
+                                                  for t in range(d_model))
+                                      for c in range(width)] for r in range(rows)])
+                out.append(per_head)
+            return out
+
+        q = proj(xq, wq, n, d_k)
+        k = proj(xkv, wk, m, d_k)
+        v = proj(xkv, wv, m, d_v)
+        heads = attention_mp(q, k, v, scale, causal=causal, key_lens=key_lens, dps=dps)
+        out = []
+        for b in range(B):
+            rows = []
+            for r in range(n):
+                cat = [heads[b][i][r][c] for i in range(h) for c in range(d_v)]
+                rows.append([mpmath.fsum(cat[t] * mpmath.mpf(float(wo[t][c])) for t in range(h * d_v))
+                             for c in range(d_model)])
+            out.append(rows)
+        return out

@@ -69,6 +69,10 @@ __all__ = [
     "attention_head",
     "attention",
     "attention_rows",
+    "project_heads",
+    "concat_heads",
+    "output_projection",
+    "multihead",
 ]
 
 # Rows of one head evaluated together.  Rows are independent in Eq. (1) (each
@@ -257,3 +261,57 @@ def attention_rows(q, k, v, picks, scale=None, causal: bool = False, key_lens=No
             out[r] = attention_head(q[b, hh, i:i + 1], k[b, hh], v[b, hh], scale, causal, L,
                                     query_pos=np.array([i]), window=win)[0]
     return out
+
+
+def project_heads(x: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """Per-head projections x W_i: x [B, len, d_model], w [h, d_model, d] →
+    [B, h, len, d] (《精读 …》 multi-head section, head_i's inputs)."""
+    return np.einsum("bld,hdk->bhlk", x, w)
+
+
+def concat_heads(heads: np.ndarray) -> np.ndarray:
+    """Concat(head_1, …, head_h): [B, h, n, d_v] → [B, n, h·d_v], head i in
+    columns i·d_v … (i+1)·d_v − 1 of each row."""
+    B, h, n, d_v = heads.shape
+    return heads.transpose(0, 2, 1, 3).reshape(B, n, h * d_v)
+
+
+def output_projection(concat: np.ndarray, wo: np.ndarray) -> np.ndarray:
+    """Concat(…) W^O: [B, n, h·d_v] · [h·d_v, d_model] → [B, n, d_model]."""
+    return concat @ wo
+
+
+def multihead(xq, xkv, wq, wk, wv, wo, scale=None, causal: bool = False, key_lens=None,
+              window=None) -> np.ndarray:
+    """The multi-head attention sublayer, fp64 (《精读 …》 multi-head section;
+    《注意力就是你所需要的一切》 §3.2.2):
+
+        MultiHead(Q, K, V) = Concat(head_1, …, head_h) W^O,
+        head_i = Attention(Q W_i^Q, K W_i^K, V W_i^V),
+
+    with the queries taken from ``xq`` [B, n, d_model] and the keys and values
+    from ``xkv`` [B, m, d_model] (the same array for self-attention, the
+    encoder output for encoder–decoder attention, §3.2.3).  The projections
+    are the pages' parameter matrices, stacked per head: ``wq`` [h, d_model,
+    d_k] holds W_i^Q, ``wk`` [h, d_model, d_k], ``wv`` [h, d_model, d_v], and
+    ``wo`` [h·d_v, d_model] is W^O.  The pages' projections carry no bias.
+    Masking and scale follow ``attention``.  Returns [B, n, d_model].
+    """
+    xq = np.asarray(xq, dtype=np.float64)
+    xkv = np.asarray(xkv, dtype=np.float64)
+    wq, wk, wv, wo = (np.asarray(w, dtype=np.float64) for w in (wq, wk, wv, wo))
+    h, d_model, d_k = wq.shape
+    d_v = wv.shape[2]
+    if xq.ndim != 3 or xkv.ndim != 3 or xq.shape[0] != xkv.shape[0]:
+        raise ValueError("xq must be [B, n, d_model] and xkv [B, m, d_model]")
+    if xq.shape[2] != d_model or xkv.shape[2] != d_model:
+        raise ValueError("model width differs between inputs and projections")
+    if wk.shape != (h, d_model, d_k) or wv.shape[:2] != (h, d_model) or wo.shape != (h * d_v, d_model):
+        raise ValueError("projection shapes do not match")
+    # The steps are looked up at call time (see the module notes).
+    mod = globals()
+    q = mod["project_heads"](xq, wq)
+    k = mod["project_heads"](xkv, wk)
+    v = mod["project_heads"](xkv, wv)
+    heads = mod["attention"](q, k, v, scale=scale, causal=causal, key_lens=key_lens, window=window)
+    return mod["output_projection"](mod["concat_heads"](heads), wo)

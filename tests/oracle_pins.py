@@ -336,6 +336,72 @@ def pin_window_reduces_to_plain_masks(so):
                           so.attention(q[:, :, 4:], k, v, key_lens=kl))
 
 
+def _mha_weights(rng, h, d_model, d_k, d_v, s=None):
+    s = 1.0 / math.sqrt(d_model) if s is None else s
+    return (s * rng.standard_normal((h, d_model, d_k)), s * rng.standard_normal((h, d_model, d_k)),
+            s * rng.standard_normal((h, d_model, d_v)), s * rng.standard_normal((h * d_v, d_model)))
+
+
+def pin_multihead_brute_force_mp(so):
+    """The multi-head sublayer against scalar-loop 50-digit projections, heads
+    and output projection (self- and cross-attention, padding, causal)."""
+    from oracle.brute_mp import multihead_mp
+
+    rng = np.random.default_rng(43)
+    for (B, n, m, d_model, h, d_k, d_v, causal) in [(2, 3, 3, 6, 2, 3, 2, True), (1, 2, 4, 4, 3, 2, 3, False)]:
+        xq = rng.standard_normal((B, n, d_model))
+        xkv = xq if causal else rng.standard_normal((B, m, d_model))
+        wq, wk, wv, wo = _mha_weights(rng, h, d_model, d_k, d_v, s=0.8)
+        kl = np.array([n, 1][:B]) if causal else None
+        o = so.multihead(xq, xkv, wq, wk, wv, wo, scale=0.6, causal=causal, key_lens=kl)
+        ref = multihead_mp(xq.tolist(), xkv.tolist(), wq.tolist(), wk.tolist(), wv.tolist(),
+                           wo.tolist(), 0.6, causal=causal, key_lens=None if kl is None else kl.tolist())
+        ref = np.array([[[float(x) for x in r] for r in bb] for bb in ref])
+        assert np.allclose(o, ref, rtol=0, atol=1e-13), (B, n, m, causal)
+
+
+def pin_multihead_single_identity_head(so):
+    """h = 1 with d_k = d_v = d_model and identity projections: the sublayer
+    is plain Eq. (1) on the inputs themselves."""
+    rng = np.random.default_rng(47)
+    B, n, m, d = 2, 4, 5, 3
+    xq, xkv = rng.standard_normal((B, n, d)), rng.standard_normal((B, m, d))
+    eye = np.eye(d)[None]
+    o = so.multihead(xq, xkv, eye, eye, eye, np.eye(d), key_lens=np.array([5, 2]))
+    ref = so.attention(xq[:, None], xkv[:, None], xkv[:, None], key_lens=np.array([5, 2]))[:, 0]
+    assert np.allclose(o, ref, rtol=0, atol=1e-14)
+
+
+def pin_multihead_head_permutation(so):
+    """Relabelling the heads (their three projections and their row block of
+    W^O together) leaves the sublayer unchanged: Concat only orders the heads,
+    and W^O's rows follow them."""
+    rng = np.random.default_rng(53)
+    B, n, d_model, h, d_k, d_v = 2, 5, 8, 4, 2, 3
+    x = rng.standard_normal((B, n, d_model))
+    wq, wk, wv, wo = _mha_weights(rng, h, d_model, d_k, d_v)
+    perm = np.array([2, 0, 3, 1])
+    wo_p = wo.reshape(h, d_v, d_model)[perm].reshape(h * d_v, d_model)
+    o1 = so.multihead(x, x, wq, wk, wv, wo, causal=True)
+    o2 = so.multihead(x, x, wq[perm], wk[perm], wv[perm], wo_p, causal=True)
+    assert np.allclose(o1, o2, rtol=0, atol=1e-13)
+    # a permutation of the projections alone (W^O kept) does change the output
+    o3 = so.multihead(x, x, wq[perm], wk[perm], wv[perm], wo, causal=True)
+    assert not np.allclose(o1, o3, rtol=0, atol=1e-6)
+
+
+def pin_multihead_page_shapes(so):
+    """《精读 …》 multi-head section's walk-through: a 10-token input of width
+    512 with h = 8 heads of d_k = d_v = 64 gives a 10 × 512 output, and the
+    four projection matrices hold 4 · 512² = 1,048,576 weights."""
+    rng = np.random.default_rng(59)
+    h, d_model, d = 8, 512, 64
+    x = rng.standard_normal((1, 10, d_model))
+    wq, wk, wv, wo = _mha_weights(rng, h, d_model, d, d)
+    assert wq.size + wk.size + wv.size + wo.size == 1_048_576
+    assert so.multihead(x, x, wq, wk, wv, wo).shape == (1, 10, d_model)
+
+
 ALL_PINS = [
     pin_worked_example_scores,
     pin_worked_example_weights,
@@ -354,4 +420,8 @@ ALL_PINS = [
     pin_window_single_key,
     pin_window_brute_force_mp,
     pin_window_reduces_to_plain_masks,
+    pin_multihead_brute_force_mp,
+    pin_multihead_single_identity_head,
+    pin_multihead_head_permutation,
+    pin_multihead_page_shapes,
 ]

@@ -107,6 +107,14 @@ MUTANTS = {
     "window_left_off_by_one": ("visible_keys", _vis_window_left_off_by_one),
     "window_sides_swapped": ("visible_keys", _vis_window_sides_swapped),
     "window_alignment_ignored": ("visible_keys", _vis_window_alignment_ignored),
+    "heads_concatenated_without_transpose": ("concat_heads",
+                                             lambda hd: hd.reshape(hd.shape[0], hd.shape[2], -1)),
+    "heads_projected_with_transposed_weights": ("project_heads",
+                                                lambda x, w: np.einsum("bld,hkd->bhlk", x, w)
+                                                if w.shape[1] == w.shape[2] else np.einsum("bld,hdk->bhlk", x, w[::-1])),
+    "output_projection_transposed": ("output_projection",
+                                     lambda c, wo: c @ wo.T if wo.shape[0] == wo.shape[1] else c @ wo[::-1]),
+    "output_projection_dropped": ("output_projection", lambda c, wo: c[..., :wo.shape[1]]),
     "mask_finite_fill": ("apply_mask", _mask_finite),
     "mask_skipped": ("apply_mask", lambda s, vis: s.copy()),
     "softmax_over_columns": ("row_softmax", _softmax_cols),
