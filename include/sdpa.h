@@ -24,6 +24,7 @@
 #ifndef SDPA_H
 #define SDPA_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -44,6 +45,7 @@ extern "C" {
 #define SDPA_ERR_LAUNCH      -7 /* the HIP runtime refused the kernel launch         */
 #define SDPA_ERR_SCALE       -8 /* scale is not finite, or not > 0                   */
 #define SDPA_ERR_ALIAS       -9 /* out overlaps q, k, v or key_lens                   */
+#define SDPA_ERR_WORKSPACE  -10 /* workspace smaller than sdpa_mha_workspace_bytes   */
 
 /* Element types (input and output share one type). */
 #define SDPA_F32  0 /* fp32 in, fp32 arithmetic, fp32 out                          */
@@ -124,6 +126,47 @@ SDPA_API int sdpa_forward_window(const void* q, const void* k, const void* v, vo
                  int32_t B, int32_t h, int32_t n, int32_t m, int32_t d_k, int32_t d_v,
                  float scale, int32_t window_left, int32_t window_right, int32_t align,
                  const int32_t* key_lens, int32_t dtype, void* stream);
+
+/*
+ * The multi-head attention sublayer (bf16), the pages' MultiHead
+ * (《精读 Attention Is All You Need：原始 Transformer 论文》 multi-head section;
+ * 《Attention Is All You Need：注意力就是你所需要的一切》 §3.2.2):
+ *
+ *     out = Concat(head_1, …, head_h) W^O,
+ *     head_i = Attention(x_q W_i^Q, x_kv W_i^K, x_kv W_i^V),
+ *
+ * with Attention as in sdpa_forward_window (scale, key window, key_lens).
+ * Self-attention passes the same tensor as x_q and x_kv; encoder–decoder
+ * attention passes the decoder states as x_q and the encoder output as x_kv.
+ * The pages' projections carry no bias, and neither do these.
+ *
+ * x_q      device, [B, n, d_model] bf16, contiguous.
+ * x_kv     device, [B, m, d_model] bf16, contiguous (may equal x_q).
+ * w_q, w_k device, [h·d_k, d_model] bf16: row i·d_k + j is column j of W_i^Q
+ *          (resp. W_i^K), i.e. the [out features, in features] layout.
+ * w_v      device, [h·d_v, d_model] bf16, row i·d_v + j = column j of W_i^V.
+ * w_o      device, [d_model, h·d_v] bf16: the transpose of W^O.
+ * out      device, [B, n, d_model] bf16, written completely; must not overlap
+ *          any input, weight or the workspace.
+ * d_k, d_v 64; d_model a multiple of 64; dtype SDPA_BF16 (other values:
+ *          SDPA_ERR_UNSUPPORTED, or SDPA_ERR_DTYPE if unknown).
+ * workspace, workspace_bytes
+ *          device scratch of at least sdpa_mha_workspace_bytes(...) bytes,
+ *          16-byte aligned, owned by the caller; it receives the projected
+ *          Q, K, V and the attention output.  Too small: SDPA_ERR_WORKSPACE.
+ * Every tensor (and the workspace) must stay below 2^31 bytes (else
+ * SDPA_ERR_SHAPE).  All other arguments and rules as in sdpa_forward_window.
+ * Enqueues three kernels on `stream` (projections, attention, output
+ * projection) and returns; allocates nothing.
+ */
+SDPA_API size_t sdpa_mha_workspace_bytes(int32_t B, int32_t n, int32_t m, int32_t h, int32_t d_k,
+                                         int32_t d_v);
+SDPA_API int sdpa_mha_forward(const void* x_q, const void* x_kv, const void* w_q, const void* w_k,
+                              const void* w_v, const void* w_o, void* out, int32_t B, int32_t n,
+                              int32_t m, int32_t d_model, int32_t h, int32_t d_k, int32_t d_v,
+                              float scale, int32_t window_left, int32_t window_right,
+                              int32_t align, const int32_t* key_lens, int32_t dtype,
+                              void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static text for a status code (never NULL). */
 SDPA_API const char* sdpa_strerror(int status);

@@ -26,7 +26,8 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-__all__ = ["Workload", "WORKLOADS", "make_inputs", "round_to_bf16", "bf16_bits", "bits_to_f32"]
+__all__ = ["Workload", "WORKLOADS", "make_inputs", "mha_case", "random_case", "round_to_bf16",
+           "bf16_bits", "bits_to_f32"]
 
 
 @dataclass(frozen=True)
@@ -163,6 +164,34 @@ def make_inputs(wl: Workload | str, dtype: str | None = None, seed: int | None =
         q, k, v = round_to_bf16(q), round_to_bf16(k), round_to_bf16(v)
     return {"q": q, "k": k, "v": v, "key_lens": key_lens, "causal": wl.causal,
             "window": wl.window, "dtype": dtype, "workload": wl}
+
+
+def mha_case(seed: int, B, n, m, d_model, h, d=64, self_attention=True, key_len_range=None):
+    """Seeded inputs of the multi-head sublayer, bf16-rounded (returned as float32):
+
+    ``xq`` [B, n, d_model] and ``xkv`` [B, m, d_model] (the same array for
+    self-attention) with N(0, 1) components; the pages' projection matrices
+    ``wq``, ``wk`` [h, d_model, d], ``wv`` [h, d_model, d] and ``wo``
+    [h·d, d_model] with N(0, 1/d_model) components, so that the projected
+    queries and keys again have unit-variance components; then the key
+    lengths.  Draw order: xq, xkv (if separate), wq, wk, wv, wo, key lengths.
+    """
+    rng = np.random.default_rng(seed)
+    xq = rng.standard_normal((B, n, d_model), dtype=np.float32)
+    xkv = xq if self_attention else rng.standard_normal((B, m, d_model), dtype=np.float32)
+    s = np.float32(1.0 / np.sqrt(d_model))
+    wq = rng.standard_normal((h, d_model, d), dtype=np.float32) * s
+    wk = rng.standard_normal((h, d_model, d), dtype=np.float32) * s
+    wv = rng.standard_normal((h, d_model, d), dtype=np.float32) * s
+    wo = rng.standard_normal((h * d, d_model), dtype=np.float32) * s
+    key_lens = None
+    if key_len_range is not None:
+        lo, hi = key_len_range
+        key_lens = rng.integers(lo, hi, size=B, endpoint=True).astype(np.int32)
+    r = round_to_bf16
+    xq_r = r(xq)
+    return {"xq": xq_r, "xkv": xq_r if self_attention else r(xkv), "wq": r(wq), "wk": r(wk),
+            "wv": r(wv), "wo": r(wo), "key_lens": key_lens, "heads": h}
 
 
 def random_case(rng: np.random.Generator, B, h, n, m, d_k, d_v, dtype="f32", causal=False,

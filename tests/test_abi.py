@@ -28,7 +28,8 @@ def lib():
 
 def test_every_declared_entry_point_is_exported(lib):
     names = re.findall(r"SDPA_API\s+[\w\s\*]+?\b(sdpa_\w+)\s*\(", _header())
-    assert set(names) == {"sdpa_forward", "sdpa_forward_window", "sdpa_strerror", "sdpa_version"}
+    assert set(names) == {"sdpa_forward", "sdpa_forward_window", "sdpa_mha_forward",
+                          "sdpa_mha_workspace_bytes", "sdpa_strerror", "sdpa_version"}
     for name in names:
         assert isinstance(getattr(lib, name), ctypes._CFuncPtr)
 
@@ -116,6 +117,48 @@ def test_window_validation_rejects_before_any_hip_call(kw, code, lib):
     Note: n != m is legal with a window (any alignment); only bad sides or an
     unknown alignment are mask errors."""
     assert call_window(**kw) == code
+
+
+def call_mha(**kw):
+    B, n, m, d_model, h = kw.get("B", 2), kw.get("n", 8), kw.get("m", 8), kw.get("d_model", 128), kw.get("h", 2)
+    need = _lib.sdpa_mha_workspace_bytes(B, n, m, h, 64, 64)
+    a = dict(x_q=P, x_kv=2 * P, w_q=3 * P, w_k=4 * P, w_v=5 * P, w_o=6 * P, out=7 * P, B=B, n=n, m=m,
+             d_model=d_model, h=h, d_k=64, d_v=64, scale=0.125, wl=-1, wr=-1, align=0, key_lens=None,
+             dtype=1, ws=8 * P, ws_bytes=need)
+    a.update(kw)
+    return _lib.sdpa_mha_forward(a["x_q"], a["x_kv"], a["w_q"], a["w_k"], a["w_v"], a["w_o"], a["out"],
+                                 a["B"], a["n"], a["m"], a["d_model"], a["h"], a["d_k"], a["d_v"],
+                                 a["scale"], a["wl"], a["wr"], a["align"], a["key_lens"], a["dtype"],
+                                 a["ws"], a["ws_bytes"], None)
+
+
+def test_mha_workspace_size(lib):
+    # Q, K, V and the attention output in bf16, each rounded up to 256 bytes
+    assert _lib.sdpa_mha_workspace_bytes(64, 64, 64, 8, 64, 64) == 4 * 64 * 8 * 64 * 64 * 2
+    assert _lib.sdpa_mha_workspace_bytes(1, 3, 5, 1, 64, 64) == 2 * 512 + 2 * 768
+    assert _lib.sdpa_mha_workspace_bytes(1, 3, 5, 1, 32, 64) == 0  # unsupported width
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x_q=None), _lib.SDPA_ERR_NULL),
+    (dict(ws=None), _lib.SDPA_ERR_NULL),
+    (dict(dtype=0), _lib.SDPA_ERR_UNSUPPORTED),  # the sublayer is bf16 only
+    (dict(dtype=5), _lib.SDPA_ERR_DTYPE),
+    (dict(d_model=96), _lib.SDPA_ERR_UNSUPPORTED),
+    (dict(d_k=32), _lib.SDPA_ERR_UNSUPPORTED),
+    (dict(h=0), _lib.SDPA_ERR_SHAPE),
+    (dict(B=1 << 16, n=1 << 12, d_model=512), _lib.SDPA_ERR_SHAPE),
+    (dict(wl=-3), _lib.SDPA_ERR_MASK),
+    (dict(align=7), _lib.SDPA_ERR_MASK),
+    (dict(scale=0.0), _lib.SDPA_ERR_SCALE),
+    (dict(w_o=6 * P + 8), _lib.SDPA_ERR_ALIGN),
+    (dict(ws_bytes=1024), _lib.SDPA_ERR_WORKSPACE),
+    (dict(out=2 * P), _lib.SDPA_ERR_ALIAS),
+    (dict(ws=P), _lib.SDPA_ERR_ALIAS),
+    (dict(out=8 * P + 64), _lib.SDPA_ERR_ALIAS),
+])
+def test_mha_validation_rejects_before_any_hip_call(kw, code, lib):
+    assert call_mha(**kw) == code
 
 
 def test_torch_wrapper_rejects_bad_windows():

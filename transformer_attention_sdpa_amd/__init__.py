@@ -12,9 +12,90 @@ from __future__ import annotations
 import math
 
 from . import _lib
-from ._lib import sdpa_forward, sdpa_forward_window, sdpa_strerror, sdpa_version  # noqa: F401
+from ._lib import (sdpa_forward, sdpa_forward_window, sdpa_mha_forward,  # noqa: F401
+                   sdpa_mha_workspace_bytes, sdpa_strerror, sdpa_version)
 
-__all__ = ["forward", "sdpa_forward", "sdpa_forward_window", "sdpa_strerror", "sdpa_version"]
+__all__ = ["forward", "mha_forward", "sdpa_forward", "sdpa_forward_window", "sdpa_mha_forward",
+           "sdpa_mha_workspace_bytes", "sdpa_strerror", "sdpa_version"]
+
+
+def _window_args(window, causal):
+    """(window_left, window_right, align code) for the C ABI."""
+    if window is None:
+        return -1, (0 if causal else -1), _lib.SDPA_ALIGN_TOP_LEFT
+    if causal:
+        raise ValueError("give the causal mask as window=(None, 0) instead of combining both")
+    left, right = window[0], window[1]
+    align = window[2] if len(window) > 2 else "top_left"
+    if align not in ("top_left", "bottom_right"):
+        raise ValueError(f"unknown window alignment {align!r}")
+    if any(x is not None and int(x) < 0 for x in (left, right)):
+        raise ValueError("window sides are >= 0 or None (unbounded)")
+    # the library treats any side wider than n + m as unbounded
+    wl = -1 if left is None else min(int(left), 2**31 - 1)
+    wr = -1 if right is None else min(int(right), 2**31 - 1)
+    al = _lib.SDPA_ALIGN_BOTTOM_RIGHT if align == "bottom_right" else _lib.SDPA_ALIGN_TOP_LEFT
+    return wl, wr, al
+
+
+def mha_forward(x_q, x_kv, w_q, w_k, w_v, w_o, *, heads: int, causal: bool = False,
+                key_lens=None, scale: float | None = None, window=None, out=None, workspace=None):
+    """The multi-head attention sublayer, bf16 (``sdpa_mha_forward`` in
+    include/sdpa.h): Concat(head_1..head_h) W^O with head_i =
+    Attention(x_q W_i^Q, x_kv W_i^K, x_kv W_i^V).
+
+    x_q [B, n, d_model] and x_kv [B, m, d_model] (pass the same tensor for
+    self-attention); w_q, w_k, w_v [heads·64, d_model] and w_o [d_model,
+    heads·64] in the [out, in] layout.  ``causal``, ``window``, ``key_lens``
+    and ``scale`` as in ``forward``.  ``workspace``: a uint8 GPU tensor of at
+    least ``sdpa_mha_workspace_bytes`` bytes, or None to have one allocated
+    here (the library itself allocates nothing).  Returns ``out`` [B, n,
+    d_model].
+    """
+    import torch
+
+    for t in (x_q, x_kv, w_q, w_k, w_v, w_o):
+        if not t.is_cuda or t.device != x_q.device:
+            raise ValueError("all tensors must be on one GPU")
+        if t.dtype != torch.bfloat16:
+            raise ValueError("the sublayer runs in bf16")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    if x_q.dim() != 3 or x_kv.dim() != 3:
+        raise ValueError("x_q must be [B, n, d_model] and x_kv [B, m, d_model]")
+    B, n, d_model = x_q.shape
+    m = x_kv.shape[1]
+    hw = heads * 64
+    if (tuple(x_kv.shape) != (B, m, d_model) or tuple(w_q.shape) != (hw, d_model)
+            or tuple(w_k.shape) != (hw, d_model) or tuple(w_v.shape) != (hw, d_model)
+            or tuple(w_o.shape) != (d_model, hw)):
+        raise ValueError("shape mismatch between inputs and projections")
+    kl_ptr = None
+    if key_lens is not None:
+        if key_lens.dtype != torch.int32 or key_lens.device != x_q.device or key_lens.numel() != B:
+            raise ValueError("key_lens must be an int32 tensor of B elements on the inputs' device")
+        key_lens = key_lens.contiguous()
+        kl_ptr = key_lens.data_ptr()
+    wl, wr, al = _window_args(window, causal)
+    if causal and window is None and n != m:
+        raise ValueError("the causal mask needs n == m; use a bottom-right window otherwise")
+    need = sdpa_mha_workspace_bytes(B, n, m, heads, 64, 64)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x_q.device)
+    if out is None:
+        out = torch.empty((B, n, d_model), dtype=torch.bfloat16, device=x_q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(64)
+    with torch.cuda.device(x_q.device):
+        stream = torch.cuda.current_stream(x_q.device).cuda_stream
+        rc = sdpa_mha_forward(x_q.data_ptr(), x_kv.data_ptr(), w_q.data_ptr(), w_k.data_ptr(),
+                              w_v.data_ptr(), w_o.data_ptr(), out.data_ptr(), B, n, m, d_model,
+                              heads, 64, 64, float(scale), wl, wr, al, kl_ptr, _lib.SDPA_BF16,
+                              workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                              stream)
+    if rc != _lib.SDPA_OK:
+        raise RuntimeError(f"sdpa_mha_forward failed ({rc}): {sdpa_strerror(rc)}")
+    return out
 
 
 def forward(q, k, v, *, causal: bool = False, key_lens=None, scale: float | None = None,
@@ -33,8 +114,7 @@ def forward(q, k, v, *, causal: bool = False, key_lens=None, scale: float | None
     """
     import torch
 
-    if window is not None and causal:
-        raise ValueError("give the causal mask as window=(None, 0) instead of combining both")
+    wl, wr, al = _window_args(window, causal)
 
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be 4-D [B, h, len, d]")
@@ -70,17 +150,6 @@ def forward(q, k, v, *, causal: bool = False, key_lens=None, scale: float | None
         raise ValueError("out must be a contiguous [B, h, n, d_v] tensor of q's dtype on q's device")
     if scale is None:
         scale = 1.0 / math.sqrt(d_k)
-    if window is not None:
-        left, right = window[0], window[1]
-        align = window[2] if len(window) > 2 else "top_left"
-        if align not in ("top_left", "bottom_right"):
-            raise ValueError(f"unknown window alignment {align!r}")
-        if any(x is not None and int(x) < 0 for x in (left, right)):
-            raise ValueError("window sides are >= 0 or None (unbounded)")
-        # the library treats any side wider than n + m as unbounded
-        wl = -1 if left is None else min(int(left), 2**31 - 1)
-        wr = -1 if right is None else min(int(right), 2**31 - 1)
-        al = _lib.SDPA_ALIGN_BOTTOM_RIGHT if align == "bottom_right" else _lib.SDPA_ALIGN_TOP_LEFT
     # The library launches on the calling thread's current HIP device.
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream

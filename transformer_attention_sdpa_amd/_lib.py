@@ -24,6 +24,7 @@ SDPA_ERR_DTYPE = -6
 SDPA_ERR_LAUNCH = -7
 SDPA_ERR_SCALE = -8
 SDPA_ERR_ALIAS = -9
+SDPA_ERR_WORKSPACE = -10
 SDPA_F32 = 0
 SDPA_BF16 = 1
 SDPA_MASK_NONE = 0
@@ -51,6 +52,11 @@ def load() -> ctypes.CDLL:
     lib.sdpa_forward_window.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                         ctypes.c_float, i32, i32, i32, vp, i32, vp]
     lib.sdpa_forward_window.restype = ctypes.c_int
+    lib.sdpa_mha_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.sdpa_mha_workspace_bytes.restype = ctypes.c_size_t
+    lib.sdpa_mha_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                     ctypes.c_float, i32, i32, i32, vp, i32, vp, ctypes.c_size_t, vp]
+    lib.sdpa_mha_forward.restype = ctypes.c_int
     lib.sdpa_strerror.argtypes = [ctypes.c_int]
     lib.sdpa_strerror.restype = ctypes.c_char_p
     lib.sdpa_version.argtypes = []
@@ -71,6 +77,20 @@ def sdpa_forward_window(q, k, v, out, B, h, n, m, d_k, d_v, scale, window_left, 
     """Forward to the C entry point of the same name (restricted attention)."""
     return load().sdpa_forward_window(q, k, v, out, B, h, n, m, d_k, d_v, scale, window_left,
                                       window_right, align, key_lens, dtype, stream)
+
+
+def sdpa_mha_workspace_bytes(B, n, m, h, d_k, d_v) -> int:
+    """Forward to the C entry point of the same name."""
+    return load().sdpa_mha_workspace_bytes(B, n, m, h, d_k, d_v)
+
+
+def sdpa_mha_forward(x_q, x_kv, w_q, w_k, w_v, w_o, out, B, n, m, d_model, h, d_k, d_v, scale,
+                     window_left, window_right, align, key_lens, dtype, workspace, workspace_bytes,
+                     stream) -> int:
+    """Forward to the C entry point of the same name (the multi-head sublayer)."""
+    return load().sdpa_mha_forward(x_q, x_kv, w_q, w_k, w_v, w_o, out, B, n, m, d_model, h, d_k,
+                                   d_v, scale, window_left, window_right, align, key_lens, dtype,
+                                   workspace, workspace_bytes, stream)
 
 
 def sdpa_strerror(status: int) -> str:

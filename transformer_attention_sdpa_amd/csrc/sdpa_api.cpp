@@ -12,7 +12,7 @@
 
 namespace {
 
-constexpr int kVersion = 1 * 10000 + 1 * 100 + 0;  // 1.1.0: sdpa_forward_window
+constexpr int kVersion = 1 * 10000 + 2 * 100 + 0;  // 1.2.0: the multi-head sublayer
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -89,6 +89,56 @@ extern "C" int sdpa_forward_window(const void* q, const void* k, const void* v, 
     return launch(a, dtype, stream);
 }
 
+extern "C" size_t sdpa_mha_workspace_bytes(int32_t B, int32_t n, int32_t m, int32_t h, int32_t d_k,
+                                           int32_t d_v) {
+    if (B < 1 || n < 1 || m < 1 || h < 1 || d_k != sdpa::kHeadDim || d_v != sdpa::kHeadDim) return 0;
+    return sdpa::mha_workspace_bytes(B, n, m, h);
+}
+
+extern "C" int sdpa_mha_forward(const void* x_q, const void* x_kv, const void* w_q, const void* w_k,
+                                const void* w_v, const void* w_o, void* out, int32_t B, int32_t n,
+                                int32_t m, int32_t d_model, int32_t h, int32_t d_k, int32_t d_v,
+                                float scale, int32_t window_left, int32_t window_right,
+                                int32_t align, const int32_t* key_lens, int32_t dtype,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+    if (!x_q || !x_kv || !w_q || !w_k || !w_v || !w_o || !out || !workspace) return SDPA_ERR_NULL;
+    if (dtype != SDPA_F32 && dtype != SDPA_BF16) return SDPA_ERR_DTYPE;
+    if (B < 1 || n < 1 || m < 1 || d_model < 1 || h < 1 || d_k < 1 || d_v < 1) return SDPA_ERR_SHAPE;
+    if (dtype != SDPA_BF16 || d_k != sdpa::kHeadDim || d_v != sdpa::kHeadDim || d_model % 64 != 0)
+        return SDPA_ERR_UNSUPPORTED;
+    // Byte sizes; the kernels index with 32-bit offsets, so each stays below 2^31.
+    const uint64_t lim = 1ull << 31;
+    const uint64_t xq_b = (uint64_t)B * n * d_model * 2, xkv_b = (uint64_t)B * m * d_model * 2;
+    const uint64_t w_b = (uint64_t)h * 64 * d_model * 2;
+    const uint64_t need = sdpa::mha_workspace_bytes(B, n, m, h);
+    if (xq_b >= lim || xkv_b >= lim || w_b >= lim || need >= lim) return SDPA_ERR_SHAPE;
+    if ((uint64_t)B * h * (((uint64_t)n + 31) / 32) >= lim) return SDPA_ERR_SHAPE;
+    if (window_left < -1 || window_right < -1) return SDPA_ERR_MASK;
+    if (align != SDPA_ALIGN_TOP_LEFT && align != SDPA_ALIGN_BOTTOM_RIGHT) return SDPA_ERR_MASK;
+    if (!std::isfinite(scale) || !(scale > 0.f)) return SDPA_ERR_SCALE;
+    for (const void* p : {x_q, x_kv, w_q, w_k, w_v, w_o, (const void*)out, (const void*)workspace})
+        if (!aligned16(p)) return SDPA_ERR_ALIGN;
+    if (key_lens && (reinterpret_cast<uintptr_t>(key_lens) & 3u)) return SDPA_ERR_ALIGN;
+    if (workspace_bytes < need) return SDPA_ERR_WORKSPACE;
+    const uint64_t out_b = xq_b;
+    struct Buf { const void* p; uint64_t n; };
+    const Buf inputs[] = {{x_q, xq_b}, {x_kv, xkv_b}, {w_q, w_b}, {w_k, w_b}, {w_v, w_b}, {w_o, w_b},
+                          {key_lens, key_lens ? (uint64_t)B * 4 : 0}};
+    for (const Buf& in : inputs) {
+        if (in.p && overlap(out, out_b, in.p, in.n)) return SDPA_ERR_ALIAS;
+        if (in.p && overlap(workspace, need, in.p, in.n)) return SDPA_ERR_ALIAS;
+    }
+    if (overlap(out, out_b, workspace, need)) return SDPA_ERR_ALIAS;
+    // A window side wider than n + m reaches past every key: unbounded.
+    const int64_t reach = (int64_t)n + m;
+    const sdpa::MhaArgs a{x_q, x_kv, w_q, w_k, w_v, w_o, out, workspace, B, n, m, d_model, h, scale,
+                          window_left > reach ? -1 : window_left,
+                          window_right > reach ? -1 : window_right,
+                          align == SDPA_ALIGN_BOTTOM_RIGHT ? 1 : 0, key_lens};
+    const hipError_t e = sdpa::launch_mha_bf16(a, reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SDPA_OK : SDPA_ERR_LAUNCH;
+}
+
 extern "C" const char* sdpa_strerror(int status) {
     switch (status) {
         case SDPA_OK: return "ok";
@@ -101,7 +151,8 @@ extern "C" const char* sdpa_strerror(int status) {
         case SDPA_ERR_DTYPE: return "unknown dtype (SDPA_F32 = 0, SDPA_BF16 = 1)";
         case SDPA_ERR_LAUNCH: return "the HIP runtime refused the kernel launch";
         case SDPA_ERR_SCALE: return "scale must be finite and > 0";
-        case SDPA_ERR_ALIAS: return "out overlaps q, k, v or key_lens";
+        case SDPA_ERR_ALIAS: return "out overlaps an input (or, for the sublayer, the workspace)";
+        case SDPA_ERR_WORKSPACE: return "workspace smaller than sdpa_mha_workspace_bytes";
         default: return "unknown status";
     }
 }

@@ -62,6 +62,24 @@ struct KeyWindow {
     }
 };
 
+// The multi-head sublayer (bf16): projections, attention, output projection.
+struct MhaArgs {
+    const void* x_q;   // [B, n, d_model]
+    const void* x_kv;  // [B, m, d_model]
+    const void* w_q;   // [h·64, d_model]
+    const void* w_k;   // [h·64, d_model]
+    const void* w_v;   // [h·64, d_model]
+    const void* w_o;   // [d_model, h·64]
+    void* out;         // [B, n, d_model]
+    void* workspace;   // mha_workspace_bytes(B, n, m, h) bytes
+    int B, n, m, d_model, h;
+    float scale;
+    int wl, wr, bottom_right;
+    const int32_t* key_lens;
+};
+size_t mha_workspace_bytes(int B, int n, int m, int h);
+hipError_t launch_mha_bf16(const MhaArgs& a, hipStream_t stream);
+
 hipError_t launch_bf16(const Args& a, hipStream_t stream);        // picks one of the three below
 hipError_t launch_bf16_long(const Args& a, hipStream_t stream);   // any n, m
 hipError_t launch_bf16_short(const Args& a, hipStream_t stream);  // n, m <= 64
