@@ -213,6 +213,97 @@ def time_workload(name, dtype, steps, warmup, clock_warm_s=0.0, case=None):
     }
 
 
+def mha_work(args, key_lens):
+    """Algorithmic FLOPs and external HBM bytes of one multi-head sublayer step.
+
+    FLOPs: the three input projections and the output projection (2 per
+    multiply-add, dense), plus the attention's 4·d per legal pair.  Bytes: the
+    sublayer's inputs, its four weight matrices and its output, each once (the
+    projected Q, K, V and the head outputs are intermediate)."""
+    from sdpa_inputs import Workload
+
+    B, n, m, d_model, h = args["B"], args["n"], args["m"], args["d_model"], args["h"]
+    hw = 64 * h
+    proj = 2 * d_model * hw * (B * n + 2 * B * m) + 2 * B * n * hw * d_model
+    wl = Workload("mha", B=B, h=h, n=n, m=m, d_k=64, d_v=64, causal=False,
+                  key_len_range=args.get("key_len_range"), seed=0)
+    att = algorithmic_work(wl, "bf16", key_lens)[0]
+    self_att = args.get("self_attention", True)
+    nbytes = 2 * (B * n * d_model * (2 if self_att else 1) + (0 if self_att else B * m * d_model)
+                  + 4 * hw * d_model)
+    return proj + att, nbytes, proj, att
+
+
+def time_mha(name, steps, warmup, clock_warm_s=0.1):
+    """The multi-head sublayer (three launches per step) on one of MHA_WORKLOADS."""
+    import numpy as np
+    import torch
+
+    from sdpa_inputs import MHA_WORKLOADS, bf16_bits, mha_case
+    from transformer_attention_sdpa_amd import _lib
+
+    args = MHA_WORKLOADS[name]
+    c = mha_case(**args)
+    B, n, m, d_model, h = args["B"], args["n"], args["m"], args["d_model"], args["h"]
+    dev = torch.device("cuda:0")
+
+    def up(x):
+        return torch.from_numpy(np.ascontiguousarray(bf16_bits(x)).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    rows = lambda w: np.ascontiguousarray(w.transpose(0, 2, 1).reshape(h * 64, d_model))
+    wq, wk, wv, wo = up(rows(c["wq"])), up(rows(c["wk"])), up(rows(c["wv"])), up(np.ascontiguousarray(c["wo"].T))
+    xq0 = up(c["xq"])
+    xkv0 = xq0 if args.get("self_attention", True) else up(c["xkv"])
+    need = _lib.sdpa_mha_workspace_bytes(B, n, m, h, 64, 64)
+    flops, nbytes, _, _ = mha_work(args, c["key_lens"])
+    per_set = nbytes + need
+    nsets = max(1, min(64, math.ceil(2 * INFINITY_CACHE_BYTES / per_set)))
+    sets = []
+    for _ in range(nsets):
+        xq = xq0.clone()
+        xkv = xq if xkv0 is xq0 else xkv0.clone()
+        sets.append((xq, xkv, torch.empty((B, n, d_model), dtype=torch.bfloat16, device=dev),
+                     torch.empty(need, dtype=torch.uint8, device=dev)))
+    kl = torch.from_numpy(c["key_lens"]).to(dev) if c["key_lens"] is not None else None
+
+    def launch(i, stream):
+        xq, xkv, out, ws = sets[i % nsets]
+        rc = _lib.sdpa_mha_forward(xq.data_ptr(), xkv.data_ptr(), wq.data_ptr(), wk.data_ptr(),
+                                   wv.data_ptr(), wo.data_ptr(), out.data_ptr(), B, n, m, d_model, h,
+                                   64, 64, 0.125, -1, -1, 0, None if kl is None else kl.data_ptr(),
+                                   _lib.SDPA_BF16, ws.data_ptr(), need, stream)
+        if rc != _lib.SDPA_OK:
+            raise RuntimeError(_lib.sdpa_strerror(rc))
+
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    for i in range(warmup):
+        launch(i, stream)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        cs = torch.cuda.current_stream(dev).cuda_stream
+        for i in range(steps):
+            launch(i, cs)
+    graph.replay()
+    torch.cuda.synchronize()
+    t_warm = time.perf_counter() + clock_warm_s
+    while time.perf_counter() < t_warm:
+        graph.replay()
+        torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / 1e3 / steps
+    del graph, sets
+    torch.cuda.empty_cache()
+    return {"ms_per_step": t * 1e3, "tflops": flops / t / 1e12, "gbs": nbytes / t / 1e9,
+            "frac_mfma_peak": flops / t / 1e12 / PEAK_TFLOPS["bf16"],
+            "frac_hbm_peak": nbytes / t / 1e9 / PEAK_HBM_GBS, "steps": steps, "sets_rotated": nsets,
+            "launches_per_step": 3}
+
+
 def copy_reference(steps, warmup, nbytes=256 << 20):
     """A plain device-to-device copy of known size: the yardstick that scales the
     FETCH_SIZE / WRITE_SIZE counters of the attention kernel to bytes."""
@@ -524,6 +615,9 @@ def main():
                 "sets_rotated", "ms_per_step_eager")}
             if args.no_cpu_baseline:
                 del cases[name, dt]
+        for name in ("mha_encoder_base", "mha_cross_big"):
+            extra[f"{name}-bf16"] = time_mha(name, max(10, min(args.steps, 200)),
+                                             min(args.warmup, 5))
         if not args.no_cpu_baseline:
             for (name, dt), case in cases.items():
                 extra[f"{name}-{dt}"]["cpu_oracle_1core"] = oracle_pass(name, dt, case=case)

@@ -26,7 +26,8 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-__all__ = ["Workload", "WORKLOADS", "make_inputs", "mha_case", "random_case", "round_to_bf16",
+__all__ = ["Workload", "WORKLOADS", "MHA_WORKLOADS", "make_inputs", "mha_case", "random_case",
+           "round_to_bf16",
            "bf16_bits", "bits_to_f32"]
 
 
@@ -164,6 +165,17 @@ def make_inputs(wl: Workload | str, dtype: str | None = None, seed: int | None =
         q, k, v = round_to_bf16(q), round_to_bf16(k), round_to_bf16(v)
     return {"q": q, "k": k, "v": v, "key_lens": key_lens, "causal": wl.causal,
             "window": wl.window, "dtype": dtype, "workload": wl}
+
+
+# Multi-head sublayer workloads (mha_case arguments): the base model's encoder
+# self-attention sublayer on the encoder batch, and the big model's
+# encoder–decoder sublayer on the cross-attention batch (both models as in
+# Table 3 of 《精读 Attention Is All You Need：原始 Transformer 论文》).
+MHA_WORKLOADS = {
+    "mha_encoder_base": dict(seed=3001, B=64, n=64, m=64, d_model=512, h=8, key_len_range=(8, 64)),
+    "mha_cross_big": dict(seed=3002, B=32, n=48, m=64, d_model=1024, h=16, self_attention=False,
+                          key_len_range=(16, 64)),
+}
 
 
 def mha_case(seed: int, B, n, m, d_model, h, d=64, self_attention=True, key_len_range=None):
