@@ -21,17 +21,19 @@
 // The projection kernel computes Cᵀ = W · Xᵀ on v_mfma_f32_32x32x16_bf16: A =
 // 32 weight rows (features), B = 32 token rows, so each lane ends up holding 4
 // consecutive features of one token and stores them as one 8-byte write.  A
-// workgroup of four waves owns 128 tokens × 64 features (one head); each wave
-// 32 tokens.  Operands come straight from HBM/L2 with buffer loads whose range
-// ends at the tensor, so token rows past M read as zeros.
+// workgroup of four waves (2 × 2) owns a tile of 64·MT tokens × 64·NT
+// features; each wave 32·MT tokens × 32·NT features.  The contraction runs in
+// stages of 64 inputs: per stage the workgroup's X and W rows (128 bytes
+// each) are copied by buffer_load … lds straight into one of two LDS buffers,
+// one stage ahead of the MFMAs, and every wave reads its operands from there.
+// Loads use buffer ranges that end at the tensor, so token rows past M and
+// feature rows past N read as zeros.
 #include "sdpa_common.hpp"
 
 namespace sdpa {
 namespace {
 
 constexpr int HD = kHeadDim;  // 64
-constexpr int TM = 128;       // tokens per workgroup
-constexpr int TN = 64;        // features per workgroup
 
 enum { ROWS = 0, HEADS = 1 };
 
@@ -49,11 +51,41 @@ struct ProjJobs {
     ProjJob job[3];
 };
 
-extern "C" __device__ i32x4 sdpa_mha_buffer_load_v4i32(i32x4 rsrc, int voffset, int soffset, int aux)
-    __asm("llvm.amdgcn.raw.buffer.load.v4i32");
+// ds_read_b128 written as an instruction: through a plain LDS load the
+// compiler cannot tell which bytes an in-flight buffer_load … lds writes, and
+// waits for all of them (the next stage's prefetch included) before the read.
+// The caller waits with lgkm_wait before using the result.
+template <int OFF>
+__device__ __forceinline__ u32x4 ds_read16(uint32_t addr) {
+    u32x4 r;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+    return r;
+}
+// Compile-time loop: f(std::integral_constant<int, I>) for I = B .. E - 1.
+template <int B, int E>
+struct StaticFor {
+    template <class F>
+    __device__ __forceinline__ static void run(F&& f) {
+        if constexpr (B < E) {
+            f(std::integral_constant<int, B>{});
+            StaticFor<B + 1, E>::run(f);
+        }
+    }
+};
+template <int N, int CNT>
+__device__ __forceinline__ void lgkm_wait(u32x4 (&x)[N]) {
+    asm volatile("s_waitcnt lgkmcnt(%0)" ::"i"(CNT));
+#pragma unroll
+    for (int i = 0; i < N; ++i) asm volatile("" : "+v"(x[i]));
+}
 
-template <int AMODE, int CMODE>
+template <int AMODE, int CMODE, int MT, int NT>
 __global__ __launch_bounds__(256) void proj_gemm_bf16(ProjJobs jobs) {
+    constexpr int TM = 64 * MT, TN = 64 * NT;     // tokens × features per workgroup
+    constexpr int XB = TM * 128, STAGE = (TM + TN) * 128;
+    constexpr int NXI = TM / 32, NWI = TN / 32;  // LDS-DMA loads per wave per stage
+    __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE];
+
     const ProjJob& J = jobs.job[blockIdx.z];
     const int t0 = blockIdx.x * TM;
     const int f0 = blockIdx.y * TN;
@@ -64,79 +96,182 @@ __global__ __launch_bounds__(256) void proj_gemm_bf16(ProjJobs jobs) {
     const int lane = tid & 63;
     const int l32 = lane & 31;
     const int hf = lane >> 5;
-    const int tok = t0 + 32 * w + l32;
     const int K = J.K;
+    const int nst = K / 64;
 
-    // Byte offsets of this lane's 16-byte operand at contraction index 0:
-    // token tok, inputs 8·hf .. +7; weight row f0 + 32·ft + l32, same inputs.
-    const i32x4 rx = make_rsrc(J.x, (uint32_t)((size_t)J.M * K * 2));
-    const i32x4 rw = make_rsrc(J.w, (uint32_t)((size_t)J.N * K * 2));
-    int xoff;
-    int xhead_stride = 0;  // HEADS: bytes from one head's block to the next
-    if (AMODE == ROWS) {
-        xoff = tok * K * 2 + hf * 16;
-    } else {
-        const int b = tok / J.len, i = tok - b * J.len;
-        xoff = ((b * (K / HD)) * J.len + i) * HD * 2 + hf * 16;
-        xhead_stride = J.len * HD * 2;
-        if (tok >= J.M) xoff = J.M * K * 2;  // past the tensor: reads zeros
-    }
-    const int woff0 = (f0 + l32) * K * 2 + hf * 16;
-    const int woff1 = woff0 + 32 * K * 2;
-
-    f32x16 acc[2];
+    // LDS-DMA: load u of wave w fills 8 rows (1 KB) of a stage's X or W tile,
+    // rows 8·(w + 4u) .. +7; lane L writes row +L/8 at chunk position L%8,
+    // which holds input chunk (L%8) ^ swz_f(row) of that row.
+    const i32x4 rx = make_rsrc(J.x, (uint32_t)J.M * (uint32_t)K * 2u);
+    const i32x4 rw = make_rsrc(J.w, (uint32_t)J.N * (uint32_t)K * 2u);
+    uint32_t xo[NXI], wo[NWI];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) { acc[0][i] = 0.f; acc[1][i] = 0.f; }
-
-    // 64 inputs per iteration (four k-steps of 16); K is a multiple of 64, so
-    // in HEADS mode one iteration is exactly one head's block.
-    for (int k0 = 0; k0 < K; k0 += 64) {
-        bf16x8 xo[4], wo[2][4];
-        const int xk = AMODE == ROWS ? xoff + k0 * 2 : xoff + (k0 / HD) * xhead_stride;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            xo[s] = __builtin_bit_cast(bf16x8, sdpa_mha_buffer_load_v4i32(rx, xk + 32 * s, 0, 0));
-            wo[0][s] = __builtin_bit_cast(bf16x8,
-                                          sdpa_mha_buffer_load_v4i32(rw, woff0 + k0 * 2 + 32 * s, 0, 0));
-            wo[1][s] = __builtin_bit_cast(bf16x8,
-                                          sdpa_mha_buffer_load_v4i32(rw, woff1 + k0 * 2 + 32 * s, 0, 0));
-        }
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            acc[0] = mfma32x32x16_bf16(wo[0][s], xo[s], acc[0]);
-            acc[1] = mfma32x32x16_bf16(wo[1][s], xo[s], acc[1]);
+    for (int u = 0; u < NXI; ++u) {
+        const int r = 8 * (w + 4 * u) + (lane >> 3);
+        const uint32_t c16 = (uint32_t)(((lane & 7) ^ swz_f(r)) * 16);
+        const int t = t0 + r;
+        if (AMODE == ROWS) {
+            xo[u] = (uint32_t)t * (uint32_t)K * 2u + c16;
+        } else {
+            const int b = t / J.len, i = t - b * J.len;
+            xo[u] = t < J.M ? ((uint32_t)(b * (K / HD)) * (uint32_t)J.len + (uint32_t)i) * (HD * 2) + c16
+                            : (uint32_t)J.M * (uint32_t)K * 2u;
         }
     }
-
-    // Register r of acc[ft] is feature f0 + 32·ft + 8·(r/4) + 4·hf + r%4 of
-    // token tok: four consecutive features per 8-byte store.
-    if (tok >= J.M) return;
-    size_t cbase;
-    int chead_stride = 0;
-    if (CMODE == ROWS) {
-        cbase = (size_t)tok * J.N;
-    } else {
-        const int b = tok / J.len, i = tok - b * J.len;
-        cbase = ((size_t)b * (J.N / HD) * J.len + i) * HD;
-        chead_stride = J.len * HD;
+#pragma unroll
+    for (int u = 0; u < NWI; ++u) {
+        const int r = 8 * (w + 4 * u) + (lane >> 3);
+        wo[u] = (uint32_t)(f0 + r) * (uint32_t)K * 2u + (uint32_t)(((lane & 7) ^ swz_f(r)) * 16);
     }
+    // Stage s: inputs 64·s .. +63.  ROWS: 128 bytes further along each row;
+    // HEADS: the next head's block of the heads layout.
+    const uint32_t xstep = AMODE == ROWS ? 128u : (uint32_t)J.len * (HD * 2);
+    auto issue = [&](int s) {
+        char* base = lds + (s & 1) * STAGE;
 #pragma unroll
-    for (int ft = 0; ft < 2; ++ft)
+        for (int u = 0; u < NXI; ++u)
+            load16_to_lds(rx, base + (w + 4 * u) * 1024, (int)(xo[u] + (uint32_t)s * xstep));
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-            const int f = f0 + 32 * ft + 8 * i4 + 4 * hf;
-            const size_t dst = CMODE == ROWS ? cbase + f
-                                             : cbase + (size_t)(f / HD) * chead_stride + (f % HD);
-            bf16x4 o;
-            o[0] = (__bf16)acc[ft][4 * i4 + 0];
-            o[1] = (__bf16)acc[ft][4 * i4 + 1];
-            o[2] = (__bf16)acc[ft][4 * i4 + 2];
-            o[3] = (__bf16)acc[ft][4 * i4 + 3];
-            *reinterpret_cast<bf16x4*>(J.c + dst) = o;
+        for (int u = 0; u < NWI; ++u)
+            load16_to_lds(rw, base + XB + (w + 4 * u) * 1024, (int)(wo[u] + (uint32_t)s * 128u));
+    };
+
+    // Operand reads: lane (l32, hf) reads row l32 of a 32-row block at input
+    // chunk 2·ks + hf of k-step ks, i.e. at chunk position (2·ks + hf) ^ sw.
+    const int wm = w & 1, wn = w >> 1;
+    const int sw = swz_f(l32);
+    const uint32_t lbase = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds;
+    uint32_t ra[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) ra[ks] = lbase + l32 * 128 + (((2 * ks + hf) ^ sw) * 16);
+    constexpr int XOFF = 0;  // X rows of wave wm: 32·MT·wm + 32·i
+    constexpr int WOFF = XB;
+
+    f32x16 acc[MT][NT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+    // Two k-steps' operands per read batch: MT + NT reads each.
+    constexpr int NR = 2 * (MT + NT);
+    const uint32_t xo_w = wm * 32 * MT * 128, wo_w = wn * 32 * NT * 128;
+    auto read_half = [&](uint32_t bufoff, auto hc, u32x4 (&v)[NR]) {
+        constexpr int h = decltype(hc)::value;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const uint32_t ax = ra[2 * h + q] + bufoff + xo_w, aw = ra[2 * h + q] + bufoff + wo_w;
+            StaticFor<0, MT>::run([&](auto ic) {
+                constexpr int i = decltype(ic)::value;
+                v[q * (MT + NT) + i] = ds_read16<XOFF + i * 4096>(ax);
+            });
+            StaticFor<0, NT>::run([&](auto jc) {
+                constexpr int j = decltype(jc)::value;
+                v[q * (MT + NT) + MT + j] = ds_read16<WOFF + j * 4096>(aw);
+            });
         }
+    };
+    auto mfma_half = [&](u32x4 (&v)[NR]) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int i = 0; i < MT; ++i)
+#pragma unroll
+                for (int j = 0; j < NT; ++j)
+                    acc[i][j] = mfma32x32x16_bf16(__builtin_bit_cast(bf16x8, v[q * (MT + NT) + MT + j]),
+                                                  __builtin_bit_cast(bf16x8, v[q * (MT + NT) + i]), acc[i][j]);
+    };
+    // The second half's reads are in flight while the first half's MFMAs run;
+    // the scheduling barrier keeps the compiler from hoisting the second
+    // wait above them.
+    auto compute = [&](int s) {
+        const uint32_t bufoff = (uint32_t)((s & 1) * STAGE);
+        u32x4 v0[NR], v1[NR];
+        read_half(bufoff, std::integral_constant<int, 0>{}, v0);
+        read_half(bufoff, std::integral_constant<int, 1>{}, v1);
+        lgkm_wait<NR, NR>(v0);
+        mfma_half(v0);
+        __builtin_amdgcn_sched_barrier(0);
+        lgkm_wait<NR, 0>(v1);
+        mfma_half(v1);
+    };
+
+    // Stage s sits in buffer s % 2.  Each wave waits for its own copies of
+    // stage s (vmcnt), the barrier for everyone's; the barrier after the
+    // reads frees the buffer for stage s + 2.
+    constexpr int NI = NXI + NWI;
+    issue(0);
+    for (int s = 0; s + 1 < nst; ++s) {
+        issue(s + 1);
+        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"i"(NI) : "memory");
+        compute(s);
+        asm volatile("s_barrier" ::: "memory");
+    }
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    compute(nst - 1);
+
+    // Register r of acc[i][j] is feature 32·j + 8·(r/4) + 4·hf + r%4 (of the
+    // wave's feature block) of token 32·i + l32 (of its token block): four
+    // consecutive features per 8-byte store.
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+        const int tok = t0 + 32 * MT * wm + 32 * i + l32;
+        if (tok >= J.M) continue;
+        size_t cbase;
+        int chead_stride = 0;
+        if (CMODE == ROWS) {
+            cbase = (size_t)tok * J.N;
+        } else {
+            const int b = tok / J.len, ii = tok - b * J.len;
+            cbase = ((size_t)b * (J.N / HD) * J.len + ii) * HD;
+            chead_stride = J.len * HD;
+        }
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+            const int fb = f0 + 32 * NT * wn + 32 * j;
+            if (fb >= J.N) continue;  // N is a multiple of 64: whole 32-feature blocks
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+                const int f = fb + 8 * i4 + 4 * hf;
+                const size_t dst = CMODE == ROWS ? cbase + f
+                                                 : cbase + (size_t)(f / HD) * chead_stride + (f % HD);
+                bf16x4 o;
+                o[0] = (__bf16)acc[i][j][4 * i4 + 0];
+                o[1] = (__bf16)acc[i][j][4 * i4 + 1];
+                o[2] = (__bf16)acc[i][j][4 * i4 + 2];
+                o[3] = (__bf16)acc[i][j][4 * i4 + 3];
+                *reinterpret_cast<bf16x4*>(J.c + dst) = o;
+            }
+        }
+    }
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Workgroup tile: the largest of 128 × 128, 128 × 64 and 64 × 64 (tokens ×
+// features) that still gives at least two workgroups per compute unit, so
+// that a second workgroup's loads overlap each one's MFMAs.
+#ifndef SDPA_PROJ_TILE
+#define SDPA_PROJ_TILE 0  // 0: by size; 1: 64 × 64; 2: 128 × 64; 3: 128 × 128
+#endif
+template <int AMODE, int CMODE>
+hipError_t launch_proj(const ProjJobs& jobs, int njobs, int max_m, int n, hipStream_t stream) {
+    auto tiles = [&](int tm, int tn) { return (long)((max_m + tm - 1) / tm) * ((n + tn - 1) / tn) * njobs; };
+    int pick = SDPA_PROJ_TILE;
+    if (pick == 0) pick = tiles(128, 128) >= 512 ? 3 : tiles(128, 64) >= 512 ? 2 : 1;
+    if (pick == 3)
+        hipLaunchKernelGGL((proj_gemm_bf16<AMODE, CMODE, 2, 2>), dim3((max_m + 127) / 128, (n + 127) / 128, njobs),
+                           dim3(256), 0, stream, jobs);
+    else if (pick == 2)
+        hipLaunchKernelGGL((proj_gemm_bf16<AMODE, CMODE, 2, 1>), dim3((max_m + 127) / 128, (n + 63) / 64, njobs),
+                           dim3(256), 0, stream, jobs);
+    else
+        hipLaunchKernelGGL((proj_gemm_bf16<AMODE, CMODE, 1, 1>), dim3((max_m + 63) / 64, (n + 63) / 64, njobs),
+                           dim3(256), 0, stream, jobs);
+    return hipGetLastError();
+}
 
 }  // namespace
 
@@ -160,9 +295,7 @@ hipError_t launch_mha_bf16(const MhaArgs& a, hipStream_t stream) {
     in.job[0] = ProjJob{(const uint16_t*)a.x_q, (const uint16_t*)a.w_q, qh, a.B * a.n, hw, a.d_model, a.n};
     in.job[1] = ProjJob{(const uint16_t*)a.x_kv, (const uint16_t*)a.w_k, kh, a.B * a.m, hw, a.d_model, a.m};
     in.job[2] = ProjJob{(const uint16_t*)a.x_kv, (const uint16_t*)a.w_v, vh, a.B * a.m, hw, a.d_model, a.m};
-    const int mt = (a.B * (a.n > a.m ? a.n : a.m) + TM - 1) / TM;
-    hipLaunchKernelGGL((proj_gemm_bf16<ROWS, HEADS>), dim3(mt, hw / TN, 3), dim3(256), 0, stream, in);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_proj<ROWS, HEADS>(in, 3, a.B * (a.n > a.m ? a.n : a.m), hw, stream);
     if (e != hipSuccess) return e;
 
     // 2. Attention over the B·h heads.
@@ -173,9 +306,7 @@ hipError_t launch_mha_bf16(const MhaArgs& a, hipStream_t stream) {
     // 3. Concat(heads) · W^O, gathered from the heads layout.
     ProjJobs outj{};
     outj.job[0] = ProjJob{oh, (const uint16_t*)a.w_o, (uint16_t*)a.out, a.B * a.n, a.d_model, hw, a.n};
-    hipLaunchKernelGGL((proj_gemm_bf16<HEADS, ROWS>), dim3((a.B * a.n + TM - 1) / TM, a.d_model / TN, 1),
-                       dim3(256), 0, stream, outj);
-    return hipGetLastError();
+    return launch_proj<HEADS, ROWS>(outj, 1, a.B * a.n, a.d_model, stream);
 }
 
 }  // namespace sdpa
