@@ -565,6 +565,8 @@ def main():
                                                         "COPY_WRITE_DB"),
                     help="print the per-launch HBM traffic record of --kernel and exit")
     ap.add_argument("--kernel", default="sdpa_short_bf16", help="kernel name for --traffic-json")
+    ap.add_argument("--mha", choices=["mha_encoder_base", "mha_cross_big"],
+                    help="time only this multi-head sublayer workload (one JSON line)")
     ap.add_argument("--context", action="store_true",
                     help="time a library bf16 GEMM and torch's fused SDPA beside this library")
     args = ap.parse_args()
@@ -581,12 +583,15 @@ def main():
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: every (batch, head) pair is independent and this "
-              "build has no multi-GPU path; run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: every (batch, head) pair is independent and the "
+              "library has no multi-GPU path; run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     if args.context:
         print(json.dumps(context()), flush=True)
+        return
+    if args.mha:
+        print(json.dumps({"workload": args.mha, **time_mha(args.mha, args.steps, args.warmup)}), flush=True)
         return
     if args.calibrate_copy:
         print(json.dumps(copy_reference(args.steps, args.warmup, int(args.copy_mib * (1 << 20)))),
