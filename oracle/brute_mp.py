@@ -107,3 +107,77 @@ def multihead_mp(xq, xkv, wq, wk, wv, wo, scale, causal=False, key_lens=None, dp
                              for c in range(d_model)])
             out.append(rows)
         return out
+
+
+def _legal_mp(i, j, n, m, causal, L, window):
+    lim = m if L is None else min(max(L, 0), m)
+    if j >= lim or (causal and j > i):
+        return False
+    if window is not None:
+        p = i if window[2] == "top_left" else i + lim - n
+        if window[0] is not None and j < p - window[0]:
+            return False
+        if window[1] is not None and j > p + window[1]:
+            return False
+    return True
+
+
+def _head_loss_mp(Q, K, V, dO, sc, legal):
+    """Σ_i dO_i · o_i for one head, every argument already ``mpf``."""
+    total = mpmath.mpf(0)
+    for i in range(len(Q)):
+        den = mpmath.mpf(0)
+        num = [mpmath.mpf(0)] * len(V[0])
+        for j in range(len(K)):
+            if not legal[i][j]:
+                continue
+            e = mpmath.exp(sc * mpmath.fsum(a * b for a, b in zip(Q[i], K[j])))
+            den += e
+            for c in range(len(num)):
+                num[c] += e * V[j][c]
+        if den != 0:
+            total += mpmath.fsum(dO[i][c] * num[c] / den for c in range(len(num)))
+    return total
+
+
+def attention_grad_fd_mp(q, k, v, do, scale, causal=False, key_lens=None, window=None, dps=60,
+                         eps=1e-20):
+    """Gradients of ℓ = Σ dO ∘ Attention(Q, K, V) by central differences at
+    ``dps`` digits, one input element at a time: (ℓ(x + ε) − ℓ(x − ε)) / 2ε.
+
+    This is the derivative itself, not a formula for it: it evaluates Eq. (1)
+    (legal keys only, no maximum subtraction, as ``attention_mp``) twice per
+    element.  With ε = 1e-20 at 60 digits the truncation error is O(ε²) and
+    the rounding error about 10^(−60)/ε, so the result is exact far beyond
+    fp64.  Returns (dq, dk, dv) as nested lists of floats, shapes as q, k, v.
+    """
+    with mpmath.workdps(dps):
+        sc = mpmath.mpf(scale)
+        ep = mpmath.mpf(eps)
+        grads = ([], [], [])
+        for b in range(len(q)):
+            L = None if key_lens is None else int(key_lens[b])
+            g_b = ([], [], [])
+            for hh in range(len(q[b])):
+                X = [[[mpmath.mpf(float(x)) for x in row] for row in t[b][hh]] for t in (q, k, v)]
+                dO = [[mpmath.mpf(float(x)) for x in row] for row in do[b][hh]]
+                n, m = len(X[0]), len(X[1])
+                legal = [[_legal_mp(i, j, n, m, causal, L, window) for j in range(m)]
+                         for i in range(n)]
+                for which in range(3):
+                    g = []
+                    for r in range(len(X[which])):
+                        row = []
+                        for c in range(len(X[which][r])):
+                            x0 = X[which][r][c]
+                            X[which][r][c] = x0 + ep
+                            up = _head_loss_mp(X[0], X[1], X[2], dO, sc, legal)
+                            X[which][r][c] = x0 - ep
+                            dn = _head_loss_mp(X[0], X[1], X[2], dO, sc, legal)
+                            X[which][r][c] = x0
+                            row.append(float((up - dn) / (2 * ep)))
+                        g.append(row)
+                    g_b[which].append(g)
+            for which in range(3):
+                grads[which].append(g_b[which])
+        return grads

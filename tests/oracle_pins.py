@@ -425,3 +425,184 @@ ALL_PINS = [
     pin_multihead_head_permutation,
     pin_multihead_page_shapes,
 ]
+
+
+# --- gradient of Eq. (1) (oracle.sdpa_backward) --------------------------------
+#
+# The pages print no gradient, so these pins rest on the derivative itself
+# (finite differences of the forward pass, at 60 digits and in fp64) and on
+# invariants that follow from the form of Eq. (1).  Each takes the backward
+# module ``sb``.
+
+_BWD_MASKS = [  # (causal, key_lens, window) for B = 2
+    (False, None, None),
+    (True, None, None),
+    (False, [3, 1], None),
+    (False, None, (1, 0, "top_left")),
+    (False, [4, 2], (None, 0, "bottom_right")),
+]
+
+
+def _bwd_case(rng, B, h, n, m, d, dv):
+    return (_rand(rng, B, h, n, d), _rand(rng, B, h, m, d), _rand(rng, B, h, m, dv),
+            _rand(rng, B, h, n, dv))
+
+
+def pin_bwd_finite_difference_mp(sb):
+    """Every gradient element against a 60-digit central difference of Eq. (1)."""
+    from oracle.brute_mp import attention_grad_fd_mp
+
+    rng = np.random.default_rng(71)
+    for (n, m) in ((3, 3), (2, 4)):
+        q, k, v, do = _bwd_case(rng, 2, 1, n, m, 3, 2)
+        for causal, kl, win in _BWD_MASKS:
+            if causal and n != m:
+                continue
+            got = sb.attention_backward(q, k, v, do, scale=0.7, causal=causal, key_lens=kl,
+                                        window=win)
+            ref = attention_grad_fd_mp(q.tolist(), k.tolist(), v.tolist(), do.tolist(), 0.7,
+                                       causal, kl, win)
+            for name, a, r in zip(("dq", "dk", "dv"), got, ref):
+                assert np.allclose(a, np.array(r), rtol=0, atol=1e-12), (name, n, m, causal, kl, win)
+
+
+def pin_bwd_finite_difference_fp64(sb):
+    """Larger shapes (several keys per row, ragged lengths, n ≠ m): fp64
+    central differences of the forward oracle, step 1e-5 (error ~1e-9)."""
+    from oracle import sdpa_oracle as so
+
+    rng = np.random.default_rng(72)
+    for (n, m, causal, kl, win) in ((6, 6, True, [6, 4], None), (5, 8, False, [8, 3], None),
+                                    (7, 7, False, None, (2, 1, "top_left")),
+                                    (3, 9, False, [9, 5], (None, 0, "bottom_right"))):
+        q, k, v, do = _bwd_case(rng, 2, 1, n, m, 4, 3)
+        got = sb.attention_backward(q, k, v, do, scale=0.6, causal=causal, key_lens=kl, window=win)
+        loss = lambda q_, k_, v_: float(np.sum(do * so.attention(q_, k_, v_, scale=0.6, causal=causal,
+                                                                  key_lens=kl, window=win)))
+        h = 1e-5
+        for which, x in enumerate((q, k, v)):
+            fd = np.zeros_like(x)
+            for idx in np.ndindex(x.shape):
+                args = [q, k, v]
+                up, dn = x.copy(), x.copy()
+                up[idx] += h
+                dn[idx] -= h
+                args[which] = up
+                lu = loss(*args)
+                args[which] = dn
+                fd[idx] = (lu - loss(*args)) / (2 * h)
+            assert np.allclose(got[which], fd, rtol=0, atol=1e-7), (which, n, m, causal, kl, win)
+
+
+def pin_bwd_key_shift_invariance(sb):
+    """Adding one vector c to every key adds scale·q_i·c to all of row i's
+    logits, which its softmax ignores: the derivative along that direction,
+    Σ_j dK_j · c, is zero for every c, so Σ_j dK_j = 0 for every head."""
+    rng = np.random.default_rng(73)
+    q, k, v, do = _bwd_case(rng, 2, 2, 5, 7, 4, 3)
+    for causal, kl, win in _BWD_MASKS:
+        if causal:
+            continue
+        _, dk, _ = sb.attention_backward(q, k, v, do, scale=0.8, key_lens=kl, window=win)
+        assert np.abs(dk.sum(axis=2)).max() < 1e-12, (kl, win)
+
+
+def pin_bwd_bilinear_balance(sb):
+    """The logits depend on q_i · k_j only, so Q → tQ, K → K/t changes
+    nothing: d/dt at t = 1 gives ⟨dQ, Q⟩ = ⟨dK, K⟩ per head."""
+    rng = np.random.default_rng(74)
+    q, k, v, do = _bwd_case(rng, 2, 2, 6, 6, 4, 3)
+    for causal, kl, win in _BWD_MASKS:
+        dq, dk, _ = sb.attention_backward(q, k, v, do, scale=0.8, causal=causal, key_lens=kl,
+                                          window=win)
+        lhs = np.einsum("bhnd,bhnd->bh", dq, q)
+        rhs = np.einsum("bhmd,bhmd->bh", dk, k)
+        assert np.allclose(lhs, rhs, rtol=0, atol=1e-12), (causal, kl, win)
+
+
+def pin_bwd_value_sum(sb):
+    """o_i is linear in V with weights summing to 1 over the legal keys, so
+    Σ_j dV_j = Σ_i dO_i over the rows that have a legal key."""
+    rng = np.random.default_rng(75)
+    q, k, v, do = _bwd_case(rng, 2, 1, 4, 6, 3, 2)
+    # key_lens [6, 0]: batch 1 has no legal key at all
+    _, _, dv = sb.attention_backward(q, k, v, do, scale=0.9, key_lens=[6, 0])
+    assert np.allclose(dv[0].sum(axis=1), do[0].sum(axis=1), rtol=0, atol=1e-12)
+    assert np.all(dv[1] == 0)
+
+
+def pin_bwd_single_key(sb):
+    """One legal key: every weight is 1 whatever the logits, so dQ = 0,
+    dK = 0, and that key's dV is the sum of the output gradients."""
+    rng = np.random.default_rng(76)
+    q, k, v, do = _bwd_case(rng, 1, 2, 3, 5, 4, 2)
+    dq, dk, dv = sb.attention_backward(q, k, v, do, scale=1.3, key_lens=[1])
+    assert np.abs(dq).max() == 0 and np.abs(dk).max() == 0
+    assert np.allclose(dv[0, :, 0], do[0].sum(axis=1), rtol=0, atol=1e-14)
+    assert np.all(dv[0, :, 1:] == 0)
+
+
+def pin_bwd_uniform_weights(sb):
+    """q = 0 makes every legal weight 1/L.  Then dV_j = (1/L) Σ_i dO_i for the
+    legal keys, and dQ_i = (scale/L) Σ_j (dO_i · (v_j − v̄)) k_j, the
+    covariance of values and keys seen through dO_i (v̄ = mean legal value)."""
+    rng = np.random.default_rng(77)
+    _, k, v, do = _bwd_case(rng, 1, 1, 3, 5, 4, 2)
+    q = np.zeros((1, 1, 3, 4))
+    L, sc = 4, 0.5
+    dq, _, dv = sb.attention_backward(q, k, v, do, scale=sc, key_lens=[L])
+    assert np.allclose(dv[0, 0, :L], np.broadcast_to(do[0, 0].sum(axis=0) / L, (L, 2)), atol=1e-14)
+    vc = v[0, 0, :L] - v[0, 0, :L].mean(axis=0)
+    ref = np.array([[sc / L * sum((do[0, 0, i] @ vc[j]) * k[0, 0, j, t] for j in range(L))
+                     for t in range(4)] for i in range(3)])
+    assert np.allclose(dq[0, 0], ref, rtol=0, atol=1e-14)
+
+
+def pin_bwd_empty_rows_pass_nothing(sb):
+    """A query with no legal key has output 0 whatever Q, K, V: its dQ row is
+    zero and its dO contributes to no dK or dV."""
+    rng = np.random.default_rng(78)
+    q, k, v, do = _bwd_case(rng, 1, 1, 4, 2, 3, 2)
+    # bottom-right causal with 2 cached keys and 4 queries: rows 0 and 1 see nothing
+    win = (None, 0, "bottom_right")
+    dq, dk, dv = sb.attention_backward(q, k, v, do, scale=0.7, window=win)
+    assert np.all(dq[0, 0, :2] == 0)
+    do2 = do.copy()
+    do2[0, 0, :2] = 123.0
+    _, dk2, dv2 = sb.attention_backward(q, k, v, do2, scale=0.7, window=win)
+    assert np.array_equal(dk, dk2) and np.array_equal(dv, dv2)
+
+
+def pin_lse_closed_forms(sb):
+    """ln Σ_j exp(s_ij): q = 0 gives ln L; one legal key gives its logit; no
+    legal key gives −∞; and exp(s − lse) sums to 1 over each row's legal keys
+    (checked against 50-digit sums)."""
+    import mpmath
+
+    rng = np.random.default_rng(79)
+    _, k, _, _ = _bwd_case(rng, 2, 1, 3, 6, 4, 2)
+    q0 = np.zeros((2, 1, 3, 4))
+    lse = sb.log_sum_exp(q0, k, scale=0.5, key_lens=[6, 0])
+    assert np.allclose(lse[0], math.log(6), atol=1e-15) and np.all(lse[1] == -np.inf)
+    q = rng.standard_normal((2, 1, 3, 4))
+    lse1 = sb.log_sum_exp(q, k, scale=0.5, key_lens=[1, 6])
+    assert np.allclose(lse1[0, 0], 0.5 * q[0, 0] @ k[0, 0, 0], atol=1e-14)
+    with mpmath.workdps(50):
+        for i in range(3):
+            s = [mpmath.mpf(0.5) * mpmath.fsum(mpmath.mpf(float(a)) * mpmath.mpf(float(b))
+                                               for a, b in zip(q[1, 0, i], k[1, 0, j]))
+                 for j in range(6)]
+            assert abs(float(mpmath.log(mpmath.fsum(mpmath.exp(x) for x in s))) - lse1[1, 0, i]) < 1e-14
+
+
+BACKWARD_PINS = [
+    pin_bwd_finite_difference_mp,
+    pin_bwd_finite_difference_fp64,
+    pin_bwd_key_shift_invariance,
+    pin_bwd_bilinear_balance,
+    pin_bwd_value_sum,
+    pin_bwd_single_key,
+    pin_bwd_uniform_weights,
+    pin_bwd_empty_rows_pass_nothing,
+    pin_lse_closed_forms,
+]

@@ -160,3 +160,47 @@ def test_key_length_taken_from_head_index(monkeypatch):
         except Exception:
             caught.append(pin.__name__)
     assert caught
+
+
+# --- the gradient oracle ------------------------------------------------------
+#
+# Mistakes one could make deriving the gradient of Eq. (1) by hand: dropping
+# the softmax's row term, flipping its sign, summing it over the wrong axis,
+# forgetting the scale in dQ or dK, or a missing transpose in dK or dV
+# (expressible when n == m).
+
+import oracle.sdpa_backward as sb  # noqa: E402
+from tests.oracle_pins import BACKWARD_PINS  # noqa: E402
+
+
+def _sq(f, g):
+    """f where the operands are square (the mistake is expressible), else g."""
+    return lambda a, b, *rest: f(a, b, *rest) if a.shape[0] == a.shape[1] else g(a, b, *rest)
+
+
+BWD_MUTANTS = {
+    "softmax_row_term_dropped": ("grad_logits", lambda p, dp: p * dp),
+    "softmax_row_term_sign": ("grad_logits", lambda p, dp: p * (np.sum(p * dp, axis=1, keepdims=True) - dp)),
+    "softmax_term_over_columns": ("grad_logits", lambda p, dp: p * (dp - np.sum(p * dp, axis=0, keepdims=True))),
+    "softmax_term_without_weights": ("grad_logits", lambda p, dp: p * (dp - np.sum(dp, axis=1, keepdims=True))),
+    "dq_scale_dropped": ("grad_queries", lambda ds, k, scale: ds @ k),
+    "dk_scale_dropped": ("grad_keys", lambda ds, q, scale: ds.T @ q),
+    "dk_not_transposed": ("grad_keys", _sq(lambda ds, q, scale: scale * (ds @ q),
+                                           lambda ds, q, scale: scale * (ds.T @ q))),
+    "dv_not_transposed": ("grad_values", _sq(lambda p, do: p @ do, lambda p, do: p.T @ do)),
+    "dp_transposed": ("grad_weights", lambda do, v: (do @ v.T) if do.shape[0] != v.shape[0]
+                      else (do @ v.T).T),
+}
+
+
+@pytest.mark.parametrize("name", sorted(BWD_MUTANTS))
+def test_some_backward_pin_catches_mutant(name, monkeypatch):
+    attr, fn = BWD_MUTANTS[name]
+    monkeypatch.setattr(sb, attr, fn)
+    caught = []
+    for pin in BACKWARD_PINS:
+        try:
+            pin(sb)
+        except Exception as e:
+            caught.append((pin.__name__, type(e).__name__))
+    assert caught, f"no pin detects mutant {name}"
