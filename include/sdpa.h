@@ -45,7 +45,7 @@ extern "C" {
 #define SDPA_ERR_LAUNCH      -7 /* the HIP runtime refused the kernel launch         */
 #define SDPA_ERR_SCALE       -8 /* scale is not finite, or not > 0                   */
 #define SDPA_ERR_ALIAS       -9 /* out overlaps q, k, v or key_lens                   */
-#define SDPA_ERR_WORKSPACE  -10 /* workspace smaller than sdpa_mha_workspace_bytes   */
+#define SDPA_ERR_WORKSPACE  -10 /* workspace smaller than its *_workspace_bytes size */
 
 /* Element types (input and output share one type). */
 #define SDPA_F32  0 /* fp32 in, fp32 arithmetic, fp32 out                          */
@@ -167,6 +167,66 @@ SDPA_API int sdpa_mha_forward(const void* x_q, const void* x_kv, const void* w_q
                               float scale, int32_t window_left, int32_t window_right,
                               int32_t align, const int32_t* key_lens, int32_t dtype,
                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * sdpa_forward_lse — sdpa_forward_window that also returns, for every query
+ * row, the natural log of its softmax denominator:
+ *
+ *     lse[b, h, i] = ln Σ_j exp(scale · q_i · k_j)   over the legal keys j,
+ *
+ * and −∞ for a row with no legal key.  The weights of Eq. (1) are then
+ * exp(scale · q_i · k_j − lse_i), which is how sdpa_backward recomputes them
+ * without storing the n × m weight matrix.
+ *
+ * lse      device, float [B, h, n], contiguous, 4-byte aligned, written
+ *          completely; must not overlap any other argument.
+ * dtype    SDPA_BF16 (SDPA_F32: SDPA_ERR_UNSUPPORTED).
+ * Everything else as in sdpa_forward_window; `out` is bitwise the same as
+ * sdpa_forward_window's.
+ */
+SDPA_API int sdpa_forward_lse(const void* q, const void* k, const void* v, void* out, float* lse,
+                              int32_t B, int32_t h, int32_t n, int32_t m, int32_t d_k, int32_t d_v,
+                              float scale, int32_t window_left, int32_t window_right,
+                              int32_t align, const int32_t* key_lens, int32_t dtype, void* stream);
+
+/*
+ * sdpa_backward — the gradient of Eq. (1) (bf16).  The pages train the model
+ * through attention but print only the forward pass; by the chain rule, for
+ * any loss with output gradient dO:
+ *
+ *     dV = Pᵀ dO,  dP = dO Vᵀ,  dS = P ∘ (dP − D) with D_i = dO_i · O_i,
+ *     dQ = scale · dS K,  dK = scale · dSᵀ Q,
+ *
+ * where P = exp(scale · Q Kᵀ − lse) row-wise over the legal keys (masked
+ * connections get no gradient; a row with no legal key passes none back).
+ *
+ * q, k, v   the forward inputs, as in sdpa_forward_window.
+ * out       the forward output O, [B, h, n, d_v].
+ * dout      dO, [B, h, n, d_v] bf16.
+ * lse       the forward pass's lse (sdpa_forward_lse), float [B, h, n].
+ * dq        device, [B, h, n, d_k] bf16, written completely.
+ * dk, dv    device, [B, h, m, d_k] and [B, h, m, d_v] bf16, written completely
+ *           (rows of keys at or past key_lens[b] are zero).
+ * scale, window_left, window_right, align, key_lens
+ *           exactly as given to the forward pass.
+ * workspace, workspace_bytes
+ *           device scratch of at least sdpa_backward_workspace_bytes(B, h, n)
+ *           bytes, 16-byte aligned, owned by the caller (it receives D and
+ *           lse · log2 e per row).  Too small: SDPA_ERR_WORKSPACE.
+ * dtype     SDPA_BF16 (SDPA_F32: SDPA_ERR_UNSUPPORTED).
+ * The outputs and the workspace must not overlap each other or any input
+ * (SDPA_ERR_ALIAS).  All tensors 16-byte aligned, lse and key_lens 4-byte
+ * aligned.  Enqueues two kernels on `stream` (dQ, then dK and dV) and
+ * returns; allocates nothing; uses no atomics, so the result is bitwise
+ * reproducible.  Other errors as in sdpa_forward_window.
+ */
+SDPA_API size_t sdpa_backward_workspace_bytes(int32_t B, int32_t h, int32_t n);
+SDPA_API int sdpa_backward(const void* q, const void* k, const void* v, const void* out,
+                           const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                           int32_t B, int32_t h, int32_t n, int32_t m, int32_t d_k, int32_t d_v,
+                           float scale, int32_t window_left, int32_t window_right, int32_t align,
+                           const int32_t* key_lens, int32_t dtype, void* workspace,
+                           size_t workspace_bytes, void* stream);
 
 /* Static text for a status code (never NULL). */
 SDPA_API const char* sdpa_strerror(int status);

@@ -26,7 +26,8 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-__all__ = ["Workload", "WORKLOADS", "MHA_WORKLOADS", "make_inputs", "mha_case", "random_case",
+__all__ = ["Workload", "WORKLOADS", "MHA_WORKLOADS", "backward_case", "grad_output", "make_inputs",
+           "mha_case", "random_case",
            "round_to_bf16",
            "bf16_bits", "bits_to_f32"]
 
@@ -204,6 +205,26 @@ def mha_case(seed: int, B, n, m, d_model, h, d=64, self_attention=True, key_len_
     xq_r = r(xq)
     return {"xq": xq_r, "xkv": xq_r if self_attention else r(xkv), "wq": r(wq), "wk": r(wk),
             "wv": r(wv), "wo": r(wo), "key_lens": key_lens, "heads": h}
+
+
+def grad_output(wl: Workload, dtype: str = "bf16") -> np.ndarray:
+    """Seeded upstream gradient dO [B, h, n, d_v] for a workload's backward
+    pass: N(0, 1) components from ``default_rng(seed + 10000)``, bf16-rounded
+    for bf16 (the gradient of a loss Σ dO ∘ O)."""
+    rng = np.random.default_rng(wl.seed + 10000)
+    do = rng.standard_normal((wl.B, wl.h, wl.n, wl.d_v), dtype=np.float32)
+    return round_to_bf16(do) if dtype == "bf16" else do
+
+
+def backward_case(seed: int, B, h, n, m, causal=False, key_lens=None, window=None):
+    """Free-shape bf16 case for the backward pass: ``random_case`` (q, k, v)
+    from ``default_rng(seed)``, then dO [B, h, n, 64] from the same generator,
+    all N(0, 1) and bf16-rounded."""
+    rng = np.random.default_rng(seed)
+    c = random_case(rng, B, h, n, m, 64, 64, dtype="bf16", causal=causal, key_lens=key_lens,
+                    window=window)
+    c["do"] = round_to_bf16(rng.standard_normal((B, h, n, 64), dtype=np.float32))
+    return c
 
 
 def random_case(rng: np.random.Generator, B, h, n, m, d_k, d_v, dtype="f32", causal=False,

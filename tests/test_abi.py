@@ -29,7 +29,8 @@ def lib():
 def test_every_declared_entry_point_is_exported(lib):
     names = re.findall(r"SDPA_API\s+[\w\s\*]+?\b(sdpa_\w+)\s*\(", _header())
     assert set(names) == {"sdpa_forward", "sdpa_forward_window", "sdpa_mha_forward",
-                          "sdpa_mha_workspace_bytes", "sdpa_strerror", "sdpa_version"}
+                          "sdpa_mha_workspace_bytes", "sdpa_forward_lse", "sdpa_backward",
+                          "sdpa_backward_workspace_bytes", "sdpa_strerror", "sdpa_version"}
     for name in names:
         assert isinstance(getattr(lib, name), ctypes._CFuncPtr)
 
@@ -43,7 +44,7 @@ def test_header_constants_match_binding():
 
 def test_version_and_strerror(lib):
     assert _lib.sdpa_version() >= 10000
-    for code in range(-9, 1):
+    for code in range(-10, 1):
         msg = _lib.sdpa_strerror(code)
         assert msg and msg != "unknown status"
     assert _lib.sdpa_strerror(-1234) == "unknown status"
@@ -159,6 +160,74 @@ def test_mha_workspace_size(lib):
 ])
 def test_mha_validation_rejects_before_any_hip_call(kw, code, lib):
     assert call_mha(**kw) == code
+
+
+def call_lse(**kw):
+    a = dict(q=P, k=2 * P, v=3 * P, out=4 * P, lse=5 * P, B=2, h=2, n=8, m=8, d_k=64, d_v=64,
+             scale=0.125, wl=-1, wr=-1, align=0, key_lens=None, dtype=1)
+    a.update(kw)
+    return _lib.sdpa_forward_lse(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["h"], a["n"],
+                                 a["m"], a["d_k"], a["d_v"], a["scale"], a["wl"], a["wr"], a["align"],
+                                 a["key_lens"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(lse=None), _lib.SDPA_ERR_NULL),
+    (dict(q=None), _lib.SDPA_ERR_NULL),
+    (dict(dtype=0), _lib.SDPA_ERR_UNSUPPORTED),  # the log-sum-exp output is bf16 only
+    (dict(dtype=4), _lib.SDPA_ERR_DTYPE),
+    (dict(lse=5 * P + 2), _lib.SDPA_ERR_ALIGN),
+    (dict(wr=-2), _lib.SDPA_ERR_MASK),
+    (dict(align=3), _lib.SDPA_ERR_MASK),
+    (dict(lse=4 * P + 64), _lib.SDPA_ERR_ALIAS),  # inside out
+    (dict(lse=P), _lib.SDPA_ERR_ALIAS),
+])
+def test_forward_lse_validation_rejects_before_any_hip_call(kw, code, lib):
+    assert call_lse(**kw) == code
+
+
+def call_bwd(**kw):
+    B, h, n = kw.get("B", 2), kw.get("h", 2), kw.get("n", 8)
+    a = dict(q=P, k=2 * P, v=3 * P, out=4 * P, dout=5 * P, lse=6 * P, dq=7 * P, dk=8 * P, dv=9 * P,
+             B=B, h=h, n=n, m=8, d_k=64, d_v=64, scale=0.125, wl=-1, wr=-1, align=0, key_lens=None,
+             dtype=1, ws=10 * P, ws_bytes=_lib.sdpa_backward_workspace_bytes(B, h, n))
+    a.update(kw)
+    return _lib.sdpa_backward(a["q"], a["k"], a["v"], a["out"], a["dout"], a["lse"], a["dq"], a["dk"],
+                              a["dv"], a["B"], a["h"], a["n"], a["m"], a["d_k"], a["d_v"], a["scale"],
+                              a["wl"], a["wr"], a["align"], a["key_lens"], a["dtype"], a["ws"],
+                              a["ws_bytes"], None)
+
+
+def test_backward_workspace_size(lib):
+    # D and lse·log2 e per query row, fp32, each rounded up to 256 bytes
+    assert _lib.sdpa_backward_workspace_bytes(64, 8, 64) == 2 * 64 * 8 * 64 * 4
+    assert _lib.sdpa_backward_workspace_bytes(1, 1, 3) == 2 * 256
+    assert _lib.sdpa_backward_workspace_bytes(0, 1, 3) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dout=None), _lib.SDPA_ERR_NULL),
+    (dict(lse=None), _lib.SDPA_ERR_NULL),
+    (dict(dk=None), _lib.SDPA_ERR_NULL),
+    (dict(ws=None), _lib.SDPA_ERR_NULL),
+    (dict(q=None), _lib.SDPA_ERR_NULL),
+    (dict(dtype=0), _lib.SDPA_ERR_UNSUPPORTED),
+    (dict(dtype=9), _lib.SDPA_ERR_DTYPE),
+    (dict(d_v=32), _lib.SDPA_ERR_UNSUPPORTED),
+    (dict(m=0), _lib.SDPA_ERR_SHAPE),
+    (dict(scale=float("inf")), _lib.SDPA_ERR_SCALE),
+    (dict(dq=7 * P + 4), _lib.SDPA_ERR_ALIGN),
+    (dict(lse=6 * P + 2), _lib.SDPA_ERR_ALIGN),
+    (dict(wl=-5), _lib.SDPA_ERR_MASK),
+    (dict(align=2), _lib.SDPA_ERR_MASK),
+    (dict(ws_bytes=16), _lib.SDPA_ERR_WORKSPACE),
+    (dict(dq=P), _lib.SDPA_ERR_ALIAS),           # dq on q
+    (dict(dv=5 * P + 64), _lib.SDPA_ERR_ALIAS),  # dv inside dout
+    (dict(dk=7 * P), _lib.SDPA_ERR_ALIAS),       # dk on dq
+    (dict(ws=9 * P), _lib.SDPA_ERR_ALIAS),       # workspace on dv
+])
+def test_backward_validation_rejects_before_any_hip_call(kw, code, lib):
+    assert call_bwd(**kw) == code
 
 
 def test_torch_wrapper_rejects_bad_windows():

@@ -12,11 +12,13 @@ from __future__ import annotations
 import math
 
 from . import _lib
-from ._lib import (sdpa_forward, sdpa_forward_window, sdpa_mha_forward,  # noqa: F401
+from ._lib import (sdpa_backward, sdpa_backward_workspace_bytes, sdpa_forward,  # noqa: F401
+                   sdpa_forward_lse, sdpa_forward_window, sdpa_mha_forward,
                    sdpa_mha_workspace_bytes, sdpa_strerror, sdpa_version)
 
-__all__ = ["forward", "mha_forward", "sdpa_forward", "sdpa_forward_window", "sdpa_mha_forward",
-           "sdpa_mha_workspace_bytes", "sdpa_strerror", "sdpa_version"]
+__all__ = ["forward", "backward", "mha_forward", "sdpa_forward", "sdpa_forward_window",
+           "sdpa_forward_lse", "sdpa_backward", "sdpa_backward_workspace_bytes",
+           "sdpa_mha_forward", "sdpa_mha_workspace_bytes", "sdpa_strerror", "sdpa_version"]
 
 
 def _window_args(window, causal):
@@ -98,23 +100,9 @@ def mha_forward(x_q, x_kv, w_q, w_k, w_v, w_o, *, heads: int, causal: bool = Fal
     return out
 
 
-def forward(q, k, v, *, causal: bool = False, key_lens=None, scale: float | None = None,
-            out=None, window=None):
-    """Attention over [B, h, n, d_k] queries and [B, h, m, d] keys/values.
-
-    key_lens: None or an int32 tensor [B] on the same device (key j of batch
-    element b is legal iff j < key_lens[b]).  window: None, or
-    (left, right) / (left, right, align) for restricted attention: query i
-    sees keys c_i - left .. c_i + right (None = unbounded side), where
-    c_i = i for align "top_left" (default) and c_i = i + L - n for
-    "bottom_right" (L = the batch element's key length); see
-    ``sdpa_forward_window`` in include/sdpa.h.  Not combined with ``causal``.
-    Returns ``out`` ([B, h, n, d_v], same dtype as q).  Raises RuntimeError
-    with the library's message on a nonzero status.
-    """
+def _check_qkv(q, k, v):
+    """Shapes and the dtype code of [B, h, n, d_k], [B, h, m, d_k], [B, h, m, d_v] GPU tensors."""
     import torch
-
-    wl, wr, al = _window_args(window, causal)
 
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be 4-D [B, h, len, d]")
@@ -137,12 +125,90 @@ def forward(q, k, v, *, causal: bool = False, key_lens=None, scale: float | None
     m, d_v = k.shape[2], v.shape[3]
     if tuple(k.shape) != (B, h, m, d_k) or tuple(v.shape) != (B, h, m, d_v):
         raise ValueError(f"shape mismatch: q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
-    kl_ptr = None
-    if key_lens is not None:
-        if key_lens.dtype != torch.int32 or key_lens.device != q.device or key_lens.numel() != B:
-            raise ValueError("key_lens must be an int32 tensor of B elements on q's device")
-        key_lens = key_lens.contiguous()
-        kl_ptr = key_lens.data_ptr()
+    return B, h, n, m, d_k, d_v, dt
+
+
+def _key_lens_ptr(key_lens, B, device):
+    import torch
+
+    if key_lens is None:
+        return None, None
+    if key_lens.dtype != torch.int32 or key_lens.device != device or key_lens.numel() != B:
+        raise ValueError("key_lens must be an int32 tensor of B elements on q's device")
+    key_lens = key_lens.contiguous()
+    return key_lens, key_lens.data_ptr()
+
+
+def _like(t, shape, dtype, device, name):
+    import torch
+
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous() or t.device != device:
+        raise ValueError(f"{name} must be a contiguous {list(shape)} {dtype} tensor on q's device")
+    return t
+
+
+def backward(q, k, v, out, dout, lse, *, causal: bool = False, key_lens=None,
+             scale: float | None = None, window=None, dq=None, dk=None, dv=None, workspace=None):
+    """Gradients (dq, dk, dv) of Eq. (1) for the output gradient ``dout`` (bf16).
+
+    ``out`` and ``lse`` come from ``forward(..., return_lse=True)`` with the same
+    q, k, v, causal, key_lens, scale and window.  dq/dk/dv/workspace may be
+    given to avoid allocations (workspace: a uint8 tensor of at least
+    ``sdpa_backward_workspace_bytes(B, h, n)`` bytes).  Raises RuntimeError with
+    the library's message on a nonzero status.
+    """
+    import torch
+
+    wl, wr, al = _window_args(window, causal)
+    B, h, n, m, d_k, d_v, dt = _check_qkv(q, k, v)
+    for name, t, shape, dtype in (("out", out, (B, h, n, d_v), q.dtype),
+                                  ("dout", dout, (B, h, n, d_v), q.dtype),
+                                  ("lse", lse, (B, h, n), torch.float32)):
+        _like(t, shape, dtype, q.device, name)
+    key_lens, kl_ptr = _key_lens_ptr(key_lens, B, q.device)
+    dq = _like(dq, (B, h, n, d_k), q.dtype, q.device, "dq")
+    dk = _like(dk, (B, h, m, d_k), q.dtype, q.device, "dk")
+    dv = _like(dv, (B, h, m, d_v), q.dtype, q.device, "dv")
+    need = sdpa_backward_workspace_bytes(B, h, n)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d_k)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        rc = sdpa_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
+                           lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, h, n, m,
+                           d_k, d_v, float(scale), wl, wr, al, kl_ptr, dt, workspace.data_ptr(),
+                           workspace.numel() * workspace.element_size(), stream)
+    if rc != _lib.SDPA_OK:
+        raise RuntimeError(f"sdpa_backward failed ({rc}): {sdpa_strerror(rc)}")
+    return dq, dk, dv
+
+
+def forward(q, k, v, *, causal: bool = False, key_lens=None, scale: float | None = None,
+            out=None, window=None, return_lse: bool = False):
+    """Attention over [B, h, n, d_k] queries and [B, h, m, d] keys/values.
+
+    key_lens: None or an int32 tensor [B] on the same device (key j of batch
+    element b is legal iff j < key_lens[b]).  window: None, or
+    (left, right) / (left, right, align) for restricted attention: query i
+    sees keys c_i - left .. c_i + right (None = unbounded side), where
+    c_i = i for align "top_left" (default) and c_i = i + L - n for
+    "bottom_right" (L = the batch element's key length); see
+    ``sdpa_forward_window`` in include/sdpa.h.  Not combined with ``causal``.
+    Returns ``out`` ([B, h, n, d_v], same dtype as q), or ``(out, lse)`` with
+    ``return_lse`` (bf16 only): lse [B, h, n] float32, the natural log of each
+    row's softmax denominator, which ``backward`` takes.  Raises RuntimeError
+    with the library's message on a nonzero status.
+    """
+    import torch
+
+    wl, wr, al = _window_args(window, causal)
+
+    B, h, n, m, d_k, d_v, dt = _check_qkv(q, k, v)
+    key_lens, kl_ptr = _key_lens_ptr(key_lens, B, q.device)
     if out is None:
         out = torch.empty((B, h, n, d_v), dtype=q.dtype, device=q.device)
     elif (tuple(out.shape) != (B, h, n, d_v) or out.dtype != q.dtype or not out.is_contiguous()
@@ -153,7 +219,12 @@ def forward(q, k, v, *, causal: bool = False, key_lens=None, scale: float | None
     # The library launches on the calling thread's current HIP device.
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
-        if window is None:
+        if return_lse:
+            lse = torch.empty((B, h, n), dtype=torch.float32, device=q.device)
+            rc = sdpa_forward_lse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                  lse.data_ptr(), B, h, n, m, d_k, d_v, float(scale), wl, wr, al,
+                                  kl_ptr, dt, stream)
+        elif window is None:
             rc = sdpa_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, h, n,
                               m, d_k, d_v, float(scale),
                               _lib.SDPA_MASK_CAUSAL if causal else _lib.SDPA_MASK_NONE, kl_ptr,
@@ -164,4 +235,4 @@ def forward(q, k, v, *, causal: bool = False, key_lens=None, scale: float | None
                                      stream)
     if rc != _lib.SDPA_OK:
         raise RuntimeError(f"sdpa_forward failed ({rc}): {sdpa_strerror(rc)}")
-    return out
+    return (out, lse) if return_lse else out

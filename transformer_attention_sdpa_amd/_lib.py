@@ -57,6 +57,15 @@ def load() -> ctypes.CDLL:
     lib.sdpa_mha_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                      ctypes.c_float, i32, i32, i32, vp, i32, vp, ctypes.c_size_t, vp]
     lib.sdpa_mha_forward.restype = ctypes.c_int
+    fp = ctypes.c_void_p
+    lib.sdpa_forward_lse.argtypes = [vp, vp, vp, vp, fp, i32, i32, i32, i32, i32, i32,
+                                     ctypes.c_float, i32, i32, i32, vp, i32, vp]
+    lib.sdpa_forward_lse.restype = ctypes.c_int
+    lib.sdpa_backward_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.sdpa_backward_workspace_bytes.restype = ctypes.c_size_t
+    lib.sdpa_backward.argtypes = [vp, vp, vp, vp, vp, fp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                  ctypes.c_float, i32, i32, i32, vp, i32, vp, ctypes.c_size_t, vp]
+    lib.sdpa_backward.restype = ctypes.c_int
     lib.sdpa_strerror.argtypes = [ctypes.c_int]
     lib.sdpa_strerror.restype = ctypes.c_char_p
     lib.sdpa_version.argtypes = []
@@ -91,6 +100,26 @@ def sdpa_mha_forward(x_q, x_kv, w_q, w_k, w_v, w_o, out, B, n, m, d_model, h, d_
     return load().sdpa_mha_forward(x_q, x_kv, w_q, w_k, w_v, w_o, out, B, n, m, d_model, h, d_k,
                                    d_v, scale, window_left, window_right, align, key_lens, dtype,
                                    workspace, workspace_bytes, stream)
+
+
+def sdpa_forward_lse(q, k, v, out, lse, B, h, n, m, d_k, d_v, scale, window_left, window_right,
+                     align, key_lens, dtype, stream) -> int:
+    """Forward to the C entry point of the same name (forward pass + row log-sum-exp)."""
+    return load().sdpa_forward_lse(q, k, v, out, lse, B, h, n, m, d_k, d_v, scale, window_left,
+                                   window_right, align, key_lens, dtype, stream)
+
+
+def sdpa_backward_workspace_bytes(B, h, n) -> int:
+    """Forward to the C entry point of the same name."""
+    return load().sdpa_backward_workspace_bytes(B, h, n)
+
+
+def sdpa_backward(q, k, v, out, dout, lse, dq, dk, dv, B, h, n, m, d_k, d_v, scale, window_left,
+                  window_right, align, key_lens, dtype, workspace, workspace_bytes, stream) -> int:
+    """Forward to the C entry point of the same name (the gradient of Eq. (1))."""
+    return load().sdpa_backward(q, k, v, out, dout, lse, dq, dk, dv, B, h, n, m, d_k, d_v, scale,
+                                window_left, window_right, align, key_lens, dtype, workspace,
+                                workspace_bytes, stream)
 
 
 def sdpa_strerror(status: int) -> str:

@@ -12,7 +12,7 @@
 
 namespace {
 
-constexpr int kVersion = 1 * 10000 + 2 * 100 + 0;  // 1.2.0: the multi-head sublayer
+constexpr int kVersion = 1 * 10000 + 3 * 100 + 0;  // 1.3.0: log-sum-exp output, backward pass
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -89,6 +89,87 @@ extern "C" int sdpa_forward_window(const void* q, const void* k, const void* v, 
     return launch(a, dtype, stream);
 }
 
+// Window arguments → (wl, wr, bottom_right), or SDPA_ERR_MASK.
+int window_args(int32_t n, int32_t m, int32_t window_left, int32_t window_right, int32_t align,
+                int32_t* wl, int32_t* wr, int32_t* br) {
+    if (window_left < -1 || window_right < -1) return SDPA_ERR_MASK;
+    if (align != SDPA_ALIGN_TOP_LEFT && align != SDPA_ALIGN_BOTTOM_RIGHT) return SDPA_ERR_MASK;
+    // A side wider than n + m reaches past every key from every query: unbounded.
+    const int64_t reach = (int64_t)n + m;
+    *wl = window_left > reach ? -1 : window_left;
+    *wr = window_right > reach ? -1 : window_right;
+    *br = align == SDPA_ALIGN_BOTTOM_RIGHT ? 1 : 0;
+    return SDPA_OK;
+}
+
+extern "C" int sdpa_forward_lse(const void* q, const void* k, const void* v, void* out, float* lse,
+                                int32_t B, int32_t h, int32_t n, int32_t m, int32_t d_k, int32_t d_v,
+                                float scale, int32_t window_left, int32_t window_right,
+                                int32_t align, const int32_t* key_lens, int32_t dtype, void* stream) {
+    int st = validate(q, k, v, out, B, h, n, m, d_k, d_v, scale, key_lens, dtype);
+    if (st != SDPA_OK) return st;
+    if (!lse) return SDPA_ERR_NULL;
+    if (dtype != SDPA_BF16) return SDPA_ERR_UNSUPPORTED;
+    if (reinterpret_cast<uintptr_t>(lse) & 3u) return SDPA_ERR_ALIGN;
+    int32_t wl, wr, br;
+    st = window_args(n, m, window_left, window_right, align, &wl, &wr, &br);
+    if (st != SDPA_OK) return st;
+    const uint64_t heads = (uint64_t)B * h;
+    const uint64_t lb = heads * n * 4;
+    const struct { const void* p; uint64_t n; } bufs[] = {
+        {q, heads * n * d_k * 2}, {k, heads * m * d_k * 2}, {v, heads * m * d_v * 2},
+        {out, heads * n * d_v * 2}, {key_lens, key_lens ? (uint64_t)B * 4 : 0}};
+    for (const auto& b : bufs)
+        if (b.p && overlap(lse, lb, b.p, b.n)) return SDPA_ERR_ALIAS;
+    sdpa::Args a{q, k, v, out, B, h, n, m, scale, wl, wr, br, key_lens};
+    a.lse = lse;
+    return launch(a, dtype, stream);
+}
+
+extern "C" size_t sdpa_backward_workspace_bytes(int32_t B, int32_t h, int32_t n) {
+    if (B < 1 || h < 1 || n < 1) return 0;
+    return sdpa::bwd_workspace_bytes(B, h, n);
+}
+
+extern "C" int sdpa_backward(const void* q, const void* k, const void* v, const void* out,
+                             const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                             int32_t B, int32_t h, int32_t n, int32_t m, int32_t d_k, int32_t d_v,
+                             float scale, int32_t window_left, int32_t window_right, int32_t align,
+                             const int32_t* key_lens, int32_t dtype, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+    if (!dout || !lse || !dq || !dk || !dv || !workspace) return SDPA_ERR_NULL;
+    // q, k, v, out, shapes, scale, key_lens (out is an input here: the alias
+    // checks below cover the outputs).
+    int st = validate(q, k, v, const_cast<void*>(out), B, h, n, m, d_k, d_v, scale, key_lens, dtype);
+    if (st != SDPA_OK) return st;
+    if (dtype != SDPA_BF16) return SDPA_ERR_UNSUPPORTED;
+    for (const void* p : {dout, (const void*)dq, (const void*)dk, (const void*)dv, (const void*)workspace})
+        if (!aligned16(p)) return SDPA_ERR_ALIGN;
+    if (reinterpret_cast<uintptr_t>(lse) & 3u) return SDPA_ERR_ALIGN;
+    int32_t wl, wr, br;
+    st = window_args(n, m, window_left, window_right, align, &wl, &wr, &br);
+    if (st != SDPA_OK) return st;
+    const size_t need = sdpa::bwd_workspace_bytes(B, h, n);
+    if (workspace_bytes < need) return SDPA_ERR_WORKSPACE;
+    const uint64_t heads = (uint64_t)B * h;
+    struct Buf { const void* p; uint64_t n; };
+    const Buf ins[] = {{q, heads * n * d_k * 2}, {k, heads * m * d_k * 2}, {v, heads * m * d_v * 2},
+                       {out, heads * n * d_v * 2}, {dout, heads * n * d_v * 2}, {lse, heads * n * 4},
+                       {key_lens, key_lens ? (uint64_t)B * 4 : 0}};
+    const Buf outs[] = {{dq, heads * n * d_k * 2}, {dk, heads * m * d_k * 2}, {dv, heads * m * d_v * 2},
+                        {workspace, need}};
+    for (int i = 0; i < 4; ++i) {
+        for (const Buf& in : ins)
+            if (in.p && overlap(outs[i].p, outs[i].n, in.p, in.n)) return SDPA_ERR_ALIAS;
+        for (int j = i + 1; j < 4; ++j)
+            if (overlap(outs[i].p, outs[i].n, outs[j].p, outs[j].n)) return SDPA_ERR_ALIAS;
+    }
+    const sdpa::BwdArgs a{q, k, v, out, dout, lse, dq, dk, dv, workspace, B, h, n, m, scale, wl, wr, br,
+                          key_lens};
+    const hipError_t e = sdpa::launch_bwd_bf16(a, reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SDPA_OK : SDPA_ERR_LAUNCH;
+}
+
 extern "C" size_t sdpa_mha_workspace_bytes(int32_t B, int32_t n, int32_t m, int32_t h, int32_t d_k,
                                            int32_t d_v) {
     if (B < 1 || n < 1 || m < 1 || h < 1 || d_k != sdpa::kHeadDim || d_v != sdpa::kHeadDim) return 0;
@@ -152,7 +233,7 @@ extern "C" const char* sdpa_strerror(int status) {
         case SDPA_ERR_LAUNCH: return "the HIP runtime refused the kernel launch";
         case SDPA_ERR_SCALE: return "scale must be finite and > 0";
         case SDPA_ERR_ALIAS: return "out overlaps an input (or, for the sublayer, the workspace)";
-        case SDPA_ERR_WORKSPACE: return "workspace smaller than sdpa_mha_workspace_bytes";
+        case SDPA_ERR_WORKSPACE: return "workspace smaller than its *_workspace_bytes size";
         default: return "unknown status";
     }
 }

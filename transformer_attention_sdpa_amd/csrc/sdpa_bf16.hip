@@ -255,7 +255,7 @@ __global__ __launch_bounds__(NW * 64) void sdpa_long_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
     int BH, int H, int n, int m, float c_log2, int wl, int wr, int bottom_right,
-    const int32_t* __restrict__ key_lens, int nqb) {
+    const int32_t* __restrict__ key_lens, int nqb, float* __restrict__ lse) {
     using KT = LongKernel<NW>;
     __shared__ __attribute__((aligned(16))) char lds[2 * 2 * TILE_BYTES];
     KT k;
@@ -371,6 +371,12 @@ __global__ __launch_bounds__(NW * 64) void sdpa_long_bf16(
         const float ltot = half_swap_sum(k.lsum[qt]);
         // no legal key ⇒ zero row; a NaN sum (NaN legal inputs) stays NaN
         const float inv = ltot != 0.f ? 1.f / ltot : 0.f;
+        // ln Σ e^(scale·s) = scale·mref + ln l, with the reference the weights
+        // were formed against: −∞ for a row with no legal key
+        if (lse && k.hf == 0 && qrow < n) {
+            const float mc = k.mref[qt] == -INFINITY ? 0.f : k.mref[qt] * k.c_log2;
+            lse[(size_t)bh * n + qrow] = (mc + log2f(ltot)) * 0.6931471805599453f;
+        }
         if (qrow < n) {
             uint16_t* dst = O + qbase + (size_t)qrow * D;
 #pragma unroll
@@ -397,7 +403,7 @@ hipError_t launch_long(const Args& a, hipStream_t stream) {
     hipLaunchKernelGGL(sdpa_long_bf16<NW>, dim3(nqb * BH), dim3(NW * 64), 0, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (uint16_t*)a.out, BH, a.H, a.n, a.m, c_log2, a.wl, a.wr, a.bottom_right,
-                       a.key_lens, nqb);
+                       a.key_lens, nqb, a.lse);
     return hipGetLastError();
 }
 

@@ -1,0 +1,518 @@
+// Gradient of scaled dot-product attention on gfx950 (bf16 in and out, fp32
+// accumulation).
+//
+// The pages print only the forward pass, Eq. (1) (《精读 Attention Is All You
+// Need：原始 Transformer 论文》, "缩放点积注意力：点积为什么要缩放";
+// 《Attention Is All You Need：注意力就是你所需要的一切》 §3.2.1), and train the
+// model through it.  By the chain rule, with s = scale·q·k, P = softmax(S)
+// row-wise and O = P V:
+//
+//   dV = Pᵀ dO,   dP = dO Vᵀ,   dS = P ∘ (dP − D),   D_i = Σ_j P_ij dP_ij = dO_i · O_i,
+//   dQ = scale · dS K,   dK = scale · dSᵀ Q.
+//
+// P is recomputed tile by tile from the forward pass's per-row log-sum-exp,
+// P_ij = exp(s_ij − lse_i), so no n×m matrix is ever stored.  Two launches,
+// neither with atomics (the result is bitwise deterministic):
+//
+//   1. sdpa_bwd_dq_bf16, one workgroup per block of 32·NW queries: computes
+//      D_i and lse_i·log2 e for its rows (written to the workspace for launch
+//      2), then streams the K/V tiles its queries may see:
+//        Sᵀ = K Qᵀ, dPᵀ = V dOᵀ (A from LDS rows, B = Qᵀ, dOᵀ in VGPRs),
+//        dSᵀ = Pᵀ ∘ (dPᵀ − D),  dQᵀ += Kᵀ dSᵀ (A via LDS transpose reads).
+//   2. sdpa_bwd_dkdv_bf16, one workgroup per block of 32·NW keys: streams the
+//      Q/dO tiles of the queries that may see them:
+//        S = Q Kᵀ, dP = dO Vᵀ (A from LDS rows, B = Kᵀ, Vᵀ in VGPRs),
+//        dVᵀ += dOᵀ P,  dKᵀ += Qᵀ dS (A via LDS transpose reads).
+//
+// Every product is v_mfma_f32_32x32x16_bf16 with the accumulator of one
+// product (lane = one column, 16 rows in groups of 4) serving directly as the
+// B operand of the next: the contraction index then runs in the permuted
+// order 16·j + 4·hf + [0..3], 16·j + 8 + 4·hf + [0..3] for k-step j, and the
+// transpose reads fetch the A operand in that same order.  P and dS are
+// rounded to bf16 for their products, as in the forward pass.
+//
+// LDS reads are written as instructions (ds_read_b128, ds_read_b64_tr_b16)
+// with explicit lgkmcnt waits: through plain loads or the builtins the
+// compiler would wait for the next tile's buffer_load … lds, which is in
+// flight during the current tile's math, before every read.
+#include "sdpa_common.hpp"
+
+namespace sdpa {
+namespace {
+
+constexpr int D = kHeadDim;              // 64
+constexpr int BT = 64;                   // rows per LDS tile
+constexpr int TILE_BYTES = BT * D * 2;   // 8 KiB
+constexpr float LOG2E = 1.4426950408889634f;
+
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+__device__ __forceinline__ u32x4 ds_read_b128(uint32_t a) {
+    u32x4 r;
+    asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(a));
+    return r;
+}
+__device__ __forceinline__ u32x2 ds_read_tr(uint32_t a) {
+    u32x2 r;
+    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(a));
+    return r;
+}
+// Wait for every LDS read of this wave; the results pass through the empty
+// asm after the wait, so no use of them can move above it.
+template <int N>
+__device__ __forceinline__ void lds_wait(u32x4 (&x)[N]) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < N; ++i) asm volatile("" : "+v"(x[i]));
+}
+template <int N>
+__device__ __forceinline__ void lds_wait(u32x2 (&x)[N]) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < N; ++i) asm volatile("" : "+v"(x[i]));
+}
+
+// Per-lane LDS offsets inside one 64-row tile (16-byte chunk c of row r at
+// lds_swz(r, c)), shared by both kernels.
+struct TileAddr {
+    int row[4];    // 16-byte A operand of k-step ks: row l32, chunk 2·ks + hf
+    int tr[2][2];  // transpose reads of k-step 0: [32-column block dt][rows +0 / +8]
+    __device__ void init(int lane) {
+        const int l32 = lane & 31, hf = lane >> 5, gi = lane & 15;
+        const int f = swz_f(l32);  // rows l32 and l32 + 32 share it
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) row[ks] = l32 * 128 + (((2 * ks + hf) ^ f) << 4);
+        // Rows 4·hf + gi/4 (+ 8) of k-step 0; k-step j adds 16·j rows, which
+        // leaves swz_f unchanged (it reads row bits 1..3).
+        const int r0 = 4 * hf + (gi >> 2);
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) {
+            const int c0 = 32 * dt + 16 * ((lane >> 4) & 1) + 4 * (gi & 3);
+            tr[dt][0] = lds_swz(r0, c0 >> 3) * 16 + (c0 & 7) * 2;
+            tr[dt][1] = lds_swz(r0 + 8, c0 >> 3) * 16 + (c0 & 7) * 2;
+        }
+    }
+};
+
+// k-step j of a two-tile accumulator pair as a bf16 B operand: tile j/2,
+// registers 8·(j%2) .. +7.
+__device__ __forceinline__ bf16x8 pack_step(const f32x16 (&x)[2], int j) {
+    const int t = j >> 1, b = 8 * (j & 1);
+    return to_bf16x8(x[t][b], x[t][b + 1], x[t][b + 2], x[t][b + 3], x[t][b + 4], x[t][b + 5],
+                     x[t][b + 6], x[t][b + 7]);
+}
+
+// acc[dt] += Aᵀ · B over one 64-row tile: A is the tile (rows = contraction
+// index, columns = the 64 output rows), fetched with transpose reads in the
+// permuted contraction order; b[j] is k-step j of the B operand.
+__device__ __forceinline__ void tr_product(uint32_t tile, const TileAddr& ta, const bf16x8 (&b)[4],
+                                           f32x16 (&acc)[2]) {
+    u32x2 a[16];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) {
+            a[4 * j + 2 * dt] = ds_read_tr(tile + ta.tr[dt][0] + j * 16 * 128);
+            a[4 * j + 2 * dt + 1] = ds_read_tr(tile + ta.tr[dt][1] + j * 16 * 128);
+        }
+    lds_wait(a);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) {
+            const u32x4 v = {a[4 * j + 2 * dt][0], a[4 * j + 2 * dt][1], a[4 * j + 2 * dt + 1][0],
+                             a[4 * j + 2 * dt + 1][1]};
+            acc[dt] = mfma32x32x16_bf16(__builtin_bit_cast(bf16x8, v), b[j], acc[dt]);
+        }
+}
+
+// s[t] = A_t · B and p[t] = A'_t · B' for the two 32-row halves t of two tiles
+// A, A' (rows from LDS) against B, B' (k = 64 dims, in VGPRs).
+__device__ __forceinline__ void row_products(uint32_t ta_, uint32_t tb_, const TileAddr& ta,
+                                             const bf16x8 (&b)[4], const bf16x8 (&b2)[4],
+                                             f32x16 (&s)[2], f32x16 (&p)[2]) {
+    u32x4 a[16];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            a[4 * t + ks] = ds_read_b128(ta_ + ta.row[ks] + t * 32 * 128);
+            a[8 + 4 * t + ks] = ds_read_b128(tb_ + ta.row[ks] + t * 32 * 128);
+        }
+    lds_wait(a);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) { s[t][i] = 0.f; p[t][i] = 0.f; }
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            s[t] = mfma32x32x16_bf16(__builtin_bit_cast(bf16x8, a[4 * t + ks]), b[ks], s[t]);
+            p[t] = mfma32x32x16_bf16(__builtin_bit_cast(bf16x8, a[8 + 4 * t + ks]), b2[ks], p[t]);
+        }
+    }
+}
+
+// This lane's 16-byte operand chunks of one 64-wide row (dims 16·ks + 8·hf
+// + [0..7]), zeros if the row is out of range.
+__device__ __forceinline__ void load_row_operand(const uint16_t* rowp, bool ok, int hf, bf16x8 (&x)[4]) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+        x[ks] = ok ? __builtin_bit_cast(bf16x8, reinterpret_cast<const u32x4*>(rowp)[2 * ks + hf])
+                   : __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+}
+
+// Store a transposed accumulator pair (register i of acc[dt] is column
+// 32·dt + 8·(i/4) + 4·hf + i%4 of this lane's row) times `mul` as bf16.
+__device__ __forceinline__ void store_rowT(uint16_t* dst, const f32x16 (&acc)[2], int hf, float mul) {
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+            bf16x4 o;
+            o[0] = (__bf16)(acc[dt][4 * i4 + 0] * mul);
+            o[1] = (__bf16)(acc[dt][4 * i4 + 1] * mul);
+            o[2] = (__bf16)(acc[dt][4 * i4 + 2] * mul);
+            o[3] = (__bf16)(acc[dt][4 * i4 + 3] * mul);
+            *reinterpret_cast<bf16x4*>(dst + 32 * dt + 8 * i4 + 4 * hf) = o;
+        }
+}
+
+// Copy rows [r0, r0 + 64) of a [len, 64] bf16 tensor into an LDS tile; rows
+// at or past `len` arrive as zeros.  Wave w of NW issues 8/NW of the eight
+// 1 KiB loads; lane ln lands in (row ln/8, position ln%8), which holds chunk
+// (ln%8) ^ swz_f(row).
+template <int NW>
+__device__ __forceinline__ void load_tile(char* lds_tile, const uint16_t* base, int r0, int len, int w,
+                                          int lane) {
+    const int left = len - r0;
+    const i32x4 rs = make_rsrc(base + (size_t)r0 * D, (uint32_t)(left > 0 ? left : 0) * (D * 2));
+#pragma unroll
+    for (int i = 0; i < 8 / NW; ++i) {
+        const int blk = w * (8 / NW) + i;
+        const int row = 8 * blk + (lane >> 3);
+        const int off = row * 128 + (((lane & 7) ^ swz_f(row)) << 4);
+        load16_to_lds(rs, lds_tile + blk * 1024, off);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Launch 1: dQ (and D, lse·log2 e for launch 2).
+
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void sdpa_bwd_dq_bf16(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO, const float* __restrict__ lse,
+    uint16_t* __restrict__ dQ, float* __restrict__ ws_d, float* __restrict__ ws_l,
+    int BH, int H, int n, int m, float scale, float c_log2, int wl, int wr, int bottom_right,
+    const int32_t* __restrict__ key_lens, int nqb) {
+    __shared__ __attribute__((aligned(1024))) char lds[2 * 2 * TILE_BYTES];  // [buf][K | V]
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+
+    // Latest query blocks first (they see the most keys under a causal mask).
+    const int g = blockIdx.x;
+    const int bh = g % BH;
+    const int q0 = (nqb - 1 - g / BH) * 32 * NW;
+    const int b = bh / H;
+    int L = m;
+    if (key_lens) {
+        const int t = key_lens[b];
+        L = t < 0 ? 0 : (t > m ? m : t);
+    }
+    const KeyWindow win{wl, wr, bottom_right ? L - n : 0, L};
+    const int qlast = min(q0 + 32 * NW, n) - 1;
+    const int kbeg = win.lo(q0), kend = win.hi(qlast);
+    const int tbeg = kbeg / BT;
+    const int tend = kend > kbeg ? (kend + BT - 1) / BT : tbeg;
+    // This wave's queries: keys [wlo, whi) are needed, [flo, fhi) legal for all.
+    const int wq0 = q0 + 32 * w;
+    const int wlast = min(wq0 + 32, n) - 1;
+    const bool wact = wlast >= wq0;
+    const int wlo = wact ? win.lo(wq0) : 0, whi = wact ? win.hi(wlast) : 0;
+    const int flo = wact ? win.lo(wlast) : 0, fhi = wact ? win.hi(wq0) : 0;
+
+    const size_t qbase = (size_t)bh * n * D, kvbase = (size_t)bh * m * D;
+    const int qrow = wq0 + l32;
+    const bool qok = qrow < n;
+    bf16x8 qop[4], dop[4];
+    load_row_operand(Q + qbase + (size_t)qrow * D, qok, hf, qop);
+    load_row_operand(dO + qbase + (size_t)qrow * D, qok, hf, dop);
+    // D_i = dO_i · O_i over this lane's 32 dims, then the other half-wave's.
+    float dsum;
+    {
+        bf16x8 oop[4];
+        load_row_operand(O + qbase + (size_t)qrow * D, qok, hf, oop);
+        float acc = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)dop[ks][e], (float)oop[ks][e], acc);
+        dsum = half_swap_sum(acc);
+    }
+    // P = 2^(s·c − lc); a row with no legal key (lse = −∞) gets lc = +∞, P = 0.
+    const float lr = qok ? lse[(size_t)bh * n + qrow] : 0.f;
+    const float lc = lr == -INFINITY ? INFINITY : lr * LOG2E;
+    if (qok && hf == 0) {
+        ws_d[(size_t)bh * n + qrow] = dsum;
+        ws_l[(size_t)bh * n + qrow] = lc;
+    }
+
+    TileAddr ta;
+    ta.init(lane);
+    const uint32_t l0 = lds_u32(lds);
+    f32x16 acc[2];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) { acc[0][i] = 0.f; acc[1][i] = 0.f; }
+
+    auto issue = [&](int t, int buf) {
+        load_tile<NW>(lds + buf * 2 * TILE_BYTES, K + kvbase, t * BT, L, w, lane);
+        load_tile<NW>(lds + buf * 2 * TILE_BYTES + TILE_BYTES, V + kvbase, t * BT, L, w, lane);
+    };
+    if (tend > tbeg) issue(tbeg, 0);
+    wait_vmem();
+    __syncthreads();
+    for (int t = tbeg; t < tend; ++t) {
+        const int buf = (t - tbeg) & 1;
+        if (t + 1 < tend) issue(t + 1, buf ^ 1);
+        const int k0 = t * BT;
+        if (k0 < whi && k0 + BT > wlo) {  // uniform: some query of the wave sees the tile
+            const uint32_t sk = l0 + buf * 2 * TILE_BYTES, sv = sk + TILE_BYTES;
+            f32x16 s[2], dp[2];
+            row_products(sk, sv, ta, qop, dop, s, dp);
+            // Register i of s[kt] is key k0 + 32·kt + 8·(i/4) + 4·hf + i%4.
+            if (k0 < flo || k0 + BT > fhi) {
+                const int llo = win.lo(qrow) - k0 - 4 * hf, lhi = win.hi(qrow) - k0 - 4 * hf;
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int off = 32 * kt + 8 * (i >> 2) + (i & 3);
+                        s[kt][i] = (off >= llo && off < lhi) ? s[kt][i] : -INFINITY;
+                    }
+            }
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const float p = exp2_hw(__builtin_fmaf(s[kt][i], c_log2, -lc));
+                    s[kt][i] = p * (dp[kt][i] - dsum);  // dSᵀ
+                }
+            bf16x8 db[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) db[j] = pack_step(s, j);
+            tr_product(sk, ta, db, acc);  // dQᵀ += Kᵀ dSᵀ
+        }
+        wait_vmem();
+        __syncthreads();
+    }
+    if (qok) store_rowT(dQ + qbase + (size_t)qrow * D, acc, hf, scale);
+}
+
+// ---------------------------------------------------------------------------
+// Launch 2: dK, dV.
+
+// Queries that may see key j form the interval [qa, qb) (the legal keys of a
+// query, [lo_i, hi_i), move right with i).  Keys at or past L see none.
+struct QueryRange {
+    int wl, wr, shift, L, n;
+    __device__ __forceinline__ int qa(int j) const {
+        if (j >= L) return 0;
+        if (wr < 0) return 0;
+        const long long c = (long long)j - shift - wr;  // hi_i > j  ⇔  i ≥ j − shift − wr
+        return c <= 0 ? 0 : (c >= n ? n : (int)c);
+    }
+    __device__ __forceinline__ int qb(int j) const {
+        if (j >= L) return 0;
+        if (wl < 0) return n;
+        const long long c = (long long)j - shift + wl + 1;  // lo_i ≤ j  ⇔  i ≤ j − shift + wl
+        return c <= 0 ? 0 : (c >= n ? n : (int)c);
+    }
+};
+
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void sdpa_bwd_dkdv_bf16(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ dO, const float* __restrict__ ws_d, const float* __restrict__ ws_l,
+    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
+    int BH, int H, int n, int m, float scale, float c_log2, int wl, int wr, int bottom_right,
+    const int32_t* __restrict__ key_lens) {
+    // [buf][Q tile | dO tile | lse·log2 e (64 floats) | D (64 floats)]
+    constexpr int STAGE = 2 * TILE_BYTES + 512;
+    __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE];
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+
+    // Earliest key blocks first (seen by the most queries under a causal mask).
+    const int g = blockIdx.x;
+    const int bh = g % BH;
+    const int k0 = (g / BH) * 32 * NW;
+    const int b = bh / H;
+    int L = m;
+    if (key_lens) {
+        const int t = key_lens[b];
+        L = t < 0 ? 0 : (t > m ? m : t);
+    }
+    const QueryRange qr{wl, wr, bottom_right ? L - n : 0, L, n};
+    // Queries [qbeg, qend) see some key of the block.
+    const int klast = min(k0 + 32 * NW, L) - 1;
+    const int qbeg = klast >= k0 ? qr.qa(k0) : 0;
+    const int qend = klast >= k0 ? qr.qb(klast) : 0;
+    const int tbeg = qbeg / BT;
+    const int tend = qend > qbeg ? (qend + BT - 1) / BT : tbeg;
+    // This wave's keys: queries [wqa, wqb) needed, [fqa, fqb) see all of them.
+    const int wk0 = k0 + 32 * w;
+    const int wlast = min(wk0 + 32, L) - 1;
+    const bool wact = wlast >= wk0;
+    const int wqa = wact ? qr.qa(wk0) : 0, wqb = wact ? qr.qb(wlast) : 0;
+    // a wave holding keys past L never has a tile legal for all of them
+    const bool wfull = wact && wk0 + 31 < L;
+    const int fqa = wfull ? qr.qa(wlast) : 0, fqb = wfull ? qr.qb(wk0) : 0;
+
+    const size_t qbase = (size_t)bh * n * D, kvbase = (size_t)bh * m * D;
+    const int key = wk0 + l32;
+    // Kᵀ, Vᵀ as B operands; keys at or past L are zeros (their rows may hold
+    // anything), so their logits are masked and their dS is exactly 0.
+    bf16x8 kop[4], vop[4];
+    load_row_operand(K + kvbase + (size_t)key * D, key < L, hf, kop);
+    load_row_operand(V + kvbase + (size_t)key * D, key < L, hf, vop);
+    const int ka = qr.qa(key), kb = qr.qb(key);
+
+    TileAddr ta;
+    ta.init(lane);
+    const uint32_t l0 = lds_u32(lds);
+    f32x16 dka[2], dva[2];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) { dka[0][i] = 0.f; dka[1][i] = 0.f; dva[0][i] = 0.f; dva[1][i] = 0.f; }
+
+    auto issue = [&](int t, int buf) {
+        char* st = lds + buf * STAGE;
+        load_tile<NW>(st, Q + qbase, t * BT, n, w, lane);
+        load_tile<NW>(st + TILE_BYTES, dO + qbase, t * BT, n, w, lane);
+        if (w == 0) {  // 64 floats each: one dword per lane
+            const int left = n - t * BT;
+            const uint32_t nb = (uint32_t)(left > 0 ? left : 0) * 4u;
+            const i32x4 rl = make_rsrc(ws_l + (size_t)bh * n + t * BT, nb);
+            const i32x4 rd = make_rsrc(ws_d + (size_t)bh * n + t * BT, nb);
+            sdpa_llvm_buffer_load_lds(rl, (__attribute__((address_space(3))) void*)(st + 2 * TILE_BYTES), 4,
+                                      lane * 4, 0, 0, 0);
+            sdpa_llvm_buffer_load_lds(rd, (__attribute__((address_space(3))) void*)(st + 2 * TILE_BYTES + 256),
+                                      4, lane * 4, 0, 0, 0);
+        }
+    };
+    if (tend > tbeg) issue(tbeg, 0);
+    wait_vmem();
+    __syncthreads();
+    for (int t = tbeg; t < tend; ++t) {
+        const int buf = (t - tbeg) & 1;
+        if (t + 1 < tend) issue(t + 1, buf ^ 1);
+        const int t0 = t * BT;
+        if (t0 < wqb && t0 + BT > wqa) {  // uniform: some query of the tile sees a key of the wave
+            const uint32_t sq = l0 + buf * STAGE, sd = sq + TILE_BYTES;
+            f32x16 s[2], dp[2];
+            row_products(sq, sd, ta, kop, vop, s, dp);
+            // Register i of s[qh] is query t0 + 32·qh + 8·(i/4) + 4·hf + i%4.
+            if (t0 < fqa || t0 + BT > fqb) {
+                const int llo = ka - t0 - 4 * hf, lhi = kb - t0 - 4 * hf;
+#pragma unroll
+                for (int qh = 0; qh < 2; ++qh)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int off = 32 * qh + 8 * (i >> 2) + (i & 3);
+                        s[qh][i] = (off >= llo && off < lhi) ? s[qh][i] : -INFINITY;
+                    }
+            }
+            // lse·log2 e and D of those queries: four consecutive floats per
+            // group of four registers.
+            u32x4 lv[8];
+#pragma unroll
+            for (int qh = 0; qh < 2; ++qh)
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq) {
+                    const uint32_t off = (uint32_t)(32 * qh + 8 * gq + 4 * hf) * 4u;
+                    lv[4 * qh + gq] = ds_read_b128(sq + 2 * TILE_BYTES + off);
+                }
+            lds_wait(lv);
+            u32x4 dv4[8];
+#pragma unroll
+            for (int qh = 0; qh < 2; ++qh)
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq) {
+                    const uint32_t off = (uint32_t)(32 * qh + 8 * gq + 4 * hf) * 4u;
+                    dv4[4 * qh + gq] = ds_read_b128(sq + 2 * TILE_BYTES + 256 + off);
+                }
+            lds_wait(dv4);
+#pragma unroll
+            for (int qh = 0; qh < 2; ++qh)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const float lc = __uint_as_float(lv[4 * qh + (i >> 2)][i & 3]);
+                    const float dd = __uint_as_float(dv4[4 * qh + (i >> 2)][i & 3]);
+                    const float p = exp2_hw(__builtin_fmaf(s[qh][i], c_log2, -lc));
+                    s[qh][i] = p;
+                    dp[qh][i] = p * (dp[qh][i] - dd);  // dS
+                }
+            bf16x8 pb[4], db[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                pb[j] = pack_step(s, j);
+                db[j] = pack_step(dp, j);
+            }
+            tr_product(sd, ta, pb, dva);  // dVᵀ += dOᵀ P
+            tr_product(sq, ta, db, dka);  // dKᵀ += Qᵀ dS
+        }
+        wait_vmem();
+        __syncthreads();
+    }
+    if (key < m) {
+        store_rowT(dK + kvbase + (size_t)key * D, dka, hf, scale);
+        store_rowT(dV + kvbase + (size_t)key * D, dva, hf, 1.f);
+    }
+}
+
+}  // namespace
+
+size_t bwd_workspace_bytes(int B, int H, int n) { return 2 * (((size_t)B * H * n * 4 + 255) & ~(size_t)255); }
+
+hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
+    const int BH = a.B * a.H;
+    const float c_log2 = (float)((double)a.scale * 1.4426950408889634);  // scale·log2(e)
+    float* ws_d = static_cast<float*>(a.workspace);
+    float* ws_l = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + bwd_workspace_bytes(a.B, a.H, a.n) / 2);
+    // 4 waves per workgroup once there are enough blocks to fill the chip.
+    const long long qblocks4 = (long long)BH * ((a.n + 127) / 128);
+    if (qblocks4 >= 1024) {
+        const int nqb = (a.n + 127) / 128;
+        hipLaunchKernelGGL(sdpa_bwd_dq_bf16<4>, dim3(nqb * BH), dim3(256), 0, stream,
+                           (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                           (const uint16_t*)a.out, (const uint16_t*)a.dout, a.lse, (uint16_t*)a.dq,
+                           ws_d, ws_l, BH, a.H, a.n, a.m, a.scale, c_log2, a.wl, a.wr, a.bottom_right,
+                           a.key_lens, nqb);
+    } else {
+        const int nqb = (a.n + 63) / 64;
+        hipLaunchKernelGGL(sdpa_bwd_dq_bf16<2>, dim3(nqb * BH), dim3(128), 0, stream,
+                           (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                           (const uint16_t*)a.out, (const uint16_t*)a.dout, a.lse, (uint16_t*)a.dq,
+                           ws_d, ws_l, BH, a.H, a.n, a.m, a.scale, c_log2, a.wl, a.wr, a.bottom_right,
+                           a.key_lens, nqb);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const long long kblocks4 = (long long)BH * ((a.m + 127) / 128);
+    if (kblocks4 >= 1024) {
+        hipLaunchKernelGGL(sdpa_bwd_dkdv_bf16<4>, dim3(((a.m + 127) / 128) * BH), dim3(256), 0, stream,
+                           (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                           (const uint16_t*)a.dout, ws_d, ws_l, (uint16_t*)a.dk, (uint16_t*)a.dv, BH, a.H,
+                           a.n, a.m, a.scale, c_log2, a.wl, a.wr, a.bottom_right, a.key_lens);
+    } else {
+        hipLaunchKernelGGL(sdpa_bwd_dkdv_bf16<2>, dim3(((a.m + 63) / 64) * BH), dim3(128), 0, stream,
+                           (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                           (const uint16_t*)a.dout, ws_d, ws_l, (uint16_t*)a.dk, (uint16_t*)a.dv, BH, a.H,
+                           a.n, a.m, a.scale, c_log2, a.wl, a.wr, a.bottom_right, a.key_lens);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace sdpa

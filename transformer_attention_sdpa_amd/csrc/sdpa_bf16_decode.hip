@@ -55,7 +55,7 @@ __global__ __launch_bounds__(NWD * 64) void sdpa_decode_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
     int H, int n, int m, float c_log2, int wl, int wr, int bottom_right,
-    const int32_t* __restrict__ key_lens) {
+    const int32_t* __restrict__ key_lens, float* __restrict__ lse) {
     constexpr int NTL = KS / 16, NJ = KS / 32, NVL = KS / 8;
     constexpr int VBUF = KS * 128;  // one step of V rows in LDS
     // Per wave: two V step buffers; after the loop the first one holds the
@@ -276,6 +276,8 @@ __global__ __launch_bounds__(NWD * 64) void sdpa_decode_bf16(
         }
         // no legal key ⇒ zero row; a NaN sum (NaN legal inputs) stays NaN
         const float inv = lt != 0.f ? 1.f / lt : 0.f;
+        // ln Σ e^(scale·s) = (mcx + log2 lt)·ln 2: −∞ for a row with no legal key
+        if (lse && fd == 0) lse[(size_t)bh * n + fq] = (mcx + log2f(lt)) * 0.6931471805599453f;
         bf16x4 ov;
         ov[0] = (__bf16)(acc[0] * inv);
         ov[1] = (__bf16)(acc[1] * inv);
@@ -300,7 +302,7 @@ hipError_t launch_bf16_decode(const Args& a, hipStream_t stream) {
     hipLaunchKernelGGL(sdpa_decode_bf16<32>, dim3(a.B * a.H), dim3(NWD * 64), 0, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (uint16_t*)a.out, a.H, a.n, a.m, c_log2, a.wl, a.wr, a.bottom_right,
-                       a.key_lens);
+                       a.key_lens, a.lse);
     return hipGetLastError();
 }
 

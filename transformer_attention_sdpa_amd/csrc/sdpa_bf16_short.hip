@@ -74,7 +74,7 @@ __global__ __launch_bounds__(NT) void sdpa_short_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
     int H, int n, int m, float c_log2, int wl, int wr, int bottom_right,
-    const int32_t* __restrict__ key_lens) {
+    const int32_t* __restrict__ key_lens, float* __restrict__ lse) {
     // K tile at 0, Q tile at 8 KiB, V tile at 16 KiB (64 rows × 128 B each).
     __shared__ __attribute__((aligned(16))) char lds[3 * MAXLEN * 128];
     const u32x4* sK = reinterpret_cast<const u32x4*>(lds);
@@ -209,6 +209,8 @@ __global__ __launch_bounds__(NT) void sdpa_short_bf16(
                 l += p;
             }
         l = quad_sum(l);
+        // ln Σ e^(scale·s) = (mc + log2 l)·ln 2: −∞ for a row with no legal key
+        if (lse && G == 0 && q < n) lse[(size_t)bh * n + q] = (mc + log2f(l)) * 0.6931471805599453f;
 #pragma unroll
         for (int j = 0; j < 2; ++j)
             pb[j] = to_bf16x8(s[2 * j][0], s[2 * j][1], s[2 * j][2], s[2 * j][3],
@@ -279,7 +281,7 @@ hipError_t launch_bf16_short(const Args& a, hipStream_t stream) {
                        dim3(NT), 0, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (uint16_t*)a.out, a.H, a.n, a.m, c_log2, a.wl, a.wr, a.bottom_right,
-                       a.key_lens);
+                       a.key_lens, a.lse);
     return hipGetLastError();
 }
 

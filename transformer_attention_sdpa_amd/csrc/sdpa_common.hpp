@@ -35,6 +35,9 @@ struct Args {
     int wl, wr;           // window sides, >= -1
     int bottom_right;     // 0: c_i = i; 1: c_i = i + L - n
     const int32_t* key_lens;  // device int32[B] or nullptr
+    // Optional: per query row, ln Σ_j exp(scale · q·k_j) over the legal keys
+    // (−∞ for a row with none), fp32 [B, H, n]; bf16 kernels only.
+    float* lse = nullptr;
 };
 
 // Legal key range [lo, hi) of query row i under the window of one batch
@@ -78,6 +81,27 @@ struct MhaArgs {
     const int32_t* key_lens;
 };
 size_t mha_workspace_bytes(int B, int n, int m, int h);
+
+// The gradient of Eq. (1) (bf16): dQ, dK, dV from Q, K, V, the forward output
+// O, its gradient dO and the forward pass's per-row log-sum-exp.
+struct BwdArgs {
+    const void* q;     // [B, H, n, 64]
+    const void* k;     // [B, H, m, 64]
+    const void* v;     // [B, H, m, 64]
+    const void* out;   // [B, H, n, 64], the forward output
+    const void* dout;  // [B, H, n, 64]
+    const float* lse;  // [B, H, n]
+    void* dq;          // [B, H, n, 64]
+    void* dk;          // [B, H, m, 64]
+    void* dv;          // [B, H, m, 64]
+    void* workspace;   // bwd_workspace_bytes(B, H, n) bytes
+    int B, H, n, m;
+    float scale;
+    int wl, wr, bottom_right;
+    const int32_t* key_lens;
+};
+size_t bwd_workspace_bytes(int B, int H, int n);
+hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_mha_bf16(const MhaArgs& a, hipStream_t stream);
 
 hipError_t launch_bf16(const Args& a, hipStream_t stream);        // picks one of the three below
