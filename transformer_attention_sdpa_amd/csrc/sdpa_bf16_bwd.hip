@@ -472,6 +472,170 @@ __global__ __launch_bounds__(NW * 64) void sdpa_bwd_dkdv_bf16(
     }
 }
 
+// ---------------------------------------------------------------------------
+// Sentence length (n, m ≤ 64): one workgroup per head, one launch.  The
+// head's Q, dO, K and V (8 KiB each) are copied into LDS once; waves 2 and 3
+// take the dQ role for queries 0..31 and 32..63 (and first publish D and
+// lse·log2 e of their rows through LDS), waves 0 and 1 the dK/dV role for keys
+// 0..31 and 32..63.  Each role is one tile of the two kernels above.
+
+__global__ __launch_bounds__(256) void sdpa_bwd_short_bf16(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO, const float* __restrict__ lse,
+    uint16_t* __restrict__ dQ, uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
+    int H, int n, int m, float scale, float c_log2, int wl, int wr, int bottom_right,
+    const int32_t* __restrict__ key_lens) {
+    // [Q | dO | K | V] tiles, then lse·log2 e and D of the 64 query rows.
+    __shared__ __attribute__((aligned(1024))) char lds[4 * TILE_BYTES + 512];
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+    const int bh = blockIdx.x;
+    const int b = bh / H;
+    const size_t qbase = (size_t)bh * n * D, kvbase = (size_t)bh * m * D;
+    int L = m;
+    if (key_lens) {
+        const int t = key_lens[b];
+        L = t < 0 ? 0 : (t > m ? m : t);
+    }
+    // Each wave copies two of the eight 1 KiB blocks of every tile.
+    load_tile<4>(lds, Q + qbase, 0, n, w, lane);
+    load_tile<4>(lds + TILE_BYTES, dO + qbase, 0, n, w, lane);
+    load_tile<4>(lds + 2 * TILE_BYTES, K + kvbase, 0, L, w, lane);
+    load_tile<4>(lds + 3 * TILE_BYTES, V + kvbase, 0, L, w, lane);
+    const KeyWindow win{wl, wr, bottom_right ? L - n : 0, L};
+    float* sl = reinterpret_cast<float*>(lds + 4 * TILE_BYTES);
+    float* sdd = sl + 64;
+
+    TileAddr ta;
+    ta.init(lane);
+    const uint32_t l0 = lds_u32(lds);
+    const uint32_t sq = l0, sdo = l0 + TILE_BYTES, sk = l0 + 2 * TILE_BYTES, sv = l0 + 3 * TILE_BYTES;
+
+    // dQ role: D and lse·log2 e of this wave's queries, from global O and dO.
+    const int qrow = 32 * (w - 2) + l32;
+    const bool qok = w >= 2 && qrow < n;
+    float dsum = 0.f, lc = 0.f;
+    if (w >= 2) {
+        bf16x8 oop[4], dop[4];
+        load_row_operand(O + qbase + (size_t)qrow * D, qok, hf, oop);
+        load_row_operand(dO + qbase + (size_t)qrow * D, qok, hf, dop);
+        float acc = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)dop[ks][e], (float)oop[ks][e], acc);
+        dsum = half_swap_sum(acc);
+        const float lr = qok ? lse[(size_t)bh * n + qrow] : 0.f;
+        lc = lr == -INFINITY ? INFINITY : lr * LOG2E;
+        if (hf == 0) {
+            sl[qrow] = lc;
+            sdd[qrow] = dsum;
+        }
+    }
+    wait_vmem();
+    __syncthreads();
+
+    if (w >= 2) {
+        // Sᵀ = K Qᵀ, dPᵀ = V dOᵀ over the 64 keys; dQᵀ += Kᵀ dSᵀ.
+        bf16x8 qop[4], dop[4];
+        {
+            u32x4 r[8];
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                r[ks] = ds_read_b128(sq + ta.row[ks] + (w - 2) * 32 * 128);
+                r[4 + ks] = ds_read_b128(sdo + ta.row[ks] + (w - 2) * 32 * 128);
+            }
+            lds_wait(r);
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                qop[ks] = __builtin_bit_cast(bf16x8, r[ks]);
+                dop[ks] = __builtin_bit_cast(bf16x8, r[4 + ks]);
+            }
+        }
+        f32x16 s[2], dp[2];
+        row_products(sk, sv, ta, qop, dop, s, dp);
+        const int llo = win.lo32(qrow) - 4 * hf, lhi = win.hi32(qrow) - 4 * hf;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int off = 32 * kt + 8 * (i >> 2) + (i & 3);
+                const float sv_ = (off >= llo && off < lhi) ? s[kt][i] : -INFINITY;
+                const float p = exp2_hw(__builtin_fmaf(sv_, c_log2, -lc));
+                s[kt][i] = p * (dp[kt][i] - dsum);  // dSᵀ
+            }
+        bf16x8 db[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) db[j] = pack_step(s, j);
+        f32x16 acc[2];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) { acc[0][i] = 0.f; acc[1][i] = 0.f; }
+        tr_product(sk, ta, db, acc);
+        if (qok) store_rowT(dQ + qbase + (size_t)qrow * D, acc, hf, scale);
+    } else {
+        // S = Q Kᵀ, dP = dO Vᵀ over the 64 queries; dVᵀ += dOᵀ P, dKᵀ += Qᵀ dS.
+        const int key = 32 * w + l32;
+        bf16x8 kop[4], vop[4];
+        {
+            u32x4 r[8];
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                r[ks] = ds_read_b128(sk + ta.row[ks] + w * 32 * 128);
+                r[4 + ks] = ds_read_b128(sv + ta.row[ks] + w * 32 * 128);
+            }
+            lds_wait(r);
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                kop[ks] = __builtin_bit_cast(bf16x8, r[ks]);
+                vop[ks] = __builtin_bit_cast(bf16x8, r[4 + ks]);
+            }
+        }
+        f32x16 s[2], dp[2];
+        row_products(sq, sdo, ta, kop, vop, s, dp);
+        const QueryRange qr{wl, wr, bottom_right ? L - n : 0, L, n};
+        const int llo = qr.qa(key) - 4 * hf, lhi = qr.qb(key) - 4 * hf;
+        u32x4 lv[8], dv4[8];
+#pragma unroll
+        for (int qh = 0; qh < 2; ++qh)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                const uint32_t off = (uint32_t)(32 * qh + 8 * gq + 4 * hf) * 4u;
+                lv[4 * qh + gq] = ds_read_b128(l0 + 4 * TILE_BYTES + off);
+                dv4[4 * qh + gq] = ds_read_b128(l0 + 4 * TILE_BYTES + 256 + off);
+            }
+        lds_wait(lv);
+        lds_wait(dv4);
+#pragma unroll
+        for (int qh = 0; qh < 2; ++qh)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int off = 32 * qh + 8 * (i >> 2) + (i & 3);
+                const float sv_ = (off >= llo && off < lhi) ? s[qh][i] : -INFINITY;
+                const float lcq = __uint_as_float(lv[4 * qh + (i >> 2)][i & 3]);
+                const float dd = __uint_as_float(dv4[4 * qh + (i >> 2)][i & 3]);
+                const float p = exp2_hw(__builtin_fmaf(sv_, c_log2, -lcq));
+                s[qh][i] = p;
+                dp[qh][i] = p * (dp[qh][i] - dd);  // dS
+            }
+        bf16x8 pb[4], db[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            pb[j] = pack_step(s, j);
+            db[j] = pack_step(dp, j);
+        }
+        f32x16 dka[2], dva[2];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) { dka[0][i] = 0.f; dka[1][i] = 0.f; dva[0][i] = 0.f; dva[1][i] = 0.f; }
+        tr_product(sdo, ta, pb, dva);
+        tr_product(sq, ta, db, dka);
+        if (key < m) {
+            store_rowT(dK + kvbase + (size_t)key * D, dka, hf, scale);
+            store_rowT(dV + kvbase + (size_t)key * D, dva, hf, 1.f);
+        }
+    }
+}
+
 }  // namespace
 
 size_t bwd_workspace_bytes(int B, int H, int n) { return 2 * (((size_t)B * H * n * 4 + 255) & ~(size_t)255); }
@@ -482,6 +646,14 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
     float* ws_d = static_cast<float*>(a.workspace);
     float* ws_l = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + bwd_workspace_bytes(a.B, a.H, a.n) / 2);
     // 4 waves per workgroup once there are enough blocks to fill the chip.
+    if (a.n <= 64 && a.m <= 64) {
+        hipLaunchKernelGGL(sdpa_bwd_short_bf16, dim3(BH), dim3(256), 0, stream, (const uint16_t*)a.q,
+                           (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.out,
+                           (const uint16_t*)a.dout, a.lse, (uint16_t*)a.dq, (uint16_t*)a.dk,
+                           (uint16_t*)a.dv, a.H, a.n, a.m, a.scale, c_log2, a.wl, a.wr, a.bottom_right,
+                           a.key_lens);
+        return hipGetLastError();
+    }
     const long long qblocks4 = (long long)BH * ((a.n + 127) / 128);
     if (qblocks4 >= 1024) {
         const int nqb = (a.n + 127) / 128;
