@@ -68,7 +68,10 @@ def call(q=P, k=2 * P, v=3 * P, out=4 * P, B=2, h=2, n=8, m=8, d_k=64, d_v=64, s
     (dict(n=0), _lib.SDPA_ERR_SHAPE),
     (dict(m=0), _lib.SDPA_ERR_SHAPE),
     (dict(B=1 << 20, h=1 << 10, n=1 << 20), _lib.SDPA_ERR_SHAPE),
-    (dict(d_k=32, d_v=32), _lib.SDPA_ERR_UNSUPPORTED),
+    (dict(d_k=32, d_v=32, dtype=0), _lib.SDPA_ERR_UNSUPPORTED),  # other widths: bf16 only
+    (dict(d_k=16, d_v=16), _lib.SDPA_ERR_UNSUPPORTED),
+    (dict(d_k=96, d_v=96), _lib.SDPA_ERR_UNSUPPORTED),
+    (dict(d_k=32, d_v=64), _lib.SDPA_ERR_UNSUPPORTED),            # d_k != d_v
     (dict(d_v=128), _lib.SDPA_ERR_UNSUPPORTED),
     (dict(q=P + 8), _lib.SDPA_ERR_ALIGN),
     (dict(out=4 * P + 2), _lib.SDPA_ERR_ALIGN),
@@ -106,7 +109,8 @@ def call_window(wl=-1, wr=-1, align=0, **kw):
     (dict(align=-1), _lib.SDPA_ERR_MASK),
     (dict(q=None), _lib.SDPA_ERR_NULL),
     (dict(n=0), _lib.SDPA_ERR_SHAPE),
-    (dict(d_k=128, d_v=128), _lib.SDPA_ERR_UNSUPPORTED),
+    (dict(d_k=128, d_v=128, dtype=0), _lib.SDPA_ERR_UNSUPPORTED),
+    (dict(d_k=128, d_v=32), _lib.SDPA_ERR_UNSUPPORTED),
     (dict(dtype=3), _lib.SDPA_ERR_DTYPE),
     (dict(scale=math.inf), _lib.SDPA_ERR_SCALE),
     (dict(out=P), _lib.SDPA_ERR_ALIAS),

@@ -1,0 +1,110 @@
+"""Head widths 32 and 128 (bf16) on the GPU against the fp64 oracle.
+
+The pages' model variants use 16 heads of 32 and 4 heads of 128 beside the
+base model's 8 heads of 64, and d_model = 256 / 1024 with 32- / 128-wide heads
+(《精读 Attention Is All You Need：原始 Transformer 论文》 Table 3, rows (A)
+and (C)).  Eq. (1) is the same at every width; the oracle takes any width.
+Bar: the bf16 one, 2e-2 absolute; the log-sum-exp within 2^-8 (this kernel
+sums fp32 weights, so it is far tighter in practice).
+"""
+
+import numpy as np
+import pytest
+
+import oracle.sdpa_backward as sb
+import oracle.sdpa_oracle as so
+from sdpa_inputs import random_case
+from tests.gpu_cases import TOL, from_device, max_abs_err, run_gpu, to_device
+
+pytestmark = pytest.mark.gpu
+
+CASES = [  # id, (B, h, n, m, d), options
+    ("A_h16_d32_encoder", (64, 16, 64, 64, 32), dict(key_lens=(8, 64))),
+    ("A_h4_d128_encoder", (64, 4, 64, 64, 128), dict(key_lens=(8, 64))),
+    ("C_dmodel256_d32_decoder", (16, 8, 64, 64, 32), dict(causal=True, key_lens=(8, 64))),
+    ("C_dmodel1024_d128_cross", (8, 8, 48, 64, 128), dict(key_lens=(16, 64))),
+    ("d32_ragged_tiles", (2, 2, 100, 130, 32), dict(key_lens=(1, 130))),
+    ("d128_multi_tile_causal", (2, 2, 300, 300, 128), dict(causal=True)),
+    ("d32_window", (2, 2, 300, 300, 32), dict(window=(40, 8))),
+    ("d128_bottom_right", (4, 2, 5, 200, 128), dict(window=(None, 0, "bottom_right"), key_lens=(0, 200))),
+    ("d32_four_wave_blocks", (8, 16, 1024, 1024, 32), dict(causal=True)),
+    ("d128_four_wave_blocks", (8, 16, 1024, 1024, 128), dict(causal=True)),
+]
+
+
+def _case(i, shape, opts):
+    B, h, n, m, d = shape
+    rng = np.random.default_rng(8000 + i)
+    opts = dict(opts)
+    if isinstance(opts.get("key_lens"), tuple):
+        lo, hi = opts["key_lens"]
+        opts["key_lens"] = rng.integers(lo, hi, size=B, endpoint=True).astype(np.int32)
+    return random_case(rng, B, h, n, m, d, d, dtype="bf16", **opts)
+
+
+@pytest.mark.parametrize("i", range(len(CASES)), ids=[c[0] for c in CASES])
+def test_width_parity(gpu_lib, i):
+    name, shape, opts = CASES[i]
+    c = _case(i, shape, opts)
+    _, got = run_gpu(c)
+    B, h, n, m, d = shape
+    if B * h * n * m > 1 << 26:  # large: sampled rows (each costs one row of the head)
+        rng = np.random.default_rng(9)
+        picks = [(int(rng.integers(B)), int(rng.integers(h)), int(q)) for q in rng.integers(0, n, 64)]
+        picks += [(0, 0, 0), (B - 1, h - 1, n - 1), (1, 3, 127), (1, 3, 128)]
+        ref = so.attention_rows(c["q"], c["k"], c["v"], picks, causal=c["causal"], key_lens=c["key_lens"],
+                                window=c["window"])
+        got = np.stack([got[b, hh, q] for b, hh, q in picks])
+    else:
+        ref = so.attention(c["q"], c["k"], c["v"], causal=c["causal"], key_lens=c["key_lens"],
+                           window=c["window"])
+    err = max_abs_err(got, ref)
+    print(f"width {name}: max abs err {err:.2e}")
+    assert err <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("i", [0, 1, 5, 7], ids=[CASES[i][0] for i in (0, 1, 5, 7)])
+def test_width_lse(gpu_lib, i):
+    import torch
+
+    from transformer_attention_sdpa_amd import forward
+
+    name, shape, opts = CASES[i]
+    c = _case(i, shape, opts)
+    q, k, v = (to_device(c[x], "bf16") for x in ("q", "k", "v"))
+    kl = None if c["key_lens"] is None else torch.from_numpy(c["key_lens"]).cuda()
+    out, lse = forward(q, k, v, causal=c["causal"], key_lens=kl, window=c["window"], return_lse=True)
+    o2 = forward(q, k, v, causal=c["causal"], key_lens=kl, window=c["window"])
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), o2.view(torch.int16))
+    got = lse.cpu().numpy().astype(np.float64)
+    ref = sb.log_sum_exp(c["q"], c["k"], causal=c["causal"], key_lens=c["key_lens"], window=c["window"])
+    inf = np.isinf(ref)
+    assert np.array_equal(np.isinf(got), inf) and np.all(got[inf] == ref[inf])
+    err = max_abs_err(got[~inf], ref[~inf])
+    print(f"width lse {name}: max abs err {err:.2e}")
+    assert err <= 2.0 ** -8
+
+
+def test_width_deterministic_and_ignores_padded_rows(gpu_lib):
+    c = _case(0, (4, 2, 100, 150, 128), dict(key_lens=np.array([150, 37, 0, 99], np.int32)))
+    _, a = run_gpu(c)
+    for b, L in enumerate(c["key_lens"]):
+        c["k"][b, :, L:] = np.nan
+        c["v"][b, :, L:] = np.nan
+    _, b2 = run_gpu(c)
+    assert np.array_equal(a, b2)
+    assert np.all(a[2] == 0)  # no legal key: zero rows
+
+
+def test_width_backward_is_rejected(gpu_lib):
+    """The backward pass is 64-wide only: other widths get a clear error."""
+    import torch
+
+    from transformer_attention_sdpa_amd import backward, forward
+
+    c = _case(1, (1, 1, 8, 8, 32), {})
+    q, k, v = (to_device(c[x], "bf16") for x in ("q", "k", "v"))
+    out, lse = forward(q, k, v, return_lse=True)
+    with pytest.raises(RuntimeError, match="unsupported"):
+        backward(q, k, v, out, torch.zeros_like(out), lse)

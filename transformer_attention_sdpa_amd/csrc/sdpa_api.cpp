@@ -36,7 +36,9 @@ int validate(const void* q, const void* k, const void* v, void* out, int32_t B, 
     const uint64_t width = (uint64_t)(d_k > d_v ? d_k : d_v);
     if (heads * rows * width >= (1ull << 48)) return SDPA_ERR_SHAPE;
     if (heads * (((uint64_t)n + 31) / 32) >= (1ull << 31)) return SDPA_ERR_SHAPE;
-    if (d_k != sdpa::kHeadDim || d_v != sdpa::kHeadDim) return SDPA_ERR_UNSUPPORTED;
+    // Head widths: 64 for both dtypes; 32 and 128 (d_k = d_v) for bf16.
+    const bool wide_ok = dtype == SDPA_BF16 && d_k == d_v && (d_k == 32 || d_k == 128);
+    if (!(d_k == sdpa::kHeadDim && d_v == sdpa::kHeadDim) && !wide_ok) return SDPA_ERR_UNSUPPORTED;
     if (!std::isfinite(scale) || !(scale > 0.f)) return SDPA_ERR_SCALE;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return SDPA_ERR_ALIGN;
     if (key_lens && (reinterpret_cast<uintptr_t>(key_lens) & 3u)) return SDPA_ERR_ALIGN;
@@ -66,8 +68,9 @@ extern "C" int sdpa_forward(const void* q, const void* k, const void* v, void* o
     if (mask_kind != SDPA_MASK_NONE && mask_kind != SDPA_MASK_CAUSAL) return SDPA_ERR_MASK;
     if (mask_kind == SDPA_MASK_CAUSAL && n != m) return SDPA_ERR_MASK;
     // causal = the window (unbounded, 0) at top-left alignment
-    const sdpa::Args a{q, k, v, out, B, h, n, m, scale, -1, mask_kind == SDPA_MASK_CAUSAL ? 0 : -1,
-                       0, key_lens};
+    sdpa::Args a{q, k, v, out, B, h, n, m, scale, -1, mask_kind == SDPA_MASK_CAUSAL ? 0 : -1,
+                 0, key_lens};
+    a.d = d_k;
     return launch(a, dtype, stream);
 }
 
@@ -84,8 +87,9 @@ extern "C" int sdpa_forward_window(const void* q, const void* k, const void* v, 
     const int64_t reach = (int64_t)n + m;
     const int32_t wl = window_left > reach ? -1 : window_left;
     const int32_t wr = window_right > reach ? -1 : window_right;
-    const sdpa::Args a{q, k, v, out, B, h, n, m, scale, wl, wr,
-                       align == SDPA_ALIGN_BOTTOM_RIGHT ? 1 : 0, key_lens};
+    sdpa::Args a{q, k, v, out, B, h, n, m, scale, wl, wr,
+                 align == SDPA_ALIGN_BOTTOM_RIGHT ? 1 : 0, key_lens};
+    a.d = d_k;
     return launch(a, dtype, stream);
 }
 
@@ -123,6 +127,7 @@ extern "C" int sdpa_forward_lse(const void* q, const void* k, const void* v, voi
         if (b.p && overlap(lse, lb, b.p, b.n)) return SDPA_ERR_ALIAS;
     sdpa::Args a{q, k, v, out, B, h, n, m, scale, wl, wr, br, key_lens};
     a.lse = lse;
+    a.d = d_k;
     return launch(a, dtype, stream);
 }
 
@@ -142,7 +147,7 @@ extern "C" int sdpa_backward(const void* q, const void* k, const void* v, const 
     // checks below cover the outputs).
     int st = validate(q, k, v, const_cast<void*>(out), B, h, n, m, d_k, d_v, scale, key_lens, dtype);
     if (st != SDPA_OK) return st;
-    if (dtype != SDPA_BF16) return SDPA_ERR_UNSUPPORTED;
+    if (dtype != SDPA_BF16 || d_k != sdpa::kHeadDim) return SDPA_ERR_UNSUPPORTED;
     for (const void* p : {dout, (const void*)dq, (const void*)dk, (const void*)dv, (const void*)workspace})
         if (!aligned16(p)) return SDPA_ERR_ALIGN;
     if (reinterpret_cast<uintptr_t>(lse) & 3u) return SDPA_ERR_ALIGN;
@@ -225,7 +230,9 @@ extern "C" const char* sdpa_strerror(int status) {
         case SDPA_OK: return "ok";
         case SDPA_ERR_NULL: return "a required pointer is NULL";
         case SDPA_ERR_SHAPE: return "bad shape: a dimension is < 1 or an element count overflows";
-        case SDPA_ERR_UNSUPPORTED: return "unsupported head width: the library supports d_k = d_v = 64";
+        case SDPA_ERR_UNSUPPORTED:
+            return "unsupported: head widths are d_k = d_v = 64 (32 and 128 in bf16 attention); "
+                   "the log-sum-exp, backward pass and sublayer are bf16, d = 64 (backward, sublayer)";
         case SDPA_ERR_ALIGN: return "a device pointer is not 16-byte aligned (key_lens: 4-byte)";
         case SDPA_ERR_MASK:
             return "bad mask: unknown mask_kind, causal with n != m, window side < -1 or unknown align";

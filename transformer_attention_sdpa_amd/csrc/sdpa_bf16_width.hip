@@ -1,0 +1,296 @@
+// Eq. (1) in bf16 for head widths other than 64: d_k = d_v = D ∈ {32, 128}.
+//
+// The pages' model variants change the head width at a constant cost per
+// layer (《精读 Attention Is All You Need：原始 Transformer 论文》 Table 3, rows
+// (A) and (C): h = 16 heads of 32 and h = 4 heads of 128 next to the base
+// model's 8 heads of 64; d_model = 256 with 32-wide heads, d_model = 1024 with
+// 128-wide ones).  The 64-wide kernels are tuned to their one width; this one
+// is written once for any width that is a multiple of 32, with the same
+// transposed products:
+//
+//   Sᵀ (64 keys × 32 queries)  = K · Qᵀ      A = K rows from LDS, B = Qᵀ in VGPRs
+//   Oᵀ (D × 32 queries)       += Vᵀ · Pᵀ    A = Vᵀ via LDS transpose reads,
+//                                           B = Pᵀ from the Sᵀ registers
+//
+// on v_mfma_f32_32x32x16_bf16, one 32-query block per wave, 64-key tiles
+// double-buffered in LDS by buffer_load … lds, and an exact online softmax
+// (the tile maximum moves the reference every tile).  Key windows, key
+// lengths and the log-sum-exp output behave exactly as in the 64-wide kernels.
+#include "sdpa_common.hpp"
+
+namespace sdpa {
+namespace {
+
+constexpr int BT = 64;  // keys per LDS tile
+
+// 16-byte chunk position of chunk c of row r in a tile with D/8 chunks per
+// row, XOR-swizzled so that 16 consecutive rows read at one chunk (one
+// 16-byte MFMA operand per lane) fall on distinct banks of gfx950's 256-byte
+// LDS pass: 64-byte rows (D = 32) share a pass four at a time, 256-byte rows
+// (D = 128) fill it alone.
+template <int D>
+__device__ __forceinline__ int wswz(int r, int c) {
+    if constexpr (D == 32) return r * 4 + (c ^ ((r >> 2) & 3));
+    else if constexpr (D == 128) return r * 16 + (c ^ (r & 15));
+    else return lds_swz(r, c);
+}
+
+__device__ __forceinline__ u32x4 wds_read_b128(uint32_t a) {
+    u32x4 r;
+    asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(a));
+    return r;
+}
+__device__ __forceinline__ u32x2 wds_read_tr(uint32_t a) {
+    u32x2 r;
+    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(a));
+    return r;
+}
+template <int N>
+__device__ __forceinline__ void wlds_wait(u32x4 (&x)[N]) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < N; ++i) asm volatile("" : "+v"(x[i]));
+}
+template <int N>
+__device__ __forceinline__ void wlds_wait(u32x2 (&x)[N]) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < N; ++i) asm volatile("" : "+v"(x[i]));
+}
+
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) void sdpa_fwd_bf16_width(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    uint16_t* __restrict__ O, float* __restrict__ lse, int BH, int H, int n, int m, float c_log2, int wl,
+    int wr, int bottom_right, const int32_t* __restrict__ key_lens, int nqb) {
+    constexpr int KS = D / 16;                // k-steps of the score product
+    constexpr int DT = D / 32;                // 32-row blocks of Oᵀ
+    constexpr int CPR = D / 8;                // 16-byte chunks per row
+    constexpr int TILE = BT * D * 2;          // bytes per tile
+    constexpr int LOADS = TILE / 1024 / NW;   // 1 KiB loads per wave per tensor per tile
+    constexpr int ROWS_PER_LOAD = 1024 / (D * 2);
+    static_assert(D % 32 == 0 && LOADS >= 1, "width");
+    __shared__ __attribute__((aligned(1024))) char lds[2 * 2 * TILE];  // [buf][K | V]
+
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, l32 = lane & 31, hf = lane >> 5, gi = lane & 15;
+
+    // Latest query blocks first (they see the most keys under a causal mask).
+    const int g = blockIdx.x;
+    const int bh = g % BH;
+    const int q0 = (nqb - 1 - g / BH) * 32 * NW;
+    const int b = bh / H;
+    int L = m;
+    if (key_lens) {
+        const int t = key_lens[b];
+        L = t < 0 ? 0 : (t > m ? m : t);
+    }
+    const KeyWindow win{wl, wr, bottom_right ? L - n : 0, L};
+    const int qlast = min(q0 + 32 * NW, n) - 1;
+    const int kbeg = win.lo(q0), kend = win.hi(qlast);
+    const int tbeg = kbeg / BT;
+    const int tend = kend > kbeg ? (kend + BT - 1) / BT : tbeg;
+    const int wq0 = q0 + 32 * w;
+    const int wlast = min(wq0 + 32, n) - 1;
+    const bool wact = wlast >= wq0;
+    const int wlo = wact ? win.lo(wq0) : 0, whi = wact ? win.hi(wlast) : 0;
+    const int flo = wact ? win.lo(wlast) : 0, fhi = wact ? win.hi(wq0) : 0;
+
+    const size_t qbase = (size_t)bh * n * D, kvbase = (size_t)bh * m * D;
+    const int qrow = wq0 + l32;
+    const bool qok = qrow < n;
+    // Qᵀ as the B operand: dims 16·ks + 8·hf + [0..7] of this lane's query.
+    bf16x8 qop[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+        qop[ks] = qok ? __builtin_bit_cast(bf16x8, reinterpret_cast<const u32x4*>(Q + qbase + (size_t)qrow * D)[2 * ks + hf])
+                      : __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+
+    // Per-lane LDS offsets: the K operand of k-step ks (row l32, chunk 2·ks + hf)
+    // and the Vᵀ transpose reads (rows 4·hf + gi/4, + 8; k-step j adds 16·j rows,
+    // which leaves the swizzle of these rows unchanged for every D here).
+    int kaddr[KS], vaddr[DT][2];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kaddr[ks] = wswz<D>(l32, 2 * ks + hf) * 16;
+    {
+        const int r0 = 4 * hf + (gi >> 2);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            const int c0 = 32 * dt + 16 * ((lane >> 4) & 1) + 4 * (gi & 3);
+            vaddr[dt][0] = wswz<D>(r0, c0 >> 3) * 16 + (c0 & 7) * 2;
+            vaddr[dt][1] = wswz<D>(r0 + 8, c0 >> 3) * 16 + (c0 & 7) * 2;
+        }
+    }
+    // Tile loads: wave w's u-th 1 KiB load fills rows ROWS_PER_LOAD·(w·LOADS + u) + lane/CPR.
+    int ld_off[LOADS], ld_lds[LOADS];
+#pragma unroll
+    for (int u = 0; u < LOADS; ++u) {
+        const int blk = w * LOADS + u;
+        const int row = ROWS_PER_LOAD * blk + lane / CPR;
+        const int pos = lane % CPR;
+        // the chunk whose swizzled position is pos (XOR is its own inverse)
+        const int chunk = wswz<D>(row, pos) - row * CPR;
+        ld_off[u] = row * D * 2 + chunk * 16;
+        ld_lds[u] = blk * 1024;
+    }
+    auto issue = [&](int t, int buf) {
+        const int left = (L - t * BT) * D * 2;
+        const i32x4 rk = make_rsrc(K + kvbase + (size_t)t * BT * D, (uint32_t)left);
+        const i32x4 rv = make_rsrc(V + kvbase + (size_t)t * BT * D, (uint32_t)left);
+#pragma unroll
+        for (int u = 0; u < LOADS; ++u) {
+            load16_to_lds(rk, lds + buf * 2 * TILE + ld_lds[u], ld_off[u]);
+            load16_to_lds(rv, lds + buf * 2 * TILE + TILE + ld_lds[u], ld_off[u]);
+        }
+    };
+
+    const uint32_t l0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds;
+    f32x16 oacc[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[dt][i] = 0.f;
+    float mref = -INFINITY, lsum = 0.f;
+
+    if (tend > tbeg) issue(tbeg, 0);
+    wait_vmem();
+    __syncthreads();
+    for (int t = tbeg; t < tend; ++t) {
+        const int buf = (t - tbeg) & 1;
+        if (t + 1 < tend) issue(t + 1, buf ^ 1);
+        const int k0 = t * BT;
+        if (k0 < whi && k0 + BT > wlo) {  // uniform: some query of the wave sees the tile
+            const uint32_t sk = l0 + buf * 2 * TILE, sv = sk + TILE;
+            f32x16 s[2];
+            {
+                u32x4 a[2 * KS];
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) a[kt * KS + ks] = wds_read_b128(sk + kaddr[ks] + kt * 32 * D * 2);
+                wlds_wait(a);
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) s[kt][i] = 0.f;
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks)
+                        s[kt] = mfma32x32x16_bf16(__builtin_bit_cast(bf16x8, a[kt * KS + ks]), qop[ks], s[kt]);
+                }
+            }
+            // Register i of s[kt] is key k0 + 32·kt + 8·(i/4) + 4·hf + i%4.
+            if (k0 < flo || k0 + BT > fhi) {
+                const int llo = win.lo(qrow) - k0 - 4 * hf, lhi = win.hi(qrow) - k0 - 4 * hf;
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int off = 32 * kt + 8 * (i >> 2) + (i & 3);
+                        s[kt][i] = (off >= llo && off < lhi) ? s[kt][i] : -INFINITY;
+                    }
+            }
+            // Exact online softmax: move the reference to the running maximum.
+            float x = s[0][0];
+#pragma unroll
+            for (int i = 1; i < 16; ++i) x = fmaxf(x, s[0][i]);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) x = fmaxf(x, s[1][i]);
+            const float mnew = fmaxf(mref, half_swap_max(x));
+            // mref = −∞: nothing accumulated yet (alpha multiplies zeros);
+            // mnew = −∞: no legal key so far, keep alpha = 1.
+            const float alpha = mnew == -INFINITY ? 1.f : exp2_hw((mref - mnew) * c_log2);
+            mref = mnew;
+            const float mc = (mnew == -INFINITY ? 0.f : mnew) * c_log2;
+            lsum *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
+            bf16x8 pb[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int kt = j >> 1, vb = 8 * (j & 1);
+                float p[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    p[e] = exp2_hw(__builtin_fmaf(s[kt][vb + e], c_log2, -mc));
+                    lsum += p[e];
+                }
+                pb[j] = to_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
+            }
+            // Oᵀ += Vᵀ · Pᵀ.
+            u32x2 va[4 * DT * 2];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) {
+                    va[(j * DT + dt) * 2] = wds_read_tr(sv + vaddr[dt][0] + j * 16 * D * 2);
+                    va[(j * DT + dt) * 2 + 1] = wds_read_tr(sv + vaddr[dt][1] + j * 16 * D * 2);
+                }
+            wlds_wait(va);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) {
+                    const u32x2 lo = va[(j * DT + dt) * 2], hi = va[(j * DT + dt) * 2 + 1];
+                    const u32x4 v4 = {lo[0], lo[1], hi[0], hi[1]};
+                    oacc[dt] = mfma32x32x16_bf16(__builtin_bit_cast(bf16x8, v4), pb[j], oacc[dt]);
+                }
+        }
+        wait_vmem();
+        __syncthreads();
+    }
+
+    // Oᵀ / l and store: register i of oacc[dt] is dim 32·dt + 8·(i/4) + 4·hf + i%4.
+    const float ltot = half_swap_sum(lsum);
+    // no legal key ⇒ zero row; a NaN sum (NaN legal inputs) stays NaN
+    const float inv = ltot != 0.f ? 1.f / ltot : 0.f;
+    if (qok) {
+        if (lse && hf == 0) {
+            const float mc = (mref == -INFINITY ? 0.f : mref) * c_log2;
+            lse[(size_t)bh * n + qrow] = (mc + log2f(ltot)) * 0.6931471805599453f;
+        }
+        uint16_t* dst = O + qbase + (size_t)qrow * D;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+                bf16x4 o;
+                o[0] = (__bf16)(oacc[dt][4 * i4 + 0] * inv);
+                o[1] = (__bf16)(oacc[dt][4 * i4 + 1] * inv);
+                o[2] = (__bf16)(oacc[dt][4 * i4 + 2] * inv);
+                o[3] = (__bf16)(oacc[dt][4 * i4 + 3] * inv);
+                *reinterpret_cast<bf16x4*>(dst + 32 * dt + 8 * i4 + 4 * hf) = o;
+            }
+    }
+}
+
+template <int D>
+hipError_t launch_width(const Args& a, hipStream_t stream) {
+    const int BH = a.B * a.H;
+    const float c_log2 = (float)((double)a.scale * 1.4426950408889634);  // scale·log2(e)
+    // 4 waves (128 queries) per workgroup once there are enough blocks.
+    if ((long long)BH * ((a.n + 127) / 128) >= 1024) {
+        const int nqb = (a.n + 127) / 128;
+        hipLaunchKernelGGL((sdpa_fwd_bf16_width<D, 4>), dim3(nqb * BH), dim3(256), 0, stream,
+                           (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.out,
+                           a.lse, BH, a.H, a.n, a.m, c_log2, a.wl, a.wr, a.bottom_right, a.key_lens, nqb);
+    } else {
+        const int nqb = (a.n + 63) / 64;
+        hipLaunchKernelGGL((sdpa_fwd_bf16_width<D, 2>), dim3(nqb * BH), dim3(128), 0, stream,
+                           (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.out,
+                           a.lse, BH, a.H, a.n, a.m, c_log2, a.wl, a.wr, a.bottom_right, a.key_lens, nqb);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bf16_width(const Args& a, hipStream_t stream) {
+    if (a.d == 32) return launch_width<32>(a, stream);
+    if (a.d == 128) return launch_width<128>(a, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace sdpa

@@ -38,6 +38,8 @@ struct Args {
     // Optional: per query row, ln Σ_j exp(scale · q·k_j) over the legal keys
     // (−∞ for a row with none), fp32 [B, H, n]; bf16 kernels only.
     float* lse = nullptr;
+    // Head width d_k = d_v: 64 (every kernel), or 32 / 128 (bf16, sdpa_bf16_width.hip).
+    int d = kHeadDim;
 };
 
 // Legal key range [lo, hi) of query row i under the window of one batch
@@ -104,7 +106,8 @@ size_t bwd_workspace_bytes(int B, int H, int n);
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_mha_bf16(const MhaArgs& a, hipStream_t stream);
 
-hipError_t launch_bf16(const Args& a, hipStream_t stream);        // picks one of the three below
+hipError_t launch_bf16(const Args& a, hipStream_t stream);        // picks one of the four below
+hipError_t launch_bf16_width(const Args& a, hipStream_t stream);  // d = 32 or 128
 hipError_t launch_bf16_long(const Args& a, hipStream_t stream);   // any n, m
 hipError_t launch_bf16_short(const Args& a, hipStream_t stream);  // n, m <= 64
 bool short_bf16_fits(const Args& a);
