@@ -79,6 +79,18 @@ WORKLOADS = {
         key_len_range=None, seed=1006, dtypes=("bf16",), window=(256, 256, "top_left"),
         what="long-sequence restricted self-attention, 8192 tokens, window of 256 keys "
              "either side of each query, no padding"),
+    # The model variants' head widths at the base model's cost per layer
+    # (h·d = 512; 《精读 …》 Table 3 row (A)): encoder batch as above.
+    "encoder_h16_d32": Workload(
+        "encoder_h16_d32", B=64, h=16, n=64, m=64, d_k=32, d_v=32, causal=False,
+        key_len_range=(8, 64), seed=1009),
+    "encoder_h4_d128": Workload(
+        "encoder_h4_d128", B=64, h=4, n=64, m=64, d_k=128, d_v=128, causal=False,
+        key_len_range=(8, 64), seed=1010),
+    # The 8k causal shape with 128-wide heads (same FLOPs as long_causal_8k).
+    "long_causal_8k_d128": Workload(
+        "long_causal_8k_d128", B=4, h=8, n=8192, m=8192, d_k=128, d_v=128, causal=True,
+        key_len_range=None, seed=1011),
     # One autoregressive decoder step (《注意力就是你所需要的一切》 §3.1: the
     # decoder consumes its previously generated symbols; §6.1: beam search
     # with beam size 4): one new query per sequence against its cached keys,

@@ -303,9 +303,13 @@ def test_wrapper_errors(gpu_lib):
     k = torch.zeros(1, 1, 5, 64, device="cuda", dtype=torch.bfloat16)
     with pytest.raises(RuntimeError, match="causal"):
         forward(q, k, k, causal=True)
-    q32 = torch.zeros(1, 1, 4, 32, device="cuda", dtype=torch.bfloat16)
+    # widths: 64 everywhere, 32 and 128 in bf16 only, nothing else
+    q16 = torch.zeros(1, 1, 4, 16, device="cuda", dtype=torch.bfloat16)
     with pytest.raises(RuntimeError, match="64"):
-        forward(q32, q32, q32)
+        forward(q16, q16, q16)
+    q32f = torch.zeros(1, 1, 4, 32, device="cuda", dtype=torch.float32)
+    with pytest.raises(RuntimeError, match="unsupported"):
+        forward(q32f, q32f, q32f)
 
 
 def test_concurrent_calls_on_separate_streams(gpu_lib):
