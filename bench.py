@@ -103,7 +103,7 @@ def measured_traffic(workload, dtype):
     return t.get("bytes_per_launch")
 
 
-def time_workload(name, dtype, steps, warmup, clock_warm_s=0.0, case=None):
+def time_workload(name, dtype, steps, warmup, clock_warm_s=0.0, case=None, split=False):
     import torch
 
     from transformer_attention_sdpa_amd import _lib
@@ -142,6 +142,12 @@ def time_workload(name, dtype, steps, warmup, clock_warm_s=0.0, case=None):
     scale = 1.0 / math.sqrt(wl.d_k)
     mask = _lib.SDPA_MASK_CAUSAL if wl.causal else _lib.SDPA_MASK_NONE
     ptrs = [(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr()) for (q, k, v, o) in sets]
+    ws = None
+    if split:  # sdpa_forward_ex with its workspace (decoder steps split per 1024 keys)
+        need = _lib.sdpa_forward_workspace_bytes(wl.B, wl.h, wl.n, wl.m, wl.d_k, wl.d_v, code)
+        if need == 0:
+            raise ValueError(f"{name}: the split path does not apply")
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
     if wl.window is not None:
         wleft = -1 if wl.window[0] is None else wl.window[0]
         wright = -1 if wl.window[1] is None else wl.window[1]
@@ -150,7 +156,14 @@ def time_workload(name, dtype, steps, warmup, clock_warm_s=0.0, case=None):
 
     def launch(i, stream):
         p = ptrs[i % nsets]
-        if wl.window is None:
+        if ws is not None:
+            wlft = -1 if wl.window is None else wleft
+            wrgt = (0 if wl.causal else -1) if wl.window is None else wright
+            wal = _lib.SDPA_ALIGN_TOP_LEFT if wl.window is None else walign
+            rc = _lib.sdpa_forward_ex(p[0], p[1], p[2], p[3], None, wl.B, wl.h, wl.n, wl.m, wl.d_k,
+                                      wl.d_v, scale, wlft, wrgt, wal, kl_ptr, code, ws.data_ptr(),
+                                      ws.numel(), stream)
+        elif wl.window is None:
             rc = _lib.sdpa_forward(p[0], p[1], p[2], p[3], wl.B, wl.h, wl.n, wl.m, wl.d_k, wl.d_v,
                                    scale, mask, kl_ptr, code, stream)
         else:
@@ -659,6 +672,8 @@ def main():
     ap.add_argument("--workload", default=HEADLINE[0], choices=sorted(WORKLOADS))
     ap.add_argument("--dtype", default=HEADLINE[1], choices=["bf16", "f32"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--split", action="store_true",
+                    help="with --workload: time sdpa_forward_ex with its workspace (split decoder steps)")
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="time a plain device copy instead (reference for HBM counters)")
@@ -709,7 +724,7 @@ def main():
         return
 
     wl = WORKLOADS[args.workload]
-    head = time_workload(args.workload, args.dtype, args.steps, args.warmup)
+    head = time_workload(args.workload, args.dtype, args.steps, args.warmup, split=args.split)
     extra = {}
     if not args.no_extra:
         # Every GPU measurement first, then the CPU oracle passes.  Each extra
@@ -730,6 +745,12 @@ def main():
                 "sets_rotated", "ms_per_step_eager")}
             if args.no_cpu_baseline:
                 del cases[name, dt]
+        # decoder steps split over 1024-key pieces (sdpa_forward_ex with a workspace)
+        r = time_workload("decode_long_cache", "bf16", 20, min(args.warmup, 5), clock_warm_s=0.1,
+                          split=True)
+        extra["decode_long_cache-bf16-split"] = {k: r[k] for k in (
+            "ms_per_step", "tflops", "gbs", "frac_mfma_peak", "frac_hbm_peak", "steps", "sets_rotated",
+            "ms_per_step_eager")}
         for name in ("encoder_self_base", "long_causal_8k"):
             extra[f"backward-{name}-bf16"] = time_backward(
                 name, 20 if name.endswith("_8k") else max(10, min(args.steps, 200)), min(args.warmup, 3))

@@ -190,6 +190,34 @@ SDPA_API int sdpa_forward_lse(const void* q, const void* k, const void* v, void*
                               int32_t align, const int32_t* key_lens, int32_t dtype, void* stream);
 
 /*
+ * sdpa_forward_ex — sdpa_forward_window with an optional log-sum-exp output
+ * and an optional workspace.
+ *
+ * lse        NULL, or as in sdpa_forward_lse (bf16 only).
+ * workspace  NULL, or device scratch of workspace_bytes >= the size
+ *            sdpa_forward_workspace_bytes gives, 16-byte aligned, owned by the
+ *            caller, overlapping no other argument.  With it, decoder steps
+ *            against long key caches (bf16, d = 64, n <= 16, m > 1024,
+ *            B·h >= 256) split each head's keys into 1024-key pieces on
+ *            separate workgroups and merge the partial softmaxes in a second
+ *            launch, which keeps the CUs busy when cache lengths differ.  The
+ *            output then differs from the workspace-free call by rounding only
+ *            (the fp32 partial sums are added in another order); each path is
+ *            deterministic.  A workspace smaller than needed: SDPA_ERR_WORKSPACE.
+ * Everything else as in sdpa_forward_window.
+ *
+ * sdpa_forward_workspace_bytes returns the workspace such a call would use,
+ * and 0 when it would use none (then any workspace argument is ignored).
+ */
+SDPA_API size_t sdpa_forward_workspace_bytes(int32_t B, int32_t h, int32_t n, int32_t m, int32_t d_k,
+                                             int32_t d_v, int32_t dtype);
+SDPA_API int sdpa_forward_ex(const void* q, const void* k, const void* v, void* out, float* lse,
+                             int32_t B, int32_t h, int32_t n, int32_t m, int32_t d_k, int32_t d_v,
+                             float scale, int32_t window_left, int32_t window_right, int32_t align,
+                             const int32_t* key_lens, int32_t dtype, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/*
  * sdpa_backward — the gradient of Eq. (1) (bf16).  The pages train the model
  * through attention but print only the forward pass; by the chain rule, for
  * any loss with output gradient dO:

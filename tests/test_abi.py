@@ -30,7 +30,8 @@ def test_every_declared_entry_point_is_exported(lib):
     names = re.findall(r"SDPA_API\s+[\w\s\*]+?\b(sdpa_\w+)\s*\(", _header())
     assert set(names) == {"sdpa_forward", "sdpa_forward_window", "sdpa_mha_forward",
                           "sdpa_mha_workspace_bytes", "sdpa_forward_lse", "sdpa_backward",
-                          "sdpa_backward_workspace_bytes", "sdpa_strerror", "sdpa_version"}
+                          "sdpa_backward_workspace_bytes", "sdpa_forward_ex",
+                          "sdpa_forward_workspace_bytes", "sdpa_strerror", "sdpa_version"}
     for name in names:
         assert isinstance(getattr(lib, name), ctypes._CFuncPtr)
 
@@ -188,6 +189,49 @@ def call_lse(**kw):
 ])
 def test_forward_lse_validation_rejects_before_any_hip_call(kw, code, lib):
     assert call_lse(**kw) == code
+
+
+def test_forward_workspace_size(lib):
+    # only decoder steps against caches past 1024 keys, with >= 256 heads, use one:
+    # ceil(m / 1024) splits × B·h heads × n queries × 68 floats
+    assert _lib.sdpa_forward_workspace_bytes(32, 8, 1, 8192, 64, 64, 1) == 8 * 256 * 1 * 68 * 4
+    assert _lib.sdpa_forward_workspace_bytes(32, 8, 4, 1025, 64, 64, 1) == 2 * 256 * 4 * 68 * 4
+    assert _lib.sdpa_forward_workspace_bytes(32, 8, 1, 1024, 64, 64, 1) == 0  # one split
+    assert _lib.sdpa_forward_workspace_bytes(16, 8, 1, 8192, 64, 64, 1) == 0  # 128 heads
+    assert _lib.sdpa_forward_workspace_bytes(32, 8, 17, 8192, 64, 64, 1) == 0  # n > 16
+    assert _lib.sdpa_forward_workspace_bytes(32, 8, 1, 8192, 64, 64, 0) == 0  # fp32
+    assert _lib.sdpa_forward_workspace_bytes(32, 8, 1, 8192, 128, 128, 1) == 0
+
+
+G = 1 << 32  # fake addresses far enough apart for the 134 MB K and V of this shape
+
+
+def call_ex(**kw):
+    a = dict(q=G, k=2 * G, v=3 * G, out=4 * G, lse=None, B=32, h=8, n=1, m=4096, d_k=64, d_v=64,
+             scale=0.125, wl=-1, wr=0, align=1, key_lens=None, dtype=1, ws=5 * G, ws_bytes=None)
+    a.update(kw)
+    if a["ws_bytes"] is None:
+        a["ws_bytes"] = _lib.sdpa_forward_workspace_bytes(a["B"], a["h"], a["n"], a["m"], a["d_k"],
+                                                          a["d_v"], a["dtype"])
+    return _lib.sdpa_forward_ex(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["h"], a["n"],
+                                a["m"], a["d_k"], a["d_v"], a["scale"], a["wl"], a["wr"], a["align"],
+                                a["key_lens"], a["dtype"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), _lib.SDPA_ERR_NULL),
+    (dict(ws_bytes=100), _lib.SDPA_ERR_WORKSPACE),
+    (dict(ws=5 * G + 8), _lib.SDPA_ERR_ALIGN),
+    (dict(ws=4 * G), _lib.SDPA_ERR_ALIAS),              # workspace on out
+    (dict(lse=6 * G, dtype=0), _lib.SDPA_ERR_UNSUPPORTED),
+    (dict(lse=6 * G + 1), _lib.SDPA_ERR_ALIGN),
+    (dict(lse=G), _lib.SDPA_ERR_ALIAS),
+    (dict(ws=6 * G, lse=6 * G + 64), _lib.SDPA_ERR_ALIAS),  # workspace on lse
+    (dict(wl=-4), _lib.SDPA_ERR_MASK),
+    (dict(scale=-1.0), _lib.SDPA_ERR_SCALE),
+])
+def test_forward_ex_validation_rejects_before_any_hip_call(kw, code, lib):
+    assert call_ex(**kw) == code
 
 
 def call_bwd(**kw):

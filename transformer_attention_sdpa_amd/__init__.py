@@ -13,11 +13,13 @@ import math
 
 from . import _lib
 from ._lib import (sdpa_backward, sdpa_backward_workspace_bytes, sdpa_forward,  # noqa: F401
-                   sdpa_forward_lse, sdpa_forward_window, sdpa_mha_forward,
+                   sdpa_forward_ex, sdpa_forward_lse, sdpa_forward_window,
+                   sdpa_forward_workspace_bytes, sdpa_mha_forward,
                    sdpa_mha_workspace_bytes, sdpa_strerror, sdpa_version)
 
 __all__ = ["forward", "backward", "mha_forward", "sdpa_forward", "sdpa_forward_window",
-           "sdpa_forward_lse", "sdpa_backward", "sdpa_backward_workspace_bytes",
+           "sdpa_forward_lse", "sdpa_forward_ex", "sdpa_forward_workspace_bytes",
+           "sdpa_backward", "sdpa_backward_workspace_bytes",
            "sdpa_mha_forward", "sdpa_mha_workspace_bytes", "sdpa_strerror", "sdpa_version"]
 
 
@@ -188,7 +190,7 @@ def backward(q, k, v, out, dout, lse, *, causal: bool = False, key_lens=None,
 
 
 def forward(q, k, v, *, causal: bool = False, key_lens=None, scale: float | None = None,
-            out=None, window=None, return_lse: bool = False):
+            out=None, window=None, return_lse: bool = False, workspace=None):
     """Attention over [B, h, n, d_k] queries and [B, h, m, d] keys/values.
 
     key_lens: None or an int32 tensor [B] on the same device (key j of batch
@@ -200,7 +202,10 @@ def forward(q, k, v, *, causal: bool = False, key_lens=None, scale: float | None
     ``sdpa_forward_window`` in include/sdpa.h.  Not combined with ``causal``.
     Returns ``out`` ([B, h, n, d_v], same dtype as q), or ``(out, lse)`` with
     ``return_lse`` (bf16 only): lse [B, h, n] float32, the natural log of each
-    row's softmax denominator, which ``backward`` takes.  Raises RuntimeError
+    row's softmax denominator, which ``backward`` takes.  ``workspace``: None,
+    or a uint8 GPU tensor of at least ``sdpa_forward_workspace_bytes(...)``
+    bytes, which lets decoder steps against long caches split each head's keys
+    over several workgroups (see ``sdpa_forward_ex``).  Raises RuntimeError
     with the library's message on a nonzero status.
     """
     import torch
@@ -219,8 +224,13 @@ def forward(q, k, v, *, causal: bool = False, key_lens=None, scale: float | None
     # The library launches on the calling thread's current HIP device.
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
-        if return_lse:
-            lse = torch.empty((B, h, n), dtype=torch.float32, device=q.device)
+        lse = torch.empty((B, h, n), dtype=torch.float32, device=q.device) if return_lse else None
+        if workspace is not None:
+            rc = sdpa_forward_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                 None if lse is None else lse.data_ptr(), B, h, n, m, d_k, d_v,
+                                 float(scale), wl, wr, al, kl_ptr, dt, workspace.data_ptr(),
+                                 workspace.numel() * workspace.element_size(), stream)
+        elif return_lse:
             rc = sdpa_forward_lse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                   lse.data_ptr(), B, h, n, m, d_k, d_v, float(scale), wl, wr, al,
                                   kl_ptr, dt, stream)

@@ -61,6 +61,11 @@ def load() -> ctypes.CDLL:
     lib.sdpa_forward_lse.argtypes = [vp, vp, vp, vp, fp, i32, i32, i32, i32, i32, i32,
                                      ctypes.c_float, i32, i32, i32, vp, i32, vp]
     lib.sdpa_forward_lse.restype = ctypes.c_int
+    lib.sdpa_forward_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+    lib.sdpa_forward_workspace_bytes.restype = ctypes.c_size_t
+    lib.sdpa_forward_ex.argtypes = [vp, vp, vp, vp, fp, i32, i32, i32, i32, i32, i32, ctypes.c_float,
+                                    i32, i32, i32, vp, i32, vp, ctypes.c_size_t, vp]
+    lib.sdpa_forward_ex.restype = ctypes.c_int
     lib.sdpa_backward_workspace_bytes.argtypes = [i32, i32, i32]
     lib.sdpa_backward_workspace_bytes.restype = ctypes.c_size_t
     lib.sdpa_backward.argtypes = [vp, vp, vp, vp, vp, fp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
@@ -107,6 +112,19 @@ def sdpa_forward_lse(q, k, v, out, lse, B, h, n, m, d_k, d_v, scale, window_left
     """Forward to the C entry point of the same name (forward pass + row log-sum-exp)."""
     return load().sdpa_forward_lse(q, k, v, out, lse, B, h, n, m, d_k, d_v, scale, window_left,
                                    window_right, align, key_lens, dtype, stream)
+
+
+def sdpa_forward_workspace_bytes(B, h, n, m, d_k, d_v, dtype) -> int:
+    """Forward to the C entry point of the same name."""
+    return load().sdpa_forward_workspace_bytes(B, h, n, m, d_k, d_v, dtype)
+
+
+def sdpa_forward_ex(q, k, v, out, lse, B, h, n, m, d_k, d_v, scale, window_left, window_right, align,
+                    key_lens, dtype, workspace, workspace_bytes, stream) -> int:
+    """Forward to the C entry point of the same name (optional lse and workspace)."""
+    return load().sdpa_forward_ex(q, k, v, out, lse, B, h, n, m, d_k, d_v, scale, window_left,
+                                  window_right, align, key_lens, dtype, workspace, workspace_bytes,
+                                  stream)
 
 
 def sdpa_backward_workspace_bytes(B, h, n) -> int:

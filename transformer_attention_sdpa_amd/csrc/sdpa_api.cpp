@@ -131,6 +131,61 @@ extern "C" int sdpa_forward_lse(const void* q, const void* k, const void* v, voi
     return launch(a, dtype, stream);
 }
 
+size_t forward_work_bytes(int32_t B, int32_t h, int32_t n, int32_t m, int32_t d_k, int32_t d_v,
+                          int32_t dtype) {
+    if (B < 1 || h < 1 || n < 1 || m < 1 || dtype != SDPA_BF16) return 0;
+    if (d_k != sdpa::kHeadDim || d_v != sdpa::kHeadDim) return 0;
+    sdpa::Args a{nullptr, nullptr, nullptr, nullptr, B, h, n, m, 1.f, -1, -1, 0, nullptr};
+    if (sdpa::short_bf16_fits(a) || !sdpa::decode_bf16_fits(a)) return 0;
+    return sdpa::decode_split_bytes(B, h, n, m);
+}
+
+extern "C" size_t sdpa_forward_workspace_bytes(int32_t B, int32_t h, int32_t n, int32_t m, int32_t d_k,
+                                               int32_t d_v, int32_t dtype) {
+    return forward_work_bytes(B, h, n, m, d_k, d_v, dtype);
+}
+
+extern "C" int sdpa_forward_ex(const void* q, const void* k, const void* v, void* out, float* lse,
+                               int32_t B, int32_t h, int32_t n, int32_t m, int32_t d_k, int32_t d_v,
+                               float scale, int32_t window_left, int32_t window_right, int32_t align,
+                               const int32_t* key_lens, int32_t dtype, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+    int st = validate(q, k, v, out, B, h, n, m, d_k, d_v, scale, key_lens, dtype);
+    if (st != SDPA_OK) return st;
+    int32_t wl, wr, br;
+    st = window_args(n, m, window_left, window_right, align, &wl, &wr, &br);
+    if (st != SDPA_OK) return st;
+    const uint64_t heads = (uint64_t)B * h;
+    struct Buf { const void* p; uint64_t n; };
+    const Buf ins[] = {{q, heads * n * d_k * (dtype == SDPA_F32 ? 4 : 2)},
+                       {k, heads * m * d_k * (dtype == SDPA_F32 ? 4 : 2)},
+                       {v, heads * m * d_v * (dtype == SDPA_F32 ? 4 : 2)},
+                       {out, heads * n * d_v * (dtype == SDPA_F32 ? 4 : 2)},
+                       {key_lens, key_lens ? (uint64_t)B * 4 : 0}};
+    if (lse) {
+        if (dtype != SDPA_BF16) return SDPA_ERR_UNSUPPORTED;
+        if (reinterpret_cast<uintptr_t>(lse) & 3u) return SDPA_ERR_ALIGN;
+        for (const Buf& b : ins)
+            if (b.p && overlap(lse, heads * n * 4, b.p, b.n)) return SDPA_ERR_ALIAS;
+    }
+    const size_t need = forward_work_bytes(B, h, n, m, d_k, d_v, dtype);
+    void* work = nullptr;
+    if (workspace && need > 0) {
+        if (!aligned16(workspace)) return SDPA_ERR_ALIGN;
+        if (workspace_bytes < need) return SDPA_ERR_WORKSPACE;
+        for (const Buf& b : ins)
+            if (b.p && overlap(workspace, need, b.p, b.n)) return SDPA_ERR_ALIAS;
+        if (lse && overlap(workspace, need, lse, heads * n * 4)) return SDPA_ERR_ALIAS;
+        work = workspace;
+    }
+    sdpa::Args a{q, k, v, out, B, h, n, m, scale, wl, wr, br, key_lens};
+    a.lse = lse;
+    a.d = d_k;
+    a.work = work;
+    a.work_bytes = work ? workspace_bytes : 0;
+    return launch(a, dtype, stream);
+}
+
 extern "C" size_t sdpa_backward_workspace_bytes(int32_t B, int32_t h, int32_t n) {
     if (B < 1 || h < 1 || n < 1) return 0;
     return sdpa::bwd_workspace_bytes(B, h, n);

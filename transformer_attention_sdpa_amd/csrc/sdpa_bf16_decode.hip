@@ -33,6 +33,7 @@ namespace {
 constexpr int D = kHeadDim;  // 64
 constexpr int QN = 16;       // query columns per head (n <= QN)
 constexpr int NWD = 4;       // waves per workgroup
+constexpr int PREC = 4 + 64; // floats per (split, head, query) record of the split mode
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -55,7 +56,8 @@ __global__ __launch_bounds__(NWD * 64) void sdpa_decode_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
     int H, int n, int m, float c_log2, int wl, int wr, int bottom_right,
-    const int32_t* __restrict__ key_lens, float* __restrict__ lse) {
+    const int32_t* __restrict__ key_lens, float* __restrict__ lse, int BH, int chunk,
+    float* __restrict__ part) {
     constexpr int NTL = KS / 16, NJ = KS / 32, NVL = KS / 8;
     constexpr int VBUF = KS * 128;  // one step of V rows in LDS
     // Per wave: two V step buffers; after the loop the first one holds the
@@ -69,7 +71,10 @@ __global__ __launch_bounds__(NWD * 64) void sdpa_decode_bf16(
     const int l16 = lane & 15;
     const int G = lane >> 4;
 
-    const int bh = blockIdx.x;
+    // Split mode (chunk > 0): workgroup g takes keys [sp·chunk, (sp+1)·chunk)
+    // of head g % BH and writes its unnormalised (max, sum, Oᵀ) to `part`.
+    const int bh = chunk > 0 ? (int)(blockIdx.x % BH) : (int)blockIdx.x;
+    const int sp = chunk > 0 ? (int)(blockIdx.x / BH) : 0;
     const int b = bh / H;
     const size_t qbase = (size_t)bh * n * D;
     const size_t kvbase = (size_t)bh * m * D;
@@ -81,7 +86,11 @@ __global__ __launch_bounds__(NWD * 64) void sdpa_decode_bf16(
     }
     const KeyWindow win{wl, wr, bottom_right ? L - n : 0, L};
     // Keys any query may see, in whole steps from kb; this wave's steps [s0, s1).
-    const int kbeg = win.lo(0), kend = win.hi(n - 1);
+    int kbeg = win.lo(0), kend = win.hi(n - 1);
+    if (chunk > 0) {
+        kbeg = max(kbeg, sp * chunk);
+        kend = min(kend, (sp + 1) * chunk);
+    }
     const int kb = kbeg & ~(KS - 1);
     const int nsteps = kend > kbeg ? (kend - kb + KS - 1) / KS : 0;
     const int per = (nsteps + NWD - 1) / NWD;
@@ -274,6 +283,17 @@ __global__ __launch_bounds__(NWD * 64) void sdpa_decode_bf16(
 #pragma unroll
             for (int e = 0; e < 4; ++e) acc[e] += sc * pu[(fd + e) * QN + fq];
         }
+        if (chunk > 0) {
+            // [m, l, -, -, O(64)] of query fq, split sp: O unnormalised, l
+            // against max m (68 floats, so that O stays 16-byte aligned)
+            float* pp = part + ((size_t)(sp * BH + bh) * n + fq) * PREC;
+            if (fd == 0) {
+                pp[0] = mx;
+                pp[1] = lt;
+            }
+            *reinterpret_cast<f32x4*>(pp + 4 + fd) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+            return;
+        }
         // no legal key ⇒ zero row; a NaN sum (NaN legal inputs) stays NaN
         const float inv = lt != 0.f ? 1.f / lt : 0.f;
         // ln Σ e^(scale·s) = (mcx + log2 lt)·ln 2: −∞ for a row with no legal key
@@ -289,20 +309,103 @@ __global__ __launch_bounds__(NWD * 64) void sdpa_decode_bf16(
 
 }  // namespace
 
+// Combine the splits of each (head, query): the usual rescale to the largest
+// maximum.  Thread t: query t % 16, dims 4·(t / 16) .. +3.
+__global__ __launch_bounds__(NWD * 64) void sdpa_decode_merge_bf16(
+    const float* __restrict__ part, uint16_t* __restrict__ O, float* __restrict__ lse, int BH, int n,
+    int nsplit, float c_log2) {
+    const int bh = blockIdx.x;
+    const int fq = threadIdx.x & (QN - 1);
+    const int fd = 4 * (threadIdx.x >> 4);
+    if (fq >= n) return;
+    const size_t stride = (size_t)BH * n * PREC;  // from one split to the next
+    const float* p0 = part + ((size_t)bh * n + fq) * PREC;
+    // Eight splits at a time: all their loads are issued before any use, then
+    // merged into the running (max, sum, O) with the usual rescale.
+    float mx = -INFINITY, lt = 0.f, acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < nsplit; s0 += 8) {
+        float ms[8], ls[8];
+        f32x4 os[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const bool ok = s0 + u < nsplit;
+            const float* ps = p0 + (size_t)(ok ? s0 + u : 0) * stride;
+            ms[u] = ok ? ps[0] : -INFINITY;
+            ls[u] = ok ? ps[1] : 0.f;
+            os[u] = ok ? *reinterpret_cast<const f32x4*>(ps + 4 + fd) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        float mnew = mx;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) mnew = fmaxf(mnew, ms[u]);
+        const float mc = (mnew == -INFINITY ? 0.f : mnew) * c_log2;
+        // the old partial and a split with no legal key (max −∞) scale by exactly 0
+        const float so = mx == -INFINITY ? 0.f : exp2_hw(mx * c_log2 - mc);
+        lt *= so;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] *= so;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const float sc = ms[u] == -INFINITY ? 0.f : exp2_hw(ms[u] * c_log2 - mc);
+            lt += sc * ls[u];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] += sc * os[u][e];
+        }
+        mx = mnew;
+    }
+    const float mcx = (mx == -INFINITY ? 0.f : mx) * c_log2;
+    // no legal key ⇒ zero row; a NaN sum (NaN legal inputs) stays NaN
+    const float inv = lt != 0.f ? 1.f / lt : 0.f;
+    if (lse && fd == 0) lse[(size_t)bh * n + fq] = (mcx + log2f(lt)) * 0.6931471805599453f;
+    bf16x4 ov;
+    ov[0] = (__bf16)(acc[0] * inv);
+    ov[1] = (__bf16)(acc[1] * inv);
+    ov[2] = (__bf16)(acc[2] * inv);
+    ov[3] = (__bf16)(acc[3] * inv);
+    *reinterpret_cast<bf16x4*>(O + ((size_t)bh * n + fq) * D + fd) = ov;
+}
+
+// Keys per split: 1024 (eight 32-key steps per wave).  Splitting pays when a
+// head's keys are long and their lengths differ: one workgroup per head then
+// leaves the CUs of short heads idle while the longest heads finish.
+// (2048- and 4096-key pieces measured slower on ragged 2k..8k caches.)
+constexpr int SPLIT_KEYS = 1024;
+
+int decode_nsplit(int m) { return (m + SPLIT_KEYS - 1) / SPLIT_KEYS; }
+
 bool decode_bf16_fits(const Args& a) {
     // A few queries against more keys than the sentence-length kernel takes,
     // and enough heads to give every CU work (one workgroup per head).
     return a.n <= QN && a.m > 64 && (long long)a.B * a.H >= 256;
 }
 
+size_t decode_split_bytes(int B, int H, int n, int m) {
+    const int ns = decode_nsplit(m);
+    if (ns < 2) return 0;
+    return (size_t)ns * B * H * n * PREC * sizeof(float);
+}
+
 hipError_t launch_bf16_decode(const Args& a, hipStream_t stream) {
     const float c_log2 = (float)((double)a.scale * 1.4426950408889634);  // scale·log2(e)
+    const int BH = a.B * a.H;
+    const size_t need = decode_split_bytes(a.B, a.H, a.n, a.m);
+    if (a.work && need > 0 && a.work_bytes >= need) {
+        const int ns = decode_nsplit(a.m);
+        hipLaunchKernelGGL(sdpa_decode_bf16<32>, dim3(BH * ns), dim3(NWD * 64), 0, stream,
+                           (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                           (uint16_t*)a.out, a.H, a.n, a.m, c_log2, a.wl, a.wr, a.bottom_right,
+                           a.key_lens, a.lse, BH, SPLIT_KEYS, (float*)a.work);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(sdpa_decode_merge_bf16, dim3(BH), dim3(NWD * 64), 0, stream,
+                           (const float*)a.work, (uint16_t*)a.out, a.lse, BH, a.n, ns, c_log2);
+        return hipGetLastError();
+    }
     // 32-key steps.  64-key steps (twice the bytes per request round trip)
     // measured no faster on 2k..8k-key caches and slower on full 8k caches.
     hipLaunchKernelGGL(sdpa_decode_bf16<32>, dim3(a.B * a.H), dim3(NWD * 64), 0, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (uint16_t*)a.out, a.H, a.n, a.m, c_log2, a.wl, a.wr, a.bottom_right,
-                       a.key_lens, a.lse);
+                       a.key_lens, a.lse, BH, 0, nullptr);
     return hipGetLastError();
 }
 

@@ -40,6 +40,9 @@ struct Args {
     float* lse = nullptr;
     // Head width d_k = d_v: 64 (every kernel), or 32 / 128 (bf16, sdpa_bf16_width.hip).
     int d = kHeadDim;
+    // Optional workspace for split-key decoder steps (decode_split_bytes), or nullptr.
+    void* work = nullptr;
+    size_t work_bytes = 0;
 };
 
 // Legal key range [lo, hi) of query row i under the window of one batch
@@ -113,6 +116,9 @@ hipError_t launch_bf16_short(const Args& a, hipStream_t stream);  // n, m <= 64
 bool short_bf16_fits(const Args& a);
 hipError_t launch_bf16_decode(const Args& a, hipStream_t stream);  // n <= 16, m > 64
 bool decode_bf16_fits(const Args& a);
+// Workspace the decoder-step kernel uses to split each head's keys over
+// several workgroups (0: it would not split these sizes).
+size_t decode_split_bytes(int B, int H, int n, int m);
 hipError_t launch_f32(const Args& a, hipStream_t stream);        // picks one of the two below
 hipError_t launch_f32_long(const Args& a, hipStream_t stream);   // any n, m
 hipError_t launch_f32_short(const Args& a, hipStream_t stream);  // n, m <= 64
