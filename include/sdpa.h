@@ -148,8 +148,9 @@ SDPA_API int sdpa_forward_window(const void* q, const void* k, const void* v, vo
  * w_o      device, [d_model, h·d_v] bf16: the transpose of W^O.
  * out      device, [B, n, d_model] bf16, written completely; must not overlap
  *          any input, weight or the workspace.
- * d_k, d_v 64; d_model a multiple of 64; dtype SDPA_BF16 (other values:
- *          SDPA_ERR_UNSUPPORTED, or SDPA_ERR_DTYPE if unknown).
+ * d_k, d_v d_k = d_v = 32, 64 or 128 with h·d_k a multiple of 64 (the model
+ *          variants' head widths); d_model a multiple of 64; dtype SDPA_BF16
+ *          (other values: SDPA_ERR_UNSUPPORTED, or SDPA_ERR_DTYPE if unknown).
  * workspace, workspace_bytes
  *          device scratch of at least sdpa_mha_workspace_bytes(...) bytes,
  *          16-byte aligned, owned by the caller; it receives the projected

@@ -142,7 +142,11 @@ def test_mha_workspace_size(lib):
     # Q, K, V and the attention output in bf16, each rounded up to 256 bytes
     assert _lib.sdpa_mha_workspace_bytes(64, 64, 64, 8, 64, 64) == 4 * 64 * 8 * 64 * 64 * 2
     assert _lib.sdpa_mha_workspace_bytes(1, 3, 5, 1, 64, 64) == 2 * 512 + 2 * 768
-    assert _lib.sdpa_mha_workspace_bytes(1, 3, 5, 1, 32, 64) == 0  # unsupported width
+    assert _lib.sdpa_mha_workspace_bytes(1, 3, 5, 1, 32, 64) == 0  # d_k != d_v
+    assert _lib.sdpa_mha_workspace_bytes(2, 4, 4, 16, 32, 32) == 4 * 2 * 16 * 4 * 32 * 2
+    assert _lib.sdpa_mha_workspace_bytes(2, 4, 4, 3, 32, 32) == 0  # h·d not a multiple of 64
+    assert _lib.sdpa_mha_workspace_bytes(1, 2, 2, 1, 128, 128) == 4 * 512
+    assert _lib.sdpa_mha_workspace_bytes(1, 2, 2, 1, 16, 16) == 0
 
 
 @pytest.mark.parametrize("kw,code", [

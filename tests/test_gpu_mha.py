@@ -53,6 +53,14 @@ CASES = [  # id, mha_case arguments, attention options
     ("long_window", dict(seed=2005, B=2, n=300, m=300, d_model=192, h=3), dict(window=(20, 5))),
     ("decode_step", dict(seed=2006, B=32, n=1, m=200, d_model=512, h=8, self_attention=False,
                          key_len_range=(1, 200)), dict(window=(None, 0, "bottom_right"))),
+    # the model variants' head widths (《精读 …》 Table 3 rows (A) and (C))
+    ("A_h16_d32", dict(seed=2011, B=16, n=64, m=64, d_model=512, h=16, d=32, key_len_range=(8, 64)), {}),
+    ("A_h4_d128_causal", dict(seed=2012, B=16, n=64, m=64, d_model=512, h=4, d=128,
+                              key_len_range=(8, 64)), dict(causal=True)),
+    ("C_dmodel256_d32_cross", dict(seed=2013, B=8, n=48, m=64, d_model=256, h=8, d=32,
+                                   self_attention=False, key_len_range=(1, 64)), {}),
+    ("C_dmodel1024_d128_window", dict(seed=2014, B=4, n=100, m=100, d_model=1024, h=8, d=128),
+     dict(window=(20, 5))),
 ]
 
 

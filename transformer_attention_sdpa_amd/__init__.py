@@ -49,8 +49,8 @@ def mha_forward(x_q, x_kv, w_q, w_k, w_v, w_o, *, heads: int, causal: bool = Fal
     Attention(x_q W_i^Q, x_kv W_i^K, x_kv W_i^V).
 
     x_q [B, n, d_model] and x_kv [B, m, d_model] (pass the same tensor for
-    self-attention); w_q, w_k, w_v [heads·64, d_model] and w_o [d_model,
-    heads·64] in the [out, in] layout.  ``causal``, ``window``, ``key_lens``
+    self-attention); w_q, w_k, w_v [heads·d, d_model] and w_o [d_model,
+    heads·d] in the [out, in] layout, d = 32, 64 or 128.  ``causal``, ``window``, ``key_lens``
     and ``scale`` as in ``forward``.  ``workspace``: a uint8 GPU tensor of at
     least ``sdpa_mha_workspace_bytes`` bytes, or None to have one allocated
     here (the library itself allocates nothing).  Returns ``out`` [B, n,
@@ -69,7 +69,10 @@ def mha_forward(x_q, x_kv, w_q, w_k, w_v, w_o, *, heads: int, causal: bool = Fal
         raise ValueError("x_q must be [B, n, d_model] and x_kv [B, m, d_model]")
     B, n, d_model = x_q.shape
     m = x_kv.shape[1]
-    hw = heads * 64
+    if w_q.dim() != 2 or w_q.shape[0] % heads:
+        raise ValueError("w_q must be [heads·d, d_model]")
+    d = w_q.shape[0] // heads  # head width d_k = d_v
+    hw = heads * d
     if (tuple(x_kv.shape) != (B, m, d_model) or tuple(w_q.shape) != (hw, d_model)
             or tuple(w_k.shape) != (hw, d_model) or tuple(w_v.shape) != (hw, d_model)
             or tuple(w_o.shape) != (d_model, hw)):
@@ -83,18 +86,18 @@ def mha_forward(x_q, x_kv, w_q, w_k, w_v, w_o, *, heads: int, causal: bool = Fal
     wl, wr, al = _window_args(window, causal)
     if causal and window is None and n != m:
         raise ValueError("the causal mask needs n == m; use a bottom-right window otherwise")
-    need = sdpa_mha_workspace_bytes(B, n, m, heads, 64, 64)
+    need = sdpa_mha_workspace_bytes(B, n, m, heads, d, d)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=x_q.device)
     if out is None:
         out = torch.empty((B, n, d_model), dtype=torch.bfloat16, device=x_q.device)
     if scale is None:
-        scale = 1.0 / math.sqrt(64)
+        scale = 1.0 / math.sqrt(d)
     with torch.cuda.device(x_q.device):
         stream = torch.cuda.current_stream(x_q.device).cuda_stream
         rc = sdpa_mha_forward(x_q.data_ptr(), x_kv.data_ptr(), w_q.data_ptr(), w_k.data_ptr(),
                               w_v.data_ptr(), w_o.data_ptr(), out.data_ptr(), B, n, m, d_model,
-                              heads, 64, 64, float(scale), wl, wr, al, kl_ptr, _lib.SDPA_BF16,
+                              heads, d, d, float(scale), wl, wr, al, kl_ptr, _lib.SDPA_BF16,
                               workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                               stream)
     if rc != _lib.SDPA_OK:

@@ -93,6 +93,13 @@ extern "C" int sdpa_forward_window(const void* q, const void* k, const void* v, 
     return launch(a, dtype, stream);
 }
 
+// Sublayer head widths: d_k = d_v ∈ {32, 64, 128}, with h·d a multiple of 64
+// (the output projection contracts over h·d in steps of 64).
+bool mha_width_ok(int32_t h, int32_t d_k, int32_t d_v) {
+    if (d_k != d_v || (d_k != 32 && d_k != 64 && d_k != 128)) return false;
+    return ((int64_t)h * d_k) % 64 == 0;
+}
+
 // Window arguments → (wl, wr, bottom_right), or SDPA_ERR_MASK.
 int window_args(int32_t n, int32_t m, int32_t window_left, int32_t window_right, int32_t align,
                 int32_t* wl, int32_t* wr, int32_t* br) {
@@ -232,8 +239,8 @@ extern "C" int sdpa_backward(const void* q, const void* k, const void* v, const 
 
 extern "C" size_t sdpa_mha_workspace_bytes(int32_t B, int32_t n, int32_t m, int32_t h, int32_t d_k,
                                            int32_t d_v) {
-    if (B < 1 || n < 1 || m < 1 || h < 1 || d_k != sdpa::kHeadDim || d_v != sdpa::kHeadDim) return 0;
-    return sdpa::mha_workspace_bytes(B, n, m, h);
+    if (B < 1 || n < 1 || m < 1 || h < 1 || !mha_width_ok(h, d_k, d_v)) return 0;
+    return sdpa::mha_workspace_bytes(B, n, m, h, d_k);
 }
 
 extern "C" int sdpa_mha_forward(const void* x_q, const void* x_kv, const void* w_q, const void* w_k,
@@ -245,13 +252,12 @@ extern "C" int sdpa_mha_forward(const void* x_q, const void* x_kv, const void* w
     if (!x_q || !x_kv || !w_q || !w_k || !w_v || !w_o || !out || !workspace) return SDPA_ERR_NULL;
     if (dtype != SDPA_F32 && dtype != SDPA_BF16) return SDPA_ERR_DTYPE;
     if (B < 1 || n < 1 || m < 1 || d_model < 1 || h < 1 || d_k < 1 || d_v < 1) return SDPA_ERR_SHAPE;
-    if (dtype != SDPA_BF16 || d_k != sdpa::kHeadDim || d_v != sdpa::kHeadDim || d_model % 64 != 0)
-        return SDPA_ERR_UNSUPPORTED;
+    if (dtype != SDPA_BF16 || !mha_width_ok(h, d_k, d_v) || d_model % 64 != 0) return SDPA_ERR_UNSUPPORTED;
     // Byte sizes; the kernels index with 32-bit offsets, so each stays below 2^31.
     const uint64_t lim = 1ull << 31;
     const uint64_t xq_b = (uint64_t)B * n * d_model * 2, xkv_b = (uint64_t)B * m * d_model * 2;
-    const uint64_t w_b = (uint64_t)h * 64 * d_model * 2;
-    const uint64_t need = sdpa::mha_workspace_bytes(B, n, m, h);
+    const uint64_t w_b = (uint64_t)h * d_k * d_model * 2;
+    const uint64_t need = sdpa::mha_workspace_bytes(B, n, m, h, d_k);
     if (xq_b >= lim || xkv_b >= lim || w_b >= lim || need >= lim) return SDPA_ERR_SHAPE;
     if ((uint64_t)B * h * (((uint64_t)n + 31) / 32) >= lim) return SDPA_ERR_SHAPE;
     if (window_left < -1 || window_right < -1) return SDPA_ERR_MASK;
@@ -275,7 +281,7 @@ extern "C" int sdpa_mha_forward(const void* x_q, const void* x_kv, const void* w
     const sdpa::MhaArgs a{x_q, x_kv, w_q, w_k, w_v, w_o, out, workspace, B, n, m, d_model, h, scale,
                           window_left > reach ? -1 : window_left,
                           window_right > reach ? -1 : window_right,
-                          align == SDPA_ALIGN_BOTTOM_RIGHT ? 1 : 0, key_lens};
+                          align == SDPA_ALIGN_BOTTOM_RIGHT ? 1 : 0, key_lens, d_k};
     const hipError_t e = sdpa::launch_mha_bf16(a, reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? SDPA_OK : SDPA_ERR_LAUNCH;
 }

@@ -84,8 +84,9 @@ struct MhaArgs {
     float scale;
     int wl, wr, bottom_right;
     const int32_t* key_lens;
+    int hd = kHeadDim;  // head width d_k = d_v: 32, 64 or 128
 };
-size_t mha_workspace_bytes(int B, int n, int m, int h);
+size_t mha_workspace_bytes(int B, int n, int m, int h, int hd);
 
 // The gradient of Eq. (1) (bf16): dQ, dK, dV from Q, K, V, the forward output
 // O, its gradient dO and the forward pass's per-row log-sum-exp.

@@ -8,11 +8,14 @@
 // launches on the caller's stream:
 //
 //   1. one projection launch computes Q, K and V (three jobs, blockIdx.z) and
-//      writes them straight into the [B, h, len, 64] layout the attention
+//      writes them straight into the [B, h, len, d] layout the attention
 //      kernels read: the split into heads is the epilogue's store pattern;
 //   2. the attention kernels of this library, on those tensors;
 //   3. one projection launch for W^O whose token rows are gathered from the
-//      [B, h, n, 64] attention output: the Concat is its load pattern.
+//      [B, h, n, d] attention output: the Concat is its load pattern.
+//
+// The head width d is 32, 64 or 128 (the pages' model variants), with h·d a
+// multiple of 64.
 //
 // Weights use the [out features, in features] layout, so that both MFMA
 // operands are contiguous along the contraction: row i·64 + j of the Q weight
@@ -33,19 +36,18 @@
 namespace sdpa {
 namespace {
 
-constexpr int HD = kHeadDim;  // 64
 
 enum { ROWS = 0, HEADS = 1 };
 
 // One projection: C = X · Wᵀ over M tokens, N output features, K inputs.
-// X is [M, K] row-major (ROWS) or the heads layout [M / len, K / 64, len, 64]
-// (HEADS, token t = b·len + i, input k = head·64 + j); C is [M, N] (ROWS) or
-// [M / len, N / 64, len, 64] (HEADS).
+// X is [M, K] row-major (ROWS) or the heads layout [M / len, K / hd, len, hd]
+// (HEADS, token t = b·len + i, input k = head·hd + j); C is [M, N] (ROWS) or
+// [M / len, N / hd, len, hd] (HEADS).  hd (the head width) is 32, 64 or 128.
 struct ProjJob {
     const uint16_t* x;
     const uint16_t* w;  // [N, K]
     uint16_t* c;
-    int M, N, K, len;
+    int M, N, K, len, hd;
 };
 struct ProjJobs {
     ProjJob job[3];
@@ -105,6 +107,7 @@ __global__ __launch_bounds__(256) void proj_gemm_bf16(ProjJobs jobs) {
     const i32x4 rx = make_rsrc(J.x, (uint32_t)J.M * (uint32_t)K * 2u);
     const i32x4 rw = make_rsrc(J.w, (uint32_t)J.N * (uint32_t)K * 2u);
     uint32_t xo[NXI], wo[NWI];
+    int xc[NXI];
 #pragma unroll
     for (int u = 0; u < NXI; ++u) {
         const int r = 8 * (w + 4 * u) + (lane >> 3);
@@ -113,9 +116,12 @@ __global__ __launch_bounds__(256) void proj_gemm_bf16(ProjJobs jobs) {
         if (AMODE == ROWS) {
             xo[u] = (uint32_t)t * (uint32_t)K * 2u + c16;
         } else {
+            // row base of token t in the heads layout; the chunk's head and
+            // offset inside it are added per stage (a stage may span heads)
             const int b = t / J.len, i = t - b * J.len;
-            xo[u] = t < J.M ? ((uint32_t)(b * (K / HD)) * (uint32_t)J.len + (uint32_t)i) * (HD * 2) + c16
-                            : (uint32_t)J.M * (uint32_t)K * 2u;
+            xo[u] = t < J.M ? ((uint32_t)(b * (K / J.hd)) * (uint32_t)J.len + (uint32_t)i) * (uint32_t)(J.hd * 2)
+                            : 0xffffffffu;
+            xc[u] = (int)c16 / 2;  // input offset of the chunk within a stage
         }
     }
 #pragma unroll
@@ -124,13 +130,20 @@ __global__ __launch_bounds__(256) void proj_gemm_bf16(ProjJobs jobs) {
         wo[u] = (uint32_t)(f0 + r) * (uint32_t)K * 2u + (uint32_t)(((lane & 7) ^ swz_f(r)) * 16);
     }
     // Stage s: inputs 64·s .. +63.  ROWS: 128 bytes further along each row;
-    // HEADS: the next head's block of the heads layout.
-    const uint32_t xstep = AMODE == ROWS ? 128u : (uint32_t)J.len * (HD * 2);
+    // HEADS: input k = 64·s + the chunk's offset sits in head k / hd at k % hd.
+    const uint32_t head_bytes = (uint32_t)J.len * (uint32_t)(J.hd * 2);
+    const int hd_shift = J.hd == 32 ? 5 : (J.hd == 64 ? 6 : 7);
+    auto xoff = [&](int u, int s) -> uint32_t {
+        if (AMODE == ROWS) return xo[u] + (uint32_t)s * 128u;
+        if (xo[u] == 0xffffffffu) return (uint32_t)J.M * (uint32_t)K * 2u;  // past the tensor: zeros
+        const int k = 64 * s + xc[u];
+        return xo[u] + (uint32_t)(k >> hd_shift) * head_bytes + (uint32_t)((k & (J.hd - 1)) * 2);
+    };
     auto issue = [&](int s) {
         char* base = lds + (s & 1) * STAGE;
 #pragma unroll
         for (int u = 0; u < NXI; ++u)
-            load16_to_lds(rx, base + (w + 4 * u) * 1024, (int)(xo[u] + (uint32_t)s * xstep));
+            load16_to_lds(rx, base + (w + 4 * u) * 1024, (int)xoff(u, s));
 #pragma unroll
         for (int u = 0; u < NWI; ++u)
             load16_to_lds(rw, base + XB + (w + 4 * u) * 1024, (int)(wo[u] + (uint32_t)s * 128u));
@@ -225,8 +238,8 @@ __global__ __launch_bounds__(256) void proj_gemm_bf16(ProjJobs jobs) {
             cbase = (size_t)tok * J.N;
         } else {
             const int b = tok / J.len, ii = tok - b * J.len;
-            cbase = ((size_t)b * (J.N / HD) * J.len + ii) * HD;
-            chead_stride = J.len * HD;
+            cbase = ((size_t)b * (J.N / J.hd) * J.len + ii) * J.hd;
+            chead_stride = J.len * J.hd;
         }
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
@@ -236,7 +249,7 @@ __global__ __launch_bounds__(256) void proj_gemm_bf16(ProjJobs jobs) {
             for (int i4 = 0; i4 < 4; ++i4) {
                 const int f = fb + 8 * i4 + 4 * hf;
                 const size_t dst = CMODE == ROWS ? cbase + f
-                                                 : cbase + (size_t)(f / HD) * chead_stride + (f % HD);
+                                                 : cbase + (size_t)(f / J.hd) * chead_stride + (f % J.hd);
                 bf16x4 o;
                 o[0] = (__bf16)acc[i][j][4 * i4 + 0];
                 o[1] = (__bf16)acc[i][j][4 * i4 + 1];
@@ -275,37 +288,39 @@ hipError_t launch_proj(const ProjJobs& jobs, int njobs, int max_m, int n, hipStr
 
 }  // namespace
 
-size_t mha_workspace_bytes(int B, int n, int m, int h) {
-    const size_t qo = (size_t)B * h * n * HD * 2, kv = (size_t)B * h * m * HD * 2;
+size_t mha_workspace_bytes(int B, int n, int m, int h, int hd) {
+    const size_t qo = (size_t)B * h * n * hd * 2, kv = (size_t)B * h * m * hd * 2;
     return 2 * align256(qo) + 2 * align256(kv);
 }
 
 hipError_t launch_mha_bf16(const MhaArgs& a, hipStream_t stream) {
     char* ws = static_cast<char*>(a.workspace);
-    const size_t qo = align256((size_t)a.B * a.h * a.n * HD * 2);
-    const size_t kv = align256((size_t)a.B * a.h * a.m * HD * 2);
+    const int hd = a.hd;
+    const size_t qo = align256((size_t)a.B * a.h * a.n * hd * 2);
+    const size_t kv = align256((size_t)a.B * a.h * a.m * hd * 2);
     uint16_t* qh = reinterpret_cast<uint16_t*>(ws);
     uint16_t* kh = reinterpret_cast<uint16_t*>(ws + qo);
     uint16_t* vh = reinterpret_cast<uint16_t*>(ws + qo + kv);
     uint16_t* oh = reinterpret_cast<uint16_t*>(ws + qo + 2 * kv);
-    const int hw = a.h * HD;
+    const int hw = a.h * hd;
 
     // 1. Q, K, V projections into the heads layout.
     ProjJobs in{};
-    in.job[0] = ProjJob{(const uint16_t*)a.x_q, (const uint16_t*)a.w_q, qh, a.B * a.n, hw, a.d_model, a.n};
-    in.job[1] = ProjJob{(const uint16_t*)a.x_kv, (const uint16_t*)a.w_k, kh, a.B * a.m, hw, a.d_model, a.m};
-    in.job[2] = ProjJob{(const uint16_t*)a.x_kv, (const uint16_t*)a.w_v, vh, a.B * a.m, hw, a.d_model, a.m};
+    in.job[0] = ProjJob{(const uint16_t*)a.x_q, (const uint16_t*)a.w_q, qh, a.B * a.n, hw, a.d_model, a.n, hd};
+    in.job[1] = ProjJob{(const uint16_t*)a.x_kv, (const uint16_t*)a.w_k, kh, a.B * a.m, hw, a.d_model, a.m, hd};
+    in.job[2] = ProjJob{(const uint16_t*)a.x_kv, (const uint16_t*)a.w_v, vh, a.B * a.m, hw, a.d_model, a.m, hd};
     hipError_t e = launch_proj<ROWS, HEADS>(in, 3, a.B * (a.n > a.m ? a.n : a.m), hw, stream);
     if (e != hipSuccess) return e;
 
     // 2. Attention over the B·h heads.
-    const Args att{qh, kh, vh, oh, a.B, a.h, a.n, a.m, a.scale, a.wl, a.wr, a.bottom_right, a.key_lens};
+    Args att{qh, kh, vh, oh, a.B, a.h, a.n, a.m, a.scale, a.wl, a.wr, a.bottom_right, a.key_lens};
+    att.d = hd;
     e = launch_bf16(att, stream);
     if (e != hipSuccess) return e;
 
     // 3. Concat(heads) · W^O, gathered from the heads layout.
     ProjJobs outj{};
-    outj.job[0] = ProjJob{oh, (const uint16_t*)a.w_o, (uint16_t*)a.out, a.B * a.n, a.d_model, hw, a.n};
+    outj.job[0] = ProjJob{oh, (const uint16_t*)a.w_o, (uint16_t*)a.out, a.B * a.n, a.d_model, hw, a.n, hd};
     return launch_proj<HEADS, ROWS>(outj, 1, a.B * a.n, a.d_model, stream);
 }
 
