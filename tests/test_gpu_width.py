@@ -97,14 +97,61 @@ def test_width_deterministic_and_ignores_padded_rows(gpu_lib):
     assert np.all(a[2] == 0)  # no legal key: zero rows
 
 
-def test_width_backward_is_rejected(gpu_lib):
-    """The backward pass is 64-wide only: other widths get a clear error."""
+BWD_CASES = [  # id, (B, h, n, m, d), options
+    ("d32_encoder_padded", (8, 4, 64, 64, 32), dict(key_lens=(8, 64))),
+    ("d128_encoder_padded", (8, 2, 64, 64, 128), dict(key_lens=(8, 64))),
+    ("d32_multi_tile_causal", (2, 2, 300, 300, 32), dict(causal=True)),
+    ("d128_multi_tile_causal", (2, 2, 300, 300, 128), dict(causal=True)),
+    ("d32_window_ragged", (2, 2, 200, 230, 32), dict(window=(30, 10), key_lens=(100, 230))),
+    ("d128_bottom_right", (2, 2, 5, 200, 128), dict(window=(None, 0, "bottom_right"), key_lens=(0, 200))),
+    ("d128_cross_padded", (3, 2, 70, 130, 128), dict(key_lens=(1, 130))),
+]
+
+
+@pytest.mark.parametrize("i", range(len(BWD_CASES)), ids=[c[0] for c in BWD_CASES])
+def test_width_backward_parity(gpu_lib, i):
+    """dQ, dK, dV at widths 32 and 128 against the fp64 gradient oracle (bar as
+    for width 64: 2e-2 of each tensor's largest magnitude, plus 2^-16)."""
     import torch
 
     from transformer_attention_sdpa_amd import backward, forward
 
-    c = _case(1, (1, 1, 8, 8, 32), {})
+    name, shape, opts = BWD_CASES[i]
+    c = _case(100 + i, shape, opts)
+    B, h, n, m, d = shape
+    rng = np.random.default_rng(8500 + i)
+    from sdpa_inputs import round_to_bf16
+
+    c["do"] = round_to_bf16(rng.standard_normal((B, h, n, d), dtype=np.float32))
+    q, k, v, do = (to_device(c[x], "bf16") for x in ("q", "k", "v", "do"))
+    kl = None if c["key_lens"] is None else torch.from_numpy(c["key_lens"]).cuda()
+    kw = dict(causal=c["causal"], key_lens=kl, window=c["window"])
+    out, lse = forward(q, k, v, return_lse=True, **kw)
+    grads = backward(q, k, v, out, do, lse, **kw)
+    torch.cuda.synchronize()
+    refs = sb.attention_backward(c["q"], c["k"], c["v"], c["do"], causal=c["causal"], key_lens=c["key_lens"],
+                                 window=c["window"])
+    msg = []
+    for what, g, r in zip(("dq", "dk", "dv"), grads, refs):
+        g = from_device(g)
+        err = max_abs_err(g, r)
+        bound = 2e-2 * float(np.abs(r).max()) + 2.0 ** -16
+        msg.append(f"{what} {err:.2e}/{np.abs(r).max():.2e}")
+        assert np.all(np.isfinite(g)) and err <= bound, (name, what, err, bound)
+    print(f"width bwd {name}: " + ", ".join(msg))
+
+
+def test_width_backward_deterministic(gpu_lib):
+    import torch
+
+    from transformer_attention_sdpa_amd import backward, forward
+
+    c = _case(120, (2, 2, 300, 300, 128), dict(causal=True))
     q, k, v = (to_device(c[x], "bf16") for x in ("q", "k", "v"))
-    out, lse = forward(q, k, v, return_lse=True)
-    with pytest.raises(RuntimeError, match="unsupported"):
-        backward(q, k, v, out, torch.zeros_like(out), lse)
+    out, lse = forward(q, k, v, causal=True, return_lse=True)
+    do = torch.randn_like(out)
+    a = backward(q, k, v, out, do, lse, causal=True)
+    b = backward(q, k, v, out, do, lse, causal=True)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))

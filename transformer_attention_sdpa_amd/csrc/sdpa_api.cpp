@@ -209,7 +209,7 @@ extern "C" int sdpa_backward(const void* q, const void* k, const void* v, const 
     // checks below cover the outputs).
     int st = validate(q, k, v, const_cast<void*>(out), B, h, n, m, d_k, d_v, scale, key_lens, dtype);
     if (st != SDPA_OK) return st;
-    if (dtype != SDPA_BF16 || d_k != sdpa::kHeadDim) return SDPA_ERR_UNSUPPORTED;
+    if (dtype != SDPA_BF16) return SDPA_ERR_UNSUPPORTED;  // widths: as validate() allows for bf16
     for (const void* p : {dout, (const void*)dq, (const void*)dk, (const void*)dv, (const void*)workspace})
         if (!aligned16(p)) return SDPA_ERR_ALIGN;
     if (reinterpret_cast<uintptr_t>(lse) & 3u) return SDPA_ERR_ALIGN;
@@ -232,7 +232,7 @@ extern "C" int sdpa_backward(const void* q, const void* k, const void* v, const 
             if (overlap(outs[i].p, outs[i].n, outs[j].p, outs[j].n)) return SDPA_ERR_ALIAS;
     }
     const sdpa::BwdArgs a{q, k, v, out, dout, lse, dq, dk, dv, workspace, B, h, n, m, scale, wl, wr, br,
-                          key_lens};
+                          key_lens, d_k};
     const hipError_t e = sdpa::launch_bwd_bf16(a, reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? SDPA_OK : SDPA_ERR_LAUNCH;
 }

@@ -40,9 +40,21 @@
 namespace sdpa {
 namespace {
 
-constexpr int D = kHeadDim;              // 64
-constexpr int BT = 64;                   // rows per LDS tile
-constexpr int TILE_BYTES = BT * D * 2;   // 8 KiB
+constexpr int BT = 64;                          // rows per LDS tile
+constexpr int TILE_BYTES = BT * kHeadDim * 2;   // 8 KiB at width 64 (the fused kernel)
+template <int D>
+constexpr int tile_bytes() { return BT * D * 2; }
+
+// 16-byte chunk position of chunk c of row r in a tile of D/8 chunks per row,
+// XOR-swizzled so that 16 consecutive rows read at one chunk fall on distinct
+// banks of the 256-byte LDS pass (64-byte rows share a pass four at a time,
+// 256-byte rows fill it alone); for D = 64 it is lds_swz.
+template <int D>
+__device__ __forceinline__ int bswz(int r, int c) {
+    if constexpr (D == 32) return r * 4 + (c ^ ((r >> 2) & 3));
+    else if constexpr (D == 128) return r * 16 + (c ^ (r & 15));
+    else return lds_swz(r, c);
+}
 constexpr float LOG2E = 1.4426950408889634f;
 
 __device__ __forceinline__ uint32_t lds_u32(const void* p) {
@@ -73,24 +85,25 @@ __device__ __forceinline__ void lds_wait(u32x2 (&x)[N]) {
     for (int i = 0; i < N; ++i) asm volatile("" : "+v"(x[i]));
 }
 
-// Per-lane LDS offsets inside one 64-row tile (16-byte chunk c of row r at
-// lds_swz(r, c)), shared by both kernels.
+// Per-lane LDS offsets inside one 64-row tile of width D (16-byte chunk c of
+// row r at bswz<D>(r, c)), shared by the kernels.
+template <int D>
 struct TileAddr {
-    int row[4];    // 16-byte A operand of k-step ks: row l32, chunk 2·ks + hf
-    int tr[2][2];  // transpose reads of k-step 0: [32-column block dt][rows +0 / +8]
+    int row[D / 16];    // 16-byte A operand of k-step ks: row l32, chunk 2·ks + hf
+    int tr[D / 32][2];  // transpose reads of k-step 0: [32-column block dt][rows +0 / +8]
     __device__ void init(int lane) {
         const int l32 = lane & 31, hf = lane >> 5, gi = lane & 15;
-        const int f = swz_f(l32);  // rows l32 and l32 + 32 share it
+        // (rows l32 and l32 + 32 share the swizzle of every width)
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) row[ks] = l32 * 128 + (((2 * ks + hf) ^ f) << 4);
+        for (int ks = 0; ks < D / 16; ++ks) row[ks] = bswz<D>(l32, 2 * ks + hf) * 16;
         // Rows 4·hf + gi/4 (+ 8) of k-step 0; k-step j adds 16·j rows, which
-        // leaves swz_f unchanged (it reads row bits 1..3).
+        // leaves the swizzle of every width unchanged.
         const int r0 = 4 * hf + (gi >> 2);
 #pragma unroll
-        for (int dt = 0; dt < 2; ++dt) {
+        for (int dt = 0; dt < D / 32; ++dt) {
             const int c0 = 32 * dt + 16 * ((lane >> 4) & 1) + 4 * (gi & 3);
-            tr[dt][0] = lds_swz(r0, c0 >> 3) * 16 + (c0 & 7) * 2;
-            tr[dt][1] = lds_swz(r0 + 8, c0 >> 3) * 16 + (c0 & 7) * 2;
+            tr[dt][0] = bswz<D>(r0, c0 >> 3) * 16 + (c0 & 7) * 2;
+            tr[dt][1] = bswz<D>(r0 + 8, c0 >> 3) * 16 + (c0 & 7) * 2;
         }
     }
 };
@@ -106,67 +119,77 @@ __device__ __forceinline__ bf16x8 pack_step(const f32x16 (&x)[2], int j) {
 // acc[dt] += Aᵀ · B over one 64-row tile: A is the tile (rows = contraction
 // index, columns = the 64 output rows), fetched with transpose reads in the
 // permuted contraction order; b[j] is k-step j of the B operand.
-__device__ __forceinline__ void tr_product(uint32_t tile, const TileAddr& ta, const bf16x8 (&b)[4],
-                                           f32x16 (&acc)[2]) {
-    u32x2 a[16];
+template <int D>
+__device__ __forceinline__ void tr_product(uint32_t tile, const TileAddr<D>& ta, const bf16x8 (&b)[4],
+                                           f32x16 (&acc)[D / 32]) {
+    constexpr int DT = D / 32;
+    u32x2 a[8 * DT];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int dt = 0; dt < 2; ++dt) {
-            a[4 * j + 2 * dt] = ds_read_tr(tile + ta.tr[dt][0] + j * 16 * 128);
-            a[4 * j + 2 * dt + 1] = ds_read_tr(tile + ta.tr[dt][1] + j * 16 * 128);
+        for (int dt = 0; dt < DT; ++dt) {
+            a[(j * DT + dt) * 2] = ds_read_tr(tile + ta.tr[dt][0] + j * 16 * D * 2);
+            a[(j * DT + dt) * 2 + 1] = ds_read_tr(tile + ta.tr[dt][1] + j * 16 * D * 2);
         }
     lds_wait(a);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int dt = 0; dt < 2; ++dt) {
-            const u32x4 v = {a[4 * j + 2 * dt][0], a[4 * j + 2 * dt][1], a[4 * j + 2 * dt + 1][0],
-                             a[4 * j + 2 * dt + 1][1]};
+        for (int dt = 0; dt < DT; ++dt) {
+            const u32x2 lo = a[(j * DT + dt) * 2], hi = a[(j * DT + dt) * 2 + 1];
+            const u32x4 v = {lo[0], lo[1], hi[0], hi[1]};
             acc[dt] = mfma32x32x16_bf16(__builtin_bit_cast(bf16x8, v), b[j], acc[dt]);
         }
 }
 
-// s[t] = A_t · B and p[t] = A'_t · B' for the two 32-row halves t of two tiles
-// A, A' (rows from LDS) against B, B' (k = 64 dims, in VGPRs).
-__device__ __forceinline__ void row_products(uint32_t ta_, uint32_t tb_, const TileAddr& ta,
-                                             const bf16x8 (&b)[4], const bf16x8 (&b2)[4],
+// s[t] = A_t · B (and, with TWO, p[t] = A'_t · B') for the two 32-row halves
+// t of tiles A, A' (rows from LDS) against B, B' (k = D dims, in VGPRs).
+template <int D, bool TWO>
+__device__ __forceinline__ void row_products(uint32_t ta_, uint32_t tb_, const TileAddr<D>& ta,
+                                             const bf16x8 (&b)[D / 16], const bf16x8 (&b2)[D / 16],
                                              f32x16 (&s)[2], f32x16 (&p)[2]) {
-    u32x4 a[16];
+    constexpr int KS = D / 16, NA = TWO ? 2 : 1;
+    u32x4 a[NA * 2 * KS];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            a[4 * t + ks] = ds_read_b128(ta_ + ta.row[ks] + t * 32 * 128);
-            a[8 + 4 * t + ks] = ds_read_b128(tb_ + ta.row[ks] + t * 32 * 128);
+        for (int ks = 0; ks < KS; ++ks) {
+            a[t * KS + ks] = ds_read_b128(ta_ + ta.row[ks] + t * 32 * D * 2);
+            if constexpr (TWO) a[2 * KS + t * KS + ks] = ds_read_b128(tb_ + ta.row[ks] + t * 32 * D * 2);
         }
     lds_wait(a);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) { s[t][i] = 0.f; p[t][i] = 0.f; }
+        for (int i = 0; i < 16; ++i) {
+            s[t][i] = 0.f;
+            if constexpr (TWO) p[t][i] = 0.f;
+        }
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            s[t] = mfma32x32x16_bf16(__builtin_bit_cast(bf16x8, a[4 * t + ks]), b[ks], s[t]);
-            p[t] = mfma32x32x16_bf16(__builtin_bit_cast(bf16x8, a[8 + 4 * t + ks]), b2[ks], p[t]);
+        for (int ks = 0; ks < KS; ++ks) {
+            s[t] = mfma32x32x16_bf16(__builtin_bit_cast(bf16x8, a[t * KS + ks]), b[ks], s[t]);
+            if constexpr (TWO)
+                p[t] = mfma32x32x16_bf16(__builtin_bit_cast(bf16x8, a[2 * KS + t * KS + ks]), b2[ks], p[t]);
         }
     }
 }
 
-// This lane's 16-byte operand chunks of one 64-wide row (dims 16·ks + 8·hf
+// This lane's 16-byte operand chunks of one D-wide row (dims 16·ks + 8·hf
 // + [0..7]), zeros if the row is out of range.
-__device__ __forceinline__ void load_row_operand(const uint16_t* rowp, bool ok, int hf, bf16x8 (&x)[4]) {
+template <int D>
+__device__ __forceinline__ void load_row_operand(const uint16_t* rowp, bool ok, int hf, bf16x8 (&x)[D / 16]) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+    for (int ks = 0; ks < D / 16; ++ks)
         x[ks] = ok ? __builtin_bit_cast(bf16x8, reinterpret_cast<const u32x4*>(rowp)[2 * ks + hf])
                    : __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
 }
 
 // Store a transposed accumulator pair (register i of acc[dt] is column
 // 32·dt + 8·(i/4) + 4·hf + i%4 of this lane's row) times `mul` as bf16.
-__device__ __forceinline__ void store_rowT(uint16_t* dst, const f32x16 (&acc)[2], int hf, float mul) {
+template <int D>
+__device__ __forceinline__ void store_rowT(uint16_t* dst, const f32x16 (&acc)[D / 32], int hf, float mul) {
 #pragma unroll
-    for (int dt = 0; dt < 2; ++dt)
+    for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
             bf16x4 o;
@@ -178,35 +201,37 @@ __device__ __forceinline__ void store_rowT(uint16_t* dst, const f32x16 (&acc)[2]
         }
 }
 
-// Copy rows [r0, r0 + 64) of a [len, 64] bf16 tensor into an LDS tile; rows
-// at or past `len` arrive as zeros.  Wave w of NW issues 8/NW of the eight
-// 1 KiB loads; lane ln lands in (row ln/8, position ln%8), which holds chunk
-// (ln%8) ^ swz_f(row).
-template <int NW>
+// Copy rows [r0, r0 + 64) of a [len, D] bf16 tensor into an LDS tile; rows
+// at or past `len` arrive as zeros.  Wave w of NW issues its share of the
+// tile's 1 KiB loads; lane ln lands in (row ln/CPR, position ln%CPR) of the
+// load's rows, which holds the chunk whose swizzled position that is.
+template <int D, int NW>
 __device__ __forceinline__ void load_tile(char* lds_tile, const uint16_t* base, int r0, int len, int w,
                                           int lane) {
+    constexpr int CPR = D / 8, LOADS = tile_bytes<D>() / 1024 / NW, RPL = 1024 / (D * 2);
     const int left = len - r0;
     const i32x4 rs = make_rsrc(base + (size_t)r0 * D, (uint32_t)(left > 0 ? left : 0) * (D * 2));
 #pragma unroll
-    for (int i = 0; i < 8 / NW; ++i) {
-        const int blk = w * (8 / NW) + i;
-        const int row = 8 * blk + (lane >> 3);
-        const int off = row * 128 + (((lane & 7) ^ swz_f(row)) << 4);
-        load16_to_lds(rs, lds_tile + blk * 1024, off);
+    for (int i = 0; i < LOADS; ++i) {
+        const int blk = w * LOADS + i;
+        const int row = RPL * blk + lane / CPR;
+        const int chunk = bswz<D>(row, lane % CPR) - row * CPR;  // XOR is its own inverse
+        load16_to_lds(rs, lds_tile + blk * 1024, row * D * 2 + chunk * 16);
     }
 }
 
 // ---------------------------------------------------------------------------
 // Launch 1: dQ (and D, lse·log2 e for launch 2).
 
-template <int NW>
+template <int D, int NW>
 __global__ __launch_bounds__(NW * 64) void sdpa_bwd_dq_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO, const float* __restrict__ lse,
     uint16_t* __restrict__ dQ, float* __restrict__ ws_d, float* __restrict__ ws_l,
     int BH, int H, int n, int m, float scale, float c_log2, int wl, int wr, int bottom_right,
     const int32_t* __restrict__ key_lens, int nqb) {
-    __shared__ __attribute__((aligned(1024))) char lds[2 * 2 * TILE_BYTES];  // [buf][K | V]
+    constexpr int TB = tile_bytes<D>(), KS = D / 16, DT = D / 32;
+    __shared__ __attribute__((aligned(1024))) char lds[2 * 2 * TB];  // [buf][K | V]
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
@@ -236,17 +261,17 @@ __global__ __launch_bounds__(NW * 64) void sdpa_bwd_dq_bf16(
     const size_t qbase = (size_t)bh * n * D, kvbase = (size_t)bh * m * D;
     const int qrow = wq0 + l32;
     const bool qok = qrow < n;
-    bf16x8 qop[4], dop[4];
-    load_row_operand(Q + qbase + (size_t)qrow * D, qok, hf, qop);
-    load_row_operand(dO + qbase + (size_t)qrow * D, qok, hf, dop);
-    // D_i = dO_i · O_i over this lane's 32 dims, then the other half-wave's.
+    bf16x8 qop[KS], dop[KS];
+    load_row_operand<D>(Q + qbase + (size_t)qrow * D, qok, hf, qop);
+    load_row_operand<D>(dO + qbase + (size_t)qrow * D, qok, hf, dop);
+    // D_i = dO_i · O_i over this lane's half of the dims, then the other half-wave's.
     float dsum;
     {
-        bf16x8 oop[4];
-        load_row_operand(O + qbase + (size_t)qrow * D, qok, hf, oop);
+        bf16x8 oop[KS];
+        load_row_operand<D>(O + qbase + (size_t)qrow * D, qok, hf, oop);
         float acc = 0.f;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
+        for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)dop[ks][e], (float)oop[ks][e], acc);
         dsum = half_swap_sum(acc);
@@ -259,16 +284,18 @@ __global__ __launch_bounds__(NW * 64) void sdpa_bwd_dq_bf16(
         ws_l[(size_t)bh * n + qrow] = lc;
     }
 
-    TileAddr ta;
+    TileAddr<D> ta;
     ta.init(lane);
     const uint32_t l0 = lds_u32(lds);
-    f32x16 acc[2];
+    f32x16 acc[DT];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) { acc[0][i] = 0.f; acc[1][i] = 0.f; }
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
 
     auto issue = [&](int t, int buf) {
-        load_tile<NW>(lds + buf * 2 * TILE_BYTES, K + kvbase, t * BT, L, w, lane);
-        load_tile<NW>(lds + buf * 2 * TILE_BYTES + TILE_BYTES, V + kvbase, t * BT, L, w, lane);
+        load_tile<D, NW>(lds + buf * 2 * TB, K + kvbase, t * BT, L, w, lane);
+        load_tile<D, NW>(lds + buf * 2 * TB + TB, V + kvbase, t * BT, L, w, lane);
     };
     if (tend > tbeg) issue(tbeg, 0);
     wait_vmem();
@@ -278,9 +305,9 @@ __global__ __launch_bounds__(NW * 64) void sdpa_bwd_dq_bf16(
         if (t + 1 < tend) issue(t + 1, buf ^ 1);
         const int k0 = t * BT;
         if (k0 < whi && k0 + BT > wlo) {  // uniform: some query of the wave sees the tile
-            const uint32_t sk = l0 + buf * 2 * TILE_BYTES, sv = sk + TILE_BYTES;
+            const uint32_t sk = l0 + buf * 2 * TB, sv = sk + TB;
             f32x16 s[2], dp[2];
-            row_products(sk, sv, ta, qop, dop, s, dp);
+            row_products<D, true>(sk, sv, ta, qop, dop, s, dp);
             // Register i of s[kt] is key k0 + 32·kt + 8·(i/4) + 4·hf + i%4.
             if (k0 < flo || k0 + BT > fhi) {
                 const int llo = win.lo(qrow) - k0 - 4 * hf, lhi = win.hi(qrow) - k0 - 4 * hf;
@@ -302,12 +329,12 @@ __global__ __launch_bounds__(NW * 64) void sdpa_bwd_dq_bf16(
             bf16x8 db[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) db[j] = pack_step(s, j);
-            tr_product(sk, ta, db, acc);  // dQᵀ += Kᵀ dSᵀ
+            tr_product<D>(sk, ta, db, acc);  // dQᵀ += Kᵀ dSᵀ
         }
         wait_vmem();
         __syncthreads();
     }
-    if (qok) store_rowT(dQ + qbase + (size_t)qrow * D, acc, hf, scale);
+    if (qok) store_rowT<D>(dQ + qbase + (size_t)qrow * D, acc, hf, scale);
 }
 
 // ---------------------------------------------------------------------------
@@ -331,7 +358,9 @@ struct QueryRange {
     }
 };
 
-template <int NW>
+// DV, DK: which gradients this launch forms (both, for D <= 64; at D = 128 one
+// launch each keeps the accumulators within the register file).
+template <int D, int NW, bool DV, bool DK>
 __global__ __launch_bounds__(NW * 64) void sdpa_bwd_dkdv_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ ws_d, const float* __restrict__ ws_l,
@@ -339,7 +368,8 @@ __global__ __launch_bounds__(NW * 64) void sdpa_bwd_dkdv_bf16(
     int BH, int H, int n, int m, float scale, float c_log2, int wl, int wr, int bottom_right,
     const int32_t* __restrict__ key_lens) {
     // [buf][Q tile | dO tile | lse·log2 e (64 floats) | D (64 floats)]
-    constexpr int STAGE = 2 * TILE_BYTES + 512;
+    constexpr int TB = tile_bytes<D>(), KS = D / 16, DT = D / 32;
+    constexpr int STAGE = 2 * TB + 512;
     __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE];
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -375,30 +405,35 @@ __global__ __launch_bounds__(NW * 64) void sdpa_bwd_dkdv_bf16(
     const int key = wk0 + l32;
     // Kᵀ, Vᵀ as B operands; keys at or past L are zeros (their rows may hold
     // anything), so their logits are masked and their dS is exactly 0.
-    bf16x8 kop[4], vop[4];
-    load_row_operand(K + kvbase + (size_t)key * D, key < L, hf, kop);
-    load_row_operand(V + kvbase + (size_t)key * D, key < L, hf, vop);
+    bf16x8 kop[KS], vop[KS];
+    load_row_operand<D>(K + kvbase + (size_t)key * D, key < L, hf, kop);
+    if constexpr (DK) load_row_operand<D>(V + kvbase + (size_t)key * D, key < L, hf, vop);
     const int ka = qr.qa(key), kb = qr.qb(key);
 
-    TileAddr ta;
+    TileAddr<D> ta;
     ta.init(lane);
     const uint32_t l0 = lds_u32(lds);
-    f32x16 dka[2], dva[2];
+    f32x16 dka[DK ? DT : 1], dva[DV ? DT : 1];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) { dka[0][i] = 0.f; dka[1][i] = 0.f; dva[0][i] = 0.f; dva[1][i] = 0.f; }
+    for (int i = 0; i < 16; ++i) {
+#pragma unroll
+        for (int dt = 0; dt < (DK ? DT : 1); ++dt) dka[dt][i] = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < (DV ? DT : 1); ++dt) dva[dt][i] = 0.f;
+    }
 
     auto issue = [&](int t, int buf) {
         char* st = lds + buf * STAGE;
-        load_tile<NW>(st, Q + qbase, t * BT, n, w, lane);
-        load_tile<NW>(st + TILE_BYTES, dO + qbase, t * BT, n, w, lane);
+        load_tile<D, NW>(st, Q + qbase, t * BT, n, w, lane);
+        load_tile<D, NW>(st + TB, dO + qbase, t * BT, n, w, lane);
         if (w == 0) {  // 64 floats each: one dword per lane
             const int left = n - t * BT;
             const uint32_t nb = (uint32_t)(left > 0 ? left : 0) * 4u;
             const i32x4 rl = make_rsrc(ws_l + (size_t)bh * n + t * BT, nb);
             const i32x4 rd = make_rsrc(ws_d + (size_t)bh * n + t * BT, nb);
-            sdpa_llvm_buffer_load_lds(rl, (__attribute__((address_space(3))) void*)(st + 2 * TILE_BYTES), 4,
+            sdpa_llvm_buffer_load_lds(rl, (__attribute__((address_space(3))) void*)(st + 2 * TB), 4,
                                       lane * 4, 0, 0, 0);
-            sdpa_llvm_buffer_load_lds(rd, (__attribute__((address_space(3))) void*)(st + 2 * TILE_BYTES + 256),
+            sdpa_llvm_buffer_load_lds(rd, (__attribute__((address_space(3))) void*)(st + 2 * TB + 256),
                                       4, lane * 4, 0, 0, 0);
         }
     };
@@ -410,9 +445,9 @@ __global__ __launch_bounds__(NW * 64) void sdpa_bwd_dkdv_bf16(
         if (t + 1 < tend) issue(t + 1, buf ^ 1);
         const int t0 = t * BT;
         if (t0 < wqb && t0 + BT > wqa) {  // uniform: some query of the tile sees a key of the wave
-            const uint32_t sq = l0 + buf * STAGE, sd = sq + TILE_BYTES;
+            const uint32_t sq = l0 + buf * STAGE, sd = sq + TB;
             f32x16 s[2], dp[2];
-            row_products(sq, sd, ta, kop, vop, s, dp);
+            row_products<D, DK>(sq, sd, ta, kop, vop, s, dp);
             // Register i of s[qh] is query t0 + 32·qh + 8·(i/4) + 4·hf + i%4.
             if (t0 < fqa || t0 + BT > fqb) {
                 const int llo = ka - t0 - 4 * hf, lhi = kb - t0 - 4 * hf;
@@ -432,43 +467,51 @@ __global__ __launch_bounds__(NW * 64) void sdpa_bwd_dkdv_bf16(
 #pragma unroll
                 for (int gq = 0; gq < 4; ++gq) {
                     const uint32_t off = (uint32_t)(32 * qh + 8 * gq + 4 * hf) * 4u;
-                    lv[4 * qh + gq] = ds_read_b128(sq + 2 * TILE_BYTES + off);
+                    lv[4 * qh + gq] = ds_read_b128(sq + 2 * TB + off);
                 }
             lds_wait(lv);
             u32x4 dv4[8];
+            if constexpr (DK) {
 #pragma unroll
-            for (int qh = 0; qh < 2; ++qh)
+                for (int qh = 0; qh < 2; ++qh)
 #pragma unroll
-                for (int gq = 0; gq < 4; ++gq) {
-                    const uint32_t off = (uint32_t)(32 * qh + 8 * gq + 4 * hf) * 4u;
-                    dv4[4 * qh + gq] = ds_read_b128(sq + 2 * TILE_BYTES + 256 + off);
-                }
-            lds_wait(dv4);
+                    for (int gq = 0; gq < 4; ++gq) {
+                        const uint32_t off = (uint32_t)(32 * qh + 8 * gq + 4 * hf) * 4u;
+                        dv4[4 * qh + gq] = ds_read_b128(sq + 2 * TB + 256 + off);
+                    }
+                lds_wait(dv4);
+            }
 #pragma unroll
             for (int qh = 0; qh < 2; ++qh)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const float lc = __uint_as_float(lv[4 * qh + (i >> 2)][i & 3]);
-                    const float dd = __uint_as_float(dv4[4 * qh + (i >> 2)][i & 3]);
                     const float p = exp2_hw(__builtin_fmaf(s[qh][i], c_log2, -lc));
                     s[qh][i] = p;
-                    dp[qh][i] = p * (dp[qh][i] - dd);  // dS
+                    if constexpr (DK) {
+                        const float dd = __uint_as_float(dv4[4 * qh + (i >> 2)][i & 3]);
+                        dp[qh][i] = p * (dp[qh][i] - dd);  // dS
+                    }
                 }
-            bf16x8 pb[4], db[4];
+            if constexpr (DV) {
+                bf16x8 pb[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                pb[j] = pack_step(s, j);
-                db[j] = pack_step(dp, j);
+                for (int j = 0; j < 4; ++j) pb[j] = pack_step(s, j);
+                tr_product<D>(sd, ta, pb, dva);  // dVᵀ += dOᵀ P
             }
-            tr_product(sd, ta, pb, dva);  // dVᵀ += dOᵀ P
-            tr_product(sq, ta, db, dka);  // dKᵀ += Qᵀ dS
+            if constexpr (DK) {
+                bf16x8 db[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) db[j] = pack_step(dp, j);
+                tr_product<D>(sq, ta, db, dka);  // dKᵀ += Qᵀ dS
+            }
         }
         wait_vmem();
         __syncthreads();
     }
     if (key < m) {
-        store_rowT(dK + kvbase + (size_t)key * D, dka, hf, scale);
-        store_rowT(dV + kvbase + (size_t)key * D, dva, hf, 1.f);
+        if constexpr (DK) store_rowT<D>(dK + kvbase + (size_t)key * D, dka, hf, scale);
+        if constexpr (DV) store_rowT<D>(dV + kvbase + (size_t)key * D, dva, hf, 1.f);
     }
 }
 
@@ -487,6 +530,7 @@ __global__ __launch_bounds__(256) void sdpa_bwd_short_bf16(
     const int32_t* __restrict__ key_lens) {
     // [Q | dO | K | V] tiles, then lse·log2 e and D of the 64 query rows.
     __shared__ __attribute__((aligned(1024))) char lds[4 * TILE_BYTES + 512];
+    constexpr int D = kHeadDim;
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
@@ -499,15 +543,15 @@ __global__ __launch_bounds__(256) void sdpa_bwd_short_bf16(
         L = t < 0 ? 0 : (t > m ? m : t);
     }
     // Each wave copies two of the eight 1 KiB blocks of every tile.
-    load_tile<4>(lds, Q + qbase, 0, n, w, lane);
-    load_tile<4>(lds + TILE_BYTES, dO + qbase, 0, n, w, lane);
-    load_tile<4>(lds + 2 * TILE_BYTES, K + kvbase, 0, L, w, lane);
-    load_tile<4>(lds + 3 * TILE_BYTES, V + kvbase, 0, L, w, lane);
+    load_tile<D, 4>(lds, Q + qbase, 0, n, w, lane);
+    load_tile<D, 4>(lds + TILE_BYTES, dO + qbase, 0, n, w, lane);
+    load_tile<D, 4>(lds + 2 * TILE_BYTES, K + kvbase, 0, L, w, lane);
+    load_tile<D, 4>(lds + 3 * TILE_BYTES, V + kvbase, 0, L, w, lane);
     const KeyWindow win{wl, wr, bottom_right ? L - n : 0, L};
     float* sl = reinterpret_cast<float*>(lds + 4 * TILE_BYTES);
     float* sdd = sl + 64;
 
-    TileAddr ta;
+    TileAddr<D> ta;
     ta.init(lane);
     const uint32_t l0 = lds_u32(lds);
     const uint32_t sq = l0, sdo = l0 + TILE_BYTES, sk = l0 + 2 * TILE_BYTES, sv = l0 + 3 * TILE_BYTES;
@@ -518,8 +562,8 @@ __global__ __launch_bounds__(256) void sdpa_bwd_short_bf16(
     float dsum = 0.f, lc = 0.f;
     if (w >= 2) {
         bf16x8 oop[4], dop[4];
-        load_row_operand(O + qbase + (size_t)qrow * D, qok, hf, oop);
-        load_row_operand(dO + qbase + (size_t)qrow * D, qok, hf, dop);
+        load_row_operand<D>(O + qbase + (size_t)qrow * D, qok, hf, oop);
+        load_row_operand<D>(dO + qbase + (size_t)qrow * D, qok, hf, dop);
         float acc = 0.f;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
@@ -554,7 +598,7 @@ __global__ __launch_bounds__(256) void sdpa_bwd_short_bf16(
             }
         }
         f32x16 s[2], dp[2];
-        row_products(sk, sv, ta, qop, dop, s, dp);
+        row_products<D, true>(sk, sv, ta, qop, dop, s, dp);
         const int llo = win.lo32(qrow) - 4 * hf, lhi = win.hi32(qrow) - 4 * hf;
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
@@ -571,8 +615,8 @@ __global__ __launch_bounds__(256) void sdpa_bwd_short_bf16(
         f32x16 acc[2];
 #pragma unroll
         for (int i = 0; i < 16; ++i) { acc[0][i] = 0.f; acc[1][i] = 0.f; }
-        tr_product(sk, ta, db, acc);
-        if (qok) store_rowT(dQ + qbase + (size_t)qrow * D, acc, hf, scale);
+        tr_product<D>(sk, ta, db, acc);
+        if (qok) store_rowT<D>(dQ + qbase + (size_t)qrow * D, acc, hf, scale);
     } else {
         // S = Q Kᵀ, dP = dO Vᵀ over the 64 queries; dVᵀ += dOᵀ P, dKᵀ += Qᵀ dS.
         const int key = 32 * w + l32;
@@ -592,7 +636,7 @@ __global__ __launch_bounds__(256) void sdpa_bwd_short_bf16(
             }
         }
         f32x16 s[2], dp[2];
-        row_products(sq, sdo, ta, kop, vop, s, dp);
+        row_products<D, true>(sq, sdo, ta, kop, vop, s, dp);
         const QueryRange qr{wl, wr, bottom_right ? L - n : 0, L, n};
         const int llo = qr.qa(key) - 4 * hf, lhi = qr.qb(key) - 4 * hf;
         u32x4 lv[8], dv4[8];
@@ -627,11 +671,11 @@ __global__ __launch_bounds__(256) void sdpa_bwd_short_bf16(
         f32x16 dka[2], dva[2];
 #pragma unroll
         for (int i = 0; i < 16; ++i) { dka[0][i] = 0.f; dka[1][i] = 0.f; dva[0][i] = 0.f; dva[1][i] = 0.f; }
-        tr_product(sdo, ta, pb, dva);
-        tr_product(sq, ta, db, dka);
+        tr_product<D>(sdo, ta, pb, dva);
+        tr_product<D>(sq, ta, db, dka);
         if (key < m) {
-            store_rowT(dK + kvbase + (size_t)key * D, dka, hf, scale);
-            store_rowT(dV + kvbase + (size_t)key * D, dva, hf, 1.f);
+            store_rowT<D>(dK + kvbase + (size_t)key * D, dka, hf, scale);
+            store_rowT<D>(dV + kvbase + (size_t)key * D, dva, hf, 1.f);
         }
     }
 }
@@ -640,13 +684,55 @@ __global__ __launch_bounds__(256) void sdpa_bwd_short_bf16(
 
 size_t bwd_workspace_bytes(int B, int H, int n) { return 2 * (((size_t)B * H * n * 4 + 255) & ~(size_t)255); }
 
+namespace {
+
+template <int D, int NW>
+hipError_t launch_bwd_width(const BwdArgs& a, hipStream_t stream, float c_log2, float* ws_d, float* ws_l) {
+    const int BH = a.B * a.H;
+    const int nqb = (a.n + 32 * NW - 1) / (32 * NW);
+    hipLaunchKernelGGL((sdpa_bwd_dq_bf16<D, NW>), dim3(nqb * BH), dim3(NW * 64), 0, stream,
+                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                       (const uint16_t*)a.out, (const uint16_t*)a.dout, a.lse, (uint16_t*)a.dq,
+                       ws_d, ws_l, BH, a.H, a.n, a.m, a.scale, c_log2, a.wl, a.wr, a.bottom_right,
+                       a.key_lens, nqb);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const dim3 grid(((a.m + 32 * NW - 1) / (32 * NW)) * BH);
+    if constexpr (D <= 64) {
+        hipLaunchKernelGGL((sdpa_bwd_dkdv_bf16<D, NW, true, true>), grid, dim3(NW * 64), 0, stream,
+                           (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                           (const uint16_t*)a.dout, ws_d, ws_l, (uint16_t*)a.dk, (uint16_t*)a.dv, BH, a.H,
+                           a.n, a.m, a.scale, c_log2, a.wl, a.wr, a.bottom_right, a.key_lens);
+    } else {
+        hipLaunchKernelGGL((sdpa_bwd_dkdv_bf16<D, NW, true, false>), grid, dim3(NW * 64), 0, stream,
+                           (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                           (const uint16_t*)a.dout, ws_d, ws_l, (uint16_t*)a.dk, (uint16_t*)a.dv, BH, a.H,
+                           a.n, a.m, a.scale, c_log2, a.wl, a.wr, a.bottom_right, a.key_lens);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((sdpa_bwd_dkdv_bf16<D, NW, false, true>), grid, dim3(NW * 64), 0, stream,
+                           (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                           (const uint16_t*)a.dout, ws_d, ws_l, (uint16_t*)a.dk, (uint16_t*)a.dv, BH, a.H,
+                           a.n, a.m, a.scale, c_log2, a.wl, a.wr, a.bottom_right, a.key_lens);
+    }
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream, float c_log2, float* ws_d, float* ws_l) {
+    // 4 waves per workgroup once there are enough query blocks to fill the chip.
+    if ((long long)a.B * a.H * ((a.n + 127) / 128) >= 1024) return launch_bwd_width<D, 4>(a, stream, c_log2, ws_d, ws_l);
+    return launch_bwd_width<D, 2>(a, stream, c_log2, ws_d, ws_l);
+}
+
+}  // namespace
+
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
     const int BH = a.B * a.H;
     const float c_log2 = (float)((double)a.scale * 1.4426950408889634);  // scale·log2(e)
     float* ws_d = static_cast<float*>(a.workspace);
     float* ws_l = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + bwd_workspace_bytes(a.B, a.H, a.n) / 2);
-    // 4 waves per workgroup once there are enough blocks to fill the chip.
-    if (a.n <= 64 && a.m <= 64) {
+    if (a.d == kHeadDim && a.n <= 64 && a.m <= 64) {
         hipLaunchKernelGGL(sdpa_bwd_short_bf16, dim3(BH), dim3(256), 0, stream, (const uint16_t*)a.q,
                            (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.out,
                            (const uint16_t*)a.dout, a.lse, (uint16_t*)a.dq, (uint16_t*)a.dk,
@@ -654,37 +740,9 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
                            a.key_lens);
         return hipGetLastError();
     }
-    const long long qblocks4 = (long long)BH * ((a.n + 127) / 128);
-    if (qblocks4 >= 1024) {
-        const int nqb = (a.n + 127) / 128;
-        hipLaunchKernelGGL(sdpa_bwd_dq_bf16<4>, dim3(nqb * BH), dim3(256), 0, stream,
-                           (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                           (const uint16_t*)a.out, (const uint16_t*)a.dout, a.lse, (uint16_t*)a.dq,
-                           ws_d, ws_l, BH, a.H, a.n, a.m, a.scale, c_log2, a.wl, a.wr, a.bottom_right,
-                           a.key_lens, nqb);
-    } else {
-        const int nqb = (a.n + 63) / 64;
-        hipLaunchKernelGGL(sdpa_bwd_dq_bf16<2>, dim3(nqb * BH), dim3(128), 0, stream,
-                           (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                           (const uint16_t*)a.out, (const uint16_t*)a.dout, a.lse, (uint16_t*)a.dq,
-                           ws_d, ws_l, BH, a.H, a.n, a.m, a.scale, c_log2, a.wl, a.wr, a.bottom_right,
-                           a.key_lens, nqb);
-    }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const long long kblocks4 = (long long)BH * ((a.m + 127) / 128);
-    if (kblocks4 >= 1024) {
-        hipLaunchKernelGGL(sdpa_bwd_dkdv_bf16<4>, dim3(((a.m + 127) / 128) * BH), dim3(256), 0, stream,
-                           (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                           (const uint16_t*)a.dout, ws_d, ws_l, (uint16_t*)a.dk, (uint16_t*)a.dv, BH, a.H,
-                           a.n, a.m, a.scale, c_log2, a.wl, a.wr, a.bottom_right, a.key_lens);
-    } else {
-        hipLaunchKernelGGL(sdpa_bwd_dkdv_bf16<2>, dim3(((a.m + 63) / 64) * BH), dim3(128), 0, stream,
-                           (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                           (const uint16_t*)a.dout, ws_d, ws_l, (uint16_t*)a.dk, (uint16_t*)a.dv, BH, a.H,
-                           a.n, a.m, a.scale, c_log2, a.wl, a.wr, a.bottom_right, a.key_lens);
-    }
-    return hipGetLastError();
+    if (a.d == 32) return launch_bwd_d<32>(a, stream, c_log2, ws_d, ws_l);
+    if (a.d == 128) return launch_bwd_d<128>(a, stream, c_log2, ws_d, ws_l);
+    return launch_bwd_d<64>(a, stream, c_log2, ws_d, ws_l);
 }
 
 }  // namespace sdpa

@@ -105,6 +105,7 @@ struct BwdArgs {
     float scale;
     int wl, wr, bottom_right;
     const int32_t* key_lens;
+    int d = kHeadDim;  // head width d_k = d_v: 32, 64 or 128
 };
 size_t bwd_workspace_bytes(int B, int H, int n);
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream);
