@@ -1,0 +1,67 @@
+"""The C ABI from C: include/sdpa.h compiles as C99 with warnings as errors,
+and a C program linked against libsdpa.so gets the documented statuses from
+the host-side validation (no GPU call is reached, so this runs on the CPU)."""
+
+import os
+import shutil
+import subprocess
+
+import pytest
+
+from transformer_attention_sdpa_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+C_PROGRAM = r"""
+#include <stdio.h>
+#include <string.h>
+#include "sdpa.h"
+
+#define CHECK(expr, want) do { int got_ = (expr); if (got_ != (want)) { \
+    printf("FAIL %s: got %d want %d\n", #expr, got_, (want)); return 1; } } while (0)
+
+int main(void) {
+    /* fake, 16-byte aligned device addresses: validation rejects before any HIP call */
+    char* base = (char*)0 + (1 << 20);
+    const void* q = base; const void* k = base + (1 << 20); const void* v = base + (2 << 20);
+    void* out = base + (3 << 20);
+    CHECK(sdpa_forward(NULL, k, v, out, 2, 2, 8, 8, 64, 64, 0.125f, SDPA_MASK_NONE, NULL, SDPA_BF16, NULL),
+          SDPA_ERR_NULL);
+    CHECK(sdpa_forward(q, k, v, out, 2, 2, 8, 9, 64, 64, 0.125f, SDPA_MASK_CAUSAL, NULL, SDPA_BF16, NULL),
+          SDPA_ERR_MASK);
+    CHECK(sdpa_forward(q, k, v, out, 2, 2, 8, 8, 16, 16, 0.125f, SDPA_MASK_NONE, NULL, SDPA_BF16, NULL),
+          SDPA_ERR_UNSUPPORTED);
+    CHECK(sdpa_forward_window(q, k, v, out, 2, 2, 8, 8, 64, 64, 0.125f, -2, 0, SDPA_ALIGN_TOP_LEFT, NULL,
+                              SDPA_BF16, NULL), SDPA_ERR_MASK);
+    CHECK(sdpa_forward_lse(q, k, v, out, (float*)(base + (4 << 20)), 2, 2, 8, 8, 64, 64, 0.125f, -1, -1,
+                           SDPA_ALIGN_TOP_LEFT, NULL, SDPA_F32, NULL), SDPA_ERR_UNSUPPORTED);
+    CHECK(sdpa_backward(q, k, v, out, base + (5 << 20), (const float*)(base + (6 << 20)), base + (7 << 20),
+                        base + (8 << 20), base + (9 << 20), 2, 2, 8, 8, 64, 64, 0.125f, -1, -1,
+                        SDPA_ALIGN_TOP_LEFT, NULL, SDPA_BF16, base + (10 << 20), 16, NULL), SDPA_ERR_WORKSPACE);
+    if (sdpa_backward_workspace_bytes(1, 1, 3) != 512) { printf("FAIL workspace size\n"); return 1; }
+    if (sdpa_mha_workspace_bytes(1, 3, 5, 1, 64, 64) != 2 * 512 + 2 * 768) { printf("FAIL mha size\n"); return 1; }
+    if (sdpa_forward_workspace_bytes(32, 8, 1, 1024, 64, 64, SDPA_BF16) != 0) { printf("FAIL fwd size\n"); return 1; }
+    if (sdpa_version() < 10300) { printf("FAIL version %d\n", sdpa_version()); return 1; }
+    if (strcmp(sdpa_strerror(SDPA_OK), "ok") != 0) { printf("FAIL strerror\n"); return 1; }
+    if (sdpa_strerror(-1234) == NULL) { printf("FAIL strerror NULL\n"); return 1; }
+    printf("c abi ok\n");
+    return 0;
+}
+"""
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc not installed")
+def test_header_is_c99_and_the_library_links_from_c(tmp_path):
+    lib = _lib.LIB_PATH
+    if not os.path.exists(lib):
+        pytest.skip("libsdpa.so is not built")
+    src = tmp_path / "abi.c"
+    src.write_text(C_PROGRAM)
+    exe = tmp_path / "abi"
+    cmd = ["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic", "-Wno-pointer-arith",
+           f"-I{os.path.join(ROOT, 'include')}", str(src), lib, f"-Wl,-rpath,{os.path.dirname(lib)}",
+           "-o", str(exe)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    run = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert run.returncode == 0 and "c abi ok" in run.stdout, run.stdout + run.stderr
