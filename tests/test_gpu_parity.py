@@ -519,6 +519,29 @@ def test_decode_kernel_parity(gpu_lib, n, m):
     print(f"decode kernel n={n} m={m}: max abs err {worst:.3e}")
 
 
+@pytest.mark.parametrize("n", [1, 4, 16])
+def test_decode_two_heads_per_workgroup(gpu_lib, n):
+    """Short caches over many heads take two heads per workgroup; an odd head
+    count (1025) leaves the last workgroup half empty.  Every decode window,
+    ragged lengths including 0, 1 and m."""
+    rng = np.random.default_rng(91 + n)
+    B, h, m = 1025, 1, 200
+    kl = rng.integers(0, m + 1, size=B).astype(np.int32)
+    kl[:4] = [0, 1, m, 33]
+    kl[-1] = m
+    base = random_case(rng, B, h, n, m, 64, 64, dtype="bf16", key_lens=kl)
+    worst = 0.0
+    for win in DECODE_WINDOWS:
+        case = dict(base, window=win)
+        _, got = run_gpu(case)
+        ref = _oracle(case)
+        err = max_abs_err(got, ref)
+        worst = max(worst, err)
+        assert err <= TOL["bf16"], (win, err)
+        assert np.all(got[0] == 0.0)
+    print(f"decode two heads per workgroup n={n}: max abs err {worst:.3e}")
+
+
 @pytest.mark.parametrize("name", ["decode_beam_base", "decode_long_cache"])
 def test_decode_workloads_full_parity(gpu_lib, name):
     case = make_inputs(name, "bf16")
