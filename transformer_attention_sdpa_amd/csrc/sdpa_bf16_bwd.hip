@@ -201,6 +201,34 @@ __device__ __forceinline__ void store_rowT(uint16_t* dst, const f32x16 (&acc)[D 
         }
 }
 
+// Store 32 output rows through a wave-private 4 KiB LDS area: the transposed
+// accumulators (register i of acc[dt] is column 32·dt + 8·(i/4) + 4·hf + i%4
+// of row l32) go in as bf16 times `mul`, and come out 16 bytes a lane, so
+// that each store instruction writes eight whole 128-byte rows instead of 32
+// scattered 16-byte pieces.  Rows at or past `nrows` are not written.
+__device__ __forceinline__ void store_rows_lds(char* area, const f32x16 (&acc)[2], int lane, float mul,
+                                               uint16_t* dst, int nrows) {
+    const int l32 = lane & 31, hf = lane >> 5;
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+            const int col = 32 * dt + 8 * i4 + 4 * hf;
+            bf16x4 o;
+            o[0] = (__bf16)(acc[dt][4 * i4 + 0] * mul);
+            o[1] = (__bf16)(acc[dt][4 * i4 + 1] * mul);
+            o[2] = (__bf16)(acc[dt][4 * i4 + 2] * mul);
+            o[3] = (__bf16)(acc[dt][4 * i4 + 3] * mul);
+            *reinterpret_cast<bf16x4*>(area + lds_swz(l32, col >> 3) * 16 + (col & 7) * 2) = o;
+        }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int row = 8 * k + (lane >> 3), c = lane & 7;
+        const u32x4 x = *reinterpret_cast<const u32x4*>(area + lds_swz(row, c) * 16);
+        if (row < nrows) store16_nt(dst + (size_t)row * kHeadDim + 8 * c, x);
+    }
+}
+
 // Copy rows [r0, r0 + 64) of a [len, D] bf16 tensor into an LDS tile; rows
 // at or past `len` arrive as zeros.  Wave w of NW issues its share of the
 // tile's 1 KiB loads; lane ln lands in (row ln/CPR, position ln%CPR) of the
@@ -580,6 +608,7 @@ __global__ __launch_bounds__(256) void sdpa_bwd_short_bf16(
     wait_vmem();
     __syncthreads();
 
+    f32x16 acc_a[2], acc_b[2];  // dQᵀ (waves 2, 3), or dKᵀ and dVᵀ (waves 0, 1)
     if (w >= 2) {
         // Sᵀ = K Qᵀ, dPᵀ = V dOᵀ over the 64 keys; dQᵀ += Kᵀ dSᵀ.
         bf16x8 qop[4], dop[4];
@@ -612,11 +641,9 @@ __global__ __launch_bounds__(256) void sdpa_bwd_short_bf16(
         bf16x8 db[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) db[j] = pack_step(s, j);
-        f32x16 acc[2];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) { acc[0][i] = 0.f; acc[1][i] = 0.f; }
-        tr_product<D>(sk, ta, db, acc);
-        if (qok) store_rowT<D>(dQ + qbase + (size_t)qrow * D, acc, hf, scale);
+        for (int i = 0; i < 16; ++i) { acc_a[0][i] = 0.f; acc_a[1][i] = 0.f; }
+        tr_product<D>(sk, ta, db, acc_a);  // dQᵀ
     } else {
         // S = Q Kᵀ, dP = dO Vᵀ over the 64 queries; dVᵀ += dOᵀ P, dKᵀ += Qᵀ dS.
         const int key = 32 * w + l32;
@@ -668,15 +695,22 @@ __global__ __launch_bounds__(256) void sdpa_bwd_short_bf16(
             pb[j] = pack_step(s, j);
             db[j] = pack_step(dp, j);
         }
-        f32x16 dka[2], dva[2];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) { dka[0][i] = 0.f; dka[1][i] = 0.f; dva[0][i] = 0.f; dva[1][i] = 0.f; }
-        tr_product<D>(sdo, ta, pb, dva);
-        tr_product<D>(sq, ta, db, dka);
-        if (key < m) {
-            store_rowT<D>(dK + kvbase + (size_t)key * D, dka, hf, scale);
-            store_rowT<D>(dV + kvbase + (size_t)key * D, dva, hf, 1.f);
-        }
+        for (int i = 0; i < 16; ++i) { acc_a[0][i] = 0.f; acc_a[1][i] = 0.f; acc_b[0][i] = 0.f; acc_b[1][i] = 0.f; }
+        tr_product<D>(sdo, ta, pb, acc_b);  // dVᵀ
+        tr_product<D>(sq, ta, db, acc_a);   // dKᵀ
+    }
+    // Every wave is done with the tiles: their space now stages the outputs
+    // (wave w < 2: dK at 8 KiB·w, dV 4 KiB further; waves 2, 3: dQ at 16 KiB + 4 KiB·(w − 2)).
+    __syncthreads();
+    if (w >= 2) {
+        const int r0 = 32 * (w - 2);
+        store_rows_lds(lds + 4 * TILE_BYTES / 2 + (w - 2) * 4096, acc_a, lane, scale,
+                       dQ + qbase + (size_t)r0 * D, n - r0);
+    } else {
+        const int r0 = 32 * w;
+        store_rows_lds(lds + w * 8192, acc_a, lane, scale, dK + kvbase + (size_t)r0 * D, m - r0);
+        store_rows_lds(lds + w * 8192 + 4096, acc_b, lane, 1.f, dV + kvbase + (size_t)r0 * D, m - r0);
     }
 }
 
