@@ -225,39 +225,49 @@ __global__ __launch_bounds__(256) void proj_gemm_bf16(ProjJobs jobs) {
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
     compute(nst - 1);
 
-    // Register r of acc[i][j] is feature 32·j + 8·(r/4) + 4·hf + r%4 (of the
-    // wave's feature block) of token 32·i + l32 (of its token block): four
-    // consecutive features per 8-byte store.
+    // The output tile goes through LDS (the stage buffers are free once every
+    // wave is past its last reads), so that the stores write 16 bytes a lane
+    // along rows instead of 8-byte pieces of 32 different rows.  Register r of
+    // acc[i][j] is feature 32·j + 8·(r/4) + 4·hf + r%4 (of the wave's feature
+    // block) of token 32·i + l32 (of its token block); the tile row of a token
+    // holds TN features, 16-byte chunk c at position c ^ (row mod CPR).
+    constexpr int CPR = TN / 8;
+    __syncthreads();
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
-        const int tok = t0 + 32 * MT * wm + 32 * i + l32;
-        if (tok >= J.M) continue;
-        size_t cbase;
-        int chead_stride = 0;
-        if (CMODE == ROWS) {
-            cbase = (size_t)tok * J.N;
-        } else {
-            const int b = tok / J.len, ii = tok - b * J.len;
-            cbase = ((size_t)b * (J.N / J.hd) * J.len + ii) * J.hd;
-            chead_stride = J.len * J.hd;
-        }
+        const int row = 32 * MT * wm + 32 * i + l32;
 #pragma unroll
-        for (int j = 0; j < NT; ++j) {
-            const int fb = f0 + 32 * NT * wn + 32 * j;
-            if (fb >= J.N) continue;  // N is a multiple of 64: whole 32-feature blocks
+        for (int j = 0; j < NT; ++j)
 #pragma unroll
             for (int i4 = 0; i4 < 4; ++i4) {
-                const int f = fb + 8 * i4 + 4 * hf;
-                const size_t dst = CMODE == ROWS ? cbase + f
-                                                 : cbase + (size_t)(f / J.hd) * chead_stride + (f % J.hd);
+                const int col = 32 * NT * wn + 32 * j + 8 * i4 + 4 * hf;
                 bf16x4 o;
                 o[0] = (__bf16)acc[i][j][4 * i4 + 0];
                 o[1] = (__bf16)acc[i][j][4 * i4 + 1];
                 o[2] = (__bf16)acc[i][j][4 * i4 + 2];
                 o[3] = (__bf16)acc[i][j][4 * i4 + 3];
-                *reinterpret_cast<bf16x4*>(J.c + dst) = o;
+                const int pos = (col >> 3) ^ (row & (CPR - 1));
+                *reinterpret_cast<bf16x4*>(lds + (row * CPR + pos) * 16 + (col & 7) * 2) = o;
             }
+    }
+    __syncthreads();
+    // Thread t stores chunks t, t + 256, …: token row id / CPR, features 8·(id % CPR) .. +7.
+#pragma unroll
+    for (int k = 0; k < TM * CPR / 256; ++k) {
+        const int id = tid + 256 * k;
+        const int row = id / CPR, c = id % CPR;
+        const int tok = t0 + row, f = f0 + 8 * c;
+        const u32x4 x = *reinterpret_cast<const u32x4*>(lds + (row * CPR + (c ^ (row & (CPR - 1)))) * 16);
+        if (tok >= J.M || f >= J.N) continue;
+        size_t dst;
+        if (CMODE == ROWS) {
+            dst = (size_t)tok * J.N + f;
+        } else {
+            // eight features inside one head: hd is 32, 64 or 128
+            const int b = tok / J.len, ii = tok - b * J.len;
+            dst = (((size_t)b * (J.N / J.hd) + f / J.hd) * J.len + ii) * J.hd + (f % J.hd);
         }
+        *reinterpret_cast<u32x4*>(J.c + dst) = x;
     }
 }
 
