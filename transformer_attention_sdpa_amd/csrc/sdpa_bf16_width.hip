@@ -246,23 +246,35 @@ __global__ __launch_bounds__(NW * 64) void sdpa_fwd_bf16_width(
     const float ltot = half_swap_sum(lsum);
     // no legal key ⇒ zero row; a NaN sum (NaN legal inputs) stays NaN
     const float inv = ltot != 0.f ? 1.f / ltot : 0.f;
-    if (qok) {
-        if (lse && hf == 0) {
-            const float mc = (mref == -INFINITY ? 0.f : mref) * c_log2;
-            lse[(size_t)bh * n + qrow] = (mc + log2f(ltot)) * 0.6931471805599453f;
+    if (qok && lse && hf == 0) {
+        const float mc = (mref == -INFINITY ? 0.f : mref) * c_log2;
+        lse[(size_t)bh * n + qrow] = (mc + log2f(ltot)) * 0.6931471805599453f;
+    }
+    // The output rows go through a wave-private LDS area (the tiles are free:
+    // every wave passed the loop's last barrier after its last read), so that
+    // the stores write 16 bytes a lane along rows.  Register i of oacc[dt] is
+    // dim 32·dt + 8·(i/4) + 4·hf + i%4 of row l32; 16-byte chunk c of a row
+    // sits at position c ^ (row mod CPR).
+    char* area = lds + w * 32 * D * 2;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+            const int col = 32 * dt + 8 * i4 + 4 * hf;
+            bf16x4 o;
+            o[0] = (__bf16)(oacc[dt][4 * i4 + 0] * inv);
+            o[1] = (__bf16)(oacc[dt][4 * i4 + 1] * inv);
+            o[2] = (__bf16)(oacc[dt][4 * i4 + 2] * inv);
+            o[3] = (__bf16)(oacc[dt][4 * i4 + 3] * inv);
+            const int pos = (col >> 3) ^ (l32 & (CPR - 1));
+            *reinterpret_cast<bf16x4*>(area + (l32 * CPR + pos) * 16 + (col & 7) * 2) = o;
         }
-        uint16_t* dst = O + qbase + (size_t)qrow * D;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-            for (int i4 = 0; i4 < 4; ++i4) {
-                bf16x4 o;
-                o[0] = (__bf16)(oacc[dt][4 * i4 + 0] * inv);
-                o[1] = (__bf16)(oacc[dt][4 * i4 + 1] * inv);
-                o[2] = (__bf16)(oacc[dt][4 * i4 + 2] * inv);
-                o[3] = (__bf16)(oacc[dt][4 * i4 + 3] * inv);
-                *reinterpret_cast<bf16x4*>(dst + 32 * dt + 8 * i4 + 4 * hf) = o;
-            }
+    for (int k = 0; k < CPR / 2; ++k) {
+        const int id = lane + 64 * k;
+        const int row = id / CPR, c = id % CPR;
+        const u32x4 x = *reinterpret_cast<const u32x4*>(area + (row * CPR + (c ^ (row & (CPR - 1)))) * 16);
+        if (wq0 + row < n) store16_nt(O + qbase + (size_t)(wq0 + row) * D + 8 * c, x);
     }
 }
 
