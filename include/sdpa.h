@@ -68,8 +68,13 @@ extern "C" {
  * out      device pointer, [B, h, n, d_v], contiguous; written completely (rows
  *          with no legal key are written as zeros).  Must not overlap q, k, v, key_lens.
  * B, h     batch size and number of heads (>= 1).
- * n, m     number of queries and of keys/values per head (>= 1).
- * d_k, d_v query/key and value widths; the library supports d_k == d_v == 64.
+ * n, m     number of queries and of keys/values per head (>= 1).  One head's
+ *          rows of any of the four tensors must span less than 2^31 bytes
+ *          (n·d·size and m·d·size; the kernels use 32-bit offsets within a
+ *          head), else SDPA_ERR_SHAPE.
+ * d_k, d_v query/key and value widths: d_k == d_v == 64 for both dtypes; for
+ *          SDPA_BF16 also d_k == d_v == 32 or 128 (the model variants of
+ *          《精读 Attention Is All You Need：原始 Transformer 论文》 Table 3).
  * scale    multiplier of the dot products; pass 1/sqrt(d_k) for Eq. (1).  Must
  *          be finite and > 0 (scale = 1 runs the unscaled dot-product form).
  * mask_kind SDPA_MASK_NONE or SDPA_MASK_CAUSAL.

@@ -69,6 +69,10 @@ def call(q=P, k=2 * P, v=3 * P, out=4 * P, B=2, h=2, n=8, m=8, d_k=64, d_v=64, s
     (dict(n=0), _lib.SDPA_ERR_SHAPE),
     (dict(m=0), _lib.SDPA_ERR_SHAPE),
     (dict(B=1 << 20, h=1 << 10, n=1 << 20), _lib.SDPA_ERR_SHAPE),
+    # one head's rows reach 2^31 bytes (32-bit offsets within a head)
+    (dict(B=1, h=1, n=1, m=1 << 24), _lib.SDPA_ERR_SHAPE),
+    (dict(B=1, h=1, n=1 << 23, m=8, d_k=128, d_v=128), _lib.SDPA_ERR_SHAPE),
+    (dict(B=1, h=1, n=1, m=1 << 23, dtype=0), _lib.SDPA_ERR_SHAPE),
     (dict(d_k=32, d_v=32, dtype=0), _lib.SDPA_ERR_UNSUPPORTED),  # other widths: bf16 only
     (dict(d_k=16, d_v=16), _lib.SDPA_ERR_UNSUPPORTED),
     (dict(d_k=96, d_v=96), _lib.SDPA_ERR_UNSUPPORTED),

@@ -36,13 +36,17 @@ int validate(const void* q, const void* k, const void* v, void* out, int32_t B, 
     const uint64_t width = (uint64_t)(d_k > d_v ? d_k : d_v);
     if (heads * rows * width >= (1ull << 48)) return SDPA_ERR_SHAPE;
     if (heads * (((uint64_t)n + 31) / 32) >= (1ull << 31)) return SDPA_ERR_SHAPE;
+    // The kernels address a head's rows with 32-bit byte offsets (buffer ranges
+    // run from a tile to the end of its head): one head's Q, K, V or output
+    // rows stay below 2 GiB.
+    const uint64_t esz = dtype == SDPA_F32 ? 4 : 2;
+    if (rows * width * esz >= (1ull << 31)) return SDPA_ERR_SHAPE;
     // Head widths: 64 for both dtypes; 32 and 128 (d_k = d_v) for bf16.
     const bool wide_ok = dtype == SDPA_BF16 && d_k == d_v && (d_k == 32 || d_k == 128);
     if (!(d_k == sdpa::kHeadDim && d_v == sdpa::kHeadDim) && !wide_ok) return SDPA_ERR_UNSUPPORTED;
     if (!std::isfinite(scale) || !(scale > 0.f)) return SDPA_ERR_SCALE;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return SDPA_ERR_ALIGN;
     if (key_lens && (reinterpret_cast<uintptr_t>(key_lens) & 3u)) return SDPA_ERR_ALIGN;
-    const uint64_t esz = dtype == SDPA_F32 ? 4 : 2;
     const uint64_t qb = heads * n * d_k * esz, kb = heads * m * d_k * esz;
     const uint64_t vb = heads * m * d_v * esz, ob = heads * n * d_v * esz;
     if (overlap(out, ob, q, qb) || overlap(out, ob, k, kb) || overlap(out, ob, v, vb))
