@@ -30,12 +30,13 @@ int validate(const void* q, const void* k, const void* v, void* out, int32_t B, 
     if (dtype != SDPA_F32 && dtype != SDPA_BF16) return SDPA_ERR_DTYPE;
     if (B < 1 || h < 1 || n < 1 || m < 1 || d_k < 1 || d_v < 1) return SDPA_ERR_SHAPE;
     // Element counts and the launch grid must stay well inside 64-bit offsets and
-    // a 31-bit grid: B·h·max(n, m)·max(d) < 2^48 and B·h·⌈n/32⌉ < 2^31.
+    // a 31-bit grid (blocks of at least 32 queries or keys per head):
+    // B·h·max(n, m)·max(d) < 2^48 and B·h·⌈max(n, m)/32⌉ < 2^31.
     const uint64_t heads = (uint64_t)B * (uint64_t)h;
     const uint64_t rows = (uint64_t)(n > m ? n : m);
     const uint64_t width = (uint64_t)(d_k > d_v ? d_k : d_v);
     if (heads * rows * width >= (1ull << 48)) return SDPA_ERR_SHAPE;
-    if (heads * (((uint64_t)n + 31) / 32) >= (1ull << 31)) return SDPA_ERR_SHAPE;
+    if (heads * ((rows + 31) / 32) >= (1ull << 31)) return SDPA_ERR_SHAPE;
     // The kernels address a head's rows with 32-bit byte offsets (buffer ranges
     // run from a tile to the end of its head): one head's Q, K, V or output
     // rows stay below 2 GiB.
