@@ -203,10 +203,11 @@ SDPA_API int sdpa_forward_lse(const void* q, const void* k, const void* v, void*
  * workspace  NULL, or device scratch of workspace_bytes >= the size
  *            sdpa_forward_workspace_bytes gives, 16-byte aligned, owned by the
  *            caller, overlapping no other argument.  With it, decoder steps
- *            against long key caches (bf16, d = 64, n <= 16, m > 1024,
- *            B·h >= 256) split each head's keys into 1024-key pieces on
- *            separate workgroups and merge the partial softmaxes in a second
- *            launch, which keeps the CUs busy when cache lengths differ.  The
+ *            against long key caches (bf16, d = 64, n <= 16, m > 1024, any
+ *            B·h) split each head's keys into 1024-key pieces on separate
+ *            workgroups and merge the partial softmaxes in a second launch,
+ *            which keeps the CUs busy when there are few heads (one sequence
+ *            decoding alone) or when cache lengths differ.  The
  *            output then differs from the workspace-free call by rounding only
  *            (the fp32 partial sums are added in another order); each path is
  *            deterministic.  A workspace smaller than needed: SDPA_ERR_WORKSPACE.

@@ -28,8 +28,12 @@ def from_device(t) -> np.ndarray:
     return t.detach().to(torch.float32).cpu().numpy().astype(np.float64)
 
 
-def run_gpu(case: dict, scale=None, out=None):
-    """Run the HIP path on a generator case; returns (device out tensor, float64 numpy)."""
+def run_gpu(case: dict, scale=None, out=None, workspace=None):
+    """Run the HIP path on a generator case; returns (device out tensor, float64 numpy).
+
+    Without a workspace (the default here) the call goes through
+    ``sdpa_forward`` / ``sdpa_forward_window``; ``workspace="auto"`` is the
+    binding's own default."""
     import torch
 
     from transformer_attention_sdpa_amd import forward
@@ -40,7 +44,7 @@ def run_gpu(case: dict, scale=None, out=None):
     if case.get("key_lens") is not None:
         kl = torch.from_numpy(np.asarray(case["key_lens"], dtype=np.int32)).cuda()
     o = forward(q, k, v, causal=case.get("causal", False), key_lens=kl, scale=scale, out=out,
-                window=case.get("window"))
+                window=case.get("window"), workspace=workspace)
     torch.cuda.synchronize()
     return o, from_device(o)
 

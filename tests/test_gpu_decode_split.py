@@ -5,7 +5,8 @@ A decoder step asks a few new queries against the cached keys of its
 sequence (《注意力就是你所需要的一切》 §3.1: the decoder consumes its own
 earlier outputs), bottom-right aligned.  With ragged cache lengths one
 workgroup per head leaves CUs idle; the split path gives every 1024-key piece
-its own workgroup.  Bar: bf16, 2e-2 absolute; the log-sum-exp within 2^-8;
+its own workgroup; with few heads (one sequence decoding alone) it is the
+only path that spreads a head over several CUs.  Bar: bf16, 2e-2 absolute; the log-sum-exp within 2^-8;
 the split and unsplit paths agree within the same bar.
 """
 
@@ -26,6 +27,10 @@ CASES = [  # id, (B, h, n, m), key lengths, window
     ("window_100", (32, 8, 4, 4100), (0, 4100), (100, 0, "bottom_right")),
     ("two_splits_exactly", (32, 8, 2, 2048), None, BR),
     ("full_no_mask", (16, 16, 3, 1500), (1500, 1500), None),
+    # fewer than 256 heads: without a workspace the long kernel serves these
+    ("one_sequence_8_heads", (1, 8, 1, 20000), (20000, 20000), BR),
+    ("one_head_16q_ragged_tail", (1, 1, 16, 5000), (4321, 4321), BR),
+    ("two_sequences_window", (2, 4, 2, 9000), (3000, 9000), (500, 0, "bottom_right")),
 ]
 
 
@@ -94,3 +99,25 @@ def test_split_decode_deterministic(gpu_lib):
     a = _run(c, True)
     b = _run(c, True)
     assert np.array_equal(a, b)
+
+
+def test_auto_workspace_splits_only_for_few_heads(gpu_lib):
+    """forward()'s default workspace="auto" takes the split path below 256
+    heads (bit-identical to an explicit workspace) and the unsplit one from
+    256 heads on (bit-identical to no workspace)."""
+    import torch
+
+    from transformer_attention_sdpa_amd import forward
+
+    for i in (5, 0):  # 8 heads, then 256 heads
+        c = _case(i)
+        q, k, v = (to_device(c[x], "bf16") for x in ("q", "k", "v"))
+        kl = torch.from_numpy(c["key_lens"]).cuda()
+        auto = forward(q, k, v, key_lens=kl, window=c["window"])
+        torch.cuda.synchronize()
+        split = _run(c, True)
+        plain = _run(c, False)
+        B, h = c["q"].shape[:2]
+        want = split if B * h < 256 else plain
+        assert np.array_equal(from_device(auto), want), CASES[i][0]
+

@@ -193,7 +193,7 @@ def backward(q, k, v, out, dout, lse, *, causal: bool = False, key_lens=None,
 
 
 def forward(q, k, v, *, causal: bool = False, key_lens=None, scale: float | None = None,
-            out=None, window=None, return_lse: bool = False, workspace=None):
+            out=None, window=None, return_lse: bool = False, workspace="auto"):
     """Attention over [B, h, n, d_k] queries and [B, h, m, d] keys/values.
 
     key_lens: None or an int32 tensor [B] on the same device (key j of batch
@@ -205,11 +205,15 @@ def forward(q, k, v, *, causal: bool = False, key_lens=None, scale: float | None
     ``sdpa_forward_window`` in include/sdpa.h.  Not combined with ``causal``.
     Returns ``out`` ([B, h, n, d_v], same dtype as q), or ``(out, lse)`` with
     ``return_lse`` (bf16 only): lse [B, h, n] float32, the natural log of each
-    row's softmax denominator, which ``backward`` takes.  ``workspace``: None,
-    or a uint8 GPU tensor of at least ``sdpa_forward_workspace_bytes(...)``
-    bytes, which lets decoder steps against long caches split each head's keys
-    over several workgroups (see ``sdpa_forward_ex``).  Raises RuntimeError
-    with the library's message on a nonzero status.
+    row's softmax denominator, which ``backward`` takes.  ``workspace``: a
+    uint8 GPU tensor of at least ``sdpa_forward_workspace_bytes(...)`` bytes,
+    which lets decoder steps against long caches split each head's keys over
+    several workgroups (see ``sdpa_forward_ex``); None for no workspace; or
+    "auto" (the default): allocate one when the split applies and there are
+    fewer than 256 heads, where a decoder step would otherwise run one
+    workgroup per head on a mostly idle GPU (with 256 heads or more the two
+    paths measure the same).  Raises RuntimeError with the library's message
+    on a nonzero status.
     """
     import torch
 
@@ -217,6 +221,11 @@ def forward(q, k, v, *, causal: bool = False, key_lens=None, scale: float | None
 
     B, h, n, m, d_k, d_v, dt = _check_qkv(q, k, v)
     key_lens, kl_ptr = _key_lens_ptr(key_lens, B, q.device)
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError('workspace must be a uint8 GPU tensor, None or "auto"')
+        need = sdpa_forward_workspace_bytes(B, h, n, m, d_k, d_v, dt) if B * h < 256 else 0
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device) if need > 0 else None
     if out is None:
         out = torch.empty((B, h, n, d_v), dtype=q.dtype, device=q.device)
     elif (tuple(out.shape) != (B, h, n, d_v) or out.dtype != q.dtype or not out.is_contiguous()

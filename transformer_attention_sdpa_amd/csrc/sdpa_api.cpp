@@ -148,7 +148,7 @@ size_t forward_work_bytes(int32_t B, int32_t h, int32_t n, int32_t m, int32_t d_
     if (B < 1 || h < 1 || n < 1 || m < 1 || dtype != SDPA_BF16) return 0;
     if (d_k != sdpa::kHeadDim || d_v != sdpa::kHeadDim) return 0;
     sdpa::Args a{nullptr, nullptr, nullptr, nullptr, B, h, n, m, 1.f, -1, -1, 0, nullptr};
-    if (sdpa::short_bf16_fits(a) || !sdpa::decode_bf16_fits(a)) return 0;
+    if (sdpa::short_bf16_fits(a)) return 0;
     return sdpa::decode_split_bytes(B, h, n, m);
 }
 

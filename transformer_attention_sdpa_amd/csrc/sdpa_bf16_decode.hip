@@ -392,16 +392,23 @@ constexpr int SPLIT_KEYS = 1024;
 
 int decode_nsplit(int m) { return (m + SPLIT_KEYS - 1) / SPLIT_KEYS; }
 
-bool decode_bf16_fits(const Args& a) {
-    // A few queries against more keys than the sentence-length kernel takes,
-    // and enough heads to give every CU work (one workgroup per head).
-    return a.n <= QN && a.m > 64 && (long long)a.B * a.H >= 256;
-}
-
 size_t decode_split_bytes(int B, int H, int n, int m) {
+    // A few queries against more keys than the sentence-length kernel takes,
+    // spread over at least two 1024-key pieces.
+    if (n > QN || m <= 64) return 0;
     const int ns = decode_nsplit(m);
     if (ns < 2) return 0;
     return (size_t)ns * B * H * n * PREC * sizeof(float);
+}
+
+bool decode_bf16_fits(const Args& a) {
+    if (a.n > QN || a.m <= 64) return false;
+    // One workgroup per head needs enough heads to give every CU work; with a
+    // workspace the split mode gives every 1024-key piece its own workgroup,
+    // so any number of heads (a single sequence's decoder step included) fits.
+    if ((long long)a.B * a.H >= 256) return true;
+    const size_t need = decode_split_bytes(a.B, a.H, a.n, a.m);
+    return a.work && need > 0 && a.work_bytes >= need;
 }
 
 hipError_t launch_bf16_decode(const Args& a, hipStream_t stream) {
