@@ -203,9 +203,11 @@ SDPA_API int sdpa_forward_lse(const void* q, const void* k, const void* v, void*
  * workspace  NULL, or device scratch of workspace_bytes >= the size
  *            sdpa_forward_workspace_bytes gives, 16-byte aligned, owned by the
  *            caller, overlapping no other argument.  With it, decoder steps
- *            against long key caches (bf16, d = 64, n <= 16, m > 1024, any
- *            B·h) split each head's keys into 1024-key pieces on separate
- *            workgroups and merge the partial softmaxes in a second launch,
+ *            against long key caches (bf16, d = 64, n <= 16, any B·h) split
+ *            each head's keys into pieces on separate workgroups (1024 keys,
+ *            or down to 256 with fewer heads, towards 1024 pieces in all;
+ *            only when that gives at least two pieces per head) and merge the
+ *            partial softmaxes in a second launch,
  *            which keeps the CUs busy when there are few heads (one sequence
  *            decoding alone) or when cache lengths differ.  The
  *            output then differs from the workspace-free call by rounding only

@@ -200,13 +200,19 @@ def test_forward_lse_validation_rejects_before_any_hip_call(kw, code, lib):
 
 
 def test_forward_workspace_size(lib):
-    # only decoder steps (n <= 16) against caches past 1024 keys use one, for any
-    # number of heads: ceil(m / 1024) splits × B·h heads × n queries × 68 floats
+    # only decoder steps (n <= 16) use one, for any number of heads, when their keys
+    # fill two pieces: ceil(m / piece) splits × B·h heads × n queries × 68 floats,
+    # pieces of 1024 keys, halved (to 256 at least) while B·h·splits < 1024
     assert _lib.sdpa_forward_workspace_bytes(32, 8, 1, 8192, 64, 64, 1) == 8 * 256 * 1 * 68 * 4
-    assert _lib.sdpa_forward_workspace_bytes(32, 8, 4, 1025, 64, 64, 1) == 2 * 256 * 4 * 68 * 4
-    assert _lib.sdpa_forward_workspace_bytes(32, 8, 1, 1024, 64, 64, 1) == 0  # one split
+    assert _lib.sdpa_forward_workspace_bytes(32, 8, 4, 1025, 64, 64, 1) == 5 * 256 * 4 * 68 * 4  # 256
+    assert _lib.sdpa_forward_workspace_bytes(32, 8, 1, 1024, 64, 64, 1) == 4 * 256 * 1 * 68 * 4  # 256
     assert _lib.sdpa_forward_workspace_bytes(16, 8, 1, 8192, 64, 64, 1) == 8 * 128 * 1 * 68 * 4
-    assert _lib.sdpa_forward_workspace_bytes(1, 1, 16, 3000, 64, 64, 1) == 3 * 1 * 16 * 68 * 4
+    assert _lib.sdpa_forward_workspace_bytes(1, 1, 16, 3000, 64, 64, 1) == 12 * 1 * 16 * 68 * 4  # 256
+    assert _lib.sdpa_forward_workspace_bytes(1, 8, 1, 1000, 64, 64, 1) == 4 * 8 * 1 * 68 * 4  # 256
+    assert _lib.sdpa_forward_workspace_bytes(1, 64, 1, 4096, 64, 64, 1) == 16 * 64 * 1 * 68 * 4  # 256
+    assert _lib.sdpa_forward_workspace_bytes(64, 8, 1, 1000, 64, 64, 1) == 2 * 512 * 1 * 68 * 4  # 512
+    assert _lib.sdpa_forward_workspace_bytes(1, 8, 1, 256, 64, 64, 1) == 0  # one piece
+    assert _lib.sdpa_forward_workspace_bytes(128, 8, 1, 1000, 64, 64, 1) == 0  # one 1024-key piece
     assert _lib.sdpa_forward_workspace_bytes(1, 1, 1, 64, 64, 64, 1) == 0  # sentence-length kernel
     assert _lib.sdpa_forward_workspace_bytes(32, 8, 17, 8192, 64, 64, 1) == 0  # n > 16
     assert _lib.sdpa_forward_workspace_bytes(32, 8, 1, 8192, 64, 64, 0) == 0  # fp32

@@ -4,7 +4,7 @@ workgroups, then merged (``sdpa_forward_ex``), against the fp64 oracle.
 A decoder step asks a few new queries against the cached keys of its
 sequence (《注意力就是你所需要的一切》 §3.1: the decoder consumes its own
 earlier outputs), bottom-right aligned.  With ragged cache lengths one
-workgroup per head leaves CUs idle; the split path gives every 1024-key piece
+workgroup per head leaves CUs idle; the split path gives every piece of keys
 its own workgroup; with few heads (one sequence decoding alone) it is the
 only path that spreads a head over several CUs.  Bar: bf16, 2e-2 absolute; the log-sum-exp within 2^-8;
 the split and unsplit paths agree within the same bar.
@@ -31,6 +31,7 @@ CASES = [  # id, (B, h, n, m), key lengths, window
     ("one_sequence_8_heads", (1, 8, 1, 20000), (20000, 20000), BR),
     ("one_head_16q_ragged_tail", (1, 1, 16, 5000), (4321, 4321), BR),
     ("two_sequences_window", (2, 4, 2, 9000), (3000, 9000), (500, 0, "bottom_right")),
+    ("one_sequence_short_cache", (1, 8, 5, 700), (300, 700), BR),  # 256-key pieces
 ]
 
 

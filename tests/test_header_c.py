@@ -40,7 +40,7 @@ int main(void) {
                         SDPA_ALIGN_TOP_LEFT, NULL, SDPA_BF16, base + (10 << 20), 16, NULL), SDPA_ERR_WORKSPACE);
     if (sdpa_backward_workspace_bytes(1, 1, 3) != 512) { printf("FAIL workspace size\n"); return 1; }
     if (sdpa_mha_workspace_bytes(1, 3, 5, 1, 64, 64) != 2 * 512 + 2 * 768) { printf("FAIL mha size\n"); return 1; }
-    if (sdpa_forward_workspace_bytes(32, 8, 1, 1024, 64, 64, SDPA_BF16) != 0) { printf("FAIL fwd size\n"); return 1; }
+    if (sdpa_forward_workspace_bytes(32, 8, 17, 1024, 64, 64, SDPA_BF16) != 0) { printf("FAIL fwd size\n"); return 1; }
     if (sdpa_version() < 10300) { printf("FAIL version %d\n", sdpa_version()); return 1; }
     if (strcmp(sdpa_strerror(SDPA_OK), "ok") != 0) { printf("FAIL strerror\n"); return 1; }
     if (sdpa_strerror(-1234) == NULL) { printf("FAIL strerror NULL\n"); return 1; }

@@ -330,33 +330,35 @@ __global__ __launch_bounds__(NWD * 64) void sdpa_decode_bf16(
 }  // namespace
 
 // Combine the splits of each (head, query): the usual rescale to the largest
-// maximum.  Thread t: query t % 16, dims 4·(t / 16) .. +3.
+// maximum.  One workgroup per (head, query); thread t takes dims
+// 4·(t % 16) .. +3 of the splits t / 16, t / 16 + 16, ..., and the sixteen
+// partial merges are combined through LDS at the end.
 __global__ __launch_bounds__(NWD * 64) void sdpa_decode_merge_bf16(
     const float* __restrict__ part, uint16_t* __restrict__ O, float* __restrict__ lse, int BH, int n,
     int nsplit, float c_log2) {
-    const int bh = blockIdx.x;
-    const int fq = threadIdx.x & (QN - 1);
-    const int fd = 4 * (threadIdx.x >> 4);
-    if (fq >= n) return;
+    constexpr int SL = NWD * 64 / 16;  // split slots
+    const int bh = blockIdx.x / n, fq = blockIdx.x % n;
+    const int fd = 4 * (threadIdx.x & 15);
+    const int sl = threadIdx.x >> 4;
     const size_t stride = (size_t)BH * n * PREC;  // from one split to the next
     const float* p0 = part + ((size_t)bh * n + fq) * PREC;
-    // Eight splits at a time: all their loads are issued before any use, then
-    // merged into the running (max, sum, O) with the usual rescale.
+    // Four splits per round: all their loads are issued before any use.
     float mx = -INFINITY, lt = 0.f, acc[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < nsplit; s0 += 8) {
-        float ms[8], ls[8];
-        f32x4 os[8];
+    for (int s0 = sl; s0 < nsplit; s0 += 4 * SL) {
+        float ms[4], ls[4];
+        f32x4 os[4];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const bool ok = s0 + u < nsplit;
-            const float* ps = p0 + (size_t)(ok ? s0 + u : 0) * stride;
+        for (int u = 0; u < 4; ++u) {
+            const int sp = s0 + u * SL;
+            const bool ok = sp < nsplit;
+            const float* ps = p0 + (size_t)(ok ? sp : 0) * stride;
             ms[u] = ok ? ps[0] : -INFINITY;
             ls[u] = ok ? ps[1] : 0.f;
             os[u] = ok ? *reinterpret_cast<const f32x4*>(ps + 4 + fd) : f32x4{0.f, 0.f, 0.f, 0.f};
         }
         float mnew = mx;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) mnew = fmaxf(mnew, ms[u]);
+        for (int u = 0; u < 4; ++u) mnew = fmaxf(mnew, ms[u]);
         const float mc = (mnew == -INFINITY ? 0.f : mnew) * c_log2;
         // the old partial and a split with no legal key (max −∞) scale by exactly 0
         const float so = mx == -INFINITY ? 0.f : exp2_hw(mx * c_log2 - mc);
@@ -364,7 +366,7 @@ __global__ __launch_bounds__(NWD * 64) void sdpa_decode_merge_bf16(
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[e] *= so;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < 4; ++u) {
             const float sc = ms[u] == -INFINITY ? 0.f : exp2_hw(ms[u] * c_log2 - mc);
             lt += sc * ls[u];
 #pragma unroll
@@ -372,31 +374,58 @@ __global__ __launch_bounds__(NWD * 64) void sdpa_decode_merge_bf16(
         }
         mx = mnew;
     }
-    const float mcx = (mx == -INFINITY ? 0.f : mx) * c_log2;
+    __shared__ float red_m[SL], red_l[SL];
+    __shared__ f32x4 red_o[SL][16];
+    if (fd == 0) {
+        red_m[sl] = mx;
+        red_l[sl] = lt;
+    }
+    red_o[sl][fd >> 2] = f32x4{acc[0], acc[1], acc[2], acc[3]};
+    __syncthreads();
+    if (sl != 0) return;
+    float mt = red_m[0];
+#pragma unroll
+    for (int i = 1; i < SL; ++i) mt = fmaxf(mt, red_m[i]);
+    const float mcx = (mt == -INFINITY ? 0.f : mt) * c_log2;
+    float ltot = 0.f;
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < SL; ++i) {
+        const float sc = red_m[i] == -INFINITY ? 0.f : exp2_hw(red_m[i] * c_log2 - mcx);
+        ltot += sc * red_l[i];
+        const f32x4 x = red_o[i][fd >> 2];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] += sc * x[e];
+    }
     // no legal key ⇒ zero row; a NaN sum (NaN legal inputs) stays NaN
-    const float inv = lt != 0.f ? 1.f / lt : 0.f;
-    if (lse && fd == 0) lse[(size_t)bh * n + fq] = (mcx + log2f(lt)) * 0.6931471805599453f;
+    const float inv = ltot != 0.f ? 1.f / ltot : 0.f;
+    if (lse && fd == 0) lse[(size_t)bh * n + fq] = (mcx + log2f(ltot)) * 0.6931471805599453f;
     bf16x4 ov;
-    ov[0] = (__bf16)(acc[0] * inv);
-    ov[1] = (__bf16)(acc[1] * inv);
-    ov[2] = (__bf16)(acc[2] * inv);
-    ov[3] = (__bf16)(acc[3] * inv);
+    ov[0] = (__bf16)(o[0] * inv);
+    ov[1] = (__bf16)(o[1] * inv);
+    ov[2] = (__bf16)(o[2] * inv);
+    ov[3] = (__bf16)(o[3] * inv);
     *reinterpret_cast<bf16x4*>(O + ((size_t)bh * n + fq) * D + fd) = ov;
 }
 
-// Keys per split: 1024 (eight 32-key steps per wave).  Splitting pays when a
-// head's keys are long and their lengths differ: one workgroup per head then
-// leaves the CUs of short heads idle while the longest heads finish.
-// (2048- and 4096-key pieces measured slower on ragged 2k..8k caches.)
-constexpr int SPLIT_KEYS = 1024;
-
-int decode_nsplit(int m) { return (m + SPLIT_KEYS - 1) / SPLIT_KEYS; }
+// Keys per split: 1024 (eight 32-key steps per wave) when that already gives
+// 1024 workgroups (four per CU, what their LDS allows); with fewer heads the
+// pieces shrink, down to 256 keys, towards that count.  Splitting pays when a
+// head's keys are long and either the heads are few (one workgroup per head
+// leaves most CUs idle) or their lengths differ.  (2048- and 4096-key pieces
+// measured slower on ragged 2k..8k caches with 256 heads.)
+int decode_chunk(long long BH, int m) {
+    int c = 1024;
+    while (c > 256 && BH * ((m + c - 1) / c) < 1024) c /= 2;
+    return c;
+}
 
 size_t decode_split_bytes(int B, int H, int n, int m) {
     // A few queries against more keys than the sentence-length kernel takes,
-    // spread over at least two 1024-key pieces.
+    // spread over at least two pieces.
     if (n > QN || m <= 64) return 0;
-    const int ns = decode_nsplit(m);
+    const int chunk = decode_chunk((long long)B * H, m);
+    const int ns = (m + chunk - 1) / chunk;
     if (ns < 2) return 0;
     return (size_t)ns * B * H * n * PREC * sizeof(float);
 }
@@ -404,7 +433,7 @@ size_t decode_split_bytes(int B, int H, int n, int m) {
 bool decode_bf16_fits(const Args& a) {
     if (a.n > QN || a.m <= 64) return false;
     // One workgroup per head needs enough heads to give every CU work; with a
-    // workspace the split mode gives every 1024-key piece its own workgroup,
+    // workspace the split mode gives every piece of keys its own workgroup,
     // so any number of heads (a single sequence's decoder step included) fits.
     if ((long long)a.B * a.H >= 256) return true;
     const size_t need = decode_split_bytes(a.B, a.H, a.n, a.m);
@@ -416,14 +445,15 @@ hipError_t launch_bf16_decode(const Args& a, hipStream_t stream) {
     const int BH = a.B * a.H;
     const size_t need = decode_split_bytes(a.B, a.H, a.n, a.m);
     if (a.work && need > 0 && a.work_bytes >= need) {
-        const int ns = decode_nsplit(a.m);
+        const int chunk = decode_chunk(BH, a.m);
+        const int ns = (a.m + chunk - 1) / chunk;
         hipLaunchKernelGGL((sdpa_decode_bf16<32, 1>), dim3(BH * ns), dim3(NWD * 64), 0, stream,
                            (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                            (uint16_t*)a.out, a.H, a.n, a.m, c_log2, a.wl, a.wr, a.bottom_right,
-                           a.key_lens, a.lse, BH, SPLIT_KEYS, (float*)a.work);
+                           a.key_lens, a.lse, BH, chunk, (float*)a.work);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(sdpa_decode_merge_bf16, dim3(BH), dim3(NWD * 64), 0, stream,
+        hipLaunchKernelGGL(sdpa_decode_merge_bf16, dim3(BH * a.n), dim3(NWD * 64), 0, stream,
                            (const float*)a.work, (uint16_t*)a.out, a.lse, BH, a.n, ns, c_log2);
         return hipGetLastError();
     }
