@@ -143,7 +143,7 @@ def time_workload(name, dtype, steps, warmup, clock_warm_s=0.0, case=None, split
     mask = _lib.SDPA_MASK_CAUSAL if wl.causal else _lib.SDPA_MASK_NONE
     ptrs = [(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr()) for (q, k, v, o) in sets]
     ws = None
-    if split:  # sdpa_forward_ex with its workspace (decoder steps split per 1024 keys)
+    if split:  # sdpa_forward_ex with its workspace (decoder steps split into pieces of keys)
         need = _lib.sdpa_forward_workspace_bytes(wl.B, wl.h, wl.n, wl.m, wl.d_k, wl.d_v, code)
         if need == 0:
             raise ValueError(f"{name}: the split path does not apply")
@@ -745,12 +745,13 @@ def main():
                 "sets_rotated", "ms_per_step_eager")}
             if args.no_cpu_baseline:
                 del cases[name, dt]
-        # decoder steps split over 1024-key pieces (sdpa_forward_ex with a workspace)
-        r = time_workload("decode_long_cache", "bf16", 20, min(args.warmup, 5), clock_warm_s=0.1,
-                          split=True)
-        extra["decode_long_cache-bf16-split"] = {k: r[k] for k in (
-            "ms_per_step", "tflops", "gbs", "frac_mfma_peak", "frac_hbm_peak", "steps", "sets_rotated",
-            "ms_per_step_eager")}
+        # decoder steps with each head's keys split over several workgroups
+        # (sdpa_forward_ex with a workspace): 256 heads, and one sequence alone
+        for name in ("decode_long_cache", "decode_one_sequence"):
+            r = time_workload(name, "bf16", 20, min(args.warmup, 5), clock_warm_s=0.1, split=True)
+            extra[f"{name}-bf16-split"] = {k: r[k] for k in (
+                "ms_per_step", "tflops", "gbs", "frac_mfma_peak", "frac_hbm_peak", "steps",
+                "sets_rotated", "ms_per_step_eager")}
         for name in ("encoder_self_base", "long_causal_8k"):
             extra[f"backward-{name}-bf16"] = time_backward(
                 name, 20 if name.endswith("_8k") else max(10, min(args.steps, 200)), min(args.warmup, 3))

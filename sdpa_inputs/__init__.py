@@ -106,6 +106,11 @@ WORKLOADS = {
         key_len_range=(2048, 8192), seed=1008, dtypes=("bf16",), window=(None, 0, "bottom_right"),
         what="decoder self-attention step, base shape, one query against 2048..8192 cached "
              "keys (memory-bound stress case)"),
+    "decode_one_sequence": Workload(
+        "decode_one_sequence", B=1, h=8, n=1, m=32768, d_k=64, d_v=64, causal=False,
+        key_len_range=None, seed=1012, dtypes=("bf16",), window=(None, 0, "bottom_right"),
+        what="decoder self-attention step of one sequence alone, base model's 8 heads, one "
+             "query against a full 32768-key cache (few heads: the split-key path)"),
 }
 
 

@@ -95,6 +95,18 @@ def test_split_decode_long_cache_workload(gpu_lib):
     assert err <= TOL["bf16"]
 
 
+def test_split_decode_one_sequence_workload(gpu_lib):
+    """The decode_one_sequence workload (one sequence, 8 heads, one query
+    against a full 32768-key cache) through the split path, every row checked."""
+    wl = WORKLOADS["decode_one_sequence"]
+    c = make_inputs(wl, "bf16")
+    got = _run(c, True)
+    ref = so.attention(c["q"], c["k"], c["v"], key_lens=c["key_lens"], window=wl.window)
+    err = max_abs_err(got, ref)
+    print(f"split decode_one_sequence: max abs err {err:.2e}")
+    assert err <= TOL["bf16"]
+
+
 def test_split_decode_deterministic(gpu_lib):
     c = _case(1)
     a = _run(c, True)
