@@ -305,6 +305,26 @@ def test_torch_wrapper_rejects_bad_windows():
             forward(x, x, x, **kw)
 
 
+@pytest.mark.parametrize("heads", [8, 512])
+@pytest.mark.parametrize("return_lse", [False, True])
+def test_torch_wrapper_rejects_causal_with_n_ne_m(heads, return_lse):
+    """causal=True is the top-left inclusive j <= i rule of decoder self-attention
+    and needs n == m.  The binding rejects n != m before it chooses an entry
+    point, so the answer does not depend on the head count (fewer than 256
+    heads take the workspace path) or on return_lse.  No launch happens: the
+    check fires on CPU tensors, before the device checks."""
+    import torch
+
+    from transformer_attention_sdpa_amd import backward, forward
+
+    q = torch.zeros(1, heads, 1, 64)
+    kv = torch.zeros(1, heads, 4096, 64)
+    with pytest.raises(ValueError, match="causal mask needs n == m"):
+        forward(q, kv, kv, causal=True, return_lse=return_lse)
+    with pytest.raises(ValueError, match="causal mask needs n == m"):
+        backward(q, kv, kv, q, q, torch.zeros(1, heads, 1), causal=True)
+
+
 def test_torch_wrapper_rejects_cpu_tensors():
     import torch
 

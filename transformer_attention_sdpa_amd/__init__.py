@@ -23,9 +23,17 @@ __all__ = ["forward", "backward", "mha_forward", "sdpa_forward", "sdpa_forward_w
            "sdpa_mha_forward", "sdpa_mha_workspace_bytes", "sdpa_strerror", "sdpa_version"]
 
 
-def _window_args(window, causal):
-    """(window_left, window_right, align code) for the C ABI."""
+def _window_args(window, causal, n=None, m=None):
+    """(window_left, window_right, align code) for the C ABI.
+
+    The decoder's causal mask is the top-left window (unbounded, 0), which is
+    the inclusive j <= i rule only when the queries and keys are the same
+    sequence: with n != m it is rejected here, whichever entry point the call
+    then takes (a bottom-right window is the decoder-step form)."""
     if window is None:
+        if causal and n is not None and n != m:
+            raise ValueError("the causal mask needs n == m; use window=(None, 0, 'bottom_right') "
+                             "for queries at the end of a longer key sequence")
         return -1, (0 if causal else -1), _lib.SDPA_ALIGN_TOP_LEFT
     if causal:
         raise ValueError("give the causal mask as window=(None, 0) instead of combining both")
@@ -83,9 +91,7 @@ def mha_forward(x_q, x_kv, w_q, w_k, w_v, w_o, *, heads: int, causal: bool = Fal
             raise ValueError("key_lens must be an int32 tensor of B elements on the inputs' device")
         key_lens = key_lens.contiguous()
         kl_ptr = key_lens.data_ptr()
-    wl, wr, al = _window_args(window, causal)
-    if causal and window is None and n != m:
-        raise ValueError("the causal mask needs n == m; use a bottom-right window otherwise")
+    wl, wr, al = _window_args(window, causal, n, m)
     need = sdpa_mha_workspace_bytes(B, n, m, heads, d, d)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=x_q.device)
@@ -103,6 +109,14 @@ def mha_forward(x_q, x_kv, w_q, w_k, w_v, w_o, *, heads: int, causal: bool = Fal
     if rc != _lib.SDPA_OK:
         raise RuntimeError(f"sdpa_mha_forward failed ({rc}): {sdpa_strerror(rc)}")
     return out
+
+
+def _lengths(q, k):
+    """(n, m) of [B, h, n, d] queries and [B, h, m, d] keys (None when not 4-D;
+    ``_check_qkv`` then rejects them)."""
+    if q.dim() != 4 or k.dim() != 4:
+        return None, None
+    return q.shape[2], k.shape[2]
 
 
 def _check_qkv(q, k, v):
@@ -166,7 +180,7 @@ def backward(q, k, v, out, dout, lse, *, causal: bool = False, key_lens=None,
     """
     import torch
 
-    wl, wr, al = _window_args(window, causal)
+    wl, wr, al = _window_args(window, causal, *_lengths(q, k))
     B, h, n, m, d_k, d_v, dt = _check_qkv(q, k, v)
     for name, t, shape, dtype in (("out", out, (B, h, n, d_v), q.dtype),
                                   ("dout", dout, (B, h, n, d_v), q.dtype),
@@ -217,8 +231,7 @@ def forward(q, k, v, *, causal: bool = False, key_lens=None, scale: float | None
     """
     import torch
 
-    wl, wr, al = _window_args(window, causal)
-
+    wl, wr, al = _window_args(window, causal, *_lengths(q, k))
     B, h, n, m, d_k, d_v, dt = _check_qkv(q, k, v)
     key_lens, kl_ptr = _key_lens_ptr(key_lens, B, q.device)
     if isinstance(workspace, str):
