@@ -402,6 +402,61 @@ def pin_multihead_page_shapes(so):
     assert so.multihead(x, x, wq, wk, wv, wo).shape == (1, 10, d_model)
 
 
+def _row_masks(n, m, key_lens):
+    """(causal, key_lens, window) combinations for the single-row helpers:
+    every mask kind, each window kind with both alignments, with and without
+    key lengths."""
+    masks = [(False, None, None), (False, key_lens, None)]
+    if n == m:
+        masks += [(True, None, None), (True, key_lens, None)]
+    masks += [(False, key_lens, w) for w in WINDOWS] + [(False, None, w) for w in WINDOWS[:3]]
+    return masks
+
+
+def pin_rows_brute_force_mp(so):
+    """``attention_rows`` (one output row per pick, for checking full-size
+    outputs row by row) against the 50-digit evaluator on tiny shapes: every
+    mask kind, key lengths 0, inside and past m, every window kind with both
+    alignments, n ≠ m, and picks in scrambled order, so that each row must use
+    its own batch element's key length, its own position and its own window
+    shift."""
+    from oracle.brute_mp import attention_mp
+
+    rng = np.random.default_rng(41)
+    for (B, h, n, m, d, dv), kl in (((2, 2, 5, 5, 3, 2), [0, 7]), ((3, 2, 3, 6, 2, 3), [6, 1, 4]),
+                                    ((2, 1, 6, 4, 3, 2), [3, 9])):
+        q, k, v = _rand(rng, B, h, n, d), _rand(rng, B, h, m, d), _rand(rng, B, h, m, dv)
+        picks = [(b, hh, i) for b in range(B) for hh in range(h) for i in range(n)]
+        picks = [picks[t] for t in rng.permutation(len(picks))]
+        for causal, key_lens, window in _row_masks(n, m, np.array(kl)):
+            got = so.attention_rows(q, k, v, picks, scale=0.7, causal=causal, key_lens=key_lens,
+                                    window=window)
+            ref = attention_mp(q.tolist(), k.tolist(), v.tolist(), 0.7, causal,
+                               None if key_lens is None else list(key_lens), window=window)
+            for r, (b, hh, i) in enumerate(picks):
+                assert np.allclose(got[r], [float(x) for x in ref[b][hh][i]], rtol=0, atol=1e-13), \
+                    (B, h, n, m, causal, key_lens, window, (b, hh, i))
+
+
+def pin_rows_match_whole_heads(so):
+    """Rows from ``attention_rows`` equal the same rows of ``attention`` (pinned
+    above) on heads longer than the oracle's 512-row evaluation slice: rows on
+    both sides of the slice edge and the last row, causal, padded, windowed
+    with both alignments, and n ≠ m."""
+    rng = np.random.default_rng(43)
+    for (B, h, n, m, kl) in ((2, 2, 600, 600, [600, 300]), (2, 1, 520, 700, [700, 0])):
+        q, k, v = _rand(rng, B, h, n, 4), _rand(rng, B, h, m, 4), _rand(rng, B, h, m, 3)
+        rows = [0, 1, 255, 256, 511, 512, 513, n - 1] + list(rng.integers(0, n, 3))
+        picks = [(b, hh, int(i)) for b in range(B) for hh in range(h) for i in rows]
+        masks = [(n == m, np.array(kl), None), (False, np.array(kl), (100, 0, "top_left")),
+                 (False, np.array(kl), (None, 0, "bottom_right")), (False, None, (64, 64, "bottom_right"))]
+        for causal, key_lens, window in masks:
+            whole = so.attention(q, k, v, causal=causal, key_lens=key_lens, window=window)
+            got = so.attention_rows(q, k, v, picks, causal=causal, key_lens=key_lens, window=window)
+            ref = np.stack([whole[b, hh, i] for (b, hh, i) in picks])
+            assert np.allclose(got, ref, rtol=0, atol=1e-13), (n, m, causal, kl, window)
+
+
 ALL_PINS = [
     pin_worked_example_scores,
     pin_worked_example_weights,
@@ -424,6 +479,8 @@ ALL_PINS = [
     pin_multihead_single_identity_head,
     pin_multihead_head_permutation,
     pin_multihead_page_shapes,
+    pin_rows_brute_force_mp,
+    pin_rows_match_whole_heads,
 ]
 
 
@@ -595,6 +652,57 @@ def pin_lse_closed_forms(sb):
             assert abs(float(mpmath.log(mpmath.fsum(mpmath.exp(x) for x in s))) - lse1[1, 0, i]) < 1e-14
 
 
+def pin_bwd_rows_finite_difference_mp(sb):
+    """``backward_query_rows`` and ``backward_key_rows`` (gradient rows for
+    checking full-size gradients) against the 60-digit central difference of
+    Eq. (1): every pick in scrambled order, every mask kind, n ≠ m."""
+    from oracle.brute_mp import attention_grad_fd_mp
+
+    rng = np.random.default_rng(81)
+    for (n, m) in ((3, 3), (2, 4)):
+        q, k, v, do = _bwd_case(rng, 2, 2, n, m, 3, 2)
+        for causal, kl, win in _BWD_MASKS:
+            if causal and n != m:
+                continue
+            fd = attention_grad_fd_mp(q.tolist(), k.tolist(), v.tolist(), do.tolist(), 0.7,
+                                      causal, kl, win)
+            picks = [(b, hh, i) for b in range(2) for hh in range(2) for i in range(n)]
+            picks = [picks[t] for t in rng.permutation(len(picks))]
+            dq = sb.backward_query_rows(q, k, v, do, picks, scale=0.7, causal=causal, key_lens=kl,
+                                        window=win)
+            for r, (b, hh, i) in enumerate(picks):
+                assert np.allclose(dq[r], fd[0][b][hh][i], rtol=0, atol=1e-12), (n, m, causal, kl, win)
+            for b in range(2):
+                for hh in range(2):
+                    keys = list(rng.permutation(m))
+                    dk, dv = sb.backward_key_rows(q, k, v, do, b, hh, keys, scale=0.7, causal=causal,
+                                                  key_lens=kl, window=win)
+                    for r, j in enumerate(keys):
+                        assert np.allclose(dk[r], fd[1][b][hh][j], rtol=0, atol=1e-12), (b, hh, j, win)
+                        assert np.allclose(dv[r], fd[2][b][hh][j], rtol=0, atol=1e-12), (b, hh, j, win)
+
+
+def pin_bwd_rows_match_whole(sb):
+    """Gradient rows from the row helpers equal those of ``attention_backward``
+    (pinned above) on heads longer than the 512-row evaluation slice, so the
+    dK/dV helper must add up every slice of queries."""
+    rng = np.random.default_rng(83)
+    for (n, m, causal, kl, win) in ((600, 600, True, [600, 333], None),
+                                    (530, 640, False, [640, 100], (None, 0, "bottom_right")),
+                                    (600, 600, False, None, (50, 50, "top_left"))):
+        q, k, v, do = _bwd_case(rng, 2, 1, n, m, 4, 3)
+        dq, dk, dv = sb.attention_backward(q, k, v, do, causal=causal, key_lens=kl, window=win)
+        picks = [(b, 0, i) for b in range(2) for i in (0, 1, 511, 512, n - 1)]
+        got = sb.backward_query_rows(q, k, v, do, picks, causal=causal, key_lens=kl, window=win)
+        assert np.allclose(got, np.stack([dq[b, hh, i] for (b, hh, i) in picks]), rtol=0, atol=1e-12)
+        for b in range(2):
+            keys = [0, 1, 99, 100, 332, 333, 511, 512, m - 1]
+            gk, gv = sb.backward_key_rows(q, k, v, do, b, 0, keys, causal=causal, key_lens=kl,
+                                          window=win)
+            assert np.allclose(gk, dk[b, 0, keys], rtol=0, atol=1e-12), (n, m, b)
+            assert np.allclose(gv, dv[b, 0, keys], rtol=0, atol=1e-12), (n, m, b)
+
+
 BACKWARD_PINS = [
     pin_bwd_finite_difference_mp,
     pin_bwd_finite_difference_fp64,
@@ -605,4 +713,6 @@ BACKWARD_PINS = [
     pin_bwd_uniform_weights,
     pin_bwd_empty_rows_pass_nothing,
     pin_lse_closed_forms,
+    pin_bwd_rows_finite_difference_mp,
+    pin_bwd_rows_match_whole,
 ]

@@ -43,22 +43,34 @@ def test_workload_full_parity(gpu_lib, name, dt):
     assert err <= TOL[dt]
 
 
+def _long_rows(n, head, rng):
+    """Rows of one 8192-query head to check: both sides of every 64-query
+    boundary (each wave's key range and tile skipping change there, and every
+    fourth one is a 256-query workgroup edge, where the heavy-first block
+    order changes), both sides of the 32-query sub-block edges inside one
+    workgroup's block (a different block per head), the first two rows, the
+    last row and two random rows."""
+    rows = {0, 1, n - 1}
+    for t in range(1, n // 64):
+        rows |= {64 * t - 1, 64 * t}
+    q0 = 256 * (head % (n // 256))
+    for t in range(1, 8):
+        rows |= {q0 + 32 * t - 1, q0 + 32 * t}
+    rows |= {int(x) for x in rng.choice(n, 2, replace=False)}
+    return sorted(rows)
+
+
 def test_long_causal_8k_sampled_rows(gpu_lib):
-    """n = m = 8192, 64 heads, causal, bf16: every head, rows across tile edges."""
+    """n = m = 8192, 64 heads, causal, bf16: every head, every block edge."""
     case = make_inputs("long_causal_8k", "bf16")
     _, got = run_gpu(case)
     wl = WORKLOADS["long_causal_8k"]
     assert np.isfinite(got).all()
     rng = np.random.default_rng(99)
-    rows = [0, 1, 31, 32, 63, 64, 127, 128, 129, 255, 256, 1000, 4095, 4096, 8063, 8064, 8190, 8191]
-    picks = []
-    for b in range(wl.B):
-        for h in range(wl.h):
-            for i in rows[:4] + list(rng.choice(wl.n, size=3, replace=False)) + rows[-2:]:
-                picks.append((b, h, int(i)))
-    for i in rows:
-        picks.append((1, 7, i))
-    ref = so.attention_rows(case["q"], case["k"], case["v"], picks, causal=True)
+    picks = [(b, h, i) for b in range(wl.B) for h in range(wl.h)
+             for i in _long_rows(wl.n, b * wl.h + h, rng)]
+    q, k, v = (case[x].astype(np.float64) for x in ("q", "k", "v"))
+    ref = so.attention_rows(q, k, v, picks, causal=True)
     g = np.stack([got[b, h, i] for (b, h, i) in picks])
     err = max_abs_err(g, ref)
     print(f"long_causal_8k: {len(picks)} sampled rows, max abs err {err:.3e}")

@@ -204,3 +204,108 @@ def test_some_backward_pin_catches_mutant(name, monkeypatch):
         except Exception as e:
             caught.append((pin.__name__, type(e).__name__))
     assert caught, f"no pin detects mutant {name}"
+
+
+# --- the single-row helpers ---------------------------------------------------
+#
+# Mistakes one could make in a helper that evaluates chosen output rows: the
+# row evaluated at position 0 instead of its own position, the window's
+# bottom-right shift dropped, every batch element given the first one's key
+# length, the neighbouring row returned, or (gradients) only the first slice
+# of queries added into dK/dV.
+
+_orig_rows = so.attention_rows
+
+
+def _rows_query_pos_dropped(q, k, v, picks, scale=None, causal=False, key_lens=None, window=None):
+    out = []
+    for (b, hh, i) in picks:
+        q0 = np.array(q, dtype=np.float64, copy=True)
+        q0[b, hh, 0] = q[b, hh, i]
+        out.append(_orig_rows(q0, k, v, [(b, hh, 0)], scale, causal, key_lens, window)[0])
+    return np.array(out)
+
+
+def _rows_shift_dropped(q, k, v, picks, scale=None, causal=False, key_lens=None, window=None):
+    if window is not None:
+        window = (window[0], window[1], "top_left")
+    return _orig_rows(q, k, v, picks, scale, causal, key_lens, window)
+
+
+def _rows_first_key_len(q, k, v, picks, scale=None, causal=False, key_lens=None, window=None):
+    if key_lens is not None:
+        key_lens = np.full(len(key_lens), key_lens[0])
+    return _orig_rows(q, k, v, picks, scale, causal, key_lens, window)
+
+
+def _rows_neighbour(q, k, v, picks, scale=None, causal=False, key_lens=None, window=None):
+    n = q.shape[2]
+    picks = [(b, hh, min(i + 1, n - 1) if i >= 1 else i) for (b, hh, i) in picks]
+    return _orig_rows(q, k, v, picks, scale, causal, key_lens, window)
+
+
+ROW_MUTANTS = {
+    "rows_query_pos_dropped": _rows_query_pos_dropped,
+    "rows_window_shift_dropped": _rows_shift_dropped,
+    "rows_first_key_len_for_all": _rows_first_key_len,
+    "rows_neighbour_returned": _rows_neighbour,
+}
+
+
+@pytest.mark.parametrize("name", sorted(ROW_MUTANTS))
+def test_some_pin_catches_row_helper_mutant(name, monkeypatch):
+    monkeypatch.setattr(so, "attention_rows", ROW_MUTANTS[name])
+    caught = []
+    for pin in ALL_PINS:
+        try:
+            pin(so)
+        except Exception as e:
+            caught.append((pin.__name__, type(e).__name__))
+    assert caught, f"no pin detects mutant {name}"
+
+
+_orig_qrows = sb.backward_query_rows
+_orig_krows = sb.backward_key_rows
+
+
+def _bwd_qrows_pos_dropped(q, k, v, do, picks, scale=None, causal=False, key_lens=None, window=None):
+    out = []
+    for (b, hh, i) in picks:
+        q0, d0 = np.array(q, np.float64, copy=True), np.array(do, np.float64, copy=True)
+        q0[b, hh, 0], d0[b, hh, 0] = q[b, hh, i], do[b, hh, i]
+        out.append(_orig_qrows(q0, k, v, d0, [(b, hh, 0)], scale, causal, key_lens, window)[0])
+    return np.array(out)
+
+
+def _bwd_krows_first_slice(q, k, v, do, b, hh, keys, scale=None, causal=False, key_lens=None,
+                           window=None):
+    d0 = np.array(do, np.float64, copy=True)
+    d0[:, :, 512:] = 0.0  # the later query slices contribute nothing
+    return _orig_krows(q, k, v, d0, b, hh, keys, scale, causal, key_lens, window)
+
+
+def _bwd_krows_shift_dropped(q, k, v, do, b, hh, keys, scale=None, causal=False, key_lens=None,
+                             window=None):
+    if window is not None:
+        window = (window[0], window[1], "top_left")
+    return _orig_krows(q, k, v, do, b, hh, keys, scale, causal, key_lens, window)
+
+
+BWD_ROW_MUTANTS = {
+    "bwd_query_rows_pos_dropped": ("backward_query_rows", _bwd_qrows_pos_dropped),
+    "bwd_key_rows_first_slice_only": ("backward_key_rows", _bwd_krows_first_slice),
+    "bwd_key_rows_window_shift_dropped": ("backward_key_rows", _bwd_krows_shift_dropped),
+}
+
+
+@pytest.mark.parametrize("name", sorted(BWD_ROW_MUTANTS))
+def test_some_backward_pin_catches_row_helper_mutant(name, monkeypatch):
+    attr, fn = BWD_ROW_MUTANTS[name]
+    monkeypatch.setattr(sb, attr, fn)
+    caught = []
+    for pin in BACKWARD_PINS:
+        try:
+            pin(sb)
+        except Exception as e:
+            caught.append((pin.__name__, type(e).__name__))
+    assert caught, f"no pin detects mutant {name}"
