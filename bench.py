@@ -5,7 +5,9 @@ A "step" is one sdpa_forward over one batch of the workload (every step of the
 path: staging, scores, masking, online softmax, weighted sum, store).  Inputs
 are seeded synthetic N(0,1) tensors already resident in HBM; the timed steps
 rotate over enough copies of the batch (> 2× the 256 MB Infinity Cache) that
-the data really streams from HBM.  The K timed steps are captured in one HIP
+the data really streams from HBM, and a copy of twice the cache's size runs
+just before the timed replay, so the sets it touches first are cold too, at
+any step count.  The K timed steps are captured in one HIP
 graph (the launches are a few microseconds each, below Python's call rate) and
 timed with HIP events on the stream they run on.
 
@@ -103,6 +105,39 @@ def measured_traffic(workload, dtype):
     return t.get("bytes_per_launch")
 
 
+class CacheFlush:
+    """Evicts the Infinity Cache (and L2) before a timed replay: a device copy
+    of twice the cache's size, read and written on the timing stream.  The
+    timed steps then find none of their sets resident, whatever set the
+    untimed replays touched last."""
+
+    def __init__(self, dev):
+        import torch
+
+        self.src = torch.ones(INFINITY_CACHE_BYTES * 2, dtype=torch.uint8, device=dev)
+        self.dst = torch.empty_like(self.src)
+        self.nbytes = 2 * self.src.numel()  # read + write
+
+    def __call__(self):
+        self.dst.copy_(self.src)
+
+
+def timed_replay(graph, flush):
+    """HIP-event time of one replay of ``graph`` on the current stream (ms),
+    right after a cache flush (not timed)."""
+    import torch
+
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    flush()
+    e0.record()
+    graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1)
+
+
 def time_workload(name, dtype, steps, warmup, clock_warm_s=0.0, case=None, split=False):
     import torch
 
@@ -125,8 +160,10 @@ def time_workload(name, dtype, steps, warmup, clock_warm_s=0.0, case=None, split
             return torch.from_numpy(x).to(dev)
         tdt, code = torch.float32, _lib.SDPA_F32
     q0, k0, v0 = up(case["q"]), up(case["k"]), up(case["v"])
-    # Enough copies that the bytes the timed steps touch (Q, O and the legal
-    # K/V rows of each copy) exceed twice the Infinity Cache.
+    # Enough copies that one pass over them (Q, O and the legal K/V rows of
+    # each copy) exceeds twice the Infinity Cache: a set is evicted before the
+    # rotation comes back to it.  The timed replay starts right after a cache
+    # flush, so the first sets it touches are cold too, at any step count.
     touched = algorithmic_work(wl, dtype, case["key_lens"])[1]
     nsets = max(1, min(64, math.ceil(2 * INFINITY_CACHE_BYTES / touched)))
     sets = []
@@ -192,19 +229,28 @@ def time_workload(name, dtype, steps, warmup, clock_warm_s=0.0, case=None, split
         graph.replay()
         torch.cuda.synchronize()
 
+    flush = CacheFlush(dev)
+    w0 = time.perf_counter()
+    graph_ms = timed_replay(graph, flush)
+    wall = time.perf_counter() - w0
+
+    # Cross-check over a long rotation: two full passes over every set (at
+    # least twice the Infinity Cache of timed bytes whatever --steps is).
+    rot = max(steps, 2 * nsets)
+    graph_rot = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph_rot):
+        cs = torch.cuda.current_stream(dev).cuda_stream
+        for i in range(rot):
+            launch(i, cs)
+    graph_rot.replay()
+    torch.cuda.synchronize()
+    rot_ms = timed_replay(graph_rot, flush)
+
+    # Same steps launched one by one from Python (host launch rate included).
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    w0 = time.perf_counter()
-    e0.record()
-    graph.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    graph_ms = e0.elapsed_time(e1)
-
-    # Same steps launched one by one from Python (host launch rate included).
-    torch.cuda.synchronize()
+    flush()
     e0.record()
     for i in range(steps):
         launch(i, stream)
@@ -214,11 +260,16 @@ def time_workload(name, dtype, steps, warmup, clock_warm_s=0.0, case=None, split
 
     flops, nbytes, dense = algorithmic_work(wl, dtype, case["key_lens"])
     t = graph_ms / 1e3 / steps
-    del graph, sets
+    del graph, graph_rot, sets, flush
     torch.cuda.empty_cache()
     return {
         "workload": name, "dtype": dtype, "steps": steps, "sets_rotated": nsets,
         "ms_per_step": graph_ms / steps, "ms_per_step_eager": eager_ms / steps,
+        "bytes_touched_timed": nbytes * steps,
+        "distinct_sets_timed": min(steps, nsets),
+        "flushed_before_timing_bytes": 4 * INFINITY_CACHE_BYTES,
+        "long_rotation": {"steps": rot, "ms_per_step": rot_ms / rot,
+                          "bytes_touched_timed": nbytes * rot},
         "wall_s_timed": wall,
         "alg_flops": flops, "dense_flops": dense, "alg_bytes": nbytes,
         "tflops": flops / t / 1e12, "gbs": nbytes / t / 1e9,
@@ -315,12 +366,7 @@ def time_backward(name, steps, warmup, clock_warm_s=0.1):
     while time.perf_counter() < t_warm:
         graph.replay()
         torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    graph.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    t = e0.elapsed_time(e1) / 1e3 / steps
+    t = timed_replay(graph, CacheFlush(dev)) / 1e3 / steps
     del graph, sets
     torch.cuda.empty_cache()
     return {"ms_per_step": t * 1e3, "tflops": flops / t / 1e12, "gbs": nbytes / t / 1e9,
@@ -407,12 +453,7 @@ def time_mha(name, steps, warmup, clock_warm_s=0.1):
     while time.perf_counter() < t_warm:
         graph.replay()
         torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    graph.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    t = e0.elapsed_time(e1) / 1e3 / steps
+    t = timed_replay(graph, CacheFlush(dev)) / 1e3 / steps
     del graph, sets
     torch.cuda.empty_cache()
     return {"ms_per_step": t * 1e3, "tflops": flops / t / 1e12, "gbs": nbytes / t / 1e9,
@@ -511,28 +552,74 @@ def traffic_record(fetch_db, write_db, copy_fetch_db, copy_write_db, copy_bytes,
             "kernel_source_hash": kernel_source_hash()}
 
 
-def cpu_baseline(name, dtype, budget_s=10.0):
-    """The fp64 oracle, as it stands, on the host cores: whole batches until the budget."""
+def _oracle_slice_worker(name, dtype, b0, b1, budget_s, ready, go, results):
+    """One host core's share of the CPU baseline: the unchanged oracle on batch
+    elements [b0, b1) of the workload, one BLAS thread, passes until the
+    budget.  Runs in a spawned process that never touches the GPU."""
     import oracle.sdpa_oracle as so
     from threadpoolctl import threadpool_limits
 
     wl = WORKLOADS[name]
     case = make_inputs(wl, dtype)
-    flops, _, _ = algorithmic_work(wl, dtype, case["key_lens"])
-    reps = 0
-    with threadpool_limits(limits=1):  # 64×64 products stay on one BLAS thread anyway
-        t0 = time.perf_counter()
+    q, k, v = (case[x][b0:b1] for x in ("q", "k", "v"))
+    kl = None if case["key_lens"] is None else case["key_lens"][b0:b1]
+    with threadpool_limits(limits=1):
+        ready.put(b0)
+        go.wait()
+        t0 = time.monotonic()
+        reps = 0
         while True:
-            so.attention(case["q"], case["k"], case["v"], causal=wl.causal, key_lens=case["key_lens"],
-                         window=wl.window)
+            so.attention(q, k, v, causal=wl.causal, key_lens=kl, window=wl.window)
             reps += 1
-            el = time.perf_counter() - t0
-            if el >= budget_s:
+            t1 = time.monotonic()
+            if t1 - t0 >= budget_s:
                 break
-    per = el / reps
-    return {"value": flops / per / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
-            "sample": f"whole {name} batch ({wl.B * wl.h} heads, {dtype} values in fp64), "
-                      f"{reps} passes in {el:.1f} s, {per * 1e3:.1f} ms per pass",
+    results.put((b0, b1, reps, t0, t1))
+
+
+def cpu_worker_count(B: int) -> int:
+    """Host cores the CPU baseline uses: every core this process may run on,
+    at most 16 (one GPU's share of the host) and at most one per batch element."""
+    return max(1, min(16, len(os.sched_getaffinity(0)), B))
+
+
+def cpu_baseline(name, dtype, budget_s=10.0):
+    """The fp64 oracle, as it stands, on the host cores: the batch is split over
+    one process per usable core (each on one BLAS thread; the oracle's 64×64
+    products gain nothing from more), every process repeats whole passes over
+    its batch elements for the budget, and the rate is the work all of them
+    finished over the span from the first start to the last end."""
+    import dataclasses
+    import multiprocessing as mp
+
+    wl = WORKLOADS[name]
+    key_lens = make_inputs(wl, dtype)["key_lens"]
+    workers = cpu_worker_count(wl.B)
+    bounds = [wl.B * i // workers for i in range(workers + 1)]
+    ctx = mp.get_context("spawn")  # fresh interpreters: nothing of this process's GPU state
+    ready, results, go = ctx.Queue(), ctx.Queue(), ctx.Event()
+    procs = [ctx.Process(target=_oracle_slice_worker,
+                         args=(name, dtype, bounds[i], bounds[i + 1], budget_s, ready, go, results))
+             for i in range(workers)]
+    for p in procs:
+        p.start()
+    for _ in procs:
+        ready.get(timeout=300)
+    go.set()
+    done = [results.get(timeout=budget_s * 10 + 300) for _ in procs]
+    for p in procs:
+        p.join()
+    flops = 0
+    for b0, b1, reps, _, _ in done:
+        part = dataclasses.replace(wl, B=b1 - b0)
+        kl = None if key_lens is None else key_lens[b0:b1]
+        flops += reps * algorithmic_work(part, dtype, kl)[0]
+    span = max(r[4] for r in done) - min(r[3] for r in done)
+    whole = algorithmic_work(wl, dtype, key_lens)[0]
+    return {"value": flops / span / 1e12, "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
+            "sample": f"{name} ({wl.B * wl.h} heads, {dtype} values in fp64) split over {workers} "
+                      f"processes by batch element, {flops / whole:.1f} whole-batch passes "
+                      f"in {span:.1f} s, {span / (flops / whole) * 1e3:.1f} ms per pass",
             "host": host_description()}
 
 
@@ -742,7 +829,7 @@ def main():
                               case=cases[name, dt])
             extra[f"{name}-{dt}"] = {k: r[k] for k in (
                 "ms_per_step", "tflops", "gbs", "frac_mfma_peak", "frac_hbm_peak", "steps",
-                "sets_rotated", "ms_per_step_eager")}
+                "sets_rotated", "ms_per_step_eager", "bytes_touched_timed", "long_rotation")}
             if args.no_cpu_baseline:
                 del cases[name, dt]
         # decoder steps with each head's keys split over several workgroups
@@ -795,6 +882,10 @@ def main():
         "frac_mfma_peak": head["frac_mfma_peak"],
         "ms_per_step_eager": head["ms_per_step_eager"],
         "sets_rotated": head["sets_rotated"],
+        "bytes_touched_timed": head["bytes_touched_timed"],
+        "distinct_sets_timed": head["distinct_sets_timed"],
+        "flushed_before_timing_bytes": head["flushed_before_timing_bytes"],
+        "long_rotation": head["long_rotation"],
         "kernel_source_hash": kernel_source_hash(),
     }
     if extra:
