@@ -138,19 +138,23 @@ __global__ __launch_bounds__(NWD * 64) void sdpa_decode_bf16(
     // unconditionally, also one step past the wave's last: there the offsets
     // start at the key length, so the loads return zeros without touching
     // memory.  Every step then has the same outstanding loads, which keeps
-    // the compiler's waits on K exact.
+    // the compiler's waits on K exact.  Offsets are unsigned 32-bit: the
+    // sentinel L·128 is below 2^31 and adds at most 4 KiB, so nothing wraps
+    // (the hardware reads the offset as unsigned).
     auto issue = [&](int s, bf16x8 (&kop)[NTL][2]) {
-        const int base = s < s1 ? (kb + s * KS) * 128 : L * 128;
+        const uint32_t base = s < s1 ? (uint32_t)(kb + s * KS) * 128u : (uint32_t)L * 128u;
 #pragma unroll
         for (int t = 0; t < NTL; ++t)
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
                 kop[t][ks] = __builtin_bit_cast(
-                    bf16x8, sdpa_dec_buffer_load_v4i32(rk, base + 16 * t * 128 + k_off + 64 * ks, 0,
-                                                       kCachePolicyNT));
+                    bf16x8, sdpa_dec_buffer_load_v4i32(
+                                rk, (int)(base + (uint32_t)(16 * t * 128 + k_off + 64 * ks)), 0,
+                                kCachePolicyNT));
         char* dst = vbuf + (s & 1) * VBUF;
 #pragma unroll
-        for (int i = 0; i < NVL; ++i) load16_to_lds_nt(rv, dst + 8 * i * 128, base + v_off[i]);
+        for (int i = 0; i < NVL; ++i)
+            load16_to_lds_nt(rv, dst + 8 * i * 128, (int)(base + (uint32_t)v_off[i]));
     };
 
     float mrun = -INFINITY, lrun = 0.f;

@@ -12,6 +12,12 @@
 // rows.  Products are computed transposed (Sᵀ = K·Qᵀ, Oᵀ += Vᵀ·Pᵀ) so each lane
 // holds one query's column, as in the bf16 kernel.  With one k value per lane
 // per MFMA, Vᵀ is read straight from the row-major V tile (no transpose read).
+//
+// Accumulation across tiles is compensated (Kahan): each tile's Oᵀ part and
+// weight sum are formed on top of what rounding has lost so far, then added
+// into the running totals, and the new loss is kept for the next tile.  A plain running sum over L keys would round L/2 times in
+// sequence, a first-order error of about L/2 · 2^-24 relative (0.25 at 2^23
+// keys); compensated, the error stays at a few units of 2^-24 whatever L is.
 #include "sdpa_common.hpp"
 
 namespace sdpa {
@@ -106,11 +112,13 @@ __global__ __launch_bounds__(NW * 64) void sdpa_fwd_f32(
         }
     };
 
-    f32x16 oacc[2];
+    // Running Oᵀ and weight sum, and what rounding has lost from each so far
+    // (to be added back).
+    f32x16 oacc[2], ofix[2];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) { oacc[0][i] = 0.f; oacc[1][i] = 0.f; }
+    for (int i = 0; i < 16; ++i) { oacc[0][i] = oacc[1][i] = 0.f; ofix[0][i] = ofix[1][i] = 0.f; }
     float mrun = -INFINITY;
-    float lrun = 0.f;
+    float lrun = 0.f, lfix = 0.f;
 
     const int wq_lo = q0 + w * QW;
     const int wq_hi = min(wq_lo + QW, n) - 1;  // < wq_lo for a wave past n: empty
@@ -161,18 +169,26 @@ __global__ __launch_bounds__(NW * 64) void sdpa_fwd_f32(
         const float alpha = exp2_hw((mrun - muse) * c_log2);
         mrun = mnew;
         const float mc = muse * c_log2;
-        lrun *= alpha;
+        if (alpha != 1.f) {  // the running maximum moved: rescale totals and corrections
+            lrun *= alpha;
+            lfix *= alpha;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) { oacc[0][i] *= alpha; oacc[1][i] *= alpha; }
+            for (int i = 0; i < 16; ++i) {
+                oacc[0][i] *= alpha; oacc[1][i] *= alpha;
+                ofix[0][i] *= alpha; ofix[1][i] *= alpha;
+            }
+        }
+        float ly = lfix;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const float p = exp2_hw(__builtin_fmaf(s[i], c_log2, -mc));
             s[i] = p;
-            lrun += p;
+            ly += p;
         }
 
-        // Oᵀ += Vᵀ · Pᵀ: step i contracts, for half-wave hf, the key held in
-        // Sᵀ register i, i.e. tile row 8·(i/4) + 4·hf + i%4.
+        // This tile's Oᵀ part, Vᵀ · Pᵀ, accumulated onto the correction, so that
+        // ofix becomes y = part + lost.  Step i contracts, for half-wave hf, the
+        // key held in Sᵀ register i, i.e. tile row 8·(i/4) + 4·hf + i%4.
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int r = 8 * (i >> 2) + 4 * hf + (i & 3);
@@ -180,12 +196,32 @@ __global__ __launch_bounds__(NW * 64) void sdpa_fwd_f32(
             for (int dt = 0; dt < 2; ++dt) {
                 const int dv = 32 * dt + l32;
                 const float a = sVf[swz16(r, dv >> 2) * 4 + (dv & 3)];
-                oacc[dt] = mfma32x32x2_f32(a, s[i], oacc[dt]);
+                ofix[dt] = mfma32x32x2_f32(a, s[i], ofix[dt]);
             }
+        }
+        // Kahan step: t = sum + y; lost = y − (t − sum); sum = t.
+        {
+#pragma clang fp contract(off)
+            const float lt = lrun + ly;
+            lfix = ly - (lt - lrun);
+            lrun = lt;
+#pragma unroll
+            for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const float y = ofix[dt][i];
+                    const float t = oacc[dt][i] + y;
+                    ofix[dt][i] = y - (t - oacc[dt][i]);
+                    oacc[dt][i] = t;
+                }
         }
     }
 
-    const float ltot = half_swap_sum(lrun);
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[dt][i] += ofix[dt][i];
+    const float ltot = half_swap_sum(lrun + lfix);
     if (qrow < n) {
         float* dst = O + qbase + (size_t)qrow * D;
 #pragma unroll
@@ -208,23 +244,16 @@ __global__ __launch_bounds__(NW * 64) void sdpa_fwd_f32(
 }  // namespace
 
 hipError_t launch_f32_long(const Args& a, hipStream_t stream) {
+    // Two waves per workgroup at every n: for n <= 32 the second wave has no
+    // queries and only shares the tile loads (its tile loop skips the math),
+    // which keeps each lane's staging registers at four 16-byte chunks.
+    constexpr int NW = 2;
     const int BH = a.B * a.H;
     const float c_log2 = (float)((double)a.scale * 1.4426950408889634);
-    if (a.n <= 32) {
-        constexpr int NW = 1;
-        const int nqb = (a.n + NW * QW - 1) / (NW * QW);
-        hipLaunchKernelGGL(sdpa_fwd_f32<NW>, dim3(nqb * BH), dim3(NW * 64), 0, stream,
-                           (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.out,
-                           BH, a.H, a.n, a.m, c_log2, a.wl, a.wr, a.bottom_right, a.key_lens,
-                           nqb);
-    } else {
-        constexpr int NW = 2;
-        const int nqb = (a.n + NW * QW - 1) / (NW * QW);
-        hipLaunchKernelGGL(sdpa_fwd_f32<NW>, dim3(nqb * BH), dim3(NW * 64), 0, stream,
-                           (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.out,
-                           BH, a.H, a.n, a.m, c_log2, a.wl, a.wr, a.bottom_right, a.key_lens,
-                           nqb);
-    }
+    const int nqb = (a.n + NW * QW - 1) / (NW * QW);
+    hipLaunchKernelGGL(sdpa_fwd_f32<NW>, dim3(nqb * BH), dim3(NW * 64), 0, stream,
+                       (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.out,
+                       BH, a.H, a.n, a.m, c_log2, a.wl, a.wr, a.bottom_right, a.key_lens, nqb);
     return hipGetLastError();
 }
 
