@@ -313,8 +313,17 @@ def test_wrapper_errors(gpu_lib):
 
     q = torch.zeros(1, 1, 4, 64, device="cuda", dtype=torch.bfloat16)
     k = torch.zeros(1, 1, 5, 64, device="cuda", dtype=torch.bfloat16)
-    with pytest.raises(RuntimeError, match="causal"):
+    # causal with n != m: the binding refuses before any entry point (ValueError);
+    # the C ABI refuses the same call with SDPA_ERR_MASK
+    with pytest.raises(ValueError, match="causal"):
         forward(q, k, k, causal=True)
+    from transformer_attention_sdpa_amd import _lib, sdpa_forward
+
+    o = torch.empty_like(q)
+    rc = sdpa_forward(q.data_ptr(), k.data_ptr(), k.data_ptr(), o.data_ptr(), 1, 1, 4, 5, 64, 64,
+                      0.125, _lib.SDPA_MASK_CAUSAL, None, _lib.SDPA_BF16,
+                      torch.cuda.current_stream().cuda_stream)
+    assert rc == _lib.SDPA_ERR_MASK
     # widths: 64 everywhere, 32 and 128 in bf16 only, nothing else
     q16 = torch.zeros(1, 1, 4, 16, device="cuda", dtype=torch.bfloat16)
     with pytest.raises(RuntimeError, match="64"):
