@@ -13,6 +13,7 @@ from transformer_attention_sdpa_amd import _lib
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 C_PROGRAM = r"""
+#include <stdint.h>
 #include <stdio.h>
 #include <string.h>
 #include "sdpa.h"
@@ -22,7 +23,7 @@ C_PROGRAM = r"""
 
 int main(void) {
     /* fake, 16-byte aligned device addresses: validation rejects before any HIP call */
-    char* base = (char*)0 + (1 << 20);
+    char* base = (char*)(uintptr_t)(1u << 20);
     const void* q = base; const void* k = base + (1 << 20); const void* v = base + (2 << 20);
     void* out = base + (3 << 20);
     CHECK(sdpa_forward(NULL, k, v, out, 2, 2, 8, 8, 64, 64, 0.125f, SDPA_MASK_NONE, NULL, SDPA_BF16, NULL),
