@@ -46,6 +46,11 @@ extern "C" {
 #define SDPA_ERR_SCALE       -8 /* scale is not finite, or not > 0                   */
 #define SDPA_ERR_ALIAS       -9 /* out overlaps q, k, v or key_lens                   */
 #define SDPA_ERR_WORKSPACE  -10 /* workspace smaller than its *_workspace_bytes size */
+#define SDPA_ERR_SCRATCH    -11 /* a call needs more than the library's static scratch */
+
+/* Size of the library's static device scratch (per GPU), used by
+ * sdpa_forward_ex_noalloc in place of a caller's workspace. */
+#define SDPA_NOALLOC_SCRATCH_BYTES (8u << 20)
 
 /* Element types (input and output share one type). */
 #define SDPA_F32  0 /* fp32 in, fp32 arithmetic, fp32 out                          */
@@ -225,6 +230,36 @@ SDPA_API int sdpa_forward_ex(const void* q, const void* k, const void* v, void* 
                              float scale, int32_t window_left, int32_t window_right, int32_t align,
                              const int32_t* key_lens, int32_t dtype, void* workspace,
                              size_t workspace_bytes, void* stream);
+
+/*
+ * sdpa_forward_ex_noalloc — sdpa_forward_ex for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight decoder-step serving
+ * loops, harnesses that forbid hipMalloc): the same call and the same kernels,
+ * but the split-key workspace is the library's own static device array of
+ * SDPA_NOALLOC_SCRATCH_BYTES, one per GPU, held until the process ends.
+ *
+ * Arguments as in sdpa_forward_ex, without workspace and workspace_bytes.
+ * When sdpa_forward_workspace_bytes(...) is 0 the call uses no scratch and is
+ * sdpa_forward_ex with workspace = NULL.  When it exceeds
+ * SDPA_NOALLOC_SCRATCH_BYTES the call returns SDPA_ERR_SCRATCH before any HIP
+ * call and launches nothing.  The output is bitwise that of sdpa_forward_ex
+ * with a workspace.
+ *
+ * Allocates nothing and calls no allocating routine.  The first call on a
+ * device looks up that device's copy of the array (hipGetSymbolAddress, on
+ * the calling thread's current device); make that first call outside graph
+ * capture.  Every call on one GPU shares its array and leaves its contents
+ * there (no call needs it zeroed: each call's merge launch reads only what its
+ * own split launch wrote): calls that may overlap on one GPU (other streams,
+ * other host threads) race on it and must be serialised by the caller, e.g.
+ * by issuing them on one stream.  A runtime error in the lookup returns
+ * SDPA_ERR_LAUNCH.
+ */
+SDPA_API int sdpa_forward_ex_noalloc(const void* q, const void* k, const void* v, void* out, float* lse,
+                                     int32_t B, int32_t h, int32_t n, int32_t m, int32_t d_k,
+                                     int32_t d_v, float scale, int32_t window_left,
+                                     int32_t window_right, int32_t align, const int32_t* key_lens,
+                                     int32_t dtype, void* stream);
 
 /*
  * sdpa_backward — the gradient of Eq. (1) (bf16).  The pages train the model

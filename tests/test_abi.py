@@ -31,7 +31,8 @@ def test_every_declared_entry_point_is_exported(lib):
     assert set(names) == {"sdpa_forward", "sdpa_forward_window", "sdpa_mha_forward",
                           "sdpa_mha_workspace_bytes", "sdpa_forward_lse", "sdpa_backward",
                           "sdpa_backward_workspace_bytes", "sdpa_forward_ex",
-                          "sdpa_forward_workspace_bytes", "sdpa_strerror", "sdpa_version"}
+                          "sdpa_forward_ex_noalloc", "sdpa_forward_workspace_bytes",
+                          "sdpa_strerror", "sdpa_version"}
     for name in names:
         assert isinstance(getattr(lib, name), ctypes._CFuncPtr)
 
@@ -248,6 +249,44 @@ def call_ex(**kw):
 ])
 def test_forward_ex_validation_rejects_before_any_hip_call(kw, code, lib):
     assert call_ex(**kw) == code
+
+
+def call_noalloc(**kw):
+    a = dict(q=G, k=2 * G, v=3 * G, out=4 * G, lse=None, B=32, h=8, n=1, m=4096, d_k=64, d_v=64,
+             scale=0.125, wl=-1, wr=0, align=1, key_lens=None, dtype=1)
+    a.update(kw)
+    return _lib.sdpa_forward_ex_noalloc(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["h"],
+                                        a["n"], a["m"], a["d_k"], a["d_v"], a["scale"], a["wl"],
+                                        a["wr"], a["align"], a["key_lens"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), _lib.SDPA_ERR_NULL),
+    (dict(out=4 * G + 8), _lib.SDPA_ERR_ALIGN),
+    (dict(out=G), _lib.SDPA_ERR_ALIAS),
+    (dict(lse=6 * G, dtype=0), _lib.SDPA_ERR_UNSUPPORTED),
+    (dict(lse=6 * G + 1), _lib.SDPA_ERR_ALIGN),
+    (dict(lse=G), _lib.SDPA_ERR_ALIAS),
+    (dict(wl=-4), _lib.SDPA_ERR_MASK),
+    (dict(align=7), _lib.SDPA_ERR_MASK),
+    (dict(scale=float("nan")), _lib.SDPA_ERR_SCALE),
+    (dict(d_k=16, d_v=16), _lib.SDPA_ERR_UNSUPPORTED),
+    # a split needing 64 pieces x 512 heads x 16 queries x 272 bytes = 142 MB > 8 MiB
+    (dict(B=64, n=16, m=65536), _lib.SDPA_ERR_SCRATCH),
+])
+def test_forward_ex_noalloc_validation_rejects_before_any_hip_call(kw, code, lib):
+    assert call_noalloc(**kw) == code
+
+
+def test_noalloc_scratch_limit_covers_the_decoder_workloads(lib):
+    """The static scratch holds the split workspace of the decoder-step shapes:
+    256 heads of 8192 keys, one sequence of 8 heads over 32768 keys, and 8
+    heads x 4 queries over 131072 keys; past it the call refuses."""
+    for (B, h, n, m) in ((32, 8, 1, 8192), (1, 8, 1, 32768), (1, 8, 4, 131072)):
+        need = _lib.sdpa_forward_workspace_bytes(B, h, n, m, 64, 64, _lib.SDPA_BF16)
+        assert 0 < need <= _lib.SDPA_NOALLOC_SCRATCH_BYTES
+    assert "SDPA_NOALLOC_SCRATCH_BYTES" in _lib.sdpa_strerror(_lib.SDPA_ERR_SCRATCH)
+    assert re.search(r"#define\s+SDPA_NOALLOC_SCRATCH_BYTES\s+\(8u << 20\)", _header())
 
 
 def call_bwd(**kw):

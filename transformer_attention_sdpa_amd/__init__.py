@@ -13,12 +13,13 @@ import math
 
 from . import _lib
 from ._lib import (sdpa_backward, sdpa_backward_workspace_bytes, sdpa_forward,  # noqa: F401
-                   sdpa_forward_ex, sdpa_forward_lse, sdpa_forward_window,
+                   sdpa_forward_ex, sdpa_forward_ex_noalloc, sdpa_forward_lse, sdpa_forward_window,
                    sdpa_forward_workspace_bytes, sdpa_mha_forward,
                    sdpa_mha_workspace_bytes, sdpa_strerror, sdpa_version)
 
 __all__ = ["forward", "backward", "mha_forward", "sdpa_forward", "sdpa_forward_window",
-           "sdpa_forward_lse", "sdpa_forward_ex", "sdpa_forward_workspace_bytes",
+           "sdpa_forward_lse", "sdpa_forward_ex", "sdpa_forward_ex_noalloc",
+           "sdpa_forward_workspace_bytes",
            "sdpa_backward", "sdpa_backward_workspace_bytes",
            "sdpa_mha_forward", "sdpa_mha_workspace_bytes", "sdpa_strerror", "sdpa_version"]
 

@@ -25,6 +25,8 @@ SDPA_ERR_LAUNCH = -7
 SDPA_ERR_SCALE = -8
 SDPA_ERR_ALIAS = -9
 SDPA_ERR_WORKSPACE = -10
+SDPA_ERR_SCRATCH = -11
+SDPA_NOALLOC_SCRATCH_BYTES = 8 << 20
 SDPA_F32 = 0
 SDPA_BF16 = 1
 SDPA_MASK_NONE = 0
@@ -66,6 +68,9 @@ def load() -> ctypes.CDLL:
     lib.sdpa_forward_ex.argtypes = [vp, vp, vp, vp, fp, i32, i32, i32, i32, i32, i32, ctypes.c_float,
                                     i32, i32, i32, vp, i32, vp, ctypes.c_size_t, vp]
     lib.sdpa_forward_ex.restype = ctypes.c_int
+    lib.sdpa_forward_ex_noalloc.argtypes = [vp, vp, vp, vp, fp, i32, i32, i32, i32, i32, i32,
+                                            ctypes.c_float, i32, i32, i32, vp, i32, vp]
+    lib.sdpa_forward_ex_noalloc.restype = ctypes.c_int
     lib.sdpa_backward_workspace_bytes.argtypes = [i32, i32, i32]
     lib.sdpa_backward_workspace_bytes.restype = ctypes.c_size_t
     lib.sdpa_backward.argtypes = [vp, vp, vp, vp, vp, fp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
@@ -125,6 +130,14 @@ def sdpa_forward_ex(q, k, v, out, lse, B, h, n, m, d_k, d_v, scale, window_left,
     return load().sdpa_forward_ex(q, k, v, out, lse, B, h, n, m, d_k, d_v, scale, window_left,
                                   window_right, align, key_lens, dtype, workspace, workspace_bytes,
                                   stream)
+
+
+def sdpa_forward_ex_noalloc(q, k, v, out, lse, B, h, n, m, d_k, d_v, scale, window_left,
+                            window_right, align, key_lens, dtype, stream) -> int:
+    """Forward to the C entry point of the same name (sdpa_forward_ex with the
+    library's static scratch in place of a workspace; allocates nothing)."""
+    return load().sdpa_forward_ex_noalloc(q, k, v, out, lse, B, h, n, m, d_k, d_v, scale,
+                                          window_left, window_right, align, key_lens, dtype, stream)
 
 
 def sdpa_backward_workspace_bytes(B, h, n) -> int:

@@ -7,12 +7,13 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "sdpa_common.hpp"
 
 namespace {
 
-constexpr int kVersion = 1 * 10000 + 3 * 100 + 0;  // 1.3.0: log-sum-exp output, backward pass
+constexpr int kVersion = 1 * 10000 + 4 * 100 + 0;  // 1.4.0: sdpa_forward_ex_noalloc
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -291,6 +292,68 @@ extern "C" int sdpa_mha_forward(const void* x_q, const void* x_kv, const void* w
     return e == hipSuccess ? SDPA_OK : SDPA_ERR_LAUNCH;
 }
 
+// ---- sdpa_forward_ex_noalloc: the split-key workspace in static device memory.
+//
+// One array per GPU (each device that loads the library holds its own copy),
+// reached through its device address, never through the host-side name.
+static __device__ __align__(256) unsigned char scratch[SDPA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+// The current device's copy of `scratch`, looked up once per device; nullptr
+// on a runtime error.
+void* scratch_on_current_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+        g_scratch[dev] = p;
+    }
+    return g_scratch[dev];
+}
+
+}  // namespace
+
+extern "C" int sdpa_forward_ex_noalloc(const void* q, const void* k, const void* v, void* out,
+                                       float* lse, int32_t B, int32_t h, int32_t n, int32_t m,
+                                       int32_t d_k, int32_t d_v, float scale, int32_t window_left,
+                                       int32_t window_right, int32_t align,
+                                       const int32_t* key_lens, int32_t dtype, void* stream) {
+    int st = validate(q, k, v, out, B, h, n, m, d_k, d_v, scale, key_lens, dtype);
+    if (st != SDPA_OK) return st;
+    int32_t wl, wr, br;
+    st = window_args(n, m, window_left, window_right, align, &wl, &wr, &br);
+    if (st != SDPA_OK) return st;
+    if (lse) {
+        if (dtype != SDPA_BF16) return SDPA_ERR_UNSUPPORTED;
+        if (reinterpret_cast<uintptr_t>(lse) & 3u) return SDPA_ERR_ALIGN;
+        const uint64_t heads = (uint64_t)B * h, esz = dtype == SDPA_F32 ? 4 : 2;
+        const struct { const void* p; uint64_t n; } ins[] = {
+            {q, heads * n * d_k * esz}, {k, heads * m * d_k * esz}, {v, heads * m * d_v * esz},
+            {out, heads * n * d_v * esz}, {key_lens, key_lens ? (uint64_t)B * 4 : 0}};
+        for (const auto& b : ins)
+            if (b.p && overlap(lse, heads * n * 4, b.p, b.n)) return SDPA_ERR_ALIAS;
+    }
+    const size_t need = forward_work_bytes(B, h, n, m, d_k, d_v, dtype);
+    if (need > SDPA_NOALLOC_SCRATCH_BYTES) return SDPA_ERR_SCRATCH;
+    sdpa::Args a{q, k, v, out, B, h, n, m, scale, wl, wr, br, key_lens};
+    a.lse = lse;
+    a.d = d_k;
+    if (need > 0) {
+        void* work = scratch_on_current_device();
+        if (!work) return SDPA_ERR_LAUNCH;
+        a.work = work;
+        a.work_bytes = SDPA_NOALLOC_SCRATCH_BYTES;
+    }
+    return launch(a, dtype, stream);
+}
+
 extern "C" const char* sdpa_strerror(int status) {
     switch (status) {
         case SDPA_OK: return "ok";
@@ -307,6 +370,9 @@ extern "C" const char* sdpa_strerror(int status) {
         case SDPA_ERR_SCALE: return "scale must be finite and > 0";
         case SDPA_ERR_ALIAS: return "out overlaps an input (or, for the sublayer, the workspace)";
         case SDPA_ERR_WORKSPACE: return "workspace smaller than its *_workspace_bytes size";
+        case SDPA_ERR_SCRATCH:
+            return "the call needs more split-key scratch than the library's static "
+                   "SDPA_NOALLOC_SCRATCH_BYTES (use sdpa_forward_ex with a workspace)";
         default: return "unknown status";
     }
 }
