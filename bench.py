@@ -5,11 +5,13 @@ A "step" is one sdpa_forward over one batch of the workload (every step of the
 path: staging, scores, masking, online softmax, weighted sum, store).  Inputs
 are seeded synthetic N(0,1) tensors already resident in HBM; the timed steps
 rotate over enough copies of the batch (> 2× the 256 MB Infinity Cache) that
-the data really streams from HBM, and a read of twice the cache's size runs
-just before the timed replay, so the sets it touches first are cold too, at
-any step count.  The K timed steps are captured in one HIP
-graph (the launches are a few microseconds each, below Python's call rate) and
-timed with HIP events on the stream they run on.
+the data really streams from HBM, and a 2 GiB read runs just before the timed
+steps, so the sets they touch first are cold too, at any step count.  The K
+timed steps are launched one after another behind that read (about 0.3 ms,
+long enough for the host to enqueue all of them, so the kernels run back to
+back) and timed with HIP events on the stream they run on.  The same steps
+replayed from a HIP graph, and a graph replay of two passes over every set,
+are reported beside them as cross-checks.
 
 Prints ONE JSON line.  Default workload: the base-model encoder self-attention
 batch (B=64, h=8, n=m=64, d_k=d_v=64, bf16, key padding U[8,64]).
@@ -106,35 +108,51 @@ def measured_traffic(workload, dtype):
 
 
 class CacheFlush:
-    """Evicts the Infinity Cache (and L2) before a timed replay: a read of twice
-    the cache's size on the timing stream.  It only reads, so it leaves no
-    dirty lines whose write-back would land in the timed region.  The timed
-    steps then find none of their sets resident, whatever set the untimed
-    replays touched last."""
+    """Evicts the Infinity Cache (and L2) before a timed region: a read of eight
+    times the cache's size (2 GiB, about 0.3 ms) on the timing stream.  It only
+    reads, so it leaves no dirty lines whose write-back would land in the
+    timed region, and it runs long enough for the host to enqueue every timed
+    launch behind it."""
 
     def __init__(self, dev):
         import torch
 
-        self.src = torch.ones(INFINITY_CACHE_BYTES * 2 // 8, dtype=torch.int64, device=dev)
+        self.src = torch.ones(INFINITY_CACHE_BYTES, dtype=torch.int64, device=dev)
         self.nbytes = 8 * self.src.numel()
 
     def __call__(self):
         self.src.sum()
 
 
-def timed_replay(graph, flush):
-    """HIP-event time of one replay of ``graph`` on the current stream (ms),
-    right after a cache flush (not timed).  A GPU-side wait of about 0.1 ms is
-    queued ahead of the start event, so the host's graph launch has finished
-    before the first timed kernel is due: the timed region holds the replayed
-    kernels back to back and no host launch latency."""
+def timed_launches(launch, steps, stream, flush):
+    """HIP-event time (ms) of ``steps`` launches issued one after another on
+    ``stream`` right behind a cache flush.  The host enqueues them while the
+    flush still runs, so the timed region holds the kernels back to back."""
     import torch
 
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     flush()
-    torch.cuda._sleep(250_000)  # GPU cycles
+    e0.record()
+    for i in range(steps):
+        launch(i, stream)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1)
+
+
+def timed_replay(graph, flush):
+    """HIP-event time (ms) of one replay of ``graph`` on the current stream,
+    right behind a cache flush.  A replay carries a fixed cost of its own
+    (about 15 µs here), so short replays read high per step; it is reported
+    as a cross-check."""
+    import torch
+
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    flush()
     e0.record()
     graph.replay()
     e1.record()
@@ -235,8 +253,9 @@ def time_workload(name, dtype, steps, warmup, clock_warm_s=0.0, case=None, split
 
     flush = CacheFlush(dev)
     w0 = time.perf_counter()
-    graph_ms = timed_replay(graph, flush)
+    step_ms = timed_launches(launch, steps, stream, flush)
     wall = time.perf_counter() - w0
+    graph_ms = timed_replay(graph, flush)
 
     # Cross-check over a long rotation: two full passes over every set (at
     # least twice the Infinity Cache of timed bytes whatever --steps is).
@@ -250,30 +269,18 @@ def time_workload(name, dtype, steps, warmup, clock_warm_s=0.0, case=None, split
     torch.cuda.synchronize()
     rot_ms = timed_replay(graph_rot, flush)
 
-    # Same steps launched one by one from Python (host launch rate included).
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    flush()
-    e0.record()
-    for i in range(steps):
-        launch(i, stream)
-    e1.record()
-    torch.cuda.synchronize()
-    eager_ms = e0.elapsed_time(e1)
-
     flops, nbytes, dense = algorithmic_work(wl, dtype, case["key_lens"])
-    t = graph_ms / 1e3 / steps
+    t = step_ms / 1e3 / steps
     del graph, graph_rot, sets, flush
     torch.cuda.empty_cache()
     return {
         "workload": name, "dtype": dtype, "steps": steps, "sets_rotated": nsets,
-        "ms_per_step": graph_ms / steps, "ms_per_step_eager": eager_ms / steps,
+        "ms_per_step": step_ms / steps, "ms_per_step_graph": graph_ms / steps,
         "bytes_touched_timed": nbytes * steps,
         "distinct_sets_timed": min(steps, nsets),
-        "flushed_before_timing_bytes": 2 * INFINITY_CACHE_BYTES,
+        "flushed_before_timing_bytes": 8 * INFINITY_CACHE_BYTES,
         "long_rotation": {"steps": rot, "ms_per_step": rot_ms / rot,
-                          "bytes_touched_timed": nbytes * rot},
+                          "bytes_touched_timed": nbytes * rot, "timing": "graph replay"},
         "wall_s_timed": wall,
         "alg_flops": flops, "dense_flops": dense, "alg_bytes": nbytes,
         "tflops": flops / t / 1e12, "gbs": nbytes / t / 1e9,
@@ -370,10 +377,13 @@ def time_backward(name, steps, warmup, clock_warm_s=0.1):
     while time.perf_counter() < t_warm:
         graph.replay()
         torch.cuda.synchronize()
-    t = timed_replay(graph, CacheFlush(dev)) / 1e3 / steps
-    del graph, sets
+    flush = CacheFlush(dev)
+    t = timed_launches(launch, steps, stream, flush) / 1e3 / steps
+    t_graph = timed_replay(graph, flush) / 1e3 / steps
+    del graph, sets, flush
     torch.cuda.empty_cache()
-    return {"ms_per_step": t * 1e3, "tflops": flops / t / 1e12, "gbs": nbytes / t / 1e9,
+    return {"ms_per_step": t * 1e3, "ms_per_step_graph": t_graph * 1e3,
+            "tflops": flops / t / 1e12, "gbs": nbytes / t / 1e9,
             "alg_flops": flops, "alg_bytes": nbytes,
             "frac_mfma_peak": flops / t / 1e12 / PEAK_TFLOPS["bf16"],
             "frac_hbm_peak": nbytes / t / 1e9 / PEAK_HBM_GBS, "steps": steps, "sets_rotated": nsets,
@@ -457,10 +467,13 @@ def time_mha(name, steps, warmup, clock_warm_s=0.1):
     while time.perf_counter() < t_warm:
         graph.replay()
         torch.cuda.synchronize()
-    t = timed_replay(graph, CacheFlush(dev)) / 1e3 / steps
-    del graph, sets
+    flush = CacheFlush(dev)
+    t = timed_launches(launch, steps, stream, flush) / 1e3 / steps
+    t_graph = timed_replay(graph, flush) / 1e3 / steps
+    del graph, sets, flush
     torch.cuda.empty_cache()
-    return {"ms_per_step": t * 1e3, "tflops": flops / t / 1e12, "gbs": nbytes / t / 1e9,
+    return {"ms_per_step": t * 1e3, "ms_per_step_graph": t_graph * 1e3,
+            "tflops": flops / t / 1e12, "gbs": nbytes / t / 1e9,
             "frac_mfma_peak": flops / t / 1e12 / PEAK_TFLOPS["bf16"],
             "frac_hbm_peak": nbytes / t / 1e9 / PEAK_HBM_GBS, "steps": steps, "sets_rotated": nsets,
             "launches_per_step": 3}
@@ -833,7 +846,7 @@ def main():
                               case=cases[name, dt])
             extra[f"{name}-{dt}"] = {k: r[k] for k in (
                 "ms_per_step", "tflops", "gbs", "frac_mfma_peak", "frac_hbm_peak", "steps",
-                "sets_rotated", "ms_per_step_eager", "bytes_touched_timed", "long_rotation")}
+                "sets_rotated", "ms_per_step_graph", "bytes_touched_timed", "long_rotation")}
             if args.no_cpu_baseline:
                 del cases[name, dt]
         # decoder steps with each head's keys split over several workgroups
@@ -842,7 +855,7 @@ def main():
             r = time_workload(name, "bf16", 20, min(args.warmup, 5), clock_warm_s=0.1, split=True)
             extra[f"{name}-bf16-split"] = {k: r[k] for k in (
                 "ms_per_step", "tflops", "gbs", "frac_mfma_peak", "frac_hbm_peak", "steps",
-                "sets_rotated", "ms_per_step_eager")}
+                "sets_rotated", "ms_per_step_graph")}
         for name in ("encoder_self_base", "long_causal_8k"):
             extra[f"backward-{name}-bf16"] = time_backward(
                 name, 20 if name.endswith("_8k") else max(10, min(args.steps, 200)), min(args.warmup, 3))
@@ -884,7 +897,7 @@ def main():
         "alg_flops_per_step": head["alg_flops"],
         "frac_hbm_peak": head["frac_hbm_peak"],
         "frac_mfma_peak": head["frac_mfma_peak"],
-        "ms_per_step_eager": head["ms_per_step_eager"],
+        "ms_per_step_graph": head["ms_per_step_graph"],
         "sets_rotated": head["sets_rotated"],
         "bytes_touched_timed": head["bytes_touched_timed"],
         "distinct_sets_timed": head["distinct_sets_timed"],
