@@ -42,7 +42,7 @@ extern "C" {
 #define SDPA_ERR_ALIGN       -4 /* a pointer is not 16-byte aligned                  */
 #define SDPA_ERR_MASK        -5 /* unknown mask_kind, causal with n != m, bad window */
 #define SDPA_ERR_DTYPE       -6 /* unknown dtype                                     */
-#define SDPA_ERR_LAUNCH      -7 /* the HIP runtime refused the kernel launch         */
+#define SDPA_ERR_LAUNCH      -7 /* the HIP runtime refused this call's kernel launch */
 #define SDPA_ERR_SCALE       -8 /* scale is not finite, or not > 0                   */
 #define SDPA_ERR_ALIAS       -9 /* out overlaps q, k, v or key_lens                   */
 #define SDPA_ERR_WORKSPACE  -10 /* workspace smaller than its *_workspace_bytes size */
@@ -96,7 +96,10 @@ extern "C" {
  * `stream`: it validates the arguments on the host (before any HIP call),
  * enqueues one kernel, and returns.  It allocates nothing, keeps no pointer
  * after returning, holds no mutable global state and is thread-safe.  The
- * caller owns every buffer.  Returns SDPA_OK or a negative status.
+ * caller owns every buffer.  Returns SDPA_OK or a negative status.  Before
+ * launching, every entry point clears the thread's pending HIP error (left by
+ * earlier, unrelated calls that no one collected), so SDPA_ERR_LAUNCH always
+ * means that this call's own launch was refused.
  */
 SDPA_API int sdpa_forward(const void* q, const void* k, const void* v, void* out,
                  int32_t B, int32_t h, int32_t n, int32_t m, int32_t d_k, int32_t d_v,

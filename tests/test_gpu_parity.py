@@ -333,6 +333,36 @@ def test_wrapper_errors(gpu_lib):
         forward(q32f, q32f, q32f)
 
 
+def test_pending_hip_error_is_not_reported_as_a_launch_failure(gpu_lib):
+    """A failed HIP call that no one collected leaves an error pending on the
+    thread; the library's own launch must still report SDPA_OK (it clears the
+    pending error before launching) and produce the right output.  The pending
+    error comes from hipSetDevice with an ordinal no device has (a host-side
+    refusal, nothing reaches the GPU), through the HIP runtime already loaded
+    in this process."""
+    import ctypes
+
+    import torch
+
+    from transformer_attention_sdpa_amd import _lib, sdpa_forward
+
+    maps = open("/proc/self/maps", encoding="utf-8").read().splitlines()
+    paths = sorted({ln.split()[-1] for ln in maps if "libamdhip64" in ln})
+    assert len(paths) == 1, paths
+    hip = ctypes.CDLL(paths[0])
+    hip.hipSetDevice.argtypes = [ctypes.c_int]
+    assert hip.hipSetDevice(12345) != 0
+    case = random_case(np.random.default_rng(77), 2, 2, 40, 40, 64, 64, dtype="bf16")
+    q, k, v = (to_device(case[x], "bf16") for x in ("q", "k", "v"))
+    o = torch.empty_like(q)
+    rc = sdpa_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), 2, 2, 40, 40, 64, 64,
+                      0.125, _lib.SDPA_MASK_NONE, None, _lib.SDPA_BF16,
+                      torch.cuda.current_stream().cuda_stream)
+    assert rc == _lib.SDPA_OK, _lib.sdpa_strerror(rc)
+    torch.cuda.synchronize()
+    assert max_abs_err(from_device(o), _oracle(case)) <= TOL["bf16"]
+
+
 def test_concurrent_calls_on_separate_streams(gpu_lib):
     """The library keeps no state: calls from several host threads, each on its
     own stream, give the same bits as one call at a time."""

@@ -57,8 +57,15 @@ int validate(const void* q, const void* k, const void* v, void* out, int32_t B, 
     return SDPA_OK;
 }
 
+// Each launcher reports hipGetLastError after its launches.  That status is
+// per thread and also holds errors of earlier, unrelated HIP calls that no one
+// collected; it is cleared first so that SDPA_ERR_LAUNCH means this call's own
+// launch was refused.
+void clear_pending_error() { (void)hipGetLastError(); }
+
 int launch(const sdpa::Args& a, int32_t dtype, void* stream) {
     const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    clear_pending_error();
     const hipError_t e = dtype == SDPA_BF16 ? sdpa::launch_bf16(a, s) : sdpa::launch_f32(a, s);
     return e == hipSuccess ? SDPA_OK : SDPA_ERR_LAUNCH;
 }
@@ -239,6 +246,7 @@ extern "C" int sdpa_backward(const void* q, const void* k, const void* v, const 
     }
     const sdpa::BwdArgs a{q, k, v, out, dout, lse, dq, dk, dv, workspace, B, h, n, m, scale, wl, wr, br,
                           key_lens, d_k};
+    clear_pending_error();
     const hipError_t e = sdpa::launch_bwd_bf16(a, reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? SDPA_OK : SDPA_ERR_LAUNCH;
 }
@@ -288,6 +296,7 @@ extern "C" int sdpa_mha_forward(const void* x_q, const void* x_kv, const void* w
                           window_left > reach ? -1 : window_left,
                           window_right > reach ? -1 : window_right,
                           align == SDPA_ALIGN_BOTTOM_RIGHT ? 1 : 0, key_lens, d_k};
+    clear_pending_error();
     const hipError_t e = sdpa::launch_mha_bf16(a, reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? SDPA_OK : SDPA_ERR_LAUNCH;
 }

@@ -230,7 +230,11 @@ __global__ __launch_bounds__(256) void proj_gemm_bf16(ProjJobs jobs) {
     // along rows instead of 8-byte pieces of 32 different rows.  Register r of
     // acc[i][j] is feature 32·j + 8·(r/4) + 4·hf + r%4 (of the wave's feature
     // block) of token 32·i + l32 (of its token block); the tile row of a token
-    // holds TN features, 16-byte chunk c at position c ^ (row mod CPR).
+    // holds TN features in 8-byte pieces, piece s at s ^ (row mod 16).  LDS
+    // takes 128 bytes of writes per cycle (16 lanes of 8 bytes) and they must
+    // fall on distinct 8-byte positions modulo 128: the 16 rows one write
+    // cycle covers then never collide.  16-byte chunk c of a row is read from
+    // chunk c ^ ((row mod 16) / 2), its halves swapped when the row is odd.
     constexpr int CPR = TN / 8;
     __syncthreads();
 #pragma unroll
@@ -246,8 +250,7 @@ __global__ __launch_bounds__(256) void proj_gemm_bf16(ProjJobs jobs) {
                 o[1] = (__bf16)acc[i][j][4 * i4 + 1];
                 o[2] = (__bf16)acc[i][j][4 * i4 + 2];
                 o[3] = (__bf16)acc[i][j][4 * i4 + 3];
-                const int pos = (col >> 3) ^ (row & (CPR - 1));
-                *reinterpret_cast<bf16x4*>(lds + (row * CPR + pos) * 16 + (col & 7) * 2) = o;
+                *reinterpret_cast<bf16x4*>(lds + row * CPR * 16 + (((col >> 2) ^ (row & 15)) * 8)) = o;
             }
     }
     __syncthreads();
@@ -257,7 +260,8 @@ __global__ __launch_bounds__(256) void proj_gemm_bf16(ProjJobs jobs) {
         const int id = tid + 256 * k;
         const int row = id / CPR, c = id % CPR;
         const int tok = t0 + row, f = f0 + 8 * c;
-        const u32x4 x = *reinterpret_cast<const u32x4*>(lds + (row * CPR + (c ^ (row & (CPR - 1)))) * 16);
+        const u32x4 y = *reinterpret_cast<const u32x4*>(lds + (row * CPR + (c ^ ((row & 15) >> 1))) * 16);
+        const u32x4 x = (row & 1) ? u32x4{y[2], y[3], y[0], y[1]} : y;
         if (tok >= J.M || f >= J.N) continue;
         size_t dst;
         if (CMODE == ROWS) {
