@@ -29,6 +29,17 @@ CASES = [  # id, (B, h, n, m, d), options
     ("d128_bottom_right", (4, 2, 5, 200, 128), dict(window=(None, 0, "bottom_right"), key_lens=(0, 200))),
     ("d32_four_wave_blocks", (8, 16, 1024, 1024, 32), dict(causal=True)),
     ("d128_four_wave_blocks", (8, 16, 1024, 1024, 128), dict(causal=True)),
+    # sentence-length kernel (n, m <= 64) at both widths: windows in both
+    # alignments, key lengths 0 and past m, ragged lengths, a lone query and
+    # key, and queries that leave waves idle (n < 16, 33, 48)
+    ("d32_short_window", (3, 2, 64, 64, 32), dict(window=(5, 3))),
+    ("d128_short_window_causal_like", (3, 2, 40, 40, 128), dict(window=(None, 0), key_lens=(0, 40))),
+    ("d128_short_bottom_right", (3, 2, 7, 50, 128), dict(window=(None, 0, "bottom_right"), key_lens=(0, 60))),
+    ("d32_short_bottom_right_band", (2, 3, 12, 64, 32), dict(window=(6, 2, "bottom_right"), key_lens=(1, 64))),
+    ("d128_short_ragged", (2, 3, 33, 17, 128), dict(key_lens=(0, 20))),
+    ("d32_short_ragged_causal", (3, 1, 63, 63, 32), dict(causal=True, key_lens=(1, 63))),
+    ("d32_short_one_by_one", (1, 1, 1, 1, 32), {}),
+    ("d128_short_one_by_one", (2, 1, 1, 1, 128), dict(key_lens=(0, 1))),
 ]
 
 
@@ -155,3 +166,44 @@ def test_width_backward_deterministic(gpu_lib):
     torch.cuda.synchronize()
     for x, y in zip(a, b):
         assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+
+
+@pytest.mark.parametrize("d", [32, 128])
+def test_short_width_padded_keys_are_never_read(gpu_lib, d):
+    """Sentence-length kernel at width 32 and 128: NaN and huge values in the
+    K/V rows at or past each key length leave the output bitwise unchanged."""
+    import torch
+
+    rng = np.random.default_rng(90 + d)
+    B, h, n, m = 3, 2, 48, 64
+    kl = np.array([m, 9, 40], np.int32)
+    c = random_case(rng, B, h, n, m, d, d, dtype="bf16", key_lens=kl)
+    o1, _ = run_gpu(c)
+    for b in range(B):
+        c["k"][b, :, kl[b]:] = np.nan
+        c["v"][b, :, kl[b]:] = 3e38
+    o2, got2 = run_gpu(c)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert np.isfinite(got2).all()
+
+
+def test_short_width_masked_weights_are_exactly_zero(gpu_lib):
+    """Width 128 holds the whole weight row (m = 64 <= d_v): V = [I | 0] makes
+    O[:, :m] the weights, and every masked one must be +0.0 (causal and key
+    padding on the sentence-length kernel)."""
+    rng = np.random.default_rng(91)
+    B, h, n, m, d = 4, 2, 64, 64, 128
+    kl = np.array([64, 17, 1, 40], np.int32)
+    c = random_case(rng, B, h, n, m, d, d, dtype="bf16", causal=True, key_lens=kl)
+    c["v"] = np.zeros_like(c["v"])
+    c["v"][:, :, np.arange(m), np.arange(m)] = 1.0
+    _, got = run_gpu(c)
+    j = np.arange(m)
+    for b in range(B):
+        for i in range(n):
+            vis = (j < kl[b]) & (j <= i)
+            row = got[b, :, i, :m]
+            assert np.all(row[:, ~vis] == 0.0) and not np.signbit(row[:, ~vis]).any()
+            assert np.allclose(row.sum(-1), 1.0, atol=4 * TOL["bf16"])
+    assert np.all(got[..., m:] == 0.0)
+    assert max_abs_err(got, so.attention(c["q"], c["k"], c["v"], causal=True, key_lens=kl)) <= TOL["bf16"]

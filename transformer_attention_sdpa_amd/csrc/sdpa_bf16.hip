@@ -423,8 +423,8 @@ hipError_t launch_bf16_long(const Args& a, hipStream_t stream) {
 }
 
 hipError_t launch_bf16(const Args& a, hipStream_t stream) {
+    if (short_bf16_fits(a)) return launch_bf16_short(a, stream);  // n, m <= 64, any width
     if (a.d != D) return launch_bf16_width(a, stream);
-    if (short_bf16_fits(a)) return launch_bf16_short(a, stream);
     if (decode_bf16_fits(a)) return launch_bf16_decode(a, stream);
     return launch_bf16_long(a, stream);
 }

@@ -31,6 +31,11 @@
 //     max/sum are lane-local plus two half/quarter-wave exchanges, and Vᵀ comes
 //     from LDS transpose reads (ds_read_b64_tr_b16).
 //
+// The head width D (d_k = d_v) is a template parameter: 64 (the base and big
+// models), or 32 and 128 (the variants of the same page's Table 3, rows (A)
+// and (C)).  Only the number of k-steps, of output tiles and of loads per
+// wave, and the LDS swizzle, depend on it.
+//
 // Same arithmetic contract as the long kernel: fp32 scores and softmax, −∞ on
 // illegal logits (《Attention Is All You Need：注意力就是你所需要的一切》
 // §3.2.3) — the keys outside each query's window (KeyWindow) and past the key
@@ -41,13 +46,32 @@
 namespace sdpa {
 namespace {
 
-constexpr int D = kHeadDim;  // 64
 constexpr int MAXLEN = 64;   // n and m bound of this kernel
 constexpr int QW = 16;       // queries per wave
 constexpr int NW = 4;        // waves per workgroup (4 × 16 = 64 queries)
 constexpr int NT = NW * 64;
 
-__device__ __forceinline__ int swz(int row, int chunk) { return lds_swz(row, chunk); }
+// Tile rows hold D bf16 values, CPR = D/8 chunks of 16 bytes; chunk c of row r
+// sits at position c ^ g(r), where g is chosen per width so that
+//   * 16 consecutive rows read at one chunk (a 16-byte MFMA operand per lane,
+//     16 lanes per 256-byte LDS read cycle) fall on 16 distinct bank groups,
+//   * the 8 rows × 32 bytes one ds_read_b64_tr_b16 cycle takes (rows
+//     4G + 0..3 for two adjacent G, 32 bytes of dv each) fall on 8 distinct
+//     32-byte bank groups:
+//     D = 64 (128-byte rows): g = 3-bit reversal of (r/2 mod 8) (lds_swz);
+//     D = 32 (64-byte rows, four to 256 bytes): g = 2-bit reversal of (r/4 mod 4);
+//     D = 128 (256-byte rows): g = 2·(r mod 8) + (r/8 mod 2).
+template <int D>
+__device__ __forceinline__ int swz(int row, int chunk) {
+    if constexpr (D == 64) {
+        return lds_swz(row, chunk);
+    } else if constexpr (D == 32) {
+        const int s = (row >> 2) & 3;
+        return row * 4 + (chunk ^ (((s & 1) << 1) | (s >> 1)));
+    } else {
+        return row * 16 + (chunk ^ (((row & 7) << 1) | ((row >> 3) & 1)));
+    }
+}
 
 // op over lanes {l, l^16, l^32, l^48}: the four 16-lane groups hold the four
 // key quarters of one query column.
@@ -69,17 +93,24 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 // WINDOWED = false: no key window or the causal one (wl = −1, wr ∈ {−1, 0},
 // top-left), whose legal keys start at 0; the general window costs this
 // latency-bound kernel a few percent, so it gets its own instantiation.
-template <bool WINDOWED>
+template <int D, bool WINDOWED>
 __global__ __launch_bounds__(NT) void sdpa_short_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
     int H, int n, int m, float c_log2, int wl, int wr, int bottom_right,
     const int32_t* __restrict__ key_lens, float* __restrict__ lse) {
-    // K tile at 0, Q tile at 8 KiB, V tile at 16 KiB (64 rows × 128 B each).
-    __shared__ __attribute__((aligned(16))) char lds[3 * MAXLEN * 128];
+    constexpr int RB = 2 * D;           // bytes per tile row
+    constexpr int TILE = MAXLEN * RB;   // K, Q and V tiles of 64 rows
+    constexpr int CPR = D / 8;          // 16-byte chunks per row
+    constexpr int KS = D / 32;          // k-steps of the score product
+    constexpr int DT = D / 16;          // 16-wide output tiles
+    constexpr int RPL = 1024 / RB;      // tile rows per 1 KiB load
+    constexpr int LPW = QW / RPL;       // loads per wave and tensor (its own 16 rows)
+    // K tile at 0, Q tile at TILE, V tile at 2·TILE.
+    __shared__ __attribute__((aligned(16))) char lds[3 * TILE];
     const u32x4* sK = reinterpret_cast<const u32x4*>(lds);
-    const u32x4* sQ = reinterpret_cast<const u32x4*>(lds + MAXLEN * 128);
-    const char* sVb = lds + 2 * MAXLEN * 128;
+    const u32x4* sQ = reinterpret_cast<const u32x4*>(lds + TILE);
+    const char* sVb = lds + 2 * TILE;
 
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -92,15 +123,16 @@ __global__ __launch_bounds__(NT) void sdpa_short_bf16(
     const size_t qbase = (size_t)bh * n * D;
     const size_t kvbase = (size_t)bh * m * D;
 
-    // HBM → LDS with buffer_load_dwordx4 … lds.  Wave w moves tile rows
-    // 8·(2w + i) .. +7 (i = 0, 1) of each tensor; lane ln lands in LDS slot
-    // (row ln/8, position ln%8), which holds logical chunk (ln%8) ^ swz_f(row).
-    int ld_off[2], ld_lds[2];
+    // HBM → LDS with buffer_load_dwordx4 … lds.  Wave w moves its own 16 tile
+    // rows of each tensor, RPL rows per 1 KiB load; lane ln lands in LDS slot
+    // (row ln/CPR, position ln%CPR), which holds the chunk whose swizzled
+    // position that is (the swizzle is an XOR, its own inverse).
+    int ld_off[LPW], ld_lds[LPW];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int row = 8 * (2 * w + i) + (lane >> 3);
-        ld_off[i] = row * 128 + ((lane & 7) ^ swz_f(row)) * 16;
-        ld_lds[i] = 8 * (2 * w + i) * 128;
+    for (int i = 0; i < LPW; ++i) {
+        const int row = QW * w + RPL * i + lane / CPR;
+        ld_off[i] = swz<D>(row, lane % CPR) * 16;  // = row·RB + chunk·16
+        ld_lds[i] = (QW * w + RPL * i) * RB;
     }
     // Q goes first, without waiting for the key length.  Then the key length,
     // then K (and V, below), whose buffer ranges stop at it: their padded rows
@@ -108,16 +140,16 @@ __global__ __launch_bounds__(NT) void sdpa_short_bf16(
     // mask discards; a zero V row meets weight 0 in P·V, and 0 · garbage must
     // not happen).
     const i32x4 rq = make_rsrc(Q + qbase, (uint32_t)(n * D * 2));
-    load16_to_lds_nt(rq, lds + MAXLEN * 128 + ld_lds[0], ld_off[0]);
-    load16_to_lds_nt(rq, lds + MAXLEN * 128 + ld_lds[1], ld_off[1]);
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) load16_to_lds_nt(rq, lds + TILE + ld_lds[i], ld_off[i]);
     int L = m;
     if (key_lens) {
         const int t = key_lens[b];
         L = t < 0 ? 0 : (t > m ? m : t);
     }
     const i32x4 rk = make_rsrc(K + kvbase, (uint32_t)(L * D * 2));
-    load16_to_lds_nt(rk, lds + ld_lds[0], ld_off[0]);
-    load16_to_lds_nt(rk, lds + ld_lds[1], ld_off[1]);
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) load16_to_lds_nt(rk, lds + ld_lds[i], ld_off[i]);
 
     // Key tiles [kt0, nkt) hold every key some query of this wave may see;
     // keys in [flo, fhi) are legal for all of its queries.  Computed while Q
@@ -152,15 +184,15 @@ __global__ __launch_bounds__(NT) void sdpa_short_bf16(
     // which the scores do not need.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     const i32x4 rv = make_rsrc(V + kvbase, (uint32_t)(L * D * 2));
-    load16_to_lds_nt(rv, lds + 2 * MAXLEN * 128 + ld_lds[0], ld_off[0]);
-    load16_to_lds_nt(rv, lds + 2 * MAXLEN * 128 + ld_lds[1], ld_off[1]);
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) load16_to_lds_nt(rv, lds + 2 * TILE + ld_lds[i], ld_off[i]);
     lds_barrier();
     const bool active = w * QW < n;  // this wave has queries (n < 64 leaves some idle)
 
     // Qᵀ as the B operand: lane holds query q, d = 32·ks + 8·G + [0..7].
-    bf16x8 qop[2];
-    qop[0] = __builtin_bit_cast(bf16x8, sQ[swz(q, G)]);
-    qop[1] = __builtin_bit_cast(bf16x8, sQ[swz(q, 4 + G)]);
+    bf16x8 qop[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qop[ks] = __builtin_bit_cast(bf16x8, sQ[swz<D>(q, 4 * ks + G)]);
 
 
     // Sᵀ = K · Qᵀ: register r of tile kt is key 16·kt + 4·G + r.
@@ -175,8 +207,8 @@ __global__ __launch_bounds__(NT) void sdpa_short_bf16(
                 const int krow = 16 * kt + l16;
                 f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    const bf16x8 a = __builtin_bit_cast(bf16x8, sK[swz(krow, 4 * ks + G)]);
+                for (int ks = 0; ks < KS; ++ks) {
+                    const bf16x8 a = __builtin_bit_cast(bf16x8, sK[swz<D>(krow, 4 * ks + G)]);
                     acc = mfma16(a, qop[ks], acc);
                 }
                 if (16 * kt < flo || 16 * kt + 16 > fhi) {  // uniform: tile has illegal keys
@@ -222,9 +254,9 @@ __global__ __launch_bounds__(NT) void sdpa_short_bf16(
 
     // Oᵀ = Vᵀ · Pᵀ: k-step j covers keys 32·j + 4·G + [0..3] (slots 0..3, from
     // tile 2j) and 32·j + 16 + 4·G + [0..3] (slots 4..7, from tile 2j+1).
-    f32x4 o[4];
+    f32x4 o[DT];
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
     const char* vb = sVb;
 #pragma unroll
@@ -233,56 +265,68 @@ __global__ __launch_bounds__(NT) void sdpa_short_bf16(
         const int r0 = 32 * j + 4 * G + (l16 >> 2);
         const int r1 = r0 + 16;
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
+        for (int dt = 0; dt < DT; ++dt) {
             const int dv0 = 16 * dt + 4 * (l16 & 3);
             const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                (lds_bf16x4*)(vb + swz(r0, dv0 >> 3) * 16 + (dv0 & 7) * 2));
+                (lds_bf16x4*)(vb + swz<D>(r0, dv0 >> 3) * 16 + (dv0 & 7) * 2));
             const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                (lds_bf16x4*)(vb + swz(r1, dv0 >> 3) * 16 + (dv0 & 7) * 2));
+                (lds_bf16x4*)(vb + swz<D>(r1, dv0 >> 3) * 16 + (dv0 & 7) * 2));
             o[dt] = mfma16(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pb[j], o[dt]);
         }
     }
 
     // Register r of o[dt] is dv = 16·dt + 4·G + r of query q.  The wave's 16
-    // output rows go through its own 2 KiB of the (now free) K tile so that
-    // every store instruction writes whole 128-byte rows, 16 bytes a lane.
+    // output rows go through its own 16 rows of the (now free) K tile so that
+    // every store instruction writes whole rows, 16 bytes a lane.
     {
         // no legal key ⇒ zero row; a NaN sum (NaN legal inputs) stays NaN
         const float inv = l != 0.f ? __builtin_amdgcn_rcpf(l) : 0.f;
-        char* ob = lds + w * QW * 128;
+        char* ob = lds + w * QW * RB;
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
+        for (int dt = 0; dt < DT; ++dt) {
             bf16x4 ov;
             ov[0] = (__bf16)(o[dt][0] * inv);
             ov[1] = (__bf16)(o[dt][1] * inv);
             ov[2] = (__bf16)(o[dt][2] * inv);
             ov[3] = (__bf16)(o[dt][3] * inv);
-            *reinterpret_cast<bf16x4*>(ob + swz(l16, 2 * dt + (G >> 1)) * 16 + (G & 1) * 8) = ov;
+            *reinterpret_cast<bf16x4*>(ob + swz<D>(l16, 2 * dt + (G >> 1)) * 16 + (G & 1) * 8) = ov;
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int row = 8 * i + (lane >> 3);
+        for (int i = 0; i < CPR / 4; ++i) {
+            const int id = lane + 64 * i;
+            const int row = id / CPR, c = id % CPR;
             const int qq = w * QW + row;
-            const u32x4 x = *reinterpret_cast<const u32x4*>(ob + swz(row, lane & 7) * 16);
-            if (qq < n) store16_nt(O + qbase + (size_t)qq * D + 8 * (lane & 7), x);
+            const u32x4 x = *reinterpret_cast<const u32x4*>(ob + swz<D>(row, c) * 16);
+            if (qq < n) store16_nt(O + qbase + (size_t)qq * D + 8 * c, x);
         }
     }
 }
 
 }  // namespace
 
-bool short_bf16_fits(const Args& a) { return a.n <= MAXLEN && a.m <= MAXLEN; }
+bool short_bf16_fits(const Args& a) {
+    return a.n <= MAXLEN && a.m <= MAXLEN && (a.d == 32 || a.d == 64 || a.d == 128);
+}
 
-hipError_t launch_bf16_short(const Args& a, hipStream_t stream) {
+namespace {
+template <int D>
+hipError_t launch_short(const Args& a, hipStream_t stream) {
     const float c_log2 = (float)((double)a.scale * 1.4426950408889634);  // scale·log2(e)
     const bool windowed = a.wl >= 0 || a.wr > 0 || a.bottom_right;
-    hipLaunchKernelGGL(windowed ? sdpa_short_bf16<true> : sdpa_short_bf16<false>, dim3(a.B * a.H),
-                       dim3(NT), 0, stream,
+    const auto kernel = windowed ? sdpa_short_bf16<D, true> : sdpa_short_bf16<D, false>;
+    hipLaunchKernelGGL(kernel, dim3(a.B * a.H), dim3(NT), 0, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (uint16_t*)a.out, a.H, a.n, a.m, c_log2, a.wl, a.wr, a.bottom_right,
                        a.key_lens, a.lse);
     return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_bf16_short(const Args& a, hipStream_t stream) {
+    if (a.d == 32) return launch_short<32>(a, stream);
+    if (a.d == 128) return launch_short<128>(a, stream);
+    return launch_short<64>(a, stream);
 }
 
 }  // namespace sdpa

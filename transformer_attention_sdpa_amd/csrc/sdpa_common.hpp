@@ -114,7 +114,7 @@ hipError_t launch_mha_bf16(const MhaArgs& a, hipStream_t stream);
 hipError_t launch_bf16(const Args& a, hipStream_t stream);        // picks one of the four below
 hipError_t launch_bf16_width(const Args& a, hipStream_t stream);  // d = 32 or 128
 hipError_t launch_bf16_long(const Args& a, hipStream_t stream);   // any n, m
-hipError_t launch_bf16_short(const Args& a, hipStream_t stream);  // n, m <= 64
+hipError_t launch_bf16_short(const Args& a, hipStream_t stream);  // n, m <= 64; d = 32, 64, 128
 bool short_bf16_fits(const Args& a);
 hipError_t launch_bf16_decode(const Args& a, hipStream_t stream);  // n <= 16, m > 64
 bool decode_bf16_fits(const Args& a);
