@@ -235,6 +235,40 @@ SDPA_API int sdpa_forward_ex(const void* q, const void* k, const void* v, void* 
                              size_t workspace_bytes, void* stream);
 
 /*
+ * sdpa_forward_strided — sdpa_forward_ex on tensors laid out at any element
+ * strides, e.g. the token-major [B, len, h, d] layout in which the multi-head
+ * section of 《精读 Attention Is All You Need：原始 Transformer 论文》 writes
+ * Concat(head_1, …, head_h) (row i of every head side by side), read and
+ * written in place without a transpose.
+ *
+ * strides   NULL (then this is sdpa_forward_ex on the packed [B, h, len, d]
+ *           layout), or a HOST array of 12 int64 element strides: batch, head
+ *           and row stride of q, then of k, v and out, in that order.  Element
+ *           (b, head, i, j) of a tensor is at base + b·batch + head·head_stride
+ *           + i·row + j: the last dimension is contiguous.  Rules:
+ *             * batch and head strides >= 0 (0 shares one tensor across that
+ *               dimension, e.g. one K/V head for all query heads);
+ *             * row stride >= the row width (d_k or d_v): rows never overlap;
+ *             * every stride times the element size is a multiple of 16;
+ *             * one head's rows span less than 2^31 bytes, and 64 rows at its
+ *               row stride do too;
+ *             * the output's (batch, head, row) rows are pairwise disjoint;
+ *           else SDPA_ERR_SHAPE, SDPA_ERR_ALIGN or SDPA_ERR_ALIAS.  out, lse
+ *           and the workspace must not overlap the span of any input, judged
+ *           from the first to the last element each layout reaches
+ *           (SDPA_ERR_ALIAS).
+ * Everything else, lse and workspace included, as in sdpa_forward_ex; lse
+ * stays packed [B, h, n].  Every forward kernel takes the strides, so the
+ * arithmetic, and the result, is that of the packed call on the same values.
+ */
+SDPA_API int sdpa_forward_strided(const void* q, const void* k, const void* v, void* out, float* lse,
+                                  int32_t B, int32_t h, int32_t n, int32_t m, int32_t d_k,
+                                  int32_t d_v, float scale, int32_t window_left,
+                                  int32_t window_right, int32_t align, const int32_t* key_lens,
+                                  int32_t dtype, const int64_t* strides, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/*
  * sdpa_forward_ex_noalloc — sdpa_forward_ex for callers that cannot allocate
  * device memory (code under HIP graph capture, tight decoder-step serving
  * loops, harnesses that forbid hipMalloc): the same call and the same kernels,

@@ -31,7 +31,8 @@ def test_every_declared_entry_point_is_exported(lib):
     assert set(names) == {"sdpa_forward", "sdpa_forward_window", "sdpa_mha_forward",
                           "sdpa_mha_workspace_bytes", "sdpa_forward_lse", "sdpa_backward",
                           "sdpa_backward_workspace_bytes", "sdpa_forward_ex",
-                          "sdpa_forward_ex_noalloc", "sdpa_forward_workspace_bytes",
+                          "sdpa_forward_ex_noalloc", "sdpa_forward_strided",
+                          "sdpa_forward_workspace_bytes",
                           "sdpa_strerror", "sdpa_version"}
     for name in names:
         assert isinstance(getattr(lib, name), ctypes._CFuncPtr)
@@ -287,6 +288,66 @@ def test_noalloc_scratch_limit_covers_the_decoder_workloads(lib):
         assert 0 < need <= _lib.SDPA_NOALLOC_SCRATCH_BYTES
     assert "SDPA_NOALLOC_SCRATCH_BYTES" in _lib.sdpa_strerror(_lib.SDPA_ERR_SCRATCH)
     assert re.search(r"#define\s+SDPA_NOALLOC_SCRATCH_BYTES\s+\(8u << 20\)", _header())
+
+
+def call_strided(strides=None, **kw):
+    """sdpa_forward_strided on fake addresses, 2 x 4 heads, n = 48, m = 80, bf16;
+    ``strides`` defaults to the token-major [B, len, h, d] layout of all four."""
+    a = dict(q=G, k=2 * G, v=3 * G, out=4 * G, lse=None, B=2, h=4, n=48, m=80, d_k=64, d_v=64,
+             scale=0.125, wl=-1, wr=-1, align=0, key_lens=None, dtype=1, ws=None, ws_bytes=0)
+    a.update(kw)
+    B, h, n, m, d = a["B"], a["h"], a["n"], a["m"], a["d_k"]
+    if strides is None:
+        strides = [n * h * d, d, h * d, m * h * d, d, h * d, m * h * d, d, h * d, n * h * d, d, h * d]
+    return _lib.sdpa_forward_strided(a["q"], a["k"], a["v"], a["out"], a["lse"], B, h, n, m, d,
+                                     a["d_v"], a["scale"], a["wl"], a["wr"], a["align"], a["key_lens"],
+                                     a["dtype"], strides, a["ws"], a["ws_bytes"], None)
+
+
+def _bshd(B, h, n, m, d):
+    return [n * h * d, d, h * d, m * h * d, d, h * d, m * h * d, d, h * d, n * h * d, d, h * d]
+
+
+def _with(strides, i, v):
+    s = list(strides)
+    s[i] = v
+    return s
+
+
+BSHD = _bshd(2, 4, 48, 80, 64)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), _lib.SDPA_ERR_NULL),
+    (dict(strides=_with(BSHD, 2, 63)), _lib.SDPA_ERR_SHAPE),          # q row stride < d_k
+    (dict(strides=_with(BSHD, 5, 32)), _lib.SDPA_ERR_SHAPE),          # k row stride < d_k
+    (dict(strides=_with(BSHD, 0, -8)), _lib.SDPA_ERR_SHAPE),          # negative batch stride
+    (dict(strides=_with(BSHD, 7, 1 << 41)), _lib.SDPA_ERR_SHAPE),     # stride past 2^40
+    (dict(strides=_with(BSHD, 8, 1 << 24)), _lib.SDPA_ERR_SHAPE),     # 64 rows past 2^31 bytes
+    (dict(strides=_with(BSHD, 2, 260)), _lib.SDPA_ERR_ALIGN),         # 520-byte rows
+    (dict(strides=_with(BSHD, 4, 4)), _lib.SDPA_ERR_ALIGN),           # 8-byte head stride
+    (dict(strides=_with(BSHD, 10, 0)), _lib.SDPA_ERR_ALIAS),          # out heads on one another
+    (dict(strides=_with(BSHD, 11, 64)), _lib.SDPA_ERR_ALIAS),         # out rows on the heads' rows
+    (dict(out=G + 64), _lib.SDPA_ERR_ALIAS),                          # out inside q's span
+    (dict(lse=4 * G + 256), _lib.SDPA_ERR_ALIAS),                     # lse inside out's span
+    (dict(lse=6 * G, dtype=0), _lib.SDPA_ERR_UNSUPPORTED),
+    (dict(wl=-3), _lib.SDPA_ERR_MASK),
+    (dict(d_k=16, d_v=16), _lib.SDPA_ERR_UNSUPPORTED),
+])
+def test_forward_strided_validation_rejects_before_any_hip_call(kw, code, lib):
+    assert call_strided(**kw) == code
+
+
+def test_forward_strided_layout_rules_accept_shared_heads():
+    """Head stride 0 on K and V (one K/V head shared by every query head) and
+    a fused [B, len, 3, h, d] Q/K/V buffer pass the layout checks; the call
+    is then refused by a later, launch-free check (out overlapping lse)."""
+    B, h, n, d = 2, 4, 48, 64
+    shared = _with(_with(BSHD, 4, 0), 7, 0)
+    assert call_strided(strides=shared, lse=4 * G + 256) == _lib.SDPA_ERR_ALIAS
+    fused = [n * 3 * h * d, d, 3 * h * d] * 3 + [n * h * d, d, h * d]
+    assert call_strided(strides=fused, m=n, q=G, k=G + h * d * 2, v=G + 2 * h * d * 2,
+                        lse=4 * G + 256) == _lib.SDPA_ERR_ALIAS
 
 
 def call_bwd(**kw):

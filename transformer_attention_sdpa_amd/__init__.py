@@ -13,12 +13,13 @@ import math
 
 from . import _lib
 from ._lib import (sdpa_backward, sdpa_backward_workspace_bytes, sdpa_forward,  # noqa: F401
-                   sdpa_forward_ex, sdpa_forward_ex_noalloc, sdpa_forward_lse, sdpa_forward_window,
+                   sdpa_forward_ex, sdpa_forward_ex_noalloc, sdpa_forward_lse, sdpa_forward_strided,
+                   sdpa_forward_window,
                    sdpa_forward_workspace_bytes, sdpa_mha_forward,
                    sdpa_mha_workspace_bytes, sdpa_strerror, sdpa_version)
 
 __all__ = ["forward", "backward", "mha_forward", "sdpa_forward", "sdpa_forward_window",
-           "sdpa_forward_lse", "sdpa_forward_ex", "sdpa_forward_ex_noalloc",
+           "sdpa_forward_lse", "sdpa_forward_ex", "sdpa_forward_ex_noalloc", "sdpa_forward_strided",
            "sdpa_forward_workspace_bytes",
            "sdpa_backward", "sdpa_backward_workspace_bytes",
            "sdpa_mha_forward", "sdpa_mha_workspace_bytes", "sdpa_strerror", "sdpa_version"]
@@ -120,8 +121,9 @@ def _lengths(q, k):
     return q.shape[2], k.shape[2]
 
 
-def _check_qkv(q, k, v):
-    """Shapes and the dtype code of [B, h, n, d_k], [B, h, m, d_k], [B, h, m, d_v] GPU tensors."""
+def _check_qkv(q, k, v, strided_ok=False):
+    """Shapes and the dtype code of [B, h, n, d_k], [B, h, m, d_k], [B, h, m, d_v] GPU tensors
+    (packed, or with ``strided_ok`` any strides whose last dimension is contiguous)."""
     import torch
 
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
@@ -139,7 +141,10 @@ def _check_qkv(q, k, v):
     else:
         raise ValueError(f"unsupported dtype {q.dtype}")
     for t in (q, k, v):
-        if not t.is_contiguous():
+        if strided_ok:
+            if t.stride(-1) != 1 and t.shape[-1] != 1:
+                raise ValueError("q, k, v need a contiguous last dimension")
+        elif not t.is_contiguous():
             raise ValueError("q, k, v must be contiguous")
     B, h, n, d_k = q.shape
     m, d_v = k.shape[2], v.shape[3]
@@ -211,6 +216,12 @@ def forward(q, k, v, *, causal: bool = False, key_lens=None, scale: float | None
             out=None, window=None, return_lse: bool = False, workspace="auto"):
     """Attention over [B, h, n, d_k] queries and [B, h, m, d] keys/values.
 
+    The tensors may be views at any strides whose last dimension is contiguous
+    (e.g. ``x.transpose(1, 2)`` of a token-major [B, len, h, d] tensor, or
+    slices of a fused Q/K/V buffer); ``out`` may be such a view too.  Those
+    calls go through ``sdpa_forward_strided`` with the tensors' own strides;
+    packed tensors take the plain entry points.
+
     key_lens: None or an int32 tensor [B] on the same device (key j of batch
     element b is legal iff j < key_lens[b]).  window: None, or
     (left, right) / (left, right, align) for restricted attention: query i
@@ -233,7 +244,7 @@ def forward(q, k, v, *, causal: bool = False, key_lens=None, scale: float | None
     import torch
 
     wl, wr, al = _window_args(window, causal, *_lengths(q, k))
-    B, h, n, m, d_k, d_v, dt = _check_qkv(q, k, v)
+    B, h, n, m, d_k, d_v, dt = _check_qkv(q, k, v, strided_ok=True)
     key_lens, kl_ptr = _key_lens_ptr(key_lens, B, q.device)
     if isinstance(workspace, str):
         if workspace != "auto":
@@ -242,16 +253,26 @@ def forward(q, k, v, *, causal: bool = False, key_lens=None, scale: float | None
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device) if need > 0 else None
     if out is None:
         out = torch.empty((B, h, n, d_v), dtype=q.dtype, device=q.device)
-    elif (tuple(out.shape) != (B, h, n, d_v) or out.dtype != q.dtype or not out.is_contiguous()
-          or out.device != q.device):
-        raise ValueError("out must be a contiguous [B, h, n, d_v] tensor of q's dtype on q's device")
+    elif (tuple(out.shape) != (B, h, n, d_v) or out.dtype != q.dtype or out.device != q.device
+          or (out.stride(-1) != 1 and d_v != 1)):
+        raise ValueError("out must be a [B, h, n, d_v] tensor of q's dtype on q's device "
+                         "with a contiguous last dimension")
+    strided = not all(t.is_contiguous() for t in (q, k, v, out))
     if scale is None:
         scale = 1.0 / math.sqrt(d_k)
     # The library launches on the calling thread's current HIP device.
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
         lse = torch.empty((B, h, n), dtype=torch.float32, device=q.device) if return_lse else None
-        if workspace is not None:
+        if strided:
+            strides = [s for t in (q, k, v, out) for s in t.stride()[:3]]
+            rc = sdpa_forward_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                      None if lse is None else lse.data_ptr(), B, h, n, m, d_k, d_v,
+                                      float(scale), wl, wr, al, kl_ptr, dt, strides,
+                                      None if workspace is None else workspace.data_ptr(),
+                                      0 if workspace is None else
+                                      workspace.numel() * workspace.element_size(), stream)
+        elif workspace is not None:
             rc = sdpa_forward_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                  None if lse is None else lse.data_ptr(), B, h, n, m, d_k, d_v,
                                  float(scale), wl, wr, al, kl_ptr, dt, workspace.data_ptr(),

@@ -68,6 +68,10 @@ def load() -> ctypes.CDLL:
     lib.sdpa_forward_ex.argtypes = [vp, vp, vp, vp, fp, i32, i32, i32, i32, i32, i32, ctypes.c_float,
                                     i32, i32, i32, vp, i32, vp, ctypes.c_size_t, vp]
     lib.sdpa_forward_ex.restype = ctypes.c_int
+    lib.sdpa_forward_strided.argtypes = [vp, vp, vp, vp, fp, i32, i32, i32, i32, i32, i32,
+                                         ctypes.c_float, i32, i32, i32, vp, i32,
+                                         ctypes.POINTER(ctypes.c_int64), vp, ctypes.c_size_t, vp]
+    lib.sdpa_forward_strided.restype = ctypes.c_int
     lib.sdpa_forward_ex_noalloc.argtypes = [vp, vp, vp, vp, fp, i32, i32, i32, i32, i32, i32,
                                             ctypes.c_float, i32, i32, i32, vp, i32, vp]
     lib.sdpa_forward_ex_noalloc.restype = ctypes.c_int
@@ -130,6 +134,20 @@ def sdpa_forward_ex(q, k, v, out, lse, B, h, n, m, d_k, d_v, scale, window_left,
     return load().sdpa_forward_ex(q, k, v, out, lse, B, h, n, m, d_k, d_v, scale, window_left,
                                   window_right, align, key_lens, dtype, workspace, workspace_bytes,
                                   stream)
+
+
+def sdpa_forward_strided(q, k, v, out, lse, B, h, n, m, d_k, d_v, scale, window_left, window_right,
+                         align, key_lens, dtype, strides, workspace, workspace_bytes, stream) -> int:
+    """Forward to the C entry point of the same name; ``strides`` is None or a
+    sequence of 12 element strides (batch, head, row of q, k, v, out)."""
+    arr = None
+    if strides is not None:
+        if len(strides) != 12:
+            raise ValueError("strides: 12 values (batch, head, row of q, k, v and out)")
+        arr = (ctypes.c_int64 * 12)(*[int(x) for x in strides])
+    return load().sdpa_forward_strided(q, k, v, out, lse, B, h, n, m, d_k, d_v, scale, window_left,
+                                       window_right, align, key_lens, dtype, arr, workspace,
+                                       workspace_bytes, stream)
 
 
 def sdpa_forward_ex_noalloc(q, k, v, out, lse, B, h, n, m, d_k, d_v, scale, window_left,

@@ -13,7 +13,7 @@
 
 namespace {
 
-constexpr int kVersion = 1 * 10000 + 4 * 100 + 0;  // 1.4.0: sdpa_forward_ex_noalloc
+constexpr int kVersion = 1 * 10000 + 5 * 100 + 0;  // 1.5.0: sdpa_forward_strided
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -23,10 +23,10 @@ bool overlap(const void* a, uint64_t na, const void* b, uint64_t nb) {
     return x < y + nb && y < x + na;
 }
 
-// Everything but the mask: pointers, dtype, shapes, scale, alignment, aliasing.
-int validate(const void* q, const void* k, const void* v, void* out, int32_t B, int32_t h,
-             int32_t n, int32_t m, int32_t d_k, int32_t d_v, float scale,
-             const int32_t* key_lens, int32_t dtype) {
+// Pointers, dtype, shapes, head widths, scale and base alignment (no aliasing).
+int validate_core(const void* q, const void* k, const void* v, void* out, int32_t B, int32_t h,
+                  int32_t n, int32_t m, int32_t d_k, int32_t d_v, float scale,
+                  const int32_t* key_lens, int32_t dtype) {
     if (!q || !k || !v || !out) return SDPA_ERR_NULL;
     if (dtype != SDPA_F32 && dtype != SDPA_BF16) return SDPA_ERR_DTYPE;
     if (B < 1 || h < 1 || n < 1 || m < 1 || d_k < 1 || d_v < 1) return SDPA_ERR_SHAPE;
@@ -49,6 +49,18 @@ int validate(const void* q, const void* k, const void* v, void* out, int32_t B, 
     if (!std::isfinite(scale) || !(scale > 0.f)) return SDPA_ERR_SCALE;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return SDPA_ERR_ALIGN;
     if (key_lens && (reinterpret_cast<uintptr_t>(key_lens) & 3u)) return SDPA_ERR_ALIGN;
+    return SDPA_OK;
+}
+
+// Everything but the mask, for the packed [B, h, len, d] layout: validate_core
+// and out overlapping none of q, k, v, key_lens.
+int validate(const void* q, const void* k, const void* v, void* out, int32_t B, int32_t h,
+             int32_t n, int32_t m, int32_t d_k, int32_t d_v, float scale,
+             const int32_t* key_lens, int32_t dtype) {
+    const int st = validate_core(q, k, v, out, B, h, n, m, d_k, d_v, scale, key_lens, dtype);
+    if (st != SDPA_OK) return st;
+    const uint64_t heads = (uint64_t)B * (uint64_t)h;
+    const uint64_t esz = dtype == SDPA_F32 ? 4 : 2;
     const uint64_t qb = heads * n * d_k * esz, kb = heads * m * d_k * esz;
     const uint64_t vb = heads * m * d_v * esz, ob = heads * n * d_v * esz;
     if (overlap(out, ob, q, qb) || overlap(out, ob, k, kb) || overlap(out, ob, v, vb))
@@ -299,6 +311,105 @@ extern "C" int sdpa_mha_forward(const void* x_q, const void* x_kv, const void* w
     clear_pending_error();
     const hipError_t e = sdpa::launch_mha_bf16(a, reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? SDPA_OK : SDPA_ERR_LAUNCH;
+}
+
+// ---- sdpa_forward_strided: q, k, v and out at any element strides.
+
+namespace {
+
+// One tensor's strides: batch, head and row stride (elements) for `len` rows
+// of `width` elements.  Fills `s` and its byte span from the base pointer.
+int check_strides(const int64_t* st, int32_t len, int32_t width, int32_t B, int32_t h, uint64_t esz,
+                  sdpa::Strides* s, uint64_t* span) {
+    const int64_t sb = st[0], sh = st[1], sr = st[2];
+    const int64_t lim = (int64_t)1 << 40;
+    if (sb < 0 || sh < 0 || sr < width || sb > lim || sh > lim || sr > lim) return SDPA_ERR_SHAPE;
+    // every row starts 16-byte aligned
+    if ((sb * (int64_t)esz) % 16 || (sh * (int64_t)esz) % 16 || (sr * (int64_t)esz) % 16)
+        return SDPA_ERR_ALIGN;
+    // 32-bit byte offsets within a head: its rows, and 64 rows from any tile start
+    if ((uint64_t)((int64_t)(len - 1) * sr + width) * esz >= (1ull << 31)) return SDPA_ERR_SHAPE;
+    if ((uint64_t)sr * esz * 64 >= (1ull << 31)) return SDPA_ERR_SHAPE;
+    s->b = sb;
+    s->h = sh;
+    s->r = (int)sr;
+    *span = (uint64_t)((int64_t)(B - 1) * sb + (int64_t)(h - 1) * sh + (int64_t)(len - 1) * sr + width) * esz;
+    return SDPA_OK;
+}
+
+// The (batch, head, row) rows of the output, `width` elements each, are
+// pairwise disjoint: taken in increasing stride order, every stride reaches
+// past everything the smaller ones span.
+bool rows_disjoint(const sdpa::Strides& s, int32_t B, int32_t h, int32_t n, int32_t width) {
+    struct Dim { int64_t stride, extent; } d[3] = {{s.b, B}, {s.h, h}, {s.r, n}};
+    for (int i = 0; i < 3; ++i)
+        for (int j = i + 1; j < 3; ++j)
+            if (d[j].stride < d[i].stride) { const Dim t = d[i]; d[i] = d[j]; d[j] = t; }
+    int64_t reach = width;  // elements spanned by one row
+    for (const Dim& x : d) {
+        if (x.extent == 1) continue;
+        if (x.stride < reach) return false;
+        reach += x.stride * (x.extent - 1);
+    }
+    return true;
+}
+
+}  // namespace
+
+extern "C" int sdpa_forward_strided(const void* q, const void* k, const void* v, void* out, float* lse,
+                                    int32_t B, int32_t h, int32_t n, int32_t m, int32_t d_k,
+                                    int32_t d_v, float scale, int32_t window_left,
+                                    int32_t window_right, int32_t align, const int32_t* key_lens,
+                                    int32_t dtype, const int64_t* strides, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+    if (!strides)
+        return sdpa_forward_ex(q, k, v, out, lse, B, h, n, m, d_k, d_v, scale, window_left,
+                               window_right, align, key_lens, dtype, workspace, workspace_bytes,
+                               stream);
+    int st = validate_core(q, k, v, out, B, h, n, m, d_k, d_v, scale, key_lens, dtype);
+    if (st != SDPA_OK) return st;
+    int32_t wl, wr, br;
+    st = window_args(n, m, window_left, window_right, align, &wl, &wr, &br);
+    if (st != SDPA_OK) return st;
+    const uint64_t esz = dtype == SDPA_F32 ? 4 : 2;
+    sdpa::Layout lay{};
+    uint64_t qs, ks, vs, os;
+    if ((st = check_strides(strides + 0, n, d_k, B, h, esz, &lay.q, &qs)) != SDPA_OK) return st;
+    if ((st = check_strides(strides + 3, m, d_k, B, h, esz, &lay.k, &ks)) != SDPA_OK) return st;
+    if ((st = check_strides(strides + 6, m, d_v, B, h, esz, &lay.v, &vs)) != SDPA_OK) return st;
+    if ((st = check_strides(strides + 9, n, d_v, B, h, esz, &lay.o, &os)) != SDPA_OK) return st;
+    if (!rows_disjoint(lay.o, B, h, n, d_v)) return SDPA_ERR_ALIAS;
+    const uint64_t heads = (uint64_t)B * h;
+    struct Buf { const void* p; uint64_t n; };
+    const Buf ins[] = {{q, qs}, {k, ks}, {v, vs}, {key_lens, key_lens ? (uint64_t)B * 4 : 0}};
+    for (const Buf& b : ins)
+        if (b.p && overlap(out, os, b.p, b.n)) return SDPA_ERR_ALIAS;
+    if (lse) {
+        if (dtype != SDPA_BF16) return SDPA_ERR_UNSUPPORTED;
+        if (reinterpret_cast<uintptr_t>(lse) & 3u) return SDPA_ERR_ALIGN;
+        for (const Buf& b : ins)
+            if (b.p && overlap(lse, heads * n * 4, b.p, b.n)) return SDPA_ERR_ALIAS;
+        if (overlap(lse, heads * n * 4, out, os)) return SDPA_ERR_ALIAS;
+    }
+    const size_t need = forward_work_bytes(B, h, n, m, d_k, d_v, dtype);
+    void* work = nullptr;
+    if (workspace && need > 0) {
+        if (!aligned16(workspace)) return SDPA_ERR_ALIGN;
+        if (workspace_bytes < need) return SDPA_ERR_WORKSPACE;
+        for (const Buf& b : ins)
+            if (b.p && overlap(workspace, need, b.p, b.n)) return SDPA_ERR_ALIAS;
+        if (overlap(workspace, need, out, os)) return SDPA_ERR_ALIAS;
+        if (lse && overlap(workspace, need, lse, heads * n * 4)) return SDPA_ERR_ALIAS;
+        work = workspace;
+    }
+    sdpa::Args a{q, k, v, out, B, h, n, m, scale, wl, wr, br, key_lens};
+    a.lse = lse;
+    a.d = d_k;
+    a.work = work;
+    a.work_bytes = work ? workspace_bytes : 0;
+    a.lay = lay;
+    a.strided = true;
+    return launch(a, dtype, stream);
 }
 
 // ---- sdpa_forward_ex_noalloc: the split-key workspace in static device memory.

@@ -60,7 +60,8 @@ constexpr int TILE_BYTES = BN * D * 2;  // 8 KiB
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
-template <int NW>
+// STRIDED: K/V row strides from the caller's layout; else the packed D.
+template <int NW, bool STRIDED>
 struct LongKernel {
     static constexpr int NT = NW * 64;
     static constexpr int BM = NW * QW;
@@ -72,7 +73,8 @@ struct LongKernel {
     int lane, l32, hf, gi;
     int kaddr[4];        // K operand byte offset for k-step ks (rows l32, chunk 2·ks + hf)
     int vaddr[2][2];     // Vᵀ transpose-read byte offset for [dv tile dt][first/second 4 keys], k-step 0
-    int ld_voff[LOADS];  // global byte offset (within a tile) of this lane's loads
+    int ld_koff[LOADS];  // global byte offset (within a tile) of this lane's K loads
+    int ld_voff[LOADS];  // same for V (K and V may have different row strides)
     int ld_lds[LOADS];   // LDS byte offset (within a tile) of those loads (wave-uniform)
     // Per-wave state.
     bf16x8 qop[QT][4];
@@ -81,6 +83,7 @@ struct LongKernel {
     // Per-workgroup scalars.
     const char* kg;
     const char* vg;
+    int kr, vr;  // row strides of K and V (elements)
     int L, wq0;
     KeyWindow win;
     // Per-wave key ranges: [wlo, whi) is needed by some query of the wave,
@@ -90,12 +93,13 @@ struct LongKernel {
 
     __device__ void issue_tile_load(int t, int buf) {
         const int k0 = t * BN;
-        const int left = (L - k0) * (D * 2);  // bytes of legal rows from k0 on (> 0 here)
-        const i32x4 rk = make_rsrc(kg + (size_t)k0 * D * 2, (uint32_t)left);
-        const i32x4 rv = make_rsrc(vg + (size_t)k0 * D * 2, (uint32_t)left);
+        // buffer ranges end with the last legal row (L - k0 > 0 rows from k0 on)
+        const int krr = STRIDED ? kr : D, vrr = STRIDED ? vr : D;
+        const i32x4 rk = make_rsrc(kg + (size_t)k0 * krr * 2, rows_span(L - k0, krr, D, 2));
+        const i32x4 rv = make_rsrc(vg + (size_t)k0 * vrr * 2, rows_span(L - k0, vrr, D, 2));
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
-            load16_to_lds(rk, lds + buf * 2 * TILE_BYTES + ld_lds[i], ld_voff[i]);
+            load16_to_lds(rk, lds + buf * 2 * TILE_BYTES + ld_lds[i], ld_koff[i]);
             load16_to_lds(rv, lds + buf * 2 * TILE_BYTES + TILE_BYTES + ld_lds[i], ld_voff[i]);
         }
     }
@@ -250,13 +254,13 @@ struct LongKernel {
     }
 };
 
-template <int NW>
+template <int NW, bool STRIDED>
 __global__ __launch_bounds__(NW * 64) void sdpa_long_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
     int BH, int H, int n, int m, float c_log2, int wl, int wr, int bottom_right,
-    const int32_t* __restrict__ key_lens, int nqb, float* __restrict__ lse) {
-    using KT = LongKernel<NW>;
+    const int32_t* __restrict__ key_lens, int nqb, float* __restrict__ lse, Layout lay) {
+    using KT = LongKernel<NW, STRIDED>;
     __shared__ __attribute__((aligned(16))) char lds[2 * 2 * TILE_BYTES];
     KT k;
     k.lds = lds;
@@ -292,10 +296,14 @@ __global__ __launch_bounds__(NW * 64) void sdpa_long_bf16(
     const int tbeg = kbeg / BN;
     const int tend = kend > kbeg ? (kend + BN - 1) / BN : tbeg;
 
-    const size_t qbase = (size_t)bh * n * D;
-    const size_t kvbase = (size_t)bh * m * D;
-    k.kg = reinterpret_cast<const char*>(K + kvbase);
-    k.vg = reinterpret_cast<const char*>(V + kvbase);
+    const int hh = bh - b * H;
+    const uint16_t* Qh = Q + (STRIDED ? head_offset(lay.q, b, hh) : (long long)bh * n * D);
+    uint16_t* Oh = O + (STRIDED ? head_offset(lay.o, b, hh) : (long long)bh * n * D);
+    k.kg = reinterpret_cast<const char*>(K + (STRIDED ? head_offset(lay.k, b, hh) : (long long)bh * m * D));
+    k.vg = reinterpret_cast<const char*>(V + (STRIDED ? head_offset(lay.v, b, hh) : (long long)bh * m * D));
+    k.kr = STRIDED ? lay.k.r : D;
+    k.vr = STRIDED ? lay.v.r : D;
+    const int qr = STRIDED ? lay.q.r : D, orr = STRIDED ? lay.o.r : D;
     k.wq0 = q0 + w * QW;
     {
         const int wlast = min(k.wq0 + QW, n) - 1;  // < wq0 for a wave past n: empty
@@ -328,7 +336,8 @@ __global__ __launch_bounds__(NW * 64) void sdpa_long_bf16(
         const int row = 8 * (w * KT::LOADS + i) + (k.lane >> 3);
         const int pos = k.lane & 7;
         const int chunk = pos ^ swz_f(row);
-        k.ld_voff[i] = row * 128 + chunk * 16;
+        k.ld_koff[i] = row * k.kr * 2 + chunk * 16;
+        k.ld_voff[i] = row * k.vr * 2 + chunk * 16;
         k.ld_lds[i] = 8 * (w * KT::LOADS + i) * 128;
     }
 
@@ -338,7 +347,7 @@ __global__ __launch_bounds__(NW * 64) void sdpa_long_bf16(
     for (int qt = 0; qt < QT; ++qt) {
         const int qrow = k.wq0 + 32 * qt + k.l32;
         if (qrow < n) {
-            const u32x4* src = reinterpret_cast<const u32x4*>(Q + qbase + (size_t)qrow * D);
+            const u32x4* src = reinterpret_cast<const u32x4*>(Qh + (size_t)qrow * qr);
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) k.qop[qt][ks] = __builtin_bit_cast(bf16x8, src[2 * ks + k.hf]);
         } else {
@@ -378,7 +387,7 @@ __global__ __launch_bounds__(NW * 64) void sdpa_long_bf16(
             lse[(size_t)bh * n + qrow] = (mc + log2f(ltot)) * 0.6931471805599453f;
         }
         if (qrow < n) {
-            uint16_t* dst = O + qbase + (size_t)qrow * D;
+            uint16_t* dst = Oh + (size_t)qrow * orr;
 #pragma unroll
             for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
@@ -400,10 +409,11 @@ hipError_t launch_long(const Args& a, hipStream_t stream) {
     const int BH = a.B * a.H;
     const float c_log2 = (float)((double)a.scale * 1.4426950408889634);  // scale·log2(e)
     const int nqb = (a.n + NW * QW - 1) / (NW * QW);
-    hipLaunchKernelGGL(sdpa_long_bf16<NW>, dim3(nqb * BH), dim3(NW * 64), 0, stream,
+    const auto kernel = a.strided ? sdpa_long_bf16<NW, true> : sdpa_long_bf16<NW, false>;
+    hipLaunchKernelGGL(kernel, dim3(nqb * BH), dim3(NW * 64), 0, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (uint16_t*)a.out, BH, a.H, a.n, a.m, c_log2, a.wl, a.wr, a.bottom_right,
-                       a.key_lens, nqb, a.lse);
+                       a.key_lens, nqb, a.lse, a.lay);
     return hipGetLastError();
 }
 
@@ -422,7 +432,9 @@ hipError_t launch_bf16_long(const Args& a, hipStream_t stream) {
     return blocks4 >= 1024 ? launch_long<4>(a, stream) : launch_long<2>(a, stream);
 }
 
-hipError_t launch_bf16(const Args& a, hipStream_t stream) {
+hipError_t launch_bf16(const Args& a0, hipStream_t stream) {
+    Args a = a0;
+    if (!a.strided) a.lay = dense_layout(a.H, a.n, a.m, a.d, a.d);  // packed layout
     if (short_bf16_fits(a)) return launch_bf16_short(a, stream);  // n, m <= 64, any width
     if (a.d != D) return launch_bf16_width(a, stream);
     if (decode_bf16_fits(a)) return launch_bf16_decode(a, stream);

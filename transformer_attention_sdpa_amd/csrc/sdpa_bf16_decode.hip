@@ -53,13 +53,14 @@ extern "C" __device__ i32x4 sdpa_dec_buffer_load_v4i32(i32x4 rsrc, int voffset, 
 // k-steps of 32 keys for P·V, NVL loads of 1 KiB (8 V rows) per step.
 // HPW heads per workgroup, NWD / HPW waves each: several short caches share a
 // workgroup, so that all heads fit on the GPU in one round of workgroups.
-template <int KS, int HPW>
+// STRIDED: runtime strides of `lay` (else the packed layout, compile-time).
+template <int KS, int HPW, bool STRIDED>
 __global__ __launch_bounds__(NWD * 64) void sdpa_decode_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
     int H, int n, int m, float c_log2, int wl, int wr, int bottom_right,
     const int32_t* __restrict__ key_lens, float* __restrict__ lse, int BH, int chunk,
-    float* __restrict__ part) {
+    float* __restrict__ part, Layout lay) {
     constexpr int NTL = KS / 16, NJ = KS / 32, NVL = KS / 8;
     constexpr int VBUF = KS * 128;  // one step of V rows in LDS
     // Per wave: two V step buffers; after the loop the first one holds the
@@ -84,8 +85,12 @@ __global__ __launch_bounds__(NWD * 64) void sdpa_decode_bf16(
     const int bh = hok ? bh_w : BH - 1;
     const int sp = chunk > 0 ? (int)(blockIdx.x / BH) : 0;
     const int b = bh / H;
-    const size_t qbase = (size_t)bh * n * D;
-    const size_t kvbase = (size_t)bh * m * D;
+    const int hh_b = bh - b * H;
+    const uint16_t* Qh = Q + (STRIDED ? head_offset(lay.q, b, hh_b) : (long long)bh * n * D);
+    const uint16_t* Kh = K + (STRIDED ? head_offset(lay.k, b, hh_b) : (long long)bh * m * D);
+    const uint16_t* Vh = V + (STRIDED ? head_offset(lay.v, b, hh_b) : (long long)bh * m * D);
+    const int qr = STRIDED ? lay.q.r : D, kr = STRIDED ? lay.k.r : D, vr = STRIDED ? lay.v.r : D;
+    const int orr = STRIDED ? lay.o.r : D;
 
     int L = m;
     if (key_lens) {
@@ -110,7 +115,7 @@ __global__ __launch_bounds__(NWD * 64) void sdpa_decode_bf16(
     const int q = l16;
     bf16x8 qop[2];
     if (q < n) {
-        const u32x4* src = reinterpret_cast<const u32x4*>(Q + qbase + (size_t)q * D);
+        const u32x4* src = reinterpret_cast<const u32x4*>(Qh + (size_t)q * qr);
         qop[0] = __builtin_bit_cast(bf16x8, src[G]);
         qop[1] = __builtin_bit_cast(bf16x8, src[4 + G]);
     } else {
@@ -120,8 +125,9 @@ __global__ __launch_bounds__(NWD * 64) void sdpa_decode_bf16(
     const int qlo = q < n ? win.lo(q) : 0;
     const int qhi = q < n ? win.hi(q) : 0;
 
-    const i32x4 rk = make_rsrc(K + kvbase, (uint32_t)(L * D * 2));
-    const i32x4 rv = make_rsrc(V + kvbase, (uint32_t)(L * D * 2));
+    const i32x4 rk = make_rsrc(Kh, rows_span(L, kr, D, 2));
+    const i32x4 rv = make_rsrc(Vh, rows_span(L, vr, D, 2));
+    const uint32_t kr2 = (uint32_t)kr * 2u, vr2 = (uint32_t)vr * 2u;  // row strides, bytes
     char* vbuf = lds + w * 2 * VBUF;
     // V loads: the i-th 1 KiB load of a step fills rows 8·i .. +7; lane ln lands
     // in LDS slot (row ln/8, position ln%8), which holds chunk (ln%8) ^ swz_f(row).
@@ -129,32 +135,34 @@ __global__ __launch_bounds__(NWD * 64) void sdpa_decode_bf16(
 #pragma unroll
     for (int i = 0; i < NVL; ++i) {
         const int row = 8 * i + (lane >> 3);
-        v_off[i] = row * 128 + (((lane & 7) ^ swz_f(row)) << 4);
+        v_off[i] = row * (int)vr2 + (((lane & 7) ^ swz_f(row)) << 4);
     }
     // K operand of tile t, k-step ks: key k0 + 16·t + l16, d = 32·ks + 8·G.
-    const int k_off = l16 * 128 + G * 16;
+    const int k_off = l16 * (int)kr2 + G * 16;
 
     // Requests step s's K (into kop) and V (into LDS buffer s & 1).  Issued
     // unconditionally, also one step past the wave's last: there the offsets
     // start at the key length, so the loads return zeros without touching
     // memory.  Every step then has the same outstanding loads, which keeps
     // the compiler's waits on K exact.  Offsets are unsigned 32-bit: the
-    // sentinel L·128 is below 2^31 and adds at most 4 KiB, so nothing wraps
-    // (the hardware reads the offset as unsigned).
+    // sentinel L·(row stride) is below 2^31 and adds less than 64 rows, which
+    // the C ABI keeps below 2^31 too, so nothing wraps (the hardware reads the
+    // offset as unsigned).
     auto issue = [&](int s, bf16x8 (&kop)[NTL][2]) {
-        const uint32_t base = s < s1 ? (uint32_t)(kb + s * KS) * 128u : (uint32_t)L * 128u;
+        const uint32_t row0 = s < s1 ? (uint32_t)(kb + s * KS) : (uint32_t)L;
+        const uint32_t kbase = row0 * kr2, vbase = row0 * vr2;
 #pragma unroll
         for (int t = 0; t < NTL; ++t)
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
                 kop[t][ks] = __builtin_bit_cast(
                     bf16x8, sdpa_dec_buffer_load_v4i32(
-                                rk, (int)(base + (uint32_t)(16 * t * 128 + k_off + 64 * ks)), 0,
+                                rk, (int)(kbase + (uint32_t)(16 * t) * kr2 + (uint32_t)(k_off + 64 * ks)), 0,
                                 kCachePolicyNT));
         char* dst = vbuf + (s & 1) * VBUF;
 #pragma unroll
         for (int i = 0; i < NVL; ++i)
-            load16_to_lds_nt(rv, dst + 8 * i * 128, (int)(base + (uint32_t)v_off[i]));
+            load16_to_lds_nt(rv, dst + 8 * i * 128, (int)(vbase + (uint32_t)v_off[i]));
     };
 
     float mrun = -INFINITY, lrun = 0.f;
@@ -283,7 +291,8 @@ __global__ __launch_bounds__(NWD * 64) void sdpa_decode_bf16(
     const int fq = tl & (QN - 1);
     const int fd = DPT * (tl >> 4);
     const int bh_t = chunk > 0 ? bh : (int)blockIdx.x * HPW + hh;  // this thread's head
-    const size_t obase = (size_t)bh_t * n * D;
+    const int b_t = bh_t / H;
+    uint16_t* Oh_t = O + (STRIDED ? head_offset(lay.o, b_t, bh_t - b_t * H) : (long long)bh_t * n * D);
     if (fq < n && bh_t < BH) {
         const int u0 = hh * WPH;
         float mx = red_m[u0][fq];
@@ -326,7 +335,7 @@ __global__ __launch_bounds__(NWD * 64) void sdpa_decode_bf16(
             ov[1] = (__bf16)(acc[c + 1] * inv);
             ov[2] = (__bf16)(acc[c + 2] * inv);
             ov[3] = (__bf16)(acc[c + 3] * inv);
-            *reinterpret_cast<bf16x4*>(O + obase + (size_t)fq * D + fd + c) = ov;
+            *reinterpret_cast<bf16x4*>(Oh_t + (size_t)fq * orr + fd + c) = ov;
         }
     }
 }
@@ -338,8 +347,8 @@ __global__ __launch_bounds__(NWD * 64) void sdpa_decode_bf16(
 // 4·(t % 16) .. +3 of the splits t / 16, t / 16 + 16, ..., and the sixteen
 // partial merges are combined through LDS at the end.
 __global__ __launch_bounds__(NWD * 64) void sdpa_decode_merge_bf16(
-    const float* __restrict__ part, uint16_t* __restrict__ O, float* __restrict__ lse, int BH, int n,
-    int nsplit, float c_log2) {
+    const float* __restrict__ part, uint16_t* __restrict__ O, float* __restrict__ lse, int BH, int H,
+    int n, int nsplit, float c_log2, Strides os) {
     constexpr int SL = NWD * 64 / 16;  // split slots
     const int bh = blockIdx.x / n, fq = blockIdx.x % n;
     const int fd = 4 * (threadIdx.x & 15);
@@ -409,7 +418,7 @@ __global__ __launch_bounds__(NWD * 64) void sdpa_decode_merge_bf16(
     ov[1] = (__bf16)(o[1] * inv);
     ov[2] = (__bf16)(o[2] * inv);
     ov[3] = (__bf16)(o[3] * inv);
-    *reinterpret_cast<bf16x4*>(O + ((size_t)bh * n + fq) * D + fd) = ov;
+    *reinterpret_cast<bf16x4*>(O + head_offset(os, bh / H, bh % H) + (size_t)fq * os.r + fd) = ov;
 }
 
 // Keys per split: 1024 (eight 32-key steps per wave) when that already gives
@@ -451,14 +460,15 @@ hipError_t launch_bf16_decode(const Args& a, hipStream_t stream) {
     if (a.work && need > 0 && a.work_bytes >= need) {
         const int chunk = decode_chunk(BH, a.m);
         const int ns = (a.m + chunk - 1) / chunk;
-        hipLaunchKernelGGL((sdpa_decode_bf16<32, 1>), dim3(BH * ns), dim3(NWD * 64), 0, stream,
+        const auto split_kernel = a.strided ? sdpa_decode_bf16<32, 1, true> : sdpa_decode_bf16<32, 1, false>;
+        hipLaunchKernelGGL(split_kernel, dim3(BH * ns), dim3(NWD * 64), 0, stream,
                            (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                            (uint16_t*)a.out, a.H, a.n, a.m, c_log2, a.wl, a.wr, a.bottom_right,
-                           a.key_lens, a.lse, BH, chunk, (float*)a.work);
+                           a.key_lens, a.lse, BH, chunk, (float*)a.work, a.lay);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(sdpa_decode_merge_bf16, dim3(BH * a.n), dim3(NWD * 64), 0, stream,
-                           (const float*)a.work, (uint16_t*)a.out, a.lse, BH, a.n, ns, c_log2);
+                           (const float*)a.work, (uint16_t*)a.out, a.lse, BH, a.H, a.n, ns, c_log2, a.lay.o);
         return hipGetLastError();
     }
     // 32-key steps.  64-key steps (twice the bytes per request round trip)
@@ -468,15 +478,17 @@ hipError_t launch_bf16_decode(const Args& a, hipStream_t stream) {
     // beam-search steps against ≤ 128 keys this measured 11.4 vs 12.4 µs;
     // long caches need all four waves on one head (113 vs 66 µs at 2k..8k).
     if (a.m <= 256 && BH >= 1024) {
-        hipLaunchKernelGGL((sdpa_decode_bf16<32, 2>), dim3((BH + 1) / 2), dim3(NWD * 64), 0, stream,
+        const auto kernel2 = a.strided ? sdpa_decode_bf16<32, 2, true> : sdpa_decode_bf16<32, 2, false>;
+        hipLaunchKernelGGL(kernel2, dim3((BH + 1) / 2), dim3(NWD * 64), 0, stream,
                            (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                            (uint16_t*)a.out, a.H, a.n, a.m, c_log2, a.wl, a.wr, a.bottom_right,
-                           a.key_lens, a.lse, BH, 0, nullptr);
+                           a.key_lens, a.lse, BH, 0, nullptr, a.lay);
     } else {
-        hipLaunchKernelGGL((sdpa_decode_bf16<32, 1>), dim3(BH), dim3(NWD * 64), 0, stream,
+        const auto kernel1 = a.strided ? sdpa_decode_bf16<32, 1, true> : sdpa_decode_bf16<32, 1, false>;
+        hipLaunchKernelGGL(kernel1, dim3(BH), dim3(NWD * 64), 0, stream,
                            (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                            (uint16_t*)a.out, a.H, a.n, a.m, c_log2, a.wl, a.wr, a.bottom_right,
-                           a.key_lens, a.lse, BH, 0, nullptr);
+                           a.key_lens, a.lse, BH, 0, nullptr, a.lay);
     }
     return hipGetLastError();
 }

@@ -93,12 +93,15 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 // WINDOWED = false: no key window or the causal one (wl = −1, wr ∈ {−1, 0},
 // top-left), whose legal keys start at 0; the general window costs this
 // latency-bound kernel a few percent, so it gets its own instantiation.
-template <int D, bool WINDOWED>
+// STRIDED = false: the packed [B, h, len, D] layout with compile-time strides
+// (the runtime-stride arithmetic would sit on this latency-bound kernel's
+// critical path); true: the strides of `lay`.
+template <int D, bool WINDOWED, bool STRIDED>
 __global__ __launch_bounds__(NT) void sdpa_short_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
     int H, int n, int m, float c_log2, int wl, int wr, int bottom_right,
-    const int32_t* __restrict__ key_lens, float* __restrict__ lse) {
+    const int32_t* __restrict__ key_lens, float* __restrict__ lse, Layout lay) {
     constexpr int RB = 2 * D;           // bytes per tile row
     constexpr int TILE = MAXLEN * RB;   // K, Q and V tiles of 64 rows
     constexpr int CPR = D / 8;          // 16-byte chunks per row
@@ -120,18 +123,27 @@ __global__ __launch_bounds__(NT) void sdpa_short_bf16(
 
     const int bh = blockIdx.x;
     const int b = bh / H;
-    const size_t qbase = (size_t)bh * n * D;
-    const size_t kvbase = (size_t)bh * m * D;
+    const int hh = bh - b * H;
+    const uint16_t* Qh = Q + (STRIDED ? head_offset(lay.q, b, hh) : (long long)bh * n * D);
+    const uint16_t* Kh = K + (STRIDED ? head_offset(lay.k, b, hh) : (long long)bh * m * D);
+    const uint16_t* Vh = V + (STRIDED ? head_offset(lay.v, b, hh) : (long long)bh * m * D);
+    uint16_t* Oh = O + (STRIDED ? head_offset(lay.o, b, hh) : (long long)bh * n * D);
+    const int qr = STRIDED ? lay.q.r : D, kr = STRIDED ? lay.k.r : D;
+    const int vr = STRIDED ? lay.v.r : D, orr = STRIDED ? lay.o.r : D;
 
     // HBM → LDS with buffer_load_dwordx4 … lds.  Wave w moves its own 16 tile
     // rows of each tensor, RPL rows per 1 KiB load; lane ln lands in LDS slot
     // (row ln/CPR, position ln%CPR), which holds the chunk whose swizzled
-    // position that is (the swizzle is an XOR, its own inverse).
-    int ld_off[LPW], ld_lds[LPW];
+    // position that is (the swizzle is an XOR, its own inverse).  Global byte
+    // offsets: row · (row stride) + chunk · 16, per tensor.
+    int q_off[LPW], k_off[LPW], v_off[LPW], ld_lds[LPW];
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
         const int row = QW * w + RPL * i + lane / CPR;
-        ld_off[i] = swz<D>(row, lane % CPR) * 16;  // = row·RB + chunk·16
+        const int c16 = (swz<D>(row, lane % CPR) - row * CPR) * 16;
+        q_off[i] = row * qr * 2 + c16;
+        k_off[i] = row * kr * 2 + c16;
+        v_off[i] = row * vr * 2 + c16;
         ld_lds[i] = (QW * w + RPL * i) * RB;
     }
     // Q goes first, without waiting for the key length.  Then the key length,
@@ -139,17 +151,17 @@ __global__ __launch_bounds__(NT) void sdpa_short_bf16(
     // arrive as zeros without being read (a zero K row only gives a score the
     // mask discards; a zero V row meets weight 0 in P·V, and 0 · garbage must
     // not happen).
-    const i32x4 rq = make_rsrc(Q + qbase, (uint32_t)(n * D * 2));
+    const i32x4 rq = make_rsrc(Qh, rows_span(n, qr, D, 2));
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) load16_to_lds_nt(rq, lds + TILE + ld_lds[i], ld_off[i]);
+    for (int i = 0; i < LPW; ++i) load16_to_lds_nt(rq, lds + TILE + ld_lds[i], q_off[i]);
     int L = m;
     if (key_lens) {
         const int t = key_lens[b];
         L = t < 0 ? 0 : (t > m ? m : t);
     }
-    const i32x4 rk = make_rsrc(K + kvbase, (uint32_t)(L * D * 2));
+    const i32x4 rk = make_rsrc(Kh, rows_span(L, kr, D, 2));
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) load16_to_lds_nt(rk, lds + ld_lds[i], ld_off[i]);
+    for (int i = 0; i < LPW; ++i) load16_to_lds_nt(rk, lds + ld_lds[i], k_off[i]);
 
     // Key tiles [kt0, nkt) hold every key some query of this wave may see;
     // keys in [flo, fhi) are legal for all of its queries.  Computed while Q
@@ -183,9 +195,9 @@ __global__ __launch_bounds__(NT) void sdpa_short_bf16(
     // the grid, every workgroup's Q and K then reach HBM ahead of V traffic,
     // which the scores do not need.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    const i32x4 rv = make_rsrc(V + kvbase, (uint32_t)(L * D * 2));
+    const i32x4 rv = make_rsrc(Vh, rows_span(L, vr, D, 2));
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) load16_to_lds_nt(rv, lds + 2 * TILE + ld_lds[i], ld_off[i]);
+    for (int i = 0; i < LPW; ++i) load16_to_lds_nt(rv, lds + 2 * TILE + ld_lds[i], v_off[i]);
     lds_barrier();
     const bool active = w * QW < n;  // this wave has queries (n < 64 leaves some idle)
 
@@ -298,7 +310,7 @@ __global__ __launch_bounds__(NT) void sdpa_short_bf16(
             const int row = id / CPR, c = id % CPR;
             const int qq = w * QW + row;
             const u32x4 x = *reinterpret_cast<const u32x4*>(ob + swz<D>(row, c) * 16);
-            if (qq < n) store16_nt(O + qbase + (size_t)qq * D + 8 * c, x);
+            if (qq < n) store16_nt(Oh + (size_t)qq * orr + 8 * c, x);
         }
     }
 }
@@ -314,11 +326,12 @@ template <int D>
 hipError_t launch_short(const Args& a, hipStream_t stream) {
     const float c_log2 = (float)((double)a.scale * 1.4426950408889634);  // scale·log2(e)
     const bool windowed = a.wl >= 0 || a.wr > 0 || a.bottom_right;
-    const auto kernel = windowed ? sdpa_short_bf16<D, true> : sdpa_short_bf16<D, false>;
+    const auto kernel = a.strided ? (windowed ? sdpa_short_bf16<D, true, true> : sdpa_short_bf16<D, false, true>)
+                                  : (windowed ? sdpa_short_bf16<D, true, false> : sdpa_short_bf16<D, false, false>);
     hipLaunchKernelGGL(kernel, dim3(a.B * a.H), dim3(NT), 0, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (uint16_t*)a.out, a.H, a.n, a.m, c_log2, a.wl, a.wr, a.bottom_right,
-                       a.key_lens, a.lse);
+                       a.key_lens, a.lse, a.lay);
     return hipGetLastError();
 }
 }  // namespace

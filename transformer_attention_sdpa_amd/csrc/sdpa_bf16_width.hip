@@ -58,11 +58,12 @@ __device__ __forceinline__ void wlds_wait(u32x2 (&x)[N]) {
     for (int i = 0; i < N; ++i) asm volatile("" : "+v"(x[i]));
 }
 
-template <int D, int NW>
+// STRIDED: runtime strides of `lay`; else the packed layout, compile-time.
+template <int D, int NW, bool STRIDED>
 __global__ __launch_bounds__(NW * 64) void sdpa_fwd_bf16_width(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ lse, int BH, int H, int n, int m, float c_log2, int wl,
-    int wr, int bottom_right, const int32_t* __restrict__ key_lens, int nqb) {
+    int wr, int bottom_right, const int32_t* __restrict__ key_lens, int nqb, Layout lay) {
     constexpr int KS = D / 16;                // k-steps of the score product
     constexpr int DT = D / 32;                // 32-row blocks of Oᵀ
     constexpr int CPR = D / 8;                // 16-byte chunks per row
@@ -97,14 +98,20 @@ __global__ __launch_bounds__(NW * 64) void sdpa_fwd_bf16_width(
     const int wlo = wact ? win.lo(wq0) : 0, whi = wact ? win.hi(wlast) : 0;
     const int flo = wact ? win.lo(wlast) : 0, fhi = wact ? win.hi(wq0) : 0;
 
-    const size_t qbase = (size_t)bh * n * D, kvbase = (size_t)bh * m * D;
+    const int hh = bh - b * H;
+    const uint16_t* Qh = Q + (STRIDED ? head_offset(lay.q, b, hh) : (long long)bh * n * D);
+    const uint16_t* Kh = K + (STRIDED ? head_offset(lay.k, b, hh) : (long long)bh * m * D);
+    const uint16_t* Vh = V + (STRIDED ? head_offset(lay.v, b, hh) : (long long)bh * m * D);
+    uint16_t* Oh = O + (STRIDED ? head_offset(lay.o, b, hh) : (long long)bh * n * D);
+    const int qr = STRIDED ? lay.q.r : D, kr = STRIDED ? lay.k.r : D;
+    const int vr = STRIDED ? lay.v.r : D, orr = STRIDED ? lay.o.r : D;
     const int qrow = wq0 + l32;
     const bool qok = qrow < n;
     // Qᵀ as the B operand: dims 16·ks + 8·hf + [0..7] of this lane's query.
     bf16x8 qop[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-        qop[ks] = qok ? __builtin_bit_cast(bf16x8, reinterpret_cast<const u32x4*>(Q + qbase + (size_t)qrow * D)[2 * ks + hf])
+        qop[ks] = qok ? __builtin_bit_cast(bf16x8, reinterpret_cast<const u32x4*>(Qh + (size_t)qrow * qr)[2 * ks + hf])
                       : __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
 
     // Per-lane LDS offsets: the K operand of k-step ks (row l32, chunk 2·ks + hf)
@@ -123,7 +130,7 @@ __global__ __launch_bounds__(NW * 64) void sdpa_fwd_bf16_width(
         }
     }
     // Tile loads: wave w's u-th 1 KiB load fills rows ROWS_PER_LOAD·(w·LOADS + u) + lane/CPR.
-    int ld_off[LOADS], ld_lds[LOADS];
+    int ldk_off[LOADS], ldv_off[LOADS], ld_lds[LOADS];
 #pragma unroll
     for (int u = 0; u < LOADS; ++u) {
         const int blk = w * LOADS + u;
@@ -131,17 +138,18 @@ __global__ __launch_bounds__(NW * 64) void sdpa_fwd_bf16_width(
         const int pos = lane % CPR;
         // the chunk whose swizzled position is pos (XOR is its own inverse)
         const int chunk = wswz<D>(row, pos) - row * CPR;
-        ld_off[u] = row * D * 2 + chunk * 16;
+        ldk_off[u] = row * kr * 2 + chunk * 16;
+        ldv_off[u] = row * vr * 2 + chunk * 16;
         ld_lds[u] = blk * 1024;
     }
     auto issue = [&](int t, int buf) {
-        const int left = (L - t * BT) * D * 2;
-        const i32x4 rk = make_rsrc(K + kvbase + (size_t)t * BT * D, (uint32_t)left);
-        const i32x4 rv = make_rsrc(V + kvbase + (size_t)t * BT * D, (uint32_t)left);
+        // buffer ranges end with the last legal row
+        const i32x4 rk = make_rsrc(Kh + (size_t)t * BT * kr, rows_span(L - t * BT, kr, D, 2));
+        const i32x4 rv = make_rsrc(Vh + (size_t)t * BT * vr, rows_span(L - t * BT, vr, D, 2));
 #pragma unroll
         for (int u = 0; u < LOADS; ++u) {
-            load16_to_lds(rk, lds + buf * 2 * TILE + ld_lds[u], ld_off[u]);
-            load16_to_lds(rv, lds + buf * 2 * TILE + TILE + ld_lds[u], ld_off[u]);
+            load16_to_lds(rk, lds + buf * 2 * TILE + ld_lds[u], ldk_off[u]);
+            load16_to_lds(rv, lds + buf * 2 * TILE + TILE + ld_lds[u], ldv_off[u]);
         }
     };
 
@@ -274,7 +282,7 @@ __global__ __launch_bounds__(NW * 64) void sdpa_fwd_bf16_width(
         const int id = lane + 64 * k;
         const int row = id / CPR, c = id % CPR;
         const u32x4 x = *reinterpret_cast<const u32x4*>(area + (row * CPR + (c ^ (row & (CPR - 1)))) * 16);
-        if (wq0 + row < n) store16_nt(O + qbase + (size_t)(wq0 + row) * D + 8 * c, x);
+        if (wq0 + row < n) store16_nt(Oh + (size_t)(wq0 + row) * orr + 8 * c, x);
     }
 }
 
@@ -285,14 +293,16 @@ hipError_t launch_width(const Args& a, hipStream_t stream) {
     // 4 waves (128 queries) per workgroup once there are enough blocks.
     if ((long long)BH * ((a.n + 127) / 128) >= 1024) {
         const int nqb = (a.n + 127) / 128;
-        hipLaunchKernelGGL((sdpa_fwd_bf16_width<D, 4>), dim3(nqb * BH), dim3(256), 0, stream,
+        const auto kernel = a.strided ? sdpa_fwd_bf16_width<D, 4, true> : sdpa_fwd_bf16_width<D, 4, false>;
+        hipLaunchKernelGGL(kernel, dim3(nqb * BH), dim3(256), 0, stream,
                            (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.out,
-                           a.lse, BH, a.H, a.n, a.m, c_log2, a.wl, a.wr, a.bottom_right, a.key_lens, nqb);
+                           a.lse, BH, a.H, a.n, a.m, c_log2, a.wl, a.wr, a.bottom_right, a.key_lens, nqb, a.lay);
     } else {
         const int nqb = (a.n + 63) / 64;
-        hipLaunchKernelGGL((sdpa_fwd_bf16_width<D, 2>), dim3(nqb * BH), dim3(128), 0, stream,
+        const auto kernel = a.strided ? sdpa_fwd_bf16_width<D, 2, true> : sdpa_fwd_bf16_width<D, 2, false>;
+        hipLaunchKernelGGL(kernel, dim3(nqb * BH), dim3(128), 0, stream,
                            (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.out,
-                           a.lse, BH, a.H, a.n, a.m, c_log2, a.wl, a.wr, a.bottom_right, a.key_lens, nqb);
+                           a.lse, BH, a.H, a.n, a.m, c_log2, a.wl, a.wr, a.bottom_right, a.key_lens, nqb, a.lay);
     }
     return hipGetLastError();
 }

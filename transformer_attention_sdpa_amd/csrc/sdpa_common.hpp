@@ -20,6 +20,34 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // big models).
 constexpr int kHeadDim = 64;
 
+// Element strides of one [B, h, len, d] tensor whose last dimension is
+// contiguous: element (b, head, i, j) sits at b·b_ + head·h + i·r + j.  Row
+// strides are at least d and fit 32-bit byte offsets within a head (the C ABI
+// checks both), so rows past a length are out of a buffer range that ends at
+// that length's last row.
+struct Strides {
+    long long b, h;
+    int r;
+};
+struct Layout {
+    Strides q, k, v, o;
+};
+// [B, h, len, d] packed row-major, the layout of the plain entry points.
+inline Layout dense_layout(int H, int n, int m, int dk, int dv) {
+    return Layout{{(long long)H * n * dk, (long long)n * dk, dk},
+                  {(long long)H * m * dk, (long long)m * dk, dk},
+                  {(long long)H * m * dv, (long long)m * dv, dv},
+                  {(long long)H * n * dv, (long long)n * dv, dv}};
+}
+__device__ __forceinline__ long long head_offset(const Strides& s, int b, int head) {
+    return (long long)b * s.b + (long long)head * s.h;
+}
+// Bytes a buffer range needs to cover rows [0, len) of width d (esz bytes per
+// element) at row stride r: up to the end of the last row.
+__device__ __forceinline__ uint32_t rows_span(int len, int r, int d, int esz) {
+    return len > 0 ? (uint32_t)(((long long)(len - 1) * r + d) * esz) : 0u;
+}
+
 // Everything a launcher needs; validated by the C ABI before any HIP call.
 // The mask is a key window around each query's aligned position c_i (i, or
 // i + L − n when bottom-right aligned): key j is legal iff j < L,
@@ -43,6 +71,11 @@ struct Args {
     // Optional workspace for split-key decoder steps (decode_split_bytes), or nullptr.
     void* work = nullptr;
     size_t work_bytes = 0;
+    // Element strides of q, k, v and out (dense_layout for the plain entry points).
+    Layout lay{};
+    // True when `lay` came from the caller (sdpa_forward_strided): the
+    // latency-bound kernels then use runtime strides, else compile-time ones.
+    bool strided = false;
 };
 
 // Legal key range [lo, hi) of query row i under the window of one batch

@@ -34,7 +34,7 @@ template <int NW>
 __global__ __launch_bounds__(NW * 64) void sdpa_fwd_f32(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     float* __restrict__ O, int BH, int H, int n, int m, float c_log2, int wl, int wr,
-    int bottom_right, const int32_t* __restrict__ key_lens, int nqb) {
+    int bottom_right, const int32_t* __restrict__ key_lens, int nqb, Layout lay) {
     constexpr int NT = NW * 64;
     constexpr int CHUNKS = BN * D * 4 / 16;  // 512
     constexpr int CPT = (CHUNKS + NT - 1) / NT;
@@ -65,15 +65,18 @@ __global__ __launch_bounds__(NW * 64) void sdpa_fwd_f32(
     const int tbeg = kbeg / BN;
     const int tend = kend > kbeg ? (kend + BN - 1) / BN : tbeg;
 
-    const size_t qbase = (size_t)bh * n * D;
-    const size_t kvbase = (size_t)bh * m * D;
+    const int hh = bh - b * H;
+    const float* Qh = Q + head_offset(lay.q, b, hh);
+    const float* Kh = K + head_offset(lay.k, b, hh);
+    const float* Vh = V + head_offset(lay.v, b, hh);
+    float* Oh = O + head_offset(lay.o, b, hh);
 
     // Qᵀ operand: MFMA step ks contracts d = ks (half-wave 0) and d = 32 + ks
     // (half-wave 1), so a lane keeps d = 32·hf + [0..31] of its query.
     const int qrow = q0 + w * QW + l32;
     float qop[32];
     if (qrow < n) {
-        const f32x4* src = reinterpret_cast<const f32x4*>(Q + qbase + (size_t)qrow * D + 32 * hf);
+        const f32x4* src = reinterpret_cast<const f32x4*>(Qh + (size_t)qrow * lay.q.r + 32 * hf);
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
             const f32x4 x = src[c];
@@ -92,8 +95,8 @@ __global__ __launch_bounds__(NW * 64) void sdpa_fwd_f32(
             const int c = tid + i * NT;
             const int key = k0 + (c >> 4);
             if (c < CHUNKS && key < L) {
-                rk[i] = reinterpret_cast<const f32x4*>(K + kvbase + (size_t)key * D)[c & 15];
-                rv[i] = reinterpret_cast<const f32x4*>(V + kvbase + (size_t)key * D)[c & 15];
+                rk[i] = reinterpret_cast<const f32x4*>(Kh + (size_t)key * lay.k.r)[c & 15];
+                rv[i] = reinterpret_cast<const f32x4*>(Vh + (size_t)key * lay.v.r)[c & 15];
             } else {
                 rk[i] = f32x4{0.f, 0.f, 0.f, 0.f};
                 rv[i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -223,7 +226,7 @@ __global__ __launch_bounds__(NW * 64) void sdpa_fwd_f32(
         for (int i = 0; i < 16; ++i) oacc[dt][i] += ofix[dt][i];
     const float ltot = half_swap_sum(lrun + lfix);
     if (qrow < n) {
-        float* dst = O + qbase + (size_t)qrow * D;
+        float* dst = Oh + (size_t)qrow * lay.o.r;
 #pragma unroll
         for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
@@ -253,11 +256,13 @@ hipError_t launch_f32_long(const Args& a, hipStream_t stream) {
     const int nqb = (a.n + NW * QW - 1) / (NW * QW);
     hipLaunchKernelGGL(sdpa_fwd_f32<NW>, dim3(nqb * BH), dim3(NW * 64), 0, stream,
                        (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.out,
-                       BH, a.H, a.n, a.m, c_log2, a.wl, a.wr, a.bottom_right, a.key_lens, nqb);
+                       BH, a.H, a.n, a.m, c_log2, a.wl, a.wr, a.bottom_right, a.key_lens, nqb, a.lay);
     return hipGetLastError();
 }
 
-hipError_t launch_f32(const Args& a, hipStream_t stream) {
+hipError_t launch_f32(const Args& a0, hipStream_t stream) {
+    Args a = a0;
+    if (!a.strided) a.lay = dense_layout(a.H, a.n, a.m, a.d, a.d);  // packed layout
     return short_f32_fits(a) ? launch_f32_short(a, stream) : launch_f32_long(a, stream);
 }
 

@@ -56,10 +56,13 @@ __device__ __forceinline__ float quad_sum_f(float x) {
     return half_swap_sum(__uint_as_float(r[0]) + __uint_as_float(r[1]));
 }
 
+// STRIDED as in the bf16 sentence-length kernel: compile-time strides for the
+// packed layout, the runtime ones of `lay` otherwise.
+template <bool STRIDED>
 __global__ __launch_bounds__(NT) void sdpa_short_f32(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     float* __restrict__ O, int H, int n, int m, float c_log2, int wl, int wr, int bottom_right,
-    const int32_t* __restrict__ key_lens) {
+    const int32_t* __restrict__ key_lens, Layout lay) {
     // K tile at 0, Q at 16 KiB, V at 32 KiB.
     __shared__ __attribute__((aligned(16))) char lds[3 * TILE];
     const f32x4* sK = reinterpret_cast<const f32x4*>(lds);
@@ -74,36 +77,45 @@ __global__ __launch_bounds__(NT) void sdpa_short_f32(
 
     const int bh = blockIdx.x;
     const int b = bh / H;
-    const size_t qbase = (size_t)bh * n * D;
-    const size_t kvbase = (size_t)bh * m * D;
+    const int hh = bh - b * H;
+    const float* Qh = Q + (STRIDED ? head_offset(lay.q, b, hh) : (long long)bh * n * D);
+    const float* Kh = K + (STRIDED ? head_offset(lay.k, b, hh) : (long long)bh * m * D);
+    const float* Vh = V + (STRIDED ? head_offset(lay.v, b, hh) : (long long)bh * m * D);
+    float* Oh = O + (STRIDED ? head_offset(lay.o, b, hh) : (long long)bh * n * D);
+    const int qr = STRIDED ? lay.q.r : D, kr = STRIDED ? lay.k.r : D;
+    const int vr = STRIDED ? lay.v.r : D, orr = STRIDED ? lay.o.r : D;
 
     // Wave w moves tile rows 4·(4w + i) .. +3 (i = 0..3) of each tensor: one
     // 1 KiB load each; lane ln lands in LDS slot (row ln/16, position ln%16),
-    // which holds logical chunk (ln%16) ^ (row mod 16).
-    int ld_off[4], ld_lds[4];
+    // which holds logical chunk (ln%16) ^ (row mod 16).  Global byte offsets:
+    // row · (row stride) + chunk · 16, per tensor.
+    int q_off[4], k_off[4], v_off[4], ld_lds[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int row = 4 * (4 * w + i) + (lane >> 4);
-        ld_off[i] = row * ROW + ((lane & 15) ^ (row & 15)) * 16;
+        const int c16 = ((lane & 15) ^ (row & 15)) * 16;
+        q_off[i] = row * qr * 4 + c16;
+        k_off[i] = row * kr * 4 + c16;
+        v_off[i] = row * vr * 4 + c16;
         ld_lds[i] = 4 * (4 * w + i) * ROW;
     }
-    const i32x4 rq = make_rsrc(Q + qbase, (uint32_t)(n * ROW));
+    const i32x4 rq = make_rsrc(Qh, rows_span(n, qr, D, 4));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) load16_to_lds_nt(rq, lds + TILE + ld_lds[i], ld_off[i]);
+    for (int i = 0; i < 4; ++i) load16_to_lds_nt(rq, lds + TILE + ld_lds[i], q_off[i]);
     int L = m;
     if (key_lens) {
         const int t = key_lens[b];
         L = t < 0 ? 0 : (t > m ? m : t);
     }
-    const i32x4 rk = make_rsrc(K + kvbase, (uint32_t)(L * ROW));
+    const i32x4 rk = make_rsrc(Kh, rows_span(L, kr, D, 4));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) load16_to_lds_nt(rk, lds + ld_lds[i], ld_off[i]);
+    for (int i = 0; i < 4; ++i) load16_to_lds_nt(rk, lds + ld_lds[i], k_off[i]);
     // V only once this wave's Q and K rows have landed (grid-wide, the score
     // operands reach HBM ahead of V); it arrives during the scores.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    const i32x4 rv = make_rsrc(V + kvbase, (uint32_t)(L * ROW));
+    const i32x4 rv = make_rsrc(Vh, rows_span(L, vr, D, 4));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) load16_to_lds_nt(rv, lds + 2 * TILE + ld_lds[i], ld_off[i]);
+    for (int i = 0; i < 4; ++i) load16_to_lds_nt(rv, lds + 2 * TILE + ld_lds[i], v_off[i]);
     lds_barrier();
 
     const int q = w * QW + l16;
@@ -208,7 +220,7 @@ __global__ __launch_bounds__(NT) void sdpa_short_f32(
         }
         // Store r writes dv 16·r + 4·G .. +3: the four 16-lane groups cover 64
         // contiguous bytes of each row per instruction.
-        float* dst = O + qbase + (size_t)q * D + 4 * G;
+        float* dst = Oh + (size_t)q * orr + 4 * G;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             f32x4 ov;
@@ -227,9 +239,9 @@ bool short_f32_fits(const Args& a) { return a.n <= MAXLEN && a.m <= MAXLEN; }
 
 hipError_t launch_f32_short(const Args& a, hipStream_t stream) {
     const float c_log2 = (float)((double)a.scale * 1.4426950408889634);  // scale·log2(e)
-    hipLaunchKernelGGL(sdpa_short_f32, dim3(a.B * a.H), dim3(NT), 0, stream,
+    hipLaunchKernelGGL(a.strided ? sdpa_short_f32<true> : sdpa_short_f32<false>, dim3(a.B * a.H), dim3(NT), 0, stream,
                        (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.out,
-                       a.H, a.n, a.m, c_log2, a.wl, a.wr, a.bottom_right, a.key_lens);
+                       a.H, a.n, a.m, c_log2, a.wl, a.wr, a.bottom_right, a.key_lens, a.lay);
     return hipGetLastError();
 }
 
