@@ -85,24 +85,37 @@ def algorithmic_work(wl, dtype, key_lens):
     return flops, nbytes, dense_flops
 
 
-def kernel_source_hash() -> str:
-    """Hash of the device-code sources (the kernels whose traffic is measured)."""
+# Source files of each measured kernel (its own file and the shared device header).
+KERNEL_SOURCES = {
+    "sdpa_short_bf16": ["sdpa_bf16_short.hip", "sdpa_common.hpp"],
+    "sdpa_short_f32": ["sdpa_f32_short.hip", "sdpa_common.hpp"],
+    "sdpa_long_bf16": ["sdpa_bf16.hip", "sdpa_common.hpp"],
+    "sdpa_decode_bf16": ["sdpa_bf16_decode.hip", "sdpa_common.hpp"],
+}
+
+
+def kernel_source_hash(files=None) -> str:
+    """Hash of device-code sources: the given files of csrc/ (the kernel whose
+    traffic was measured), or every kernel source."""
+    if files is None:
+        files = sorted(n for n in os.listdir(CSRC) if n.endswith((".hip", ".hpp")))
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
-        if name.endswith((".hip", ".hpp")):
-            with open(os.path.join(CSRC, name), "rb") as f:
-                h.update(name.encode() + f.read())
+    for name in files:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
 
 
 def measured_traffic(workload, dtype):
-    """Per-launch HBM bytes from committed rocprofv3 counter runs, if still current."""
+    """Per-launch HBM bytes from committed rocprofv3 counter runs, if still
+    current: null once the measured kernel's sources changed."""
     path = os.path.join(PROFILES, f"traffic_{workload}_{dtype}.json")
     if not os.path.exists(path):
         return None
     with open(path, encoding="utf-8") as f:
         t = json.load(f)
-    if t.get("kernel_source_hash") != kernel_source_hash():
+    files = t.get("kernel_sources")
+    if not files or t.get("kernel_source_hash") != kernel_source_hash(files):
         return None  # the kernel changed since the counters were taken
     return t.get("bytes_per_launch")
 
@@ -566,7 +579,8 @@ def traffic_record(fetch_db, write_db, copy_fetch_db, copy_write_db, copy_bytes,
             "fetch_scale": sf, "write_scale": sw,
             "read_bytes_per_launch": read_b, "write_bytes_per_launch": write_b,
             "bytes_per_launch": read_b + write_b,
-            "kernel_source_hash": kernel_source_hash()}
+            "kernel_sources": KERNEL_SOURCES.get(kernel),
+            "kernel_source_hash": kernel_source_hash(KERNEL_SOURCES.get(kernel))}
 
 
 def _oracle_slice_worker(name, dtype, b0, b1, budget_s, ready, go, results):
