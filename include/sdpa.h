@@ -38,7 +38,7 @@ extern "C" {
 #define SDPA_OK               0
 #define SDPA_ERR_NULL        -1 /* a required pointer is NULL                        */
 #define SDPA_ERR_SHAPE       -2 /* a dimension < 1, or an element count overflows   */
-#define SDPA_ERR_UNSUPPORTED -3 /* d_k / d_v not supported (64 only)                 */
+#define SDPA_ERR_UNSUPPORTED -3 /* d_k / d_v, dtype or option not supported here    */
 #define SDPA_ERR_ALIGN       -4 /* a pointer is not 16-byte aligned                  */
 #define SDPA_ERR_MASK        -5 /* unknown mask_kind, causal with n != m, bad window */
 #define SDPA_ERR_DTYPE       -6 /* unknown dtype                                     */
@@ -78,8 +78,10 @@ extern "C" {
  *          (n·d·size and m·d·size; the kernels use 32-bit offsets within a
  *          head), else SDPA_ERR_SHAPE.
  * d_k, d_v query/key and value widths: d_k == d_v == 64 for both dtypes; for
- *          SDPA_BF16 also d_k == d_v == 32 or 128 (the model variants of
- *          《精读 Attention Is All You Need：原始 Transformer 论文》 Table 3).
+ *          SDPA_BF16 also d_k == d_v == 16, 32 or 128, and d_v == 64 with
+ *          d_k == 16 or 32 (the model variants of 《精读 Attention Is All
+ *          You Need：原始 Transformer 论文》 Table 3, rows (A), (B) and (C)).
+ *          Other pairs: SDPA_ERR_UNSUPPORTED.
  * scale    multiplier of the dot products; pass 1/sqrt(d_k) for Eq. (1).  Must
  *          be finite and > 0 (scale = 1 runs the unscaled dot-product form).
  * mask_kind SDPA_MASK_NONE or SDPA_MASK_CAUSAL.
@@ -323,6 +325,7 @@ SDPA_API int sdpa_forward_ex_noalloc(const void* q, const void* k, const void* v
  *           bytes, 16-byte aligned, owned by the caller (it receives D and
  *           lse · log2 e per row).  Too small: SDPA_ERR_WORKSPACE.
  * dtype     SDPA_BF16 (SDPA_F32: SDPA_ERR_UNSUPPORTED).
+ * d_k, d_v  d_k == d_v == 32, 64 or 128 (other pairs: SDPA_ERR_UNSUPPORTED).
  * The outputs and the workspace must not overlap each other or any input
  * (SDPA_ERR_ALIAS).  All tensors 16-byte aligned, lse and key_lens 4-byte
  * aligned.  Enqueues two kernels on `stream` (dQ, then dK and dV) and

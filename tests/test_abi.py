@@ -76,9 +76,13 @@ def call(q=P, k=2 * P, v=3 * P, out=4 * P, B=2, h=2, n=8, m=8, d_k=64, d_v=64, s
     (dict(B=1, h=1, n=1 << 23, m=8, d_k=128, d_v=128), _lib.SDPA_ERR_SHAPE),
     (dict(B=1, h=1, n=1, m=1 << 23, dtype=0), _lib.SDPA_ERR_SHAPE),
     (dict(d_k=32, d_v=32, dtype=0), _lib.SDPA_ERR_UNSUPPORTED),  # other widths: bf16 only
-    (dict(d_k=16, d_v=16), _lib.SDPA_ERR_UNSUPPORTED),
+    (dict(d_k=16, d_v=64, dtype=0), _lib.SDPA_ERR_UNSUPPORTED),
+    (dict(d_k=8, d_v=8), _lib.SDPA_ERR_UNSUPPORTED),
     (dict(d_k=96, d_v=96), _lib.SDPA_ERR_UNSUPPORTED),
-    (dict(d_k=32, d_v=64), _lib.SDPA_ERR_UNSUPPORTED),            # d_k != d_v
+    (dict(d_k=512, d_v=512), _lib.SDPA_ERR_UNSUPPORTED),
+    (dict(d_k=16, d_v=32), _lib.SDPA_ERR_UNSUPPORTED),            # d_k != d_v: only d_v = 64
+    (dict(d_k=128, d_v=64), _lib.SDPA_ERR_UNSUPPORTED),           # ... with d_k = 16 or 32
+    (dict(d_k=64, d_v=16), _lib.SDPA_ERR_UNSUPPORTED),
     (dict(d_v=128), _lib.SDPA_ERR_UNSUPPORTED),
     (dict(q=P + 8), _lib.SDPA_ERR_ALIGN),
     (dict(out=4 * P + 2), _lib.SDPA_ERR_ALIGN),
@@ -271,7 +275,7 @@ def call_noalloc(**kw):
     (dict(wl=-4), _lib.SDPA_ERR_MASK),
     (dict(align=7), _lib.SDPA_ERR_MASK),
     (dict(scale=float("nan")), _lib.SDPA_ERR_SCALE),
-    (dict(d_k=16, d_v=16), _lib.SDPA_ERR_UNSUPPORTED),
+    (dict(d_k=8, d_v=8), _lib.SDPA_ERR_UNSUPPORTED),
     # a split needing 64 pieces x 512 heads x 16 queries x 272 bytes = 142 MB > 8 MiB
     (dict(B=64, n=16, m=65536), _lib.SDPA_ERR_SCRATCH),
 ])
@@ -332,7 +336,7 @@ BSHD = _bshd(2, 4, 48, 80, 64)
     (dict(lse=4 * G + 256), _lib.SDPA_ERR_ALIAS),                     # lse inside out's span
     (dict(lse=6 * G, dtype=0), _lib.SDPA_ERR_UNSUPPORTED),
     (dict(wl=-3), _lib.SDPA_ERR_MASK),
-    (dict(d_k=16, d_v=16), _lib.SDPA_ERR_UNSUPPORTED),
+    (dict(d_k=8, d_v=8), _lib.SDPA_ERR_UNSUPPORTED),
 ])
 def test_forward_strided_validation_rejects_before_any_hip_call(kw, code, lib):
     assert call_strided(**kw) == code
@@ -378,6 +382,10 @@ def test_backward_workspace_size(lib):
     (dict(dtype=0), _lib.SDPA_ERR_UNSUPPORTED),
     (dict(dtype=9), _lib.SDPA_ERR_DTYPE),
     (dict(d_v=32), _lib.SDPA_ERR_UNSUPPORTED),
+    # forward-only widths: the backward kernels take equal widths 32, 64, 128
+    (dict(d_k=16, d_v=16), _lib.SDPA_ERR_UNSUPPORTED),
+    (dict(d_k=16, d_v=64), _lib.SDPA_ERR_UNSUPPORTED),
+    (dict(d_k=32, d_v=64), _lib.SDPA_ERR_UNSUPPORTED),
     (dict(m=0), _lib.SDPA_ERR_SHAPE),
     (dict(scale=float("inf")), _lib.SDPA_ERR_SCALE),
     (dict(dq=7 * P + 4), _lib.SDPA_ERR_ALIGN),

@@ -30,7 +30,7 @@ int main(void) {
           SDPA_ERR_NULL);
     CHECK(sdpa_forward(q, k, v, out, 2, 2, 8, 9, 64, 64, 0.125f, SDPA_MASK_CAUSAL, NULL, SDPA_BF16, NULL),
           SDPA_ERR_MASK);
-    CHECK(sdpa_forward(q, k, v, out, 2, 2, 8, 8, 16, 16, 0.125f, SDPA_MASK_NONE, NULL, SDPA_BF16, NULL),
+    CHECK(sdpa_forward(q, k, v, out, 2, 2, 8, 8, 8, 8, 0.125f, SDPA_MASK_NONE, NULL, SDPA_BF16, NULL),
           SDPA_ERR_UNSUPPORTED);
     CHECK(sdpa_forward_window(q, k, v, out, 2, 2, 8, 8, 64, 64, 0.125f, -2, 0, SDPA_ALIGN_TOP_LEFT, NULL,
                               SDPA_BF16, NULL), SDPA_ERR_MASK);

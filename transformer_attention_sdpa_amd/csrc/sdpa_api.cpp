@@ -43,8 +43,9 @@ int validate_core(const void* q, const void* k, const void* v, void* out, int32_
     // rows stay below 2 GiB.
     const uint64_t esz = dtype == SDPA_F32 ? 4 : 2;
     if (rows * width * esz >= (1ull << 31)) return SDPA_ERR_SHAPE;
-    // Head widths: 64 for both dtypes; 32 and 128 (d_k = d_v) for bf16.
-    const bool wide_ok = dtype == SDPA_BF16 && d_k == d_v && (d_k == 32 || d_k == 128);
+    // Head widths: 64 and 64 for both dtypes; for bf16 also the pairs of
+    // sdpa::width_supported (equal widths 16, 32, 128; d_v = 64 with d_k = 16 or 32).
+    const bool wide_ok = dtype == SDPA_BF16 && sdpa::width_supported(d_k, d_v);
     if (!(d_k == sdpa::kHeadDim && d_v == sdpa::kHeadDim) && !wide_ok) return SDPA_ERR_UNSUPPORTED;
     if (!std::isfinite(scale) || !(scale > 0.f)) return SDPA_ERR_SCALE;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return SDPA_ERR_ALIGN;
@@ -96,6 +97,7 @@ extern "C" int sdpa_forward(const void* q, const void* k, const void* v, void* o
     sdpa::Args a{q, k, v, out, B, h, n, m, scale, -1, mask_kind == SDPA_MASK_CAUSAL ? 0 : -1,
                  0, key_lens};
     a.d = d_k;
+    a.dv = d_v;
     return launch(a, dtype, stream);
 }
 
@@ -115,6 +117,7 @@ extern "C" int sdpa_forward_window(const void* q, const void* k, const void* v, 
     sdpa::Args a{q, k, v, out, B, h, n, m, scale, wl, wr,
                  align == SDPA_ALIGN_BOTTOM_RIGHT ? 1 : 0, key_lens};
     a.d = d_k;
+    a.dv = d_v;
     return launch(a, dtype, stream);
 }
 
@@ -160,6 +163,7 @@ extern "C" int sdpa_forward_lse(const void* q, const void* k, const void* v, voi
     sdpa::Args a{q, k, v, out, B, h, n, m, scale, wl, wr, br, key_lens};
     a.lse = lse;
     a.d = d_k;
+    a.dv = d_v;
     return launch(a, dtype, stream);
 }
 
@@ -213,6 +217,7 @@ extern "C" int sdpa_forward_ex(const void* q, const void* k, const void* v, void
     sdpa::Args a{q, k, v, out, B, h, n, m, scale, wl, wr, br, key_lens};
     a.lse = lse;
     a.d = d_k;
+    a.dv = d_v;
     a.work = work;
     a.work_bytes = work ? workspace_bytes : 0;
     return launch(a, dtype, stream);
@@ -234,7 +239,9 @@ extern "C" int sdpa_backward(const void* q, const void* k, const void* v, const 
     // checks below cover the outputs).
     int st = validate(q, k, v, const_cast<void*>(out), B, h, n, m, d_k, d_v, scale, key_lens, dtype);
     if (st != SDPA_OK) return st;
-    if (dtype != SDPA_BF16) return SDPA_ERR_UNSUPPORTED;  // widths: as validate() allows for bf16
+    if (dtype != SDPA_BF16) return SDPA_ERR_UNSUPPORTED;
+    // The backward kernels take equal widths 32, 64 and 128.
+    if (d_k != d_v || (d_k != 32 && d_k != 64 && d_k != 128)) return SDPA_ERR_UNSUPPORTED;
     for (const void* p : {dout, (const void*)dq, (const void*)dk, (const void*)dv, (const void*)workspace})
         if (!aligned16(p)) return SDPA_ERR_ALIGN;
     if (reinterpret_cast<uintptr_t>(lse) & 3u) return SDPA_ERR_ALIGN;
@@ -405,6 +412,7 @@ extern "C" int sdpa_forward_strided(const void* q, const void* k, const void* v,
     sdpa::Args a{q, k, v, out, B, h, n, m, scale, wl, wr, br, key_lens};
     a.lse = lse;
     a.d = d_k;
+    a.dv = d_v;
     a.work = work;
     a.work_bytes = work ? workspace_bytes : 0;
     a.lay = lay;
@@ -465,6 +473,7 @@ extern "C" int sdpa_forward_ex_noalloc(const void* q, const void* k, const void*
     sdpa::Args a{q, k, v, out, B, h, n, m, scale, wl, wr, br, key_lens};
     a.lse = lse;
     a.d = d_k;
+    a.dv = d_v;
     if (need > 0) {
         void* work = scratch_on_current_device();
         if (!work) return SDPA_ERR_LAUNCH;
@@ -480,8 +489,9 @@ extern "C" const char* sdpa_strerror(int status) {
         case SDPA_ERR_NULL: return "a required pointer is NULL";
         case SDPA_ERR_SHAPE: return "bad shape: a dimension is < 1 or an element count overflows";
         case SDPA_ERR_UNSUPPORTED:
-            return "unsupported: head widths are d_k = d_v = 64 (32 and 128 in bf16 attention); "
-                   "the log-sum-exp, backward pass and sublayer are bf16, d = 64 (backward, sublayer)";
+            return "unsupported: head widths are d_k = d_v = 64; bf16 attention also takes d_k = d_v = "
+                   "16, 32, 128 and d_v = 64 with d_k = 16 or 32; the log-sum-exp, backward pass and "
+                   "sublayer are bf16, with d_k = d_v = 32, 64 or 128 (backward, sublayer)";
         case SDPA_ERR_ALIGN: return "a device pointer is not 16-byte aligned (key_lens: 4-byte)";
         case SDPA_ERR_MASK:
             return "bad mask: unknown mask_kind, causal with n != m, window side < -1 or unknown align";

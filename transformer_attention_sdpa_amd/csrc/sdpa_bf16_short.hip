@@ -318,7 +318,7 @@ __global__ __launch_bounds__(NT) void sdpa_short_bf16(
 }  // namespace
 
 bool short_bf16_fits(const Args& a) {
-    return a.n <= MAXLEN && a.m <= MAXLEN && (a.d == 32 || a.d == 64 || a.d == 128);
+    return a.n <= MAXLEN && a.m <= MAXLEN && a.d == a.dv && (a.d == 32 || a.d == 64 || a.d == 128);
 }
 
 namespace {

@@ -1,21 +1,24 @@
-// Eq. (1) in bf16 for head widths other than 64: d_k = d_v = D ∈ {32, 128}.
+// Eq. (1) in bf16 for head widths other than the 64-wide kernels' one:
+// d_k, d_v ∈ {16, 32, 64, 128} in the combinations listed by width_supported.
 //
-// The pages' model variants change the head width at a constant cost per
-// layer (《精读 Attention Is All You Need：原始 Transformer 论文》 Table 3, rows
-// (A) and (C): h = 16 heads of 32 and h = 4 heads of 128 next to the base
-// model's 8 heads of 64; d_model = 256 with 32-wide heads, d_model = 1024 with
-// 128-wide ones).  The 64-wide kernels are tuned to their one width; this one
-// is written once for any width that is a multiple of 32, with the same
-// transposed products:
+// The pages' model variants change the head widths (《精读 Attention Is All
+// You Need：原始 Transformer 论文》 Table 3: row (A) runs h = 4, 16 and 32 heads of
+// 128, 32 and 16 next to the base model's 8 heads of 64; row (B) shrinks the
+// key width d_k to 16 or 32 and keeps d_v = 64; row (C) pairs d_model = 256
+// with 32-wide heads and d_model = 1024 with 128-wide ones).  The 64-wide
+// kernels are tuned to their one width; this one is written once for any
+// pair of widths, with the same transposed products:
 //
 //   Sᵀ (64 keys × 32 queries)  = K · Qᵀ      A = K rows from LDS, B = Qᵀ in VGPRs
-//   Oᵀ (D × 32 queries)       += Vᵀ · Pᵀ    A = Vᵀ via LDS transpose reads,
+//   Oᵀ (d_v × 32 queries)     += Vᵀ · Pᵀ    A = Vᵀ via LDS transpose reads,
 //                                           B = Pᵀ from the Sᵀ registers
 //
-// on v_mfma_f32_32x32x16_bf16, one 32-query block per wave, 64-key tiles
-// double-buffered in LDS by buffer_load … lds, and an exact online softmax
-// (the tile maximum moves the reference every tile).  Key windows, key
-// lengths and the log-sum-exp output behave exactly as in the 64-wide kernels.
+// on v_mfma_f32_32x32x16_bf16 (its 16-long contraction is one k-step at
+// d_k = 16; at d_v = 16 the upper half of the 32-row Oᵀ block is computed
+// and dropped), one 32-query block per wave, 64-key tiles double-buffered in
+// LDS by buffer_load … lds, and an exact online softmax (the tile maximum
+// moves the reference every tile).  Key windows, key lengths and the
+// log-sum-exp output behave exactly as in the 64-wide kernels.
 #include "sdpa_common.hpp"
 
 namespace sdpa {
@@ -26,11 +29,12 @@ constexpr int BT = 64;  // keys per LDS tile
 // 16-byte chunk position of chunk c of row r in a tile with D/8 chunks per
 // row, XOR-swizzled so that 16 consecutive rows read at one chunk (one
 // 16-byte MFMA operand per lane) fall on distinct banks of gfx950's 256-byte
-// LDS pass: 64-byte rows (D = 32) share a pass four at a time, 256-byte rows
-// (D = 128) fill it alone.
+// LDS pass: 32-byte rows (D = 16) share a pass eight at a time, 64-byte rows
+// (D = 32) four at a time, 256-byte rows (D = 128) fill it alone.
 template <int D>
 __device__ __forceinline__ int wswz(int r, int c) {
-    if constexpr (D == 32) return r * 4 + (c ^ ((r >> 2) & 3));
+    if constexpr (D == 16) return r * 2 + (c ^ ((r >> 3) & 1));
+    else if constexpr (D == 32) return r * 4 + (c ^ ((r >> 2) & 3));
     else if constexpr (D == 128) return r * 16 + (c ^ (r & 15));
     else return lds_swz(r, c);
 }
@@ -59,19 +63,20 @@ __device__ __forceinline__ void wlds_wait(u32x2 (&x)[N]) {
 }
 
 // STRIDED: runtime strides of `lay`; else the packed layout, compile-time.
-template <int D, int NW, bool STRIDED>
+template <int DK, int DV, int NW, bool STRIDED>
 __global__ __launch_bounds__(NW * 64) void sdpa_fwd_bf16_width(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ lse, int BH, int H, int n, int m, float c_log2, int wl,
     int wr, int bottom_right, const int32_t* __restrict__ key_lens, int nqb, Layout lay) {
-    constexpr int KS = D / 16;                // k-steps of the score product
-    constexpr int DT = D / 32;                // 32-row blocks of Oᵀ
-    constexpr int CPR = D / 8;                // 16-byte chunks per row
-    constexpr int TILE = BT * D * 2;          // bytes per tile
-    constexpr int LOADS = TILE / 1024 / NW;   // 1 KiB loads per wave per tensor per tile
-    constexpr int ROWS_PER_LOAD = 1024 / (D * 2);
-    static_assert(D % 32 == 0 && LOADS >= 1, "width");
-    __shared__ __attribute__((aligned(1024))) char lds[2 * 2 * TILE];  // [buf][K | V]
+    constexpr int KS = DK / 16;               // k-steps of the score product
+    constexpr int DT = (DV + 31) / 32;        // 32-row blocks of Oᵀ
+    constexpr int CPK = DK / 8, CPV = DV / 8; // 16-byte chunks per K / V row
+    constexpr int TK = BT * DK * 2, TV = BT * DV * 2;  // bytes per K / V tile
+    constexpr int NLK = TK / 1024, NLV = TV / 1024;    // 1 KiB loads per tile
+    constexpr int LPK = (NLK + NW - 1) / NW, LPV = (NLV + NW - 1) / NW;  // per wave, at most
+    static_assert(DK % 16 == 0 && DV % 16 == 0 && NLK >= 1 && NLV >= 1, "width");
+    static_assert(NW * 32 * DV * 2 <= 2 * (TK + TV), "output staging");
+    __shared__ __attribute__((aligned(1024))) char lds[2 * (TK + TV)];  // [buf][K | V]
 
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -99,12 +104,12 @@ __global__ __launch_bounds__(NW * 64) void sdpa_fwd_bf16_width(
     const int flo = wact ? win.lo(wlast) : 0, fhi = wact ? win.hi(wq0) : 0;
 
     const int hh = bh - b * H;
-    const uint16_t* Qh = Q + (STRIDED ? head_offset(lay.q, b, hh) : (long long)bh * n * D);
-    const uint16_t* Kh = K + (STRIDED ? head_offset(lay.k, b, hh) : (long long)bh * m * D);
-    const uint16_t* Vh = V + (STRIDED ? head_offset(lay.v, b, hh) : (long long)bh * m * D);
-    uint16_t* Oh = O + (STRIDED ? head_offset(lay.o, b, hh) : (long long)bh * n * D);
-    const int qr = STRIDED ? lay.q.r : D, kr = STRIDED ? lay.k.r : D;
-    const int vr = STRIDED ? lay.v.r : D, orr = STRIDED ? lay.o.r : D;
+    const uint16_t* Qh = Q + (STRIDED ? head_offset(lay.q, b, hh) : (long long)bh * n * DK);
+    const uint16_t* Kh = K + (STRIDED ? head_offset(lay.k, b, hh) : (long long)bh * m * DK);
+    const uint16_t* Vh = V + (STRIDED ? head_offset(lay.v, b, hh) : (long long)bh * m * DV);
+    uint16_t* Oh = O + (STRIDED ? head_offset(lay.o, b, hh) : (long long)bh * n * DV);
+    const int qr = STRIDED ? lay.q.r : DK, kr = STRIDED ? lay.k.r : DK;
+    const int vr = STRIDED ? lay.v.r : DV, orr = STRIDED ? lay.o.r : DV;
     const int qrow = wq0 + l32;
     const bool qok = qrow < n;
     // Qᵀ as the B operand: dims 16·ks + 8·hf + [0..7] of this lane's query.
@@ -116,41 +121,50 @@ __global__ __launch_bounds__(NW * 64) void sdpa_fwd_bf16_width(
 
     // Per-lane LDS offsets: the K operand of k-step ks (row l32, chunk 2·ks + hf)
     // and the Vᵀ transpose reads (rows 4·hf + gi/4, + 8; k-step j adds 16·j rows,
-    // which leaves the swizzle of these rows unchanged for every D here).
+    // which leaves the swizzle of these rows unchanged for every width here).
+    // At d_v = 16 the lanes of dims 16..31 read dims 0..15 again: those rows of
+    // Oᵀ are never stored.
     int kaddr[KS], vaddr[DT][2];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) kaddr[ks] = wswz<D>(l32, 2 * ks + hf) * 16;
+    for (int ks = 0; ks < KS; ++ks) kaddr[ks] = wswz<DK>(l32, 2 * ks + hf) * 16;
     {
         const int r0 = 4 * hf + (gi >> 2);
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-            const int c0 = 32 * dt + 16 * ((lane >> 4) & 1) + 4 * (gi & 3);
-            vaddr[dt][0] = wswz<D>(r0, c0 >> 3) * 16 + (c0 & 7) * 2;
-            vaddr[dt][1] = wswz<D>(r0 + 8, c0 >> 3) * 16 + (c0 & 7) * 2;
+            const int c0 = (32 * dt + 16 * ((lane >> 4) & 1) + 4 * (gi & 3)) & (DV >= 32 ? 1023 : DV - 1);
+            vaddr[dt][0] = wswz<DV>(r0, c0 >> 3) * 16 + (c0 & 7) * 2;
+            vaddr[dt][1] = wswz<DV>(r0 + 8, c0 >> 3) * 16 + (c0 & 7) * 2;
         }
     }
-    // Tile loads: wave w's u-th 1 KiB load fills rows ROWS_PER_LOAD·(w·LOADS + u) + lane/CPR.
-    int ldk_off[LOADS], ldv_off[LOADS], ld_lds[LOADS];
+    // Tile loads: 1 KiB load u of a tile fills rows (1024 / row bytes)·u + lane/CP;
+    // wave w issues loads w, w + NW, … of each tensor.
+    int ldk_off[LPK], ldk_lds[LPK], ldv_off[LPV], ldv_lds[LPV];
 #pragma unroll
-    for (int u = 0; u < LOADS; ++u) {
-        const int blk = w * LOADS + u;
-        const int row = ROWS_PER_LOAD * blk + lane / CPR;
-        const int pos = lane % CPR;
+    for (int u = 0; u < LPK; ++u) {
+        const int blk = w + NW * u;
+        const int row = (1024 / (DK * 2)) * blk + lane / CPK, pos = lane % CPK;
         // the chunk whose swizzled position is pos (XOR is its own inverse)
-        const int chunk = wswz<D>(row, pos) - row * CPR;
-        ldk_off[u] = row * kr * 2 + chunk * 16;
-        ldv_off[u] = row * vr * 2 + chunk * 16;
-        ld_lds[u] = blk * 1024;
+        ldk_off[u] = row * kr * 2 + (wswz<DK>(row, pos) - row * CPK) * 16;
+        ldk_lds[u] = blk * 1024;
+    }
+#pragma unroll
+    for (int u = 0; u < LPV; ++u) {
+        const int blk = w + NW * u;
+        const int row = (1024 / (DV * 2)) * blk + lane / CPV, pos = lane % CPV;
+        ldv_off[u] = row * vr * 2 + (wswz<DV>(row, pos) - row * CPV) * 16;
+        ldv_lds[u] = TK + blk * 1024;
     }
     auto issue = [&](int t, int buf) {
         // buffer ranges end with the last legal row
-        const i32x4 rk = make_rsrc(Kh + (size_t)t * BT * kr, rows_span(L - t * BT, kr, D, 2));
-        const i32x4 rv = make_rsrc(Vh + (size_t)t * BT * vr, rows_span(L - t * BT, vr, D, 2));
+        const i32x4 rk = make_rsrc(Kh + (size_t)t * BT * kr, rows_span(L - t * BT, kr, DK, 2));
+        const i32x4 rv = make_rsrc(Vh + (size_t)t * BT * vr, rows_span(L - t * BT, vr, DV, 2));
+        char* base = lds + buf * (TK + TV);
 #pragma unroll
-        for (int u = 0; u < LOADS; ++u) {
-            load16_to_lds(rk, lds + buf * 2 * TILE + ld_lds[u], ldk_off[u]);
-            load16_to_lds(rv, lds + buf * 2 * TILE + TILE + ld_lds[u], ldv_off[u]);
-        }
+        for (int u = 0; u < LPK; ++u)
+            if (NLK % NW == 0 || w + NW * u < NLK) load16_to_lds(rk, base + ldk_lds[u], ldk_off[u]);
+#pragma unroll
+        for (int u = 0; u < LPV; ++u)
+            if (NLV % NW == 0 || w + NW * u < NLV) load16_to_lds(rv, base + ldv_lds[u], ldv_off[u]);
     };
 
     const uint32_t l0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds;
@@ -169,14 +183,14 @@ __global__ __launch_bounds__(NW * 64) void sdpa_fwd_bf16_width(
         if (t + 1 < tend) issue(t + 1, buf ^ 1);
         const int k0 = t * BT;
         if (k0 < whi && k0 + BT > wlo) {  // uniform: some query of the wave sees the tile
-            const uint32_t sk = l0 + buf * 2 * TILE, sv = sk + TILE;
+            const uint32_t sk = l0 + buf * (TK + TV), sv = sk + TK;
             f32x16 s[2];
             {
                 u32x4 a[2 * KS];
 #pragma unroll
                 for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-                    for (int ks = 0; ks < KS; ++ks) a[kt * KS + ks] = wds_read_b128(sk + kaddr[ks] + kt * 32 * D * 2);
+                    for (int ks = 0; ks < KS; ++ks) a[kt * KS + ks] = wds_read_b128(sk + kaddr[ks] + kt * 32 * DK * 2);
                 wlds_wait(a);
 #pragma unroll
                 for (int kt = 0; kt < 2; ++kt) {
@@ -233,8 +247,8 @@ __global__ __launch_bounds__(NW * 64) void sdpa_fwd_bf16_width(
             for (int j = 0; j < 4; ++j)
 #pragma unroll
                 for (int dt = 0; dt < DT; ++dt) {
-                    va[(j * DT + dt) * 2] = wds_read_tr(sv + vaddr[dt][0] + j * 16 * D * 2);
-                    va[(j * DT + dt) * 2 + 1] = wds_read_tr(sv + vaddr[dt][1] + j * 16 * D * 2);
+                    va[(j * DT + dt) * 2] = wds_read_tr(sv + vaddr[dt][0] + j * 16 * DV * 2);
+                    va[(j * DT + dt) * 2 + 1] = wds_read_tr(sv + vaddr[dt][1] + j * 16 * DV * 2);
                 }
             wlds_wait(va);
 #pragma unroll
@@ -262,44 +276,46 @@ __global__ __launch_bounds__(NW * 64) void sdpa_fwd_bf16_width(
     // every wave passed the loop's last barrier after its last read), so that
     // the stores write 16 bytes a lane along rows.  Register i of oacc[dt] is
     // dim 32·dt + 8·(i/4) + 4·hf + i%4 of row l32; 16-byte chunk c of a row
-    // sits at position c ^ (row mod CPR).
-    char* area = lds + w * 32 * D * 2;
+    // sits at position c ^ (row mod CPV).
+    char* area = lds + w * 32 * DV * 2;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
             const int col = 32 * dt + 8 * i4 + 4 * hf;
-            bf16x4 o;
-            o[0] = (__bf16)(oacc[dt][4 * i4 + 0] * inv);
-            o[1] = (__bf16)(oacc[dt][4 * i4 + 1] * inv);
-            o[2] = (__bf16)(oacc[dt][4 * i4 + 2] * inv);
-            o[3] = (__bf16)(oacc[dt][4 * i4 + 3] * inv);
-            const int pos = (col >> 3) ^ (l32 & (CPR - 1));
-            *reinterpret_cast<bf16x4*>(area + (l32 * CPR + pos) * 16 + (col & 7) * 2) = o;
+            if (DV >= 32 || 8 * i4 < DV) {  // at d_v = 16, dims 16..31 are the dropped half
+                bf16x4 o;
+                o[0] = (__bf16)(oacc[dt][4 * i4 + 0] * inv);
+                o[1] = (__bf16)(oacc[dt][4 * i4 + 1] * inv);
+                o[2] = (__bf16)(oacc[dt][4 * i4 + 2] * inv);
+                o[3] = (__bf16)(oacc[dt][4 * i4 + 3] * inv);
+                const int pos = (col >> 3) ^ (l32 & (CPV - 1));
+                *reinterpret_cast<bf16x4*>(area + (l32 * CPV + pos) * 16 + (col & 7) * 2) = o;
+            }
         }
 #pragma unroll
-    for (int k = 0; k < CPR / 2; ++k) {
+    for (int k = 0; k < CPV / 2; ++k) {
         const int id = lane + 64 * k;
-        const int row = id / CPR, c = id % CPR;
-        const u32x4 x = *reinterpret_cast<const u32x4*>(area + (row * CPR + (c ^ (row & (CPR - 1)))) * 16);
+        const int row = id / CPV, c = id % CPV;
+        const u32x4 x = *reinterpret_cast<const u32x4*>(area + (row * CPV + (c ^ (row & (CPV - 1)))) * 16);
         if (wq0 + row < n) store16_nt(Oh + (size_t)(wq0 + row) * orr + 8 * c, x);
     }
 }
 
-template <int D>
+template <int DK, int DV>
 hipError_t launch_width(const Args& a, hipStream_t stream) {
     const int BH = a.B * a.H;
     const float c_log2 = (float)((double)a.scale * 1.4426950408889634);  // scale·log2(e)
     // 4 waves (128 queries) per workgroup once there are enough blocks.
     if ((long long)BH * ((a.n + 127) / 128) >= 1024) {
         const int nqb = (a.n + 127) / 128;
-        const auto kernel = a.strided ? sdpa_fwd_bf16_width<D, 4, true> : sdpa_fwd_bf16_width<D, 4, false>;
+        const auto kernel = a.strided ? sdpa_fwd_bf16_width<DK, DV, 4, true> : sdpa_fwd_bf16_width<DK, DV, 4, false>;
         hipLaunchKernelGGL(kernel, dim3(nqb * BH), dim3(256), 0, stream,
                            (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.out,
                            a.lse, BH, a.H, a.n, a.m, c_log2, a.wl, a.wr, a.bottom_right, a.key_lens, nqb, a.lay);
     } else {
         const int nqb = (a.n + 63) / 64;
-        const auto kernel = a.strided ? sdpa_fwd_bf16_width<D, 2, true> : sdpa_fwd_bf16_width<D, 2, false>;
+        const auto kernel = a.strided ? sdpa_fwd_bf16_width<DK, DV, 2, true> : sdpa_fwd_bf16_width<DK, DV, 2, false>;
         hipLaunchKernelGGL(kernel, dim3(nqb * BH), dim3(128), 0, stream,
                            (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.out,
                            a.lse, BH, a.H, a.n, a.m, c_log2, a.wl, a.wr, a.bottom_right, a.key_lens, nqb, a.lay);
@@ -309,9 +325,17 @@ hipError_t launch_width(const Args& a, hipStream_t stream) {
 
 }  // namespace
 
+bool width_supported(int d_k, int d_v) {
+    if (d_k == d_v) return d_k == 16 || d_k == 32 || d_k == 64 || d_k == 128;
+    return d_v == 64 && (d_k == 16 || d_k == 32);
+}
+
 hipError_t launch_bf16_width(const Args& a, hipStream_t stream) {
-    if (a.d == 32) return launch_width<32>(a, stream);
-    if (a.d == 128) return launch_width<128>(a, stream);
+    if (a.d == 16 && a.dv == 16) return launch_width<16, 16>(a, stream);
+    if (a.d == 32 && a.dv == 32) return launch_width<32, 32>(a, stream);
+    if (a.d == 128 && a.dv == 128) return launch_width<128, 128>(a, stream);
+    if (a.d == 16 && a.dv == 64) return launch_width<16, 64>(a, stream);
+    if (a.d == 32 && a.dv == 64) return launch_width<32, 64>(a, stream);
     return hipErrorInvalidValue;
 }
 

@@ -66,8 +66,10 @@ struct Args {
     // Optional: per query row, ln Σ_j exp(scale · q·k_j) over the legal keys
     // (−∞ for a row with none), fp32 [B, H, n]; bf16 kernels only.
     float* lse = nullptr;
-    // Head width d_k = d_v: 64 (every kernel), or 32 / 128 (bf16, sdpa_bf16_width.hip).
+    // Head widths d_k (d) and d_v (dv): 64 and 64 in every kernel; the other
+    // pairs that width_supported lists in the bf16 kernels.
     int d = kHeadDim;
+    int dv = kHeadDim;
     // Optional workspace for split-key decoder steps (decode_split_bytes), or nullptr.
     void* work = nullptr;
     size_t work_bytes = 0;
@@ -145,7 +147,9 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_mha_bf16(const MhaArgs& a, hipStream_t stream);
 
 hipError_t launch_bf16(const Args& a, hipStream_t stream);        // picks one of the four below
-hipError_t launch_bf16_width(const Args& a, hipStream_t stream);  // d = 32 or 128
+hipError_t launch_bf16_width(const Args& a, hipStream_t stream);  // widths other than 64/64
+// bf16 head widths (d_k, d_v): equal widths 16, 32, 64 or 128, or d_v = 64 with d_k = 16 or 32.
+bool width_supported(int d_k, int d_v);
 hipError_t launch_bf16_long(const Args& a, hipStream_t stream);   // any n, m
 hipError_t launch_bf16_short(const Args& a, hipStream_t stream);  // n, m <= 64; d = 32, 64, 128
 bool short_bf16_fits(const Args& a);

@@ -329,6 +329,7 @@ hipError_t launch_mha_bf16(const MhaArgs& a, hipStream_t stream) {
     // 2. Attention over the B·h heads.
     Args att{qh, kh, vh, oh, a.B, a.h, a.n, a.m, a.scale, a.wl, a.wr, a.bottom_right, a.key_lens};
     att.d = hd;
+    att.dv = hd;
     e = launch_bf16(att, stream);
     if (e != hipSuccess) return e;
 
