@@ -324,10 +324,14 @@ def test_wrapper_errors(gpu_lib):
                       0.125, _lib.SDPA_MASK_CAUSAL, None, _lib.SDPA_BF16,
                       torch.cuda.current_stream().cuda_stream)
     assert rc == _lib.SDPA_ERR_MASK
-    # widths: 64 everywhere, 32 and 128 in bf16 only, nothing else
-    q16 = torch.zeros(1, 1, 4, 16, device="cuda", dtype=torch.bfloat16)
+    # widths: 64 everywhere; 16, 32, 128 (and d_k = 16 or 32 with d_v = 64) in
+    # bf16 only; nothing else
+    q8 = torch.zeros(1, 1, 4, 8, device="cuda", dtype=torch.bfloat16)
     with pytest.raises(RuntimeError, match="64"):
-        forward(q16, q16, q16)
+        forward(q8, q8, q8)
+    q96 = torch.zeros(1, 1, 4, 96, device="cuda", dtype=torch.bfloat16)
+    with pytest.raises(RuntimeError, match="unsupported"):
+        forward(q96, q96, q96)
     q32f = torch.zeros(1, 1, 4, 32, device="cuda", dtype=torch.float32)
     with pytest.raises(RuntimeError, match="unsupported"):
         forward(q32f, q32f, q32f)
@@ -531,6 +535,10 @@ def test_local_window_8k_sampled_rows(gpu_lib):
                 picks.append((b, h, int(i)))
     for i in rows:
         picks.append((2, 9, i))
+    # both sides of every 128-query block edge (a workgroup walks four blocks)
+    for b, h in ((0, 0), (3, 15)):
+        for e in range(128, wl.n, 128):
+            picks += [(b, h, e - 1), (b, h, e)]
     ref = so.attention_rows(case["q"], case["k"], case["v"], picks, window=wl.window)
     g = np.stack([got[b, h, i] for (b, h, i) in picks])
     err = max_abs_err(g, ref)
