@@ -21,13 +21,18 @@ from __future__ import annotations
 import mpmath
 
 
-def attention_mp(q, k, v, scale, causal=False, key_lens=None, dps=50, window=None):
+def attention_mp(q, k, v, scale, causal=False, key_lens=None, dps=50, window=None, keep=None,
+                 keep_scale=1.0):
     """q: [B][h][n][d_k], k: [B][h][m][d_k], v: [B][h][m][d_v] nested sequences.
 
     ``window``: None or (left, right, align): key j is legal for query i only
     if p − left ≤ j ≤ p + right, where p = i (align 'top_left') or
     p = i + len − n (align 'bottom_right': the queries end where the keys end);
     a None side is unbounded.
+
+    ``keep`` (attention dropout): None, or [B][h][n][m] booleans; a legal key
+    then still counts in the denominator, but its value enters the sum only if
+    kept, and the sum is multiplied by ``keep_scale``.
 
     Returns nested lists of ``mpmath.mpf`` with shape [B][h][n][d_v].
     """
@@ -60,12 +65,15 @@ def attention_mp(q, k, v, scale, causal=False, key_lens=None, dps=50, window=Non
                                           for t in range(len(Q[i])))
                         e = mpmath.exp(sc * dot)
                         den += e
+                        if keep is not None and not keep[b][hh][i][j]:
+                            continue
                         for c in range(d_v):
                             num[c] += e * mpmath.mpf(float(V[j][c]))
                     if den == 0:
                         rows.append([mpmath.mpf(0)] * d_v)
                     else:
-                        rows.append([x / den for x in num])
+                        ks = mpmath.mpf(1) if keep is None else mpmath.mpf(keep_scale)
+                        rows.append([x / den * ks for x in num])
                 heads.append(rows)
             out.append(heads)
         return out
@@ -122,8 +130,10 @@ def _legal_mp(i, j, n, m, causal, L, window):
     return True
 
 
-def _head_loss_mp(Q, K, V, dO, sc, legal):
-    """Σ_i dO_i · o_i for one head, every argument already ``mpf``."""
+def _head_loss_mp(Q, K, V, dO, sc, legal, keep=None, ks=None):
+    """Σ_i dO_i · o_i for one head, every argument already ``mpf``; with
+    ``keep`` the dropped weights leave the sum (not the denominator) and the
+    sum is scaled by ``ks``."""
     total = mpmath.mpf(0)
     for i in range(len(Q)):
         den = mpmath.mpf(0)
@@ -133,15 +143,18 @@ def _head_loss_mp(Q, K, V, dO, sc, legal):
                 continue
             e = mpmath.exp(sc * mpmath.fsum(a * b for a, b in zip(Q[i], K[j])))
             den += e
+            if keep is not None and not keep[i][j]:
+                continue
             for c in range(len(num)):
                 num[c] += e * V[j][c]
         if den != 0:
-            total += mpmath.fsum(dO[i][c] * num[c] / den for c in range(len(num)))
+            mul = mpmath.mpf(1) if keep is None else ks
+            total += mpmath.fsum(dO[i][c] * num[c] / den * mul for c in range(len(num)))
     return total
 
 
 def attention_grad_fd_mp(q, k, v, do, scale, causal=False, key_lens=None, window=None, dps=60,
-                         eps=1e-20):
+                         eps=1e-20, keep=None, keep_scale=1.0):
     """Gradients of ℓ = Σ dO ∘ Attention(Q, K, V) by central differences at
     ``dps`` digits, one input element at a time: (ℓ(x + ε) − ℓ(x − ε)) / 2ε.
 
@@ -149,11 +162,13 @@ def attention_grad_fd_mp(q, k, v, do, scale, causal=False, key_lens=None, window
     (legal keys only, no maximum subtraction, as ``attention_mp``) twice per
     element.  With ε = 1e-20 at 60 digits the truncation error is O(ε²) and
     the rounding error about 10^(−60)/ε, so the result is exact far beyond
-    fp64.  Returns (dq, dk, dv) as nested lists of floats, shapes as q, k, v.
+    fp64.  ``keep``/``keep_scale``: attention dropout as in ``attention_mp``.
+    Returns (dq, dk, dv) as nested lists of floats, shapes as q, k, v.
     """
     with mpmath.workdps(dps):
         sc = mpmath.mpf(scale)
         ep = mpmath.mpf(eps)
+        ksc = mpmath.mpf(keep_scale)
         grads = ([], [], [])
         for b in range(len(q)):
             L = None if key_lens is None else int(key_lens[b])
@@ -171,9 +186,10 @@ def attention_grad_fd_mp(q, k, v, do, scale, causal=False, key_lens=None, window
                         for c in range(len(X[which][r])):
                             x0 = X[which][r][c]
                             X[which][r][c] = x0 + ep
-                            up = _head_loss_mp(X[0], X[1], X[2], dO, sc, legal)
+                            kp = None if keep is None else keep[b][hh]
+                            up = _head_loss_mp(X[0], X[1], X[2], dO, sc, legal, kp, ksc)
                             X[which][r][c] = x0 - ep
-                            dn = _head_loss_mp(X[0], X[1], X[2], dO, sc, legal)
+                            dn = _head_loss_mp(X[0], X[1], X[2], dO, sc, legal, kp, ksc)
                             X[which][r][c] = x0
                             row.append(float((up - dn) / (2 * ep)))
                         g.append(row)

@@ -716,3 +716,154 @@ BACKWARD_PINS = [
     pin_bwd_rows_finite_difference_mp,
     pin_bwd_rows_match_whole,
 ]
+
+
+# --- attention dropout (oracle.sdpa_dropout) ---------------------------------
+#
+# Dropout on the attention weights after the softmax, kept weights scaled by
+# c = 1/(1 − p) (the reading the dropout oracle states).  Each pin takes the
+# module ``oracle.sdpa_dropout``.
+
+def _drop_case(rng, B, h, n, m, d, dv):
+    q = rng.standard_normal((B, h, n, d))
+    k = rng.standard_normal((B, h, m, d))
+    v = rng.standard_normal((B, h, m, dv))
+    return q, k, v
+
+
+def pin_drop_unpack_bit_order(sd):
+    """Bit j mod 32 of word ⌊j/32⌋ is key j (least significant bit first)."""
+    words = np.array([[0x00000005, 0x80000002]], dtype=np.uint32)
+    got = sd.unpack_keep(words, 64)[0]
+    assert set(np.flatnonzero(got)) == {0, 2, 33, 63}
+    assert sd.unpack_keep(words, 35)[0].tolist() == got[:35].tolist()
+
+
+def pin_drop_all_kept_is_plain(sd):
+    """Every weight kept and c = 1: Eq. (1) itself (the pinned oracle)."""
+    import oracle.sdpa_oracle as so
+
+    rng = np.random.default_rng(90)
+    q, k, v = _drop_case(rng, 2, 2, 5, 7, 4, 3)
+    keep = np.ones((2, 2, 5, 7), bool)
+    for kw in (dict(), dict(key_lens=[7, 2]), dict(window=(1, 2, "top_left")),
+               dict(window=(None, 0, "bottom_right"), key_lens=[3, 7])):
+        assert np.array_equal(sd.attention_dropout(q, k, v, keep, 1.0, **kw), so.attention(q, k, v, **kw))
+
+
+def pin_drop_all_dropped_is_zero(sd):
+    rng = np.random.default_rng(91)
+    q, k, v = _drop_case(rng, 1, 2, 4, 6, 3, 2)
+    out = sd.attention_dropout(q, k, v, np.zeros((1, 2, 4, 6), bool), 1.25)
+    assert np.all(out == 0.0)
+
+
+def pin_drop_single_kept_key_closed_form(sd):
+    """Two keys with scaled logits x0, x1 and only key 0 kept in row 0: the
+    row is c · σ(x0 − x1) · v_0, with σ the logistic function (the softmax of
+    two logits); in row 1 only key 1 is kept: c · σ(x1 − x0) · v_1."""
+    c = 1.0 / (1.0 - 0.3)
+    for s0, s1, scale in ((8.0, 0.0, 1.0 / 8.0), (2.0, -1.0, 0.5), (0.0, 0.0, 1.0)):
+        q = np.array([[[[1.0, 0.0], [1.0, 0.0]]]])
+        k = np.array([[[[s0, 0.0], [s1, 1.0]]]])
+        v = np.array([[[[1.5, -2.0, 0.25], [-3.0, 0.5, 4.0]]]])
+        keep = np.array([[[[True, False], [False, True]]]])
+        out = sd.attention_dropout(q, k, v, keep, c, scale=scale)[0, 0]
+        x = scale * (s0 - s1)
+        sig = 1.0 / (1.0 + math.exp(-x))
+        assert np.allclose(out[0], c * sig * v[0, 0, 0], rtol=1e-14, atol=1e-15)
+        assert np.allclose(out[1], c * (1.0 - sig) * v[0, 0, 1], rtol=1e-14, atol=1e-15)
+
+
+def pin_drop_expectation_over_masks(sd):
+    """Averaging the output over every mask of a tiny head, each weighted by
+    its probability (keep with 1 − p, independently), gives Eq. (1) without
+    dropout: E[Z] = 1 − p and c = 1/(1 − p)."""
+    import itertools
+
+    import oracle.sdpa_oracle as so
+
+    rng = np.random.default_rng(92)
+    n, m, p = 2, 3, 0.3
+    q, k, v = _drop_case(rng, 1, 1, n, m, 3, 2)
+    for kw in (dict(), dict(key_lens=[2]), dict(window=(0, 1, "top_left"))):
+        mean = np.zeros((1, 1, n, 2))
+        for bits in itertools.product((0, 1), repeat=n * m):
+            keep = np.array(bits, bool).reshape(1, 1, n, m)
+            pr = (1 - p) ** keep.sum() * p ** (n * m - keep.sum())
+            mean += pr * sd.attention_dropout(q, k, v, keep, 1.0 / (1.0 - p), **kw)
+        assert np.allclose(mean, so.attention(q, k, v, **kw), rtol=0, atol=1e-13), kw
+
+
+def pin_drop_disjoint_masks_add(sd):
+    """The output is linear in Z: masks with no kept weight in common add."""
+    rng = np.random.default_rng(93)
+    q, k, v = _drop_case(rng, 2, 2, 6, 9, 4, 4)
+    u = rng.random((2, 2, 6, 9))
+    z1, z2 = u < 0.3, (u >= 0.3) & (u < 0.75)
+    c = 1.7
+    a = sd.attention_dropout(q, k, v, z1, c, causal=False, key_lens=[9, 4])
+    b = sd.attention_dropout(q, k, v, z2, c, causal=False, key_lens=[9, 4])
+    both = sd.attention_dropout(q, k, v, z1 | z2, c, causal=False, key_lens=[9, 4])
+    assert np.allclose(a + b, both, rtol=0, atol=1e-13)
+
+
+def pin_drop_brute_force_mp(sd):
+    """50-digit scalar loops (``oracle.brute_mp.attention_mp`` with a mask):
+    the legal keys fill the denominator, the kept ones the sum."""
+    from oracle.brute_mp import attention_mp
+
+    rng = np.random.default_rng(94)
+    for (B, h, n, m, d, dv) in ((2, 2, 4, 4, 3, 2), (1, 2, 3, 5, 2, 3)):
+        q, k, v = _drop_case(rng, B, h, n, m, d, dv)
+        keep = rng.random((B, h, n, m)) < 0.6
+        for causal, kl, win in ((False, None, None), (n == m, [m, 1][:B], None),
+                                (False, [m, 2][:B], (1, 1, "top_left")), (False, None, (None, 0, "bottom_right"))):
+            ref = np.array(attention_mp(q.tolist(), k.tolist(), v.tolist(), 0.6, causal, kl, window=win,
+                                        keep=keep.tolist(), keep_scale=1.25), dtype=np.float64)
+            got = sd.attention_dropout(q, k, v, keep, 1.25, scale=0.6, causal=causal, key_lens=kl, window=win)
+            assert np.allclose(got, ref, rtol=0, atol=1e-14), (causal, kl, win)
+
+
+def pin_drop_bwd_finite_difference_mp(sd):
+    """Gradients against 60-digit central differences of the forward with the
+    same mask (``attention_grad_fd_mp`` with ``keep``)."""
+    from oracle.brute_mp import attention_grad_fd_mp
+
+    rng = np.random.default_rng(95)
+    for (n, m) in ((3, 3), (2, 4)):
+        q, k, v = _drop_case(rng, 2, 1, n, m, 3, 2)
+        do = rng.standard_normal((2, 1, n, 2))
+        keep = rng.random((2, 1, n, m)) < 0.5
+        for causal, kl, win in ((False, None, None), (n == m, [m, 1], None), (False, [m, 2], (1, 0, "top_left"))):
+            fd = attention_grad_fd_mp(q.tolist(), k.tolist(), v.tolist(), do.tolist(), 0.7, causal, kl, win,
+                                      keep=keep.tolist(), keep_scale=1.6)
+            got = sd.attention_dropout_backward(q, k, v, do, keep, 1.6, scale=0.7, causal=causal, key_lens=kl,
+                                                window=win)
+            for g, f in zip(got, fd):
+                assert np.allclose(g, np.array(f), rtol=0, atol=1e-12), (n, m, causal, kl, win)
+
+
+def pin_drop_bwd_all_kept_is_plain(sd):
+    import oracle.sdpa_backward as sb
+
+    rng = np.random.default_rng(96)
+    q, k, v = _drop_case(rng, 2, 1, 5, 6, 3, 4)
+    do = rng.standard_normal((2, 1, 5, 4))
+    keep = np.ones((2, 1, 5, 6), bool)
+    for a, b in zip(sd.attention_dropout_backward(q, k, v, do, keep, 1.0, key_lens=[6, 3]),
+                    sb.attention_backward(q, k, v, do, key_lens=[6, 3])):
+        assert np.array_equal(a, b)
+
+
+DROPOUT_PINS = [
+    pin_drop_unpack_bit_order,
+    pin_drop_all_kept_is_plain,
+    pin_drop_all_dropped_is_zero,
+    pin_drop_single_kept_key_closed_form,
+    pin_drop_expectation_over_masks,
+    pin_drop_disjoint_masks_add,
+    pin_drop_brute_force_mp,
+    pin_drop_bwd_finite_difference_mp,
+    pin_drop_bwd_all_kept_is_plain,
+]

@@ -309,3 +309,51 @@ def test_some_backward_pin_catches_row_helper_mutant(name, monkeypatch):
         except Exception as e:
             caught.append((pin.__name__, type(e).__name__))
     assert caught, f"no pin detects mutant {name}"
+
+
+# --- attention dropout ---------------------------------------------------------
+#
+# Mistakes one could make in the dropout step: the rescale 1/(1 − p) left
+# out, the mask read transposed or inverted, the kept weights renormalised
+# (a softmax over the kept keys only), the gradient passed through the mask
+# unmasked or unscaled, or the mask's bits read most significant first.
+
+import oracle.sdpa_dropout as sd  # noqa: E402
+from tests.oracle_pins import DROPOUT_PINS  # noqa: E402
+
+
+def _renormalised(p, keep, c):
+    x = p * keep
+    s = x.sum(axis=1, keepdims=True)
+    return np.divide(x, s, out=np.zeros_like(x), where=s > 0)
+
+
+def _msb_first(words, m):
+    words = np.asarray(words, dtype=np.uint32)
+    j = np.arange(m)
+    return ((words[..., j // 32] >> (31 - j % 32).astype(np.uint32)) & 1).astype(bool)
+
+
+DROPOUT_MUTANTS = {
+    "keep_scale_dropped": ("dropped_weights", lambda p, keep, c: p * keep),
+    "keep_inverted": ("dropped_weights", lambda p, keep, c: p * ~keep * c),
+    "keep_transposed": ("dropped_weights", lambda p, keep, c: p * (keep.T if keep.shape[0] == keep.shape[1]
+                                                                    else keep) * c),
+    "kept_weights_renormalised": ("dropped_weights", _renormalised),
+    "grad_not_masked": ("grad_through_dropout", lambda dpt, keep, c: dpt * c),
+    "grad_not_scaled": ("grad_through_dropout", lambda dpt, keep, c: dpt * keep),
+    "bits_msb_first": ("unpack_keep", _msb_first),
+}
+
+
+@pytest.mark.parametrize("name", sorted(DROPOUT_MUTANTS))
+def test_some_dropout_pin_catches_mutant(name, monkeypatch):
+    attr, fn = DROPOUT_MUTANTS[name]
+    monkeypatch.setattr(sd, attr, fn)
+    caught = []
+    for pin in DROPOUT_PINS:
+        try:
+            pin(sd)
+        except Exception as e:
+            caught.append((pin.__name__, type(e).__name__))
+    assert caught, f"no pin detects mutant {name}"

@@ -19,3 +19,13 @@ def test_backward_pin(pin):
     import oracle.sdpa_backward as sb
 
     pin(sb)
+
+
+from tests.oracle_pins import DROPOUT_PINS  # noqa: E402
+
+
+@pytest.mark.parametrize("pin", DROPOUT_PINS, ids=[p.__name__ for p in DROPOUT_PINS])
+def test_dropout_pin(pin):
+    import oracle.sdpa_dropout as sd
+
+    pin(sd)
