@@ -48,10 +48,12 @@ def test_algorithmic_work_matches_brute_force(name):
     for dt, esz in (("bf16", 2), ("f32", 4)):
         flops, nbytes, dense = bench.algorithmic_work(wl, dt, key_lens)
         pairs, kv_rows = _brute(wl, key_lens)
-        d = wl.d_k
-        assert flops == 2 * (wl.d_k + wl.d_v) * pairs == 4 * d * pairs
-        assert dense == 4 * d * wl.B * wl.h * wl.n * wl.m
-        assert nbytes == esz * (2 * wl.B * wl.h * wl.n * d + 2 * kv_rows * d)
+        # 2·d_k per score and 2·d_v per weighted value; Q, O and the legal
+        # K, V rows (d_k + d_v elements per query row and per key row)
+        dk, dv = wl.d_k, wl.d_v
+        assert flops == 2 * (dk + dv) * pairs
+        assert dense == 2 * (dk + dv) * wl.B * wl.h * wl.n * wl.m
+        assert nbytes == esz * (wl.B * wl.h * wl.n * (dk + dv) + kv_rows * (dk + dv))
 
 
 def test_key_length_edge_cases():
