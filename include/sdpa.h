@@ -43,7 +43,7 @@ extern "C" {
 #define SDPA_ERR_MASK        -5 /* unknown mask_kind, causal with n != m, bad window */
 #define SDPA_ERR_DTYPE       -6 /* unknown dtype                                     */
 #define SDPA_ERR_LAUNCH      -7 /* the HIP runtime refused this call's kernel launch */
-#define SDPA_ERR_SCALE       -8 /* scale is not finite, or not > 0                   */
+#define SDPA_ERR_SCALE       -8 /* scale (or keep_scale) not finite, or not > 0     */
 #define SDPA_ERR_ALIAS       -9 /* out overlaps q, k, v or key_lens                   */
 #define SDPA_ERR_WORKSPACE  -10 /* workspace smaller than its *_workspace_bytes size */
 #define SDPA_ERR_SCRATCH    -11 /* a call needs more than the library's static scratch */
@@ -339,6 +339,45 @@ SDPA_API int sdpa_backward(const void* q, const void* k, const void* v, const vo
                            float scale, int32_t window_left, int32_t window_right, int32_t align,
                            const int32_t* key_lens, int32_t dtype, void* workspace,
                            size_t workspace_bytes, void* stream);
+
+/*
+ * Attention dropout (training).  The pages train with dropout (《Attention Is
+ * All You Need：注意力就是你所需要的一切》 §5.4, citing the dropout paper [33])
+ * and tune an attention dropout for parsing (same page, §6.3) without placing
+ * it; here it acts on the weights after the softmax of Eq. (1):
+ *
+ *     O = (P ∘ Z) V · keep_scale,    P = softmax(scale · Q Kᵀ) over the legal keys,
+ *
+ * with Z the caller's keep mask (draw Z_ij = 1 with probability 1 − p and
+ * pass keep_scale = 1/(1 − p) for the usual unbiased form).  The softmax is
+ * unchanged: its normaliser, and lse, count every legal key, kept or not.
+ *
+ * sdpa_forward_dropout: arguments as in sdpa_forward_window, plus
+ * lse        optional (NULL or float [B, h, n], as in sdpa_forward_lse).
+ * keep_mask  device, uint32 [B, h, n, ⌈m/32⌉], 4-byte aligned, read only: bit
+ *            (j mod 32) of word ⌊j/32⌋ of row (b, head, i) is 1 to keep
+ *            weight (i, j).  Bits of illegal keys and past m are ignored.
+ * keep_scale finite and > 0 (else SDPA_ERR_SCALE).
+ * dtype SDPA_BF16 and d_k == d_v == 64 only (else SDPA_ERR_UNSUPPORTED).  out
+ * and lse must not overlap the mask or the inputs (SDPA_ERR_ALIAS).
+ *
+ * sdpa_backward_dropout: the gradient of that forward pass for the same mask
+ * and factor (dV = (P ∘ Z)ᵀ dO · keep_scale, dP = (dO Vᵀ) ∘ Z · keep_scale,
+ * then as in sdpa_backward, whose other arguments it takes unchanged; `out`
+ * and `lse` are the dropout forward's).  Widths and dtype as for the forward;
+ * the outputs and workspace must not overlap the mask either.
+ */
+SDPA_API int sdpa_forward_dropout(const void* q, const void* k, const void* v, void* out, float* lse,
+                                  int32_t B, int32_t h, int32_t n, int32_t m, int32_t d_k, int32_t d_v,
+                                  float scale, int32_t window_left, int32_t window_right, int32_t align,
+                                  const int32_t* key_lens, const uint32_t* keep_mask, float keep_scale,
+                                  int32_t dtype, void* stream);
+SDPA_API int sdpa_backward_dropout(const void* q, const void* k, const void* v, const void* out,
+                                   const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                                   int32_t B, int32_t h, int32_t n, int32_t m, int32_t d_k, int32_t d_v,
+                                   float scale, int32_t window_left, int32_t window_right, int32_t align,
+                                   const int32_t* key_lens, const uint32_t* keep_mask, float keep_scale,
+                                   int32_t dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static text for a status code (never NULL). */
 SDPA_API const char* sdpa_strerror(int status);

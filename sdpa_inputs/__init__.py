@@ -266,3 +266,21 @@ def random_case(rng: np.random.Generator, B, h, n, m, d_k, d_v, dtype="f32", cau
     kl = None if key_lens is None else np.asarray(key_lens, dtype=np.int32)
     return {"q": q, "k": k, "v": v, "key_lens": kl, "causal": causal, "window": window,
             "dtype": dtype}
+
+
+def random_keep(rng: np.random.Generator, B, h, n, m, p: float):
+    """Attention-dropout draw: bool [B, h, n, m], each entry True (kept) with
+    probability 1 − p, independently."""
+    return rng.random((B, h, n, m)) >= p
+
+
+def pack_keep(keep) -> np.ndarray:
+    """The keep mask in the layout the GPU path reads: uint32 [B, h, n, ⌈m/32⌉],
+    bit (j mod 32) of word ⌊j/32⌋ for key j; bits past m are 0."""
+    keep = np.asarray(keep, dtype=bool)
+    m = keep.shape[-1]
+    W = (m + 31) // 32
+    padded = np.zeros(keep.shape[:-1] + (W * 32,), dtype=np.uint64)
+    padded[..., :m] = keep
+    weights = np.left_shift(np.uint64(1), np.arange(32, dtype=np.uint64))
+    return (padded.reshape(keep.shape[:-1] + (W, 32)) * weights).sum(-1).astype(np.uint32)

@@ -32,8 +32,8 @@ def test_every_declared_entry_point_is_exported(lib):
                           "sdpa_mha_workspace_bytes", "sdpa_forward_lse", "sdpa_backward",
                           "sdpa_backward_workspace_bytes", "sdpa_forward_ex",
                           "sdpa_forward_ex_noalloc", "sdpa_forward_strided",
-                          "sdpa_forward_workspace_bytes",
-                          "sdpa_strerror", "sdpa_version"}
+                          "sdpa_forward_workspace_bytes", "sdpa_forward_dropout",
+                          "sdpa_backward_dropout", "sdpa_strerror", "sdpa_version"}
     for name in names:
         assert isinstance(getattr(lib, name), ctypes._CFuncPtr)
 
@@ -453,3 +453,66 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
         _lib.sdpa_version()
     with pytest.raises(ImportError):
         call()
+
+
+# --- attention dropout -----------------------------------------------------------
+
+def call_fwd_drop(**kw):
+    a = dict(q=P, k=2 * P, v=3 * P, out=4 * P, lse=None, B=2, h=2, n=8, m=40, d_k=64, d_v=64, scale=0.125,
+             wl=-1, wr=-1, align=0, key_lens=None, keep=11 * P, keep_scale=1.25, dtype=1)
+    a.update(kw)
+    return _lib.sdpa_forward_dropout(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["h"], a["n"], a["m"],
+                                     a["d_k"], a["d_v"], a["scale"], a["wl"], a["wr"], a["align"], a["key_lens"],
+                                     a["keep"], a["keep_scale"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(keep=None), _lib.SDPA_ERR_NULL),
+    (dict(q=None), _lib.SDPA_ERR_NULL),
+    (dict(dtype=0), _lib.SDPA_ERR_UNSUPPORTED),                  # bf16 only
+    (dict(d_k=32, d_v=32), _lib.SDPA_ERR_UNSUPPORTED),           # width 64 only
+    (dict(d_k=16, d_v=64), _lib.SDPA_ERR_UNSUPPORTED),
+    (dict(dtype=5), _lib.SDPA_ERR_DTYPE),
+    (dict(keep_scale=0.0), _lib.SDPA_ERR_SCALE),
+    (dict(keep_scale=-1.0), _lib.SDPA_ERR_SCALE),
+    (dict(keep_scale=math.nan), _lib.SDPA_ERR_SCALE),
+    (dict(keep_scale=math.inf), _lib.SDPA_ERR_SCALE),
+    (dict(keep=11 * P + 2), _lib.SDPA_ERR_ALIGN),
+    (dict(lse=6 * P + 1), _lib.SDPA_ERR_ALIGN),
+    (dict(wl=-2), _lib.SDPA_ERR_MASK),
+    (dict(keep=4 * P + 16), _lib.SDPA_ERR_ALIAS),                # mask inside out
+    (dict(keep=4 * P - 2 * 2 * 8 * 2 * 4 + 4), _lib.SDPA_ERR_ALIAS),  # mask's last word on out
+    (dict(lse=11 * P + 8), _lib.SDPA_ERR_ALIAS),                 # lse on the mask
+    (dict(lse=4 * P), _lib.SDPA_ERR_ALIAS),                      # lse on out
+])
+def test_forward_dropout_validation_rejects_before_any_hip_call(kw, code, lib):
+    assert call_fwd_drop(**kw) == code
+
+
+def call_bwd_drop(**kw):
+    B, h, n = kw.get("B", 2), kw.get("h", 2), kw.get("n", 8)
+    a = dict(q=P, k=2 * P, v=3 * P, out=4 * P, dout=5 * P, lse=6 * P, dq=7 * P, dk=8 * P, dv=9 * P,
+             B=B, h=h, n=n, m=8, d_k=64, d_v=64, scale=0.125, wl=-1, wr=-1, align=0, key_lens=None,
+             keep=11 * P, keep_scale=2.0, dtype=1, ws=10 * P, ws_bytes=_lib.sdpa_backward_workspace_bytes(B, h, n))
+    a.update(kw)
+    return _lib.sdpa_backward_dropout(a["q"], a["k"], a["v"], a["out"], a["dout"], a["lse"], a["dq"], a["dk"],
+                                      a["dv"], a["B"], a["h"], a["n"], a["m"], a["d_k"], a["d_v"], a["scale"],
+                                      a["wl"], a["wr"], a["align"], a["key_lens"], a["keep"], a["keep_scale"],
+                                      a["dtype"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(keep=None), _lib.SDPA_ERR_NULL),
+    (dict(dout=None), _lib.SDPA_ERR_NULL),
+    (dict(dtype=0), _lib.SDPA_ERR_UNSUPPORTED),
+    (dict(dtype=7), _lib.SDPA_ERR_DTYPE),
+    (dict(d_k=128, d_v=128), _lib.SDPA_ERR_UNSUPPORTED),  # the backward takes 128; dropout does not
+    (dict(keep_scale=math.inf), _lib.SDPA_ERR_SCALE),
+    (dict(keep=11 * P + 1), _lib.SDPA_ERR_ALIGN),
+    (dict(ws_bytes=8), _lib.SDPA_ERR_WORKSPACE),
+    (dict(dq=11 * P), _lib.SDPA_ERR_ALIAS),                # dq on the mask
+    (dict(ws=11 * P + 16), _lib.SDPA_ERR_ALIAS),           # workspace on the mask
+    (dict(dv=P), _lib.SDPA_ERR_ALIAS),
+])
+def test_backward_dropout_validation_rejects_before_any_hip_call(kw, code, lib):
+    assert call_bwd_drop(**kw) == code

@@ -12,15 +12,16 @@ from __future__ import annotations
 import math
 
 from . import _lib
-from ._lib import (sdpa_backward, sdpa_backward_workspace_bytes, sdpa_forward,  # noqa: F401
-                   sdpa_forward_ex, sdpa_forward_ex_noalloc, sdpa_forward_lse, sdpa_forward_strided,
-                   sdpa_forward_window,
+from ._lib import (sdpa_backward, sdpa_backward_dropout, sdpa_backward_workspace_bytes,  # noqa: F401
+                   sdpa_forward, sdpa_forward_dropout, sdpa_forward_ex, sdpa_forward_ex_noalloc,
+                   sdpa_forward_lse, sdpa_forward_strided, sdpa_forward_window,
                    sdpa_forward_workspace_bytes, sdpa_mha_forward,
                    sdpa_mha_workspace_bytes, sdpa_strerror, sdpa_version)
 
-__all__ = ["forward", "backward", "mha_forward", "sdpa_forward", "sdpa_forward_window",
+__all__ = ["forward", "backward", "mha_forward", "dropout_keep_mask", "forward_dropout", "backward_dropout",
+           "sdpa_forward", "sdpa_forward_window",
            "sdpa_forward_lse", "sdpa_forward_ex", "sdpa_forward_ex_noalloc", "sdpa_forward_strided",
-           "sdpa_forward_workspace_bytes",
+           "sdpa_forward_workspace_bytes", "sdpa_forward_dropout", "sdpa_backward_dropout",
            "sdpa_backward", "sdpa_backward_workspace_bytes",
            "sdpa_mha_forward", "sdpa_mha_workspace_bytes", "sdpa_strerror", "sdpa_version"]
 
@@ -293,3 +294,93 @@ def forward(q, k, v, *, causal: bool = False, key_lens=None, scale: float | None
     if rc != _lib.SDPA_OK:
         raise RuntimeError(f"sdpa_forward failed ({rc}): {sdpa_strerror(rc)}")
     return (out, lse) if return_lse else out
+
+
+# --- attention dropout ----------------------------------------------------------
+
+def dropout_keep_mask(B: int, h: int, n: int, m: int, p: float, *, device="cuda", generator=None):
+    """A keep mask for ``forward_dropout``: each weight (i, j) kept with
+    probability 1 − p, packed as the library reads it, int32 [B, h, n, ⌈m/32⌉]
+    with bit (j mod 32) of word ⌊j/32⌋ for key j.  Drawn with torch on
+    ``device`` (input preparation, not a step of the attention path)."""
+    import torch
+
+    if not 0.0 <= p < 1.0:
+        raise ValueError("the dropout probability p must be in [0, 1)")
+    W = (m + 31) // 32
+    u = torch.rand((B, h, n, W * 32), device=device, generator=generator)
+    bits = (u >= p).view(B, h, n, W, 32).to(torch.int64)
+    words = (bits << torch.arange(32, device=device, dtype=torch.int64)).sum(-1)
+    return torch.where(words >= 1 << 31, words - (1 << 32), words).to(torch.int32)
+
+
+def _check_keep(keep_mask, B, h, n, m, device):
+    import torch
+
+    W = (m + 31) // 32
+    if (keep_mask.dtype != torch.int32 or tuple(keep_mask.shape) != (B, h, n, W)
+            or not keep_mask.is_contiguous() or keep_mask.device != device):
+        raise ValueError(f"keep_mask must be a contiguous int32 [{B}, {h}, {n}, {W}] tensor on q's device")
+
+
+def forward_dropout(q, k, v, keep_mask, keep_scale: float, *, causal: bool = False, key_lens=None,
+                    scale: float | None = None, window=None, out=None, return_lse: bool = False):
+    """Eq. (1) with attention dropout: O = (P ∘ Z) V · keep_scale, the keep
+    mask Z as ``dropout_keep_mask`` packs it (pass keep_scale = 1/(1 − p)).
+    bf16, d_k = d_v = 64, packed [B, h, len, 64] tensors; other arguments as
+    in ``forward``.  lse (with ``return_lse``) is the softmax's, unchanged by
+    the mask, and is what ``backward_dropout`` takes."""
+    import torch
+
+    wl, wr, al = _window_args(window, causal, *_lengths(q, k))
+    B, h, n, m, d_k, d_v, dt = _check_qkv(q, k, v)
+    _check_keep(keep_mask, B, h, n, m, q.device)
+    key_lens, kl_ptr = _key_lens_ptr(key_lens, B, q.device)
+    out = _like(out, (B, h, n, d_v), q.dtype, q.device, "out")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d_k)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        lse = torch.empty((B, h, n), dtype=torch.float32, device=q.device) if return_lse else None
+        rc = sdpa_forward_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                  None if lse is None else lse.data_ptr(), B, h, n, m, d_k, d_v, float(scale),
+                                  wl, wr, al, kl_ptr, keep_mask.data_ptr(), float(keep_scale), dt, stream)
+    if rc != _lib.SDPA_OK:
+        raise RuntimeError(f"sdpa_forward_dropout failed ({rc}): {sdpa_strerror(rc)}")
+    return (out, lse) if return_lse else out
+
+
+def backward_dropout(q, k, v, out, dout, lse, keep_mask, keep_scale: float, *, causal: bool = False,
+                     key_lens=None, scale: float | None = None, window=None, dq=None, dk=None, dv=None,
+                     workspace=None):
+    """Gradients (dq, dk, dv) of ``forward_dropout`` for the same mask and
+    factor; ``out`` and ``lse`` are that forward's.  Arguments as in
+    ``backward``."""
+    import torch
+
+    wl, wr, al = _window_args(window, causal, *_lengths(q, k))
+    B, h, n, m, d_k, d_v, dt = _check_qkv(q, k, v)
+    _check_keep(keep_mask, B, h, n, m, q.device)
+    for name, t, shape, dtype in (("out", out, (B, h, n, d_v), q.dtype),
+                                  ("dout", dout, (B, h, n, d_v), q.dtype),
+                                  ("lse", lse, (B, h, n), torch.float32)):
+        _like(t, shape, dtype, q.device, name)
+    key_lens, kl_ptr = _key_lens_ptr(key_lens, B, q.device)
+    dq = _like(dq, (B, h, n, d_k), q.dtype, q.device, "dq")
+    dk = _like(dk, (B, h, m, d_k), q.dtype, q.device, "dk")
+    dv = _like(dv, (B, h, m, d_v), q.dtype, q.device, "dv")
+    need = sdpa_backward_workspace_bytes(B, h, n)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d_k)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        rc = sdpa_backward_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
+                                   lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, h, n, m,
+                                   d_k, d_v, float(scale), wl, wr, al, kl_ptr, keep_mask.data_ptr(),
+                                   float(keep_scale), dt, workspace.data_ptr(),
+                                   workspace.numel() * workspace.element_size(), stream)
+    if rc != _lib.SDPA_OK:
+        raise RuntimeError(f"sdpa_backward_dropout failed ({rc}): {sdpa_strerror(rc)}")
+    return dq, dk, dv

@@ -80,6 +80,13 @@ def load() -> ctypes.CDLL:
     lib.sdpa_backward.argtypes = [vp, vp, vp, vp, vp, fp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                   ctypes.c_float, i32, i32, i32, vp, i32, vp, ctypes.c_size_t, vp]
     lib.sdpa_backward.restype = ctypes.c_int
+    lib.sdpa_forward_dropout.argtypes = [vp, vp, vp, vp, fp, i32, i32, i32, i32, i32, i32, ctypes.c_float,
+                                         i32, i32, i32, vp, vp, ctypes.c_float, i32, vp]
+    lib.sdpa_forward_dropout.restype = ctypes.c_int
+    lib.sdpa_backward_dropout.argtypes = [vp, vp, vp, vp, vp, fp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                          ctypes.c_float, i32, i32, i32, vp, vp, ctypes.c_float, i32, vp,
+                                          ctypes.c_size_t, vp]
+    lib.sdpa_backward_dropout.restype = ctypes.c_int
     lib.sdpa_strerror.argtypes = [ctypes.c_int]
     lib.sdpa_strerror.restype = ctypes.c_char_p
     lib.sdpa_version.argtypes = []
@@ -161,6 +168,22 @@ def sdpa_forward_ex_noalloc(q, k, v, out, lse, B, h, n, m, d_k, d_v, scale, wind
 def sdpa_backward_workspace_bytes(B, h, n) -> int:
     """Forward to the C entry point of the same name."""
     return load().sdpa_backward_workspace_bytes(B, h, n)
+
+
+def sdpa_forward_dropout(q, k, v, out, lse, B, h, n, m, d_k, d_v, scale, window_left, window_right, align,
+                         key_lens, keep_mask, keep_scale, dtype, stream) -> int:
+    """Forward to the C entry point of the same name (attention dropout)."""
+    return load().sdpa_forward_dropout(q, k, v, out, lse, B, h, n, m, d_k, d_v, scale, window_left,
+                                       window_right, align, key_lens, keep_mask, keep_scale, dtype, stream)
+
+
+def sdpa_backward_dropout(q, k, v, out, dout, lse, dq, dk, dv, B, h, n, m, d_k, d_v, scale, window_left,
+                          window_right, align, key_lens, keep_mask, keep_scale, dtype, workspace,
+                          workspace_bytes, stream) -> int:
+    """Forward to the C entry point of the same name (gradient with attention dropout)."""
+    return load().sdpa_backward_dropout(q, k, v, out, dout, lse, dq, dk, dv, B, h, n, m, d_k, d_v, scale,
+                                        window_left, window_right, align, key_lens, keep_mask, keep_scale,
+                                        dtype, workspace, workspace_bytes, stream)
 
 
 def sdpa_backward(q, k, v, out, dout, lse, dq, dk, dv, B, h, n, m, d_k, d_v, scale, window_left,

@@ -13,7 +13,7 @@
 
 namespace {
 
-constexpr int kVersion = 1 * 10000 + 5 * 100 + 0;  // 1.5.0: sdpa_forward_strided
+constexpr int kVersion = 1 * 10000 + 6 * 100 + 0;  // 1.6.0: attention dropout
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -228,12 +228,27 @@ extern "C" size_t sdpa_backward_workspace_bytes(int32_t B, int32_t h, int32_t n)
     return sdpa::bwd_workspace_bytes(B, h, n);
 }
 
-extern "C" int sdpa_backward(const void* q, const void* k, const void* v, const void* out,
-                             const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                             int32_t B, int32_t h, int32_t n, int32_t m, int32_t d_k, int32_t d_v,
-                             float scale, int32_t window_left, int32_t window_right, int32_t align,
-                             const int32_t* key_lens, int32_t dtype, void* workspace,
-                             size_t workspace_bytes, void* stream) {
+namespace {
+
+// Keep-bit words of attention dropout: [B, h, n, ⌈m/32⌉] uint32.
+uint64_t keep_bytes(int32_t B, int32_t h, int32_t n, int32_t m) {
+    return (uint64_t)B * h * n * (((uint64_t)m + 31) / 32) * 4;
+}
+
+// The mask, its factor and the widths the dropout kernels take.
+int validate_dropout(const uint32_t* keep, float keep_scale, int32_t d_k, int32_t d_v, int32_t dtype) {
+    if (!keep) return SDPA_ERR_NULL;
+    if (dtype != SDPA_BF16 || d_k != sdpa::kHeadDim || d_v != sdpa::kHeadDim) return SDPA_ERR_UNSUPPORTED;
+    if (!std::isfinite(keep_scale) || !(keep_scale > 0.f)) return SDPA_ERR_SCALE;
+    if (reinterpret_cast<uintptr_t>(keep) & 3u) return SDPA_ERR_ALIGN;
+    return SDPA_OK;
+}
+
+int backward_impl(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                  const float* lse, void* dq, void* dk, void* dv, int32_t B, int32_t h, int32_t n,
+                  int32_t m, int32_t d_k, int32_t d_v, float scale, int32_t window_left,
+                  int32_t window_right, int32_t align, const int32_t* key_lens, const uint32_t* keep,
+                  float keep_scale, int32_t dtype, void* workspace, size_t workspace_bytes, void* stream) {
     if (!dout || !lse || !dq || !dk || !dv || !workspace) return SDPA_ERR_NULL;
     // q, k, v, out, shapes, scale, key_lens (out is an input here: the alias
     // checks below cover the outputs).
@@ -254,7 +269,8 @@ extern "C" int sdpa_backward(const void* q, const void* k, const void* v, const 
     struct Buf { const void* p; uint64_t n; };
     const Buf ins[] = {{q, heads * n * d_k * 2}, {k, heads * m * d_k * 2}, {v, heads * m * d_v * 2},
                        {out, heads * n * d_v * 2}, {dout, heads * n * d_v * 2}, {lse, heads * n * 4},
-                       {key_lens, key_lens ? (uint64_t)B * 4 : 0}};
+                       {key_lens, key_lens ? (uint64_t)B * 4 : 0},
+                       {keep, keep ? keep_bytes(B, h, n, m) : 0}};
     const Buf outs[] = {{dq, heads * n * d_k * 2}, {dk, heads * m * d_k * 2}, {dv, heads * m * d_v * 2},
                         {workspace, need}};
     for (int i = 0; i < 4; ++i) {
@@ -263,11 +279,71 @@ extern "C" int sdpa_backward(const void* q, const void* k, const void* v, const 
         for (int j = i + 1; j < 4; ++j)
             if (overlap(outs[i].p, outs[i].n, outs[j].p, outs[j].n)) return SDPA_ERR_ALIAS;
     }
-    const sdpa::BwdArgs a{q, k, v, out, dout, lse, dq, dk, dv, workspace, B, h, n, m, scale, wl, wr, br,
-                          key_lens, d_k};
+    sdpa::BwdArgs a{q, k, v, out, dout, lse, dq, dk, dv, workspace, B, h, n, m, scale, wl, wr, br,
+                    key_lens, d_k};
+    a.keep = keep;
+    a.keep_scale = keep_scale;
     clear_pending_error();
     const hipError_t e = sdpa::launch_bwd_bf16(a, reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? SDPA_OK : SDPA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" int sdpa_backward(const void* q, const void* k, const void* v, const void* out,
+                             const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                             int32_t B, int32_t h, int32_t n, int32_t m, int32_t d_k, int32_t d_v,
+                             float scale, int32_t window_left, int32_t window_right, int32_t align,
+                             const int32_t* key_lens, int32_t dtype, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+    return backward_impl(q, k, v, out, dout, lse, dq, dk, dv, B, h, n, m, d_k, d_v, scale, window_left,
+                         window_right, align, key_lens, nullptr, 1.f, dtype, workspace, workspace_bytes,
+                         stream);
+}
+
+extern "C" int sdpa_forward_dropout(const void* q, const void* k, const void* v, void* out, float* lse,
+                                    int32_t B, int32_t h, int32_t n, int32_t m, int32_t d_k, int32_t d_v,
+                                    float scale, int32_t window_left, int32_t window_right, int32_t align,
+                                    const int32_t* key_lens, const uint32_t* keep_mask, float keep_scale,
+                                    int32_t dtype, void* stream) {
+    int st = validate(q, k, v, out, B, h, n, m, d_k, d_v, scale, key_lens, dtype);
+    if (st != SDPA_OK) return st;
+    if ((st = validate_dropout(keep_mask, keep_scale, d_k, d_v, dtype)) != SDPA_OK) return st;
+    if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return SDPA_ERR_ALIGN;
+    int32_t wl, wr, br;
+    st = window_args(n, m, window_left, window_right, align, &wl, &wr, &br);
+    if (st != SDPA_OK) return st;
+    const uint64_t heads = (uint64_t)B * h;
+    const uint64_t ob = heads * n * d_v * 2, lb = heads * n * 4, kb = keep_bytes(B, h, n, m);
+    if (overlap(out, ob, keep_mask, kb)) return SDPA_ERR_ALIAS;
+    if (lse) {
+        const struct { const void* p; uint64_t n; } bufs[] = {
+            {q, heads * n * d_k * 2}, {k, heads * m * d_k * 2}, {v, heads * m * d_v * 2},
+            {out, ob}, {key_lens, key_lens ? (uint64_t)B * 4 : 0}, {keep_mask, kb}};
+        for (const auto& b : bufs)
+            if (b.p && overlap(lse, lb, b.p, b.n)) return SDPA_ERR_ALIAS;
+    }
+    sdpa::Args a{q, k, v, out, B, h, n, m, scale, wl, wr, br, key_lens};
+    a.lse = lse;
+    a.d = d_k;
+    a.dv = d_v;
+    a.keep = keep_mask;
+    a.keep_scale = keep_scale;
+    return launch(a, dtype, stream);
+}
+
+extern "C" int sdpa_backward_dropout(const void* q, const void* k, const void* v, const void* out,
+                                     const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                                     int32_t B, int32_t h, int32_t n, int32_t m, int32_t d_k, int32_t d_v,
+                                     float scale, int32_t window_left, int32_t window_right, int32_t align,
+                                     const int32_t* key_lens, const uint32_t* keep_mask, float keep_scale,
+                                     int32_t dtype, void* workspace, size_t workspace_bytes, void* stream) {
+    if (dtype != SDPA_F32 && dtype != SDPA_BF16) return SDPA_ERR_DTYPE;
+    const int st = validate_dropout(keep_mask, keep_scale, d_k, d_v, dtype);
+    if (st != SDPA_OK) return st;
+    return backward_impl(q, k, v, out, dout, lse, dq, dk, dv, B, h, n, m, d_k, d_v, scale, window_left,
+                         window_right, align, key_lens, keep_mask, keep_scale, dtype, workspace,
+                         workspace_bytes, stream);
 }
 
 extern "C" size_t sdpa_mha_workspace_bytes(int32_t B, int32_t n, int32_t m, int32_t h, int32_t d_k,
@@ -497,8 +573,8 @@ extern "C" const char* sdpa_strerror(int status) {
             return "bad mask: unknown mask_kind, causal with n != m, window side < -1 or unknown align";
         case SDPA_ERR_DTYPE: return "unknown dtype (SDPA_F32 = 0, SDPA_BF16 = 1)";
         case SDPA_ERR_LAUNCH: return "the HIP runtime refused the kernel launch";
-        case SDPA_ERR_SCALE: return "scale must be finite and > 0";
-        case SDPA_ERR_ALIAS: return "out overlaps an input (or, for the sublayer, the workspace)";
+        case SDPA_ERR_SCALE: return "scale (and keep_scale) must be finite and > 0";
+        case SDPA_ERR_ALIAS: return "an output overlaps an input, the keep mask or another output";
         case SDPA_ERR_WORKSPACE: return "workspace smaller than its *_workspace_bytes size";
         case SDPA_ERR_SCRATCH:
             return "the call needs more split-key scratch than the library's static "

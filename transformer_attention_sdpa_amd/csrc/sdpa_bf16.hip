@@ -61,7 +61,9 @@ constexpr int TILE_BYTES = BN * D * 2;  // 8 KiB
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 // STRIDED: K/V row strides from the caller's layout; else the packed D.
-template <int NW, bool STRIDED>
+// DROP: attention dropout with a keep-bit mask (weights of dropped pairs leave
+// the P·V product, not the row sums; the output is scaled by keep_scale).
+template <int NW, bool STRIDED, bool DROP>
 struct LongKernel {
     static constexpr int NT = NW * 64;
     static constexpr int BM = NW * QW;
@@ -90,6 +92,9 @@ struct LongKernel {
     // [flo, fhi) is legal for every query of the wave.
     int wlo, whi, flo, fhi;
     float c_log2;
+    // Dropout: this lane's keep-bit rows (one per sub-block) and their words.
+    const uint32_t* krow[QT];
+    int kwords;
 
     __device__ void issue_tile_load(int t, int buf) {
         const int k0 = t * BN;
@@ -152,6 +157,17 @@ struct LongKernel {
     __device__ void compute_tile(int k0) {
         const char* sk = lds + BUF * 2 * TILE_BYTES;
         const char* sv = sk + TILE_BYTES;
+        // Dropout: the keep words of keys k0..k0+31 and k0+32..k0+63 of this
+        // lane's queries, requested before the products so they arrive in time.
+        uint32_t kw[QT][2];
+        if constexpr (DROP) {
+            const int w0 = k0 >> 5;
+#pragma unroll
+            for (int qt = 0; qt < QT; ++qt) {
+                kw[qt][0] = w0 < kwords ? krow[qt][w0] : 0u;
+                kw[qt][1] = w0 + 1 < kwords ? krow[qt][w0 + 1] : 0u;
+            }
+        }
 
         // Sᵀ = K · Qᵀ over d = 64 (four k-steps of 16).
         f32x16 s[QT][2];
@@ -220,6 +236,18 @@ struct LongKernel {
         }
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) lsum[qt] += lt[qt];
+        // Dropout: zero the dropped weights of k-step j (keys 16·j + 4·hf +
+        // [0..3] and + 8, bits of word j/2 from 16·(j%2) + 4·hf) after the row
+        // sums have counted them.
+        if constexpr (DROP) {
+#pragma unroll
+            for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t wd = kw[qt][j >> 1] >> (16 * (j & 1) + 4 * hf);
+                    pb[qt][j] = keep_pairs(pb[qt][j], (wd & 0xFu) | ((wd >> 4) & 0xF0u));
+                }
+        }
 
         // Oᵀ += Vᵀ · Pᵀ.  The Vᵀ operand lists the same keys as Pᵀ: two LDS
         // transpose reads, each giving 4 consecutive keys (rows 16·j + 4·hf +
@@ -254,13 +282,14 @@ struct LongKernel {
     }
 };
 
-template <int NW, bool STRIDED>
+template <int NW, bool STRIDED, bool DROP>
 __global__ __launch_bounds__(NW * 64) void sdpa_long_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
     int BH, int H, int n, int m, float c_log2, int wl, int wr, int bottom_right,
-    const int32_t* __restrict__ key_lens, int nqb, float* __restrict__ lse, Layout lay) {
-    using KT = LongKernel<NW, STRIDED>;
+    const int32_t* __restrict__ key_lens, int nqb, float* __restrict__ lse, Layout lay,
+    const uint32_t* __restrict__ keep, float keep_scale) {
+    using KT = LongKernel<NW, STRIDED, DROP>;
     __shared__ __attribute__((aligned(16))) char lds[2 * 2 * TILE_BYTES];
     KT k;
     k.lds = lds;
@@ -358,6 +387,12 @@ __global__ __launch_bounds__(NW * 64) void sdpa_long_bf16(
         for (int i = 0; i < 16; ++i) { k.oacc[qt][0][i] = 0.f; k.oacc[qt][1][i] = 0.f; }
         k.mref[qt] = -INFINITY;
         k.lsum[qt] = 0.f;
+        if constexpr (DROP) {
+            // rows past n read row n − 1 (their outputs are not stored)
+            const int qrow = min(k.wq0 + 32 * qt + k.l32, n - 1);
+            k.kwords = (m + 31) >> 5;
+            k.krow[qt] = keep + ((size_t)bh * n + qrow) * k.kwords;
+        }
     }
 
     if (tend > tbeg) {
@@ -379,7 +414,7 @@ __global__ __launch_bounds__(NW * 64) void sdpa_long_bf16(
         const int qrow = k.wq0 + 32 * qt + k.l32;
         const float ltot = half_swap_sum(k.lsum[qt]);
         // no legal key ⇒ zero row; a NaN sum (NaN legal inputs) stays NaN
-        const float inv = ltot != 0.f ? 1.f / ltot : 0.f;
+        const float inv = ltot != 0.f ? (DROP ? keep_scale : 1.f) / ltot : 0.f;
         // ln Σ e^(scale·s) = scale·mref + ln l, with the reference the weights
         // were formed against: −∞ for a row with no legal key
         if (lse && k.hf == 0 && qrow < n) {
@@ -409,11 +444,12 @@ hipError_t launch_long(const Args& a, hipStream_t stream) {
     const int BH = a.B * a.H;
     const float c_log2 = (float)((double)a.scale * 1.4426950408889634);  // scale·log2(e)
     const int nqb = (a.n + NW * QW - 1) / (NW * QW);
-    const auto kernel = a.strided ? sdpa_long_bf16<NW, true> : sdpa_long_bf16<NW, false>;
+    const auto kernel = a.keep ? (a.strided ? sdpa_long_bf16<NW, true, true> : sdpa_long_bf16<NW, false, true>)
+                               : (a.strided ? sdpa_long_bf16<NW, true, false> : sdpa_long_bf16<NW, false, false>);
     hipLaunchKernelGGL(kernel, dim3(nqb * BH), dim3(NW * 64), 0, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (uint16_t*)a.out, BH, a.H, a.n, a.m, c_log2, a.wl, a.wr, a.bottom_right,
-                       a.key_lens, nqb, a.lse, a.lay);
+                       a.key_lens, nqb, a.lse, a.lay, a.keep, a.keep_scale);
     return hipGetLastError();
 }
 
@@ -435,6 +471,7 @@ hipError_t launch_bf16_long(const Args& a, hipStream_t stream) {
 hipError_t launch_bf16(const Args& a0, hipStream_t stream) {
     Args a = a0;
     if (!a.strided) a.lay = dense_layout(a.H, a.n, a.m, a.d, a.dv);  // packed layout
+    if (a.keep) return launch_bf16_long(a, stream);  // attention dropout: d_k = d_v = 64, any n, m
     if (short_bf16_fits(a)) return launch_bf16_short(a, stream);  // n, m <= 64, d_k = d_v ∈ {32, 64, 128}
     if (a.d != D || a.dv != D) return launch_bf16_width(a, stream);
     if (decode_bf16_fits(a)) return launch_bf16_decode(a, stream);

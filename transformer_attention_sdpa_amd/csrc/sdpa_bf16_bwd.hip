@@ -251,13 +251,15 @@ __device__ __forceinline__ void load_tile(char* lds_tile, const uint16_t* base, 
 // ---------------------------------------------------------------------------
 // Launch 1: dQ (and D, lse·log2 e for launch 2).
 
-template <int D, int NW>
+// DROP: attention dropout of the forward pass with keep-bit words [BH, n, ⌈m/32⌉]:
+// dP = (dO Vᵀ) ∘ Z · keep_scale.
+template <int D, int NW, bool DROP>
 __global__ __launch_bounds__(NW * 64) void sdpa_bwd_dq_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO, const float* __restrict__ lse,
     uint16_t* __restrict__ dQ, float* __restrict__ ws_d, float* __restrict__ ws_l,
     int BH, int H, int n, int m, float scale, float c_log2, int wl, int wr, int bottom_right,
-    const int32_t* __restrict__ key_lens, int nqb) {
+    const int32_t* __restrict__ key_lens, int nqb, const uint32_t* __restrict__ keep, float keep_scale) {
     constexpr int TB = tile_bytes<D>(), KS = D / 16, DT = D / 32;
     __shared__ __attribute__((aligned(1024))) char lds[2 * 2 * TB];  // [buf][K | V]
     const int tid = threadIdx.x;
@@ -312,6 +314,11 @@ __global__ __launch_bounds__(NW * 64) void sdpa_bwd_dq_bf16(
         ws_l[(size_t)bh * n + qrow] = lc;
     }
 
+    // Dropout: this lane's row of keep words (rows past n read row n − 1; their
+    // dQ is not stored).
+    const int kwords = (m + 31) >> 5;
+    const uint32_t* krow = DROP ? keep + ((size_t)bh * n + min(qrow, n - 1)) * kwords : nullptr;
+
     TileAddr<D> ta;
     ta.init(lane);
     const uint32_t l0 = lds_u32(lds);
@@ -334,6 +341,12 @@ __global__ __launch_bounds__(NW * 64) void sdpa_bwd_dq_bf16(
         const int k0 = t * BT;
         if (k0 < whi && k0 + BT > wlo) {  // uniform: some query of the wave sees the tile
             const uint32_t sk = l0 + buf * 2 * TB, sv = sk + TB;
+            uint32_t kw[2] = {0u, 0u};  // keep words of keys k0.. and k0 + 32..
+            if constexpr (DROP) {
+                const int w0 = k0 >> 5;
+                kw[0] = w0 < kwords ? krow[w0] : 0u;
+                kw[1] = w0 + 1 < kwords ? krow[w0 + 1] : 0u;
+            }
             f32x16 s[2], dp[2];
             row_products<D, true>(sk, sv, ta, qop, dop, s, dp);
             // Register i of s[kt] is key k0 + 32·kt + 8·(i/4) + 4·hf + i%4.
@@ -352,7 +365,10 @@ __global__ __launch_bounds__(NW * 64) void sdpa_bwd_dq_bf16(
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const float p = exp2_hw(__builtin_fmaf(s[kt][i], c_log2, -lc));
-                    s[kt][i] = p * (dp[kt][i] - dsum);  // dSᵀ
+                    float g = dp[kt][i];
+                    if constexpr (DROP)
+                        g = (kw[kt] >> (8 * (i >> 2) + 4 * hf + (i & 3))) & 1u ? g * keep_scale : 0.f;
+                    s[kt][i] = p * (g - dsum);  // dSᵀ
                 }
             bf16x8 db[4];
 #pragma unroll
@@ -388,16 +404,18 @@ struct QueryRange {
 
 // DV, DK: which gradients this launch forms (both, for D <= 64; at D = 128 one
 // launch each keeps the accumulators within the register file).
-template <int D, int NW, bool DV, bool DK>
+// DROP: attention dropout as in the dQ kernel; dVᵀ += dOᵀ (P ∘ Z · keep_scale).
+template <int D, int NW, bool DV, bool DK, bool DROP>
 __global__ __launch_bounds__(NW * 64) void sdpa_bwd_dkdv_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ ws_d, const float* __restrict__ ws_l,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
     int BH, int H, int n, int m, float scale, float c_log2, int wl, int wr, int bottom_right,
-    const int32_t* __restrict__ key_lens) {
-    // [buf][Q tile | dO tile | lse·log2 e (64 floats) | D (64 floats)]
+    const int32_t* __restrict__ key_lens, const uint32_t* __restrict__ keep, float keep_scale) {
+    // [buf][Q tile | dO tile | lse·log2 e (64 floats) | D (64 floats) | with
+    // DROP, per wave the keep words of its 32 keys for the tile's 64 queries]
     constexpr int TB = tile_bytes<D>(), KS = D / 16, DT = D / 32;
-    constexpr int STAGE = 2 * TB + 512;
+    constexpr int STAGE = 2 * TB + 512 + (DROP ? NW * 256 : 0);
     __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE];
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -430,6 +448,7 @@ __global__ __launch_bounds__(NW * 64) void sdpa_bwd_dkdv_bf16(
     const int fqa = wfull ? qr.qa(wlast) : 0, fqb = wfull ? qr.qb(wk0) : 0;
 
     const size_t qbase = (size_t)bh * n * D, kvbase = (size_t)bh * m * D;
+    const int kwords = (m + 31) >> 5;
     const int key = wk0 + l32;
     // Kᵀ, Vᵀ as B operands; keys at or past L are zeros (their rows may hold
     // anything), so their logits are masked and their dS is exactly 0.
@@ -463,6 +482,15 @@ __global__ __launch_bounds__(NW * 64) void sdpa_bwd_dkdv_bf16(
                                       lane * 4, 0, 0, 0);
             sdpa_llvm_buffer_load_lds(rd, (__attribute__((address_space(3))) void*)(st + 2 * TB + 256),
                                       4, lane * 4, 0, 0, 0);
+        }
+        if constexpr (DROP) {  // word wk0/32 of query rows t·BT + lane, zeros past n
+            // (a wave whose keys start at or past m has no word: nothing is read)
+            const int left = n - t * BT;
+            const uint32_t nb = left > 0 && wk0 < m ? (uint32_t)(((left < BT ? left : BT) - 1) * kwords + 1) * 4u
+                                                    : 0u;
+            const i32x4 rk = make_rsrc(keep + ((size_t)bh * n + t * BT) * kwords + (wk0 < m ? wk0 >> 5 : 0), nb);
+            sdpa_llvm_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(st + 2 * TB + 512 + w * 256),
+                                      4, lane * kwords * 4, 0, 0, 0);
         }
     };
     if (tend > tbeg) issue(tbeg, 0);
@@ -509,16 +537,41 @@ __global__ __launch_bounds__(NW * 64) void sdpa_bwd_dkdv_bf16(
                     }
                 lds_wait(dv4);
             }
+            // Dropout: the keep words of those queries for this wave's keys;
+            // bit i of zb[qh] is bit l32 (this lane's key) of register i's query.
+            uint32_t zb[2] = {0u, 0u};
+            if constexpr (DROP) {
+                u32x4 kq[8];
+#pragma unroll
+                for (int qh = 0; qh < 2; ++qh)
+#pragma unroll
+                    for (int gq = 0; gq < 4; ++gq) {
+                        const uint32_t off = (uint32_t)(32 * qh + 8 * gq + 4 * hf) * 4u;
+                        kq[4 * qh + gq] = ds_read_b128(sq + 2 * TB + 512 + w * 256 + off);
+                    }
+                lds_wait(kq);
+#pragma unroll
+                for (int qh = 0; qh < 2; ++qh)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) zb[qh] |= ((kq[4 * qh + (i >> 2)][i & 3] >> l32) & 1u) << i;
+            }
 #pragma unroll
             for (int qh = 0; qh < 2; ++qh)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const float lc = __uint_as_float(lv[4 * qh + (i >> 2)][i & 3]);
                     const float p = exp2_hw(__builtin_fmaf(s[qh][i], c_log2, -lc));
-                    s[qh][i] = p;
+                    float pd = p;  // the weight that multiplied the value (P ∘ Z · c)
+                    float g = DK ? dp[qh][i] : 0.f;
+                    if constexpr (DROP) {
+                        const bool z = (zb[qh] >> i) & 1u;
+                        pd = z ? p * keep_scale : 0.f;
+                        g = z ? g * keep_scale : 0.f;
+                    }
+                    s[qh][i] = pd;
                     if constexpr (DK) {
                         const float dd = __uint_as_float(dv4[4 * qh + (i >> 2)][i & 3]);
-                        dp[qh][i] = p * (dp[qh][i] - dd);  // dS
+                        dp[qh][i] = p * (g - dd);  // dS
                     }
                 }
             if constexpr (DV) {
@@ -720,34 +773,34 @@ size_t bwd_workspace_bytes(int B, int H, int n) { return 2 * (((size_t)B * H * n
 
 namespace {
 
-template <int D, int NW>
+template <int D, int NW, bool DROP>
 hipError_t launch_bwd_width(const BwdArgs& a, hipStream_t stream, float c_log2, float* ws_d, float* ws_l) {
     const int BH = a.B * a.H;
     const int nqb = (a.n + 32 * NW - 1) / (32 * NW);
-    hipLaunchKernelGGL((sdpa_bwd_dq_bf16<D, NW>), dim3(nqb * BH), dim3(NW * 64), 0, stream,
+    hipLaunchKernelGGL((sdpa_bwd_dq_bf16<D, NW, DROP>), dim3(nqb * BH), dim3(NW * 64), 0, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (const uint16_t*)a.out, (const uint16_t*)a.dout, a.lse, (uint16_t*)a.dq,
                        ws_d, ws_l, BH, a.H, a.n, a.m, a.scale, c_log2, a.wl, a.wr, a.bottom_right,
-                       a.key_lens, nqb);
+                       a.key_lens, nqb, a.keep, a.keep_scale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const dim3 grid(((a.m + 32 * NW - 1) / (32 * NW)) * BH);
-    if constexpr (D <= 64) {
-        hipLaunchKernelGGL((sdpa_bwd_dkdv_bf16<D, NW, true, true>), grid, dim3(NW * 64), 0, stream,
-                           (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                           (const uint16_t*)a.dout, ws_d, ws_l, (uint16_t*)a.dk, (uint16_t*)a.dv, BH, a.H,
-                           a.n, a.m, a.scale, c_log2, a.wl, a.wr, a.bottom_right, a.key_lens);
-    } else {
-        hipLaunchKernelGGL((sdpa_bwd_dkdv_bf16<D, NW, true, false>), grid, dim3(NW * 64), 0, stream,
-                           (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                           (const uint16_t*)a.dout, ws_d, ws_l, (uint16_t*)a.dk, (uint16_t*)a.dv, BH, a.H,
-                           a.n, a.m, a.scale, c_log2, a.wl, a.wr, a.bottom_right, a.key_lens);
+    // Both gradients in one launch for D <= 64; at D = 128 one launch each
+    // keeps the accumulators within the register file.
+    constexpr bool ONE = D <= 64;
+    hipLaunchKernelGGL((sdpa_bwd_dkdv_bf16<D, NW, true, ONE, DROP>), grid, dim3(NW * 64), 0, stream,
+                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                       (const uint16_t*)a.dout, ws_d, ws_l, (uint16_t*)a.dk, (uint16_t*)a.dv, BH, a.H,
+                       a.n, a.m, a.scale, c_log2, a.wl, a.wr, a.bottom_right, a.key_lens, a.keep,
+                       a.keep_scale);
+    if constexpr (!ONE) {
         e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((sdpa_bwd_dkdv_bf16<D, NW, false, true>), grid, dim3(NW * 64), 0, stream,
+        hipLaunchKernelGGL((sdpa_bwd_dkdv_bf16<D, NW, false, true, DROP>), grid, dim3(NW * 64), 0, stream,
                            (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                            (const uint16_t*)a.dout, ws_d, ws_l, (uint16_t*)a.dk, (uint16_t*)a.dv, BH, a.H,
-                           a.n, a.m, a.scale, c_log2, a.wl, a.wr, a.bottom_right, a.key_lens);
+                           a.n, a.m, a.scale, c_log2, a.wl, a.wr, a.bottom_right, a.key_lens, a.keep,
+                           a.keep_scale);
     }
     return hipGetLastError();
 }
@@ -755,8 +808,12 @@ hipError_t launch_bwd_width(const BwdArgs& a, hipStream_t stream, float c_log2, 
 template <int D>
 hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream, float c_log2, float* ws_d, float* ws_l) {
     // 4 waves per workgroup once there are enough query blocks to fill the chip.
-    if ((long long)a.B * a.H * ((a.n + 127) / 128) >= 1024) return launch_bwd_width<D, 4>(a, stream, c_log2, ws_d, ws_l);
-    return launch_bwd_width<D, 2>(a, stream, c_log2, ws_d, ws_l);
+    const bool four = (long long)a.B * a.H * ((a.n + 127) / 128) >= 1024;
+    if (a.keep)
+        return four ? launch_bwd_width<D, 4, true>(a, stream, c_log2, ws_d, ws_l)
+                    : launch_bwd_width<D, 2, true>(a, stream, c_log2, ws_d, ws_l);
+    return four ? launch_bwd_width<D, 4, false>(a, stream, c_log2, ws_d, ws_l)
+                : launch_bwd_width<D, 2, false>(a, stream, c_log2, ws_d, ws_l);
 }
 
 }  // namespace
@@ -766,7 +823,7 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
     const float c_log2 = (float)((double)a.scale * 1.4426950408889634);  // scale·log2(e)
     float* ws_d = static_cast<float*>(a.workspace);
     float* ws_l = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + bwd_workspace_bytes(a.B, a.H, a.n) / 2);
-    if (a.d == kHeadDim && a.n <= 64 && a.m <= 64) {
+    if (a.d == kHeadDim && a.n <= 64 && a.m <= 64 && !a.keep) {
         hipLaunchKernelGGL(sdpa_bwd_short_bf16, dim3(BH), dim3(256), 0, stream, (const uint16_t*)a.q,
                            (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.out,
                            (const uint16_t*)a.dout, a.lse, (uint16_t*)a.dq, (uint16_t*)a.dk,

@@ -73,6 +73,10 @@ struct Args {
     // Optional workspace for split-key decoder steps (decode_split_bytes), or nullptr.
     void* work = nullptr;
     size_t work_bytes = 0;
+    // Attention dropout: keep-bit words [B, H, n, ⌈m/32⌉] (bit j mod 32 of word
+    // ⌊j/32⌋ keeps weight (i, j)) and the factor of the kept weights, or nullptr.
+    const uint32_t* keep = nullptr;
+    float keep_scale = 1.f;
     // Element strides of q, k, v and out (dense_layout for the plain entry points).
     Layout lay{};
     // True when `lay` came from the caller (sdpa_forward_strided): the
@@ -141,6 +145,9 @@ struct BwdArgs {
     int wl, wr, bottom_right;
     const int32_t* key_lens;
     int d = kHeadDim;  // head width d_k = d_v: 32, 64 or 128
+    // Attention dropout of the forward pass (as in Args), or nullptr.
+    const uint32_t* keep = nullptr;
+    float keep_scale = 1.f;
 };
 size_t bwd_workspace_bytes(int B, int H, int n);
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream);
@@ -247,6 +254,19 @@ __device__ __forceinline__ void load16_to_lds_nt(i32x4 rsrc, void* lds, int voff
 __device__ __forceinline__ void store16_nt(void* p, u32x4 x) {
     __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(p));
 }
+// Keep-bit helpers of attention dropout.  keep_pairs zeroes the elements of
+// eight packed bf16 values whose bit in `bits` (bit e for element e) is 0.
+__device__ __forceinline__ uint32_t keep_pair_mask(uint32_t bits, int e) {
+    const uint32_t lo = 0u - ((bits >> e) & 1u), hi = 0u - ((bits >> (e + 1)) & 1u);
+    return (lo & 0xFFFFu) | (hi & 0xFFFF0000u);
+}
+__device__ __forceinline__ bf16x8 keep_pairs(bf16x8 v, uint32_t bits) {
+    u32x4 w = __builtin_bit_cast(u32x4, v);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] &= keep_pair_mask(bits, 2 * e);
+    return __builtin_bit_cast(bf16x8, w);
+}
+
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Workgroup barrier without the release fence of __syncthreads (which waits
