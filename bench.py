@@ -46,7 +46,7 @@ EXTRA = [("single_head_16", "f32"), ("encoder_self_base", "f32"), ("decoder_caus
          ("cross_big", "bf16"), ("long_causal_8k", "bf16"), ("local_window_8k", "bf16"),
          ("decode_beam_base", "bf16"), ("decode_long_cache", "bf16"), ("encoder_h16_d32", "bf16"),
          ("encoder_h4_d128", "bf16"), ("long_causal_8k_d128", "bf16"), ("encoder_h32_d16", "bf16"),
-         ("encoder_dk16_dv64", "bf16"), ("encoder_dk32_dv64", "bf16")]
+         ("encoder_dk16_dv64", "bf16"), ("encoder_dk32_dv64", "bf16"), ("encoder_h1_d512", "bf16")]
 
 
 def algorithmic_work(wl, dtype, key_lens):

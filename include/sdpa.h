@@ -78,7 +78,7 @@ extern "C" {
  *          (n·d·size and m·d·size; the kernels use 32-bit offsets within a
  *          head), else SDPA_ERR_SHAPE.
  * d_k, d_v query/key and value widths: d_k == d_v == 64 for both dtypes; for
- *          SDPA_BF16 also d_k == d_v == 16, 32 or 128, and d_v == 64 with
+ *          SDPA_BF16 also d_k == d_v == 16, 32, 128 or 512, and d_v == 64 with
  *          d_k == 16 or 32 (the model variants of 《精读 Attention Is All
  *          You Need：原始 Transformer 论文》 Table 3, rows (A), (B) and (C)).
  *          Other pairs: SDPA_ERR_UNSUPPORTED.

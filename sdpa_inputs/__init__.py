@@ -87,14 +87,17 @@ WORKLOADS = {
     "encoder_h4_d128": Workload(
         "encoder_h4_d128", B=64, h=4, n=64, m=64, d_k=128, d_v=128, causal=False,
         key_len_range=(8, 64), seed=1010),
-    # Row (A)'s 32 heads of 16 and row (B)'s narrow keys (d_k = 16 or 32
-    # against d_v = 64), encoder batch as above.
+    # Row (A)'s 32 heads of 16 and single head of 512, and row (B)'s narrow
+    # keys (d_k = 16 or 32 against d_v = 64), encoder batch as above.
     "encoder_h32_d16": Workload(
         "encoder_h32_d16", B=64, h=32, n=64, m=64, d_k=16, d_v=16, causal=False,
         key_len_range=(8, 64), seed=1013, dtypes=("bf16",)),
     "encoder_dk16_dv64": Workload(
         "encoder_dk16_dv64", B=64, h=8, n=64, m=64, d_k=16, d_v=64, causal=False,
         key_len_range=(8, 64), seed=1014, dtypes=("bf16",)),
+    "encoder_h1_d512": Workload(
+        "encoder_h1_d512", B=64, h=1, n=64, m=64, d_k=512, d_v=512, causal=False,
+        key_len_range=(8, 64), seed=1016, dtypes=("bf16",)),
     "encoder_dk32_dv64": Workload(
         "encoder_dk32_dv64", B=64, h=8, n=64, m=64, d_k=32, d_v=64, causal=False,
         key_len_range=(8, 64), seed=1015, dtypes=("bf16",)),

@@ -79,7 +79,8 @@ def call(q=P, k=2 * P, v=3 * P, out=4 * P, B=2, h=2, n=8, m=8, d_k=64, d_v=64, s
     (dict(d_k=16, d_v=64, dtype=0), _lib.SDPA_ERR_UNSUPPORTED),
     (dict(d_k=8, d_v=8), _lib.SDPA_ERR_UNSUPPORTED),
     (dict(d_k=96, d_v=96), _lib.SDPA_ERR_UNSUPPORTED),
-    (dict(d_k=512, d_v=512), _lib.SDPA_ERR_UNSUPPORTED),
+    (dict(d_k=256, d_v=256), _lib.SDPA_ERR_UNSUPPORTED),
+    (dict(d_k=512, d_v=64), _lib.SDPA_ERR_UNSUPPORTED),
     (dict(d_k=16, d_v=32), _lib.SDPA_ERR_UNSUPPORTED),            # d_k != d_v: only d_v = 64
     (dict(d_k=128, d_v=64), _lib.SDPA_ERR_UNSUPPORTED),           # ... with d_k = 16 or 32
     (dict(d_k=64, d_v=16), _lib.SDPA_ERR_UNSUPPORTED),

@@ -2,11 +2,12 @@
 the fp64 oracle.
 
 《精读 Attention Is All You Need：原始 Transformer 论文》 Table 3 varies the
-head widths: row (A) runs 32 heads of d_k = d_v = 16, and row (B) keeps
+head widths: row (A) runs 32 heads of d_k = d_v = 16 and one of 512, and row (B) keeps
 d_v = 64 while it shrinks the key width d_k to 16 or 32.  Eq. (1) contracts
 queries with keys over d_k and weights with values over d_v, so the two
 widths are independent; the oracle takes any pair.  These widths run on the
-width kernel at every length.  Bar: the bf16 one, 2e-2 absolute; the
+width kernel at every length, and row (A)'s single head of 512 on a kernel
+of its own.  Bar: the bf16 one, 2e-2 absolute; the
 log-sum-exp within 2^-8.
 """
 
@@ -38,6 +39,15 @@ CASES = [  # id, (B, h, n, m, d_k, d_v), options
     ("dk32_dv64_one_by_one", (2, 1, 1, 1, 32, 64), dict(key_lens=(0, 1))),
     ("d16_four_wave_blocks", (8, 16, 1024, 1024, 16, 16), dict(causal=True)),
     ("dk32_dv64_four_wave_blocks", (8, 16, 1024, 1024, 32, 64), dict(causal=True)),
+    # row (A)'s single head of 512
+    ("A_h1_d512_encoder", (64, 1, 64, 64, 512, 512), dict(key_lens=(8, 64))),
+    ("A_d512_decoder", (16, 1, 64, 64, 512, 512), dict(causal=True, key_lens=(8, 64))),
+    ("d512_cross", (8, 1, 48, 64, 512, 512), dict(key_lens=(16, 64))),
+    ("d512_multi_tile_causal", (2, 2, 300, 300, 512, 512), dict(causal=True)),
+    ("d512_window_ragged", (2, 2, 260, 260, 512, 512), dict(window=(40, 8), key_lens=(100, 260))),
+    ("d512_bottom_right", (4, 2, 5, 200, 512, 512), dict(window=(None, 0, "bottom_right"), key_lens=(0, 200))),
+    ("d512_ragged", (2, 3, 33, 17, 512, 512), dict(key_lens=(0, 20))),
+    ("d512_one_by_one", (1, 1, 1, 1, 512, 512), {}),
 ]
 
 
@@ -75,7 +85,10 @@ def test_table3_width_parity(gpu_lib, i):
     assert err <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("i", [0, 1, 5, 9], ids=[CASES[i][0] for i in (0, 1, 5, 9)])
+LSE_CASES = [0, 1, 5, 9, 17, 20, 22]
+
+
+@pytest.mark.parametrize("i", LSE_CASES, ids=[CASES[i][0] for i in LSE_CASES])
 def test_table3_width_lse(gpu_lib, i):
     import torch
 
@@ -98,7 +111,7 @@ def test_table3_width_lse(gpu_lib, i):
     assert err <= 2.0 ** -8
 
 
-@pytest.mark.parametrize("dk,dv", [(16, 16), (16, 64), (32, 64)])
+@pytest.mark.parametrize("dk,dv", [(16, 16), (16, 64), (32, 64), (512, 512)])
 def test_table3_padded_keys_are_never_read(gpu_lib, dk, dv):
     """NaN and huge values in the K/V rows at or past each key length leave
     the output bitwise unchanged; a head with no legal key gives zero rows."""
@@ -118,16 +131,20 @@ def test_table3_padded_keys_are_never_read(gpu_lib, dk, dv):
     assert np.all(a[2] == 0)
 
 
-def test_table3_masked_weights_are_exactly_zero(gpu_lib):
-    """d_k = 16 against d_v = m = 64: V = I makes the output the weight matrix
-    itself, and every masked weight must be +0.0 (causal and key padding)."""
-    rng = np.random.default_rng(96)
+@pytest.mark.parametrize("dk,dv", [(16, 64), (512, 512)])
+def test_table3_masked_weights_are_exactly_zero(gpu_lib, dk, dv):
+    """m = 64 keys and d_v ≥ m: V = [I | 0] makes the output's first m columns
+    the weight matrix itself, and every masked weight must be +0.0 (causal
+    and key padding)."""
+    rng = np.random.default_rng(96 + dk)
     B, h, n, m = 4, 2, 64, 64
     kl = np.array([64, 17, 1, 40], np.int32)
-    c = random_case(rng, B, h, n, m, 16, 64, dtype="bf16", causal=True, key_lens=kl)
+    c = random_case(rng, B, h, n, m, dk, dv, dtype="bf16", causal=True, key_lens=kl)
     c["v"] = np.zeros_like(c["v"])
     c["v"][:, :, np.arange(m), np.arange(m)] = 1.0
     _, got = run_gpu(c)
+    assert np.all(got[..., m:] == 0.0)
+    got = got[..., :m]
     j = np.arange(m)
     for b in range(B):
         for i in range(n):
@@ -135,10 +152,11 @@ def test_table3_masked_weights_are_exactly_zero(gpu_lib):
             row = got[b, :, i]
             assert np.all(row[:, ~vis] == 0.0) and not np.signbit(row[:, ~vis]).any()
             assert np.allclose(row.sum(-1), 1.0, atol=4 * TOL["bf16"])
-    assert max_abs_err(got, so.attention(c["q"], c["k"], c["v"], causal=True, key_lens=kl)) <= TOL["bf16"]
+    ref = so.attention(c["q"], c["k"], c["v"], causal=True, key_lens=kl)[..., :m]
+    assert max_abs_err(got, ref) <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("dk,dv", [(16, 16), (16, 64), (32, 64)])
+@pytest.mark.parametrize("dk,dv", [(16, 16), (16, 64), (32, 64), (512, 512)])
 def test_table3_token_major_matches_packed_bitwise(gpu_lib, dk, dv):
     """Token-major [B, len, h, d] views of q, k, v and out through
     sdpa_forward_strided: bitwise equal to the packed call."""

@@ -44,7 +44,7 @@ int validate_core(const void* q, const void* k, const void* v, void* out, int32_
     const uint64_t esz = dtype == SDPA_F32 ? 4 : 2;
     if (rows * width * esz >= (1ull << 31)) return SDPA_ERR_SHAPE;
     // Head widths: 64 and 64 for both dtypes; for bf16 also the pairs of
-    // sdpa::width_supported (equal widths 16, 32, 128; d_v = 64 with d_k = 16 or 32).
+    // sdpa::width_supported (equal widths 16, 32, 128, 512; d_v = 64 with d_k = 16 or 32).
     const bool wide_ok = dtype == SDPA_BF16 && sdpa::width_supported(d_k, d_v);
     if (!(d_k == sdpa::kHeadDim && d_v == sdpa::kHeadDim) && !wide_ok) return SDPA_ERR_UNSUPPORTED;
     if (!std::isfinite(scale) || !(scale > 0.f)) return SDPA_ERR_SCALE;
@@ -566,8 +566,9 @@ extern "C" const char* sdpa_strerror(int status) {
         case SDPA_ERR_SHAPE: return "bad shape: a dimension is < 1 or an element count overflows";
         case SDPA_ERR_UNSUPPORTED:
             return "unsupported: head widths are d_k = d_v = 64; bf16 attention also takes d_k = d_v = "
-                   "16, 32, 128 and d_v = 64 with d_k = 16 or 32; the log-sum-exp, backward pass and "
-                   "sublayer are bf16, with d_k = d_v = 32, 64 or 128 (backward, sublayer)";
+                   "16, 32, 128, 512 and d_v = 64 with d_k = 16 or 32; the log-sum-exp, backward pass and "
+                   "sublayer are bf16, with d_k = d_v = 32, 64 or 128 (backward, sublayer); dropout is "
+                   "bf16 with d_k = d_v = 64";
         case SDPA_ERR_ALIGN: return "a device pointer is not 16-byte aligned (key_lens: 4-byte)";
         case SDPA_ERR_MASK:
             return "bad mask: unknown mask_kind, causal with n != m, window side < -1 or unknown align";

@@ -326,7 +326,7 @@ hipError_t launch_width(const Args& a, hipStream_t stream) {
 }  // namespace
 
 bool width_supported(int d_k, int d_v) {
-    if (d_k == d_v) return d_k == 16 || d_k == 32 || d_k == 64 || d_k == 128;
+    if (d_k == d_v) return d_k == 16 || d_k == 32 || d_k == 64 || d_k == 128 || d_k == 512;
     return d_v == 64 && (d_k == 16 || d_k == 32);
 }
 
@@ -336,6 +336,7 @@ hipError_t launch_bf16_width(const Args& a, hipStream_t stream) {
     if (a.d == 128 && a.dv == 128) return launch_width<128, 128>(a, stream);
     if (a.d == 16 && a.dv == 64) return launch_width<16, 64>(a, stream);
     if (a.d == 32 && a.dv == 64) return launch_width<32, 64>(a, stream);
+    if (a.d == 512 && a.dv == 512) return launch_bf16_wide(a, stream);
     return hipErrorInvalidValue;
 }
 

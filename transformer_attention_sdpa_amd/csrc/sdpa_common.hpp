@@ -155,7 +155,8 @@ hipError_t launch_mha_bf16(const MhaArgs& a, hipStream_t stream);
 
 hipError_t launch_bf16(const Args& a, hipStream_t stream);        // picks one of the four below
 hipError_t launch_bf16_width(const Args& a, hipStream_t stream);  // widths other than 64/64
-// bf16 head widths (d_k, d_v): equal widths 16, 32, 64 or 128, or d_v = 64 with d_k = 16 or 32.
+hipError_t launch_bf16_wide(const Args& a, hipStream_t stream);   // d_k = d_v = 512
+// bf16 head widths (d_k, d_v): equal widths 16, 32, 64, 128 or 512, or d_v = 64 with d_k = 16 or 32.
 bool width_supported(int d_k, int d_v);
 hipError_t launch_bf16_long(const Args& a, hipStream_t stream);   // any n, m
 hipError_t launch_bf16_short(const Args& a, hipStream_t stream);  // n, m <= 64; d = 32, 64, 128
