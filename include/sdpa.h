@@ -196,7 +196,8 @@ SDPA_API int sdpa_mha_forward(const void* x_q, const void* x_kv, const void* w_q
  *
  * lse      device, float [B, h, n], contiguous, 4-byte aligned, written
  *          completely; must not overlap any other argument.
- * dtype    SDPA_BF16 (SDPA_F32: SDPA_ERR_UNSUPPORTED).
+ * dtype    SDPA_BF16 or SDPA_F32 (the fp32 kernels form it from their fp32
+ *          running sum, to a few fp32 ulps of |lse|).
  * Everything else as in sdpa_forward_window; `out` is bitwise the same as
  * sdpa_forward_window's.
  */
@@ -209,7 +210,7 @@ SDPA_API int sdpa_forward_lse(const void* q, const void* k, const void* v, void*
  * sdpa_forward_ex — sdpa_forward_window with an optional log-sum-exp output
  * and an optional workspace.
  *
- * lse        NULL, or as in sdpa_forward_lse (bf16 only).
+ * lse        NULL, or as in sdpa_forward_lse (either dtype).
  * workspace  NULL, or device scratch of workspace_bytes >= the size
  *            sdpa_forward_workspace_bytes gives, 16-byte aligned, owned by the
  *            caller, overlapping no other argument.  With it, decoder steps

@@ -194,7 +194,7 @@ def call_lse(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(lse=None), _lib.SDPA_ERR_NULL),
     (dict(q=None), _lib.SDPA_ERR_NULL),
-    (dict(dtype=0), _lib.SDPA_ERR_UNSUPPORTED),  # the log-sum-exp output is bf16 only
+    (dict(lse=4 * P + 6000, dtype=0), _lib.SDPA_ERR_ALIAS),  # inside out's fp32 span (8 KiB), past its bf16 one
     (dict(dtype=4), _lib.SDPA_ERR_DTYPE),
     (dict(lse=5 * P + 2), _lib.SDPA_ERR_ALIGN),
     (dict(wr=-2), _lib.SDPA_ERR_MASK),
@@ -246,7 +246,7 @@ def call_ex(**kw):
     (dict(ws_bytes=100), _lib.SDPA_ERR_WORKSPACE),
     (dict(ws=5 * G + 8), _lib.SDPA_ERR_ALIGN),
     (dict(ws=4 * G), _lib.SDPA_ERR_ALIAS),              # workspace on out
-    (dict(lse=6 * G, dtype=0), _lib.SDPA_ERR_UNSUPPORTED),
+    (dict(lse=4 * G + 40000, dtype=0), _lib.SDPA_ERR_ALIAS),  # inside out's fp32 span (64 KiB) only
     (dict(lse=6 * G + 1), _lib.SDPA_ERR_ALIGN),
     (dict(lse=G), _lib.SDPA_ERR_ALIAS),
     (dict(ws=6 * G, lse=6 * G + 64), _lib.SDPA_ERR_ALIAS),  # workspace on lse
@@ -270,7 +270,7 @@ def call_noalloc(**kw):
     (dict(q=None), _lib.SDPA_ERR_NULL),
     (dict(out=4 * G + 8), _lib.SDPA_ERR_ALIGN),
     (dict(out=G), _lib.SDPA_ERR_ALIAS),
-    (dict(lse=6 * G, dtype=0), _lib.SDPA_ERR_UNSUPPORTED),
+    (dict(lse=4 * G + 40000, dtype=0), _lib.SDPA_ERR_ALIAS),  # inside out's fp32 span (64 KiB) only
     (dict(lse=6 * G + 1), _lib.SDPA_ERR_ALIGN),
     (dict(lse=G), _lib.SDPA_ERR_ALIAS),
     (dict(wl=-4), _lib.SDPA_ERR_MASK),
@@ -335,7 +335,7 @@ BSHD = _bshd(2, 4, 48, 80, 64)
     (dict(strides=_with(BSHD, 11, 64)), _lib.SDPA_ERR_ALIAS),         # out rows on the heads' rows
     (dict(out=G + 64), _lib.SDPA_ERR_ALIAS),                          # out inside q's span
     (dict(lse=4 * G + 256), _lib.SDPA_ERR_ALIAS),                     # lse inside out's span
-    (dict(lse=6 * G, dtype=0), _lib.SDPA_ERR_UNSUPPORTED),
+    (dict(lse=4 * G + 60000, dtype=0), _lib.SDPA_ERR_ALIAS),          # inside out's fp32 span only
     (dict(wl=-3), _lib.SDPA_ERR_MASK),
     (dict(d_k=8, d_v=8), _lib.SDPA_ERR_UNSUPPORTED),
 ])

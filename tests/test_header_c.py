@@ -34,8 +34,8 @@ int main(void) {
           SDPA_ERR_UNSUPPORTED);
     CHECK(sdpa_forward_window(q, k, v, out, 2, 2, 8, 8, 64, 64, 0.125f, -2, 0, SDPA_ALIGN_TOP_LEFT, NULL,
                               SDPA_BF16, NULL), SDPA_ERR_MASK);
-    CHECK(sdpa_forward_lse(q, k, v, out, (float*)(base + (4 << 20)), 2, 2, 8, 8, 64, 64, 0.125f, -1, -1,
-                           SDPA_ALIGN_TOP_LEFT, NULL, SDPA_F32, NULL), SDPA_ERR_UNSUPPORTED);
+    CHECK(sdpa_forward_lse(q, k, v, out, (float*)(base + (4 << 20) + 2), 2, 2, 8, 8, 64, 64, 0.125f, -1, -1,
+                           SDPA_ALIGN_TOP_LEFT, NULL, SDPA_F32, NULL), SDPA_ERR_ALIGN);
     CHECK(sdpa_backward(q, k, v, out, base + (5 << 20), (const float*)(base + (6 << 20)), base + (7 << 20),
                         base + (8 << 20), base + (9 << 20), 2, 2, 8, 8, 64, 64, 0.125f, -1, -1,
                         SDPA_ALIGN_TOP_LEFT, NULL, SDPA_BF16, base + (10 << 20), 16, NULL), SDPA_ERR_WORKSPACE);

@@ -231,7 +231,7 @@ def forward(q, k, v, *, causal: bool = False, key_lens=None, scale: float | None
     "bottom_right" (L = the batch element's key length); see
     ``sdpa_forward_window`` in include/sdpa.h.  Not combined with ``causal``.
     Returns ``out`` ([B, h, n, d_v], same dtype as q), or ``(out, lse)`` with
-    ``return_lse`` (bf16 only): lse [B, h, n] float32, the natural log of each
+    ``return_lse`` (either dtype): lse [B, h, n] float32, the natural log of each
     row's softmax denominator, which ``backward`` takes.  ``workspace``: a
     uint8 GPU tensor of at least ``sdpa_forward_workspace_bytes(...)`` bytes,
     which lets decoder steps against long caches split each head's keys over

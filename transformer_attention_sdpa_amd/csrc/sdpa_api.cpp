@@ -148,16 +148,16 @@ extern "C" int sdpa_forward_lse(const void* q, const void* k, const void* v, voi
     int st = validate(q, k, v, out, B, h, n, m, d_k, d_v, scale, key_lens, dtype);
     if (st != SDPA_OK) return st;
     if (!lse) return SDPA_ERR_NULL;
-    if (dtype != SDPA_BF16) return SDPA_ERR_UNSUPPORTED;
     if (reinterpret_cast<uintptr_t>(lse) & 3u) return SDPA_ERR_ALIGN;
     int32_t wl, wr, br;
     st = window_args(n, m, window_left, window_right, align, &wl, &wr, &br);
     if (st != SDPA_OK) return st;
     const uint64_t heads = (uint64_t)B * h;
     const uint64_t lb = heads * n * 4;
+    const uint64_t esz = dtype == SDPA_F32 ? 4 : 2;
     const struct { const void* p; uint64_t n; } bufs[] = {
-        {q, heads * n * d_k * 2}, {k, heads * m * d_k * 2}, {v, heads * m * d_v * 2},
-        {out, heads * n * d_v * 2}, {key_lens, key_lens ? (uint64_t)B * 4 : 0}};
+        {q, heads * n * d_k * esz}, {k, heads * m * d_k * esz}, {v, heads * m * d_v * esz},
+        {out, heads * n * d_v * esz}, {key_lens, key_lens ? (uint64_t)B * 4 : 0}};
     for (const auto& b : bufs)
         if (b.p && overlap(lse, lb, b.p, b.n)) return SDPA_ERR_ALIAS;
     sdpa::Args a{q, k, v, out, B, h, n, m, scale, wl, wr, br, key_lens};
@@ -199,7 +199,6 @@ extern "C" int sdpa_forward_ex(const void* q, const void* k, const void* v, void
                        {out, heads * n * d_v * (dtype == SDPA_F32 ? 4 : 2)},
                        {key_lens, key_lens ? (uint64_t)B * 4 : 0}};
     if (lse) {
-        if (dtype != SDPA_BF16) return SDPA_ERR_UNSUPPORTED;
         if (reinterpret_cast<uintptr_t>(lse) & 3u) return SDPA_ERR_ALIGN;
         for (const Buf& b : ins)
             if (b.p && overlap(lse, heads * n * 4, b.p, b.n)) return SDPA_ERR_ALIAS;
@@ -468,7 +467,6 @@ extern "C" int sdpa_forward_strided(const void* q, const void* k, const void* v,
     for (const Buf& b : ins)
         if (b.p && overlap(out, os, b.p, b.n)) return SDPA_ERR_ALIAS;
     if (lse) {
-        if (dtype != SDPA_BF16) return SDPA_ERR_UNSUPPORTED;
         if (reinterpret_cast<uintptr_t>(lse) & 3u) return SDPA_ERR_ALIGN;
         for (const Buf& b : ins)
             if (b.p && overlap(lse, heads * n * 4, b.p, b.n)) return SDPA_ERR_ALIAS;
@@ -535,7 +533,6 @@ extern "C" int sdpa_forward_ex_noalloc(const void* q, const void* k, const void*
     st = window_args(n, m, window_left, window_right, align, &wl, &wr, &br);
     if (st != SDPA_OK) return st;
     if (lse) {
-        if (dtype != SDPA_BF16) return SDPA_ERR_UNSUPPORTED;
         if (reinterpret_cast<uintptr_t>(lse) & 3u) return SDPA_ERR_ALIGN;
         const uint64_t heads = (uint64_t)B * h, esz = dtype == SDPA_F32 ? 4 : 2;
         const struct { const void* p; uint64_t n; } ins[] = {

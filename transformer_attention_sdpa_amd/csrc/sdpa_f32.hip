@@ -34,7 +34,7 @@ template <int NW>
 __global__ __launch_bounds__(NW * 64) void sdpa_fwd_f32(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     float* __restrict__ O, int BH, int H, int n, int m, float c_log2, int wl, int wr,
-    int bottom_right, const int32_t* __restrict__ key_lens, int nqb, Layout lay) {
+    int bottom_right, const int32_t* __restrict__ key_lens, int nqb, float* __restrict__ lse, Layout lay) {
     constexpr int NT = NW * 64;
     constexpr int CHUNKS = BN * D * 4 / 16;  // 512
     constexpr int CPT = (CHUNKS + NT - 1) / NT;
@@ -241,6 +241,12 @@ __global__ __launch_bounds__(NW * 64) void sdpa_fwd_f32(
                 o[3] = ltot != 0.f ? oacc[dt][4 * i4 + 3] / ltot : 0.f;
                 *reinterpret_cast<f32x4*>(dst + dv) = o;
             }
+        // Natural-log log-sum-exp of the scaled logits, relative to the final
+        // running maximum (−∞ for a query with no legal key: ltot = 0).
+        if (lse && hf == 0) {
+            const float mc = (mrun == -INFINITY ? 0.f : mrun) * c_log2;
+            lse[(size_t)bh * n + qrow] = (mc + log2f(ltot)) * 0.6931471805599453f;
+        }
     }
 }
 
@@ -256,7 +262,7 @@ hipError_t launch_f32_long(const Args& a, hipStream_t stream) {
     const int nqb = (a.n + NW * QW - 1) / (NW * QW);
     hipLaunchKernelGGL(sdpa_fwd_f32<NW>, dim3(nqb * BH), dim3(NW * 64), 0, stream,
                        (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.out,
-                       BH, a.H, a.n, a.m, c_log2, a.wl, a.wr, a.bottom_right, a.key_lens, nqb, a.lay);
+                       BH, a.H, a.n, a.m, c_log2, a.wl, a.wr, a.bottom_right, a.key_lens, nqb, a.lse, a.lay);
     return hipGetLastError();
 }
 

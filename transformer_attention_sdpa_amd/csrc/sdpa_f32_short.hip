@@ -62,7 +62,7 @@ template <bool STRIDED>
 __global__ __launch_bounds__(NT) void sdpa_short_f32(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     float* __restrict__ O, int H, int n, int m, float c_log2, int wl, int wr, int bottom_right,
-    const int32_t* __restrict__ key_lens, Layout lay) {
+    const int32_t* __restrict__ key_lens, float* __restrict__ lse, Layout lay) {
     // K tile at 0, Q at 16 KiB, V at 32 KiB.
     __shared__ __attribute__((aligned(16))) char lds[3 * TILE];
     const f32x4* sK = reinterpret_cast<const f32x4*>(lds);
@@ -138,7 +138,7 @@ __global__ __launch_bounds__(NT) void sdpa_short_f32(
 
     // Sᵀ tiles; register r of tile kt is key 16·kt + 4·G + r of query q.
     f32x4 s[4];
-    float l = 0.f;
+    float l = 0.f, mc = 0.f;
     if (active) {
         // Key tiles in pairs (a tile of a pair past nkt is masked out below):
         // four independent accumulation chains keep the matrix pipe busy.
@@ -174,7 +174,7 @@ __global__ __launch_bounds__(NT) void sdpa_short_f32(
                         max3(s[1][2], s[1][3], s[2][0]));
         mx = max3(mx, max3(s[2][1], s[2][2], s[2][3]), max3(s[3][0], s[3][1], s[3][2]));
         mx = quad_max_f(max2(mx, s[3][3]));
-        const float mc = (mx == -INFINITY ? 0.f : mx) * c_log2;  // no (−∞) − (−∞)
+        mc = (mx == -INFINITY ? 0.f : mx) * c_log2;  // no (−∞) − (−∞)
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
@@ -230,6 +230,9 @@ __global__ __launch_bounds__(NT) void sdpa_short_f32(
             ov[3] = o[3][r] * inv;
             store16_nt(dst + 16 * r, __builtin_bit_cast(u32x4, ov));
         }
+        // Natural-log log-sum-exp of the scaled logits: mc + log2 l in base 2,
+        // −∞ for a query with no legal key (l = 0).
+        if (lse && G == 0) lse[(size_t)bh * n + q] = (mc + log2f(l)) * 0.6931471805599453f;
     }
 }
 
@@ -241,7 +244,7 @@ hipError_t launch_f32_short(const Args& a, hipStream_t stream) {
     const float c_log2 = (float)((double)a.scale * 1.4426950408889634);  // scale·log2(e)
     hipLaunchKernelGGL(a.strided ? sdpa_short_f32<true> : sdpa_short_f32<false>, dim3(a.B * a.H), dim3(NT), 0, stream,
                        (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.out,
-                       a.H, a.n, a.m, c_log2, a.wl, a.wr, a.bottom_right, a.key_lens, a.lay);
+                       a.H, a.n, a.m, c_log2, a.wl, a.wr, a.bottom_right, a.key_lens, a.lse, a.lay);
     return hipGetLastError();
 }
 
