@@ -303,28 +303,30 @@ def time_workload(name, dtype, steps, warmup, clock_warm_s=0.0, case=None, split
     }
 
 
-def backward_work(wl, key_lens):
-    """Algorithmic FLOPs and HBM bytes of one backward step (bf16).
+def backward_work(wl, key_lens, dtype="bf16"):
+    """Algorithmic FLOPs and HBM bytes of one backward step.
 
     FLOPs: the five products per legal pair — S recomputed (2·d_k), dP (2·d_v),
     dV (2·d_v), dQ (2·d_k), dK (2·d_k) — i.e. 10·d per pair, 2.5× the forward
-    count.  Bytes: Q, O, dO and the log-sum-exp of every query row and the
-    legal K/V rows read; dQ and every dK, dV row written.
+    count.  Bytes (at the dtype's element size; the log-sum-exp is fp32 either
+    way): Q, O, dO and the log-sum-exp of every query row and the legal K/V
+    rows read; dQ and every dK, dV row written.
     """
-    fwd_flops, _, _ = algorithmic_work(wl, "bf16", key_lens)
+    esz = 2 if dtype == "bf16" else 4
+    fwd_flops, _, _ = algorithmic_work(wl, dtype, key_lens)
     pairs = fwd_flops // (2 * (wl.d_k + wl.d_v))
     flops = 2 * (3 * wl.d_k + 2 * wl.d_v) * pairs
     kv_rows = sum(wl.h * (wl.m if key_lens is None else min(max(int(key_lens[b]), 0), wl.m))
                   for b in range(wl.B))
     rows_q = wl.B * wl.h * wl.n
-    nbytes = (2 * rows_q * (wl.d_k + 2 * wl.d_v) + 4 * rows_q + 2 * kv_rows * (wl.d_k + wl.d_v)
-              + 2 * rows_q * wl.d_k + 2 * wl.B * wl.h * wl.m * (wl.d_k + wl.d_v))
+    nbytes = (esz * rows_q * (wl.d_k + 2 * wl.d_v) + 4 * rows_q + esz * kv_rows * (wl.d_k + wl.d_v)
+              + esz * rows_q * wl.d_k + esz * wl.B * wl.h * wl.m * (wl.d_k + wl.d_v))
     return flops, nbytes
 
 
-def time_backward(name, steps, warmup, clock_warm_s=0.1):
-    """sdpa_backward (two launches per step) on a workload, bf16, with the
-    forward output and log-sum-exp computed once beforehand."""
+def time_backward(name, steps, warmup, clock_warm_s=0.1, dtype="bf16"):
+    """sdpa_backward (two launches per step) on a workload, in bf16 or fp32,
+    with the forward output and log-sum-exp computed once beforehand."""
     import numpy as np
     import torch
 
@@ -332,13 +334,16 @@ def time_backward(name, steps, warmup, clock_warm_s=0.1):
     from transformer_attention_sdpa_amd import _lib
 
     wl = WORKLOADS[name]
-    case = make_inputs(wl, "bf16")
+    case = make_inputs(wl, dtype)
     dev = torch.device("cuda:0")
+    tdt, cdt = ((torch.bfloat16, _lib.SDPA_BF16) if dtype == "bf16" else (torch.float32, _lib.SDPA_F32))
 
     def up(x):
+        if dtype != "bf16":
+            return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(dev)
         return torch.from_numpy(bf16_bits(x).view(np.int16)).to(dev).view(torch.bfloat16)
 
-    q0, k0, v0, do0 = up(case["q"]), up(case["k"]), up(case["v"]), up(grad_output(wl))
+    q0, k0, v0, do0 = up(case["q"]), up(case["k"]), up(case["v"]), up(grad_output(wl, dtype))
     kl = torch.from_numpy(case["key_lens"]).to(dev) if case["key_lens"] is not None else None
     kl_ptr = None if kl is None else kl.data_ptr()
     B, h, n, m, d = wl.B, wl.h, wl.n, wl.m, wl.d_k
@@ -350,18 +355,17 @@ def time_backward(name, steps, warmup, clock_warm_s=0.1):
         wright = -1 if wl.window[1] is None else wl.window[1]
         walign = (_lib.SDPA_ALIGN_BOTTOM_RIGHT if len(wl.window) > 2 and wl.window[2] == "bottom_right"
                   else _lib.SDPA_ALIGN_TOP_LEFT)
-    flops, nbytes = backward_work(wl, case["key_lens"])
+    flops, nbytes = backward_work(wl, case["key_lens"], dtype)
     nsets = max(1, min(64, math.ceil(2 * INFINITY_CACHE_BYTES / nbytes)))
     need = _lib.sdpa_backward_workspace_bytes(B, h, n)
     stream = torch.cuda.current_stream(dev).cuda_stream
     sets = []
     for _ in range(nsets):
         q, k, v, do = q0.clone(), k0.clone(), v0.clone(), do0.clone()
-        o = torch.empty((B, h, n, d), dtype=torch.bfloat16, device=dev)
+        o = torch.empty((B, h, n, d), dtype=tdt, device=dev)
         lse = torch.empty((B, h, n), dtype=torch.float32, device=dev)
         rc = _lib.sdpa_forward_lse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                                   B, h, n, m, d, d, scale, wleft, wright, walign, kl_ptr, _lib.SDPA_BF16,
-                                   stream)
+                                   B, h, n, m, d, d, scale, wleft, wright, walign, kl_ptr, cdt, stream)
         if rc != _lib.SDPA_OK:
             raise RuntimeError(_lib.sdpa_strerror(rc))
         grads = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)]
@@ -372,8 +376,7 @@ def time_backward(name, steps, warmup, clock_warm_s=0.1):
         q, k, v, o, do, lse, dq, dk, dv, ws = sets[i % nsets]
         rc = _lib.sdpa_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
                                 lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, h, n, m,
-                                d, d, scale, wleft, wright, walign, kl_ptr, _lib.SDPA_BF16,
-                                ws.data_ptr(), need, st)
+                                d, d, scale, wleft, wright, walign, kl_ptr, cdt, ws.data_ptr(), need, st)
         if rc != _lib.SDPA_OK:
             raise RuntimeError(_lib.sdpa_strerror(rc))
 
@@ -399,7 +402,7 @@ def time_backward(name, steps, warmup, clock_warm_s=0.1):
     return {"ms_per_step": t * 1e3, "ms_per_step_graph": t_graph * 1e3,
             "tflops": flops / t / 1e12, "gbs": nbytes / t / 1e9,
             "alg_flops": flops, "alg_bytes": nbytes,
-            "frac_mfma_peak": flops / t / 1e12 / PEAK_TFLOPS["bf16"],
+            "frac_mfma_peak": flops / t / 1e12 / PEAK_TFLOPS[dtype],
             "frac_hbm_peak": nbytes / t / 1e9 / PEAK_HBM_GBS, "steps": steps, "sets_rotated": nsets,
             "launches_per_step": 2}
 
@@ -820,7 +823,8 @@ def main():
         return
     if args.backward:
         print(json.dumps({"workload": args.backward, "pass": "backward",
-                          **time_backward(args.backward, args.steps, args.warmup)}), flush=True)
+                          "dtype": args.dtype,
+                          **time_backward(args.backward, args.steps, args.warmup, dtype=args.dtype)}), flush=True)
         return
     if args.mha:
         print(json.dumps({"workload": args.mha, **time_mha(args.mha, args.steps, args.warmup)}), flush=True)
@@ -860,8 +864,10 @@ def main():
                 "ms_per_step", "tflops", "gbs", "frac_mfma_peak", "frac_hbm_peak", "steps",
                 "sets_rotated", "ms_per_step_graph")}
         for name in ("encoder_self_base", "long_causal_8k"):
-            extra[f"backward-{name}-bf16"] = time_backward(
-                name, 20 if name.endswith("_8k") else max(10, min(args.steps, 200)), min(args.warmup, 3))
+            for dt in ("bf16", "f32"):
+                extra[f"backward-{name}-{dt}"] = time_backward(
+                    name, (20 if dt == "bf16" else 5) if name.endswith("_8k") else max(10, min(args.steps, 200)),
+                    min(args.warmup, 3), dtype=dt)
         for name in ("mha_encoder_base", "mha_cross_big"):
             extra[f"{name}-bf16"] = time_mha(name, max(10, min(args.steps, 200)),
                                              min(args.warmup, 5))

@@ -302,7 +302,7 @@ SDPA_API int sdpa_forward_ex_noalloc(const void* q, const void* k, const void* v
                                      int32_t dtype, void* stream);
 
 /*
- * sdpa_backward — the gradient of Eq. (1) (bf16).  The pages train the model
+ * sdpa_backward — the gradient of Eq. (1) (bf16 or fp32).  The pages train the model
  * through attention but print only the forward pass; by the chain rule, for
  * any loss with output gradient dO:
  *
@@ -314,10 +314,10 @@ SDPA_API int sdpa_forward_ex_noalloc(const void* q, const void* k, const void* v
  *
  * q, k, v   the forward inputs, as in sdpa_forward_window.
  * out       the forward output O, [B, h, n, d_v].
- * dout      dO, [B, h, n, d_v] bf16.
+ * dout      dO, [B, h, n, d_v], of the inputs' dtype.
  * lse       the forward pass's lse (sdpa_forward_lse), float [B, h, n].
- * dq        device, [B, h, n, d_k] bf16, written completely.
- * dk, dv    device, [B, h, m, d_k] and [B, h, m, d_v] bf16, written completely
+ * dq        device, [B, h, n, d_k] of the inputs' dtype, written completely.
+ * dk, dv    device, [B, h, m, d_k] and [B, h, m, d_v] of the inputs' dtype, written completely
  *           (rows of keys at or past key_lens[b] are zero).
  * scale, window_left, window_right, align, key_lens
  *           exactly as given to the forward pass.
@@ -325,8 +325,10 @@ SDPA_API int sdpa_forward_ex_noalloc(const void* q, const void* k, const void* v
  *           device scratch of at least sdpa_backward_workspace_bytes(B, h, n)
  *           bytes, 16-byte aligned, owned by the caller (it receives D and
  *           lse · log2 e per row).  Too small: SDPA_ERR_WORKSPACE.
- * dtype     SDPA_BF16 (SDPA_F32: SDPA_ERR_UNSUPPORTED).
- * d_k, d_v  d_k == d_v == 32, 64 or 128 (other pairs: SDPA_ERR_UNSUPPORTED).
+ * dtype     SDPA_BF16 (P and dS rounded to bf16 for their products, as in
+ *           the forward pass) or SDPA_F32 (fp32 throughout).
+ * d_k, d_v  bf16: d_k == d_v == 32, 64 or 128; fp32: d_k == d_v == 64 (other
+ *           pairs: SDPA_ERR_UNSUPPORTED).
  * The outputs and the workspace must not overlap each other or any input
  * (SDPA_ERR_ALIAS).  All tensors 16-byte aligned, lse and key_lens 4-byte
  * aligned.  Enqueues two kernels on `stream` (dQ, then dK and dV) and

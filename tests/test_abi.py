@@ -380,7 +380,9 @@ def test_backward_workspace_size(lib):
     (dict(dk=None), _lib.SDPA_ERR_NULL),
     (dict(ws=None), _lib.SDPA_ERR_NULL),
     (dict(q=None), _lib.SDPA_ERR_NULL),
-    (dict(dtype=0), _lib.SDPA_ERR_UNSUPPORTED),
+    (dict(dtype=0, d_k=32, d_v=32), _lib.SDPA_ERR_UNSUPPORTED),    # the fp32 gradient takes width 64
+    (dict(dtype=0, d_k=128, d_v=128), _lib.SDPA_ERR_UNSUPPORTED),
+    (dict(dtype=0, dk=7 * P + 6000), _lib.SDPA_ERR_ALIAS),         # inside dq's fp32 span (8 KiB) only
     (dict(dtype=9), _lib.SDPA_ERR_DTYPE),
     (dict(d_v=32), _lib.SDPA_ERR_UNSUPPORTED),
     # forward-only widths: the backward kernels take equal widths 32, 64, 128

@@ -74,3 +74,18 @@ def test_window_pair_count(window):
     flops, _, _ = bench.algorithmic_work(wl, "bf16", kl)
     pairs, _ = _brute(wl, kl)
     assert flops == 4 * 64 * pairs
+
+
+@pytest.mark.parametrize("name", ["encoder_self_base", "decoder_causal_base", "cross_big"])
+def test_backward_work_matches_brute_force(name):
+    """Five products per legal pair (S, dP, dV, dQ, dK: 2·d each); bytes at the
+    element size: Q, O, dO, dQ of every query row, the fp32 log-sum-exp, the
+    legal K, V rows read and every dK, dV row written."""
+    wl = WORKLOADS[name]
+    key_lens = make_inputs(wl, wl.dtypes[0])["key_lens"]
+    pairs, kv_rows = _brute(wl, key_lens)
+    rows_q = wl.B * wl.h * wl.n
+    for dt, esz in (("bf16", 2), ("f32", 4)):
+        flops, nbytes = bench.backward_work(wl, key_lens, dt)
+        assert flops == 10 * 64 * pairs
+        assert nbytes == (esz * 64 * (4 * rows_q + 2 * kv_rows + 2 * wl.B * wl.h * wl.m) + 4 * rows_q)

@@ -177,7 +177,8 @@ def _like(t, shape, dtype, device, name):
 
 def backward(q, k, v, out, dout, lse, *, causal: bool = False, key_lens=None,
              scale: float | None = None, window=None, dq=None, dk=None, dv=None, workspace=None):
-    """Gradients (dq, dk, dv) of Eq. (1) for the output gradient ``dout`` (bf16).
+    """Gradients (dq, dk, dv) of Eq. (1) for the output gradient ``dout`` (bf16,
+    or fp32 at d = 64), in q's dtype.
 
     ``out`` and ``lse`` come from ``forward(..., return_lse=True)`` with the same
     q, k, v, causal, key_lens, scale and window.  dq/dk/dv/workspace may be

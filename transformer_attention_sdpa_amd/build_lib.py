@@ -22,7 +22,7 @@ LIB = os.path.join(PKG, "libsdpa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["sdpa_api.cpp", "sdpa_bf16.hip", "sdpa_bf16_short.hip", "sdpa_bf16_decode.hip",
-           "sdpa_f32.hip", "sdpa_f32_short.hip", "sdpa_mha.hip", "sdpa_bf16_bwd.hip",
+           "sdpa_f32.hip", "sdpa_f32_short.hip", "sdpa_f32_bwd.hip", "sdpa_mha.hip", "sdpa_bf16_bwd.hip",
            "sdpa_bf16_width.hip", "sdpa_bf16_wide.hip"]
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops.

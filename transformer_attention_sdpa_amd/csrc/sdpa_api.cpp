@@ -13,7 +13,7 @@
 
 namespace {
 
-constexpr int kVersion = 1 * 10000 + 6 * 100 + 0;  // 1.6.0: attention dropout
+constexpr int kVersion = 1 * 10000 + 7 * 100 + 0;  // 1.7.0: fp32 log-sum-exp and gradient
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -253,9 +253,9 @@ int backward_impl(const void* q, const void* k, const void* v, const void* out, 
     // checks below cover the outputs).
     int st = validate(q, k, v, const_cast<void*>(out), B, h, n, m, d_k, d_v, scale, key_lens, dtype);
     if (st != SDPA_OK) return st;
-    if (dtype != SDPA_BF16) return SDPA_ERR_UNSUPPORTED;
-    // The backward kernels take equal widths 32, 64 and 128.
+    // The bf16 backward kernels take equal widths 32, 64 and 128; the fp32 ones 64.
     if (d_k != d_v || (d_k != 32 && d_k != 64 && d_k != 128)) return SDPA_ERR_UNSUPPORTED;
+    if (dtype == SDPA_F32 && d_k != sdpa::kHeadDim) return SDPA_ERR_UNSUPPORTED;
     for (const void* p : {dout, (const void*)dq, (const void*)dk, (const void*)dv, (const void*)workspace})
         if (!aligned16(p)) return SDPA_ERR_ALIGN;
     if (reinterpret_cast<uintptr_t>(lse) & 3u) return SDPA_ERR_ALIGN;
@@ -264,13 +264,13 @@ int backward_impl(const void* q, const void* k, const void* v, const void* out, 
     if (st != SDPA_OK) return st;
     const size_t need = sdpa::bwd_workspace_bytes(B, h, n);
     if (workspace_bytes < need) return SDPA_ERR_WORKSPACE;
-    const uint64_t heads = (uint64_t)B * h;
+    const uint64_t heads = (uint64_t)B * h, esz = dtype == SDPA_F32 ? 4 : 2;
     struct Buf { const void* p; uint64_t n; };
-    const Buf ins[] = {{q, heads * n * d_k * 2}, {k, heads * m * d_k * 2}, {v, heads * m * d_v * 2},
-                       {out, heads * n * d_v * 2}, {dout, heads * n * d_v * 2}, {lse, heads * n * 4},
+    const Buf ins[] = {{q, heads * n * d_k * esz}, {k, heads * m * d_k * esz}, {v, heads * m * d_v * esz},
+                       {out, heads * n * d_v * esz}, {dout, heads * n * d_v * esz}, {lse, heads * n * 4},
                        {key_lens, key_lens ? (uint64_t)B * 4 : 0},
                        {keep, keep ? keep_bytes(B, h, n, m) : 0}};
-    const Buf outs[] = {{dq, heads * n * d_k * 2}, {dk, heads * m * d_k * 2}, {dv, heads * m * d_v * 2},
+    const Buf outs[] = {{dq, heads * n * d_k * esz}, {dk, heads * m * d_k * esz}, {dv, heads * m * d_v * esz},
                         {workspace, need}};
     for (int i = 0; i < 4; ++i) {
         for (const Buf& in : ins)
@@ -283,7 +283,8 @@ int backward_impl(const void* q, const void* k, const void* v, const void* out, 
     a.keep = keep;
     a.keep_scale = keep_scale;
     clear_pending_error();
-    const hipError_t e = sdpa::launch_bwd_bf16(a, reinterpret_cast<hipStream_t>(stream));
+    const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const hipError_t e = dtype == SDPA_F32 ? sdpa::launch_bwd_f32(a, s) : sdpa::launch_bwd_bf16(a, s);
     return e == hipSuccess ? SDPA_OK : SDPA_ERR_LAUNCH;
 }
 

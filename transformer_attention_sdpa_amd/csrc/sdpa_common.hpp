@@ -127,8 +127,8 @@ struct MhaArgs {
 };
 size_t mha_workspace_bytes(int B, int n, int m, int h, int hd);
 
-// The gradient of Eq. (1) (bf16): dQ, dK, dV from Q, K, V, the forward output
-// O, its gradient dO and the forward pass's per-row log-sum-exp.
+// The gradient of Eq. (1) (bf16 or fp32): dQ, dK, dV from Q, K, V, the
+// forward output O, its gradient dO and the forward pass's per-row log-sum-exp.
 struct BwdArgs {
     const void* q;     // [B, H, n, 64]
     const void* k;     // [B, H, m, 64]
@@ -151,6 +151,7 @@ struct BwdArgs {
 };
 size_t bwd_workspace_bytes(int B, int H, int n);
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_f32(const BwdArgs& a, hipStream_t stream);   // d_k = d_v = 64
 hipError_t launch_mha_bf16(const MhaArgs& a, hipStream_t stream);
 
 hipError_t launch_bf16(const Args& a, hipStream_t stream);        // picks one of the four below
