@@ -6,8 +6,8 @@ head widths: row (A) runs 32 heads of d_k = d_v = 16 and one of 512, and row (B)
 d_v = 64 while it shrinks the key width d_k to 16 or 32.  Eq. (1) contracts
 queries with keys over d_k and weights with values over d_v, so the two
 widths are independent; the oracle takes any pair.  These widths run on the
-width kernel at every length, and row (A)'s single head of 512 on a kernel
-of its own.  Bar: the bf16 one, 2e-2 absolute; the
+sentence-length kernel when n, m ≤ 64 and on the width kernel beyond, and row
+(A)'s single head of 512 on a kernel of its own.  Bar: the bf16 one, 2e-2 absolute; the
 log-sum-exp within 2^-8.
 """
 
@@ -156,16 +156,18 @@ def test_table3_masked_weights_are_exactly_zero(gpu_lib, dk, dv):
     assert max_abs_err(got, ref) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("n,m", [(130, 190), (48, 64)], ids=["tiled", "sentence"])
 @pytest.mark.parametrize("dk,dv", [(16, 16), (16, 64), (32, 64), (512, 512)])
-def test_table3_token_major_matches_packed_bitwise(gpu_lib, dk, dv):
+def test_table3_token_major_matches_packed_bitwise(gpu_lib, dk, dv, n, m):
     """Token-major [B, len, h, d] views of q, k, v and out through
-    sdpa_forward_strided: bitwise equal to the packed call."""
+    sdpa_forward_strided: bitwise equal to the packed call, on the tiled
+    kernels and on the sentence-length one (n, m ≤ 64)."""
     import torch
 
     from transformer_attention_sdpa_amd import forward
 
-    rng = np.random.default_rng(97 + dk + dv)
-    B, h, n, m = 3, 4, 130, 190
+    rng = np.random.default_rng(97 + dk + dv + n)
+    B, h = 3, 4
     c = random_case(rng, B, h, n, m, dk, dv, dtype="bf16", causal=False,
                     key_lens=rng.integers(1, m, size=B, endpoint=True).astype(np.int32))
     q, k, v = (to_device(c[x], "bf16") for x in ("q", "k", "v"))
