@@ -370,6 +370,272 @@ __global__ __launch_bounds__(NW * 64) void sdpa_bwd_dkdv_f32(
     }
 }
 
+// ---------------------------------------------------------------------------
+// Split forms, for grids too small to fill the chip with one wave per 32 rows
+// (sentence-length batches): a workgroup owns one block of 32 queries (dQ) or
+// keys (dK, dV), and its NW waves take every NW-th tile of the stream (wave w:
+// tiles tbeg + w, tbeg + w + NW, …), each into tiles of its own in LDS
+// (buffer_load … lds, no barrier between waves).  The partial gradients are
+// then summed through LDS in wave order, so the result stays deterministic.
+
+// Rows [r0, r0 + 32) of a [rows, 64] fp32 tensor (rows past `rows` read as
+// zeros) into a swizzled 8 KiB LDS tile, by this wave alone: load u fills rows
+// 4u .. 4u + 3; lane ln lands at (row 4u + ln / 16, position ln % 16), which
+// holds chunk (ln % 16) ^ (row mod 16).
+__device__ __forceinline__ void wave_tile_load(const float* base, int rows, int r0, f32x4* tile, int lane) {
+    const i32x4 rs = make_rsrc(base, rows > 0 ? (uint32_t)rows * (uint32_t)(D * 4) : 0u);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        const int row = 4 * u + (lane >> 4);
+        const int c = (lane & 15) ^ (row & 15);
+        load16_to_lds(rs, tile + 64 * u, (r0 + row) * D * 4 + c * 16);
+    }
+}
+
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void sdpa_bwd_dq_f32_split(
+    const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
+    const float* __restrict__ O, const float* __restrict__ dO, const float* __restrict__ lse,
+    float* __restrict__ dQ, float* __restrict__ ws_d, float* __restrict__ ws_l, int BH, int H, int n,
+    int m, float scale, float c_log2, int wl, int wr, int bottom_right, const int32_t* __restrict__ key_lens,
+    int nqb) {
+    __shared__ f32x4 lds[NW][2][BT * 16];  // per wave: K tile, V tile
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+
+    const int g = blockIdx.x;
+    const int bh = g % BH;
+    const int q0 = (nqb - 1 - g / BH) * 32;
+    const int b = bh / H;
+    int L = m;
+    if (key_lens) {
+        const int t = key_lens[b];
+        L = t < 0 ? 0 : (t > m ? m : t);
+    }
+    const KeyWindow win{wl, wr, bottom_right ? L - n : 0, L};
+    const int qlast = min(q0 + 32, n) - 1;
+    const int kbeg = win.lo(q0), kend = win.hi(qlast);
+    const int tbeg = kbeg / BT;
+    const int tend = kend > kbeg ? (kend + BT - 1) / BT : tbeg;
+    const int flo = win.lo(qlast), fhi = win.hi(q0);  // keys legal for every query of the block
+
+    const size_t qbase = (size_t)bh * n * D, kvbase = (size_t)bh * m * D;
+    f32x4* sK = lds[w][0];
+    f32x4* sV = lds[w][1];
+    // The first tile is requested before the row operands, so that both
+    // round trips to memory overlap.
+    if (tbeg + w < tend) {
+        wave_tile_load(K + kvbase, L, (tbeg + w) * BT, sK, lane);
+        wave_tile_load(V + kvbase, L, (tbeg + w) * BT, sV, lane);
+    }
+    const int qrow = q0 + l32;
+    const bool qok = qrow < n;
+    const int qlo = win.lo(qrow), qhi = win.hi(qrow);
+    float qop[32], dop[32];
+    load_half_row(Q + qbase + (size_t)qrow * D, qok, hf, qop);
+    load_half_row(dO + qbase + (size_t)qrow * D, qok, hf, dop);
+    float dsum;
+    {
+        float oop[32];
+        load_half_row(O + qbase + (size_t)qrow * D, qok, hf, oop);
+        float acc = 0.f;
+#pragma unroll
+        for (int e = 0; e < 32; ++e) acc = __builtin_fmaf(dop[e], oop[e], acc);
+        dsum = half_swap_sum(acc);
+    }
+    const float lr = qok ? lse[(size_t)bh * n + qrow] : 0.f;
+    const float lc = lr == -INFINITY ? INFINITY : lr * LOG2E;
+    if (w == 0 && qok && hf == 0) {
+        ws_d[(size_t)bh * n + qrow] = dsum;
+        ws_l[(size_t)bh * n + qrow] = lc;
+    }
+
+    f32x16 acc[2];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[0][i] = acc[1][i] = 0.f;
+    for (int t = tbeg + w; t < tend; t += NW) {
+        if (t != tbeg + w) {
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the previous tile's reads are done
+            wave_tile_load(K + kvbase, L, t * BT, sK, lane);
+            wave_tile_load(V + kvbase, L, t * BT, sV, lane);
+        }
+        wait_vmem();
+        const int k0 = t * BT;
+        f32x16 s, dp;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
+        row_product(sK, l32, hf, qop, s);   // Sᵀ = K Qᵀ
+        row_product(sV, l32, hf, dop, dp);  // dPᵀ = V dOᵀ
+        if (k0 < flo || k0 + BT > fhi) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int key = k0 + 8 * (i >> 2) + 4 * hf + (i & 3);
+                if (key < qlo || key >= qhi) s[i] = -INFINITY;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const float p = exp2_hw(__builtin_fmaf(s[i], c_log2, -lc));
+            s[i] = p * (dp[i] - dsum);  // dSᵀ
+        }
+        col_product(reinterpret_cast<const float*>(sK), l32, hf, s, acc);  // dQᵀ += Kᵀ dSᵀ
+    }
+
+    // dQ = Σ_w partial_w in wave order: waves 1.. park theirs in LDS.
+    __syncthreads();
+    float* red = reinterpret_cast<float*>(&lds[0][0][0]);
+    if (w > 0) {
+#pragma unroll
+        for (int r = 0; r < 32; ++r) red[((w - 1) * 32 + r) * 64 + lane] = acc[r >> 4][r & 15];
+    }
+    __syncthreads();
+    if (w == 0 && qok) {
+#pragma unroll
+        for (int u = 1; u < NW; ++u)
+#pragma unroll
+            for (int r = 0; r < 32; ++r) acc[r >> 4][r & 15] += red[((u - 1) * 32 + r) * 64 + lane];
+        store_row(dQ + qbase + (size_t)qrow * D, acc, hf, scale);
+    }
+}
+
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void sdpa_bwd_dkdv_f32_split(
+    const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
+    const float* __restrict__ dO, const float* __restrict__ ws_d, const float* __restrict__ ws_l,
+    float* __restrict__ dK, float* __restrict__ dV, int BH, int H, int n, int m, float scale,
+    float c_log2, int wl, int wr, int bottom_right, const int32_t* __restrict__ key_lens) {
+    // per wave: Q tile, dO tile, then lse·log2 e and D of the tile's rows
+    // (64 floats each: the 4-byte loads fill a whole wave's worth)
+    __shared__ f32x4 lds[NW][2 * BT * 16 + 32];
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+
+    const int g = blockIdx.x;
+    const int bh = g % BH;
+    const int k0 = (g / BH) * 32;
+    const int b = bh / H;
+    int L = m;
+    if (key_lens) {
+        const int t = key_lens[b];
+        L = t < 0 ? 0 : (t > m ? m : t);
+    }
+    const QueryInterval qr{wl, wr, bottom_right ? L - n : 0, L, n};
+    const int klast = min(k0 + 32, L) - 1;
+    const bool any = klast >= k0;
+    const int qbeg = any ? qr.qa(k0) : 0;
+    const int qend = any ? qr.qb(klast) : 0;
+    const int tbeg = qbeg / BT;
+    const int tend = qend > qbeg ? (qend + BT - 1) / BT : tbeg;
+    const bool full = any && k0 + 31 < L;
+    const int fqa = full ? qr.qa(klast) : 0, fqb = full ? qr.qb(k0) : 0;
+
+    const size_t qbase = (size_t)bh * n * D, kvbase = (size_t)bh * m * D;
+    f32x4* sQ = lds[w];
+    f32x4* sG = lds[w] + BT * 16;
+    f32x4* sL = lds[w] + 2 * BT * 16;       // 64 floats
+    f32x4* sDs = lds[w] + 2 * BT * 16 + 16; // 64 floats
+    auto issue = [&](int t0) {
+        wave_tile_load(Q + qbase, n, t0, sQ, lane);
+        wave_tile_load(dO + qbase, n, t0, sG, lane);
+        const uint32_t nb = (uint32_t)max(n - t0, 0) * 4u;  // rows past n read as zeros
+        sdpa_llvm_buffer_load_lds(make_rsrc(ws_l + (size_t)bh * n + t0, nb),
+                                  (__attribute__((address_space(3))) void*)sL, 4, lane * 4, 0, 0, 0);
+        sdpa_llvm_buffer_load_lds(make_rsrc(ws_d + (size_t)bh * n + t0, nb),
+                                  (__attribute__((address_space(3))) void*)sDs, 4, lane * 4, 0, 0, 0);
+    };
+    // The first tile is requested before the row operands (both round trips overlap).
+    if (tbeg + w < tend) issue((tbeg + w) * BT);
+    const int key = k0 + l32;
+    float kop[32], vop[32];
+    load_half_row(K + kvbase + (size_t)key * D, key < L, hf, kop);
+    load_half_row(V + kvbase + (size_t)key * D, key < L, hf, vop);
+    const int ka = qr.qa(key), kb = qr.qb(key);
+
+    f32x16 dka[2], dva[2];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dka[0][i] = dka[1][i] = dva[0][i] = dva[1][i] = 0.f;
+    for (int t = tbeg + w; t < tend; t += NW) {
+        const int t0 = t * BT;
+        if (t != tbeg + w) {
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the previous tile's reads are done
+            issue(t0);
+        }
+        wait_vmem();
+        f32x16 s, dp;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
+        row_product(sQ, l32, hf, kop, s);   // S = Q Kᵀ
+        row_product(sG, l32, hf, vop, dp);  // dP = dO Vᵀ
+        if (t0 < fqa || t0 + BT > fqb) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int q = t0 + 8 * (i >> 2) + 4 * hf + (i & 3);
+                if (q < ka || q >= kb) s[i] = -INFINITY;
+            }
+        }
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+            const f32x4 lc = sL[2 * i4 + hf];
+            const f32x4 dd = sDs[2 * i4 + hf];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 4 * i4 + e;
+                const float p = exp2_hw(__builtin_fmaf(s[i], c_log2, -lc[e]));
+                s[i] = p;
+                dp[i] = p * (dp[i] - dd[e]);  // dS
+            }
+        }
+        col_product(reinterpret_cast<const float*>(sG), l32, hf, s, dva);   // dVᵀ += dOᵀ P
+        col_product(reinterpret_cast<const float*>(sQ), l32, hf, dp, dka);  // dKᵀ += Qᵀ dS
+    }
+
+    // dK, dV = Σ_w partial_w in wave order: waves 1.. park theirs in LDS.
+    __syncthreads();
+    float* red = reinterpret_cast<float*>(&lds[0][0]);
+    if (w > 0) {
+#pragma unroll
+        for (int r = 0; r < 32; ++r) {
+            red[((w - 1) * 64 + r) * 64 + lane] = dka[r >> 4][r & 15];
+            red[((w - 1) * 64 + 32 + r) * 64 + lane] = dva[r >> 4][r & 15];
+        }
+    }
+    __syncthreads();
+    if (w == 0 && key < m) {
+#pragma unroll
+        for (int u = 1; u < NW; ++u)
+#pragma unroll
+            for (int r = 0; r < 32; ++r) {
+                dka[r >> 4][r & 15] += red[((u - 1) * 64 + r) * 64 + lane];
+                dva[r >> 4][r & 15] += red[((u - 1) * 64 + 32 + r) * 64 + lane];
+            }
+        store_row(dK + kvbase + (size_t)key * D, dka, hf, scale);
+        store_row(dV + kvbase + (size_t)key * D, dva, hf, 1.f);
+    }
+}
+
+}  // namespace
+
+namespace {
+
+template <int NW>
+hipError_t launch_split(const BwdArgs& a, hipStream_t stream, float c_log2, float* ws_d, float* ws_l) {
+    const int BH = a.B * a.H;
+    const int nqb = (a.n + 31) / 32;
+    hipLaunchKernelGGL(sdpa_bwd_dq_f32_split<NW>, dim3(nqb * BH), dim3(NW * 64), 0, stream, (const float*)a.q,
+                       (const float*)a.k, (const float*)a.v, (const float*)a.out, (const float*)a.dout, a.lse,
+                       (float*)a.dq, ws_d, ws_l, BH, a.H, a.n, a.m, a.scale, c_log2, a.wl, a.wr, a.bottom_right,
+                       a.key_lens, nqb);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(sdpa_bwd_dkdv_f32_split<NW>, dim3(((a.m + 31) / 32) * BH), dim3(NW * 64), 0, stream,
+                       (const float*)a.q, (const float*)a.k, (const float*)a.v, (const float*)a.dout, ws_d, ws_l,
+                       (float*)a.dk, (float*)a.dv, BH, a.H, a.n, a.m, a.scale, c_log2, a.wl, a.wr,
+                       a.bottom_right, a.key_lens);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_bwd_f32(const BwdArgs& a, hipStream_t stream) {
@@ -378,6 +644,11 @@ hipError_t launch_bwd_f32(const BwdArgs& a, hipStream_t stream) {
     const float c_log2 = (float)((double)a.scale * 1.4426950408889634);  // scale·log2(e)
     float* ws_d = static_cast<float*>(a.workspace);
     float* ws_l = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + bwd_workspace_bytes(a.B, a.H, a.n) / 2);
+    // Fewer than 1024 blocks of 64 rows (four waves per CU): the split forms,
+    // with four waves per block once the streams reach four tiles.
+    if ((long long)BH * ((a.n + 63) / 64) < 1024 && (long long)BH * ((a.m + 63) / 64) < 1024)
+        return (a.n > 96 && a.m > 96) ? launch_split<4>(a, stream, c_log2, ws_d, ws_l)
+                                      : launch_split<2>(a, stream, c_log2, ws_d, ws_l);
     const int nqb = (a.n + 32 * NW - 1) / (32 * NW);
     hipLaunchKernelGGL(sdpa_bwd_dq_f32<NW>, dim3(nqb * BH), dim3(NW * 64), 0, stream, (const float*)a.q,
                        (const float*)a.k, (const float*)a.v, (const float*)a.out, (const float*)a.dout, a.lse,
