@@ -106,6 +106,24 @@ def test_f32_backward_long_causal_sampled(gpu_lib):
     check("long_causal_sampled", (got_q, dk[1, 3, keys], dv[1, 3, keys]), (ref_q, ref_k, ref_v))
 
 
+def test_f32_backward_large_grid_sampled(gpu_lib):
+    """128 heads of 520 (a ragged last block; 1152 blocks of 64 rows, so the
+    launches that give each wave its own 32 rows and share tiles between
+    waves): dQ rows at every 64-row block edge of two heads and the dK/dV rows
+    at every edge of one, with key padding."""
+    B, h, n = 4, 32, 520
+    kl = [520, 333, 64, 1]
+    c = backward_case(9903, B, h, n, n, key_lens=kl, dtype="f32")
+    dq, dk, dv = (from_device(t) for t in run_bwd(c))
+    picks = [(b, hh, q) for b, hh in ((0, 0), (1, 31)) for e in range(64, n, 64) for q in (e - 1, e)]
+    picks += [(2, 5, 0), (3, 7, n - 1)]
+    ref_q = sb.backward_query_rows(c["q"], c["k"], c["v"], c["do"], picks, key_lens=kl)
+    got_q = np.stack([dq[b, hh, q] for b, hh, q in picks])
+    keys = sorted({0, n - 1} | {x for e in range(64, n, 64) for x in (e - 1, e)})
+    ref_k, ref_v = sb.backward_key_rows(c["q"], c["k"], c["v"], c["do"], 1, 9, keys, key_lens=kl)
+    check("large_grid_sampled", (got_q, dk[1, 9, keys], dv[1, 9, keys]), (ref_q, ref_k, ref_v))
+
+
 def test_f32_backward_deterministic(gpu_lib):
     """No atomics: two runs agree bit for bit."""
     import torch

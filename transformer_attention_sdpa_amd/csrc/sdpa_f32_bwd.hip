@@ -620,15 +620,19 @@ __global__ __launch_bounds__(NW * 64) void sdpa_bwd_dkdv_f32_split(
 namespace {
 
 template <int NW>
-hipError_t launch_split(const BwdArgs& a, hipStream_t stream, float c_log2, float* ws_d, float* ws_l) {
+hipError_t launch_dq_split(const BwdArgs& a, hipStream_t stream, float c_log2, float* ws_d, float* ws_l) {
     const int BH = a.B * a.H;
     const int nqb = (a.n + 31) / 32;
     hipLaunchKernelGGL(sdpa_bwd_dq_f32_split<NW>, dim3(nqb * BH), dim3(NW * 64), 0, stream, (const float*)a.q,
                        (const float*)a.k, (const float*)a.v, (const float*)a.out, (const float*)a.dout, a.lse,
                        (float*)a.dq, ws_d, ws_l, BH, a.H, a.n, a.m, a.scale, c_log2, a.wl, a.wr, a.bottom_right,
                        a.key_lens, nqb);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    return hipGetLastError();
+}
+
+template <int NW>
+hipError_t launch_dkdv_split(const BwdArgs& a, hipStream_t stream, float c_log2, float* ws_d, float* ws_l) {
+    const int BH = a.B * a.H;
     hipLaunchKernelGGL(sdpa_bwd_dkdv_f32_split<NW>, dim3(((a.m + 31) / 32) * BH), dim3(NW * 64), 0, stream,
                        (const float*)a.q, (const float*)a.k, (const float*)a.v, (const float*)a.dout, ws_d, ws_l,
                        (float*)a.dk, (float*)a.dv, BH, a.H, a.n, a.m, a.scale, c_log2, a.wl, a.wr,
@@ -644,11 +648,16 @@ hipError_t launch_bwd_f32(const BwdArgs& a, hipStream_t stream) {
     const float c_log2 = (float)((double)a.scale * 1.4426950408889634);  // scale·log2(e)
     float* ws_d = static_cast<float*>(a.workspace);
     float* ws_l = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + bwd_workspace_bytes(a.B, a.H, a.n) / 2);
-    // Fewer than 1024 blocks of 64 rows (four waves per CU): the split forms,
-    // with four waves per block once the streams reach four tiles.
-    if ((long long)BH * ((a.n + 63) / 64) < 1024 && (long long)BH * ((a.m + 63) / 64) < 1024)
-        return (a.n > 96 && a.m > 96) ? launch_split<4>(a, stream, c_log2, ws_d, ws_l)
-                                      : launch_split<2>(a, stream, c_log2, ws_d, ws_l);
+    // Fewer than 1024 blocks of 64 rows (four waves per CU): the split forms.
+    // Each launch's waves split the tiles it streams: four once there are
+    // more than three (dQ streams keys, dK/dV queries).
+    if ((long long)BH * ((a.n + 63) / 64) < 1024 && (long long)BH * ((a.m + 63) / 64) < 1024) {
+        const hipError_t e = a.m > 96 ? launch_dq_split<4>(a, stream, c_log2, ws_d, ws_l)
+                                      : launch_dq_split<2>(a, stream, c_log2, ws_d, ws_l);
+        if (e != hipSuccess) return e;
+        return a.n > 96 ? launch_dkdv_split<4>(a, stream, c_log2, ws_d, ws_l)
+                        : launch_dkdv_split<2>(a, stream, c_log2, ws_d, ws_l);
+    }
     const int nqb = (a.n + 32 * NW - 1) / (32 * NW);
     hipLaunchKernelGGL(sdpa_bwd_dq_f32<NW>, dim3(nqb * BH), dim3(NW * 64), 0, stream, (const float*)a.q,
                        (const float*)a.k, (const float*)a.v, (const float*)a.out, (const float*)a.dout, a.lse,
