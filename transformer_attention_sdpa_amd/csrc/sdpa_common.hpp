@@ -174,7 +174,10 @@ bool short_f32_fits(const Args& a);
 
 // max(a, b, c) in one v_max3_f32 and max(a, b) in one v_max_f32.  Written as
 // instructions because fmaxf on MFMA results is lowered with an extra
-// NaN-quieting v_max per operand.
+// NaN-quieting v_max per operand.  The compiler inserts no wait states between
+// an MFMA and an inline-asm reader of its result (up to 19 are needed): every
+// use here sits far enough behind its MFMA, which a CPU test checks in the
+// gfx950 assembly of each kernel.
 __device__ __forceinline__ float max3(float a, float b, float c) {
     float r;
     asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
