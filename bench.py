@@ -774,6 +774,41 @@ def context(steps=400):
     return out
 
 
+def context_gemm_shapes(iters=200):
+    """The multi-head sublayer's projection GEMMs through torch.matmul
+    (hipBLASLt), for a kernel trace beside this library's sublayer: per
+    workload, Q, K, V as one GEMM when the sublayer attends to itself (Q
+    alone and K, V together otherwise) and the output projection.  Per-call
+    event times of these small GEMMs are bound by the host's launch rate;
+    the kernel durations come from the trace.  Context only; not a step."""
+    import torch
+
+    from sdpa_inputs import MHA_WORKLOADS
+
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+    out = {"what": "context: library GEMMs on the sublayer's projection shapes"}
+    for name, a in MHA_WORKLOADS.items():
+        B, n, m, dm, hw = a["B"], a["n"], a["m"], a["d_model"], 64 * a["h"]
+        self_att = a.get("self_attention", True)
+        shapes = ([("qkv", B * n, dm, 3 * hw)] if self_att else [("q", B * n, dm, hw), ("kv", B * m, dm, 2 * hw)])
+        shapes.append(("out", B * n, hw, dm))
+        for what, M, K, N in shapes:
+            x = torch.randn(M, K, device=dev, dtype=torch.bfloat16, generator=gen)
+            w = torch.randn(K, N, device=dev, dtype=torch.bfloat16, generator=gen)
+            y = torch.empty(M, N, device=dev, dtype=torch.bfloat16)
+            for _ in range(20):
+                torch.matmul(x, w, out=y)
+            torch.cuda.synchronize()
+            for _ in range(iters):
+                torch.matmul(x, w, out=y)
+            torch.cuda.synchronize()
+            out[f"{name}/{what}"] = {"M": M, "K": K, "N": N, "calls": 20 + iters}
+    out["torch"] = torch.__version__
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -800,6 +835,8 @@ def main():
                     help="time only this multi-head sublayer workload (one JSON line)")
     ap.add_argument("--context", action="store_true",
                     help="time a library bf16 GEMM (the matrix-core ceiling) beside this library")
+    ap.add_argument("--context-gemm-shapes", action="store_true",
+                    help="run library GEMMs of the sublayer's projection shapes (for a kernel trace)")
     args = ap.parse_args()
 
     if args.rocprof_summary:
@@ -820,6 +857,9 @@ def main():
 
     if args.context:
         print(json.dumps(context()), flush=True)
+        return
+    if args.context_gemm_shapes:
+        print(json.dumps(context_gemm_shapes()), flush=True)
         return
     if args.backward:
         print(json.dumps({"workload": args.backward, "pass": "backward",
