@@ -39,6 +39,11 @@ CASES = [  # id, (B, h, n, m, d_k, d_v), options
     ("dk32_dv64_one_by_one", (2, 1, 1, 1, 32, 64), dict(key_lens=(0, 1))),
     ("d16_four_wave_blocks", (8, 16, 1024, 1024, 16, 16), dict(causal=True)),
     ("dk32_dv64_four_wave_blocks", (8, 16, 1024, 1024, 32, 64), dict(causal=True)),
+    # windows and empty key lengths on the sentence-length kernel (n, m <= 64)
+    ("dk16_dv64_short_window", (4, 2, 40, 64, 16, 64), dict(window=(5, 3), key_lens=(0, 64))),
+    ("dk32_dv64_short_bottom_right", (4, 2, 7, 60, 32, 64), dict(window=(None, 0, "bottom_right"), key_lens=(0, 60))),
+    ("d16_short_window_ragged", (3, 4, 50, 50, 16, 16), dict(window=(9, 2), key_lens=(0, 50))),
+    ("dk32_dv64_short_right_only", (2, 3, 64, 33, 32, 64), dict(window=(None, 4), key_lens=(1, 33))),
     # row (A)'s single head of 512
     ("A_h1_d512_encoder", (64, 1, 64, 64, 512, 512), dict(key_lens=(8, 64))),
     ("A_d512_decoder", (16, 1, 64, 64, 512, 512), dict(causal=True, key_lens=(8, 64))),
@@ -85,7 +90,7 @@ def test_table3_width_parity(gpu_lib, i):
     assert err <= TOL["bf16"]
 
 
-LSE_CASES = [0, 1, 5, 9, 17, 20, 22]
+LSE_CASES = [0, 1, 5, 9, 17, 18, 19, 20, 21, 24, 26]
 
 
 @pytest.mark.parametrize("i", LSE_CASES, ids=[CASES[i][0] for i in LSE_CASES])
