@@ -361,7 +361,7 @@ SDPA_API int sdpa_backward(const void* q, const void* k, const void* v, const vo
  *            (j mod 32) of word ⌊j/32⌋ of row (b, head, i) is 1 to keep
  *            weight (i, j).  Bits of illegal keys and past m are ignored.
  * keep_scale finite and > 0 (else SDPA_ERR_SCALE).
- * dtype SDPA_BF16 and d_k == d_v == 64 only (else SDPA_ERR_UNSUPPORTED).  out
+ * dtype SDPA_BF16 and d_k == d_v ∈ {32, 64, 128} only (else SDPA_ERR_UNSUPPORTED).  out
  * and lse must not overlap the mask or the inputs (SDPA_ERR_ALIAS).
  *
  * sdpa_backward_dropout: the gradient of that forward pass for the same mask

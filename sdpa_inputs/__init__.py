@@ -247,14 +247,15 @@ def grad_output(wl: Workload, dtype: str = "bf16") -> np.ndarray:
     return round_to_bf16(do) if dtype == "bf16" else do
 
 
-def backward_case(seed: int, B, h, n, m, causal=False, key_lens=None, window=None, dtype="bf16"):
-    """Free-shape case for the backward pass: ``random_case`` (q, k, v) from
-    ``default_rng(seed)``, then dO [B, h, n, 64] from the same generator, all
-    N(0, 1) (bf16-rounded for dtype "bf16", fp32 as drawn for "f32")."""
+def backward_case(seed: int, B, h, n, m, causal=False, key_lens=None, window=None, dtype="bf16", d=64):
+    """Free-shape case for the backward pass: ``random_case`` (q, k, v with
+    d_k = d_v = d) from ``default_rng(seed)``, then dO [B, h, n, d] from the
+    same generator, all N(0, 1) (bf16-rounded for dtype "bf16", fp32 as drawn
+    for "f32")."""
     rng = np.random.default_rng(seed)
-    c = random_case(rng, B, h, n, m, 64, 64, dtype=dtype, causal=causal, key_lens=key_lens,
+    c = random_case(rng, B, h, n, m, d, d, dtype=dtype, causal=causal, key_lens=key_lens,
                     window=window)
-    do = rng.standard_normal((B, h, n, 64), dtype=np.float32)
+    do = rng.standard_normal((B, h, n, d), dtype=np.float32)
     c["do"] = round_to_bf16(do) if dtype == "bf16" else do
     return c
 

@@ -473,8 +473,11 @@ def call_fwd_drop(**kw):
     (dict(keep=None), _lib.SDPA_ERR_NULL),
     (dict(q=None), _lib.SDPA_ERR_NULL),
     (dict(dtype=0), _lib.SDPA_ERR_UNSUPPORTED),                  # bf16 only
-    (dict(d_k=32, d_v=32), _lib.SDPA_ERR_UNSUPPORTED),           # width 64 only
+    (dict(d_k=16, d_v=16), _lib.SDPA_ERR_UNSUPPORTED),           # equal widths 32, 64, 128 only
+    (dict(d_k=512, d_v=512), _lib.SDPA_ERR_UNSUPPORTED),
     (dict(d_k=16, d_v=64), _lib.SDPA_ERR_UNSUPPORTED),
+    (dict(d_k=32, d_v=64), _lib.SDPA_ERR_UNSUPPORTED),
+    (dict(d_k=32, d_v=32, dtype=0), _lib.SDPA_ERR_UNSUPPORTED),
     (dict(dtype=5), _lib.SDPA_ERR_DTYPE),
     (dict(keep_scale=0.0), _lib.SDPA_ERR_SCALE),
     (dict(keep_scale=-1.0), _lib.SDPA_ERR_SCALE),
@@ -509,7 +512,9 @@ def call_bwd_drop(**kw):
     (dict(dout=None), _lib.SDPA_ERR_NULL),
     (dict(dtype=0), _lib.SDPA_ERR_UNSUPPORTED),
     (dict(dtype=7), _lib.SDPA_ERR_DTYPE),
-    (dict(d_k=128, d_v=128), _lib.SDPA_ERR_UNSUPPORTED),  # the backward takes 128; dropout does not
+    (dict(d_k=16, d_v=16), _lib.SDPA_ERR_UNSUPPORTED),    # equal widths 32, 64, 128 only
+    (dict(d_k=512, d_v=512), _lib.SDPA_ERR_UNSUPPORTED),
+    (dict(d_k=128, d_v=128, dtype=0), _lib.SDPA_ERR_UNSUPPORTED),
     (dict(keep_scale=math.inf), _lib.SDPA_ERR_SCALE),
     (dict(keep=11 * P + 1), _lib.SDPA_ERR_ALIGN),
     (dict(ws_bytes=8), _lib.SDPA_ERR_WORKSPACE),

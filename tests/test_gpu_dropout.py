@@ -1,4 +1,5 @@
-"""Attention dropout on the GPU (bf16, d = 64) against the fp64 dropout oracle.
+"""Attention dropout on the GPU (bf16, d_k = d_v = 32, 64 or 128) against the
+fp64 dropout oracle.
 
 The pages train with dropout and tune an attention dropout (《Attention Is All
 You Need：注意力就是你所需要的一切》 §5.4, §6.3) without placing it; the
@@ -16,6 +17,9 @@ proportional to |O|, and the kept terms of O carry the factor c (on the
 bottom-right decoder case an fp64 evaluation that rounds only O to bf16
 before D accounts for 6.6e-3 of the kernel's 7.5e-3 on dK).  Where each
 dropped weight's place is known (V = I), the zero pattern is compared exactly.
+Width 64 runs through the 64-wide tiled kernel, widths 32 and 128 through the
+kernel written for the other head widths; the cases cover both, with their
+two launch shapes (2 and 4 waves per workgroup).
 """
 
 import numpy as np
@@ -39,7 +43,22 @@ CASES = [  # id, (B, h, n, m), options, p
     ("bottom_right_decode", (2, 2, 5, 200), dict(window=(None, 0, "bottom_right"), key_lens=[150, 3]), 0.1),
     ("single_query_key", (3, 1, 1, 1), {}, 0.5),
     ("four_wave_blocks", (4, 16, 1100, 1100), dict(causal=True), 0.1),
+    ("w32_encoder_padded", (8, 4, 64, 64), dict(d=32, key_lens=[64, 8, 33, 50, 64, 1, 0, 40]), 0.1),
+    ("w128_decoder_causal", (4, 4, 64, 64), dict(d=128, causal=True), 0.5),
+    ("w32_multi_tile_causal", (2, 2, 300, 300), dict(d=32, causal=True, key_lens=[260, 300]), 0.1),
+    ("w128_window_ragged_words", (2, 2, 300, 270), dict(d=128, window=(40, 8), key_lens=[270, 211]), 0.2),
+    ("w128_bottom_right_decode", (2, 2, 5, 200), dict(d=128, window=(None, 0, "bottom_right"), key_lens=[150, 3]),
+     0.1),
+    ("w32_single_query_key", (3, 1, 1, 1), dict(d=32), 0.5),
+    ("w128_four_wave_blocks", (2, 64, 1100, 1100), dict(d=128, causal=True), 0.1),
+    ("w32_four_wave_blocks", (2, 64, 1100, 1100), dict(d=32, window=(300, 0)), 0.3),
 ]
+LARGE = 1 << 24  # B·h·n·m above this: forward only, three whole heads against the oracle
+
+
+def _large(i):
+    B, h, n, m = CASES[i][1]
+    return B * h * n * m > LARGE
 
 
 def _case(i):
@@ -84,7 +103,7 @@ def test_dropout_forward_parity(gpu_lib, i):
     got = from_device(out)
     B, h, n, m = CASES[i][1]
     kw = dict(causal=c["causal"], key_lens=c["key_lens"], window=c["window"])
-    if B * h * n * m > 1 << 24:  # large: three whole heads
+    if _large(i):  # three whole heads
         errs = []
         for b, hh in ((0, 0), (B - 1, h - 1), (1, 5)):
             one = lambda x: x[b:b + 1, hh:hh + 1]  # noqa: E731
@@ -99,7 +118,7 @@ def test_dropout_forward_parity(gpu_lib, i):
     print(f"dropout fwd {CASES[i][0]}: max abs err {err:.2e} (c = {c['keep_scale']:.3f})")
     assert err <= TOL["bf16"] * c["keep_scale"]
     # the softmax (and so lse) does not see the mask
-    if B * h * n * m <= 1 << 24:
+    if not _large(i):
         ref_l = sb.log_sum_exp(c["q"], c["k"], **kw)
         got_l = lse.cpu().numpy().astype(np.float64)
         inf = np.isinf(ref_l)
@@ -107,7 +126,10 @@ def test_dropout_forward_parity(gpu_lib, i):
         assert max_abs_err(got_l[~inf], ref_l[~inf]) <= 2.0 ** -8
 
 
-@pytest.mark.parametrize("i", [0, 1, 2, 3, 4, 5, 6], ids=[CASES[i][0] for i in range(7)])
+BWD = [i for i in range(len(CASES)) if not _large(i)]
+
+
+@pytest.mark.parametrize("i", BWD, ids=[CASES[i][0] for i in BWD])
 def test_dropout_backward_parity(gpu_lib, i):
     c = _case(i)
     _, _, grads = _run(c, backward=True)
@@ -122,15 +144,16 @@ def test_dropout_backward_parity(gpu_lib, i):
     print(f"dropout bwd {CASES[i][0]}: " + ", ".join(msgs))
 
 
-@pytest.mark.parametrize("m", [64, 45])
-def test_dropout_pattern_is_exact(gpu_lib, m):
+@pytest.mark.parametrize("d,m", [(64, 64), (64, 45), (32, 32), (128, 100)])
+def test_dropout_pattern_is_exact(gpu_lib, d, m):
     """V = I (m ≤ d_v) makes the output row i the dropped weights themselves:
     exactly 0 wherever Z_ij = 0 or the key is illegal, positive elsewhere."""
     B, h, n = 4, 3, 64
-    c = backward_case(9300 + m, B, h, n, m, causal=m == n, key_lens=[m, 17, 1, m - 5])
+    seed = 9300 + m if d == 64 else 9350 + d
+    c = backward_case(seed, B, h, n, m, causal=m == n, key_lens=[m, 17, 1, m - 5], d=d)
     c["v"] = np.zeros_like(c["v"])
     c["v"][:, :, np.arange(m), np.arange(m)] = 1.0
-    rng = np.random.default_rng(9400 + m)
+    rng = np.random.default_rng(9400 + m if d == 64 else 9450 + d)
     c["keep"] = random_keep(rng, B, h, n, m, 0.4)
     c["keep_scale"] = 1.0 / 0.6
     out, _, _ = _run(c)
@@ -142,14 +165,15 @@ def test_dropout_pattern_is_exact(gpu_lib, m):
     assert max_abs_err(got, ref) <= TOL["bf16"] * c["keep_scale"]
 
 
-def test_all_kept_equals_plain_bitwise(gpu_lib):
+@pytest.mark.parametrize("d", [32, 64, 128])
+def test_all_kept_equals_plain_bitwise(gpu_lib, d):
     """Every weight kept and c = 1: the same arithmetic as the plain tiled
     path (n, m > 64), so output, lse and gradients agree bit for bit."""
     import torch
 
     from transformer_attention_sdpa_amd import backward, backward_dropout, forward, forward_dropout
 
-    c = backward_case(9500, 2, 4, 200, 260, key_lens=[260, 101])
+    c = backward_case(9500 if d == 64 else 9500 + d, 2, 4, 200, 260, key_lens=[260, 101], d=d)
     q, k, v, do = (to_device(c[x], "bf16") for x in ("q", "k", "v", "do"))
     kl = torch.from_numpy(np.asarray(c["key_lens"], np.int32)).cuda()
     ones = torch.full((2, 4, 200, (260 + 31) // 32), -1, dtype=torch.int32, device="cuda")
@@ -186,10 +210,10 @@ def test_dropout_wrapper_errors(gpu_lib):
 
     from transformer_attention_sdpa_amd import forward_dropout
 
-    q = torch.zeros(1, 1, 8, 32, device="cuda", dtype=torch.bfloat16)
+    q = torch.zeros(1, 1, 8, 16, device="cuda", dtype=torch.bfloat16)
     mask = torch.zeros(1, 1, 8, 1, dtype=torch.int32, device="cuda")
     with pytest.raises(RuntimeError, match="unsupported"):
-        forward_dropout(q, q, q, mask, 1.0)  # width 32: the dropout kernels take 64
+        forward_dropout(q, q, q, mask, 1.0)  # width 16: the dropout kernels take 32, 64, 128
     q64 = torch.zeros(1, 1, 8, 64, device="cuda", dtype=torch.bfloat16)
     with pytest.raises(RuntimeError, match="scale"):
         forward_dropout(q64, q64, q64, mask, float("inf"))

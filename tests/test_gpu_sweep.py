@@ -11,7 +11,8 @@ with either side open and either alignment), per-sequence key lengths from 0
 to past m, the caller's layout (packed, or token-major views through
 sdpa_forward_strided), the log-sum-exp output and the split-key workspace.
 The gradient cases draw the backward widths (bf16 32, 64, 128; fp32 64) and
-the dropout cases a keep probability.  Every case prints its draw, so a
+the dropout cases a keep probability and a width (32, 64 or 128, from a stream
+of their own so that the other draws of a case do not depend on it).  Every case prints its draw, so a
 failure names it.
 
 Bars: the forward ones of the other parity tests (2e-2 bf16, 1e-5 fp32
@@ -207,11 +208,12 @@ def test_dropout_sweep(gpu_lib, i):
     causal, window = _mask(rng, n, m)
     kl = rng.integers(0, m + 4, size=B).astype(np.int32) if rng.random() < 0.6 else None
     p = float(rng.uniform(0.05, 0.5))
-    c = random_case(rng, B, h, n, m, 64, 64, dtype="bf16", causal=causal, key_lens=kl, window=window)
-    c["do"] = round_to_bf16(rng.standard_normal((B, h, n, 64), dtype=np.float32))
+    d = int(np.random.default_rng([SEED, 2500 + i]).choice([32, 64, 64, 128]))
+    c = random_case(rng, B, h, n, m, d, d, dtype="bf16", causal=causal, key_lens=kl, window=window)
+    c["do"] = round_to_bf16(rng.standard_normal((B, h, n, d), dtype=np.float32))
     keep = random_keep(rng, B, h, n, m, p)
     ks = 1.0 / (1.0 - p)
-    print(f"dropout case {i}: B={B} h={h} n={n} m={m} p={p:.2f} causal={causal} window={window} "
+    print(f"dropout case {i}: B={B} h={h} n={n} m={m} d={d} p={p:.2f} causal={causal} window={window} "
           f"key_lens={None if kl is None else kl.tolist()}", flush=True)
     q, k, v, do = (to_device(c[x], "bf16") for x in ("q", "k", "v", "do"))
     mask = torch.from_numpy(pack_keep(keep).view(np.int32)).cuda()

@@ -328,8 +328,8 @@ def forward_dropout(q, k, v, keep_mask, keep_scale: float, *, causal: bool = Fal
                     scale: float | None = None, window=None, out=None, return_lse: bool = False):
     """Eq. (1) with attention dropout: O = (P ∘ Z) V · keep_scale, the keep
     mask Z as ``dropout_keep_mask`` packs it (pass keep_scale = 1/(1 − p)).
-    bf16, d_k = d_v = 64, packed [B, h, len, 64] tensors; other arguments as
-    in ``forward``.  lse (with ``return_lse``) is the softmax's, unchanged by
+    bf16, d_k = d_v = 32, 64 or 128, packed [B, h, len, d] tensors; other
+    arguments as in ``forward``.  lse (with ``return_lse``) is the softmax's, unchanged by
     the mask, and is what ``backward_dropout`` takes."""
     import torch
 

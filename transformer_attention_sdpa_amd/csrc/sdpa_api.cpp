@@ -13,7 +13,7 @@
 
 namespace {
 
-constexpr int kVersion = 1 * 10000 + 7 * 100 + 0;  // 1.7.0: fp32 log-sum-exp and gradient
+constexpr int kVersion = 1 * 10000 + 8 * 100 + 0;  // 1.8.0: dropout at widths 32 and 128
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -237,7 +237,7 @@ uint64_t keep_bytes(int32_t B, int32_t h, int32_t n, int32_t m) {
 // The mask, its factor and the widths the dropout kernels take.
 int validate_dropout(const uint32_t* keep, float keep_scale, int32_t d_k, int32_t d_v, int32_t dtype) {
     if (!keep) return SDPA_ERR_NULL;
-    if (dtype != SDPA_BF16 || d_k != sdpa::kHeadDim || d_v != sdpa::kHeadDim) return SDPA_ERR_UNSUPPORTED;
+    if (dtype != SDPA_BF16 || d_k != d_v || (d_k != 32 && d_k != 64 && d_k != 128)) return SDPA_ERR_UNSUPPORTED;
     if (!std::isfinite(keep_scale) || !(keep_scale > 0.f)) return SDPA_ERR_SCALE;
     if (reinterpret_cast<uintptr_t>(keep) & 3u) return SDPA_ERR_ALIGN;
     return SDPA_OK;
@@ -564,9 +564,9 @@ extern "C" const char* sdpa_strerror(int status) {
         case SDPA_ERR_SHAPE: return "bad shape: a dimension is < 1 or an element count overflows";
         case SDPA_ERR_UNSUPPORTED:
             return "unsupported: head widths are d_k = d_v = 64; bf16 attention also takes d_k = d_v = "
-                   "16, 32, 128, 512 and d_v = 64 with d_k = 16 or 32; the log-sum-exp, backward pass and "
-                   "sublayer are bf16, with d_k = d_v = 32, 64 or 128 (backward, sublayer); dropout is "
-                   "bf16 with d_k = d_v = 64";
+                   "16, 32, 128, 512 and d_v = 64 with d_k = 16 or 32; the backward pass takes d_k = d_v = "
+                   "32, 64 or 128 in bf16 and 64 in fp32; the sublayer and dropout are bf16 with d_k = d_v "
+                   "= 32, 64 or 128";
         case SDPA_ERR_ALIGN: return "a device pointer is not 16-byte aligned (key_lens: 4-byte)";
         case SDPA_ERR_MASK:
             return "bad mask: unknown mask_kind, causal with n != m, window side < -1 or unknown align";

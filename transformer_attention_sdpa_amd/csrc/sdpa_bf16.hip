@@ -471,7 +471,8 @@ hipError_t launch_bf16_long(const Args& a, hipStream_t stream) {
 hipError_t launch_bf16(const Args& a0, hipStream_t stream) {
     Args a = a0;
     if (!a.strided) a.lay = dense_layout(a.H, a.n, a.m, a.d, a.dv);  // packed layout
-    if (a.keep) return launch_bf16_long(a, stream);  // attention dropout: d_k = d_v = 64, any n, m
+    // attention dropout: d_k = d_v ∈ {32, 64, 128}, any n, m
+    if (a.keep) return a.d == D ? launch_bf16_long(a, stream) : launch_bf16_width(a, stream);
     if (short_bf16_fits(a)) return launch_bf16_short(a, stream);  // n, m <= 64, d_k = d_v ∈ {32, 64, 128}
     if (a.d != D || a.dv != D) return launch_bf16_width(a, stream);
     if (decode_bf16_fits(a)) return launch_bf16_decode(a, stream);

@@ -17,8 +17,9 @@
 // d_k = 16; at d_v = 16 the upper half of the 32-row Oᵀ block is computed
 // and dropped), one 32-query block per wave, 64-key tiles double-buffered in
 // LDS by buffer_load … lds, and an exact online softmax (the tile maximum
-// moves the reference every tile).  Key windows, key lengths and the
-// log-sum-exp output behave exactly as in the 64-wide kernels.
+// moves the reference every tile).  Key windows, key lengths, the
+// log-sum-exp output and attention dropout (at d_k = d_v = 32 and 128) behave
+// exactly as in the 64-wide kernels.
 #include "sdpa_common.hpp"
 
 namespace sdpa {
@@ -63,11 +64,15 @@ __device__ __forceinline__ void wlds_wait(u32x2 (&x)[N]) {
 }
 
 // STRIDED: runtime strides of `lay`; else the packed layout, compile-time.
-template <int DK, int DV, int NW, bool STRIDED>
+// DROP: attention dropout with keep-bit words [BH, n, ⌈m/32⌉]: the dropped
+// weights leave the P·V product but not the row sums, and the output is
+// scaled by keep_scale.
+template <int DK, int DV, int NW, bool STRIDED, bool DROP>
 __global__ __launch_bounds__(NW * 64) void sdpa_fwd_bf16_width(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ lse, int BH, int H, int n, int m, float c_log2, int wl,
-    int wr, int bottom_right, const int32_t* __restrict__ key_lens, int nqb, Layout lay) {
+    int wr, int bottom_right, const int32_t* __restrict__ key_lens, int nqb, Layout lay,
+    const uint32_t* __restrict__ keep, float keep_scale) {
     constexpr int KS = DK / 16;               // k-steps of the score product
     constexpr int DT = (DV + 31) / 32;        // 32-row blocks of Oᵀ
     constexpr int CPK = DK / 8, CPV = DV / 8; // 16-byte chunks per K / V row
@@ -112,6 +117,10 @@ __global__ __launch_bounds__(NW * 64) void sdpa_fwd_bf16_width(
     const int vr = STRIDED ? lay.v.r : DV, orr = STRIDED ? lay.o.r : DV;
     const int qrow = wq0 + l32;
     const bool qok = qrow < n;
+    // Dropout: this lane's row of keep words (rows past n read row n − 1;
+    // their outputs are not stored).
+    const int kwords = (m + 31) >> 5;
+    const uint32_t* krow = DROP ? keep + ((size_t)bh * n + min(qrow, n - 1)) * kwords : nullptr;
     // Qᵀ as the B operand: dims 16·ks + 8·hf + [0..7] of this lane's query.
     bf16x8 qop[KS];
 #pragma unroll
@@ -184,6 +193,12 @@ __global__ __launch_bounds__(NW * 64) void sdpa_fwd_bf16_width(
         const int k0 = t * BT;
         if (k0 < whi && k0 + BT > wlo) {  // uniform: some query of the wave sees the tile
             const uint32_t sk = l0 + buf * (TK + TV), sv = sk + TK;
+            uint32_t kw[2] = {0u, 0u};  // keep words of keys k0..k0+31 and k0+32..k0+63
+            if constexpr (DROP) {
+                const int w0 = k0 >> 5;
+                kw[0] = w0 < kwords ? krow[w0] : 0u;
+                kw[1] = w0 + 1 < kwords ? krow[w0 + 1] : 0u;
+            }
             f32x16 s[2];
             {
                 u32x4 a[2 * KS];
@@ -240,6 +255,13 @@ __global__ __launch_bounds__(NW * 64) void sdpa_fwd_bf16_width(
                     lsum += p[e];
                 }
                 pb[j] = to_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
+                // Dropout, after the row sum has counted the weights: element e
+                // of pb[j] is key 16·(j%2) + 4·hf + e (e < 4) or + 8 + (e − 4) of
+                // word kt.
+                if constexpr (DROP) {
+                    const uint32_t wd = kw[kt] >> (16 * (j & 1) + 4 * hf);
+                    pb[j] = keep_pairs(pb[j], (wd & 0xFu) | ((wd >> 4) & 0xF0u));
+                }
             }
             // Oᵀ += Vᵀ · Pᵀ.
             u32x2 va[4 * DT * 2];
@@ -267,7 +289,7 @@ __global__ __launch_bounds__(NW * 64) void sdpa_fwd_bf16_width(
     // Oᵀ / l and store: register i of oacc[dt] is dim 32·dt + 8·(i/4) + 4·hf + i%4.
     const float ltot = half_swap_sum(lsum);
     // no legal key ⇒ zero row; a NaN sum (NaN legal inputs) stays NaN
-    const float inv = ltot != 0.f ? 1.f / ltot : 0.f;
+    const float inv = ltot != 0.f ? (DROP ? keep_scale : 1.f) / ltot : 0.f;
     if (qok && lse && hf == 0) {
         const float mc = (mref == -INFINITY ? 0.f : mref) * c_log2;
         lse[(size_t)bh * n + qrow] = (mc + log2f(ltot)) * 0.6931471805599453f;
@@ -302,25 +324,27 @@ __global__ __launch_bounds__(NW * 64) void sdpa_fwd_bf16_width(
     }
 }
 
-template <int DK, int DV>
-hipError_t launch_width(const Args& a, hipStream_t stream) {
+template <int DK, int DV, int NW>
+hipError_t launch_width_nw(const Args& a, hipStream_t stream) {
     const int BH = a.B * a.H;
     const float c_log2 = (float)((double)a.scale * 1.4426950408889634);  // scale·log2(e)
-    // 4 waves (128 queries) per workgroup once there are enough blocks.
-    if ((long long)BH * ((a.n + 127) / 128) >= 1024) {
-        const int nqb = (a.n + 127) / 128;
-        const auto kernel = a.strided ? sdpa_fwd_bf16_width<DK, DV, 4, true> : sdpa_fwd_bf16_width<DK, DV, 4, false>;
-        hipLaunchKernelGGL(kernel, dim3(nqb * BH), dim3(256), 0, stream,
-                           (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.out,
-                           a.lse, BH, a.H, a.n, a.m, c_log2, a.wl, a.wr, a.bottom_right, a.key_lens, nqb, a.lay);
-    } else {
-        const int nqb = (a.n + 63) / 64;
-        const auto kernel = a.strided ? sdpa_fwd_bf16_width<DK, DV, 2, true> : sdpa_fwd_bf16_width<DK, DV, 2, false>;
-        hipLaunchKernelGGL(kernel, dim3(nqb * BH), dim3(128), 0, stream,
-                           (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.out,
-                           a.lse, BH, a.H, a.n, a.m, c_log2, a.wl, a.wr, a.bottom_right, a.key_lens, nqb, a.lay);
-    }
+    const int nqb = (a.n + 32 * NW - 1) / (32 * NW);
+    const auto kernel = a.keep ? (a.strided ? sdpa_fwd_bf16_width<DK, DV, NW, true, true>
+                                            : sdpa_fwd_bf16_width<DK, DV, NW, false, true>)
+                               : (a.strided ? sdpa_fwd_bf16_width<DK, DV, NW, true, false>
+                                            : sdpa_fwd_bf16_width<DK, DV, NW, false, false>);
+    hipLaunchKernelGGL(kernel, dim3(nqb * BH), dim3(NW * 64), 0, stream,
+                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.out,
+                       a.lse, BH, a.H, a.n, a.m, c_log2, a.wl, a.wr, a.bottom_right, a.key_lens, nqb, a.lay,
+                       a.keep, a.keep_scale);
     return hipGetLastError();
+}
+
+template <int DK, int DV>
+hipError_t launch_width(const Args& a, hipStream_t stream) {
+    // 4 waves (128 queries) per workgroup once there are enough blocks.
+    if ((long long)a.B * a.H * ((a.n + 127) / 128) >= 1024) return launch_width_nw<DK, DV, 4>(a, stream);
+    return launch_width_nw<DK, DV, 2>(a, stream);
 }
 
 }  // namespace
