@@ -324,13 +324,16 @@ def backward_work(wl, key_lens, dtype="bf16"):
     return flops, nbytes
 
 
-def time_backward(name, steps, warmup, clock_warm_s=0.1, dtype="bf16"):
-    """sdpa_backward (two launches per step) on a workload, in bf16 or fp32,
-    with the forward output and log-sum-exp computed once beforehand."""
+def time_backward(name, steps, warmup, clock_warm_s=0.1, dtype="bf16", dropout=0.0):
+    """sdpa_backward on a workload, in bf16 or fp32, with the forward output
+    and log-sum-exp computed once beforehand (one fused launch per step at
+    sentence length in bf16, else the dQ and dK/dV launches).  With dropout
+    p > 0: sdpa_forward_dropout / sdpa_backward_dropout with a seeded keep mask
+    (keep probability 1 − p, factor 1/(1 − p)), whose words count as read."""
     import numpy as np
     import torch
 
-    from sdpa_inputs import bf16_bits, grad_output
+    from sdpa_inputs import bf16_bits, grad_output, pack_keep, random_keep
     from transformer_attention_sdpa_amd import _lib
 
     wl = WORKLOADS[name]
@@ -356,6 +359,12 @@ def time_backward(name, steps, warmup, clock_warm_s=0.1, dtype="bf16"):
         walign = (_lib.SDPA_ALIGN_BOTTOM_RIGHT if len(wl.window) > 2 and wl.window[2] == "bottom_right"
                   else _lib.SDPA_ALIGN_TOP_LEFT)
     flops, nbytes = backward_work(wl, case["key_lens"], dtype)
+    keep0, keep_scale = None, 1.0
+    if dropout > 0:
+        keep0 = torch.from_numpy(pack_keep(random_keep(np.random.default_rng(1234), B, h, n, m, dropout))
+                                 .view(np.int32)).to(dev)
+        keep_scale = 1.0 / (1.0 - dropout)
+        nbytes += keep0.numel() * 4
     nsets = max(1, min(64, math.ceil(2 * INFINITY_CACHE_BYTES / nbytes)))
     need = _lib.sdpa_backward_workspace_bytes(B, h, n)
     stream = torch.cuda.current_stream(dev).cuda_stream
@@ -364,19 +373,31 @@ def time_backward(name, steps, warmup, clock_warm_s=0.1, dtype="bf16"):
         q, k, v, do = q0.clone(), k0.clone(), v0.clone(), do0.clone()
         o = torch.empty((B, h, n, d), dtype=tdt, device=dev)
         lse = torch.empty((B, h, n), dtype=torch.float32, device=dev)
-        rc = _lib.sdpa_forward_lse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                                   B, h, n, m, d, d, scale, wleft, wright, walign, kl_ptr, cdt, stream)
+        keep = None if keep0 is None else keep0.clone()
+        if keep is None:
+            rc = _lib.sdpa_forward_lse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                       B, h, n, m, d, d, scale, wleft, wright, walign, kl_ptr, cdt, stream)
+        else:
+            rc = _lib.sdpa_forward_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                           B, h, n, m, d, d, scale, wleft, wright, walign, kl_ptr,
+                                           keep.data_ptr(), keep_scale, cdt, stream)
         if rc != _lib.SDPA_OK:
             raise RuntimeError(_lib.sdpa_strerror(rc))
         grads = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)]
         ws = torch.empty(need, dtype=torch.uint8, device=dev)
-        sets.append((q, k, v, o, do, lse, *grads, ws))
+        sets.append((q, k, v, o, do, lse, *grads, ws, keep))
 
     def launch(i, st):
-        q, k, v, o, do, lse, dq, dk, dv, ws = sets[i % nsets]
-        rc = _lib.sdpa_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
-                                lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, h, n, m,
-                                d, d, scale, wleft, wright, walign, kl_ptr, cdt, ws.data_ptr(), need, st)
+        q, k, v, o, do, lse, dq, dk, dv, ws, keep = sets[i % nsets]
+        if keep is None:
+            rc = _lib.sdpa_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                                    lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, h, n, m,
+                                    d, d, scale, wleft, wright, walign, kl_ptr, cdt, ws.data_ptr(), need, st)
+        else:
+            rc = _lib.sdpa_backward_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                            do.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                            dv.data_ptr(), B, h, n, m, d, d, scale, wleft, wright, walign,
+                                            kl_ptr, keep.data_ptr(), keep_scale, cdt, ws.data_ptr(), need, st)
         if rc != _lib.SDPA_OK:
             raise RuntimeError(_lib.sdpa_strerror(rc))
 
@@ -404,7 +425,9 @@ def time_backward(name, steps, warmup, clock_warm_s=0.1, dtype="bf16"):
             "alg_flops": flops, "alg_bytes": nbytes,
             "frac_mfma_peak": flops / t / 1e12 / PEAK_TFLOPS[dtype],
             "frac_hbm_peak": nbytes / t / 1e9 / PEAK_HBM_GBS, "steps": steps, "sets_rotated": nsets,
-            "launches_per_step": 2}
+            "launches_per_step": (1 if dtype == "bf16" and n <= 64 and m <= 64
+                                  else 3 if dtype == "bf16" and d == 128 else 2),
+            "dropout": dropout}
 
 
 def mha_work(args, key_lens):
@@ -829,8 +852,11 @@ def main():
                                                         "COPY_WRITE_DB"),
                     help="print the per-launch HBM traffic record of --kernel and exit")
     ap.add_argument("--kernel", default="sdpa_short_bf16", help="kernel name for --traffic-json")
-    ap.add_argument("--backward", choices=["encoder_self_base", "decoder_causal_base", "long_causal_8k"],
+    ap.add_argument("--backward", choices=["encoder_self_base", "decoder_causal_base", "long_causal_8k",
+                                           "encoder_h16_d32", "encoder_h4_d128"],
                     help="time only the backward pass of this workload (one JSON line)")
+    ap.add_argument("--dropout", type=float, default=0.0,
+                    help="with --backward: attention dropout probability of the timed pass")
     ap.add_argument("--mha", choices=["mha_encoder_base", "mha_cross_big"],
                     help="time only this multi-head sublayer workload (one JSON line)")
     ap.add_argument("--context", action="store_true",
@@ -864,7 +890,8 @@ def main():
     if args.backward:
         print(json.dumps({"workload": args.backward, "pass": "backward",
                           "dtype": args.dtype,
-                          **time_backward(args.backward, args.steps, args.warmup, dtype=args.dtype)}), flush=True)
+                          **time_backward(args.backward, args.steps, args.warmup, dtype=args.dtype,
+                                          dropout=args.dropout)}), flush=True)
         return
     if args.mha:
         print(json.dumps({"workload": args.mha, **time_mha(args.mha, args.steps, args.warmup)}), flush=True)
@@ -908,6 +935,10 @@ def main():
                 extra[f"backward-{name}-{dt}"] = time_backward(
                     name, (20 if dt == "bf16" else 5) if name.endswith("_8k") else max(10, min(args.steps, 200)),
                     min(args.warmup, 3), dtype=dt)
+        # Table 3 widths and attention dropout (p = 0.1) at sentence length
+        for name, p in (("encoder_h16_d32", 0.0), ("encoder_h4_d128", 0.0), ("encoder_self_base", 0.1)):
+            key = f"backward-{name}-bf16" + (f"-dropout{p}" if p else "")
+            extra[key] = time_backward(name, max(10, min(args.steps, 200)), min(args.warmup, 3), dropout=p)
         for name in ("mha_encoder_base", "mha_cross_big"):
             extra[f"{name}-bf16"] = time_mha(name, max(10, min(args.steps, 200)),
                                              min(args.warmup, 5))

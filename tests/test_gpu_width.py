@@ -116,6 +116,13 @@ BWD_CASES = [  # id, (B, h, n, m, d), options
     ("d32_window_ragged", (2, 2, 200, 230, 32), dict(window=(30, 10), key_lens=(100, 230))),
     ("d128_bottom_right", (2, 2, 5, 200, 128), dict(window=(None, 0, "bottom_right"), key_lens=(0, 200))),
     ("d128_cross_padded", (3, 2, 70, 130, 128), dict(key_lens=(1, 130))),
+    # sentence length (n, m <= 64): the fused one-launch kernel at both widths
+    ("d32_short_causal_padded", (4, 3, 64, 64, 32), dict(causal=True, key_lens=(0, 64))),
+    ("d128_short_window", (3, 2, 64, 64, 128), dict(window=(5, 3), key_lens=(1, 64))),
+    ("d32_short_bottom_right", (3, 2, 7, 50, 32), dict(window=(None, 0, "bottom_right"), key_lens=(0, 60))),
+    ("d128_short_ragged_cross", (2, 3, 33, 17, 128), dict(key_lens=(0, 20))),
+    ("d32_short_n_gt_m", (2, 2, 64, 9, 32), {}),
+    ("d128_short_one_by_one", (2, 1, 1, 1, 128), dict(key_lens=(0, 1))),
 ]
 
 
@@ -150,6 +157,40 @@ def test_width_backward_parity(gpu_lib, i):
         msg.append(f"{what} {err:.2e}/{np.abs(r).max():.2e}")
         assert np.all(np.isfinite(g)) and err <= bound, (name, what, err, bound)
     print(f"width bwd {name}: " + ", ".join(msg))
+
+
+@pytest.mark.parametrize("d", [32, 128])
+def test_short_width_backward_ignores_rows_past_key_length(gpu_lib, d):
+    """The fused sentence-length gradient: NaN in the K and V rows at or past
+    each key length changes no bit of the gradients, and those rows' dK, dV
+    are exactly zero."""
+    import torch
+
+    from transformer_attention_sdpa_amd import backward, forward
+
+    c = _case(130 + d, (3, 2, 48, 64, d), dict(key_lens=np.array([64, 21, 0], np.int32)))
+    rng = np.random.default_rng(8600 + d)
+    from sdpa_inputs import round_to_bf16
+
+    do_ = round_to_bf16(rng.standard_normal((3, 2, 48, d), dtype=np.float32))
+    kl = torch.from_numpy(c["key_lens"]).cuda()
+
+    def run():
+        q, k, v, do = (to_device(x, "bf16") for x in (c["q"], c["k"], c["v"], do_))
+        out, lse = forward(q, k, v, key_lens=kl, return_lse=True)
+        g = backward(q, k, v, out, do, lse, key_lens=kl)
+        torch.cuda.synchronize()
+        return [x.view(torch.int16).cpu() for x in g]
+
+    clean = run()
+    for b, L in enumerate(c["key_lens"]):
+        c["k"][b, :, L:] = np.nan
+        c["v"][b, :, L:] = np.nan
+    dirty = run()
+    for x, y in zip(clean, dirty):
+        assert torch.equal(x, y)
+    for b, L in enumerate(c["key_lens"]):
+        assert torch.all(dirty[1][b, :, L:] == 0) and torch.all(dirty[2][b, :, L:] == 0)
 
 
 def test_width_backward_deterministic(gpu_lib):

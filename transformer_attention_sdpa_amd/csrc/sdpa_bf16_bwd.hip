@@ -41,7 +41,6 @@ namespace sdpa {
 namespace {
 
 constexpr int BT = 64;                          // rows per LDS tile
-constexpr int TILE_BYTES = BT * kHeadDim * 2;   // 8 KiB at width 64 (the fused kernel)
 template <int D>
 constexpr int tile_bytes() { return BT * D * 2; }
 
@@ -201,16 +200,18 @@ __device__ __forceinline__ void store_rowT(uint16_t* dst, const f32x16 (&acc)[D 
         }
 }
 
-// Store 32 output rows through a wave-private 4 KiB LDS area: the transposed
-// accumulators (register i of acc[dt] is column 32·dt + 8·(i/4) + 4·hf + i%4
-// of row l32) go in as bf16 times `mul`, and come out 16 bytes a lane, so
-// that each store instruction writes eight whole 128-byte rows instead of 32
-// scattered 16-byte pieces.  Rows at or past `nrows` are not written.
-__device__ __forceinline__ void store_rows_lds(char* area, const f32x16 (&acc)[2], int lane, float mul,
+// Store 32 output rows of width D through a wave-private LDS area of 64·D
+// bytes: the transposed accumulators (register i of acc[dt] is column 32·dt +
+// 8·(i/4) + 4·hf + i%4 of row l32) go in as bf16 times `mul`, and come out 16
+// bytes a lane, so that each store instruction writes whole rows instead of
+// 32 scattered 8-byte pieces.  Rows at or past `nrows` are not written.
+template <int D>
+__device__ __forceinline__ void store_rows_lds(char* area, const f32x16 (&acc)[D / 32], int lane, float mul,
                                                uint16_t* dst, int nrows) {
+    constexpr int CPR = D / 8;  // 16-byte chunks per row
     const int l32 = lane & 31, hf = lane >> 5;
 #pragma unroll
-    for (int dt = 0; dt < 2; ++dt)
+    for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
             const int col = 32 * dt + 8 * i4 + 4 * hf;
@@ -219,13 +220,13 @@ __device__ __forceinline__ void store_rows_lds(char* area, const f32x16 (&acc)[2
             o[1] = (__bf16)(acc[dt][4 * i4 + 1] * mul);
             o[2] = (__bf16)(acc[dt][4 * i4 + 2] * mul);
             o[3] = (__bf16)(acc[dt][4 * i4 + 3] * mul);
-            *reinterpret_cast<bf16x4*>(area + lds_swz(l32, col >> 3) * 16 + (col & 7) * 2) = o;
+            *reinterpret_cast<bf16x4*>(area + bswz<D>(l32, col >> 3) * 16 + (col & 7) * 2) = o;
         }
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const int row = 8 * k + (lane >> 3), c = lane & 7;
-        const u32x4 x = *reinterpret_cast<const u32x4*>(area + lds_swz(row, c) * 16);
-        if (row < nrows) store16_nt(dst + (size_t)row * kHeadDim + 8 * c, x);
+    for (int k = 0; k < D / 16; ++k) {
+        const int row = (64 / CPR) * k + lane / CPR, c = lane % CPR;
+        const u32x4 x = *reinterpret_cast<const u32x4*>(area + bswz<D>(row, c) * 16);
+        if (row < nrows) store16_nt(dst + (size_t)row * D + 8 * c, x);
     }
 }
 
@@ -598,20 +599,25 @@ __global__ __launch_bounds__(NW * 64) void sdpa_bwd_dkdv_bf16(
 
 // ---------------------------------------------------------------------------
 // Sentence length (n, m ≤ 64): one workgroup per head, one launch.  The
-// head's Q, dO, K and V (8 KiB each) are copied into LDS once; waves 2 and 3
-// take the dQ role for queries 0..31 and 32..63 (and first publish D and
-// lse·log2 e of their rows through LDS), waves 0 and 1 the dK/dV role for keys
-// 0..31 and 32..63.  Each role is one tile of the two kernels above.
+// head's Q, dO, K and V (64·D·2 bytes each) are copied into LDS once; waves 2
+// and 3 take the dQ role for queries 0..31 and 32..63 (and first publish D
+// and lse·log2 e of their rows through LDS), waves 0 and 1 the dK/dV role for
+// keys 0..31 and 32..63.  Each role is one tile of the two kernels above.
+// DROP: the head's keep words (at most 64 rows of 2) are staged in LDS as
+// [word][query], and dP, and the weights of dV, take the mask and factor as
+// in the two kernels above.
 
+template <int D, bool DROP>
 __global__ __launch_bounds__(256) void sdpa_bwd_short_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO, const float* __restrict__ lse,
     uint16_t* __restrict__ dQ, uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
     int H, int n, int m, float scale, float c_log2, int wl, int wr, int bottom_right,
-    const int32_t* __restrict__ key_lens) {
-    // [Q | dO | K | V] tiles, then lse·log2 e and D of the 64 query rows.
-    __shared__ __attribute__((aligned(1024))) char lds[4 * TILE_BYTES + 512];
-    constexpr int D = kHeadDim;
+    const int32_t* __restrict__ key_lens, const uint32_t* __restrict__ keep, float keep_scale) {
+    constexpr int TB = tile_bytes<D>(), KS = D / 16, DT = D / 32, RB = D * 2;  // RB: bytes per row
+    // [Q | dO | K | V] tiles, lse·log2 e and D of the 64 query rows, then (DROP)
+    // the keep words.
+    __shared__ __attribute__((aligned(1024))) char lds[4 * TB + 512 + (DROP ? 512 : 0)];
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
@@ -623,31 +629,39 @@ __global__ __launch_bounds__(256) void sdpa_bwd_short_bf16(
         const int t = key_lens[b];
         L = t < 0 ? 0 : (t > m ? m : t);
     }
-    // Each wave copies two of the eight 1 KiB blocks of every tile.
+    // Each wave copies a quarter of the 1 KiB blocks of every tile.
     load_tile<D, 4>(lds, Q + qbase, 0, n, w, lane);
-    load_tile<D, 4>(lds + TILE_BYTES, dO + qbase, 0, n, w, lane);
-    load_tile<D, 4>(lds + 2 * TILE_BYTES, K + kvbase, 0, L, w, lane);
-    load_tile<D, 4>(lds + 3 * TILE_BYTES, V + kvbase, 0, L, w, lane);
+    load_tile<D, 4>(lds + TB, dO + qbase, 0, n, w, lane);
+    load_tile<D, 4>(lds + 2 * TB, K + kvbase, 0, L, w, lane);
+    load_tile<D, 4>(lds + 3 * TB, V + kvbase, 0, L, w, lane);
     const KeyWindow win{wl, wr, bottom_right ? L - n : 0, L};
-    float* sl = reinterpret_cast<float*>(lds + 4 * TILE_BYTES);
+    float* sl = reinterpret_cast<float*>(lds + 4 * TB);
     float* sdd = sl + 64;
+    uint32_t* skw = reinterpret_cast<uint32_t*>(lds + 4 * TB + 512);  // DROP: [word][query]
+    if constexpr (DROP) {
+        // word w2 of query row q (zero past n and past the row's words)
+        if (tid < 128) {
+            const int q = tid & 63, w2 = tid >> 6, kwords = (m + 31) >> 5;
+            skw[tid] = q < n && w2 < kwords ? keep[((size_t)bh * n + q) * kwords + w2] : 0u;
+        }
+    }
 
     TileAddr<D> ta;
     ta.init(lane);
     const uint32_t l0 = lds_u32(lds);
-    const uint32_t sq = l0, sdo = l0 + TILE_BYTES, sk = l0 + 2 * TILE_BYTES, sv = l0 + 3 * TILE_BYTES;
+    const uint32_t sq = l0, sdo = l0 + TB, sk = l0 + 2 * TB, sv = l0 + 3 * TB;
 
     // dQ role: D and lse·log2 e of this wave's queries, from global O and dO.
     const int qrow = 32 * (w - 2) + l32;
     const bool qok = w >= 2 && qrow < n;
     float dsum = 0.f, lc = 0.f;
     if (w >= 2) {
-        bf16x8 oop[4], dop[4];
+        bf16x8 oop[KS], dop[KS];
         load_row_operand<D>(O + qbase + (size_t)qrow * D, qok, hf, oop);
         load_row_operand<D>(dO + qbase + (size_t)qrow * D, qok, hf, dop);
         float acc = 0.f;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
+        for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)dop[ks][e], (float)oop[ks][e], acc);
         dsum = half_swap_sum(acc);
@@ -661,23 +675,29 @@ __global__ __launch_bounds__(256) void sdpa_bwd_short_bf16(
     wait_vmem();
     __syncthreads();
 
-    f32x16 acc_a[2], acc_b[2];  // dQᵀ (waves 2, 3), or dKᵀ and dVᵀ (waves 0, 1)
+    f32x16 acc_a[DT], acc_b[DT];  // dQᵀ (waves 2, 3), or dKᵀ and dVᵀ (waves 0, 1)
     if (w >= 2) {
         // Sᵀ = K Qᵀ, dPᵀ = V dOᵀ over the 64 keys; dQᵀ += Kᵀ dSᵀ.
-        bf16x8 qop[4], dop[4];
+        bf16x8 qop[KS], dop[KS];
         {
-            u32x4 r[8];
+            u32x4 r[2 * KS];
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                r[ks] = ds_read_b128(sq + ta.row[ks] + (w - 2) * 32 * 128);
-                r[4 + ks] = ds_read_b128(sdo + ta.row[ks] + (w - 2) * 32 * 128);
+            for (int ks = 0; ks < KS; ++ks) {
+                r[ks] = ds_read_b128(sq + ta.row[ks] + (w - 2) * 32 * RB);
+                r[KS + ks] = ds_read_b128(sdo + ta.row[ks] + (w - 2) * 32 * RB);
             }
             lds_wait(r);
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
+            for (int ks = 0; ks < KS; ++ks) {
                 qop[ks] = __builtin_bit_cast(bf16x8, r[ks]);
-                dop[ks] = __builtin_bit_cast(bf16x8, r[4 + ks]);
+                dop[ks] = __builtin_bit_cast(bf16x8, r[KS + ks]);
             }
+        }
+        // Dropout: this query's keep words of keys 0..31 and 32..63.
+        uint32_t kw[2] = {0u, 0u};
+        if constexpr (DROP) {
+            kw[0] = skw[qrow];
+            kw[1] = skw[64 + qrow];
         }
         f32x16 s[2], dp[2];
         row_products<D, true>(sk, sv, ta, qop, dop, s, dp);
@@ -689,31 +709,53 @@ __global__ __launch_bounds__(256) void sdpa_bwd_short_bf16(
                 const int off = 32 * kt + 8 * (i >> 2) + (i & 3);
                 const float sv_ = (off >= llo && off < lhi) ? s[kt][i] : -INFINITY;
                 const float p = exp2_hw(__builtin_fmaf(sv_, c_log2, -lc));
-                s[kt][i] = p * (dp[kt][i] - dsum);  // dSᵀ
+                float g = dp[kt][i];
+                if constexpr (DROP) g = (kw[kt] >> (8 * (i >> 2) + 4 * hf + (i & 3))) & 1u ? g * keep_scale : 0.f;
+                s[kt][i] = p * (g - dsum);  // dSᵀ
             }
         bf16x8 db[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) db[j] = pack_step(s, j);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) { acc_a[0][i] = 0.f; acc_a[1][i] = 0.f; }
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc_a[dt][i] = 0.f;
         tr_product<D>(sk, ta, db, acc_a);  // dQᵀ
     } else {
         // S = Q Kᵀ, dP = dO Vᵀ over the 64 queries; dVᵀ += dOᵀ P, dKᵀ += Qᵀ dS.
         const int key = 32 * w + l32;
-        bf16x8 kop[4], vop[4];
+        bf16x8 kop[KS], vop[KS];
         {
-            u32x4 r[8];
+            u32x4 r[2 * KS];
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                r[ks] = ds_read_b128(sk + ta.row[ks] + w * 32 * 128);
-                r[4 + ks] = ds_read_b128(sv + ta.row[ks] + w * 32 * 128);
+            for (int ks = 0; ks < KS; ++ks) {
+                r[ks] = ds_read_b128(sk + ta.row[ks] + w * 32 * RB);
+                r[KS + ks] = ds_read_b128(sv + ta.row[ks] + w * 32 * RB);
             }
             lds_wait(r);
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
+            for (int ks = 0; ks < KS; ++ks) {
                 kop[ks] = __builtin_bit_cast(bf16x8, r[ks]);
-                vop[ks] = __builtin_bit_cast(bf16x8, r[4 + ks]);
+                vop[ks] = __builtin_bit_cast(bf16x8, r[KS + ks]);
             }
+        }
+        // Dropout: bit l32 of word w (this key's word) of every query row,
+        // packed per 32-query half in the order of the S registers.
+        uint32_t zb[2] = {0u, 0u};
+        if constexpr (DROP) {
+            u32x4 kv4[8];
+#pragma unroll
+            for (int qh = 0; qh < 2; ++qh)
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq)
+                    kv4[4 * qh + gq] = ds_read_b128(lds_u32(skw) + (uint32_t)(64 * w + 32 * qh + 8 * gq + 4 * hf) * 4u);
+            lds_wait(kv4);
+#pragma unroll
+            for (int qh = 0; qh < 2; ++qh)
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) zb[qh] |= ((kv4[4 * qh + gq][e] >> l32) & 1u) << (4 * gq + e);
         }
         f32x16 s[2], dp[2];
         row_products<D, true>(sq, sdo, ta, kop, vop, s, dp);
@@ -725,8 +767,8 @@ __global__ __launch_bounds__(256) void sdpa_bwd_short_bf16(
 #pragma unroll
             for (int gq = 0; gq < 4; ++gq) {
                 const uint32_t off = (uint32_t)(32 * qh + 8 * gq + 4 * hf) * 4u;
-                lv[4 * qh + gq] = ds_read_b128(l0 + 4 * TILE_BYTES + off);
-                dv4[4 * qh + gq] = ds_read_b128(l0 + 4 * TILE_BYTES + 256 + off);
+                lv[4 * qh + gq] = ds_read_b128(l0 + 4 * TB + off);
+                dv4[4 * qh + gq] = ds_read_b128(l0 + 4 * TB + 256 + off);
             }
         lds_wait(lv);
         lds_wait(dv4);
@@ -739,8 +781,14 @@ __global__ __launch_bounds__(256) void sdpa_bwd_short_bf16(
                 const float lcq = __uint_as_float(lv[4 * qh + (i >> 2)][i & 3]);
                 const float dd = __uint_as_float(dv4[4 * qh + (i >> 2)][i & 3]);
                 const float p = exp2_hw(__builtin_fmaf(sv_, c_log2, -lcq));
-                s[qh][i] = p;
-                dp[qh][i] = p * (dp[qh][i] - dd);  // dS
+                float g = dp[qh][i], pd = p;
+                if constexpr (DROP) {
+                    const bool z = (zb[qh] >> i) & 1u;
+                    pd = z ? p * keep_scale : 0.f;
+                    g = z ? g * keep_scale : 0.f;
+                }
+                s[qh][i] = pd;             // the weights of dV
+                dp[qh][i] = p * (g - dd);  // dS
             }
         bf16x8 pb[4], db[4];
 #pragma unroll
@@ -749,21 +797,24 @@ __global__ __launch_bounds__(256) void sdpa_bwd_short_bf16(
             db[j] = pack_step(dp, j);
         }
 #pragma unroll
-        for (int i = 0; i < 16; ++i) { acc_a[0][i] = 0.f; acc_a[1][i] = 0.f; acc_b[0][i] = 0.f; acc_b[1][i] = 0.f; }
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) { acc_a[dt][i] = 0.f; acc_b[dt][i] = 0.f; }
         tr_product<D>(sdo, ta, pb, acc_b);  // dVᵀ
         tr_product<D>(sq, ta, db, acc_a);   // dKᵀ
     }
     // Every wave is done with the tiles: their space now stages the outputs
-    // (wave w < 2: dK at 8 KiB·w, dV 4 KiB further; waves 2, 3: dQ at 16 KiB + 4 KiB·(w − 2)).
+    // in 64·D-byte areas (wave w < 2: dK at area 2·w, dV at 2·w + 1; waves 2,
+    // 3: dQ at area 4 + w − 2).
     __syncthreads();
+    constexpr int AREA = 32 * RB;
     if (w >= 2) {
         const int r0 = 32 * (w - 2);
-        store_rows_lds(lds + 4 * TILE_BYTES / 2 + (w - 2) * 4096, acc_a, lane, scale,
-                       dQ + qbase + (size_t)r0 * D, n - r0);
+        store_rows_lds<D>(lds + (2 + w) * AREA, acc_a, lane, scale, dQ + qbase + (size_t)r0 * D, n - r0);
     } else {
         const int r0 = 32 * w;
-        store_rows_lds(lds + w * 8192, acc_a, lane, scale, dK + kvbase + (size_t)r0 * D, m - r0);
-        store_rows_lds(lds + w * 8192 + 4096, acc_b, lane, 1.f, dV + kvbase + (size_t)r0 * D, m - r0);
+        store_rows_lds<D>(lds + 2 * w * AREA, acc_a, lane, scale, dK + kvbase + (size_t)r0 * D, m - r0);
+        store_rows_lds<D>(lds + (2 * w + 1) * AREA, acc_b, lane, 1.f, dV + kvbase + (size_t)r0 * D, m - r0);
     }
 }
 
@@ -816,20 +867,27 @@ hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream, float c_log2, floa
                 : launch_bwd_width<D, 2, false>(a, stream, c_log2, ws_d, ws_l);
 }
 
+template <int D>
+hipError_t launch_bwd_short(const BwdArgs& a, hipStream_t stream, float c_log2) {
+    const auto kernel = a.keep ? sdpa_bwd_short_bf16<D, true> : sdpa_bwd_short_bf16<D, false>;
+    hipLaunchKernelGGL(kernel, dim3(a.B * a.H), dim3(256), 0, stream, (const uint16_t*)a.q,
+                       (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.out,
+                       (const uint16_t*)a.dout, a.lse, (uint16_t*)a.dq, (uint16_t*)a.dk, (uint16_t*)a.dv,
+                       a.H, a.n, a.m, a.scale, c_log2, a.wl, a.wr, a.bottom_right, a.key_lens, a.keep,
+                       a.keep_scale);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
-    const int BH = a.B * a.H;
     const float c_log2 = (float)((double)a.scale * 1.4426950408889634);  // scale·log2(e)
     float* ws_d = static_cast<float*>(a.workspace);
     float* ws_l = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + bwd_workspace_bytes(a.B, a.H, a.n) / 2);
-    if (a.d == kHeadDim && a.n <= 64 && a.m <= 64 && !a.keep) {
-        hipLaunchKernelGGL(sdpa_bwd_short_bf16, dim3(BH), dim3(256), 0, stream, (const uint16_t*)a.q,
-                           (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.out,
-                           (const uint16_t*)a.dout, a.lse, (uint16_t*)a.dq, (uint16_t*)a.dk,
-                           (uint16_t*)a.dv, a.H, a.n, a.m, a.scale, c_log2, a.wl, a.wr, a.bottom_right,
-                           a.key_lens);
-        return hipGetLastError();
+    if (a.n <= 64 && a.m <= 64) {
+        if (a.d == 32) return launch_bwd_short<32>(a, stream, c_log2);
+        if (a.d == 128) return launch_bwd_short<128>(a, stream, c_log2);
+        return launch_bwd_short<64>(a, stream, c_log2);
     }
     if (a.d == 32) return launch_bwd_d<32>(a, stream, c_log2, ws_d, ws_l);
     if (a.d == 128) return launch_bwd_d<128>(a, stream, c_log2, ws_d, ws_l);
