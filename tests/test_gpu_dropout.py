@@ -188,22 +188,26 @@ def test_all_kept_equals_plain_bitwise(gpu_lib, d):
 
 
 @pytest.mark.parametrize("d", [32, 64, 128])
-def test_all_kept_backward_equals_plain_bitwise_sentence_length(gpu_lib, d):
-    """n, m <= 64 (the fused one-launch gradient): with every weight kept and
-    c = 1 the dropout form's gradients equal the plain ones bit for bit, from
-    the same forward output and lse."""
+@pytest.mark.parametrize("window", [None, (9, 2, "bottom_right")])
+def test_all_kept_equals_plain_bitwise_sentence_length(gpu_lib, d, window):
+    """n, m <= 64 (the sentence-length forward kernel and the fused one-launch
+    gradient): with every weight kept and c = 1 the dropout forms equal the
+    plain ones bit for bit (output and lse; gradients from the same forward
+    output and lse)."""
     import torch
 
-    from transformer_attention_sdpa_amd import backward, backward_dropout, forward
+    from transformer_attention_sdpa_amd import backward, backward_dropout, forward, forward_dropout
 
-    c = backward_case(9600 + d, 3, 4, 64, 50, key_lens=[50, 17, 0], d=d)
+    c = backward_case(9600 + d, 3, 4, 64, 50, key_lens=[50, 17, 0], window=window, d=d)
     q, k, v, do = (to_device(c[x], "bf16") for x in ("q", "k", "v", "do"))
     kl = torch.from_numpy(np.asarray(c["key_lens"], np.int32)).cuda()
     ones = torch.full((3, 4, 64, 2), -1, dtype=torch.int32, device="cuda")
-    o, lse = forward(q, k, v, key_lens=kl, return_lse=True)
-    g1 = backward(q, k, v, o, do, lse, key_lens=kl)
-    g2 = backward_dropout(q, k, v, o, do, lse, ones, 1.0, key_lens=kl)
+    o, lse = forward(q, k, v, key_lens=kl, window=window, return_lse=True)
+    o2, l2 = forward_dropout(q, k, v, ones, 1.0, key_lens=kl, window=window, return_lse=True)
+    g1 = backward(q, k, v, o, do, lse, key_lens=kl, window=window)
+    g2 = backward_dropout(q, k, v, o, do, lse, ones, 1.0, key_lens=kl, window=window)
     torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16)) and torch.equal(lse, l2)
     for a, b in zip(g1, g2):
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 

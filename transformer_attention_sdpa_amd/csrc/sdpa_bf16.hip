@@ -471,9 +471,10 @@ hipError_t launch_bf16_long(const Args& a, hipStream_t stream) {
 hipError_t launch_bf16(const Args& a0, hipStream_t stream) {
     Args a = a0;
     if (!a.strided) a.lay = dense_layout(a.H, a.n, a.m, a.d, a.dv);  // packed layout
-    // attention dropout: d_k = d_v ∈ {32, 64, 128}, any n, m
+    // n, m <= 64: the Table 3 width pairs, and attention dropout at d_k = d_v ∈ {32, 64, 128}
+    if (short_bf16_fits(a)) return launch_bf16_short(a, stream);
+    // attention dropout, longer: d_k = d_v ∈ {32, 64, 128}
     if (a.keep) return a.d == D ? launch_bf16_long(a, stream) : launch_bf16_width(a, stream);
-    if (short_bf16_fits(a)) return launch_bf16_short(a, stream);  // n, m <= 64, d_k = d_v ∈ {32, 64, 128}
     if (a.d != D || a.dv != D) return launch_bf16_width(a, stream);
     if (decode_bf16_fits(a)) return launch_bf16_decode(a, stream);
     return launch_bf16_long(a, stream);

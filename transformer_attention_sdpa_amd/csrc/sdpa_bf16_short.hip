@@ -109,12 +109,16 @@ __device__ __forceinline__ f32x4 mfma16k16(s16x4 a, s16x4 b, f32x4 c) {
 // STRIDED = false: the packed [B, h, len, D] layout with compile-time strides
 // (the runtime-stride arithmetic would sit on this latency-bound kernel's
 // critical path); true: the strides of `lay`.
-template <int DK, int DV, bool WINDOWED, bool STRIDED>
+// DROP: attention dropout with keep-bit words [B·h, n, ⌈m/32⌉] (packed layout
+// only): the dropped weights leave P·V but not the row sum, and the output is
+// scaled by keep_scale.
+template <int DK, int DV, bool WINDOWED, bool STRIDED, bool DROP>
 __global__ __launch_bounds__(NT) void sdpa_short_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
     int H, int n, int m, float c_log2, int wl, int wr, int bottom_right,
-    const int32_t* __restrict__ key_lens, float* __restrict__ lse, Layout lay) {
+    const int32_t* __restrict__ key_lens, float* __restrict__ lse, Layout lay,
+    const uint32_t* __restrict__ keep, float keep_scale) {
     constexpr int RBK = 2 * DK, RBV = 2 * DV;  // bytes per tile row
     constexpr int TILE_K = MAXLEN * RBK;       // Q and K tiles of 64 rows
     constexpr int TILE_V = MAXLEN * RBV;       // V tile (and the output staging)
@@ -184,6 +188,15 @@ __global__ __launch_bounds__(NT) void sdpa_short_bf16(
 #pragma unroll
         for (int i = 0; i < LPK; ++i) load16_to_lds_nt(rq, lds + TILE_K + kq_lds[i], q_off[i]);
     }
+    // Dropout: the keep words of this lane's query (keys 0..31, 32..63); rows
+    // past n read row n − 1 (their outputs are not stored).
+    uint32_t kw[2] = {0u, 0u};
+    if constexpr (DROP) {
+        const int kwords = (m + 31) >> 5;
+        const uint32_t* krow = keep + ((size_t)bh * n + min(w * QW + (lane & 15), n - 1)) * kwords;
+        kw[0] = krow[0];
+        kw[1] = kwords > 1 ? krow[1] : 0u;
+    }
     int L = m;
     if (key_lens) {
         const int t = key_lens[b];
@@ -227,6 +240,9 @@ __global__ __launch_bounds__(NT) void sdpa_short_bf16(
     // the grid, every workgroup's Q and K then reach HBM ahead of V traffic,
     // which the scores do not need.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // (the keep words are in too: any wait the compiler adds for them goes
+    // here, ahead of the V requests, not behind them)
+    if constexpr (DROP) asm volatile("" : "+v"(kw[0]), "+v"(kw[1]));
     const i32x4 rv = make_rsrc(Vh, rows_span(L, vr, DV, 2));
     if (vload) {
 #pragma unroll
@@ -301,9 +317,17 @@ __global__ __launch_bounds__(NT) void sdpa_short_bf16(
         // ln Σ e^(scale·s) = (mc + log2 l)·ln 2: −∞ for a row with no legal key
         if (lse && G == 0 && q < n) lse[(size_t)bh * n + q] = (mc + log2f(l)) * 0.6931471805599453f;
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < 2; ++j) {
             pb[j] = to_bf16x8(s[2 * j][0], s[2 * j][1], s[2 * j][2], s[2 * j][3],
                               s[2 * j + 1][0], s[2 * j + 1][1], s[2 * j + 1][2], s[2 * j + 1][3]);
+            // Dropout, after the row sum: slot e of pb[j] is key 32·j + 4·G + e
+            // (e < 4) or 32·j + 16 + 4·G + (e − 4), bit 4·G + e or 16 + 4·G +
+            // (e − 4) of word j.
+            if constexpr (DROP) {
+                const uint32_t wd = kw[j] >> (4 * G);
+                pb[j] = keep_pairs(pb[j], (wd & 0xFu) | ((wd >> 12) & 0xF0u));
+            }
+        }
     }
     wait_vmem();  // V in
     lds_barrier();
@@ -338,7 +362,7 @@ __global__ __launch_bounds__(NT) void sdpa_short_bf16(
     // store instruction writes whole rows, 16 bytes a lane.
     {
         // no legal key ⇒ zero row; a NaN sum (NaN legal inputs) stays NaN
-        const float inv = l != 0.f ? __builtin_amdgcn_rcpf(l) : 0.f;
+        const float inv = l != 0.f ? (DROP ? keep_scale * __builtin_amdgcn_rcpf(l) : __builtin_amdgcn_rcpf(l)) : 0.f;
         char* ob = lds + w * QW * RBV;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
@@ -377,12 +401,19 @@ template <int DK, int DV>
 hipError_t launch_short(const Args& a, hipStream_t stream) {
     const float c_log2 = (float)((double)a.scale * 1.4426950408889634);  // scale·log2(e)
     const bool windowed = a.wl >= 0 || a.wr > 0 || a.bottom_right;
-    const auto kernel = a.strided ? (windowed ? sdpa_short_bf16<DK, DV, true, true> : sdpa_short_bf16<DK, DV, false, true>)
-                                  : (windowed ? sdpa_short_bf16<DK, DV, true, false> : sdpa_short_bf16<DK, DV, false, false>);
+    auto kernel = a.strided ? (windowed ? sdpa_short_bf16<DK, DV, true, true, false> : sdpa_short_bf16<DK, DV, false, true, false>)
+                            : (windowed ? sdpa_short_bf16<DK, DV, true, false, false> : sdpa_short_bf16<DK, DV, false, false, false>);
+    if constexpr (DK == DV && DK >= 32) {  // the widths attention dropout takes; packed layout
+        if (a.keep) {
+            if (a.strided) return hipErrorInvalidValue;
+            kernel = windowed ? sdpa_short_bf16<DK, DV, true, false, true> : sdpa_short_bf16<DK, DV, false, false, true>;
+        }
+    }
+    if (a.keep && !(DK == DV && DK >= 32)) return hipErrorInvalidValue;
     hipLaunchKernelGGL(kernel, dim3(a.B * a.H), dim3(NT), 0, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (uint16_t*)a.out, a.H, a.n, a.m, c_log2, a.wl, a.wr, a.bottom_right,
-                       a.key_lens, a.lse, a.lay);
+                       a.key_lens, a.lse, a.lay, a.keep, a.keep_scale);
     return hipGetLastError();
 }
 }  // namespace
