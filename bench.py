@@ -174,7 +174,12 @@ def timed_replay(graph, flush):
     return e0.elapsed_time(e1)
 
 
-def time_workload(name, dtype, steps, warmup, clock_warm_s=0.0, case=None, split=False):
+def time_workload(name, dtype, steps, warmup, clock_warm_s=0.0, case=None, split=False, dropout=0.0):
+    """The forward pass of a workload, timed by the driver's protocol (plus a
+    graph replay and a long rotation as cross-checks).  split: sdpa_forward_ex
+    with a workspace.  dropout p > 0: sdpa_forward_dropout with a seeded keep
+    mask per set (keep probability 1 − p, factor 1/(1 − p)), whose words count
+    as read."""
     import torch
 
     from transformer_attention_sdpa_amd import _lib
@@ -200,13 +205,22 @@ def time_workload(name, dtype, steps, warmup, clock_warm_s=0.0, case=None, split
     # each copy) exceeds twice the Infinity Cache: a set is evicted before the
     # rotation comes back to it.  The timed replay starts right after a cache
     # flush, so the first sets it touches are cold too, at any step count.
-    touched = algorithmic_work(wl, dtype, case["key_lens"])[1]
+    keep0 = None
+    mask_bytes = 0
+    if dropout > 0:
+        import numpy as np
+
+        from sdpa_inputs import pack_keep, random_keep
+        keep0 = torch.from_numpy(pack_keep(random_keep(np.random.default_rng(1234), wl.B, wl.h, wl.n, wl.m,
+                                                       dropout)).view(np.int32)).to(dev)
+        mask_bytes = keep0.numel() * 4
+    touched = algorithmic_work(wl, dtype, case["key_lens"])[1] + mask_bytes
     nsets = max(1, min(64, math.ceil(2 * INFINITY_CACHE_BYTES / touched)))
     sets = []
     for _ in range(nsets):
         q, k, v = q0.clone(), k0.clone(), v0.clone()
         o = torch.empty((wl.B, wl.h, wl.n, wl.d_v), dtype=tdt, device=dev)
-        sets.append((q, k, v, o))
+        sets.append((q, k, v, o, None if keep0 is None else keep0.clone()))
     kl = None
     kl_ptr = None
     if case["key_lens"] is not None:
@@ -214,7 +228,8 @@ def time_workload(name, dtype, steps, warmup, clock_warm_s=0.0, case=None, split
         kl_ptr = kl.data_ptr()
     scale = 1.0 / math.sqrt(wl.d_k)
     mask = _lib.SDPA_MASK_CAUSAL if wl.causal else _lib.SDPA_MASK_NONE
-    ptrs = [(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr()) for (q, k, v, o) in sets]
+    ptrs = [(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), None if z is None else z.data_ptr())
+            for (q, k, v, o, z) in sets]
     ws = None
     if split:  # sdpa_forward_ex with its workspace (decoder steps split into pieces of keys)
         need = _lib.sdpa_forward_workspace_bytes(wl.B, wl.h, wl.n, wl.m, wl.d_k, wl.d_v, code)
@@ -229,7 +244,14 @@ def time_workload(name, dtype, steps, warmup, clock_warm_s=0.0, case=None, split
 
     def launch(i, stream):
         p = ptrs[i % nsets]
-        if ws is not None:
+        if p[4] is not None:
+            wlft = -1 if wl.window is None else wleft
+            wrgt = (0 if wl.causal else -1) if wl.window is None else wright
+            wal = _lib.SDPA_ALIGN_TOP_LEFT if wl.window is None else walign
+            rc = _lib.sdpa_forward_dropout(p[0], p[1], p[2], p[3], None, wl.B, wl.h, wl.n, wl.m, wl.d_k,
+                                           wl.d_v, scale, wlft, wrgt, wal, kl_ptr, p[4], 1.0 / (1.0 - dropout),
+                                           code, stream)
+        elif ws is not None:
             wlft = -1 if wl.window is None else wleft
             wrgt = (0 if wl.causal else -1) if wl.window is None else wright
             wal = _lib.SDPA_ALIGN_TOP_LEFT if wl.window is None else walign
@@ -284,11 +306,12 @@ def time_workload(name, dtype, steps, warmup, clock_warm_s=0.0, case=None, split
     rot_ms = timed_replay(graph_rot, flush)
 
     flops, nbytes, dense = algorithmic_work(wl, dtype, case["key_lens"])
+    nbytes += mask_bytes
     t = step_ms / 1e3 / steps
     del graph, graph_rot, sets, flush
     torch.cuda.empty_cache()
     return {
-        "workload": name, "dtype": dtype, "steps": steps, "sets_rotated": nsets,
+        "workload": name, "dtype": dtype, "steps": steps, "sets_rotated": nsets, "dropout": dropout,
         "ms_per_step": step_ms / steps, "ms_per_step_graph": graph_ms / steps,
         "bytes_touched_timed": nbytes * steps,
         "distinct_sets_timed": min(steps, nsets),
@@ -928,6 +951,13 @@ def main():
         for name in ("decode_long_cache", "decode_one_sequence"):
             r = time_workload(name, "bf16", 20, min(args.warmup, 5), clock_warm_s=0.1, split=True)
             extra[f"{name}-bf16-split"] = {k: r[k] for k in (
+                "ms_per_step", "tflops", "gbs", "frac_mfma_peak", "frac_hbm_peak", "steps",
+                "sets_rotated", "ms_per_step_graph")}
+        # attention dropout (p = 0.1) in the forward pass: sentence length and 8k causal
+        for name in ("encoder_self_base", "long_causal_8k"):
+            r = time_workload(name, "bf16", 20 if name.endswith("_8k") else max(10, min(args.steps, 200)),
+                              min(args.warmup, 5), clock_warm_s=0.1, dropout=0.1)
+            extra[f"{name}-bf16-dropout0.1"] = {k: r[k] for k in (
                 "ms_per_step", "tflops", "gbs", "frac_mfma_peak", "frac_hbm_peak", "steps",
                 "sets_rotated", "ms_per_step_graph")}
         for name in ("encoder_self_base", "long_causal_8k"):

@@ -761,6 +761,41 @@ __global__ __launch_bounds__(256) void sdpa_bwd_short_bf16(
         row_products<D, true>(sq, sdo, ta, kop, vop, s, dp);
         const QueryRange qr{wl, wr, bottom_right ? L - n : 0, L, n};
         const int llo = qr.qa(key) - 4 * hf, lhi = qr.qb(key) - 4 * hf;
+        // The weights (query 32·qh + 8·(i/4) + 4·hf + i%4, this key) and dS, from
+        // each query's lse·log2 e and D.
+        if constexpr (D == 32) {
+            // One 32-query half at a time: this keeps the kernel within the
+            // 128 registers of four waves per SIMD (16 heads of 32 are twice
+            // the workgroups of 8 heads of 64).
+#pragma unroll
+            for (int qh = 0; qh < 2; ++qh) {
+                u32x4 lv[4], dv4[4];
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq) {
+                    const uint32_t off = (uint32_t)(32 * qh + 8 * gq + 4 * hf) * 4u;
+                    lv[gq] = ds_read_b128(l0 + 4 * TB + off);
+                    dv4[gq] = ds_read_b128(l0 + 4 * TB + 256 + off);
+                }
+                lds_wait(lv);
+                lds_wait(dv4);
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int off = 32 * qh + 8 * (i >> 2) + (i & 3);
+                    const float sv_ = (off >= llo && off < lhi) ? s[qh][i] : -INFINITY;
+                    const float lcq = __uint_as_float(lv[i >> 2][i & 3]);
+                    const float dd = __uint_as_float(dv4[i >> 2][i & 3]);
+                    const float p = exp2_hw(__builtin_fmaf(sv_, c_log2, -lcq));
+                    float g = dp[qh][i], pd = p;
+                    if constexpr (DROP) {
+                        const bool z = (zb[qh] >> i) & 1u;
+                        pd = z ? p * keep_scale : 0.f;
+                        g = z ? g * keep_scale : 0.f;
+                    }
+                    s[qh][i] = pd;             // the weights of dV
+                    dp[qh][i] = p * (g - dd);  // dS
+                }
+            }
+        } else {
         u32x4 lv[8], dv4[8];
 #pragma unroll
         for (int qh = 0; qh < 2; ++qh)
@@ -790,6 +825,7 @@ __global__ __launch_bounds__(256) void sdpa_bwd_short_bf16(
                 s[qh][i] = pd;             // the weights of dV
                 dp[qh][i] = p * (g - dd);  // dS
             }
+        }
         bf16x8 pb[4], db[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
