@@ -879,7 +879,8 @@ def main():
                                            "encoder_h16_d32", "encoder_h4_d128"],
                     help="time only the backward pass of this workload (one JSON line)")
     ap.add_argument("--dropout", type=float, default=0.0,
-                    help="with --backward: attention dropout probability of the timed pass")
+                    help="attention dropout probability of the timed pass (--workload or --backward; "
+                         "default 0: none)")
     ap.add_argument("--mha", choices=["mha_encoder_base", "mha_cross_big"],
                     help="time only this multi-head sublayer workload (one JSON line)")
     ap.add_argument("--context", action="store_true",
@@ -925,7 +926,8 @@ def main():
         return
 
     wl = WORKLOADS[args.workload]
-    head = time_workload(args.workload, args.dtype, args.steps, args.warmup, split=args.split)
+    head = time_workload(args.workload, args.dtype, args.steps, args.warmup, split=args.split,
+                         dropout=args.dropout)
     extra = {}
     if not args.no_extra:
         # Every GPU measurement first, then the CPU oracle passes.  Each extra
@@ -1001,7 +1003,8 @@ def main():
         "data": "synthetic N(0,1), seeded",
         "config": {"workload": args.workload, "B": wl.B, "h": wl.h, "n": wl.n, "m": wl.m,
                    "d_k": wl.d_k, "d_v": wl.d_v, "causal": wl.causal,
-                   "key_len_range": wl.key_len_range, "seed": wl.seed},
+                   "key_len_range": wl.key_len_range, "seed": wl.seed,
+                   **({"dropout": args.dropout} if args.dropout else {})},
         "roofline": roof,
         "alg_bytes_per_step": head["alg_bytes"],
         "alg_flops_per_step": head["alg_flops"],

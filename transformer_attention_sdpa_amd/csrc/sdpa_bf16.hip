@@ -92,9 +92,28 @@ struct LongKernel {
     // [flo, fhi) is legal for every query of the wave.
     int wlo, whi, flo, fhi;
     float c_log2;
-    // Dropout: this lane's keep-bit rows (one per sub-block) and their words.
+    // Dropout: this lane's keep-bit rows (one per sub-block), and the words
+    // of two consecutive tiles (keys k0 .. k0 + 127 of the even step's tile).
     const uint32_t* krow[QT];
     int kwords;
+    u32x4 kwv[QT];
+
+    // The keep words of tiles t and t + 1, one 16-byte load per row where all
+    // four lie in the row (zero past its last word).  One load per lane for
+    // two tiles keeps the cache traffic of the mask (each lane reads its own
+    // row, 32 rows per instruction) at a quarter of single-word loads.
+    __device__ void load_keep2(int t) {
+        const int w0 = 2 * t;
+        if (w0 + 4 <= kwords) {  // uniform
+#pragma unroll
+            for (int qt = 0; qt < QT; ++qt) __builtin_memcpy(&kwv[qt], krow[qt] + w0, 16);
+        } else {
+#pragma unroll
+            for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) kwv[qt][i] = w0 + i < kwords ? krow[qt][w0 + i] : 0u;
+        }
+    }
 
     __device__ void issue_tile_load(int t, int buf) {
         const int k0 = t * BN;
@@ -157,17 +176,6 @@ struct LongKernel {
     __device__ void compute_tile(int k0) {
         const char* sk = lds + BUF * 2 * TILE_BYTES;
         const char* sv = sk + TILE_BYTES;
-        // Dropout: the keep words of keys k0..k0+31 and k0+32..k0+63 of this
-        // lane's queries, requested before the products so they arrive in time.
-        uint32_t kw[QT][2];
-        if constexpr (DROP) {
-            const int w0 = k0 >> 5;
-#pragma unroll
-            for (int qt = 0; qt < QT; ++qt) {
-                kw[qt][0] = w0 < kwords ? krow[qt][w0] : 0u;
-                kw[qt][1] = w0 + 1 < kwords ? krow[qt][w0 + 1] : 0u;
-            }
-        }
 
         // Sᵀ = K · Qᵀ over d = 64 (four k-steps of 16).
         f32x16 s[QT][2];
@@ -244,8 +252,8 @@ struct LongKernel {
             for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const uint32_t wd = kw[qt][j >> 1] >> (16 * (j & 1) + 4 * hf);
-                    pb[qt][j] = keep_pairs(pb[qt][j], (wd & 0xFu) | ((wd >> 4) & 0xF0u));
+                    const uint32_t wd = kwv[qt][2 * BUF + (j >> 1)] >> (16 * (j & 1) + 4 * hf);
+                    pb[qt][j] = keep_pairs(pb[qt][j], wd);
                 }
         }
 
@@ -273,6 +281,9 @@ struct LongKernel {
     template <int BUF>
     __device__ void step(int t, int tend) {
         if (t + 1 < tend) issue_tile_load(t + 1, BUF ^ 1);
+        // Dropout: the even step (BUF 0) loads the keep words of its tile and
+        // of the next one, which the odd step uses.
+        if constexpr (DROP && BUF == 0) load_keep2(t);
         const int k0 = t * BN;
         if (k0 < whi && k0 + BN > wlo) {  // else: no query of this wave sees the tile
             compute_tile<BUF>(k0);

@@ -325,7 +325,7 @@ __global__ __launch_bounds__(NT) void sdpa_short_bf16(
             // (e − 4) of word j.
             if constexpr (DROP) {
                 const uint32_t wd = kw[j] >> (4 * G);
-                pb[j] = keep_pairs(pb[j], (wd & 0xFu) | ((wd >> 12) & 0xF0u));
+                pb[j] = keep_pairs(pb[j], (wd & 0xFu) | ((wd >> 8) & 0xF00u));
             }
         }
     }

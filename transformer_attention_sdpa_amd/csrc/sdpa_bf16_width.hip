@@ -260,7 +260,7 @@ __global__ __launch_bounds__(NW * 64) void sdpa_fwd_bf16_width(
                 // word kt.
                 if constexpr (DROP) {
                     const uint32_t wd = kw[kt] >> (16 * (j & 1) + 4 * hf);
-                    pb[j] = keep_pairs(pb[j], (wd & 0xFu) | ((wd >> 4) & 0xF0u));
+                    pb[j] = keep_pairs(pb[j], wd);
                 }
             }
             // Oᵀ += Vᵀ · Pᵀ.

@@ -259,16 +259,23 @@ __device__ __forceinline__ void load16_to_lds_nt(i32x4 rsrc, void* lds, int voff
 __device__ __forceinline__ void store16_nt(void* p, u32x4 x) {
     __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(p));
 }
-// Keep-bit helpers of attention dropout.  keep_pairs zeroes the elements of
-// eight packed bf16 values whose bit in `bits` (bit e for element e) is 0.
-__device__ __forceinline__ uint32_t keep_pair_mask(uint32_t bits, int e) {
-    const uint32_t lo = 0u - ((bits >> e) & 1u), hi = 0u - ((bits >> (e + 1)) & 1u);
-    return (lo & 0xFFFFu) | (hi & 0xFFFF0000u);
-}
-__device__ __forceinline__ bf16x8 keep_pairs(bf16x8 v, uint32_t bits) {
+// Attention dropout: keep_pairs zeroes the elements of eight packed bf16
+// values whose keep bit is 0; the bits of elements 0..3 are bits 0..3 of
+// `nib`, those of elements 4..7 bits 8..11 (other bits are ignored).  Each
+// 32-bit pair of elements gets its mask from two 16-bit lanes: the low lane
+// holds `nib`, the high lane `nib` >> 1, so both bits of a pair sit at one
+// position q; a packed 16-bit shift left by 15 − q and an arithmetic shift
+// right by 15 then fill each lane with its bit.
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ bf16x8 keep_pairs(bf16x8 v, uint32_t nib) {
     u32x4 w = __builtin_bit_cast(u32x4, v);
+    const s16x2 t = __builtin_bit_cast(s16x2, (nib & 0xFFFFu) | ((nib << 15) & 0xFFFF0000u));
 #pragma unroll
-    for (int e = 0; e < 4; ++e) w[e] &= keep_pair_mask(bits, 2 * e);
+    for (int p = 0; p < 4; ++p) {
+        const short q = p < 2 ? 2 * p : 2 * p + 4;  // bit position of element 2·p
+        const s16x2 x = (t << (short)(15 - q)) >> (short)15;
+        w[p] &= __builtin_bit_cast(uint32_t, x);
+    }
     return __builtin_bit_cast(bf16x8, w);
 }
 
