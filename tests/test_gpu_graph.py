@@ -2,7 +2,8 @@
 
 Every entry point only launches kernels on the caller's stream (no
 allocation, no memset, no synchronisation), so a forward with its
-log-sum-exp, the backward on it, a split decoder step and the projected
+log-sum-exp, the backward on it, the same two with attention dropout (a keep
+mask copied in with the inputs), a split decoder step and the projected
 sublayer can be captured into one graph and replayed.  Each replay gets new
 inputs copied into the captured buffers, with eager work and a
 synchronisation between replays, and must reproduce the eager call on the
@@ -14,7 +15,7 @@ import numpy as np
 import pytest
 
 import oracle.sdpa_oracle as so
-from sdpa_inputs import bf16_bits, mha_case, random_case, round_to_bf16
+from sdpa_inputs import bf16_bits, mha_case, pack_keep, random_case, random_keep, round_to_bf16
 from tests.gpu_cases import TOL, from_device, max_abs_err
 
 pytestmark = pytest.mark.gpu
@@ -47,6 +48,7 @@ def _inputs(seed):
     host = {f"enc_{t}": _bits(enc[t]) for t in ("q", "k", "v")}
     host["enc_do"] = _bits(dout)
     host["enc_kl"] = torch.from_numpy(enc["key_lens"])
+    host["enc_keep"] = torch.from_numpy(pack_keep(random_keep(rng, B, h, n, m, 0.2)).view(np.int32))
     host.update({f"dec_{t}": _bits(dec[t]) for t in ("q", "k", "v")})
     host["dec_kl"] = torch.from_numpy(dec["key_lens"])
     host["x"] = _bits(x)
@@ -54,15 +56,19 @@ def _inputs(seed):
 
 
 def _pipeline(s, w, ws_dec, ws_mha):
-    """One pass over the four calls on the current stream; returns the outputs."""
-    from transformer_attention_sdpa_amd import backward, forward, mha_forward
+    """One pass over the six calls on the current stream; returns the outputs."""
+    from transformer_attention_sdpa_amd import backward, backward_dropout, forward, forward_dropout, mha_forward
 
     out, lse = forward(s["enc_q"], s["enc_k"], s["enc_v"], key_lens=s["enc_kl"], return_lse=True)
     dq, dk, dv = backward(s["enc_q"], s["enc_k"], s["enc_v"], out, s["enc_do"], lse, key_lens=s["enc_kl"])
+    o_d, l_d = forward_dropout(s["enc_q"], s["enc_k"], s["enc_v"], s["enc_keep"], 1.25, key_lens=s["enc_kl"],
+                               return_lse=True)
+    g_d = backward_dropout(s["enc_q"], s["enc_k"], s["enc_v"], o_d, s["enc_do"], l_d, s["enc_keep"], 1.25,
+                           key_lens=s["enc_kl"])
     dec = forward(s["dec_q"], s["dec_k"], s["dec_v"], key_lens=s["dec_kl"], window=(None, 0, "bottom_right"),
                   workspace=ws_dec)
     y = mha_forward(s["x"], s["x"], *w, heads=8, workspace=ws_mha)
-    return [out, lse, dq, dk, dv, dec, y]
+    return [out, lse, dq, dk, dv, o_d, l_d, *g_d, dec, y]
 
 
 def test_graph_replays_match_eager(gpu_lib):
@@ -93,7 +99,8 @@ def test_graph_replays_match_eager(gpu_lib):
         captured = _pipeline(s, w, ws_dec, ws_mha)
     torch.cuda.synchronize()
 
-    names = ("out", "lse", "dq", "dk", "dv", "decoder", "sublayer")
+    names = ("out", "lse", "dq", "dk", "dv", "dropout out", "dropout lse", "dropout dq", "dropout dk",
+             "dropout dv", "decoder", "sublayer")
     for r in range(3):
         host, enc = _inputs(7001 + r)
         for k, t in host.items():
