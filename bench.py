@@ -876,7 +876,7 @@ def main():
                     help="print the per-launch HBM traffic record of --kernel and exit")
     ap.add_argument("--kernel", default="sdpa_short_bf16", help="kernel name for --traffic-json")
     ap.add_argument("--backward", choices=["encoder_self_base", "decoder_causal_base", "long_causal_8k",
-                                           "encoder_h16_d32", "encoder_h4_d128"],
+                                           "encoder_h16_d32", "encoder_h4_d128", "long_causal_8k_d128"],
                     help="time only the backward pass of this workload (one JSON line)")
     ap.add_argument("--dropout", type=float, default=0.0,
                     help="attention dropout probability of the timed pass (--workload or --backward; "

@@ -47,11 +47,14 @@ constexpr int tile_bytes() { return BT * D * 2; }
 // 16-byte chunk position of chunk c of row r in a tile of D/8 chunks per row,
 // XOR-swizzled so that 16 consecutive rows read at one chunk fall on distinct
 // banks of the 256-byte LDS pass (64-byte rows share a pass four at a time,
-// 256-byte rows fill it alone); for D = 64 it is lds_swz.
+// 256-byte rows fill it alone); for D = 64 it is lds_swz.  At D = 128 the
+// row's low two bits select the 4-chunk group and the next two the chunk in
+// it, so that the transpose reads (rows 4·G' + [0..3] at four consecutive
+// chunks) spread over all banks too.
 template <int D>
 __device__ __forceinline__ int bswz(int r, int c) {
     if constexpr (D == 32) return r * 4 + (c ^ ((r >> 2) & 3));
-    else if constexpr (D == 128) return r * 16 + (c ^ (r & 15));
+    else if constexpr (D == 128) return r * 16 + (c ^ (((r & 3) << 2) | ((r >> 2) & 3)));
     else return lds_swz(r, c);
 }
 constexpr float LOG2E = 1.4426950408889634f;

@@ -31,12 +31,17 @@ constexpr int BT = 64;  // keys per LDS tile
 // row, XOR-swizzled so that 16 consecutive rows read at one chunk (one
 // 16-byte MFMA operand per lane) fall on distinct banks of gfx950's 256-byte
 // LDS pass: 32-byte rows (D = 16) share a pass eight at a time, 64-byte rows
-// (D = 32) four at a time, 256-byte rows (D = 128) fill it alone.
+// (D = 32) four at a time, 256-byte rows (D = 128) fill it alone.  The
+// transpose reads of Vᵀ take rows 4·G' + [0..3] at four consecutive chunks of
+// one 4-chunk group; at D = 128 the row's low two bits therefore pick the
+// chunk group (bits 2–3 of the XOR) and its next two bits the chunk within
+// it, which spreads those reads over all banks as well (an XOR with r mod 16
+// alone keeps them inside one group: four-way conflicts).
 template <int D>
 __device__ __forceinline__ int wswz(int r, int c) {
     if constexpr (D == 16) return r * 2 + (c ^ ((r >> 3) & 1));
     else if constexpr (D == 32) return r * 4 + (c ^ ((r >> 2) & 3));
-    else if constexpr (D == 128) return r * 16 + (c ^ (r & 15));
+    else if constexpr (D == 128) return r * 16 + (c ^ (((r & 3) << 2) | ((r >> 2) & 3)));
     else return lds_swz(r, c);
 }
 
