@@ -13,9 +13,12 @@
 // on v_mfma_f32_32x32x16_bf16, with 32-key tiles of K and V (32 KiB each) and
 // an exact online softmax (the tile maximum moves the reference every tile),
 // computed identically by every wave from the same summed scores.  Rows of
-// 1 KiB are swizzled by 16-byte chunk (chunk c of row r at c ^ (r mod 16)),
-// so the 16 rows that one operand read touches fall on distinct banks, and
-// one 1 KiB buffer_load … lds fills one row.  Key windows, key lengths, the
+// 1 KiB are swizzled by 16-byte chunk (chunk c of row r at c ^ g(r), g(r) =
+// 4·(r mod 4) + (r / 4) mod 4), so the 16 rows that one operand read touches
+// fall on distinct banks, and so do the transpose reads of Vᵀ, whose rows
+// 4·G' + [0..3] take four consecutive chunks of one 4-chunk group (g's low
+// bits alone would keep them in one group of 16 banks); one 1 KiB
+// buffer_load … lds fills one row.  Key windows, key lengths, the
 // log-sum-exp output and caller strides behave as in the other kernels.
 #include "sdpa_common.hpp"
 
@@ -32,8 +35,9 @@ constexpr int WSLICE = WD / WNW;  // dims per wave (128)
 constexpr int LQ = 0, LK = WBQ * ROWB, LV = LK + WBT * ROWB, LRED = LV + WBT * ROWB;
 constexpr int LDS_BYTES = LRED + WNW * 4096;  // Q, K, V (32 KiB each), partial scores (16 KiB)
 
-// Byte offset of 16-byte chunk c of row r.
-__device__ __forceinline__ int wide_off(int r, int c) { return (r * WCH + (c ^ (r & 15))) * 16; }
+// The chunk swizzle g(r) of row r, and the byte offset of 16-byte chunk c of row r.
+__device__ __forceinline__ int wide_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+__device__ __forceinline__ int wide_off(int r, int c) { return (r * WCH + (c ^ wide_swz(r))) * 16; }
 
 __device__ __forceinline__ u32x4 wds_read_b128(uint32_t a) {
     u32x4 r;
@@ -66,7 +70,7 @@ __device__ __forceinline__ void load_rows(char* dst, const uint16_t* base, int r
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int r = 8 * w + i;
-        load16_to_lds(rsrc, dst + r * ROWB, r * rs * 2 + ((lane ^ (r & 15)) * 16));
+        load16_to_lds(rsrc, dst + r * ROWB, r * rs * 2 + ((lane ^ wide_swz(r)) * 16));
     }
 }
 
@@ -151,9 +155,10 @@ __global__ __launch_bounds__(WNW * 64) void sdpa_fwd_bf16_wide(
                                        sp);
         }
         {
-            u32x4* red = reinterpret_cast<u32x4*>(lds + LRED + w * 4096 + lane * 64);
+            // [wave][q4][lane]: consecutive lanes write consecutive 16 bytes
+            u32x4* red = reinterpret_cast<u32x4*>(lds + LRED + w * 4096 + lane * 16);
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) red[q4] = u32x4{__float_as_uint(sp[4 * q4]), __float_as_uint(sp[4 * q4 + 1]),
+            for (int q4 = 0; q4 < 4; ++q4) red[64 * q4] = u32x4{__float_as_uint(sp[4 * q4]), __float_as_uint(sp[4 * q4 + 1]),
                                                            __float_as_uint(sp[4 * q4 + 2]),
                                                            __float_as_uint(sp[4 * q4 + 3])};
         }
@@ -166,10 +171,10 @@ __global__ __launch_bounds__(WNW * 64) void sdpa_fwd_bf16_wide(
         for (int i = 0; i < 16; ++i) s[i] = 0.f;
 #pragma unroll
         for (int w2 = 0; w2 < WNW; ++w2) {
-            const u32x4* red = reinterpret_cast<const u32x4*>(lds + LRED + w2 * 4096 + lane * 64);
+            const u32x4* red = reinterpret_cast<const u32x4*>(lds + LRED + w2 * 4096 + lane * 16);
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
-                const u32x4 x = red[q4];
+                const u32x4 x = red[64 * q4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) s[4 * q4 + e] += __uint_as_float(x[e]);
             }
