@@ -109,3 +109,109 @@ def test_largest_head(gpu_lib, i):
     print(f"max size {name}: max abs err {err:.2e} (bar {tol:.1e}; the markers move the output by {shift:.2f})")
     assert shift > 5 * tol
     assert np.all(np.isfinite(got)) and err <= tol
+
+
+# --- the gradient at the largest heads ---------------------------------------
+#
+# The same repetition turns the gradient of the huge head into a small one:
+# R copies of a key share one weight, so over the copies the gradient terms of
+# dQ add up to R times one copy's, which is the gradient of a head holding the
+# block once with every logit raised by ln R.  The oracle gets that head with
+# an extra input dimension (q: ln R / scale, block keys: 1, marker keys: 0).
+# Each copy's dK and dV row is then the block row's divided by R (its weight is
+# 1/R of the aggregate, its dP the same), the marker rows are the small head's
+# marker rows, and rows past the key length are exactly zero.  dQ sums over all
+# m keys: in fp32 its bar is the textbook bound of a running sum, N·2^-24·scale·
+# Σ_j |dS_ij||k_j| with N = m / 16 + 16 (each matrix-core step adds a partial sum
+# of 16 products into one fp32 accumulator, without compensation) plus the
+# usual fp32 gradient bar; in bf16 the usual gradient bar.
+
+BWD_CASES = [  # id, dtype, n, d, m, key length below m
+    ("bf16_d64", "bf16", 40, 64, (1 << 24) - 1, True),
+    ("bf16_d64_full", "bf16", 24, 64, (1 << 24) - 1, False),
+    ("bf16_d128", "bf16", 20, 128, (1 << 23) - 1, True),
+    ("f32_d64", "f32", 20, 64, (1 << 23) - 1, True),
+]
+
+
+def _small_head(c, R, t, mv, d):
+    """The small head equivalent to R block copies plus t markers (values mv)."""
+    q = c["q"][0, 0].astype(np.float64)
+    kb = c["k"][0, 0].astype(np.float64)
+    vb = c["v"][0, 0].astype(np.float64)
+    scale = 1.0 / math.sqrt(d)
+    qa = np.concatenate([q, np.full((q.shape[0], 1), math.log(R) / scale)], axis=1)
+    ka = np.concatenate([np.concatenate([kb, np.ones((kb.shape[0], 1))], axis=1),
+                         np.concatenate([kb[:t], np.zeros((t, 1))], axis=1)], axis=0)
+    va = np.concatenate([vb, np.full((t, d), mv)], axis=0)
+    return qa, ka, va, scale
+
+
+@pytest.mark.parametrize("i", range(len(BWD_CASES)), ids=[c[0] for c in BWD_CASES])
+def test_largest_head_backward(gpu_lib, i):
+    import torch
+
+    from transformer_attention_sdpa_amd import backward, forward
+
+    name, dt, n, d, m, padded = BWD_CASES[i]
+    rng = np.random.default_rng(9700 + i)
+    c = random_case(rng, 1, 1, n, P, d, d, dtype=dt)
+    do_h = rng.standard_normal((1, 1, n, d), dtype=np.float32)
+    R = (m - T) // P
+    t = T if padded else m - R * P
+    L = R * P + t
+    mv = marker_value(t)
+    print(f"max size backward {name}: n={n} m={m} d={d} key length {L}", flush=True)
+    q, do = to_device(c["q"], dt), to_device(do_h, dt)
+    kb, vb = to_device(c["k"], dt)[0, 0], to_device(c["v"], dt)[0, 0]
+    k = torch.empty((1, 1, m, d), dtype=q.dtype, device="cuda")
+    v = torch.empty_like(k)
+    k[0, 0, :R * P] = kb.repeat(R, 1)
+    v[0, 0, :R * P] = vb.repeat(R, 1)
+    k[0, 0, R * P:L] = kb[:t]
+    v[0, 0, R * P:L] = mv
+    k[0, 0, L:] = float("nan")
+    v[0, 0, L:] = float("nan")
+    kl = torch.tensor([L], dtype=torch.int32, device="cuda") if padded else None
+    out, lse = forward(q, k, v, key_lens=kl, return_lse=True)
+    dq, dk, dv = backward(q, k, v, out, do, lse, key_lens=kl)
+    torch.cuda.synchronize()
+    rows = {"first copy": slice(0, P), "last copy": slice((R - 1) * P, R * P), "markers": slice(R * P, L)}
+    got_k = {w: from_device(dk[0, 0, s]) for w, s in rows.items()}
+    got_v = {w: from_device(dv[0, 0, s]) for w, s in rows.items()}
+    past_zero = bool(torch.all(dk[0, 0, L:] == 0).item() and torch.all(dv[0, 0, L:] == 0).item())
+    got_q = from_device(dq)[0, 0]
+    del k, v, dk, dv
+    torch.cuda.empty_cache()
+
+    do64 = do_h[0, 0].astype(np.float64) if dt == "f32" else from_device(do)[0, 0]
+    qa, ka, va, scale = _small_head(c, R, t, mv, d)
+    rq, rk, rv = sb.attention_head_backward(qa, ka, va, do64, scale)
+    rq = rq[:, :d]
+    ref_k = {"first copy": rk[:P, :d] / R, "last copy": rk[:P, :d] / R, "markers": rk[P:, :d]}
+    ref_v = {"first copy": rv[:P] / R, "last copy": rv[:P] / R, "markers": rv[P:]}
+
+    def bar(ref):
+        mx = float(np.abs(ref).max())
+        return 2e-2 * mx + 2.0 ** -16 if dt == "bf16" else 2.0 ** -16 * (mx + 1.0)
+
+    msgs = []
+    for w in rows:
+        for what, g, r in (("dk", got_k[w], ref_k[w]), ("dv", got_v[w], ref_v[w])):
+            err = max_abs_err(g, r)
+            msgs.append(f"{what} {w} {err:.1e}/{np.abs(r).max():.1e}")
+            assert np.all(np.isfinite(g)) and err <= bar(r), (name, what, w, err)
+    # dQ: the running sum over ≈ m / 64 tiles
+    P_ = np.exp(qa @ ka.T * scale - np.log(np.exp(qa @ ka.T * scale).sum(1, keepdims=True)))
+    dP = do64 @ va.T
+    dS = P_ * (dP - (P_ * dP).sum(1, keepdims=True))
+    sum_abs = scale * np.abs(dS) @ np.abs(ka[:, :d])  # the aggregate rows already hold the R copies
+    if dt == "bf16":
+        qbar = np.full_like(rq, 2e-2 * float(np.abs(rq).max()) + 2.0 ** -16)
+    else:
+        qbar = (m / 16 + 16) * 2.0 ** -24 * sum_abs + 2.0 ** -16 * (float(np.abs(rq).max()) + 1.0)
+    err_q = np.abs(got_q - rq)
+    msgs.append(f"dq {float(err_q.max()):.1e}/{np.abs(rq).max():.1e}")
+    print(f"max size backward {name}: " + ", ".join(msgs))
+    assert np.all(np.isfinite(got_q)) and np.all(err_q <= qbar), (name, float(err_q.max()))
+    assert past_zero, "rows past the key length must get zero dK, dV"
