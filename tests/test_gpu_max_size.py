@@ -122,9 +122,9 @@ def test_largest_head(gpu_lib, i):
 # 1/R of the aggregate, its dP the same), the marker rows are the small head's
 # marker rows, and rows past the key length are exactly zero.  dQ sums over all
 # m keys: in fp32 its bar is the textbook bound of a running sum, N·2^-24·scale·
-# Σ_j |dS_ij||k_j| with N = m / 16 + 16 (each matrix-core step adds a partial sum
-# of 16 products into one fp32 accumulator, without compensation) plus the
-# usual fp32 gradient bar; in bf16 the usual gradient bar.
+# Σ_j |dS_ij||k_j| with N = m / 2 + 2 (each fp32 matrix-core step adds a partial
+# sum of 2 products into one accumulator, without compensation) plus the usual
+# fp32 gradient bar; in bf16 the usual gradient bar.
 
 BWD_CASES = [  # id, dtype, n, d, m, key length below m
     ("bf16_d64", "bf16", 40, 64, (1 << 24) - 1, True),
@@ -209,7 +209,7 @@ def test_largest_head_backward(gpu_lib, i):
     if dt == "bf16":
         qbar = np.full_like(rq, 2e-2 * float(np.abs(rq).max()) + 2.0 ** -16)
     else:
-        qbar = (m / 16 + 16) * 2.0 ** -24 * sum_abs + 2.0 ** -16 * (float(np.abs(rq).max()) + 1.0)
+        qbar = (m / 2 + 2) * 2.0 ** -24 * sum_abs + 2.0 ** -16 * (float(np.abs(rq).max()) + 1.0)
     err_q = np.abs(got_q - rq)
     msgs.append(f"dq {float(err_q.max()):.1e}/{np.abs(rq).max():.1e}")
     print(f"max size backward {name}: " + ", ".join(msgs))
