@@ -89,3 +89,17 @@ def test_backward_work_matches_brute_force(name):
         flops, nbytes = bench.backward_work(wl, key_lens, dt)
         assert flops == 10 * 64 * pairs
         assert nbytes == (esz * 64 * (4 * rows_q + 2 * kv_rows + 2 * wl.B * wl.h * wl.m) + 4 * rows_q)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: --gpus N > 1 exits with status 2 and says so,
+    before touching a device."""
+    import os
+    import subprocess
+    import sys
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=300, cwd=root)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
