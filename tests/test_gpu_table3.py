@@ -53,6 +53,9 @@ CASES = [  # id, (B, h, n, m, d_k, d_v), options
     ("d512_bottom_right", (4, 2, 5, 200, 512, 512), dict(window=(None, 0, "bottom_right"), key_lens=(0, 200))),
     ("d512_ragged", (2, 3, 33, 17, 512, 512), dict(key_lens=(0, 20))),
     ("d512_one_by_one", (1, 1, 1, 1, 512, 512), {}),
+    # 320 query blocks: one workgroup per block (fewer than 256 blocks split
+    # each block's output dims over two workgroups, as in every case above)
+    ("d512_many_blocks", (64, 1, 130, 130, 512, 512), dict(key_lens=(8, 130))),
 ]
 
 

@@ -74,6 +74,10 @@ __device__ __forceinline__ void load_rows(char* dst, const uint16_t* base, int r
     }
 }
 
+// NS: the workgroups that share one query block, each producing WD / NS of
+// the output dims (every one forms the whole scores; 2 when the query blocks
+// alone would leave compute units idle).
+template <int NS>
 __global__ __launch_bounds__(WNW * 64) void sdpa_fwd_bf16_wide(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ lse, int BH, int H, int n, int m, float c_log2, int wl,
@@ -83,7 +87,9 @@ __global__ __launch_bounds__(WNW * 64) void sdpa_fwd_bf16_wide(
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, l32 = lane & 31, hf = lane >> 5, gi = lane & 15;
 
-    const int g = blockIdx.x;
+    constexpr int OSLICE = WD / NS / WNW;  // output dims per wave
+    const int sidx = NS == 1 ? 0 : (int)(blockIdx.x % NS);  // this workgroup's share of the output dims
+    const int g = blockIdx.x / NS;
     const int bh = g % BH;
     const int q0 = (nqb - 1 - g / BH) * WBQ;  // latest query blocks first
     const int b = bh / H, hh = bh - b * H;
@@ -109,20 +115,20 @@ __global__ __launch_bounds__(WNW * 64) void sdpa_fwd_bf16_wide(
     // and the Vᵀ transpose reads of this wave's output dims (rows 4·hf + gi/4,
     // + 8; k-step j adds 16·j rows, which keeps the swizzle).
     const uint32_t l0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds;
-    int vaddr[WSLICE / 32][2];
+    int vaddr[OSLICE / 32][2];
     {
         const int r0 = 4 * hf + (gi >> 2);
 #pragma unroll
-        for (int dt = 0; dt < WSLICE / 32; ++dt) {
-            const int c0 = WSLICE * w + 32 * dt + 16 * ((lane >> 4) & 1) + 4 * (gi & 3);
+        for (int dt = 0; dt < OSLICE / 32; ++dt) {
+            const int c0 = (WD / NS) * sidx + OSLICE * w + 32 * dt + 16 * ((lane >> 4) & 1) + 4 * (gi & 3);
             vaddr[dt][0] = LV + wide_off(r0, c0 >> 3) + (c0 & 7) * 2;
             vaddr[dt][1] = LV + wide_off(r0 + 8, c0 >> 3) + (c0 & 7) * 2;
         }
     }
 
-    f32x16 oacc[WSLICE / 32];
+    f32x16 oacc[OSLICE / 32];
 #pragma unroll
-    for (int dt = 0; dt < WSLICE / 32; ++dt)
+    for (int dt = 0; dt < OSLICE / 32; ++dt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[dt][i] = 0.f;
     float mref = -INFINITY, lsum = 0.f;
@@ -197,7 +203,7 @@ __global__ __launch_bounds__(WNW * 64) void sdpa_fwd_bf16_wide(
         const float mc = (mnew == -INFINITY ? 0.f : mnew) * c_log2;
         lsum *= alpha;
 #pragma unroll
-        for (int dt = 0; dt < WSLICE / 32; ++dt)
+        for (int dt = 0; dt < OSLICE / 32; ++dt)
 #pragma unroll
             for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
         bf16x8 pb[2];
@@ -213,20 +219,20 @@ __global__ __launch_bounds__(WNW * 64) void sdpa_fwd_bf16_wide(
         }
         // Oᵀ_w += V_wᵀ · Pᵀ.
         {
-            u32x2 va[2 * (WSLICE / 32) * 2];
+            u32x2 va[2 * (OSLICE / 32) * 2];
 #pragma unroll
             for (int j = 0; j < 2; ++j)
 #pragma unroll
-                for (int dt = 0; dt < WSLICE / 32; ++dt) {
-                    va[(j * (WSLICE / 32) + dt) * 2] = wds_read_tr(l0 + vaddr[dt][0] + j * 16 * ROWB);
-                    va[(j * (WSLICE / 32) + dt) * 2 + 1] = wds_read_tr(l0 + vaddr[dt][1] + j * 16 * ROWB);
+                for (int dt = 0; dt < OSLICE / 32; ++dt) {
+                    va[(j * (OSLICE / 32) + dt) * 2] = wds_read_tr(l0 + vaddr[dt][0] + j * 16 * ROWB);
+                    va[(j * (OSLICE / 32) + dt) * 2 + 1] = wds_read_tr(l0 + vaddr[dt][1] + j * 16 * ROWB);
                 }
             wlds_wait(va);
 #pragma unroll
             for (int j = 0; j < 2; ++j)
 #pragma unroll
-                for (int dt = 0; dt < WSLICE / 32; ++dt) {
-                    const u32x2 lo = va[(j * (WSLICE / 32) + dt) * 2], hi = va[(j * (WSLICE / 32) + dt) * 2 + 1];
+                for (int dt = 0; dt < OSLICE / 32; ++dt) {
+                    const u32x2 lo = va[(j * (OSLICE / 32) + dt) * 2], hi = va[(j * (OSLICE / 32) + dt) * 2 + 1];
                     const u32x4 v4 = {lo[0], lo[1], hi[0], hi[1]};
                     oacc[dt] = mfma32x32x16_bf16(__builtin_bit_cast(bf16x8, v4), pb[j], oacc[dt]);
                 }
@@ -242,13 +248,13 @@ __global__ __launch_bounds__(WNW * 64) void sdpa_fwd_bf16_wide(
     const float ltot = half_swap_sum(lsum);
     const float inv = ltot != 0.f ? 1.f / ltot : 0.f;  // no legal key ⇒ zero row
     if (qrow < n) {
-        if (lse && w == 0 && hf == 0) {
+        if (lse && sidx == 0 && w == 0 && hf == 0) {
             const float mc = (mref == -INFINITY ? 0.f : mref) * c_log2;
             lse[(size_t)bh * n + qrow] = (mc + log2f(ltot)) * 0.6931471805599453f;
         }
-        uint16_t* dst = Oh + (size_t)qrow * lay.o.r + WSLICE * w;
+        uint16_t* dst = Oh + (size_t)qrow * lay.o.r + (WD / NS) * sidx + OSLICE * w;
 #pragma unroll
-        for (int dt = 0; dt < WSLICE / 32; ++dt)
+        for (int dt = 0; dt < OSLICE / 32; ++dt)
 #pragma unroll
             for (int i4 = 0; i4 < 4; ++i4) {
                 bf16x4 o;
@@ -267,7 +273,11 @@ hipError_t launch_bf16_wide(const Args& a, hipStream_t stream) {
     const int BH = a.B * a.H;
     const float c_log2 = (float)((double)a.scale * 1.4426950408889634);  // scale·log2(e)
     const int nqb = (a.n + WBQ - 1) / WBQ;
-    hipLaunchKernelGGL(sdpa_fwd_bf16_wide, dim3(nqb * BH), dim3(WNW * 64), 0, stream, (const uint16_t*)a.q,
+    // Two workgroups per query block (each half of the output dims) while the
+    // query blocks alone are fewer than the compute units.
+    const bool split = (long long)nqb * BH < 256;
+    const auto kernel = split ? sdpa_fwd_bf16_wide<2> : sdpa_fwd_bf16_wide<1>;
+    hipLaunchKernelGGL(kernel, dim3(nqb * BH * (split ? 2 : 1)), dim3(WNW * 64), 0, stream, (const uint16_t*)a.q,
                        (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.out, a.lse, BH, a.H, a.n, a.m,
                        c_log2, a.wl, a.wr, a.bottom_right, a.key_lens, nqb, a.lay);
     return hipGetLastError();
